@@ -1,0 +1,159 @@
+"""MXFP8 codecs and the quantization-faithful MXFP8 expert path (test infrastructure).
+
+Source: "Dist-MoE - Speed-of-light distributed Mixture-of-Experts kernels",
+section 02 "Expert Computation and Tensor Precision":
+  * E4M3 has 4 exponent bits and 3 fraction bits; its largest finite
+    magnitude is 448.  E8M0 encodes a power-of-two scale in one byte.
+  * MXFP8 stores E4M3 values with one E8M0 scale per 32 logical values; the
+    producer picks the scale, rounds the values and publishes both.
+  * forward GEMMs contract over features, so activation rows carry scales
+    along that axis (1x32); weight gradients contract over token rows and use
+    a separately quantized column bundle (32x1 down the rows); static weights
+    use 32x32 blocks, so forward and input-gradient GEMMs share the same
+    values with two scale orientations.
+  * MXFP8 training quantizes the BF16 rows after the gather.
+
+Readings taken where the page is silent (each is a choice, listed in the
+design notes):
+  * E4M3 is the finite-only variant: exponent bias 7, subnormals down to
+    2^-9, no infinities, S.1111.111 is NaN, so 448 = 1.75 * 2^8 is the top.
+    Rounding is to nearest, ties to even; magnitudes above 448 saturate.
+  * E8M0 scale of a block: the smallest integer e with amax <= 448 * 2^e,
+    clamped to [-127, 127]; an all-zero block gets e = -127.  With this rule
+    no scaled value exceeds 448 (parity unpinned: the rule itself is a choice).
+  * Blocks start at index 0 of each axis of each expert's matrix; column
+    bundles pad an expert's rows with zero rows up to a multiple of 32.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_MIN_NORMAL = 2.0 ** -6
+E4M3_MIN_SUBNORMAL = 2.0 ** -9
+BLOCK = 32
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 byte (NaN for S.1111.111)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    exp = (c >> 3) & 0xF
+    man = c & 0x7
+    val = np.where(exp == 0, man / 8.0 * 2.0 ** -6,
+                   (1.0 + man / 8.0) * np.ldexp(1.0, (exp - 7).astype(np.int64)))
+    val = np.where((exp == 0xF) & (man == 0x7), np.nan, val)
+    return sign * val
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Round float64 values onto the E4M3 grid (nearest, ties to even; saturate at 448)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, p = np.frexp(a)                    # a = m * 2^p, m in [0.5, 1)
+    # Normal binade [2^(p-1), 2^p) has 8 steps of 2^(p-4); below 2^-6 the
+    # subnormal step is 2^-9.
+    step = np.where(a >= E4M3_MIN_NORMAL, np.ldexp(1.0, (p - 4).astype(np.int64)),
+                    E4M3_MIN_SUBNORMAL)
+    q = np.rint(a / step) * step          # rint rounds half to even
+    q = np.minimum(q, E4M3_MAX)
+    return np.copysign(q, v)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 byte of each value after ``e4m3_round``."""
+    q = e4m3_round(v)
+    a = np.abs(q)
+    sign = np.where(np.signbit(q), 0x80, 0)
+    _, p = np.frexp(a)
+    normal = a >= E4M3_MIN_NORMAL
+    exp = np.where(normal, p - 1 + 7, 0)
+    man = np.where(normal, np.rint((a / np.ldexp(1.0, (p - 1).astype(np.int64)) - 1.0) * 8.0),
+                   np.rint(a / E4M3_MIN_SUBNORMAL))
+    return (sign | (exp.astype(np.int64) << 3) | man.astype(np.int64)).astype(np.uint8)
+
+
+def e8m0_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e, clamped to [-127, 127] (-127 for 0)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, p = np.frexp(amax)                 # 448 = 0.875 * 2^9
+    e = np.where(m <= 0.875, p - 9, p - 8)
+    e = np.where(amax == 0.0, -127, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def _qdq_blocks(blocks: np.ndarray, axes) -> np.ndarray:
+    amax = np.max(np.abs(blocks), axis=axes, keepdims=True)
+    e = e8m0_exponent(amax)
+    scale = np.ldexp(1.0, e)
+    return e4m3_round(blocks / scale) * scale
+
+
+def qdq_rows(v: np.ndarray) -> np.ndarray:
+    """Quantize-dequantize with 1x32 blocks along the last axis (length % 32 == 0)."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[-1]
+    if n % BLOCK:
+        raise ValueError("row length must be a multiple of 32")
+    b = v.reshape(v.shape[:-1] + (n // BLOCK, BLOCK))
+    return _qdq_blocks(b, -1).reshape(v.shape)
+
+
+def qdq_cols(v: np.ndarray) -> np.ndarray:
+    """32x1 blocks down the rows of one expert's [M, N] matrix; rows are padded
+    with zeros to a multiple of 32 for blocking and the pad is dropped again."""
+    v = np.asarray(v, dtype=np.float64)
+    M, N = v.shape
+    Mp = -(-M // BLOCK) * BLOCK
+    pad = np.zeros((Mp, N))
+    pad[:M] = v
+    b = pad.reshape(Mp // BLOCK, BLOCK, N)
+    return _qdq_blocks(b, 1).reshape(Mp, N)[:M]
+
+
+def qdq_32x32(w: np.ndarray) -> np.ndarray:
+    """32x32 blocks over a weight matrix [N, K] (both multiples of 32)."""
+    w = np.asarray(w, dtype=np.float64)
+    N, K = w.shape
+    if N % BLOCK or K % BLOCK:
+        raise ValueError("weight dims must be multiples of 32")
+    b = w.reshape(N // BLOCK, BLOCK, K // BLOCK, BLOCK)
+    return _qdq_blocks(b, (1, 3)).reshape(N, K)
+
+
+# --------------------------------------------------------------------------
+# Quantization-faithful expert FFN: quantize -> dequantize at every operand
+# the MXFP8 path feeds to a block-scaled GEMM, fp64 everywhere else.
+# --------------------------------------------------------------------------
+
+def expert_ffn_mx(x_rows, w13q, w2q):
+    """Forward.  x rows quantized 1x32 along D (after the gather); h2 quantized
+    1x32 along F for the W2 GEMM.  ``w13q``/``w2q`` are 32x32-block
+    dequantized weights.  Returns dense h1, h2 and h3."""
+    from .moe import silu
+    F = w2q.shape[1]
+    h1 = qdq_rows(x_rows) @ w13q.T
+    g, u = h1[:, :F], h1[:, F:]
+    h2 = silu(g) * u
+    h3 = qdq_rows(h2) @ w2q.T
+    return h1, h2, h3
+
+
+def expert_ffn_backward_mx(x_rows, w13q, w2q, h1, dh3):
+    """Backward.  DGRAD operands are quantized along their contraction axis
+    (dh3 1x32 along D, dh1 1x32 along 2F) and use the same 32x32 weight
+    values; WGRAD operands are column bundles (32x1 down the expert's rows)
+    of dh3, h2, dh1 and x."""
+    from .moe import silu, silu_grad
+    F = w2q.shape[1]
+    g, u = h1[:, :F], h1[:, F:]
+    h2 = silu(g) * u
+    dh2 = qdq_rows(dh3) @ w2q
+    dw2 = qdq_cols(dh3).T @ qdq_cols(h2)
+    dg = dh2 * u * silu_grad(g)
+    du = dh2 * silu(g)
+    dh1 = np.concatenate([dg, du], axis=1)
+    dx = qdq_rows(dh1) @ w13q
+    dw13 = qdq_cols(dh1).T @ qdq_cols(x_rows)
+    return dx, dw13, dw2, dh1

@@ -1,0 +1,52 @@
+"""Saved-state byte accounting and the save/replay decision (test infrastructure).
+
+Source: "Dist-MoE - Speed-of-light distributed Mixture-of-Experts kernels",
+section 03 (align128(n) = ceil(n / 128) * 128; BF16 forward scratch
+2R(D + 3F) bytes before alignment) and section 04 "Save and Recompute
+Decisions": before saving a layer's full state the planner replays instead
+when the worst rank's saved bytes plus that layer's full state, plus the
+remaining layers times the bytes each must keep for replay, exceed the slot
+capacity.  A replaying layer keeps only its replay input.  Backward runs the
+layers in reverse and rewinds the cursor to each layer's start.
+
+One GPU has one rank, so the worst-rank maximum is the value itself.
+"""
+
+from __future__ import annotations
+
+
+def align128(n: int) -> int:
+    return -(-int(n) // 128) * 128
+
+
+def dm_full_state_bytes(R: int, T: int, K: int, D: int, F: int) -> int:
+    """BF16 full state as the explainer counts it: gathered x [R,D], h1
+    [R,2F] and the route-output slots [T*K, D], each aligned to 128 B."""
+    return align128(R * D * 2) + align128(R * 2 * F * 2) + align128(T * K * D * 2)
+
+
+def bf16_forward_scratch_bytes(R: int, D: int, F: int) -> int:
+    """x_gathered, h1 and h2 of one call: 2R(D + 3F) bytes (before alignment)."""
+    return 2 * R * (D + 3 * F)
+
+
+def decide(full_bytes, keep_bytes: int, capacity: int):
+    """Run the forward decisions of a stack of layers in one slot.
+
+    ``full_bytes[l]`` is layer l's full saved state, ``keep_bytes`` what a
+    replaying layer keeps (its replay input).  Returns (need_recompute list,
+    start cursor of each layer, candidate value tested for each layer).
+    Layer l replays iff cursor + full_l + (L - 1 - l) * keep > capacity; the
+    cursor then advances by keep (replay) or full_l (save).
+    """
+    L = len(full_bytes)
+    cursor = 0
+    flags, starts, tested = [], [], []
+    for l, full in enumerate(full_bytes):
+        cand = cursor + int(full) + (L - 1 - l) * int(keep_bytes)
+        starts.append(cursor)
+        tested.append(cand)
+        replay = cand > capacity
+        flags.append(replay)
+        cursor += int(keep_bytes) if replay else int(full)
+    return flags, starts, tested

@@ -1,0 +1,42 @@
+"""The seeded input generators: determinism and the stated recipe (CPU only)."""
+import numpy as np
+import torch
+
+from mixture_experts_routed_03_amd import workloads as wl
+
+
+def test_routing_recipe_uniform_and_padding():
+    ids, s = wl.make_routing(256, 8, 2, n_pad=26, seed=0)
+    ids2, s2 = wl.make_routing(256, 8, 2, n_pad=26, seed=0)
+    np.testing.assert_array_equal(ids, ids2); np.testing.assert_array_equal(s, s2)
+    assert ids.dtype == np.int32 and s.dtype == np.float32
+    assert (ids == -1).sum() == 26 and np.all(s[ids == -1] == 0)
+    full = np.all(ids >= 0, axis=1)
+    np.testing.assert_allclose(s[full].sum(axis=1), 1.0, rtol=1e-6)
+    for row in ids:
+        live = row[row >= 0]
+        assert len(set(live.tolist())) == len(live)        # distinct experts per token
+    # scores are the softmax of the selected logits, largest first
+    assert np.all(np.diff(s[full], axis=1) <= 0)
+
+
+def test_routing_recipe_zipf_skew():
+    ids, s = wl.make_routing(2048, 384, 6, zipf_s=1.2, seed=0)
+    counts = np.bincount(ids.reshape(-1), minlength=384)
+    assert counts.sum() == 2048 * 6
+    assert counts.max() > 1000 and (counts == 0).sum() >= 1
+    for row in ids[:64]:
+        assert len(set(row.tolist())) == 6
+    ids0, _ = wl.make_routing(2048, 384, 6, zipf_s=0.0, seed=0)
+    c0 = np.bincount(ids0.reshape(-1), minlength=384)
+    assert c0.max() < 80          # s = 0 is uniform
+
+
+def test_dense_tensors_are_seeded():
+    a = wl.normal((4, 8), 0.5, seed=3, dtype=torch.bfloat16)
+    b = wl.normal((4, 8), 0.5, seed=3, dtype=torch.bfloat16)
+    assert torch.equal(a, b) and a.dtype == torch.bfloat16
+    cfg = wl.scaled(wl.CONFIGS["tiny_f32"], T=16)
+    lay = wl.make_layer(cfg)
+    assert lay["x"].shape == (16, 256) and lay["w13"].shape == (8, 256, 256)
+    assert lay["w2"].shape == (8, 256, 128) and lay["x"].dtype == torch.float32
