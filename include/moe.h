@@ -1,0 +1,232 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) routed-expert MoE layer library.
+ *
+ * The layer computes, for tokens x[T,D], caller-supplied expert ids and
+ * scores [T,K], gate|up weights W13[E,2F,D] and down weights W2[E,D,F]:
+ *
+ *   for every valid route r = t*K + k (0 <= ids[t,k] < E):
+ *     h1 = W13[e] x[t] = [g; u]      (gate rows first)
+ *     h2 = SiLU(g) * u,  SiLU(z) = z / (1 + e^-z)
+ *     h3 = W2[e] h2
+ *   y[t] = sum over valid k, ascending, of scores[t,k] * h3(t,k)   (fp32 sum)
+ *
+ * and its backward (dx, dW13, dW2, dscores).  Sources: the Dist-MoE visual
+ * explainer ("Speed-of-light distributed Mixture-of-Experts kernels"),
+ * section 01 (the caller-inputs table and the contract that id -1 disables a
+ * route, needs score 0, and an all-inactive row returns exact zero; the
+ * owner applies the scores and sums the K routes in FP32), section 02 (the
+ * expert equation and the MXFP8 formats), sections 03-04 (activation budget,
+ * align128 byte accounting, the save/replay inequality, reverse-order
+ * backward); and "Mixture of Experts: How Routing Becomes GPU Computation",
+ * section 2 (packing rows by expert with a stable sort and exclusive prefix
+ * offsets, grouped GEMM C_e = A_e B_e^T and its gradients, SwiGLU backward),
+ * section 5 (the combine gradients dH = p dY, dp = <H, dY>).
+ *
+ * Conventions for every call
+ *  - All tensors are contiguous, row-major, in device memory (HBM) unless a
+ *    parameter says "host".  Activations and weights are float32 for
+ *    MOE_PREC_F32 and bfloat16 for MOE_PREC_BF16 / MOE_PREC_MXFP8.
+ *  - The caller owns every buffer and allocates it with the sizes reported
+ *    by moe_plan_sizes; the library never allocates or frees device memory
+ *    and keeps no pointer after a call returns.
+ *  - Work is enqueued on the caller's stream; nothing but moe_read_status
+ *    waits for the device, so a step can be captured in a HIP graph.
+ *  - A plan with its workspaces serves one stream at a time (not reentrant);
+ *    concurrent layers need separate plans or workspaces.
+ *  - Errors detected on the host return a status code before anything is
+ *    enqueued.  Errors only the device can see (ids outside [-1, E)) set
+ *    sticky bits read by moe_read_status and never trap; such routes are
+ *    treated as padding.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* null / misaligned pointer, T > t_max, bad layer index */
+  MOE_ERR_SHAPE = 2,        /* D, F, E, K outside the supported set */
+  MOE_ERR_UNSUPPORTED = 3,  /* combination not built (e.g. backward of an inference plan) */
+  MOE_ERR_WORKSPACE = 4,    /* workspace smaller than moe_plan_sizes reported */
+  MOE_ERR_HIP = 5           /* a HIP runtime call failed */
+} moe_status;
+
+typedef enum moe_prec {
+  MOE_PREC_F32 = 0,         /* fp32 operands, fp32 MFMA */
+  MOE_PREC_BF16 = 1,        /* bf16 operands, fp32 accumulation */
+  MOE_PREC_MXFP8 = 2        /* E4M3 operands with E8M0 scales per 32 values */
+} moe_prec;
+
+typedef enum moe_dtype {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1
+} moe_dtype;
+
+/* Device status bits (moe_read_status). */
+#define MOE_STATUS_BAD_ID     0x1u  /* some id < -1 or >= E: treated as padding */
+#define MOE_STATUS_PAD_SCORE  0x2u  /* nonzero score on an id -1 route: ignored */
+#define MOE_STATUS_ARENA      0x4u  /* backward of a layer whose forward state is gone */
+#define MOE_STATUS_NULL_INPUT 0x8u  /* null x/scores/dy for a call with rows: rows skipped */
+
+/* moe_expert_bwd flags */
+#define MOE_BWD_ACCUMULATE_DX 0x1u  /* dx += result instead of dx = result */
+
+/* Layer description.  Supported: D % 128 == 0, F % 128 == 0, 1 <= K <= 16,
+ * K <= E <= 4096, 0 <= t_max <= 2^24 / K. */
+typedef struct moe_desc {
+  int64_t t_max;            /* most tokens any call will pass */
+  int32_t d;                /* token width D */
+  int32_t f;                /* expert intermediate width F */
+  int32_t e;                /* experts E (all local) */
+  int32_t k;                /* routes per token K */
+  int32_t prec;             /* moe_prec */
+  int32_t dw_dtype;         /* moe_dtype of dW13/dW2 (MOE_PREC_F32 needs F32) */
+  int32_t training;         /* 1: forward keeps state for moe_expert_bwd */
+  int32_t max_layers;       /* layers whose saved state shares one arena (>= 1) */
+  int64_t arena_budget;     /* bytes of saved state the arena may hold;
+                               0 = enough to save every layer at R = t_max*K */
+} moe_desc;
+
+/* Byte sizes of the caller-owned buffers (all 256-byte aligned). */
+typedef struct moe_sizes {
+  size_t route_ws;          /* per layer: routing metadata + planner record */
+  size_t scratch;           /* per call, reused by every layer and both passes */
+  size_t h3_slots;          /* per layer: route outputs [t_max*K, D] (act dtype) */
+  size_t arena;             /* shared by the layers of one step (header + budget) */
+  size_t layer_state_max;   /* one layer's full saved state at R = t_max*K */
+  size_t q13, s13, q2, s2;  /* MXFP8 prepared weights (0 otherwise) */
+} moe_sizes;
+
+typedef struct moe_plan_s* moe_plan_t;
+
+/* Expert weights of one layer.  w13/w2 are the caller's [E,2F,D] / [E,D,F]
+ * tensors; q13/s13/q2/s2 the MXFP8 copies made by moe_prepare_weights
+ * (E4M3 bytes with the weight's shape, E8M0 bytes [E,2F/32,D/32] and
+ * [E,D/32,F/32]).  Unused members may be null. */
+typedef struct moe_weights {
+  const void* w13;
+  const void* w2;
+  const void* q13;
+  const void* s13;
+  const void* q2;
+  const void* s2;
+} moe_weights;
+
+/* Gradient outputs of one layer.  dx [T,D] act dtype; dw13 [E,2F,D] and
+ * dw2 [E,D,F] in the plan's dw_dtype (fully written: experts with no rows
+ * get exact zeros); dscores [T,K] float32 or null (0 for padding routes). */
+typedef struct moe_grads {
+  void* dx;
+  void* dw13;
+  void* dw2;
+  float* dscores;
+} moe_grads;
+
+/* Validate a description and build a host-side plan (no device work).
+ * *out receives a handle owned by the library; free it with moe_plan_destroy. */
+moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out);
+
+/* Buffer sizes for a plan (host only). */
+moe_status moe_plan_sizes(moe_plan_t plan, moe_sizes* sizes);
+
+/* Human-readable breakdown of the plan's buffers into buf (host, NUL
+ * terminated, truncated to cap bytes).  Cf. plan_memory().explain() of the
+ * Dist-MoE API, which likewise runs without touching a device. */
+moe_status moe_plan_explain(moe_plan_t plan, char* buf, size_t cap);
+
+void moe_plan_destroy(moe_plan_t plan);
+
+/* MXFP8 weight preparation (explainer section 02: static weights use 32x32
+ * blocks so forward and input-gradient GEMMs share the E4M3 values).  Reads
+ * w13/w2 (bf16), writes q13/s13/q2/s2.  Done once per weight update; it is
+ * not part of a timed step. */
+moe_status moe_prepare_weights(moe_plan_t plan, const void* w13, const void* w2,
+                               void* q13, void* s13, void* q2, void* s2,
+                               hipStream_t stream);
+
+/* Routing metadata (grouped-GEMM blog section 2 "Packing"): per-expert row
+ * counts, exclusive prefix offsets, the stable expert-major order of valid
+ * routes (ascending r = t*K + k inside an expert) and its inverse, and the
+ * tile schedule of the grouped GEMMs.  ids: device int32 [T,K]; T <= t_max
+ * (host value).  Writes route_ws only; clears the status bits. */
+moe_status moe_route(moe_plan_t plan, int64_t T, const int32_t* ids, void* route_ws,
+                     hipStream_t stream);
+
+/* Expert forward of one layer (explainer section 02, staged form): gather
+ * x rows in expert order, h1 = x W13^T with the SwiGLU epilogue, then
+ * h3 = h2 W2^T stored bf16 (fp32 for F32 plans) into route slot
+ * h3_slots[t*K + k].  Slots of padding routes are not written.  In training
+ * the planner decides on the device whether this layer's state is saved in
+ * the arena or rebuilt by backward (explainer section 04); layer is the
+ * index of this layer in the stack (0 .. max_layers-1) and layer 0 starts
+ * a new step (arena cursor 0).  x: [T,D]. arena may be null for inference. */
+moe_status moe_expert_fwd(moe_plan_t plan, int32_t layer, void* route_ws, const void* x,
+                          const moe_weights* w, void* h3_slots, void* arena, void* scratch,
+                          hipStream_t stream);
+
+/* Token-owner combine (explainer section 01): y[t] = sum over valid k,
+ * ascending, of scores[t,k] * h3_slots[t*K+k] in fp32, plus y_addend[t]
+ * (e.g. a shared expert's output, act dtype, nullable), stored in the act
+ * dtype.  A token with no valid route gets exactly y_addend (or 0). */
+moe_status moe_combine(moe_plan_t plan, void* route_ws, const float* scores,
+                       const void* h3_slots, const void* y_addend, void* y,
+                       hipStream_t stream);
+
+/* Backward of one layer (blog section 2 SwiGLU backward, section 5): from
+ * dy [T,D] computes dscores, W2 DGRAD with the SwiGLU backward epilogue,
+ * W2 and W13 WGRAD, W13 DGRAD and the per-token sum of the K route input
+ * gradients into g->dx.  Rebuilds the layer's state first when its forward
+ * replayed.  Layers of a step must run in reverse forward order; each
+ * backward rewinds the arena cursor to its layer's start. */
+moe_status moe_expert_bwd(moe_plan_t plan, int32_t layer, void* route_ws, const void* x,
+                          const float* scores, const void* dy, const moe_weights* w,
+                          const void* h3_slots, void* arena, void* scratch,
+                          const moe_grads* g, uint32_t flags, hipStream_t stream);
+
+/* Synchronizes stream and returns the sticky MOE_STATUS_* bits of route_ws
+ * (host out-parameter) together with, when not null, the layer's planner
+ * decision (*replayed = 1 when its forward chose replay). */
+moe_status moe_read_status(void* route_ws, uint32_t* status, int32_t* replayed,
+                           hipStream_t stream);
+
+/* Rewind the arena to empty (after an aborted step, when no backward still
+ * needs a saved state). */
+moe_status moe_arena_reset(moe_plan_t plan, void* arena, hipStream_t stream);
+
+/* Routing results of route_ws copied to host memory (synchronizes stream):
+ * counts [E], offsets [E+1], poffsets [E+1] (counts rounded up to 32),
+ * sorted_route [R] and route_to_row [T*K]; any pointer may be null; *R_out
+ * receives the number of valid routes. */
+moe_status moe_route_readback(moe_plan_t plan, void* route_ws, int32_t* counts,
+                              int32_t* offsets, int32_t* poffsets, int32_t* sorted_route,
+                              int32_t* route_to_row, int32_t* R_out, hipStream_t stream);
+
+/* Device pointers of the layer's saved tensors inside scratch/arena, for
+ * inspection by tests (synchronizes stream): gathered x rows [R,D] and h1
+ * [R,2F] in the act dtype. */
+moe_status moe_saved_ptrs(moe_plan_t plan, void* route_ws, void** x_rows, void** h1,
+                          hipStream_t stream);
+
+/* Kernel timing, for benchmarks.  While enabled, every kernel launched by a
+ * call of this plan is bracketed by two HIP events recorded on that call's
+ * stream.  moe_timing_read synchronizes on the recorded events, folds them
+ * into per-kernel totals and returns entry idx (0-based; MOE_ERR_ARG past
+ * the last): its name (host buffer, NUL terminated), total milliseconds and
+ * launch count.  moe_timing_enable(plan, 0) stops recording and clears the
+ * totals. */
+moe_status moe_timing_enable(moe_plan_t plan, int32_t enable);
+moe_status moe_timing_read(moe_plan_t plan, int32_t idx, char* name, size_t cap,
+                           double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,425 @@
+// Host entry points of libmoe (the C ABI declared in include/moe.h).
+//
+// Argument validation happens here, before anything is enqueued; every
+// kernel launch goes to the caller's stream.  The plan is host memory owned
+// by the library; every device buffer belongs to the caller.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+
+hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
+                        const RouteLayout& L, hipStream_t s);
+hipError_t launch_plan_decide(RouteHdr* hdr, const PlanArgs& a, hipStream_t s);
+hipError_t launch_plan_rewind(RouteHdr* hdr, void* arena, hipStream_t s);
+hipError_t launch_arena_reset(void* arena, hipStream_t s);
+hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
+                         const int32_t* sorted_route, int64_t R_max, hipStream_t s);
+hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
+                          const float* scores, const void* h3, const void* addend, void* y,
+                          int K, int64_t D, int64_t T_max, uint32_t* status, hipStream_t s);
+hipError_t launch_combine_bwd(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
+                              const float* scores, const void* dy, const void* h3, void* dh3,
+                              float* dscores, int K, int64_t D, int64_t T_max, hipStream_t s);
+hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
+                            const float* dxr, void* dx, int K, int64_t D, int64_t T_max,
+                            int accumulate, hipStream_t s);
+hipError_t launch_gemm_fwd(int prec, int mode, const FwdArgs& a, int64_t mt_max, int cus,
+                           hipStream_t s);
+hipError_t launch_backward(int prec, int dw_f32, const RouteHdr* hdr, const int32_t* offsets,
+                           const int32_t* mtoff, const void* dh3, const void* w13, const void* w2,
+                           void* dh1, float* dxr, void* dw13, void* dw2, int D, int F, int E,
+                           int64_t mt_max, int cus, hipStream_t s);
+}  // namespace moe
+
+using namespace moe;
+
+struct moe_plan_s {
+  moe_desc d;
+  int es;                 // activation element bytes
+  int64_t R_max;          // t_max * K
+  int64_t mt_max;         // upper bound on m-tiles
+  RouteLayout rl;
+  ScratchLayout sl;
+  int64_t h3_bytes;
+  int64_t state_max;      // one layer's full saved state at R_max
+  int64_t budget;         // arena data bytes
+  int64_t arena_bytes;
+  int cus;                // compute units (queried at first launch)
+  struct TimerSlot {
+    std::string name;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+    double total_ms = 0.0;
+    int64_t launches = 0;
+  };
+  bool timing = false;
+  std::vector<TimerSlot> slots;
+  std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+int64_t a256(int64_t n) { return align_up(n, 256); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int plan_cus(moe_plan_s* p) {
+  if (p->cus > 0) return p->cus;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  p->cus = n;
+  return n;
+}
+
+RouteHdr* hdr_of(void* ws) { return reinterpret_cast<RouteHdr*>(ws); }
+
+hipEvent_t take_event(moe_plan_s* p) {
+  if (!p->pool.empty()) {
+    hipEvent_t e = p->pool.back();
+    p->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+moe_plan_s::TimerSlot& timer_slot(moe_plan_s* p, const char* name) {
+  for (auto& sl : p->slots)
+    if (sl.name == name) return sl;
+  p->slots.emplace_back();
+  p->slots.back().name = name;
+  return p->slots.back();
+}
+
+// Runs one launcher; when timing is on, brackets it with events on stream s.
+template <class Fn>
+hipError_t timed(moe_plan_s* p, const char* name, hipStream_t s, Fn&& fn) {
+  if (!p->timing) return fn();
+  hipEvent_t a = take_event(p), b = take_event(p);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  timer_slot(p, name).pending.emplace_back(a, b);
+  return e;
+}
+
+template <typename T>
+T* at(void* base, int64_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
+  if (!desc || !out) return MOE_ERR_ARG;
+  *out = nullptr;
+  const moe_desc& d = *desc;
+  if (d.t_max < 0 || d.k < 1 || d.k > kMaxK || d.e < d.k || d.e > kMaxE || d.d <= 0 ||
+      d.f <= 0 || d.d % 128 || d.f % 128 || d.t_max * d.k > (int64_t(1) << 24))
+    return MOE_ERR_SHAPE;
+  if (d.prec != MOE_PREC_F32 && d.prec != MOE_PREC_BF16 && d.prec != MOE_PREC_MXFP8)
+    return MOE_ERR_ARG;
+  if (d.prec == MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (d.dw_dtype != MOE_DTYPE_F32 && d.dw_dtype != MOE_DTYPE_BF16) return MOE_ERR_ARG;
+  if (d.prec == MOE_PREC_F32 && d.dw_dtype != MOE_DTYPE_F32) return MOE_ERR_ARG;
+  if (d.max_layers < 1 || d.arena_budget < 0) return MOE_ERR_ARG;
+
+  moe_plan_s* p = new (std::nothrow) moe_plan_s();
+  if (!p) return MOE_ERR_ARG;
+  p->d = d;
+  p->es = d.prec == MOE_PREC_F32 ? 4 : 2;
+  p->R_max = d.t_max * d.k;
+  p->mt_max = std::min<int64_t>(p->R_max, (p->R_max + kBM - 1) / kBM + d.e);
+  const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es;
+
+  RouteLayout& L = p->rl;
+  L.nchunks = (R + kRankChunk - 1) / kRankChunk;
+  int64_t o = 0;
+  L.hdr = o; o = a256(o + 512);
+  L.counts = o; o = a256(o + 4 * E);
+  L.offsets = o; o = a256(o + 4 * (E + 1));
+  L.poffsets = o; o = a256(o + 4 * (E + 1));
+  L.mtoff = o; o = a256(o + 4 * (E + 1));
+  L.chunk_hist = o; o = a256(o + 4 * L.nchunks * E);
+  L.chunk_flags = o; o = a256(o + 4 * L.nchunks);
+  L.sorted_route = o; o = a256(o + 4 * R);
+  L.route_to_row = o; o = a256(o + 4 * R);
+  L.total = o;
+
+  ScratchLayout& S = p->sl;
+  o = 0;
+  S.x_rows = o; o = a256(o + R * D * es);
+  S.h1 = o; o = a256(o + R * 2 * F * es);
+  S.h2 = o; o = a256(o + R * F * es);
+  if (d.training) {
+    S.dh3 = o; o = a256(o + R * D * es);
+    S.dh1 = o; o = a256(o + R * 2 * F * es);
+    S.dxr = o; o = a256(o + R * D * 4);
+  } else {
+    S.dh3 = S.dh1 = S.dxr = -1;
+  }
+  S.total = std::max<int64_t>(o, 256);
+
+  p->h3_bytes = std::max<int64_t>(a256(R * D * es), 256);
+  p->state_max = align128(R * D * es) + align128(R * 2 * F * es);
+  p->budget = d.arena_budget > 0 ? d.arena_budget : int64_t(d.max_layers) * p->state_max;
+  p->arena_bytes = d.training ? kArenaHdrBytes + a256(p->budget) : kArenaHdrBytes;
+  p->cus = 0;
+  *out = p;
+  return MOE_OK;
+}
+
+moe_status moe_plan_sizes(moe_plan_t p, moe_sizes* s) {
+  if (!p || !s) return MOE_ERR_ARG;
+  std::memset(s, 0, sizeof(*s));
+  s->route_ws = size_t(p->rl.total);
+  s->scratch = size_t(p->sl.total);
+  s->h3_slots = size_t(p->h3_bytes);
+  s->arena = size_t(p->arena_bytes);
+  s->layer_state_max = size_t(p->state_max);
+  return MOE_OK;
+}
+
+moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
+  if (!p || !buf || cap == 0) return MOE_ERR_ARG;
+  const moe_desc& d = p->d;
+  const char* prec = d.prec == MOE_PREC_F32 ? "f32" : d.prec == MOE_PREC_BF16 ? "bf16" : "mxfp8";
+  auto mib = [](int64_t b) { return double(b) / (1024.0 * 1024.0); };
+  std::string s;
+  char line[256];
+  std::snprintf(line, sizeof line,
+                "moe plan: T_max=%lld D=%d F=%d E=%d K=%d prec=%s dW=%s training=%d layers=%d\n",
+                (long long)d.t_max, d.d, d.f, d.e, d.k, prec,
+                d.dw_dtype == MOE_DTYPE_F32 ? "f32" : "bf16", d.training, d.max_layers);
+  s += line;
+  std::snprintf(line, sizeof line, "  routed rows R <= %lld, m-tiles <= %lld (%d rows each)\n",
+                (long long)p->R_max, (long long)p->mt_max, kBM);
+  s += line;
+  std::snprintf(line, sizeof line, "  route_ws   %10.2f MiB per layer (metadata + planner record)\n",
+                mib(p->rl.total));
+  s += line;
+  std::snprintf(line, sizeof line, "  h3_slots   %10.2f MiB per layer [T*K, D]\n", mib(p->h3_bytes));
+  s += line;
+  std::snprintf(line, sizeof line,
+                "  scratch    %10.2f MiB shared: x_rows %.2f, h1 %.2f, h2 %.2f",
+                mib(p->sl.total), mib(p->sl.h1 - p->sl.x_rows), mib(p->sl.h2 - p->sl.h1),
+                mib((d.training ? p->sl.dh3 : p->sl.total) - p->sl.h2));
+  s += line;
+  if (d.training) {
+    std::snprintf(line, sizeof line, ", dh3 %.2f, dh1 %.2f, dxr %.2f",
+                  mib(p->sl.dh1 - p->sl.dh3), mib(p->sl.dxr - p->sl.dh1),
+                  mib(p->sl.total - p->sl.dxr));
+    s += line;
+  }
+  s += "\n";
+  std::snprintf(line, sizeof line,
+                "  arena      %10.2f MiB: budget %.2f MiB, full layer state %.2f MiB at R_max "
+                "(x_rows + h1, 128-B aligned)\n",
+                mib(p->arena_bytes), mib(p->budget), mib(p->state_max));
+  s += line;
+  std::snprintf(line, sizeof line,
+                "  planner: a layer replays iff cursor + full_state > budget (device decision "
+                "on the realized R)\n");
+  s += line;
+  std::strncpy(buf, s.c_str(), cap - 1);
+  buf[cap - 1] = '\0';
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan_t p) {
+  if (!p) return;
+  for (auto& sl : p->slots)
+    for (auto& ev : sl.pending) {
+      hipEventSynchronize(ev.second);
+      hipEventDestroy(ev.first);
+      hipEventDestroy(ev.second);
+    }
+  for (hipEvent_t e : p->pool) hipEventDestroy(e);
+  delete p;
+}
+
+moe_status moe_prepare_weights(moe_plan_t p, const void*, const void*, void*, void*, void*,
+                               void*, hipStream_t) {
+  if (!p) return MOE_ERR_ARG;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+moe_status moe_route(moe_plan_t p, int64_t T, const int32_t* ids, void* ws, hipStream_t s) {
+  if (!p || !ws || T < 0 || T > p->d.t_max || (T > 0 && !ids)) return MOE_ERR_ARG;
+  if (!aligned16(ws)) return MOE_ERR_ARG;
+  return hip_status(timed(p, "route", s, [&] {
+    return launch_route(ids, T, p->d.k, p->d.e, reinterpret_cast<char*>(ws), p->rl, s);
+  }));
+}
+
+moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
+                          const moe_weights* w, void* h3, void* arena, void* scratch,
+                          hipStream_t s) {
+  if (!p || !ws || !w || !w->w13 || !w->w2 || !h3 || !scratch) return MOE_ERR_ARG;
+  if (layer < 0 || layer >= p->d.max_layers) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(w->w13) || !aligned16(w->w2) ||
+      !aligned16(h3) || !aligned16(scratch) || !aligned16(ws))
+    return MOE_ERR_ARG;
+  if (p->d.training && arena && !aligned16(arena)) return MOE_ERR_ARG;
+  const moe_desc& d = p->d;
+  RouteHdr* hdr = hdr_of(ws);
+  char* sc = reinterpret_cast<char*>(scratch);
+  PlanArgs pa{layer, d.max_layers, d.training, p->es, d.d, d.f, p->budget,
+              uint64_t(d.training ? arena : nullptr), uint64_t(sc + p->sl.x_rows),
+              uint64_t(sc + p->sl.h1)};
+  hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
+  e = timed(p, "gather", s,
+            [&] { return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, p->R_max, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int cus = plan_cus(p);
+  FwdArgs a13{hdr, at<int32_t>(ws, p->rl.offsets), at<int32_t>(ws, p->rl.mtoff), sorted_route,
+              nullptr, w->w13, nullptr, sc + p->sl.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e};
+  e = timed(p, "w13_swiglu", s,
+            [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  FwdArgs a2{hdr, at<int32_t>(ws, p->rl.offsets), at<int32_t>(ws, p->rl.mtoff), sorted_route,
+             sc + p->sl.h2, w->w2, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e};
+  return hip_status(timed(p, "w2_scatter", s,
+                          [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
+}
+
+moe_status moe_combine(moe_plan_t p, void* ws, const float* scores, const void* h3,
+                       const void* y_addend, void* y, hipStream_t s) {
+  if (!p || !ws || !h3) return MOE_ERR_ARG;
+  if (!aligned16(h3) || !aligned16(y) || !aligned16(y_addend))
+    return MOE_ERR_ARG;
+  RouteHdr* hdr = hdr_of(ws);
+  return hip_status(timed(p, "combine", s, [&] {
+    return launch_combine(p->d.prec, hdr, at<int32_t>(ws, p->rl.route_to_row), scores, h3,
+                          y_addend, y, p->d.k, p->d.d, p->d.t_max, &hdr->status, s);
+  }));
+}
+
+moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
+                          const float* scores, const void* dy, const moe_weights* w,
+                          const void* h3, void* arena, void* scratch, const moe_grads* g,
+                          uint32_t flags, hipStream_t s) {
+  if (!p || !ws || !w || !g || !scratch) return MOE_ERR_ARG;
+  if (!p->d.training) return MOE_ERR_UNSUPPORTED;
+  (void)layer; (void)x; (void)scores; (void)dy; (void)h3; (void)arena; (void)flags; (void)s;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+moe_status moe_read_status(void* ws, uint32_t* status, int32_t* replayed, hipStream_t s) {
+  if (!ws || !status) return MOE_ERR_ARG;
+  RouteHdr h;
+  if (hipMemcpyAsync(&h, ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MOE_ERR_HIP;
+  *status = h.status;
+  if (replayed) *replayed = h.rec.replay;
+  return MOE_OK;
+}
+
+moe_status moe_arena_reset(moe_plan_t p, void* arena, hipStream_t s) {
+  if (!p || !arena) return MOE_ERR_ARG;
+  return hip_status(launch_arena_reset(arena, s));
+}
+
+moe_status moe_route_readback(moe_plan_t p, void* ws, int32_t* counts, int32_t* offsets,
+                              int32_t* poffsets, int32_t* sorted_route, int32_t* route_to_row,
+                              int32_t* R_out, hipStream_t s) {
+  if (!p || !ws) return MOE_ERR_ARG;
+  RouteHdr h;
+  if (hipMemcpyAsync(&h, ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MOE_ERR_HIP;
+  const int64_t E = p->d.e;
+  struct Item { void* dst; int64_t off; int64_t n; } items[] = {
+      {counts, p->rl.counts, E},
+      {offsets, p->rl.offsets, E + 1},
+      {poffsets, p->rl.poffsets, E + 1},
+      {sorted_route, p->rl.sorted_route, h.R},
+      {route_to_row, p->rl.route_to_row, int64_t(h.T) * p->d.k},
+  };
+  for (auto& it : items) {
+    if (!it.dst || it.n <= 0) continue;
+    if (hipMemcpyAsync(it.dst, at<char>(ws, it.off), size_t(it.n) * 4, hipMemcpyDeviceToHost, s) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  if (R_out) *R_out = h.R;
+  return MOE_OK;
+}
+
+moe_status moe_saved_ptrs(moe_plan_t p, void* ws, void** x_rows, void** h1, hipStream_t s) {
+  if (!p || !ws) return MOE_ERR_ARG;
+  RouteHdr h;
+  if (hipMemcpyAsync(&h, ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (x_rows) *x_rows = reinterpret_cast<void*>(h.rec.x_rows);
+  if (h1) *h1 = reinterpret_cast<void*>(h.rec.h1);
+  return MOE_OK;
+}
+
+moe_status moe_timing_enable(moe_plan_t p, int32_t enable) {
+  if (!p) return MOE_ERR_ARG;
+  if (!enable) {
+    for (auto& sl : p->slots)
+      for (auto& ev : sl.pending) {
+        hipEventSynchronize(ev.second);
+        p->pool.push_back(ev.first);
+        p->pool.push_back(ev.second);
+      }
+    p->slots.clear();
+  }
+  p->timing = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_timing_read(moe_plan_t p, int32_t idx, char* name, size_t cap, double* total_ms,
+                           int64_t* launches) {
+  if (!p || idx < 0) return MOE_ERR_ARG;
+  for (auto& sl : p->slots) {
+    for (auto& ev : sl.pending) {
+      float ms = 0.f;
+      if (hipEventSynchronize(ev.second) != hipSuccess ||
+          hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess)
+        return MOE_ERR_HIP;
+      sl.total_ms += ms;
+      sl.launches += 1;
+      p->pool.push_back(ev.first);
+      p->pool.push_back(ev.second);
+    }
+    sl.pending.clear();
+  }
+  if (size_t(idx) >= p->slots.size()) return MOE_ERR_ARG;
+  const auto& sl = p->slots[size_t(idx)];
+  if (name && cap) {
+    std::strncpy(name, sl.name.c_str(), cap - 1);
+    name[cap - 1] = '\0';
+  }
+  if (total_ms) *total_ms = sl.total_ms;
+  if (launches) *launches = sl.launches;
+  return MOE_OK;
+}
+
+}  // extern "C"

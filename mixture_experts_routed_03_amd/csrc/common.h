@@ -1,0 +1,140 @@
+// Internal layouts and device helpers shared by the gfx950 kernels and the
+// host entry points of libmoe.  Nothing here is part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- constants
+constexpr int kBM = 64;           // token rows per grouped-GEMM m-tile
+constexpr int kRankChunk = 256;   // routes per counting-sort chunk
+constexpr int kMxBlock = 32;      // MX block length (values per E8M0 scale)
+constexpr int kMaxE = 4096;
+constexpr int kMaxK = 16;
+
+__host__ __device__ inline int64_t align_up(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
+__host__ __device__ inline int64_t align128(int64_t n) { return align_up(n, 128); }
+
+// ------------------------------------------------- per-layer planner record
+// Written on the device by the planner kernel during forward, read by every
+// later kernel of that layer (forward and backward).  Pointers are device
+// addresses resolved from the arena cursor or the scratch buffer.
+struct LayerRec {
+  int64_t start;        // arena byte offset of this layer's saved state
+  int64_t bytes;        // bytes this layer keeps in the arena
+  int32_t replay;       // 1: state lives in scratch; backward rebuilds it
+  int32_t layer;
+  int32_t done;         // forward ran
+  int32_t pad0;
+  uint64_t x_rows;      // gathered x rows [R, D] (act dtype)
+  uint64_t h1;          // h1 [R, 2F] (act dtype)
+  uint64_t aux[6];      // MXFP8 bundles
+};
+
+// Header at the start of a route workspace.
+struct RouteHdr {
+  int32_t T;            // tokens of the call
+  int32_t R;            // valid routes = packed rows
+  int32_t Rpad;         // sum over experts of counts rounded up to 32
+  int32_t n_mt;         // m-tiles of kBM rows over all experts
+  uint32_t status;      // MOE_STATUS_* bits
+  int32_t max_count;    // largest expert row count
+  int32_t pad[10];
+  LayerRec rec;
+};
+static_assert(sizeof(RouteHdr) <= 512, "route header must fit its slot");
+
+struct ArenaHdr {
+  int64_t cursor;       // next free byte of the data region
+  int64_t pad[31];
+};
+constexpr int64_t kArenaHdrBytes = 4096;  // data region starts here
+
+// Byte offsets inside a route workspace (host computed from the plan).
+struct RouteLayout {
+  int64_t hdr, counts, offsets, poffsets, mtoff, chunk_hist, chunk_flags,
+      sorted_route, route_to_row, total;
+  int64_t nchunks;
+};
+
+// Byte offsets inside the scratch buffer (regions sized for R = t_max*K).
+struct ScratchLayout {
+  int64_t x_rows, h1, h2, dh3, dh1, dxr, total;
+};
+
+// Arguments of the grouped forward GEMM launches.
+struct FwdArgs {
+  const RouteHdr* hdr;
+  const int32_t* offsets;
+  const int32_t* mtoff;
+  const int32_t* sorted_route;
+  const void* A;    // token rows [R, Kd]; null = the layer record's x_rows
+  const void* W;    // [E, N, Kd]
+  void* out0;       // W13: h1 [R, 2F] (null = record); W2: h3 slots [T*K, D]
+  void* out1;       // W13: h2 [R, F]
+  int Kd;           // contraction length (D for W13, F for W2)
+  int N;            // weight rows per expert (2F or D)
+  int F;
+  int NT;           // n-tiles per expert
+  int E;
+};
+
+// Arguments of the device planner (one layer).
+struct PlanArgs {
+  int32_t layer, max_layers, training, es, D, F;
+  int64_t budget;
+  uint64_t arena;           // device base of the arena (0 when none)
+  uint64_t scratch_x_rows;  // scratch regions used when state is not saved
+  uint64_t scratch_h1;
+};
+
+// ------------------------------------------------------------ device utils
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(uint32_t(h) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// SiLU(z) = z / (1 + e^-z); one definition for forward and backward replays.
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Storage element traits: float (F32 plans) or bf16 bits (BF16 / MXFP8 plans).
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+  static __device__ __forceinline__ float round(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float to_f(uint16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ uint16_t from_f(float v) { return f32_to_bf16(v); }
+  static __device__ __forceinline__ float round(float v) { return round_bf16(v); }
+};
+
+// Number of XCDs of the MI355X; workgroups are dispatched round-robin over them.
+constexpr int kXcds = 8;
+
+}  // namespace moe

@@ -1,0 +1,324 @@
+// Grouped forward GEMMs of the expert FFN on gfx950 MFMA.
+//
+//   W13 pass:  h1 = A_e W13_e^T per expert (A_e = the expert's gathered rows),
+//              epilogue stores h1 = [g | u] and h2 = SiLU(g) * u.
+//   W2 pass:   h3 = H2_e W2_e^T, epilogue stores each row into its route slot
+//              sorted_route[row] of h3_slots [T*K, D].
+//
+// Sources: Dist-MoE explainer section 02 (h1 = W13 x = [g; u],
+// h2 = SiLU(g) * u, h3 = W2 h2) and section 05 (a persistent scheduler hands
+// (expert, row tile, output tile) work to workgroups, one launch covers all
+// local experts, tails are masked; the W2 epilogue writes each result to its
+// return slot).  "Mixture of Experts: How Routing Becomes GPU Computation",
+// section 2 (grouped GEMM over variable M_e with B stored [E, N, K]), section
+// 1 (at small M_e the GEMM is bound by reading the weights) and section 6
+// (column-major tile order so row tiles that share a weight block run next
+// to each other).
+//
+// MI355X design
+//  * Weights are streamed from HBM straight into MFMA operand registers: a
+//    weight row is K-contiguous, so lane (row r, half h) loads its 8-value
+//    operand as one 16-byte load; within a BK stage half h owns the
+//    contiguous half [h*BK/2, (h+1)*BK/2) of the row (the contraction order
+//    inside a stage is a permutation applied identically to both operands).
+//  * The token tile (<= 64 rows x BK) is shared by the 4 waves through a
+//    double-buffered LDS tile.
+//  * Workgroup tile: 128 weight rows (4 waves x 32) x 64 token rows; each
+//    wave holds two 32x32 fp32 accumulators (v_mfma_f32_32x32x16_bf16, or
+//    v_mfma_f32_32x32x2f32 for fp32 operands).  A tile whose expert has <= 32
+//    rows left skips the second accumulator.
+//  * Persistent grid, XCD-aware: work item w is run by a workgroup of XCD
+//    (w / chunk), so one XCD's L2 holds an expert's token rows while its
+//    n-tiles stream by; items are expert-major, then n-tile, then m-tile, so
+//    m-tiles sharing a weight tile are adjacent.
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Mma;
+template <>
+struct Mma<uint16_t> {
+  static constexpr int kV = 1;  // u32x4 per 8-value operand
+  static __device__ __forceinline__ void step(f32x16& acc, const u32x4* a, const u32x4* b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                                  __builtin_bit_cast(bf16x8, b[0]), acc, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<float> {
+  static constexpr int kV = 2;
+  static __device__ __forceinline__ void step(f32x16& acc, const u32x4* a, const u32x4* b) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[p >> 2][p & 3]),
+                                                 __uint_as_float(b[p >> 2][p & 3]), acc, 0, 0, 0);
+  }
+};
+
+// Stores 4 consecutive values of the accumulator as T.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c,
+                                                 float d) {
+  u32x2 v;
+  v[0] = pack_bf16x2(a, b);
+  v[1] = pack_bf16x2(c, d);
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+template <typename T, int BK>
+struct FwdTile {
+  static constexpr int ES = sizeof(T);
+  static constexpr int kRowBytes = BK * ES;                    // one token row of a stage
+  static constexpr int kLdsStride = kRowBytes + 16;             // padded LDS row
+  static constexpr int kBuf = kBM * kLdsStride;                 // one LDS stage buffer
+  static constexpr int kWChunks = BK * ES / 2 / 16;             // u32x4 per lane per stage
+  static constexpr int kAChunks = kBM * kRowBytes / 16 / 256;   // u32x4 per thread per stage
+  static constexpr int kSteps = BK / 16;                        // MFMA k-steps per stage
+};
+
+// Finds the expert of work item w: the largest e with mtoff[e]*NT <= w.
+__device__ __forceinline__ int find_expert(const int32_t* __restrict__ mtoff, int E, int NT,
+                                           int w) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (mtoff[mid] * NT <= w)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+template <typename T, int MODE, int BK>
+__global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
+  using Tl = FwdTile<T, BK>;
+  __shared__ __attribute__((aligned(16))) char lds[2 * Tl::kBuf];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;   // row inside the 32-row operand block
+  const int lh = lane >> 5;   // operand half
+
+  const RouteHdr* hdr = a.hdr;
+  const int n_items = hdr->n_mt * a.NT;
+  const char* Abase = reinterpret_cast<const char*>(a.A ? a.A : (const void*)hdr->rec.x_rows);
+  T* out0 = reinterpret_cast<T*>(a.out0 ? a.out0 : (void*)hdr->rec.h1);
+  T* out1 = reinterpret_cast<T*>(a.out1);
+  const int64_t a_row_bytes = int64_t(a.Kd) * Tl::ES;
+
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per = gridDim.x / kXcds;
+  const int chunk = (n_items + kXcds - 1) / kXcds;
+  const int S = a.Kd / BK;
+
+  for (int it = slot; it < chunk; it += per) {
+    const int w = xcd * chunk + it;
+    if (w >= n_items) break;
+    const int e = find_expert(a.mtoff, a.E, a.NT, w);
+    const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
+    const int u = w - a.mtoff[e] * a.NT;
+    const int nt = u / mt_e;
+    const int mt = u - nt * mt_e;
+    const int row0 = a.offsets[e] + mt * kBM;
+    const int rows = min(kBM, a.offsets[e + 1] - row0);
+    const bool two = rows > 32;
+
+    // Weight row of this lane.
+    int nrow;
+    if (MODE == 0)
+      nrow = (wave < 2 ? 0 : a.F) + nt * 64 + (wave & 1) * 32 + lr;
+    else
+      nrow = nt * 128 + wave * 32 + lr;
+    const char* wp = reinterpret_cast<const char*>(a.W) +
+                     (int64_t(e) * a.N + nrow) * a_row_bytes + lh * (BK / 2) * Tl::ES;
+
+    // Token-tile chunk owned by this thread for the global->LDS copy.
+    constexpr int kCPR = Tl::kRowBytes / 16;  // 16-byte chunks per token row
+    const char* ap[Tl::kAChunks];
+    int lds_off[Tl::kAChunks];
+#pragma unroll
+    for (int j = 0; j < Tl::kAChunks; ++j) {
+      const int i = tid + 256 * j;
+      const int r = i / kCPR, c = i % kCPR;
+      ap[j] = r < rows ? Abase + int64_t(row0 + r) * a_row_bytes + c * 16 : nullptr;
+      lds_off[j] = r * Tl::kLdsStride + c * 16;
+    }
+
+    f32x16 acc0 = {}, acc1 = {};
+    u32x4 wa[Tl::kWChunks], wb[Tl::kWChunks], at[Tl::kAChunks];
+
+    auto load_w = [&](u32x4* dst, int s) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(wp + int64_t(s) * Tl::kRowBytes);
+#pragma unroll
+      for (int j = 0; j < Tl::kWChunks; ++j) dst[j] = p[j];
+    };
+    auto load_a = [&](int s) {
+#pragma unroll
+      for (int j = 0; j < Tl::kAChunks; ++j)
+        at[j] = ap[j] ? *reinterpret_cast<const u32x4*>(ap[j] + int64_t(s) * Tl::kRowBytes)
+                      : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < Tl::kAChunks; ++j)
+        *reinterpret_cast<u32x4*>(lds + buf * Tl::kBuf + lds_off[j]) = at[j];
+    };
+    auto compute = [&](const u32x4* wr, int buf) {
+      const char* base = lds + buf * Tl::kBuf + lh * (BK / 2) * Tl::ES;
+#pragma unroll
+      for (int q = 0; q < Tl::kSteps; ++q) {
+        u32x4 b[Mma<T>::kV];
+        const char* p0 = base + lr * Tl::kLdsStride + q * 8 * Tl::ES;
+#pragma unroll
+        for (int v = 0; v < Mma<T>::kV; ++v) b[v] = *reinterpret_cast<const u32x4*>(p0 + 16 * v);
+        Mma<T>::step(acc0, wr + q * Mma<T>::kV, b);
+        if (two) {
+          const char* p1 = p0 + 32 * Tl::kLdsStride;
+#pragma unroll
+          for (int v = 0; v < Mma<T>::kV; ++v)
+            b[v] = *reinterpret_cast<const u32x4*>(p1 + 16 * v);
+          Mma<T>::step(acc1, wr + q * Mma<T>::kV, b);
+        }
+      }
+    };
+
+    // Software pipeline: stage s+1 loads are in flight while stage s computes.
+    load_w(wa, 0);
+    load_a(0);
+    store_a(0);
+    __syncthreads();
+    for (int s = 0; s < S; s += 2) {
+      if (s + 1 < S) {
+        load_w(wb, s + 1);
+        load_a(s + 1);
+      }
+      compute(wa, 0);
+      if (s + 1 < S) store_a(1);
+      __syncthreads();
+      if (s + 1 >= S) break;
+      if (s + 2 < S) {
+        load_w(wa, s + 2);
+        load_a(s + 2);
+      }
+      compute(wb, 1);
+      if (s + 2 < S) store_a(0);
+      __syncthreads();
+    }
+
+    // ---------------------------------------------------------- epilogue
+    // acc[b][v] is C[weight row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
+    if (MODE == 0) {
+      const int F = a.F;
+      const int ncol = (wave < 2 ? 0 : F) + nt * 64 + (wave & 1) * 32 + 4 * lh;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const f32x16& acc = b ? acc1 : acc0;
+        const int m = 32 * b + lr;
+        if (m < rows) {
+          T* o = out0 + int64_t(row0 + m) * (2 * F) + ncol;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store4<T>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+      }
+      // SwiGLU: up waves (2,3) hand their rounded values to gate waves (0,1).
+      float* xch = reinterpret_cast<float*>(lds);
+      if (wave >= 2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          xch[(((wave - 2) * 2 + 0) * 16 + v) * 64 + lane] = Elem<T>::round(acc0[v]);
+          xch[(((wave - 2) * 2 + 1) * 16 + v) * 64 + lane] = Elem<T>::round(acc1[v]);
+        }
+      }
+      __syncthreads();
+      if (wave < 2) {
+        const int jcol = nt * 64 + wave * 32 + 4 * lh;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const f32x16& acc = b ? acc1 : acc0;
+          const int m = 32 * b + lr;
+          if (m < rows) {
+            float h[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float g = Elem<T>::round(acc[v]);
+              const float up = xch[((wave * 2 + b) * 16 + v) * 64 + lane];
+              h[v] = silu_f(g) * up;
+            }
+            T* o = out1 + int64_t(row0 + m) * F + jcol;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              store4<T>(o + 8 * g, h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
+          }
+        }
+      }
+      __syncthreads();
+    } else {
+      const int ncol = nt * 128 + wave * 32 + 4 * lh;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const f32x16& acc = b ? acc1 : acc0;
+        const int m = 32 * b + lr;
+        if (m < rows) {
+          const int64_t slotr = a.sorted_route[row0 + m];
+          T* o = out0 + slotr * a.N + ncol;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store4<T>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
+// Persistent grid size: a multiple of the XCD count, at most the upper bound
+// on work items.
+static unsigned fwd_grid(int64_t items_max, int cus, int per_cu) {
+  int64_t g = std::min<int64_t>(items_max, int64_t(cus) * per_cu);
+  g = (g + kXcds - 1) / kXcds * kXcds;
+  return unsigned(std::max<int64_t>(g, kXcds));
+}
+
+template <typename T, int MODE>
+static hipError_t launch_fwd_t(const FwdArgs& a, int64_t mt_max, int cus, hipStream_t s) {
+  constexpr int BK = sizeof(T) == 2 ? 64 : 32;
+  static int per_cu = 0;  // resident workgroups per CU (same on every gfx950 device)
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_fwd<T, MODE, BK>, 256, 0) !=
+            hipSuccess ||
+        n <= 0)
+      n = 1;
+    per_cu = n;
+  }
+  const unsigned g = fwd_grid(mt_max * a.NT, cus, per_cu);
+  hipLaunchKernelGGL((k_gemm_fwd<T, MODE, BK>), dim3(g), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// mode 0: W13 + SwiGLU (out0 = h1 or null, out1 = h2); mode 1: W2 -> slots.
+hipError_t launch_gemm_fwd(int prec, int mode, const FwdArgs& a, int64_t mt_max, int cus,
+                           hipStream_t s) {
+  if (mt_max == 0) return hipSuccess;
+  if (prec == MOE_PREC_F32)
+    return mode == 0 ? launch_fwd_t<float, 0>(a, mt_max, cus, s)
+                     : launch_fwd_t<float, 1>(a, mt_max, cus, s);
+  return mode == 0 ? launch_fwd_t<uint16_t, 0>(a, mt_max, cus, s)
+                   : launch_fwd_t<uint16_t, 1>(a, mt_max, cus, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,75 @@
+"""Helpers shared by the GPU parity tests: run the library through its C ABI
+and compute the oracle's answer on the same (seeded) inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from mixture_experts_routed_03_amd import workloads as wl
+from oracle import moe as om
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp8": 6e-2}
+
+
+def banner(msg: str):
+    print(f"[case] {msg}", flush=True)
+
+
+def make_inputs(T, D, F, E, K, prec="bf16", zipf=None, n_pad=0, seed=0, device="cuda",
+                training=False):
+    cfg = wl.Config("adhoc", T, D, F, E, K, prec, zipf=(zipf,), seed=seed, training=training)
+    lay = wl.make_layer(cfg, 0, device=device)
+    if n_pad:
+        ids, scores = wl.make_routing(T, E, K, zipf_s=zipf, n_pad=n_pad, seed=seed)
+        lay["ids"] = torch.from_numpy(ids).to(device)
+        lay["scores"] = torch.from_numpy(scores).to(device)
+    return lay
+
+
+def run_forward(layer, lay, y_addend=None):
+    """route -> expert_fwd -> combine on the current stream; returns y."""
+    T = lay["x"].shape[0]
+    y = torch.empty((T, layer.D), dtype=layer.act_dtype, device=layer.device)
+    layer.route(lay["ids"])
+    layer.forward(lay["x"], lay["w13"], lay["w2"])
+    layer.combine(lay["scores"], y, y_addend=y_addend)
+    return y
+
+
+def oracle_forward(lay, keep=False):
+    return om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                      keep=keep)
+
+
+def check_route(got: dict, ids, E):
+    ref = om.route(ids, E)
+    assert got["R"] == ref["R"]
+    np.testing.assert_array_equal(got["counts"], ref["counts"])
+    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(got["poffsets"], ref["poffsets"])
+    np.testing.assert_array_equal(got["sorted_route"], ref["sorted_route"])
+    np.testing.assert_array_equal(got["route_to_row"], ref["route_to_row"])
+    return ref
+
+
+def sampled_forward_ref(lay, tokens):
+    """Oracle Y for selected tokens only, one expert's weights at a time."""
+    ids = lay["ids"].cpu().numpy()
+    s = lay["scores"].cpu().numpy().astype(np.float64)
+    X = lay["x"]
+    E = lay["w13"].shape[0]
+    out = {t: np.zeros(X.shape[1]) for t in tokens}
+    by_e = {}
+    for t in tokens:
+        for k in range(ids.shape[1]):
+            e = int(ids[t, k])
+            if 0 <= e < E:
+                by_e.setdefault(e, []).append((t, k))
+    for e, lst in sorted(by_e.items()):
+        w13 = om.as_f64(lay["w13"][e])
+        w2 = om.as_f64(lay["w2"][e])
+        xr = om.as_f64(X[[t for t, _ in lst]])
+        _, _, h3 = om.expert_ffn(xr, w13, w2)
+        for i, (t, k) in enumerate(lst):
+            out[t] += s[t, k] * h3[i]
+    return np.stack([out[t] for t in tokens])
