@@ -23,7 +23,8 @@ hipError_t launch_plan_decide(RouteHdr* hdr, const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_rewind(RouteHdr* hdr, void* arena, hipStream_t s);
 hipError_t launch_arena_reset(void* arena, hipStream_t s);
 hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
-                         const int32_t* sorted_route, int64_t R_max, hipStream_t s);
+                         const int32_t* sorted_route, int64_t R_max, int replay_only,
+                         hipStream_t s);
 hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
                           const float* scores, const void* h3, const void* addend, void* y,
                           int K, int64_t D, int64_t T_max, uint32_t* status, hipStream_t s);
@@ -35,10 +36,8 @@ hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_
                             int accumulate, hipStream_t s);
 hipError_t launch_gemm_fwd(int prec, int mode, const FwdArgs& a, int64_t mt_max, int cus,
                            hipStream_t s);
-hipError_t launch_backward(int prec, int dw_f32, const RouteHdr* hdr, const int32_t* offsets,
-                           const int32_t* mtoff, const void* dh3, const void* w13, const void* w2,
-                           void* dh1, float* dxr, void* dw13, void* dw2, int D, int F, int E,
-                           int64_t mt_max, int cus, hipStream_t s);
+hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hipStream_t s);
+hipError_t launch_wgrad(int kind, int dw_f32, const BwdArgs& a, int cus, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -290,16 +289,16 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   e = timed(p, "gather", s,
-            [&] { return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, p->R_max, s); });
+            [&] { return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, p->R_max, 0, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int cus = plan_cus(p);
   FwdArgs a13{hdr, at<int32_t>(ws, p->rl.offsets), at<int32_t>(ws, p->rl.mtoff), sorted_route,
-              nullptr, w->w13, nullptr, sc + p->sl.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e};
+              nullptr, w->w13, nullptr, sc + p->sl.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e, 0};
   e = timed(p, "w13_swiglu", s,
             [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   FwdArgs a2{hdr, at<int32_t>(ws, p->rl.offsets), at<int32_t>(ws, p->rl.mtoff), sorted_route,
-             sc + p->sl.h2, w->w2, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e};
+             sc + p->sl.h2, w->w2, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0};
   return hip_status(timed(p, "w2_scatter", s,
                           [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
 }
@@ -320,10 +319,66 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
                           const float* scores, const void* dy, const moe_weights* w,
                           const void* h3, void* arena, void* scratch, const moe_grads* g,
                           uint32_t flags, hipStream_t s) {
-  if (!p || !ws || !w || !g || !scratch) return MOE_ERR_ARG;
-  if (!p->d.training) return MOE_ERR_UNSUPPORTED;
-  (void)layer; (void)x; (void)scores; (void)dy; (void)h3; (void)arena; (void)flags; (void)s;
-  return MOE_ERR_UNSUPPORTED;
+  if (!p || !ws || !w || !g || !scratch || !h3) return MOE_ERR_ARG;
+  const moe_desc& d = p->d;
+  if (!d.training || d.prec != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
+  if (layer < 0 || layer >= d.max_layers) return MOE_ERR_ARG;
+  if (!w->w13 || !w->w2 || !g->dw13 || !g->dw2) return MOE_ERR_ARG;
+  if (!aligned16(ws) || !aligned16(x) || !aligned16(dy) || !aligned16(w->w13) ||
+      !aligned16(w->w2) || !aligned16(h3) || !aligned16(scratch) || !aligned16(g->dx) ||
+      !aligned16(g->dw13) || !aligned16(g->dw2) || !aligned16(arena))
+    return MOE_ERR_ARG;
+  RouteHdr* hdr = hdr_of(ws);
+  char* sc = reinterpret_cast<char*>(scratch);
+  const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
+  const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
+  const int32_t* route_to_row = at<int32_t>(ws, p->rl.route_to_row);
+  const int cus = plan_cus(p);
+  void* dh3 = sc + p->sl.dh3;
+  void* dh1 = sc + p->sl.dh1;
+  float* dxr = reinterpret_cast<float*>(sc + p->sl.dxr);
+  const int dw_f32 = d.dw_dtype == MOE_DTYPE_F32;
+  hipError_t e;
+  // Replay (device predicate): rebuild gathered x and h1 in scratch when the
+  // forward did not save them.
+  e = timed(p, "replay_gather", s, [&] {
+    return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, p->R_max, 1, s);
+  });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
+              d.d, 2 * d.f, d.f, d.f / 64, d.e, 1};
+  e = timed(p, "replay_w13", s, [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = timed(p, "combine_bwd", s, [&] {
+    return launch_combine_bwd(d.prec, hdr, route_to_row, scores, dy, h3, dh3, g->dscores, d.k,
+                              d.d, d.t_max, s);
+  });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  BwdArgs b{hdr, offsets, mtoff, w->w2, dh3, nullptr, dh1, d.d, d.f, d.f, d.d, d.e, d.f / 128,
+            0, 0};
+  e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_dgrad(0, b, p->mt_max, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  BwdArgs bw2{hdr, offsets, mtoff, nullptr, nullptr, dh3, g->dw2, 0, 0, d.f, d.d, d.e, 0,
+              d.f / 128, d.d / 128};
+  e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(2, dw_f32, bw2, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  BwdArgs b13{hdr, offsets, mtoff, w->w13, dh1, nullptr, dxr, 2 * d.f, d.d, d.f, d.d, d.e,
+              d.d / 128, 0, 0};
+  e = timed(p, "w13_dgrad", s, [&] { return launch_dgrad(1, b13, p->mt_max, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  BwdArgs bw13{hdr, offsets, mtoff, nullptr, nullptr, dh1, g->dw13, 0, 0, d.f, d.d, d.e, 0,
+               d.d / 128, 2 * d.f / 128};
+  e = timed(p, "w13_wgrad", s, [&] { return launch_wgrad(3, dw_f32, bw13, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = timed(p, "dx_reduce", s, [&] {
+    return launch_dx_reduce(d.prec, hdr, route_to_row, dxr, g->dx, d.k, d.d, d.t_max,
+                            (flags & MOE_BWD_ACCUMULATE_DX) ? 1 : 0, s);
+  });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(timed(p, "rewind", s, [&] {
+    return launch_plan_rewind(hdr, d.training ? arena : nullptr, s);
+  }));
 }
 
 moe_status moe_read_status(void* ws, uint32_t* status, int32_t* replayed, hipStream_t s) {

@@ -81,6 +81,23 @@ struct FwdArgs {
   int F;
   int NT;           // n-tiles per expert
   int E;
+  int replay_only;  // 1: run only when the layer's forward chose replay
+};
+
+// Arguments of the grouped backward GEMM launches.
+struct BwdArgs {
+  const RouteHdr* hdr;
+  const int32_t* offsets;
+  const int32_t* mtoff;
+  const void* W;        // DGRAD weight [E, Kd, N] (row = contraction index)
+  const void* tok;      // DGRAD token operand rows [R, Kd] (dH3 or dH1)
+  const void* grad;     // WGRAD gradient rows (dH3 [R, D] or dH1 [R, 2F])
+  void* out;            // dH1 [R, 2F] / dXr [R, D] fp32 / dW2 [E, D, F] / dW13 [E, 2F, D]
+  int Kd;               // DGRAD contraction length
+  int N;                // DGRAD output columns
+  int F, D, E;
+  int NT;               // DGRAD n-tiles per expert
+  int NA, NB;           // WGRAD 128-wide tiles along the A and B output axes
 };
 
 // Arguments of the device planner (one layer).

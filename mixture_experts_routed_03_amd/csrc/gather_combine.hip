@@ -61,9 +61,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // layer's planner record (arena or scratch).
 __global__ __launch_bounds__(256) void k_gather(const u32x4* __restrict__ x, int64_t row_chunks,
                                                 int K, const RouteHdr* __restrict__ hdr,
-                                                const int32_t* __restrict__ sorted_route) {
+                                                const int32_t* __restrict__ sorted_route,
+                                                int replay_only) {
   const int lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (replay_only && !hdr->rec.replay) return;
   if (row >= hdr->R) return;
   if (!x) {  // T > 0 needs x: report instead of faulting
     if (row == 0 && lane == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
@@ -141,6 +143,11 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= hdr->T) return;
+  if (!scores || !dy) {
+    if (t == 0 && lane == 0)
+      atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
+    return;
+  }
   constexpr int n = Vec16<T>::n;
   for (int k = 0; k < K; ++k) {
     const int64_t r = t * K + k;
@@ -177,6 +184,11 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= hdr->T) return;
+  if (!dx) {
+    if (t == 0 && lane == 0)
+      atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
+    return;
+  }
   int rows[kMaxK];
 #pragma unroll
   for (int k = 0; k < kMaxK; ++k) rows[k] = k < K ? route_to_row[t * K + k] : -1;
@@ -209,10 +221,12 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ 
 static inline unsigned rows_grid(int64_t rows) { return unsigned((rows + 3) / 4); }
 
 hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
-                         const int32_t* sorted_route, int64_t R_max, hipStream_t s) {
+                         const int32_t* sorted_route, int64_t R_max, int replay_only,
+                         hipStream_t s) {
   if (R_max == 0) return hipSuccess;
   hipLaunchKernelGGL(k_gather, dim3(rows_grid(R_max)), dim3(256), 0, s,
-                     reinterpret_cast<const u32x4*>(x), D * es / 16, K, hdr, sorted_route);
+                     reinterpret_cast<const u32x4*>(x), D * es / 16, K, hdr, sorted_route,
+                     replay_only);
   return hipGetLastError();
 }
 

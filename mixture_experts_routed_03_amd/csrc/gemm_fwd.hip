@@ -113,6 +113,7 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
   const int lh = lane >> 5;   // operand half
 
   const RouteHdr* hdr = a.hdr;
+  if (a.replay_only && !hdr->rec.replay) return;
   const int n_items = hdr->n_mt * a.NT;
   const char* Abase = reinterpret_cast<const char*>(a.A ? a.A : (const void*)hdr->rec.x_rows);
   T* out0 = reinterpret_cast<T*>(a.out0 ? a.out0 : (void*)hdr->rec.h1);

@@ -73,3 +73,62 @@ def sampled_forward_ref(lay, tokens):
         for i, (t, k) in enumerate(lst):
             out[t] += s[t, k] * h3[i]
     return np.stack([out[t] for t in tokens])
+
+
+def run_train(layer, lay, dw_f32=False, dx_init=None, flags=0):
+    """Forward + backward on the current stream; returns y, dx, dw13, dw2, dscores."""
+    T = lay["x"].shape[0]
+    dev = layer.device
+    y = run_forward(layer, lay)
+    dx = (torch.empty((T, layer.D), dtype=layer.act_dtype, device=dev) if dx_init is None
+          else dx_init.clone())
+    dw13 = torch.empty((layer.E, 2 * layer.F, layer.D), dtype=layer.dw_dtype, device=dev)
+    dw2 = torch.empty((layer.E, layer.D, layer.F), dtype=layer.dw_dtype, device=dev)
+    ds = torch.empty((T, layer.K), dtype=torch.float32, device=dev)
+    layer.backward(lay["x"], lay["scores"], lay["dy"], lay["w13"], lay["w2"], dx, dw13, dw2, ds,
+                   flags=flags)
+    return y, dx, dw13, dw2, ds
+
+
+def sampled_backward_ref(lay, tokens, experts):
+    """Oracle dX and dS for selected tokens and dW13/dW2 for selected experts,
+    computed per route from the layer inputs (one expert's weights at a time)."""
+    ids = lay["ids"].cpu().numpy()
+    s = lay["scores"].cpu().numpy().astype(np.float64)
+    X = lay["x"]
+    dY = lay["dy"]
+    E = lay["w13"].shape[0]
+    D = X.shape[1]
+    F = lay["w2"].shape[2]
+    dx = {t: np.zeros(D) for t in tokens}
+    ds = {t: np.zeros(ids.shape[1]) for t in tokens}
+    dw13 = {e: np.zeros((2 * F, D)) for e in experts}
+    dw2 = {e: np.zeros((D, F)) for e in experts}
+    work = {}
+    for t in tokens:
+        for k in range(ids.shape[1]):
+            e = int(ids[t, k])
+            if 0 <= e < E:
+                work.setdefault(e, set()).add((t, k))
+    for e in experts:
+        for t, k in zip(*np.nonzero(ids == e)):
+            work.setdefault(int(e), set()).add((int(t), int(k)))
+    for e, routes in sorted(work.items()):
+        routes = sorted(routes)
+        w13 = om.as_f64(lay["w13"][e])
+        w2 = om.as_f64(lay["w2"][e])
+        ts = [t for t, _ in routes]
+        xr = om.as_f64(X[ts])
+        dyr = om.as_f64(dY[ts])
+        sr = np.array([s[t, k] for t, k in routes])
+        h1, _, h3 = om.expert_ffn(xr, w13, w2)
+        dh3 = sr[:, None] * dyr
+        dxr, dw13e, dw2e, _ = om.expert_ffn_backward(xr, w13, w2, h1, dh3)
+        if e in dw13:
+            dw13[e], dw2[e] = dw13e, dw2e
+        for i, (t, k) in enumerate(routes):
+            if t in dx:
+                dx[t] += dxr[i]
+                ds[t][k] = float(h3[i] @ dyr[i])
+    return (np.stack([dx[t] for t in tokens]), np.stack([ds[t] for t in tokens]),
+            np.stack([dw13[e] for e in experts]), np.stack([dw2[e] for e in experts]))
