@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-experts", type=int, default=24,
                     help="experts in the CPU-oracle sample (all their routes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a reference kernel "
+                         "for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -96,6 +99,15 @@ def main():
     counts = rb["counts"].astype(np.int64)
     R = int(rb["R"])
     nonempty = int((counts > 0).sum())
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads and writes copy_probe_mb MiB each
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- timed region: K steps, bracketed by synchronize on both sides
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

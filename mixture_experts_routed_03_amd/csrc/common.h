@@ -92,12 +92,14 @@ struct BwdArgs {
   const void* W;        // DGRAD weight [E, Kd, N] (row = contraction index)
   const void* tok;      // DGRAD token operand rows [R, Kd] (dH3 or dH1)
   const void* grad;     // WGRAD gradient rows (dH3 [R, D] or dH1 [R, 2F])
+  const void* arows;    // WGRAD A-operand rows (h2 [R, F] or x rows [R, D]; null = record x rows)
   void* out;            // dH1 [R, 2F] / dXr [R, D] fp32 / dW2 [E, D, F] / dW13 [E, 2F, D]
+  void* out2;           // W2 DGRAD: h2 [R, F] rebuilt from h1 for W2 WGRAD
   int Kd;               // DGRAD contraction length
   int N;                // DGRAD output columns
   int F, D, E;
   int NT;               // DGRAD n-tiles per expert
-  int NA, NB;           // WGRAD 128-wide tiles along the A and B output axes
+  int a_ld, b_ld;       // WGRAD row lengths of the A rows (= dW row length) and B rows (= dW rows)
 };
 
 // Arguments of the device planner (one layer).
@@ -118,24 +120,35 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(uint32_t(h) << 16);
 }
 
-// Round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair, round to nearest even (one
+// v_cvt_pk_bf16_f32 on gfx950).  Every bf16 value the library stores goes
+// through this one conversion, so recomputed values match bit for bit.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return uint16_t(pack_bf16x2(f, 0.0f)); }
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
-}
 
 // SiLU(z) = z / (1 + e^-z); one definition for forward and backward replays.
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Workgroup barrier for LDS hand-offs.  The fences cover LDS only, so the
+// barrier waits for this wave's LDS operations but not for its outstanding
+// global loads or stores: prefetched tiles stay in flight across it (a full
+// __syncthreads() drains every outstanding global access on gfx9).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Storage element traits: float (F32 plans) or bf16 bits (BF16 / MXFP8 plans).
 template <typename T> struct Elem;

@@ -11,21 +11,33 @@
 // gives the h1 gradient for W13 DGRAD/WGRAD; weight gradients accumulate in
 // fp32 and are stored BF16 or FP32; experts with no rows get zero gradients.
 //
-//   k_gemm_dgrad<0>: dH2 = dH3_e W2_e (contraction over D) with the SwiGLU
-//                    backward epilogue -> dH1 = [dG | dU] (bf16).
+//   k_gemm_dgrad<0>: dH2 = dH3_e W2_e (contraction over D), SwiGLU backward
+//                    epilogue -> dH1 = [dG | dU] (bf16); also writes
+//                    h2 = SiLU(g) * u rebuilt from h1 (the forward formula) for
+//                    the W2 weight gradient.
 //   k_gemm_dgrad<1>: dXr = dH1_e W13_e (contraction over 2F) -> fp32 rows.
-//   k_gemm_wgrad<2>: dW2_e  = dH3_e^T H2_e, H2 = SiLU(g) * u rebuilt from h1.
-//   k_gemm_wgrad<3>: dW13_e = dH1_e^T X_e.
+//   k_gemm_wgrad:    dW_e[b][a] = sum over the expert's rows m of
+//                    B[m][b] A[m][a]: dW2 = dH3^T H2 (a = F, b = D) and
+//                    dW13 = dH1^T X (a = D, b = 2F).
 //
-// MI355X design.  In DGRAD the weight rows run along the contraction, so the
-// weight tile is transposed on its way into LDS: each thread loads the same
-// 16-byte column chunk of two consecutive weight rows, interleaves them into
-// eight dwords (k, k+1) and writes one dword per output column.  MFMA
-// operands are then 16-byte LDS reads with the contraction contiguous.
-// WGRAD contracts over token rows, so both operands take the same
-// transposing path.  Work is a persistent, XCD-aware loop as in the forward
-// kernels; WGRAD tiles are 128 x 128 outputs of one expert, ordered
-// expert-major so the expert's operand rows stay in one XCD's L2.
+// MI355X design
+//  * Every global load is coalesced: sixteen consecutive lanes read one
+//    256-byte row segment.  Operands whose rows run along the contraction
+//    (DGRAD weights, both WGRAD operands) are transposed on their way into
+//    LDS: a thread holds the same 16-byte column chunk of two consecutive rows,
+//    interleaves them into eight (k, k+1) dwords and writes one dword per
+//    output column.  LDS rows hold 64 contraction values (32 dwords); their
+//    4-dword groups are XOR-swizzled with (o ^ o>>3) & 7 of the row o, which
+//    keeps these writes at most 2-way and the 16-byte MFMA operand reads
+//    conflict-free.
+//  * DGRAD: 128 output columns x 64 token rows per workgroup, 64 contraction
+//    values per stage, two more stages in flight in registers.
+//  * WGRAD: 128 x 128 outputs of one expert per work item, 64 token rows per
+//    stage; the next item's first stage is loaded while the current tile is
+//    staged through LDS and stored as whole 256/512-byte row segments.  Items
+//    run expert-major with the output column tile fastest, so the workgroups
+//    of one XCD write long contiguous runs of dW rows.
+//  * Persistent, XCD-aware grids as in the forward kernels.
 #include <algorithm>
 
 #include "common.h"
@@ -85,20 +97,32 @@ __device__ __forceinline__ int find_expert_b(const int32_t* __restrict__ mtoff, 
   return lo;
 }
 
+// Transposed tile: dword of contraction pair kpair in LDS row o, and the
+// first dword of 4-dword group g of row o.
+__device__ __forceinline__ int tsw(int o, int kpair) {
+  return o * 32 + ((((kpair >> 2) ^ o ^ (o >> 3)) & 7) << 2) + (kpair & 3);
+}
+__device__ __forceinline__ int tsw_g(int o, int g) { return o * 32 + (((g ^ o ^ (o >> 3)) & 7) << 2); }
+
+// Row tile (contraction contiguous): 128-byte rows, 16-byte chunks swizzled.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
+
 // ------------------------------------------------------------------ DGRAD
 template <int KIND>
 __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
-  constexpr int BK = 64;                       // contraction values per stage
-  constexpr int kAStrideDw = BK / 2 + 4;       // weight^T LDS row: 36 dwords (144 B)
-  constexpr int kABuf = 128 * kAStrideDw * 4;  // 18432 B
-  constexpr int kBStride = BK * 2 + 16;        // token LDS row: 144 B
-  constexpr int kBBuf = kBM * kBStride;        // 9216 B
-  __shared__ __attribute__((aligned(16))) char lds[2 * (kABuf + kBBuf)];
+  constexpr int kW = 128 * 32 * 4;   // transposed weight stage: 128 columns x 64 values
+  constexpr int kT = kBM * 128;      // token stage: 64 rows x 64 values
+  constexpr int kStage = kW + kT;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 31;
   const int lh = lane >> 5;
+  const int c16 = tid & 15;   // weight loader: 8-column chunk of a 256-byte row segment
+  const int kp = tid >> 4;    // weight loader: row pairs kp and kp + 16 of a stage
+  const int lc = tid & 7;     // token loader: 16-byte chunk of a 128-byte row segment
+  const int lrow = tid >> 3;  // token loader: tile row (+ 32 j)
 
   const RouteHdr* hdr = a.hdr;
   const int n_items = hdr->n_mt * a.NT;
@@ -106,12 +130,9 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   const int chunk = (n_items + kXcds - 1) / kXcds;
-  const int S = a.Kd / BK;
+  const int S = a.Kd / 64;
+  const int64_t N = a.N;
   const uint16_t* h1 = reinterpret_cast<const uint16_t*>(hdr->rec.h1);
-
-  // weight^T loader: row pairs kp and kp + 16 of the stage, 8-column chunk c
-  const int kp = tid & 15;
-  const int c = tid >> 4;
 
   for (int it = slot; it < chunk; it += per) {
     const int w = xcd * chunk + it;
@@ -125,74 +146,79 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
     const int rows = min(kBM, a.offsets[e + 1] - row0);
     const bool two = rows > 32;
 
-    const uint16_t* wbase = reinterpret_cast<const uint16_t*>(a.W) +
-                            (int64_t(e) * a.Kd + 2 * kp) * a.N + nt * 128 + c * 8;
-    const char* tbase = reinterpret_cast<const char*>(a.tok);
-    const int64_t trow_bytes = int64_t(a.Kd) * 2;
-    const char* tp[2];
-    int toff[2];
+    const uint16_t* wsrc = reinterpret_cast<const uint16_t*>(a.W) +
+                           (int64_t(e) * a.Kd + 2 * kp) * N + nt * 128 + c16 * 8;
+    const char* tsrc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i >> 3, cc = i & 7;
-      tp[j] = r < rows ? tbase + int64_t(row0 + r) * trow_bytes + cc * 16 : nullptr;
-      toff[j] = r * kBStride + cc * 16;
+      const int r = lrow + 32 * j;
+      tsrc[j] = r < rows ? reinterpret_cast<const char*>(a.tok) +
+                               (int64_t(row0 + r) * a.Kd) * 2 + lc * 16
+                         : nullptr;
     }
 
     f32x16 acc0 = {}, acc1 = {};
-    u32x4 wr[4], tr[2];
-    auto load = [&](int s) {
-      const uint16_t* p = wbase + int64_t(s) * BK * a.N;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        wr[2 * pp] = *reinterpret_cast<const u32x4*>(p + int64_t(32 * pp) * a.N);
-        wr[2 * pp + 1] = *reinterpret_cast<const u32x4*>(p + int64_t(32 * pp + 1) * a.N);
-      }
+    u32x4 R0[6], R1[6];
+    auto load = [&](u32x4* R, int s) {
+      const uint16_t* p = wsrc + int64_t(s) * 64 * N;
+      R[0] = *reinterpret_cast<const u32x4*>(p);
+      R[1] = *reinterpret_cast<const u32x4*>(p + N);
+      R[2] = *reinterpret_cast<const u32x4*>(p + 32 * N);
+      R[3] = *reinterpret_cast<const u32x4*>(p + 33 * N);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        tr[j] = tp[j] ? *reinterpret_cast<const u32x4*>(tp[j] + int64_t(s) * BK * 2)
-                      : u32x4{0u, 0u, 0u, 0u};
+        R[4 + j] = tsrc[j] ? *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128)
+                           : u32x4{0u, 0u, 0u, 0u};
     };
-    auto store = [&](int buf) {
-      uint32_t* la = reinterpret_cast<uint32_t*>(lds + buf * (kABuf + kBBuf));
+    auto store = [&](const u32x4* R, int buf) {
+      uint32_t* la = reinterpret_cast<uint32_t*>(lds + buf * kStage);
+      uint32_t d[8];
+      interleave8(R[0], R[1], d);
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        uint32_t d[8];
-        interleave8(wr[2 * pp], wr[2 * pp + 1], d);
+      for (int q = 0; q < 8; ++q) la[tsw(c16 * 8 + q, kp)] = d[q];
+      interleave8(R[2], R[3], d);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) la[(c * 8 + q) * kAStrideDw + kp + 16 * pp] = d[q];
-      }
-      char* lb = lds + buf * (kABuf + kBBuf) + kABuf;
+      for (int q = 0; q < 8; ++q) la[tsw(c16 * 8 + q, kp + 16)] = d[q];
+      char* lt = lds + buf * kStage + kW;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lb + toff[j]) = tr[j];
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
     };
     auto compute = [&](int buf) {
-      const char* la = lds + buf * (kABuf + kBBuf);
-      const char* lb = la + kABuf;
+      const char* la = lds + buf * kStage;
+      const char* lt = la + kW;
+      const int orow = 32 * wave + lr;
 #pragma unroll
-      for (int q = 0; q < BK / 16; ++q) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(
-            la + ((32 * wave + lr) * kAStrideDw + q * 8 + lh * 4) * 4);
-        const u32x4 b0 =
-            *reinterpret_cast<const u32x4*>(lb + lr * kBStride + (q * 16 + lh * 8) * 2);
+      for (int q = 0; q < 4; ++q) {
+        const int g = 2 * q + lh;
+        const u32x4 av = *reinterpret_cast<const u32x4*>(la + tsw_g(orow, g) * 4);
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lt + swz(lr, g));
         mfma_bf16(acc0, av, b0);
         if (two) {
-          const u32x4 b1 = *reinterpret_cast<const u32x4*>(lb + (32 + lr) * kBStride +
-                                                           (q * 16 + lh * 8) * 2);
+          const u32x4 b1 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, g));
           mfma_bf16(acc1, av, b1);
         }
       }
     };
 
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int s = 0; s < S; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < S) load(s + 1);
-      compute(cur);
-      if (s + 1 < S) store(cur ^ 1);
-      __syncthreads();
+    load(R0, 0);
+    if (S > 1) load(R1, 1);
+    store(R0, 0);
+    if (S > 2) load(R0, 2);
+    lds_barrier();
+    for (int s = 0; s < S; s += 2) {
+      compute(0);
+      if (s + 1 < S) {
+        store(R1, 1);
+        if (s + 3 < S) load(R1, s + 3);
+      }
+      lds_barrier();
+      if (s + 1 >= S) break;
+      compute(1);
+      if (s + 2 < S) {
+        store(R0, 0);
+        if (s + 4 < S) load(R0, s + 4);
+      }
+      lds_barrier();
     }
 
     // acc[b][v]: output column 32*wave + 8*(v/4) + 4*lh + v%4, token 32*b + lr
@@ -206,25 +232,29 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
       if (KIND == 0) {
         const int F = a.F;
         uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + row * (2 * F);
+        uint16_t* h2o = reinterpret_cast<uint16_t*>(a.out2);
         const uint16_t* hr = h1 + row * (2 * F);
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int j = col + 8 * g4;
-          float gv[4], uv[4], dg[4], du[4];
+          float gv[4], uv[4], dg[4], du[4], hv[4];
           load4_bf16(hr + j, gv);
           load4_bf16(hr + F + j, uv);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float dh2 = acc[4 * g4 + i];
             const float sg = sigmoid_f(gv[i]);
+            const float sl = silu_f(gv[i]);
             dg[i] = dh2 * uv[i] * (sg * (1.0f + gv[i] * (1.0f - sg)));
-            du[i] = dh2 * silu_f(gv[i]);
+            du[i] = dh2 * sl;
+            hv[i] = sl * uv[i];
           }
           store4<uint16_t>(o + j, dg[0], dg[1], dg[2], dg[3]);
           store4<uint16_t>(o + F + j, du[0], du[1], du[2], du[3]);
+          if (h2o) store4<uint16_t>(h2o + row * F + j, hv[0], hv[1], hv[2], hv[3]);
         }
       } else {
-        float* o = reinterpret_cast<float*>(a.out) + row * a.N;
+        float* o = reinterpret_cast<float*>(a.out) + row * N;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
           store4<float>(o + col + 8 * g4, acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2],
@@ -235,130 +265,162 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ WGRAD
-template <int KIND, typename TW>
+template <typename TW>
 __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
-  constexpr int BK = 32;                       // token rows per stage
-  constexpr int kStrideDw = BK / 2 + 4;        // 20 dwords (80 B) per LDS row
-  constexpr int kBuf = 128 * kStrideDw * 4;    // 10240 B per operand
-  __shared__ __attribute__((aligned(16))) char lds[2 * 2 * kBuf];
+  constexpr int kOp = 128 * 32 * 4;                    // one transposed operand stage
+  constexpr int kRowB = 128 * int(sizeof(TW)) + 16;    // padded output-staging row
+  constexpr int kHalves = sizeof(TW) == 4 ? 2 : 1;     // fp32 tiles are staged in two halves
+  constexpr int kRowsPerPass = 128 / kHalves;
+  constexpr int kOut = kRowsPerPass * kRowB;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kOp + kOut];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int kp = tid & 15;   // row pair of the stage
-  const int c = tid >> 4;    // 8-column chunk of the 128-wide tile
+  const int c16 = tid & 15;   // loader: 8-column chunk of a 256-byte row segment
+  const int kp = tid >> 4;    // loader: row pairs kp and kp + 16 of a 64-row stage
 
   const RouteHdr* hdr = a.hdr;
-  const int F = a.F, D = a.D;
-  const int per_e = a.NA * a.NB;
+  const int a_ld = a.a_ld, b_ld = a.b_ld;
+  const int NA = a_ld / 128, NB = b_ld / 128;
+  const int per_e = NA * NB;
   const int n_items = a.E * per_e;
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   const int chunk = (n_items + kXcds - 1) / kXcds;
-  // A operand source (rows of the expert): KIND 2 -> h1 (H2 rebuilt), KIND 3 -> x rows.
-  const uint16_t* asrc = reinterpret_cast<const uint16_t*>(KIND == 2 ? hdr->rec.h1
-                                                                     : hdr->rec.x_rows);
-  const int a_ld = KIND == 2 ? 2 * F : D;          // row length of the A source
+  const uint16_t* asrc = reinterpret_cast<const uint16_t*>(a.arows ? a.arows
+                                                                   : (const void*)hdr->rec.x_rows);
   const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(a.grad);
-  const int b_ld = KIND == 2 ? D : 2 * F;          // row length of the B source
 
-  for (int it = slot; it < chunk; it += per) {
-    const int w = xcd * chunk + it;
-    if (w >= n_items) break;
-    const int e = w / per_e;
-    const int rem = w - e * per_e;
-    const int ta = rem / a.NB;
-    const int tb = rem - ta * a.NB;
-    const int r0 = a.offsets[e];
-    const int Me = a.offsets[e + 1] - r0;
-    const int S = (Me + BK - 1) / BK;
-
-    const int acol = ta * 128 + c * 8;
-    const int bcol = tb * 128 + c * 8;
-    u32x4 ar[2], br[2];
-    auto load = [&](int s) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int m = s * BK + 2 * kp + h;
-        if (m < Me) {
-          const int64_t row = r0 + m;
-          if (KIND == 2) {
-            const u32x4 gq = *reinterpret_cast<const u32x4*>(asrc + row * a_ld + acol);
-            const u32x4 uq = *reinterpret_cast<const u32x4*>(asrc + row * a_ld + F + acol);
-            u32x4 hq;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float g0 = __uint_as_float(gq[i] << 16), g1 = __uint_as_float(gq[i] & 0xffff0000u);
-              const float u0 = __uint_as_float(uq[i] << 16), u1 = __uint_as_float(uq[i] & 0xffff0000u);
-              hq[i] = pack_bf16x2(silu_f(g0) * u0, silu_f(g1) * u1);
-            }
-            ar[h] = hq;
-          } else {
-            ar[h] = *reinterpret_cast<const u32x4*>(asrc + row * a_ld + acol);
-          }
-          br[h] = *reinterpret_cast<const u32x4*>(bsrc + row * b_ld + bcol);
-        } else {
-          ar[h] = u32x4{0u, 0u, 0u, 0u};
-          br[h] = u32x4{0u, 0u, 0u, 0u};
-        }
+  struct Item {
+    int e, ta, tb, r0, Me, S;
+  };
+  // Work items of this workgroup are w = xcd*chunk + it for it = slot, slot +
+  // per, ...; (e, tb, ta) advance by carries instead of a division per item.
+  int w0 = xcd * chunk + slot;
+  int ie = w0 / per_e;
+  int irem = w0 - ie * per_e;
+  int itb = irem / NA;
+  int ita = irem - itb * NA;
+  const int wend = min(xcd * chunk + chunk, n_items);
+  int wcur = w0;
+  auto fill = [&](Item& t) {
+    if (wcur >= wend) {
+      t.e = -1;
+      return;
+    }
+    t.e = ie;
+    t.ta = ita;
+    t.tb = itb;
+    t.r0 = a.offsets[ie];
+    t.Me = a.offsets[ie + 1] - t.r0;
+    t.S = (t.Me + 63) / 64;
+    // advance to the next item of this workgroup
+    wcur += per;
+    ita += per;
+    while (ita >= NA) {
+      ita -= NA;
+      if (++itb == NB) {
+        itb = 0;
+        ++ie;
       }
-    };
-    auto store = [&](int buf) {
-      uint32_t* la = reinterpret_cast<uint32_t*>(lds + buf * 2 * kBuf);
-      uint32_t* lb = la + kBuf / 4;
-      uint32_t d[8];
-      interleave8(ar[0], ar[1], d);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) la[(c * 8 + q) * kStrideDw + kp] = d[q];
-      interleave8(br[0], br[1], d);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) lb[(c * 8 + q) * kStrideDw + kp] = d[q];
-    };
+    }
+  };
 
+  u32x4 R[8];  // one stage: rows 2kp, 2kp+1, 32+2kp, 33+2kp of A then B
+  auto load = [&](const Item& t, int s) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int m = s * 64 + 2 * kp + (h & 1) + (h >> 1) * 32;
+      if (m < t.Me) {
+        const int64_t row = t.r0 + m;
+        R[h] = *reinterpret_cast<const u32x4*>(asrc + row * a_ld + t.ta * 128 + c16 * 8);
+        R[4 + h] = *reinterpret_cast<const u32x4*>(bsrc + row * b_ld + t.tb * 128 + c16 * 8);
+      } else {
+        R[h] = u32x4{0u, 0u, 0u, 0u};
+        R[4 + h] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store = [&]() {
+    uint32_t* la = reinterpret_cast<uint32_t*>(lds);
+    uint32_t* lb = la + kOp / 4;
+    uint32_t d[8];
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      interleave8(R[2 * pp], R[2 * pp + 1], d);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) la[tsw(c16 * 8 + q, kp + 16 * pp)] = d[q];
+      interleave8(R[4 + 2 * pp], R[5 + 2 * pp], d);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lb[tsw(c16 * 8 + q, kp + 16 * pp)] = d[q];
+    }
+  };
+
+  Item cur, nxt;
+  fill(cur);
+  if (cur.e >= 0 && cur.S > 0) load(cur, 0);
+  while (cur.e >= 0) {
+    fill(nxt);
     f32x16 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-    if (S > 0) {
-      load(0);
-      store(0);
-      __syncthreads();
-      for (int s = 0; s < S; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < S) load(s + 1);
-        const char* la = lds + cur * 2 * kBuf;
-        const char* lb = la + kBuf;
+    for (int s = 0; s < cur.S; ++s) {
+      store();
+      lds_barrier();
+      if (s + 1 < cur.S)
+        load(cur, s + 1);
+      else if (nxt.e >= 0 && nxt.S > 0)
+        load(nxt, 0);
+      const char* la = lds;
+      const char* lb = lds + kOp;
 #pragma unroll
-        for (int q = 0; q < BK / 16; ++q) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(
-              la + ((32 * wave + lr) * kStrideDw + q * 8 + lh * 4) * 4);
+      for (int q = 0; q < 4; ++q) {
+        const int g = 2 * q + lh;
+        const u32x4 av = *reinterpret_cast<const u32x4*>(la + tsw_g(32 * wave + lr, g) * 4);
 #pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const u32x4 bv = *reinterpret_cast<const u32x4*>(
-                lb + ((32 * bb + lr) * kStrideDw + q * 8 + lh * 4) * 4);
-            mfma_bf16(acc[bb], av, bv);
-          }
+        for (int bb = 0; bb < 4; ++bb) {
+          const u32x4 bv = *reinterpret_cast<const u32x4*>(lb + tsw_g(32 * bb + lr, g) * 4);
+          mfma_bf16(acc[bb], av, bv);
         }
-        if (s + 1 < S) store(cur ^ 1);
-        __syncthreads();
       }
+      lds_barrier();
     }
+    if (cur.S == 0 && nxt.e >= 0 && nxt.S > 0) load(nxt, 0);
 
-    // acc[bb][v] = dW[b = tb*128 + 32*bb + lr][a = ta*128 + 32*wave + 8*(v/4) + 4*lh + v%4]
-    const int64_t nb_total = KIND == 2 ? D : 2 * F;   // rows of dW per expert
-    const int a_len = KIND == 2 ? F : D;               // row length of dW
-    TW* o = reinterpret_cast<TW*>(a.out) + int64_t(e) * nb_total * a_len;
-    const int acol0 = ta * 128 + 32 * wave + 4 * lh;
+    // acc[bb][v] = dW[b = tb*128 + 32*bb + lr][a = ta*128 + 32*wave + 8*(v/4) + 4*lh + v%4],
+    // staged through LDS and stored as whole row segments.
+    TW* o = reinterpret_cast<TW*>(a.out) + (int64_t(cur.e) * b_ld + int64_t(cur.tb) * 128) * a_ld +
+            cur.ta * 128;
+    char* stg = lds + 2 * kOp;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int64_t brow = tb * 128 + 32 * bb + lr;
-      TW* orow = o + brow * a_len + acol0;
+    for (int h = 0; h < kHalves; ++h) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        store4<TW>(orow + 8 * g4, acc[bb][4 * g4], acc[bb][4 * g4 + 1], acc[bb][4 * g4 + 2],
-                   acc[bb][4 * g4 + 3]);
+      for (int bb = 0; bb < 4; ++bb) {
+        if (bb / (4 / kHalves) != h) continue;
+        const int rl = 32 * bb + lr - h * kRowsPerPass;
+        TW* rowp = reinterpret_cast<TW*>(stg + rl * kRowB) + 32 * wave + 4 * lh;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          store4<TW>(rowp + 8 * g4, acc[bb][4 * g4], acc[bb][4 * g4 + 1], acc[bb][4 * g4 + 2],
+                     acc[bb][4 * g4 + 3]);
+      }
+      lds_barrier();
+      constexpr int kChunksPerRow = 128 * int(sizeof(TW)) / 16;
+      constexpr int kChunks = kRowsPerPass * kChunksPerRow;
+#pragma unroll
+      for (int j = 0; j < kChunks / 256; ++j) {
+        const int i = tid + 256 * j;
+        const int rl = i / kChunksPerRow, cc = i % kChunksPerRow;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * kRowB + cc * 16);
+        char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
+      lds_barrier();
     }
+    cur = nxt;
   }
 }
 
@@ -395,28 +457,17 @@ hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hip
   return hipGetLastError();
 }
 
-// kind 2: W2 WGRAD; 3: W13 WGRAD.  dw_f32 selects the dW storage type.
-hipError_t launch_wgrad(int kind, int dw_f32, const BwdArgs& a, int cus, hipStream_t s) {
-  const int64_t items = int64_t(a.E) * a.NA * a.NB;
+// dW[e] = B_e^T A_e for every expert; dw_f32 selects the dW storage type.
+hipError_t launch_wgrad(int dw_f32, const BwdArgs& a, int cus, hipStream_t s) {
+  const int64_t items = int64_t(a.E) * (a.a_ld / 128) * (a.b_ld / 128);
   if (items == 0) return hipSuccess;
-#define MOE_WG(KD, TW)                                                                    \
-  do {                                                                                    \
-    const unsigned g = persistent_grid(occupancy<10 * KD + int(sizeof(TW))>(k_gemm_wgrad<KD, TW>), \
-                                       items, cus);                                       \
-    hipLaunchKernelGGL((k_gemm_wgrad<KD, TW>), dim3(g), dim3(256), 0, s, a);              \
-  } while (0)
-  if (kind == 2) {
-    if (dw_f32)
-      MOE_WG(2, float);
-    else
-      MOE_WG(2, uint16_t);
+  if (dw_f32) {
+    const unsigned g = persistent_grid(occupancy<2>(k_gemm_wgrad<float>), items, cus);
+    hipLaunchKernelGGL(k_gemm_wgrad<float>, dim3(g), dim3(256), 0, s, a);
   } else {
-    if (dw_f32)
-      MOE_WG(3, float);
-    else
-      MOE_WG(3, uint16_t);
+    const unsigned g = persistent_grid(occupancy<3>(k_gemm_wgrad<uint16_t>), items, cus);
+    hipLaunchKernelGGL(k_gemm_wgrad<uint16_t>, dim3(g), dim3(256), 0, s, a);
   }
-#undef MOE_WG
   return hipGetLastError();
 }
 

@@ -16,17 +16,20 @@
 // to each other).
 //
 // MI355X design
-//  * Weights are streamed from HBM straight into MFMA operand registers: a
-//    weight row is K-contiguous, so lane (row r, half h) loads its 8-value
-//    operand as one 16-byte load; within a BK stage half h owns the
-//    contiguous half [h*BK/2, (h+1)*BK/2) of the row (the contraction order
-//    inside a stage is a permutation applied identically to both operands).
-//  * The token tile (<= 64 rows x BK) is shared by the 4 waves through a
-//    double-buffered LDS tile.
+//  * The GEMMs are bound by streaming expert weights from HBM (~32 rows per
+//    expert).  Each stage moves a 128-byte segment of 128 weight rows and of
+//    the tile's <= 64 token rows with fully coalesced 16-byte loads (eight
+//    consecutive lanes cover one row segment), stores them into LDS with a
+//    per-row XOR swizzle of the 16-byte chunks, and the MFMA operands are
+//    16-byte LDS reads.  Two further stages are in flight in registers
+//    (ring of two), so ~48 KiB per workgroup is outstanding while a stage
+//    computes.
 //  * Workgroup tile: 128 weight rows (4 waves x 32) x 64 token rows; each
 //    wave holds two 32x32 fp32 accumulators (v_mfma_f32_32x32x16_bf16, or
-//    v_mfma_f32_32x32x2f32 for fp32 operands).  A tile whose expert has <= 32
-//    rows left skips the second accumulator.
+//    v_mfma_f32_32x32x2f32 for fp32 operands).  A tile with <= 32 rows skips
+//    the second accumulator.  Within a stage, half h of a lane's operands
+//    covers chunks [4h, 4h+4) of the row segment: a permutation of the
+//    contraction applied identically to both operands.
 //  * Persistent grid, XCD-aware: work item w is run by a workgroup of XCD
 //    (w / chunk), so one XCD's L2 holds an expert's token rows while its
 //    n-tiles stream by; items are expert-major, then n-tile, then m-tile, so
@@ -77,17 +80,6 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
-template <typename T, int BK>
-struct FwdTile {
-  static constexpr int ES = sizeof(T);
-  static constexpr int kRowBytes = BK * ES;                    // one token row of a stage
-  static constexpr int kLdsStride = kRowBytes + 16;             // padded LDS row
-  static constexpr int kBuf = kBM * kLdsStride;                 // one LDS stage buffer
-  static constexpr int kWChunks = BK * ES / 2 / 16;             // u32x4 per lane per stage
-  static constexpr int kAChunks = kBM * kRowBytes / 16 / 256;   // u32x4 per thread per stage
-  static constexpr int kSteps = BK / 16;                        // MFMA k-steps per stage
-};
-
 // Finds the expert of work item w: the largest e with mtoff[e]*NT <= w.
 __device__ __forceinline__ int find_expert(const int32_t* __restrict__ mtoff, int E, int NT,
                                            int w) {
@@ -102,15 +94,28 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ mtoff, in
   return lo;
 }
 
-template <typename T, int MODE, int BK>
+// LDS byte offset of 16-byte chunk c of tile row r (128-byte rows).  Chunks
+// are XOR-swizzled by (r ^ r>>3) & 7 so that both the row-wise writes (8 lanes
+// per row) and the MFMA-layout reads (32 rows, one chunk) are spread over all
+// banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
+
+template <typename T, int MODE>
 __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
-  using Tl = FwdTile<T, BK>;
-  __shared__ __attribute__((aligned(16))) char lds[2 * Tl::kBuf];
+  constexpr int ES = sizeof(T);
+  constexpr int kW = 128 * 128;          // weight stage: 128 rows x 128 B
+  constexpr int kA = kBM * 128;          // token stage: 64 rows x 128 B
+  constexpr int kStage = kW + kA;
+  constexpr int kSteps = 128 / ES / 16;  // MFMA k-steps (16 values) per stage
+  constexpr int kV = Mma<T>::kV;         // 16-byte chunks per 8-value operand
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 31;   // row inside the 32-row operand block
-  const int lh = lane >> 5;   // operand half
+  const int lh = lane >> 5;   // operand half: chunks [4*lh, 4*lh + 4) of a stage row
+  const int lc = tid & 7;     // loader: 16-byte chunk of a 128-byte row segment
+  const int lrow = tid >> 3;  // loader: tile row (+ 32 j)
 
   const RouteHdr* hdr = a.hdr;
   if (a.replay_only && !hdr->rec.replay) return;
@@ -118,13 +123,13 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
   const char* Abase = reinterpret_cast<const char*>(a.A ? a.A : (const void*)hdr->rec.x_rows);
   T* out0 = reinterpret_cast<T*>(a.out0 ? a.out0 : (void*)hdr->rec.h1);
   T* out1 = reinterpret_cast<T*>(a.out1);
-  const int64_t a_row_bytes = int64_t(a.Kd) * Tl::ES;
+  const int64_t row_bytes = int64_t(a.Kd) * ES;
 
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   const int chunk = (n_items + kXcds - 1) / kXcds;
-  const int S = a.Kd / BK;
+  const int S = int(row_bytes / 128);
 
   for (int it = slot; it < chunk; it += per) {
     const int w = xcd * chunk + it;
@@ -138,86 +143,85 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
     const int rows = min(kBM, a.offsets[e + 1] - row0);
     const bool two = rows > 32;
 
-    // Weight row of this lane.
-    int nrow;
-    if (MODE == 0)
-      nrow = (wave < 2 ? 0 : a.F) + nt * 64 + (wave & 1) * 32 + lr;
-    else
-      nrow = nt * 128 + wave * 32 + lr;
-    const char* wp = reinterpret_cast<const char*>(a.W) +
-                     (int64_t(e) * a.N + nrow) * a_row_bytes + lh * (BK / 2) * Tl::ES;
-
-    // Token-tile chunk owned by this thread for the global->LDS copy.
-    constexpr int kCPR = Tl::kRowBytes / 16;  // 16-byte chunks per token row
-    const char* ap[Tl::kAChunks];
-    int lds_off[Tl::kAChunks];
+    // Global sources of this thread's four weight chunks and two token chunks.
+    const char* wsrc[4];
 #pragma unroll
-    for (int j = 0; j < Tl::kAChunks; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i / kCPR, c = i % kCPR;
-      ap[j] = r < rows ? Abase + int64_t(row0 + r) * a_row_bytes + c * 16 : nullptr;
-      lds_off[j] = r * Tl::kLdsStride + c * 16;
+    for (int j = 0; j < 4; ++j) {
+      const int rho = lrow + 32 * j;
+      const int wr = MODE == 0 ? (rho < 64 ? nt * 64 + rho : a.F + nt * 64 + rho - 64)
+                               : nt * 128 + rho;
+      wsrc[j] = reinterpret_cast<const char*>(a.W) + (int64_t(e) * a.N + wr) * row_bytes + lc * 16;
+    }
+    const char* tsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = lrow + 32 * j;
+      tsrc[j] = r < rows ? Abase + int64_t(row0 + r) * row_bytes + lc * 16 : nullptr;
     }
 
     f32x16 acc0 = {}, acc1 = {};
-    u32x4 wa[Tl::kWChunks], wb[Tl::kWChunks], at[Tl::kAChunks];
-
-    auto load_w = [&](u32x4* dst, int s) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(wp + int64_t(s) * Tl::kRowBytes);
+    u32x4 R0[6], R1[6];
+    auto load = [&](u32x4* R, int s) {
+      const int64_t off = int64_t(s) * 128;
 #pragma unroll
-      for (int j = 0; j < Tl::kWChunks; ++j) dst[j] = p[j];
+      for (int j = 0; j < 4; ++j) R[j] = *reinterpret_cast<const u32x4*>(wsrc[j] + off);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        R[4 + j] = tsrc[j] ? *reinterpret_cast<const u32x4*>(tsrc[j] + off) : u32x4{0u, 0u, 0u, 0u};
     };
-    auto load_a = [&](int s) {
+    auto store = [&](const u32x4* R, int buf) {
+      char* base = lds + buf * kStage;
 #pragma unroll
-      for (int j = 0; j < Tl::kAChunks; ++j)
-        at[j] = ap[j] ? *reinterpret_cast<const u32x4*>(ap[j] + int64_t(s) * Tl::kRowBytes)
-                      : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x4*>(base + swz(lrow + 32 * j, lc)) = R[j];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
     };
-    auto store_a = [&](int buf) {
+    auto compute = [&](int buf) {
+      const char* wl = lds + buf * kStage;
+      const char* tl = wl + kW;
+      const int wrow = 32 * wave + lr;
 #pragma unroll
-      for (int j = 0; j < Tl::kAChunks; ++j)
-        *reinterpret_cast<u32x4*>(lds + buf * Tl::kBuf + lds_off[j]) = at[j];
-    };
-    auto compute = [&](const u32x4* wr, int buf) {
-      const char* base = lds + buf * Tl::kBuf + lh * (BK / 2) * Tl::ES;
+      for (int q = 0; q < kSteps; ++q) {
+        u32x4 av[kV], b0[kV], b1[kV];
 #pragma unroll
-      for (int q = 0; q < Tl::kSteps; ++q) {
-        u32x4 b[Mma<T>::kV];
-        const char* p0 = base + lr * Tl::kLdsStride + q * 8 * Tl::ES;
-#pragma unroll
-        for (int v = 0; v < Mma<T>::kV; ++v) b[v] = *reinterpret_cast<const u32x4*>(p0 + 16 * v);
-        Mma<T>::step(acc0, wr + q * Mma<T>::kV, b);
+        for (int v = 0; v < kV; ++v) {
+          const int c = 4 * lh + q * kV + v;
+          av[v] = *reinterpret_cast<const u32x4*>(wl + swz(wrow, c));
+          b0[v] = *reinterpret_cast<const u32x4*>(tl + swz(lr, c));
+        }
+        Mma<T>::step(acc0, av, b0);
         if (two) {
-          const char* p1 = p0 + 32 * Tl::kLdsStride;
 #pragma unroll
-          for (int v = 0; v < Mma<T>::kV; ++v)
-            b[v] = *reinterpret_cast<const u32x4*>(p1 + 16 * v);
-          Mma<T>::step(acc1, wr + q * Mma<T>::kV, b);
+          for (int v = 0; v < kV; ++v)
+            b1[v] = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, 4 * lh + q * kV + v));
+          Mma<T>::step(acc1, av, b1);
         }
       }
     };
 
-    // Software pipeline: stage s+1 loads are in flight while stage s computes.
-    load_w(wa, 0);
-    load_a(0);
-    store_a(0);
-    __syncthreads();
+    // Pipeline: stage s computes from LDS while stages s+1 and s+2 are in
+    // flight in registers (stage k lives in R[k % 2] until stored).
+    load(R0, 0);
+    if (S > 1) load(R1, 1);
+    store(R0, 0);
+    if (S > 2) load(R0, 2);
+    lds_barrier();
     for (int s = 0; s < S; s += 2) {
+      compute(0);
       if (s + 1 < S) {
-        load_w(wb, s + 1);
-        load_a(s + 1);
+        store(R1, 1);
+        if (s + 3 < S) load(R1, s + 3);
       }
-      compute(wa, 0);
-      if (s + 1 < S) store_a(1);
-      __syncthreads();
+      lds_barrier();
       if (s + 1 >= S) break;
+      compute(1);
       if (s + 2 < S) {
-        load_w(wa, s + 2);
-        load_a(s + 2);
+        store(R0, 0);
+        if (s + 4 < S) load(R0, s + 4);
       }
-      compute(wb, 1);
-      if (s + 2 < S) store_a(0);
-      __syncthreads();
+      lds_barrier();
     }
 
     // ---------------------------------------------------------- epilogue
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
           xch[(((wave - 2) * 2 + 1) * 16 + v) * 64 + lane] = Elem<T>::round(acc1[v]);
         }
       }
-      __syncthreads();
+      lds_barrier();
       if (wave < 2) {
         const int jcol = nt * 64 + wave * 32 + 4 * lh;
 #pragma unroll
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
     } else {
       const int ncol = nt * 128 + wave * 32 + 4 * lh;
 #pragma unroll
@@ -296,18 +300,17 @@ static unsigned fwd_grid(int64_t items_max, int cus, int per_cu) {
 
 template <typename T, int MODE>
 static hipError_t launch_fwd_t(const FwdArgs& a, int64_t mt_max, int cus, hipStream_t s) {
-  constexpr int BK = sizeof(T) == 2 ? 64 : 32;
   static int per_cu = 0;  // resident workgroups per CU (same on every gfx950 device)
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_fwd<T, MODE, BK>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_fwd<T, MODE>, 256, 0) !=
             hipSuccess ||
         n <= 0)
       n = 1;
     per_cu = n;
   }
   const unsigned g = fwd_grid(mt_max * a.NT, cus, per_cu);
-  hipLaunchKernelGGL((k_gemm_fwd<T, MODE, BK>), dim3(g), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_gemm_fwd<T, MODE>), dim3(g), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
