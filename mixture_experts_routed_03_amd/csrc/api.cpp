@@ -37,7 +37,7 @@ hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_
 hipError_t launch_gemm_fwd(int prec, int mode, const FwdArgs& a, int64_t mt_max, int cus,
                            hipStream_t s);
 hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hipStream_t s);
-hipError_t launch_wgrad(int dw_f32, const BwdArgs& a, int cus, hipStream_t s);
+hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -363,7 +363,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw2{hdr, offsets, mtoff, nullptr, nullptr, dh3, h2, g->dw2, nullptr,
               0, 0, d.f, d.d, d.e, 0, d.f, d.d};
-  e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(dw_f32, bw2, cus, s); });
+  e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(dw_f32, 2, bw2, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs b13{hdr, offsets, mtoff, w->w13, dh1, nullptr, nullptr, dxr, nullptr,
               2 * d.f, d.d, d.f, d.d, d.e, d.d / 128, 0, 0};
@@ -371,7 +371,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw13{hdr, offsets, mtoff, nullptr, nullptr, dh1, nullptr, g->dw13, nullptr,
                0, 0, d.f, d.d, d.e, 0, d.d, 2 * d.f};
-  e = timed(p, "w13_wgrad", s, [&] { return launch_wgrad(dw_f32, bw13, cus, s); });
+  e = timed(p, "w13_wgrad", s, [&] { return launch_wgrad(dw_f32, 13, bw13, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = timed(p, "dx_reduce", s, [&] {
     return launch_dx_reduce(d.prec, hdr, route_to_row, dxr, g->dx, d.k, d.d, d.t_max,

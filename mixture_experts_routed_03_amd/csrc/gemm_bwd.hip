@@ -265,7 +265,8 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ WGRAD
-template <typename TW>
+// TAG only separates the two launches in profiles (2: dW2, 13: dW13).
+template <typename TW, int TAG>
 __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
   constexpr int kOp = 128 * 32 * 4;                    // one transposed operand stage
   constexpr int kRowB = 128 * int(sizeof(TW)) + 16;    // padded output-staging row
@@ -416,7 +417,9 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
         const int rl = i / kChunksPerRow, cc = i % kChunksPerRow;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * kRowB + cc * 16);
         char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
-        *reinterpret_cast<u32x4*>(dst) = v;
+        // dW is written once and not read back here: stream it past the L2 so
+        // the expert's operand rows stay cached for the other tiles.
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
       }
       lds_barrier();
     }
@@ -457,17 +460,28 @@ hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hip
   return hipGetLastError();
 }
 
-// dW[e] = B_e^T A_e for every expert; dw_f32 selects the dW storage type.
-hipError_t launch_wgrad(int dw_f32, const BwdArgs& a, int cus, hipStream_t s) {
+// dW[e] = B_e^T A_e for every expert; dw_f32 selects the dW storage type;
+// tag names the launch (2: dW2, 13: dW13).
+hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s) {
   const int64_t items = int64_t(a.E) * (a.a_ld / 128) * (a.b_ld / 128);
   if (items == 0) return hipSuccess;
+#define MOE_WG(TW, TAG, ID)                                                                  \
+  do {                                                                                     \
+    const unsigned g = persistent_grid(occupancy<ID>(k_gemm_wgrad<TW, TAG>), items, cus);  \
+    hipLaunchKernelGGL((k_gemm_wgrad<TW, TAG>), dim3(g), dim3(256), 0, s, a);             \
+  } while (0)
   if (dw_f32) {
-    const unsigned g = persistent_grid(occupancy<2>(k_gemm_wgrad<float>), items, cus);
-    hipLaunchKernelGGL(k_gemm_wgrad<float>, dim3(g), dim3(256), 0, s, a);
+    if (tag == 2)
+      MOE_WG(float, 2, 2);
+    else
+      MOE_WG(float, 13, 3);
   } else {
-    const unsigned g = persistent_grid(occupancy<3>(k_gemm_wgrad<uint16_t>), items, cus);
-    hipLaunchKernelGGL(k_gemm_wgrad<uint16_t>, dim3(g), dim3(256), 0, s, a);
+    if (tag == 2)
+      MOE_WG(uint16_t, 2, 4);
+    else
+      MOE_WG(uint16_t, 13, 5);
   }
+#undef MOE_WG
   return hipGetLastError();
 }
 

@@ -157,3 +157,112 @@ def expert_ffn_backward_mx(x_rows, w13q, w2q, h1, dh3):
     dx = qdq_rows(dh1) @ w13q
     dw13 = qdq_cols(dh1).T @ qdq_cols(x_rows)
     return dx, dw13, dw2, dh1
+
+
+# --------------------------------------------------------------------------
+# Codes (what a producer publishes): E4M3 bytes and E8M0 exponents.
+# --------------------------------------------------------------------------
+
+def quantize_rows(v):
+    """1x32 blocks along the last axis: (E4M3 bytes, E8M0 exponents e)."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[-1]
+    b = v.reshape(v.shape[:-1] + (n // BLOCK, BLOCK))
+    e = e8m0_exponent(np.max(np.abs(b), axis=-1))
+    q = e4m3_encode(b / np.ldexp(1.0, e)[..., None])
+    return q.reshape(v.shape), e
+
+
+def quantize_32x32(w):
+    """32x32 blocks over [N, K]: (E4M3 bytes [N, K], exponents [N/32, K/32])."""
+    w = np.asarray(w, dtype=np.float64)
+    N, K = w.shape
+    b = w.reshape(N // BLOCK, BLOCK, K // BLOCK, BLOCK)
+    e = e8m0_exponent(np.max(np.abs(b), axis=(1, 3)))
+    q = e4m3_encode(b / np.ldexp(1.0, e)[:, None, :, None])
+    return q.reshape(N, K), e
+
+
+def quantize_cols(v):
+    """32x1 blocks down the rows of one expert's [M, N] matrix, rows padded
+    with zeros to Mp = a multiple of 32.  Returns the column bundle as the
+    transposed codes [N, Mp] and exponents [N, Mp/32]."""
+    v = np.asarray(v, dtype=np.float64)
+    M, N = v.shape
+    Mp = -(-M // BLOCK) * BLOCK
+    pad = np.zeros((Mp, N))
+    pad[:M] = v
+    b = pad.T.reshape(N, Mp // BLOCK, BLOCK)
+    e = e8m0_exponent(np.max(np.abs(b), axis=-1))
+    q = e4m3_encode(b / np.ldexp(1.0, e)[..., None])
+    return q.reshape(N, Mp), e
+
+
+# --------------------------------------------------------------------------
+# Whole layer, quantization-faithful (same routing and combine as moe.py)
+# --------------------------------------------------------------------------
+
+def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False):
+    """MXFP8 layer forward: weights in 32x32 blocks, activations per the
+    expert functions above; combine in fp64."""
+    from . import moe
+    X = moe.as_f64(x)
+    S = moe.as_f64(scores)
+    T, D = X.shape
+    ids_a = moe.as_i64(ids)
+    K = ids_a.shape[1]
+    E = w13.shape[0]
+    F = w2.shape[2]
+    rt = moe.route(ids_a, E)
+    H1 = np.zeros((rt["R"], 2 * F))
+    H3S = np.zeros((T * K, D))
+    for e in range(E):
+        a, b = rt["offsets"][e], rt["offsets"][e + 1]
+        if a == b:
+            continue
+        routes = rt["sorted_route"][a:b]
+        h1, _, h3 = expert_ffn_mx(X[routes // K], qdq_32x32(moe.as_f64(w13[e])),
+                                  qdq_32x32(moe.as_f64(w2[e])))
+        H1[a:b], H3S[routes] = h1, h3
+    Y = moe.combine(H3S, S, ids_a, E)
+    if y_addend is not None:
+        Y = Y + moe.as_f64(y_addend)
+    if keep:
+        return Y, dict(route=rt, H1=H1, H3S=H3S, K=K, E=E)
+    return Y
+
+
+def backward(dy, x, ids, scores, w13, w2, cache):
+    """MXFP8 layer backward (dX, dW13, dW2, dS), quantization-faithful."""
+    from . import moe
+    dY = moe.as_f64(dy)
+    X = moe.as_f64(x)
+    S = moe.as_f64(scores)
+    ids_a = moe.as_i64(ids)
+    T, K = ids_a.shape
+    rt = cache["route"]
+    E = cache["E"]
+    D = X.shape[1]
+    F = w2.shape[2]
+    valid = ((ids_a >= 0) & (ids_a < E)).reshape(-1)
+    H3S = cache["H3S"]
+    tok = np.arange(T * K) // K
+    dS = np.where(valid, np.einsum("rd,rd->r", H3S, dY[tok]), 0.0).reshape(T, K)
+    dH3S = np.where(valid[:, None], S.reshape(-1)[:, None] * dY[tok], 0.0)
+    dX = np.zeros((T, D))
+    dW13 = np.zeros((E, 2 * F, D))
+    dW2 = np.zeros((E, D, F))
+    dXr = np.zeros((T * K, D))
+    for e in range(E):
+        a, b = rt["offsets"][e], rt["offsets"][e + 1]
+        if a == b:
+            continue
+        routes = rt["sorted_route"][a:b]
+        dxe, dw13e, dw2e, _ = expert_ffn_backward_mx(
+            X[routes // K], qdq_32x32(moe.as_f64(w13[e])), qdq_32x32(moe.as_f64(w2[e])),
+            cache["H1"][a:b], dH3S[routes])
+        dW13[e], dW2[e] = dw13e, dw2e
+        dXr[routes] = dxe
+    for k in range(K):
+        dX += np.where(valid[k::K][:, None], dXr[k::K], 0.0)
+    return dX, dW13, dW2, dS

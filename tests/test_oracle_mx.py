@@ -117,3 +117,37 @@ def test_mx_path_error_is_quantization_sized():
     r3 = moe.expert_ffn(x, w13, w2)[2]
     err = moe.max_abs_rel(h3, r3)
     assert 1e-3 < err < 0.1
+
+
+def test_codes_match_quantize_dequantize():
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((5, 64)) * np.exp(2 * rng.standard_normal((5, 64)))
+    q, e = mx.quantize_rows(v)
+    np.testing.assert_array_equal(mx.e4m3_decode(q) * np.ldexp(1.0, np.repeat(e, 32, 1)),
+                                  mx.qdq_rows(v))
+    w = rng.standard_normal((64, 96))
+    q, e = mx.quantize_32x32(w)
+    np.testing.assert_array_equal(
+        mx.e4m3_decode(q) * np.ldexp(1.0, np.repeat(np.repeat(e, 32, 0), 32, 1)), mx.qdq_32x32(w))
+    m = rng.standard_normal((45, 64))
+    q, e = mx.quantize_cols(m)
+    assert q.shape == (64, 64) and e.shape == (64, 2)
+    deq = mx.e4m3_decode(q) * np.ldexp(1.0, np.repeat(e, 32, 1))
+    np.testing.assert_array_equal(deq.T[:45], mx.qdq_cols(m))
+    assert np.all(q[:, 45:] == 0)          # pad rows quantize to +0
+
+
+def test_mx_layer_reduces_to_fp64_layer_without_rounding(monkeypatch):
+    from oracle import moe
+    rng = np.random.default_rng(8)
+    T, D, F, E, K = 6, 64, 32, 3, 2
+    x = rng.standard_normal((T, D)); w13 = rng.standard_normal((E, 2 * F, D))
+    w2 = rng.standard_normal((E, D, F)); ids = np.array([[0, 1], [1, 2], [2, -1], [0, 2], [1, 0], [-1, -1]])
+    s = rng.random((T, K)); s[ids < 0] = 0; dy = rng.standard_normal((T, D))
+    for name in ("qdq_rows", "qdq_cols", "qdq_32x32"):
+        monkeypatch.setattr(mx, name, lambda v: np.asarray(v, dtype=np.float64))
+    y, c = mx.forward(x, ids, s, w13, w2, keep=True)
+    ry, rc = moe.forward(x, ids, s, w13, w2, keep=True)
+    np.testing.assert_allclose(y, ry, rtol=1e-12, atol=1e-12)
+    for a, b in zip(mx.backward(dy, x, ids, s, w13, w2, c), moe.backward(dy, x, ids, s, w13, w2, rc)):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-10)
