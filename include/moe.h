@@ -151,6 +151,17 @@ moe_status moe_prepare_weights(moe_plan_t plan, const void* w13, const void* w2,
                                void* q13, void* s13, void* q2, void* s2,
                                hipStream_t stream);
 
+/* MXFP8 quantization of bf16 rows src [R, n] of a routed layer (R = the
+ * valid routes of route_ws; n % 128 == 0), explainer section 02.  kind 0:
+ * 1x32 row blocks -> q [R, n] E4M3 bytes, sc [R, n/32] E8M0 bytes.  kind 1:
+ * column bundles, 32x1 blocks down each expert's rows padded to Mp_e =
+ * counts[e] rounded up to 32 -> for expert e, q[n*poffsets[e] + c*Mp_e + m]
+ * and sc[n*poffsets[e]/32 + c*Mp_e/32 + m/32]; pad rows are +0.  E8M0 byte =
+ * e + 127 where e is the smallest integer with amax <= 448 * 2^e (clamped to
+ * [-127, 127]); E4M3 values are rounded to nearest even. */
+moe_status moe_mx_quantize(moe_plan_t plan, void* route_ws, const void* src, int32_t n,
+                           int32_t kind, void* q, void* sc, hipStream_t stream);
+
 /* Routing metadata (grouped-GEMM blog section 2 "Packing"): per-expert row
  * counts, exclusive prefix offsets, the stable expert-major order of valid
  * routes (ascending r = t*K + k inside an expert) and its inverse, and the

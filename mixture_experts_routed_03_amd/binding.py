@@ -76,6 +76,7 @@ _SIGS = {
     "moe_arena_reset": [_P, _P, _P],
     "moe_route_readback": [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(ctypes.c_int32), _P],
     "moe_saved_ptrs": [_P, _P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P],
+    "moe_mx_quantize": [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P],
     "moe_timing_enable": [_P, ctypes.c_int32],
     "moe_timing_read": [_P, ctypes.c_int32, ctypes.c_char_p, ctypes.c_size_t,
                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
@@ -214,6 +215,16 @@ def moe_saved_ptrs(plan, route_ws, stream=None):
     return xr.value, h1.value
 
 
+def moe_prepare_weights(plan, w13, w2, q13, s13, q2, s2, stream=None):
+    _check(lib().moe_prepare_weights(plan, _ptr(w13), _ptr(w2), _ptr(q13), _ptr(s13), _ptr(q2),
+                                     _ptr(s2), _stream(stream)), "moe_prepare_weights")
+
+
+def moe_mx_quantize(plan, route_ws, src, n, kind, q, sc, stream=None):
+    _check(lib().moe_mx_quantize(plan, _ptr(route_ws), _ptr(src), int(n), int(kind), _ptr(q),
+                                 _ptr(sc), _stream(stream)), "moe_mx_quantize")
+
+
 def moe_timing_enable(plan, enable=True):
     _check(lib().moe_timing_enable(plan, int(bool(enable))), "moe_timing_enable")
 
@@ -258,6 +269,27 @@ class MoeLayer:
         self.scratch = _bytes(self.sizes["scratch"], self.device)
         self.arena = _bytes(self.sizes["arena"], self.device) if training else None
         self.route_ws, self.h3 = self.new_layer_buffers()
+        self.prepared = None
+
+    def prepare(self, w13, w2):
+        """MXFP8: quantize bf16 weights once into E4M3 + 32x32 E8M0 scales."""
+        E, D, F = self.E, self.D, self.F
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        q13 = torch.empty((E, 2 * F, D), **u8)
+        s13 = torch.empty((E, 2 * F // 32, D // 32), **u8)
+        q2 = torch.empty((E, D, F), **u8)
+        s2 = torch.empty((E, D // 32, F // 32), **u8)
+        moe_prepare_weights(self.plan, w13, w2, q13, s13, q2, s2)
+        self.prepared = (q13, s13, q2, s2)
+        return self.prepared
+
+    def _w(self, w13, w2, prepared=None):
+        prep = prepared if prepared is not None else self.prepared
+        if self.prec == "mxfp8":
+            if prep is None:
+                raise RuntimeError("MXFP8 layer: call prepare(w13, w2) first")
+            return (w13, w2) + tuple(prep)
+        return (w13, w2)
 
     def new_layer_buffers(self):
         route_ws = _bytes(self.sizes["route_ws"], self.device)
@@ -271,19 +303,37 @@ class MoeLayer:
         T = ids.shape[0]
         moe_route(self.plan, T, ids, self.route_ws if route_ws is None else route_ws)
 
-    def forward(self, x, w13, w2, layer=0, route_ws=None, h3=None):
+    def forward(self, x, w13, w2, layer=0, route_ws=None, h3=None, prepared=None):
         moe_expert_fwd(self.plan, layer, self.route_ws if route_ws is None else route_ws, x,
-                       (w13, w2), self.h3 if h3 is None else h3, self.arena, self.scratch)
+                       self._w(w13, w2, prepared), self.h3 if h3 is None else h3, self.arena,
+                       self.scratch)
 
     def combine(self, scores, y, y_addend=None, route_ws=None, h3=None):
         moe_combine(self.plan, self.route_ws if route_ws is None else route_ws, scores,
                     self.h3 if h3 is None else h3, y_addend, y)
 
     def backward(self, x, scores, dy, w13, w2, dx, dw13, dw2, dscores=None, layer=0, flags=0,
-                 route_ws=None, h3=None):
+                 route_ws=None, h3=None, prepared=None):
         moe_expert_bwd(self.plan, layer, self.route_ws if route_ws is None else route_ws, x,
-                       scores, dy, (w13, w2), self.h3 if h3 is None else h3, self.arena,
-                       self.scratch, dx, dw13, dw2, dscores, flags)
+                       scores, dy, self._w(w13, w2, prepared), self.h3 if h3 is None else h3,
+                       self.arena, self.scratch, dx, dw13, dw2, dscores, flags)
+
+    def quantize(self, src, kind, route_ws=None):
+        """MXFP8 codes of bf16 rows src [R, n]: kind 0 = 1x32 row blocks,
+        1 = per-expert column bundles (see moe_mx_quantize)."""
+        n = src.shape[1]
+        rb = self.readback(self.T_max, route_ws)
+        if kind == 0:
+            R = src.shape[0]
+            q = torch.zeros((R, n), dtype=torch.uint8, device=self.device)
+            sc = torch.zeros((R, n // 32), dtype=torch.uint8, device=self.device)
+        else:
+            Rp = int(rb["poffsets"][-1])
+            q = torch.zeros((max(1, n * Rp),), dtype=torch.uint8, device=self.device)
+            sc = torch.zeros((max(1, n * Rp // 32),), dtype=torch.uint8, device=self.device)
+        moe_mx_quantize(self.plan, self.route_ws if route_ws is None else route_ws, src, n, kind,
+                        q, sc)
+        return q, sc, rb
 
     def status(self, route_ws=None):
         return moe_read_status(self.route_ws if route_ws is None else route_ws)

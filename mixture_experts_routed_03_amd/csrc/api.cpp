@@ -37,6 +37,12 @@ hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_
 hipError_t launch_gemm_fwd(int prec, int mode, const FwdArgs& a, int64_t mt_max, int cus,
                            hipStream_t s);
 hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hipStream_t s);
+hipError_t launch_prep_w(const void* w, void* q, void* s, int E, int N, int K, hipStream_t st);
+hipError_t launch_rowq(const RowqArgs& a, int64_t R_max, hipStream_t st);
+hipError_t launch_colq(const ColqArgs& a, int64_t Rpad_max, hipStream_t st);
+hipError_t launch_mx_fwd(int mode, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s);
+hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s);
+hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStream_t s);
 hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s);
 }  // namespace moe
 
@@ -46,6 +52,7 @@ struct moe_plan_s {
   moe_desc d;
   int es;                 // activation element bytes
   int64_t R_max;          // t_max * K
+  int64_t Rp_max;         // upper bound on rows padded to 32 per expert
   int64_t mt_max;         // upper bound on m-tiles
   RouteLayout rl;
   ScratchLayout sl;
@@ -124,6 +131,109 @@ T* at(void* base, int64_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
 }
 
+
+// MXFP8 forward up to h2 (after the gather): x rows -> 1x32 blocks (and the x
+// column bundle in training), the W13 grouped GEMM with the SwiGLU epilogue,
+// and the h2 column bundle in training.  replay_only = 1 runs the same
+// launches as backward's replay predicate.
+hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const moe_weights* w,
+                          int replay_only, int cus, hipStream_t s) {
+  const moe_desc& d = p->d;
+  const ScratchLayout& L = p->sl;
+  const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
+  const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
+  const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
+  const char* tag = replay_only ? "replay_quant_x" : "quant_x";
+  RowqArgs rx{hdr, sc + L.x_rows, reinterpret_cast<uint8_t*>(sc + L.qx),
+              reinterpret_cast<uint8_t*>(sc + L.sx), d.d, -1, -1, -1, replay_only};
+  hipError_t e = timed(p, tag, s, [&] { return launch_rowq(rx, p->R_max, s); });
+  if (e != hipSuccess) return e;
+  if (d.training) {
+    ColqArgs cx{hdr, offsets, poffsets, sc + L.x_rows, nullptr, nullptr, d.d, d.e,
+                -1, 0, 1, replay_only};
+    e = timed(p, replay_only ? "replay_bundle_x" : "bundle_x", s,
+              [&] { return launch_colq(cx, p->Rp_max, s); });
+    if (e != hipSuccess) return e;
+  }
+  MxArgs a13{hdr, offsets, poffsets, mtoff, sorted_route,
+             reinterpret_cast<const uint8_t*>(sc + L.qx), reinterpret_cast<const uint8_t*>(sc + L.sx),
+             reinterpret_cast<const uint8_t*>(w->q13), reinterpret_cast<const uint8_t*>(w->s13),
+             nullptr, nullptr, nullptr, sc + L.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, 0, -1,
+             replay_only};
+  e = timed(p, replay_only ? "replay_w13" : "w13_swiglu", s,
+            [&] { return launch_mx_fwd(0, a13, p->mt_max, cus, s); });
+  if (e != hipSuccess) return e;
+  if (d.training) {
+    ColqArgs ch{hdr, offsets, poffsets, sc + L.h2, nullptr, nullptr, d.f, d.e, -1, 2, 3, replay_only};
+    e = timed(p, replay_only ? "replay_bundle_h2" : "bundle_h2", s,
+              [&] { return launch_colq(ch, p->Rp_max, s); });
+  }
+  return e;
+}
+
+
+// MXFP8 backward after the replay gather: replay of the quantized forward
+// state when needed, combine backward, both DGRADs on 1x32-quantized
+// gradients with the shared 32x32 weights, both WGRADs on column bundles.
+moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const moe_weights* w,
+                       const float* scores, const void* dy, const void* h3, void* arena,
+                       const moe_grads* g, uint32_t flags, int cus, hipStream_t s) {
+  const moe_desc& d = p->d;
+  const ScratchLayout& L = p->sl;
+  const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
+  const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
+  const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
+  const int32_t* route_to_row = at<int32_t>(ws, p->rl.route_to_row);
+  const int dw_f32 = d.dw_dtype == MOE_DTYPE_F32;
+  auto u8 = [&](int64_t off) { return reinterpret_cast<uint8_t*>(sc + off); };
+  hipError_t e = mx_forward_w13(p, hdr, ws, sc, w, 1, cus, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = timed(p, "combine_bwd", s, [&] {
+    return launch_combine_bwd(d.prec, hdr, route_to_row, scores, dy, h3, sc + L.dh3, g->dscores,
+                              d.k, d.d, d.t_max, s);
+  });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  RowqArgs r3{hdr, sc + L.dh3, u8(L.qdh3), u8(L.sdh3), d.d, -1, -1, -1, 0};
+  e = timed(p, "quant_dh3", s, [&] { return launch_rowq(r3, p->R_max, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  ColqArgs c3{hdr, offsets, poffsets, sc + L.dh3, u8(L.dh3cq), u8(L.dh3cs), d.d, d.e, -1, -1, -1, 0};
+  e = timed(p, "bundle_dh3", s, [&] { return launch_colq(c3, p->Rp_max, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  MxArgs dg2{hdr, offsets, poffsets, mtoff, sorted_route, u8(L.qdh3), u8(L.sdh3),
+             reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
+             nullptr, nullptr, sc + L.dh1, nullptr, d.d, d.f, d.f, d.f / 128, d.e, 0, 0, -1, 0};
+  e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_mx_dgrad(0, dg2, p->mt_max, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  MxArgs wg2{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
+             u8(L.dh3cq), u8(L.dh3cs), g->dw2, nullptr, 0, 0, d.f, 0, d.e, d.f, d.d, 2, 0};
+  e = timed(p, "w2_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 2, wg2, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  RowqArgs r1{hdr, sc + L.dh1, u8(L.qdh1), u8(L.sdh1), 2 * d.f, -1, -1, -1, 0};
+  e = timed(p, "quant_dh1", s, [&] { return launch_rowq(r1, p->R_max, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  ColqArgs c1{hdr, offsets, poffsets, sc + L.dh1, u8(L.dh1cq), u8(L.dh1cs), 2 * d.f, d.e,
+              -1, -1, -1, 0};
+  e = timed(p, "bundle_dh1", s, [&] { return launch_colq(c1, p->Rp_max, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  MxArgs dg13{hdr, offsets, poffsets, mtoff, sorted_route, u8(L.qdh1), u8(L.sdh1),
+              reinterpret_cast<const uint8_t*>(w->q13), reinterpret_cast<const uint8_t*>(w->s13),
+              nullptr, nullptr, sc + L.dxr, nullptr, 2 * d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0};
+  e = timed(p, "w13_dgrad", s, [&] { return launch_mx_dgrad(1, dg13, p->mt_max, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  MxArgs wg13{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
+              u8(L.dh1cq), u8(L.dh1cs), g->dw13, nullptr, 0, 0, d.f, 0, d.e, d.d, 2 * d.f, 0, 0};
+  e = timed(p, "w13_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 13, wg13, cus, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = timed(p, "dx_reduce", s, [&] {
+    return launch_dx_reduce(d.prec, hdr, route_to_row, reinterpret_cast<float*>(sc + L.dxr), g->dx,
+                            d.k, d.d, d.t_max, (flags & MOE_BWD_ACCUMULATE_DX) ? 1 : 0, s);
+  });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(timed(p, "rewind", s, [&] { return launch_plan_rewind(hdr, arena, s); }));
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,7 +247,6 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
     return MOE_ERR_SHAPE;
   if (d.prec != MOE_PREC_F32 && d.prec != MOE_PREC_BF16 && d.prec != MOE_PREC_MXFP8)
     return MOE_ERR_ARG;
-  if (d.prec == MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
   if (d.dw_dtype != MOE_DTYPE_F32 && d.dw_dtype != MOE_DTYPE_BF16) return MOE_ERR_ARG;
   if (d.prec == MOE_PREC_F32 && d.dw_dtype != MOE_DTYPE_F32) return MOE_ERR_ARG;
   if (d.max_layers < 1 || d.arena_budget < 0) return MOE_ERR_ARG;
@@ -148,7 +257,9 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   p->es = d.prec == MOE_PREC_F32 ? 4 : 2;
   p->R_max = d.t_max * d.k;
   p->mt_max = std::min<int64_t>(p->R_max, (p->R_max + kBM - 1) / kBM + d.e);
-  const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es;
+  p->Rp_max = align_up(p->R_max + 31 * std::min<int64_t>(d.e, p->R_max), 32);
+  const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es, Rp = p->Rp_max;
+  const bool mx = d.prec == MOE_PREC_MXFP8;
 
   RouteLayout& L = p->rl;
   L.nchunks = (R + kRankChunk - 1) / kRankChunk;
@@ -165,21 +276,49 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   L.total = o;
 
   ScratchLayout& S = p->sl;
+  {
+    int64_t* all = &S.x_rows;
+    for (int i = 0; i < int(sizeof(ScratchLayout) / sizeof(int64_t)); ++i) all[i] = -1;
+  }
   o = 0;
-  S.x_rows = o; o = a256(o + R * D * es);
-  S.h1 = o; o = a256(o + R * 2 * F * es);
-  S.h2 = o; o = a256(o + R * F * es);
+  auto take = [&](int64_t& field, int64_t bytes) {
+    field = o;
+    o = a256(o + bytes);
+  };
+  take(S.x_rows, R * D * es);
+  take(S.h1, R * 2 * F * es);
+  take(S.h2, R * F * es);
+  if (mx) {
+    take(S.qx, R * D);
+    take(S.sx, R * D / 32);
+    take(S.qh2, R * F);
+    take(S.sh2, R * F / 32);
+    take(S.xcq, Rp * D);
+    take(S.xcs, Rp / 32 * D);
+    take(S.h2cq, Rp * F);
+    take(S.h2cs, Rp / 32 * F);
+  }
   if (d.training) {
-    S.dh3 = o; o = a256(o + R * D * es);
-    S.dh1 = o; o = a256(o + R * 2 * F * es);
-    S.dxr = o; o = a256(o + R * D * 4);
-  } else {
-    S.dh3 = S.dh1 = S.dxr = -1;
+    take(S.dh3, R * D * es);
+    take(S.dh1, R * 2 * F * es);
+    take(S.dxr, R * D * 4);
+    if (mx) {
+      take(S.qdh3, R * D);
+      take(S.sdh3, R * D / 32);
+      take(S.dh3cq, Rp * D);
+      take(S.dh3cs, Rp / 32 * D);
+      take(S.qdh1, R * 2 * F);
+      take(S.sdh1, R * 2 * F / 32);
+      take(S.dh1cq, Rp * 2 * F);
+      take(S.dh1cs, Rp / 32 * 2 * F);
+    }
   }
   S.total = std::max<int64_t>(o, 256);
 
   p->h3_bytes = std::max<int64_t>(a256(R * D * es), 256);
-  p->state_max = align128(R * D * es) + align128(R * 2 * F * es);
+  p->state_max = mx ? align128(Rp * D) + align128(Rp / 32 * D) + align128(R * 2 * F * 2) +
+                          align128(Rp * F) + align128(Rp / 32 * F)
+                    : align128(R * D * es) + align128(R * 2 * F * es);
   p->budget = d.arena_budget > 0 ? d.arena_budget : int64_t(d.max_layers) * p->state_max;
   p->arena_bytes = d.training ? kArenaHdrBytes + a256(p->budget) : kArenaHdrBytes;
   p->cus = 0;
@@ -195,6 +334,13 @@ moe_status moe_plan_sizes(moe_plan_t p, moe_sizes* s) {
   s->h3_slots = size_t(p->h3_bytes);
   s->arena = size_t(p->arena_bytes);
   s->layer_state_max = size_t(p->state_max);
+  if (p->d.prec == MOE_PREC_MXFP8) {
+    const int64_t E = p->d.e, D = p->d.d, F = p->d.f;
+    s->q13 = size_t(a256(E * 2 * F * D));
+    s->s13 = size_t(a256(E * 2 * F * D / 1024));
+    s->q2 = size_t(a256(E * D * F));
+    s->s2 = size_t(a256(E * D * F / 1024));
+  }
   return MOE_OK;
 }
 
@@ -256,10 +402,38 @@ void moe_plan_destroy(moe_plan_t p) {
   delete p;
 }
 
-moe_status moe_prepare_weights(moe_plan_t p, const void*, const void*, void*, void*, void*,
-                               void*, hipStream_t) {
+moe_status moe_prepare_weights(moe_plan_t p, const void* w13, const void* w2, void* q13,
+                               void* s13, void* q2, void* s2, hipStream_t s) {
   if (!p) return MOE_ERR_ARG;
-  return MOE_ERR_UNSUPPORTED;
+  if (p->d.prec != MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (!w13 || !w2 || !q13 || !s13 || !q2 || !s2) return MOE_ERR_ARG;
+  const moe_desc& d = p->d;
+  hipError_t e = timed(p, "prep_w13", s, [&] {
+    return launch_prep_w(w13, q13, s13, d.e, 2 * d.f, d.d, s);
+  });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(timed(p, "prep_w2", s, [&] {
+    return launch_prep_w(w2, q2, s2, d.e, d.d, d.f, s);
+  }));
+}
+
+moe_status moe_mx_quantize(moe_plan_t p, void* ws, const void* src, int32_t n, int32_t kind,
+                           void* q, void* sc, hipStream_t s) {
+  if (!p || !ws || !src || !q || !sc) return MOE_ERR_ARG;
+  if (n <= 0 || n % 128) return MOE_ERR_SHAPE;
+  RouteHdr* hdr = hdr_of(ws);
+  if (kind == 0) {
+    RowqArgs r{hdr, src, reinterpret_cast<uint8_t*>(q), reinterpret_cast<uint8_t*>(sc), n,
+               -1, -1, -1, 0};
+    return hip_status(launch_rowq(r, p->R_max, s));
+  }
+  if (kind == 1) {
+    ColqArgs c{hdr, at<int32_t>(ws, p->rl.offsets), at<int32_t>(ws, p->rl.poffsets), src,
+               reinterpret_cast<uint8_t*>(q), reinterpret_cast<uint8_t*>(sc), n, p->d.e,
+               -1, -1, -1, 0};
+    return hip_status(launch_colq(c, p->Rp_max, s));
+  }
+  return MOE_ERR_ARG;
 }
 
 moe_status moe_route(moe_plan_t p, int64_t T, const int32_t* ids, void* ws, hipStream_t s) {
@@ -273,34 +447,56 @@ moe_status moe_route(moe_plan_t p, int64_t T, const int32_t* ids, void* ws, hipS
 moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
                           const moe_weights* w, void* h3, void* arena, void* scratch,
                           hipStream_t s) {
-  if (!p || !ws || !w || !w->w13 || !w->w2 || !h3 || !scratch) return MOE_ERR_ARG;
-  if (layer < 0 || layer >= p->d.max_layers) return MOE_ERR_ARG;
-  if (!aligned16(x) || !aligned16(w->w13) || !aligned16(w->w2) ||
-      !aligned16(h3) || !aligned16(scratch) || !aligned16(ws))
-    return MOE_ERR_ARG;
-  if (p->d.training && arena && !aligned16(arena)) return MOE_ERR_ARG;
+  if (!p || !ws || !w || !h3 || !scratch) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
+  const bool mx = d.prec == MOE_PREC_MXFP8;
+  if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;
+  if (layer < 0 || layer >= d.max_layers) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(w->w13) || !aligned16(w->w2) || !aligned16(w->q13) ||
+      !aligned16(w->q2) || !aligned16(h3) || !aligned16(scratch) || !aligned16(ws))
+    return MOE_ERR_ARG;
+  if (d.training && arena && !aligned16(arena)) return MOE_ERR_ARG;
   RouteHdr* hdr = hdr_of(ws);
   char* sc = reinterpret_cast<char*>(scratch);
+  const ScratchLayout& L = p->sl;
   PlanArgs pa{layer, d.max_layers, d.training, p->es, d.d, d.f, p->budget,
-              uint64_t(d.training ? arena : nullptr), uint64_t(sc + p->sl.x_rows),
-              uint64_t(sc + p->sl.h1)};
+              uint64_t(d.training ? arena : nullptr), uint64_t(sc + L.x_rows), uint64_t(sc + L.h1),
+              mx ? 1 : 0, 0,
+              {mx ? uint64_t(sc + L.xcq) : 0, mx ? uint64_t(sc + L.xcs) : 0,
+               mx ? uint64_t(sc + L.h2cq) : 0, mx ? uint64_t(sc + L.h2cs) : 0}};
   hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
+  const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
+  const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
+  const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   e = timed(p, "gather", s,
             [&] { return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, p->R_max, 0, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int cus = plan_cus(p);
-  FwdArgs a13{hdr, at<int32_t>(ws, p->rl.offsets), at<int32_t>(ws, p->rl.mtoff), sorted_route,
-              nullptr, w->w13, nullptr, sc + p->sl.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e, 0};
-  e = timed(p, "w13_swiglu", s,
-            [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
+  if (!mx) {
+    FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
+                d.d, 2 * d.f, d.f, d.f / 64, d.e, 0};
+    e = timed(p, "w13_swiglu", s,
+              [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    FwdArgs a2{hdr, offsets, mtoff, sorted_route, sc + L.h2, w->w2, h3, nullptr,
+               d.f, d.d, d.f, d.d / 128, d.e, 0};
+    return hip_status(timed(p, "w2_scatter", s,
+                            [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
+  }
+  e = mx_forward_w13(p, hdr, ws, sc, w, 0, cus, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  FwdArgs a2{hdr, at<int32_t>(ws, p->rl.offsets), at<int32_t>(ws, p->rl.mtoff), sorted_route,
-             sc + p->sl.h2, w->w2, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0};
-  return hip_status(timed(p, "w2_scatter", s,
-                          [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
+  // h2 -> 1x32 row blocks for the W2 GEMM
+  RowqArgs rq{hdr, sc + L.h2, reinterpret_cast<uint8_t*>(sc + L.qh2),
+              reinterpret_cast<uint8_t*>(sc + L.sh2), d.f, -1, -1, -1, 0};
+  e = timed(p, "quant_h2", s, [&] { return launch_rowq(rq, p->R_max, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  MxArgs a2{hdr, offsets, poffsets, mtoff, sorted_route,
+            reinterpret_cast<const uint8_t*>(sc + L.qh2), reinterpret_cast<const uint8_t*>(sc + L.sh2),
+            reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
+            nullptr, nullptr, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0};
+  return hip_status(timed(p, "w2_scatter", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); }));
 }
 
 moe_status moe_combine(moe_plan_t p, void* ws, const float* scores, const void* h3,
@@ -321,9 +517,11 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
                           uint32_t flags, hipStream_t s) {
   if (!p || !ws || !w || !g || !scratch || !h3) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
-  if (!d.training || d.prec != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!d.training || d.prec == MOE_PREC_F32) return MOE_ERR_UNSUPPORTED;
   if (layer < 0 || layer >= d.max_layers) return MOE_ERR_ARG;
-  if (!w->w13 || !w->w2 || !g->dw13 || !g->dw2) return MOE_ERR_ARG;
+  const bool mx = d.prec == MOE_PREC_MXFP8;
+  if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;
+  if (!g->dw13 || !g->dw2) return MOE_ERR_ARG;
   if (!aligned16(ws) || !aligned16(x) || !aligned16(dy) || !aligned16(w->w13) ||
       !aligned16(w->w2) || !aligned16(h3) || !aligned16(scratch) || !aligned16(g->dx) ||
       !aligned16(g->dw13) || !aligned16(g->dw2) || !aligned16(arena))
@@ -346,6 +544,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, p->R_max, 1, s);
   });
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (mx) return mx_backward(p, hdr, ws, sc, w, scores, dy, h3, arena, g, flags, cus, s);
   FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
               d.d, 2 * d.f, d.f, d.f / 64, d.e, 1};
   e = timed(p, "replay_w13", s, [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });

@@ -61,9 +61,14 @@ struct RouteLayout {
   int64_t nchunks;
 };
 
-// Byte offsets inside the scratch buffer (regions sized for R = t_max*K).
+// Byte offsets inside the scratch buffer (regions sized for R = t_max*K and
+// the padded row count Rp; -1 = region absent).
 struct ScratchLayout {
-  int64_t x_rows, h1, h2, dh3, dh1, dxr, total;
+  int64_t x_rows, h1, h2, dh3, dh1, dxr;
+  // MXFP8: row-quantized operands (codes, exponents) and column bundles
+  int64_t qx, sx, qh2, sh2, xcq, xcs, h2cq, h2cs;
+  int64_t qdh3, sdh3, dh3cq, dh3cs, qdh1, sdh1, dh1cq, dh1cs;
+  int64_t total;
 };
 
 // Arguments of the grouped forward GEMM launches.
@@ -102,6 +107,50 @@ struct BwdArgs {
   int a_ld, b_ld;       // WGRAD row lengths of the A rows (= dW row length) and B rows (= dW rows)
 };
 
+// Arguments of the MXFP8 grouped GEMM launches.
+struct MxArgs {
+  const RouteHdr* hdr;
+  const int32_t* offsets;
+  const int32_t* poffsets;
+  const int32_t* mtoff;
+  const int32_t* sorted_route;
+  const uint8_t* qa;    // FPROP/DGRAD: row-quantized token operand [R, Kd]; WGRAD: A column bundle
+  const uint8_t* sa;    //   exponents [R, Kd/32] / A bundle exponents
+  const uint8_t* qw;    // FPROP/DGRAD: E4M3 weights [E, N, Kd] (DGRAD: [E, Kd, N])
+  const uint8_t* sw;    //   32x32 exponents
+  const uint8_t* qb;    // WGRAD: B column bundle
+  const uint8_t* sb;
+  void* out0;           // h1 (null = record) / h3 slots / dH1 / dXr / dW
+  void* out1;           // h2 (W13 forward)
+  int Kd, N, F, NT, E;
+  int a_ld, b_ld;       // WGRAD row lengths of A (= dW row length) and B (= dW rows)
+  int a_slot;           // WGRAD: >= 0 takes A codes/exponents from record aux[a_slot], aux[a_slot+1]
+  int replay_only;
+};
+
+// Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:
+// 0..5 = rec.aux[slot], 6 = rec.x_rows, 7 = rec.h1).
+struct RowqArgs {
+  const RouteHdr* hdr;
+  const void* src;      // bf16 [R, N]
+  uint8_t* q;           // [R, N]
+  uint8_t* s;           // [R, N/32]
+  int N;
+  int src_slot, q_slot, s_slot;
+  int replay_only;
+};
+struct ColqArgs {
+  const RouteHdr* hdr;
+  const int32_t* offsets;
+  const int32_t* poffsets;
+  const void* src;      // bf16 [R, N]
+  uint8_t* q;           // column-bundle codes (sum_e N * Mp_e bytes)
+  uint8_t* s;           // column-bundle exponents (sum_e N * Mp_e / 32 bytes)
+  int N, E;
+  int src_slot, q_slot, s_slot;
+  int replay_only;
+};
+
 // Arguments of the device planner (one layer).
 struct PlanArgs {
   int32_t layer, max_layers, training, es, D, F;
@@ -109,6 +158,9 @@ struct PlanArgs {
   uint64_t arena;           // device base of the arena (0 when none)
   uint64_t scratch_x_rows;  // scratch regions used when state is not saved
   uint64_t scratch_h1;
+  int32_t mx;               // MXFP8 layer: state = x/h2 column bundles + h1
+  int32_t pad0;
+  uint64_t scratch_aux[4];  // x bundle codes/exponents, h2 bundle codes/exponents
 };
 
 // ------------------------------------------------------------ device utils

@@ -1,0 +1,719 @@
+// Grouped GEMMs of the expert FFN with MXFP8 operands on gfx950
+// (v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 x E4M3 with one E8M0 scale per 32
+// values of each operand, fp32 accumulation).
+//
+// Dist-MoE explainer section 02: forward GEMMs contract over features with
+// 1x32 activation blocks; weights are prepared in 32x32 blocks so the forward
+// and the input-gradient GEMM read the same E4M3 values with the scale matrix
+// read in the other orientation; weight gradients contract over token rows
+// and read column bundles (32x1 blocks down each expert's padded rows).
+// "Mixture of Experts: How Routing Becomes GPU Computation", section 2: the
+// grouped GEMM and its two gradients.
+//
+//   k_mx_fwd<0>: h1 = Xq W13q^T per expert (+ SwiGLU epilogue -> h1, h2 bf16)
+//   k_mx_fwd<1>: h3 = H2q W2q^T per expert -> route slots (bf16)
+//   k_mx_dgrad<0>: dH2 = dH3q W2q (contraction over D) + SwiGLU backward -> dH1
+//   k_mx_dgrad<1>: dXr = dH1q W13q (contraction over 2F) -> fp32 rows
+//   k_mx_wgrad:  dW[b][a] = sum_m B[m][b] A[m][a] from column bundles
+//
+// MFMA operand layout (measured on gfx950): one MFMA covers 64 contraction
+// values of a row, held by lanes r and r + 32 with 32 bytes each; scale block
+// b is bytes [16b, 16b + 16) of both lanes, and its E8M0 scale is the one
+// supplied by lane r + 32b.  So lane (r, h) carries 16 values of each of the
+// two MX blocks of the step: contraction chunks h and 2 + h (16 values each),
+// and supplies the scale of block h.
+//
+// MI355X design: the same coalesced, XOR-swizzled LDS staging as the BF16
+// kernels (128-byte row segments per stage; fp8 stages span 128 contraction
+// values).  DGRAD transposes the E4M3 weight tile in registers (a 4x4 byte
+// transpose of four rows with v_perm_b32) before writing it to LDS, so one
+// copy of the E4M3 weights serves forward and backward.
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void mfma_mx(f32x16& acc, u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1,
+                                        int sa, int sb) {
+  const i32x8 a = {int(a0[0]), int(a0[1]), int(a0[2]), int(a0[3]),
+                   int(a1[0]), int(a1[1]), int(a1[2]), int(a1[3])};
+  const i32x8 b = {int(b0[0]), int(b0[1]), int(b0[2]), int(b0[3]),
+                   int(b1[0]), int(b1[1]), int(b1[2]), int(b1[3])};
+  // cbsz = blgp = 0: both operands E4M3; opsel 0: scale in byte 0.
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ int byte_of(uint32_t w, int i) { return int((w >> (8 * i)) & 0xffu); }
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
+__device__ __forceinline__ int tsw(int o, int kq) {
+  return o * 32 + ((((kq >> 2) ^ o ^ (o >> 3)) & 7) << 2) + (kq & 3);
+}
+__device__ __forceinline__ int tsw_g(int o, int g) { return o * 32 + (((g ^ o ^ (o >> 3)) & 7) << 2); }
+// 64-byte rows (WGRAD): 16-byte chunk ch of row r
+__device__ __forceinline__ int swz64(int r, int ch) { return r * 64 + ((ch ^ ((r >> 2) & 3)) << 4); }
+
+__device__ __forceinline__ int find_expert_m(const int32_t* __restrict__ mtoff, int E, int NT,
+                                             int w) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (mtoff[mid] * NT <= w)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c,
+                                                 float d) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 v;
+  v[0] = pack_bf16x2(a, b);
+  v[1] = pack_bf16x2(c, d);
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+__device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  f[0] = __uint_as_float(v[0] << 16);
+  f[1] = __uint_as_float(v[0] & 0xffff0000u);
+  f[2] = __uint_as_float(v[1] << 16);
+  f[3] = __uint_as_float(v[1] & 0xffff0000u);
+}
+
+// ------------------------------------------------------------------ forward
+template <int MODE>
+__global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
+  constexpr int kW = 128 * 128;      // weight stage: 128 rows x 128 E4M3 values
+  constexpr int kA = kBM * 128;      // token stage: 64 rows x 128 values
+  constexpr int kSc = kBM * 4;       // token scales of the stage: 4 blocks per row
+  constexpr int kStage = kW + kA + kSc;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int lc = tid & 7;
+  const int lrow = tid >> 3;
+
+  const RouteHdr* hdr = a.hdr;
+  if (a.replay_only && !hdr->rec.replay) return;
+  const int n_items = hdr->n_mt * a.NT;
+  uint16_t* out0 = reinterpret_cast<uint16_t*>(a.out0 ? a.out0 : (void*)hdr->rec.h1);
+  uint16_t* out1 = reinterpret_cast<uint16_t*>(a.out1);
+  const int Kd = a.Kd;
+  const int KB = Kd / 32;           // scale bytes per row
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per = gridDim.x / kXcds;
+  const int chunk = (n_items + kXcds - 1) / kXcds;
+  const int S = Kd / 128;
+
+  for (int it = slot; it < chunk; it += per) {
+    const int w = xcd * chunk + it;
+    if (w >= n_items) break;
+    const int e = find_expert_m(a.mtoff, a.E, a.NT, w);
+    const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
+    const int u = w - a.mtoff[e] * a.NT;
+    const int nt = u / mt_e;
+    const int mt = u - nt * mt_e;
+    const int row0 = a.offsets[e] + mt * kBM;
+    const int rows = min(kBM, a.offsets[e + 1] - row0);
+    const bool two = rows > 32;
+
+    const uint8_t* wsrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rho = lrow + 32 * j;
+      const int wr = MODE == 0 ? (rho < 64 ? nt * 64 + rho : a.F + nt * 64 + rho - 64)
+                               : nt * 128 + rho;
+      wsrc[j] = a.qw + (int64_t(e) * a.N + wr) * Kd + lc * 16;
+    }
+    // the 32 weight rows of this wave form one 32-row scale block
+    const int wrow0 = MODE == 0 ? ((wave < 2 ? 0 : a.F) + nt * 64 + (wave & 1) * 32)
+                                : nt * 128 + wave * 32;
+    const uint32_t* wsc_src = reinterpret_cast<const uint32_t*>(
+        a.sw + (int64_t(e) * (a.N / 32) + wrow0 / 32) * KB);
+    const uint8_t* tsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = lrow + 32 * j;
+      tsrc[j] = r < rows ? a.qa + int64_t(row0 + r) * Kd + lc * 16 : nullptr;
+    }
+    const uint32_t* tsc_src =
+        tid < rows ? reinterpret_cast<const uint32_t*>(a.sa + int64_t(row0 + tid) * KB) : nullptr;
+
+    f32x16 acc0 = {}, acc1 = {};
+    u32x4 R0[6], R1[6];
+    uint32_t S0[2], S1[2];   // [0] weight scales of the wave, [1] token scales of row tid
+    uint32_t wsc[2];
+    auto load = [&](u32x4* R, uint32_t* Sc, int s) {
+      const int64_t off = int64_t(s) * 128;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) R[j] = *reinterpret_cast<const u32x4*>(wsrc[j] + off);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        R[4 + j] = tsrc[j] ? *reinterpret_cast<const u32x4*>(tsrc[j] + off) : u32x4{0u, 0u, 0u, 0u};
+      Sc[0] = wsc_src[s];
+      Sc[1] = tsc_src ? tsc_src[s] : 0x7f7f7f7fu;
+    };
+    auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
+      char* base = lds + buf * kStage;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x4*>(base + swz(lrow + 32 * j, lc)) = R[j];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
+      if (tid < kBM) reinterpret_cast<uint32_t*>(base + kW + kA)[tid] = Sc[1];
+      wsc[buf] = Sc[0];
+    };
+    auto compute = [&](int buf) {
+      const char* wl = lds + buf * kStage;
+      const char* tl = wl + kW;
+      const uint32_t* tsc = reinterpret_cast<const uint32_t*>(tl + kA);
+      const uint32_t ts0 = tsc[lr];
+      const uint32_t ts1 = tsc[32 + lr];
+      const int wrow = 32 * wave + lr;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ca = 4 * q + lh, cb = 4 * q + 2 + lh;
+        const int blk = 2 * q + lh;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, ca));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, cb));
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(tl + swz(lr, ca));
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(tl + swz(lr, cb));
+        const int sa = byte_of(wsc[buf], blk);
+        mfma_mx(acc0, a0, a1, b0, b1, sa, byte_of(ts0, blk));
+        if (two) {
+          const u32x4 d0 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, ca));
+          const u32x4 d1 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, cb));
+          mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
+        }
+      }
+    };
+
+    load(R0, S0, 0);
+    if (S > 1) load(R1, S1, 1);
+    store(R0, S0, 0);
+    if (S > 2) load(R0, S0, 2);
+    lds_barrier();
+    for (int s = 0; s < S; s += 2) {
+      compute(0);
+      if (s + 1 < S) {
+        store(R1, S1, 1);
+        if (s + 3 < S) load(R1, S1, s + 3);
+      }
+      lds_barrier();
+      if (s + 1 >= S) break;
+      compute(1);
+      if (s + 2 < S) {
+        store(R0, S0, 0);
+        if (s + 4 < S) load(R0, S0, s + 4);
+      }
+      lds_barrier();
+    }
+
+    // Epilogue (as the BF16 kernels): acc[b][v] = C[row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
+    if (MODE == 0) {
+      const int F = a.F;
+      const int ncol = (wave < 2 ? 0 : F) + nt * 64 + (wave & 1) * 32 + 4 * lh;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const f32x16& acc = b ? acc1 : acc0;
+        const int m = 32 * b + lr;
+        if (m < rows) {
+          uint16_t* o = out0 + int64_t(row0 + m) * (2 * F) + ncol;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store4<uint16_t>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+      }
+      float* xch = reinterpret_cast<float*>(lds);
+      if (wave >= 2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          xch[(((wave - 2) * 2 + 0) * 16 + v) * 64 + lane] = round_bf16(acc0[v]);
+          xch[(((wave - 2) * 2 + 1) * 16 + v) * 64 + lane] = round_bf16(acc1[v]);
+        }
+      }
+      lds_barrier();
+      if (wave < 2) {
+        const int jcol = nt * 64 + wave * 32 + 4 * lh;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const f32x16& acc = b ? acc1 : acc0;
+          const int m = 32 * b + lr;
+          if (m < rows) {
+            float h[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              h[v] = silu_f(round_bf16(acc[v])) * xch[((wave * 2 + b) * 16 + v) * 64 + lane];
+            uint16_t* o = out1 + int64_t(row0 + m) * F + jcol;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              store4<uint16_t>(o + 8 * g, h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
+          }
+        }
+      }
+      lds_barrier();
+    } else {
+      const int ncol = nt * 128 + wave * 32 + 4 * lh;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const f32x16& acc = b ? acc1 : acc0;
+        const int m = 32 * b + lr;
+        if (m < rows) {
+          const int64_t slotr = a.sorted_route[row0 + m];
+          uint16_t* o = out0 + slotr * a.N + ncol;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store4<uint16_t>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ DGRAD
+// 4x4 byte transpose: out[j] = (r0.byte j, r1.byte j, r2.byte j, r3.byte j).
+__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                             uint32_t* out) {
+  const uint32_t t01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
+  const uint32_t t23 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);  // r2.b0 r3.b0 r2.b1 r3.b1
+  const uint32_t u01 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
+  const uint32_t u23 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(u23, u01, 0x07060302u);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
+  constexpr int kW = 128 * 32 * 4;   // transposed weight stage: 128 columns x 128 values
+  constexpr int kT = kBM * 128;      // token stage
+  constexpr int kSc = kBM * 4;
+  constexpr int kStage = kW + kT + kSc;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int c16 = tid & 7;    // weight loader: 16-column chunk of a 128-byte row segment
+  const int kq = tid >> 3;    // weight loader: rows 4kq .. 4kq+3 of the stage
+  const int lc = tid & 7;
+  const int lrow = tid >> 3;
+
+  const RouteHdr* hdr = a.hdr;
+  const int n_items = hdr->n_mt * a.NT;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per = gridDim.x / kXcds;
+  const int chunk = (n_items + kXcds - 1) / kXcds;
+  const int Kd = a.Kd;
+  const int KB = Kd / 32;
+  const int S = Kd / 128;
+  const int64_t N = a.N;
+  const uint16_t* h1 = reinterpret_cast<const uint16_t*>(hdr->rec.h1);
+
+  for (int it = slot; it < chunk; it += per) {
+    const int w = xcd * chunk + it;
+    if (w >= n_items) break;
+    const int e = find_expert_m(a.mtoff, a.E, a.NT, w);
+    const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
+    const int u = w - a.mtoff[e] * a.NT;
+    const int nt = u / mt_e;
+    const int mt = u - nt * mt_e;
+    const int row0 = a.offsets[e] + mt * kBM;
+    const int rows = min(kBM, a.offsets[e + 1] - row0);
+    const bool two = rows > 32;
+
+    const uint8_t* wsrc = a.qw + (int64_t(e) * Kd + 4 * kq) * N + nt * 128 + c16 * 16;
+    // the wave's 32 output columns are one scale column block; 4 blocks along k per stage
+    const uint8_t* wsc_src = a.sw + int64_t(e) * KB * (N / 32) + (nt * 128 + 32 * wave) / 32;
+    const uint8_t* tsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = lrow + 32 * j;
+      tsrc[j] = r < rows ? a.qa + int64_t(row0 + r) * Kd + lc * 16 : nullptr;
+    }
+    const uint32_t* tsc_src =
+        tid < rows ? reinterpret_cast<const uint32_t*>(a.sa + int64_t(row0 + tid) * KB) : nullptr;
+
+    f32x16 acc0 = {}, acc1 = {};
+    u32x4 R0[6], R1[6];
+    uint32_t S0[2], S1[2];
+    uint32_t wsc[2];
+    auto load = [&](u32x4* R, uint32_t* Sc, int s) {
+      const uint8_t* p = wsrc + int64_t(s) * 128 * N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R[i] = *reinterpret_cast<const u32x4*>(p + i * N);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        R[4 + j] = tsrc[j] ? *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128)
+                           : u32x4{0u, 0u, 0u, 0u};
+      uint32_t ws = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ws |= uint32_t(wsc_src[int64_t(4 * s + i) * (N / 32)]) << (8 * i);
+      Sc[0] = ws;
+      Sc[1] = tsc_src ? tsc_src[s] : 0x7f7f7f7fu;
+    };
+    auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
+      uint32_t* la = reinterpret_cast<uint32_t*>(lds + buf * kStage);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t d[4];
+        transpose4x4(R[0][i], R[1][i], R[2][i], R[3][i], d);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) la[tsw(c16 * 16 + 4 * i + j, kq)] = d[j];
+      }
+      char* lt = lds + buf * kStage + kW;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
+      if (tid < kBM) reinterpret_cast<uint32_t*>(lt + kT)[tid] = Sc[1];
+      wsc[buf] = Sc[0];
+    };
+    auto compute = [&](int buf) {
+      const char* la = lds + buf * kStage;
+      const char* lt = la + kW;
+      const uint32_t* tsc = reinterpret_cast<const uint32_t*>(lt + kT);
+      const uint32_t ts0 = tsc[lr];
+      const uint32_t ts1 = tsc[32 + lr];
+      const int orow = 32 * wave + lr;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ga = 4 * q + lh, gb = 4 * q + 2 + lh;
+        const int blk = 2 * q + lh;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(la + tsw_g(orow, ga) * 4);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + tsw_g(orow, gb) * 4);
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lt + swz(lr, ga));
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(lt + swz(lr, gb));
+        const int sa = byte_of(wsc[buf], blk);
+        mfma_mx(acc0, a0, a1, b0, b1, sa, byte_of(ts0, blk));
+        if (two) {
+          const u32x4 d0 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, ga));
+          const u32x4 d1 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, gb));
+          mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
+        }
+      }
+    };
+
+    load(R0, S0, 0);
+    if (S > 1) load(R1, S1, 1);
+    store(R0, S0, 0);
+    if (S > 2) load(R0, S0, 2);
+    lds_barrier();
+    for (int s = 0; s < S; s += 2) {
+      compute(0);
+      if (s + 1 < S) {
+        store(R1, S1, 1);
+        if (s + 3 < S) load(R1, S1, s + 3);
+      }
+      lds_barrier();
+      if (s + 1 >= S) break;
+      compute(1);
+      if (s + 2 < S) {
+        store(R0, S0, 0);
+        if (s + 4 < S) load(R0, S0, s + 4);
+      }
+      lds_barrier();
+    }
+
+    const int col = nt * 128 + 32 * wave + 4 * lh;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x16& acc = b ? acc1 : acc0;
+      const int m = 32 * b + lr;
+      if (m >= rows) continue;
+      const int64_t row = row0 + m;
+      if (KIND == 0) {
+        const int F = a.F;
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out0) + row * (2 * F);
+        const uint16_t* hr = h1 + row * (2 * F);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int j = col + 8 * g4;
+          float gv[4], uv[4], dg[4], du[4];
+          load4_bf16(hr + j, gv);
+          load4_bf16(hr + F + j, uv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float dh2 = acc[4 * g4 + i];
+            const float sg = sigmoid_f(gv[i]);
+            dg[i] = dh2 * uv[i] * (sg * (1.0f + gv[i] * (1.0f - sg)));
+            du[i] = dh2 * silu_f(gv[i]);
+          }
+          store4<uint16_t>(o + j, dg[0], dg[1], dg[2], dg[3]);
+          store4<uint16_t>(o + F + j, du[0], du[1], du[2], du[3]);
+        }
+      } else {
+        float* o = reinterpret_cast<float*>(a.out0) + row * N;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          store4<float>(o + col + 8 * g4, acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2],
+                        acc[4 * g4 + 3]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ WGRAD
+// A and B are column bundles: for expert e, the codes of column c are the Mp
+// bytes at base + N*poffsets[e] + c*Mp (Mp = padded rows of e), exponents at
+// sbase + N*poffsets[e]/32 + c*Mp/32.
+__device__ __forceinline__ uint64_t rec_ptr_m(const RouteHdr* h, int slot) {
+  if (slot == 6) return h->rec.x_rows;
+  if (slot == 7) return h->rec.h1;
+  return h->rec.aux[slot];
+}
+
+template <typename TW, int TAG>
+__global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
+  constexpr int kOp = 128 * 64;                        // one operand stage: 128 columns x 64 rows
+  constexpr int kRowB = 128 * int(sizeof(TW)) + 16;
+  constexpr int kHalves = sizeof(TW) == 4 ? 2 : 1;
+  constexpr int kRowsPerPass = 128 / kHalves;
+  constexpr int kOut = kRowsPerPass * kRowB;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kOp + kOut];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int ch = tid & 3;      // loader: 16-byte chunk of a 64-byte column segment
+  const int lrow = tid >> 2;   // loader: column (+ 64 j) of the 128-column tile
+
+  const RouteHdr* hdr = a.hdr;
+  const int a_ld = a.a_ld, b_ld = a.b_ld;
+  const int NA = a_ld / 128, NB = b_ld / 128;
+  const int per_e = NA * NB;
+  const int n_items = a.E * per_e;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per = gridDim.x / kXcds;
+  const int chunk = (n_items + kXcds - 1) / kXcds;
+  const uint8_t* qa = a.a_slot >= 0 ? reinterpret_cast<const uint8_t*>(rec_ptr_m(hdr, a.a_slot)) : a.qa;
+  const uint8_t* sa = a.a_slot >= 0 ? reinterpret_cast<const uint8_t*>(rec_ptr_m(hdr, a.a_slot + 1)) : a.sa;
+  const uint8_t* qb = a.qb;
+  const uint8_t* sb = a.sb;
+
+  struct Item {
+    int e, ta, tb, pb, mp, S;
+  };
+  int w0 = xcd * chunk + slot;
+  int ie = w0 / per_e;
+  int irem = w0 - ie * per_e;
+  int itb = irem / NA;
+  int ita = irem - itb * NA;
+  const int wend = min(xcd * chunk + chunk, n_items);
+  int wcur = w0;
+  auto fill = [&](Item& t) {
+    if (wcur >= wend) {
+      t.e = -1;
+      return;
+    }
+    t.e = ie;
+    t.ta = ita;
+    t.tb = itb;
+    t.pb = a.poffsets[ie];
+    t.mp = a.poffsets[ie + 1] - t.pb;
+    t.S = (t.mp + 63) / 64;
+    wcur += per;
+    ita += per;
+    while (ita >= NA) {
+      ita -= NA;
+      if (++itb == NB) {
+        itb = 0;
+        ++ie;
+      }
+    }
+  };
+
+  u32x4 R[4];              // codes: A columns lrow, lrow+64; B columns lrow, lrow+64
+  uint32_t SA, SB[4];      // scales of this lane's MFMA rows for the stage
+  auto load = [&](const Item& t, int s) {
+    const int m0 = s * 64 + ch * 16;
+    const bool in = m0 < t.mp;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = lrow + 64 * j;
+      R[j] = in ? *reinterpret_cast<const u32x4*>(qa + int64_t(a_ld) * t.pb +
+                                                  int64_t(t.ta * 128 + c) * t.mp + m0)
+                : u32x4{0u, 0u, 0u, 0u};
+      R[2 + j] = in ? *reinterpret_cast<const u32x4*>(qb + int64_t(b_ld) * t.pb +
+                                                      int64_t(t.tb * 128 + c) * t.mp + m0)
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int mb = 2 * s + lh;   // MX block of this lane's half of the stage
+    const int nmb = t.mp / 32;
+    if (mb < nmb) {
+      SA = sa[int64_t(a_ld) * (t.pb / 32) + int64_t(t.ta * 128 + 32 * wave + lr) * nmb + mb];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+        SB[bb] = sb[int64_t(b_ld) * (t.pb / 32) + int64_t(t.tb * 128 + 32 * bb + lr) * nmb + mb];
+    } else {
+      SA = 127;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) SB[bb] = 127;
+    }
+  };
+  uint32_t sa_cur = 127, sb_cur[4] = {127, 127, 127, 127};
+  auto store = [&]() {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<u32x4*>(lds + swz64(lrow + 64 * j, ch)) = R[j];
+      *reinterpret_cast<u32x4*>(lds + kOp + swz64(lrow + 64 * j, ch)) = R[2 + j];
+    }
+    sa_cur = SA;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) sb_cur[bb] = SB[bb];
+  };
+
+  Item cur, nxt;
+  fill(cur);
+  if (cur.e >= 0 && cur.S > 0) load(cur, 0);
+  while (cur.e >= 0) {
+    fill(nxt);
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    for (int s = 0; s < cur.S; ++s) {
+      store();
+      lds_barrier();
+      if (s + 1 < cur.S)
+        load(cur, s + 1);
+      else if (nxt.e >= 0 && nxt.S > 0)
+        load(nxt, 0);
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(lds + swz64(32 * wave + lr, lh));
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(lds + swz64(32 * wave + lr, 2 + lh));
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lds + kOp + swz64(32 * bb + lr, lh));
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(lds + kOp + swz64(32 * bb + lr, 2 + lh));
+        mfma_mx(acc[bb], a0, a1, b0, b1, int(sa_cur), int(sb_cur[bb]));
+      }
+      lds_barrier();
+    }
+    if (cur.S == 0 && nxt.e >= 0 && nxt.S > 0) load(nxt, 0);
+
+    TW* o = reinterpret_cast<TW*>(a.out0) + (int64_t(cur.e) * b_ld + int64_t(cur.tb) * 128) * a_ld +
+            cur.ta * 128;
+    char* stg = lds + 2 * kOp;
+#pragma unroll
+    for (int h = 0; h < kHalves; ++h) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        if (bb / (4 / kHalves) != h) continue;
+        const int rl = 32 * bb + lr - h * kRowsPerPass;
+        TW* rowp = reinterpret_cast<TW*>(stg + rl * kRowB) + 32 * wave + 4 * lh;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          store4<TW>(rowp + 8 * g4, acc[bb][4 * g4], acc[bb][4 * g4 + 1], acc[bb][4 * g4 + 2],
+                     acc[bb][4 * g4 + 3]);
+      }
+      lds_barrier();
+      constexpr int kChunksPerRow = 128 * int(sizeof(TW)) / 16;
+      constexpr int kChunks = kRowsPerPass * kChunksPerRow;
+#pragma unroll
+      for (int j = 0; j < kChunks / 256; ++j) {
+        const int i = tid + 256 * j;
+        const int rl = i / kChunksPerRow, cc = i % kChunksPerRow;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * kRowB + cc * 16);
+        char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+      }
+      lds_barrier();
+    }
+    cur = nxt;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+template <int ID, typename K>
+static int occupancy_m(K kernel) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n <= 0)
+      n = 1;
+    per_cu = n;
+  }
+  return per_cu;
+}
+
+static unsigned grid_m(int per_cu, int64_t items, int cus) {
+  int64_t g = std::min<int64_t>(items, int64_t(cus) * per_cu);
+  g = (g + kXcds - 1) / kXcds * kXcds;
+  return unsigned(std::max<int64_t>(g, kXcds));
+}
+
+// mode 0: W13 (+ SwiGLU), 1: W2 -> slots
+hipError_t launch_mx_fwd(int mode, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s) {
+  if (mt_max == 0) return hipSuccess;
+  if (mode == 0) {
+    hipLaunchKernelGGL(k_mx_fwd<0>, dim3(grid_m(occupancy_m<0>(k_mx_fwd<0>), mt_max * a.NT, cus)),
+                       dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_mx_fwd<1>, dim3(grid_m(occupancy_m<1>(k_mx_fwd<1>), mt_max * a.NT, cus)),
+                       dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// kind 0: W2 DGRAD + SwiGLU backward; 1: W13 DGRAD
+hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s) {
+  if (mt_max == 0) return hipSuccess;
+  if (kind == 0) {
+    hipLaunchKernelGGL(k_mx_dgrad<0>,
+                       dim3(grid_m(occupancy_m<2>(k_mx_dgrad<0>), mt_max * a.NT, cus)), dim3(256),
+                       0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_mx_dgrad<1>,
+                       dim3(grid_m(occupancy_m<3>(k_mx_dgrad<1>), mt_max * a.NT, cus)), dim3(256),
+                       0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// tag 2: dW2, 13: dW13
+hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStream_t s) {
+  const int64_t items = int64_t(a.E) * (a.a_ld / 128) * (a.b_ld / 128);
+  if (items == 0) return hipSuccess;
+#define MOE_MXWG(TW, TAG, ID)                                                                 \
+  do {                                                                                      \
+    const unsigned g = grid_m(occupancy_m<ID>(k_mx_wgrad<TW, TAG>), items, cus);            \
+    hipLaunchKernelGGL((k_mx_wgrad<TW, TAG>), dim3(g), dim3(256), 0, s, a);                 \
+  } while (0)
+  if (dw_f32) {
+    if (tag == 2)
+      MOE_MXWG(float, 2, 4);
+    else
+      MOE_MXWG(float, 13, 5);
+  } else {
+    if (tag == 2)
+      MOE_MXWG(uint16_t, 2, 6);
+    else
+      MOE_MXWG(uint16_t, 13, 7);
+  }
+#undef MOE_MXWG
+  return hipGetLastError();
+}
+
+}  // namespace moe

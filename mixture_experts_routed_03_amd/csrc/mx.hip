@@ -1,0 +1,216 @@
+// MXFP8 producers: E4M3 values with one E8M0 power-of-two scale per 32
+// values (Dist-MoE explainer, section 02: the producer picks the scale,
+// rounds the values and publishes both; MXFP8 training quantizes BF16 rows
+// after the gather; forward GEMMs take scales along the contraction (1x32
+// row blocks), weight gradients take column bundles (32x1 blocks down an
+// expert's token rows), static weights use 32x32 blocks).
+//
+//   k_prep_w : W [E, N, K] bf16 -> q [E, N, K] e4m3, s [E, N/32, K/32] e8m0
+//   k_rowq   : rows [R, N] bf16 -> q [R, N], s [R, N/32]           (1x32)
+//   k_colq   : rows [R, N] bf16 -> per expert e, q^T [N, Mp_e] and
+//              s^T [N, Mp_e/32] at offsets N*poffsets[e] and N*poffsets[e]/32,
+//              Mp_e = counts[e] rounded up to 32, pad rows quantized as 0.
+//
+// Scale rule: e = the smallest integer with amax <= 448 * 2^e, clamped to
+// [-127, 127] (-127 for an all-zero block), stored as the byte e + 127.  With
+// it no scaled value exceeds 448, the largest E4M3 magnitude.  E4M3 here is
+// the finite-only variant (bias 7, subnormals to 2^-9); values are rounded to
+// nearest, ties to even.
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int e8m0_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int p;
+  const float m = frexpf(amax, &p);  // amax = m * 2^p, m in [0.5, 1); 448 = 0.875 * 2^9
+  const int e = m <= 0.875f ? p - 9 : p - 8;
+  return min(127, max(-127, e));
+}
+
+// E4M3 byte of v (|v| <= 448 after scaling; larger magnitudes saturate).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal step 2^-9
+    code = uint32_t(__builtin_rintf(a * 512.0f));  // 8 -> smallest normal, also right
+  } else {
+    const uint32_t ab = __float_as_uint(a);
+    int E = int(ab >> 23) - 127;             // -6 .. 8
+    uint32_t man = ab & 0x7fffffu;
+    // round the 23-bit mantissa to 3 bits, ties to even
+    const uint32_t lsb = (man >> 20) & 1u;
+    man += 0x7ffffu + lsb;
+    if (man & 0x800000u) {                   // carried into the exponent
+      man = 0;
+      E += 1;
+    }
+    code = (uint32_t(E + 7) << 3) | (man >> 20);
+    code = min(code, 0x7eu);                 // 448 is the top (only reachable by rounding)
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float ldexp_i(float v, int e) { return ldexpf(v, e); }
+
+// ------------------------------------------------------------------ weights
+// One workgroup per (expert, 32-row block, 256 columns): thread = column.
+__global__ __launch_bounds__(256) void k_prep_w(const uint16_t* __restrict__ w,
+                                                uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                int N, int K) {
+  const int kc = blockIdx.x * 256 + threadIdx.x;     // column
+  const int nb = blockIdx.y;                         // 32-row block
+  const int64_t e = blockIdx.z;
+  if (kc >= K) return;
+  const uint16_t* src = w + (e * N + int64_t(nb) * 32) * K + kc;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    v[r] = bf16_to_f32(src[int64_t(r) * K]);
+    amax = fmaxf(amax, fabsf(v[r]));
+  }
+  // 32x32 block = 32 consecutive columns = half a wave
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const int ex = e8m0_exp(amax);
+  uint8_t* dst = q + (e * N + int64_t(nb) * 32) * K + kc;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) dst[int64_t(r) * K] = uint8_t(e4m3_rne(ldexp_i(v[r], -ex)));
+  if ((threadIdx.x & 31) == 0) s[(e * (N / 32) + nb) * (K / 32) + kc / 32] = uint8_t(ex + 127);
+}
+
+// ------------------------------------------------------------------ rows (1x32)
+// Pointers may come from the layer record (slots 0..5 = aux, 6 = x rows, 7 = h1).
+__device__ __forceinline__ uint64_t rec_ptr(const RouteHdr* h, int slot) {
+  if (slot == 6) return h->rec.x_rows;
+  if (slot == 7) return h->rec.h1;
+  return h->rec.aux[slot];
+}
+
+// Lane = 8 consecutive values; 4 lanes = one block.  A wave covers 512
+// values of a row per step.
+__global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
+  const RouteHdr* hdr = a.hdr;
+  if (a.replay_only && !hdr->rec.replay) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= hdr->R) return;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(
+      a.src_slot >= 0 ? (const void*)rec_ptr(hdr, a.src_slot) : a.src);
+  uint8_t* q = a.q_slot >= 0 ? reinterpret_cast<uint8_t*>(rec_ptr(hdr, a.q_slot)) : a.q;
+  uint8_t* s = a.s_slot >= 0 ? reinterpret_cast<uint8_t*>(rec_ptr(hdr, a.s_slot)) : a.s;
+  const int N = a.N;
+  for (int c0 = lane * 8; c0 < N; c0 += 512) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + row * N + c0);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(raw[i] << 16);
+      v[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int ex = e8m0_exp(amax);
+    u32x2 out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t wv = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv |= e4m3_rne(ldexp_i(v[4 * h + i], -ex)) << (8 * i);
+      out[h] = wv;
+    }
+    *reinterpret_cast<u32x2*>(q + row * N + c0) = out;
+    if ((lane & 3) == 0) s[row * (N / 32) + c0 / 32] = uint8_t(ex + 127);
+  }
+}
+
+// ------------------------------------------------------------------ column bundles (32x1)
+// One workgroup per (32-row block of the padded row space, 256 columns):
+// thread = column; reads 32 rows down its column (a wave reads 128 contiguous
+// bytes per row), writes 32 contiguous code bytes and one exponent.
+__global__ __launch_bounds__(256) void k_colq(ColqArgs a) {
+  const RouteHdr* hdr = a.hdr;
+  if (a.replay_only && !hdr->rec.replay) return;
+  const int gb = blockIdx.x;                 // 32-row block in the padded row space
+  if (gb * 32 >= hdr->Rpad) return;
+  const int col = blockIdx.y * 256 + threadIdx.x;
+  if (col >= a.N) return;
+  // expert of this block: the largest e with poffsets[e] <= 32*gb
+  int lo = 0, hi = a.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.poffsets[mid] <= gb * 32)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo;
+  const int pbase = a.poffsets[e];
+  const int mp = a.poffsets[e + 1] - pbase;
+  const int mb = (gb * 32 - pbase) / 32;     // block index inside the expert
+  const int r0 = a.offsets[e] + mb * 32;
+  const int rows = min(32, a.offsets[e + 1] - r0);
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(
+      a.src_slot >= 0 ? (const void*)rec_ptr(hdr, a.src_slot) : a.src);
+  uint8_t* q = a.q_slot >= 0 ? reinterpret_cast<uint8_t*>(rec_ptr(hdr, a.q_slot)) : a.q;
+  uint8_t* s = a.s_slot >= 0 ? reinterpret_cast<uint8_t*>(rec_ptr(hdr, a.s_slot)) : a.s;
+  const int N = a.N;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    v[r] = r < rows ? bf16_to_f32(src[int64_t(r0 + r) * N + col]) : 0.0f;
+    amax = fmaxf(amax, fabsf(v[r]));
+  }
+  const int ex = e8m0_exp(amax);
+  u32x4 o0, o1;
+#pragma unroll
+  for (int w4 = 0; w4 < 8; ++w4) {
+    uint32_t wv = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv |= e4m3_rne(ldexp_i(v[4 * w4 + i], -ex)) << (8 * i);
+    if (w4 < 4)
+      o0[w4] = wv;
+    else
+      o1[w4 - 4] = wv;
+  }
+  uint8_t* qd = q + int64_t(N) * pbase + int64_t(col) * mp + mb * 32;
+  *reinterpret_cast<u32x4*>(qd) = o0;
+  *reinterpret_cast<u32x4*>(qd + 16) = o1;
+  s[int64_t(N) * (pbase / 32) + int64_t(col) * (mp / 32) + mb] = uint8_t(ex + 127);
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_prep_w(const void* w, void* q, void* s, int E, int N, int K, hipStream_t st) {
+  if (E == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prep_w, dim3((K + 255) / 256, N / 32, E), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(w), reinterpret_cast<uint8_t*>(q),
+                     reinterpret_cast<uint8_t*>(s), N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowq(const RowqArgs& a, int64_t R_max, hipStream_t st) {
+  if (R_max == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rowq, dim3(unsigned((R_max + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_colq(const ColqArgs& a, int64_t Rpad_max, hipStream_t st) {
+  if (Rpad_max == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_colq, dim3(unsigned(Rpad_max / 32), unsigned((a.N + 255) / 256)),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

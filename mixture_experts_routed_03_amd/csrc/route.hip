@@ -175,17 +175,34 @@ __global__ void k_plan_decide(RouteHdr* __restrict__ hdr, PlanArgs a) {
   if (threadIdx.x != 0) return;
   LayerRec& rec = hdr->rec;
   const int64_t R = hdr->R;
-  const int64_t bx = align128(R * a.D * a.es);
-  const int64_t bh = align128(R * 2 * a.F * a.es);
-  const int64_t full = bx + bh;
+  const int64_t Rp = hdr->Rpad;
+  // Saved state of the layer.  BF16/FP32: gathered x rows and h1.  MXFP8
+  // (explainer section 04, MXFP8 full-save): x and h2 column bundles (codes +
+  // exponents) and dense h1; the gathered bf16 rows stay in scratch.
+  int64_t part[5] = {0, 0, 0, 0, 0};
+  if (a.mx) {
+    part[0] = align128(Rp * a.D);
+    part[1] = align128(Rp / 32 * a.D);
+    part[2] = align128(R * 2 * a.F * 2);
+    part[3] = align128(Rp * a.F);
+    part[4] = align128(Rp / 32 * a.F);
+  } else {
+    part[0] = align128(R * a.D * a.es);
+    part[2] = align128(R * 2 * a.F * a.es);
+  }
+  const int64_t full = part[0] + part[1] + part[2] + part[3] + part[4];
   rec.layer = a.layer;
   rec.done = 1;
+  auto to_scratch = [&]() {
+    rec.x_rows = a.scratch_x_rows;
+    rec.h1 = a.scratch_h1;
+    for (int i = 0; i < 4; ++i) rec.aux[i] = a.scratch_aux[i];
+  };
   if (!a.training || a.arena == 0) {
     rec.start = 0;
     rec.bytes = 0;
     rec.replay = a.training ? 1 : 0;
-    rec.x_rows = a.scratch_x_rows;
-    rec.h1 = a.scratch_h1;
+    to_scratch();
     return;
   }
   ArenaHdr* ah = reinterpret_cast<ArenaHdr*>(a.arena);
@@ -198,13 +215,21 @@ __global__ void k_plan_decide(RouteHdr* __restrict__ hdr, PlanArgs a) {
   rec.replay = replay ? 1 : 0;
   if (replay) {
     rec.bytes = keep;
-    rec.x_rows = a.scratch_x_rows;
-    rec.h1 = a.scratch_h1;
+    to_scratch();
   } else {
     rec.bytes = full;
     const uint64_t base = a.arena + uint64_t(kArenaHdrBytes) + uint64_t(cursor);
-    rec.x_rows = base;
-    rec.h1 = base + uint64_t(bx);
+    if (a.mx) {
+      rec.x_rows = a.scratch_x_rows;
+      rec.aux[0] = base;
+      rec.aux[1] = base + uint64_t(part[0]);
+      rec.h1 = base + uint64_t(part[0] + part[1]);
+      rec.aux[2] = rec.h1 + uint64_t(part[2]);
+      rec.aux[3] = rec.aux[2] + uint64_t(part[3]);
+    } else {
+      rec.x_rows = base;
+      rec.h1 = base + uint64_t(part[0]);
+    }
   }
   ah->cursor = cursor + rec.bytes;
 }

@@ -23,6 +23,13 @@ design notes):
     no scaled value exceeds 448 (parity unpinned: the rule itself is a choice).
   * Blocks start at index 0 of each axis of each expert's matrix; column
     bundles pad an expert's rows with zero rows up to a multiple of 32.
+  * Every tensor that is quantized is first materialized in BF16, as the
+    page describes for the gathered rows (BF16 rows are published and
+    quantized afterwards): h1 is stored BF16 and h2 = SiLU(g) * u is formed
+    from it and rounded to BF16; the route gradients s * dY and the h1
+    gradient are rounded to BF16 before their row and column blocks are
+    quantized.  The E4M3 codes are integer decisions, so they are taken on
+    the same BF16 values the kernels quantize.
 """
 
 from __future__ import annotations
@@ -33,6 +40,19 @@ E4M3_MAX = 448.0
 E4M3_MIN_NORMAL = 2.0 ** -6
 E4M3_MIN_SUBNORMAL = 2.0 ** -9
 BLOCK = 32
+
+
+def bf16_round(v) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (8 significant bits,
+    exponent range of fp32, subnormals down to 2^-133), ties to even;
+    magnitudes that round past the largest finite value become infinite."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, p = np.frexp(a)                          # a in [2^(p-1), 2^p)
+    step = np.ldexp(1.0, np.maximum(p - 8, -133).astype(np.int64))
+    q = np.rint(a / step) * step
+    q = np.where(q > 3.3895313892515355e38, np.inf, q)
+    return np.copysign(q, v)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -128,32 +148,35 @@ def qdq_32x32(w: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def expert_ffn_mx(x_rows, w13q, w2q):
-    """Forward.  x rows quantized 1x32 along D (after the gather); h2 quantized
-    1x32 along F for the W2 GEMM.  ``w13q``/``w2q`` are 32x32-block
-    dequantized weights.  Returns dense h1, h2 and h3."""
+    """Forward.  x rows (BF16) quantized 1x32 along D after the gather; h1
+    stored BF16; h2 = SiLU(g) * u from it, rounded to BF16 and quantized 1x32
+    along F for the W2 GEMM.  ``w13q``/``w2q`` are 32x32-block dequantized
+    weights.  Returns h1 (BF16 values), h2 (BF16 values) and h3."""
     from .moe import silu
     F = w2q.shape[1]
-    h1 = qdq_rows(x_rows) @ w13q.T
+    h1 = bf16_round(qdq_rows(x_rows) @ w13q.T)
     g, u = h1[:, :F], h1[:, F:]
-    h2 = silu(g) * u
+    h2 = bf16_round(silu(g) * u)
     h3 = qdq_rows(h2) @ w2q.T
     return h1, h2, h3
 
 
 def expert_ffn_backward_mx(x_rows, w13q, w2q, h1, dh3):
-    """Backward.  DGRAD operands are quantized along their contraction axis
-    (dh3 1x32 along D, dh1 1x32 along 2F) and use the same 32x32 weight
-    values; WGRAD operands are column bundles (32x1 down the expert's rows)
-    of dh3, h2, dh1 and x."""
+    """Backward.  ``h1`` is the stored BF16 h1, ``dh3`` the route gradient
+    (rounded to BF16 here).  DGRAD operands are quantized along their
+    contraction axis (dh3 1x32 along D, dh1 1x32 along 2F) and use the same
+    32x32 weight values; WGRAD operands are column bundles (32x1 down the
+    expert's rows) of dh3, h2, dh1 and x."""
     from .moe import silu, silu_grad
     F = w2q.shape[1]
     g, u = h1[:, :F], h1[:, F:]
-    h2 = silu(g) * u
+    h2 = bf16_round(silu(g) * u)
+    dh3 = bf16_round(dh3)
     dh2 = qdq_rows(dh3) @ w2q
     dw2 = qdq_cols(dh3).T @ qdq_cols(h2)
     dg = dh2 * u * silu_grad(g)
     du = dh2 * silu(g)
-    dh1 = np.concatenate([dg, du], axis=1)
+    dh1 = bf16_round(np.concatenate([dg, du], axis=1))
     dx = qdq_rows(dh1) @ w13q
     dw13 = qdq_cols(dh1).T @ qdq_cols(x_rows)
     return dx, dw13, dw2, dh1

@@ -30,6 +30,8 @@ def run_forward(layer, lay, y_addend=None):
     """route -> expert_fwd -> combine on the current stream; returns y."""
     T = lay["x"].shape[0]
     y = torch.empty((T, layer.D), dtype=layer.act_dtype, device=layer.device)
+    if layer.prec == "mxfp8" and layer.prepared is None:
+        layer.prepare(lay["w13"], lay["w2"])
     layer.route(lay["ids"])
     layer.forward(lay["x"], lay["w13"], lay["w2"])
     layer.combine(lay["scores"], y, y_addend=y_addend)
@@ -52,8 +54,18 @@ def check_route(got: dict, ids, E):
     return ref
 
 
-def sampled_forward_ref(lay, tokens):
+def _expert_weights(lay, e, mx):
+    from oracle import mx as omx
+    w13 = om.as_f64(lay["w13"][e])
+    w2 = om.as_f64(lay["w2"][e])
+    if mx:
+        return omx.qdq_32x32(w13), omx.qdq_32x32(w2)
+    return w13, w2
+
+
+def sampled_forward_ref(lay, tokens, mx=False):
     """Oracle Y for selected tokens only, one expert's weights at a time."""
+    from oracle import mx as omx
     ids = lay["ids"].cpu().numpy()
     s = lay["scores"].cpu().numpy().astype(np.float64)
     X = lay["x"]
@@ -66,10 +78,9 @@ def sampled_forward_ref(lay, tokens):
             if 0 <= e < E:
                 by_e.setdefault(e, []).append((t, k))
     for e, lst in sorted(by_e.items()):
-        w13 = om.as_f64(lay["w13"][e])
-        w2 = om.as_f64(lay["w2"][e])
+        w13, w2 = _expert_weights(lay, e, mx)
         xr = om.as_f64(X[[t for t, _ in lst]])
-        _, _, h3 = om.expert_ffn(xr, w13, w2)
+        _, _, h3 = (omx.expert_ffn_mx if mx else om.expert_ffn)(xr, w13, w2)
         for i, (t, k) in enumerate(lst):
             out[t] += s[t, k] * h3[i]
     return np.stack([out[t] for t in tokens])
@@ -90,9 +101,13 @@ def run_train(layer, lay, dw_f32=False, dx_init=None, flags=0):
     return y, dx, dw13, dw2, ds
 
 
-def sampled_backward_ref(lay, tokens, experts):
+def sampled_backward_ref(lay, tokens, experts, mx=False):
     """Oracle dX and dS for selected tokens and dW13/dW2 for selected experts,
-    computed per route from the layer inputs (one expert's weights at a time)."""
+    computed per route from the layer inputs (one expert's weights at a time).
+    With mx, the quantization-faithful MXFP8 expert functions are used; an
+    expert's column bundles need all of its rows, so dW is computed from every
+    route of a sampled expert in packed (ascending route) order."""
+    from oracle import mx as omx
     ids = lay["ids"].cpu().numpy()
     s = lay["scores"].cpu().numpy().astype(np.float64)
     X = lay["x"]
@@ -114,16 +129,16 @@ def sampled_backward_ref(lay, tokens, experts):
         for t, k in zip(*np.nonzero(ids == e)):
             work.setdefault(int(e), set()).add((int(t), int(k)))
     for e, routes in sorted(work.items()):
-        routes = sorted(routes)
-        w13 = om.as_f64(lay["w13"][e])
-        w2 = om.as_f64(lay["w2"][e])
+        routes = sorted(routes, key=lambda tk: tk[0] * ids.shape[1] + tk[1])
+        w13, w2 = _expert_weights(lay, e, mx)
         ts = [t for t, _ in routes]
         xr = om.as_f64(X[ts])
         dyr = om.as_f64(dY[ts])
         sr = np.array([s[t, k] for t, k in routes])
-        h1, _, h3 = om.expert_ffn(xr, w13, w2)
+        h1, _, h3 = (omx.expert_ffn_mx if mx else om.expert_ffn)(xr, w13, w2)
         dh3 = sr[:, None] * dyr
-        dxr, dw13e, dw2e, _ = om.expert_ffn_backward(xr, w13, w2, h1, dh3)
+        dxr, dw13e, dw2e, _ = (omx.expert_ffn_backward_mx if mx else om.expert_ffn_backward)(
+            xr, w13, w2, h1, dh3)
         if e in dw13:
             dw13[e], dw2[e] = dw13e, dw2e
         for i, (t, k) in enumerate(routes):

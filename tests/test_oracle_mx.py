@@ -97,7 +97,7 @@ def test_mx_path_reduces_to_exact_path_without_rounding(monkeypatch):
     M, D, F = 7, 64, 32
     x = rng.standard_normal((M, D)); w13 = rng.standard_normal((2 * F, D)); w2 = rng.standard_normal((D, F))
     dh3 = rng.standard_normal((M, D))
-    for name in ("qdq_rows", "qdq_cols"):
+    for name in ("qdq_rows", "qdq_cols", "bf16_round"):
         monkeypatch.setattr(mx, name, lambda v: np.asarray(v, dtype=np.float64))
     h1, h2, h3 = mx.expert_ffn_mx(x, w13, w2)
     r1, r2, r3 = moe.expert_ffn(x, w13, w2)
@@ -144,10 +144,32 @@ def test_mx_layer_reduces_to_fp64_layer_without_rounding(monkeypatch):
     x = rng.standard_normal((T, D)); w13 = rng.standard_normal((E, 2 * F, D))
     w2 = rng.standard_normal((E, D, F)); ids = np.array([[0, 1], [1, 2], [2, -1], [0, 2], [1, 0], [-1, -1]])
     s = rng.random((T, K)); s[ids < 0] = 0; dy = rng.standard_normal((T, D))
-    for name in ("qdq_rows", "qdq_cols", "qdq_32x32"):
+    for name in ("qdq_rows", "qdq_cols", "qdq_32x32", "bf16_round"):
         monkeypatch.setattr(mx, name, lambda v: np.asarray(v, dtype=np.float64))
     y, c = mx.forward(x, ids, s, w13, w2, keep=True)
     ry, rc = moe.forward(x, ids, s, w13, w2, keep=True)
     np.testing.assert_allclose(y, ry, rtol=1e-12, atol=1e-12)
     for a, b in zip(mx.backward(dy, x, ids, s, w13, w2, c), moe.backward(dy, x, ids, s, w13, w2, rc)):
         np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-10)
+
+
+def test_bf16_round_matches_library_conversion():
+    """RNE to bfloat16 from the definition equals torch's float32 -> bfloat16
+    conversion (a library routine) on values across all binades, on exact
+    ties and on the special cases."""
+    import torch
+    rng = np.random.default_rng(9)
+    f32 = np.concatenate([
+        (rng.standard_normal(200000) * np.exp(rng.uniform(-95, 88, 200000))),
+        rng.standard_normal(20000) * 1e-40,                      # fp32 subnormals
+        np.array([0.0, -0.0, 3.3895313e38, 3.4e38, -3.4e38, 1.0, 1.00390625, 1.01171875]),
+    ]).astype(np.float32)
+    # exact ties: bf16 values plus half an ulp
+    base = torch.from_numpy(rng.standard_normal(20000).astype(np.float32)).to(torch.bfloat16)
+    b32 = base.float().numpy()
+    ulp = np.abs(b32) * 2.0 ** -7
+    ties = (b32 + np.sign(b32) * ulp / 2).astype(np.float32)
+    x = np.concatenate([f32, ties, b32])
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    got = mx.bf16_round(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
