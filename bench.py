@@ -5,36 +5,72 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 route (histogram, scan, stable permutation) -> expert forward (gather, W13
 grouped GEMM + SwiGLU, W2 grouped GEMM into route slots) -> combine, and for
 training workloads the backward (combine backward, W2 DGRAD + SwiGLU
-backward, W2/W13 WGRAD, W13 DGRAD, input-gradient reduction).
+backward, W2/W13 WGRAD, W13 DGRAD, input-gradient reduction).  MXFP8
+workloads add the row quantizers and column bundles.
 
-Default workload: T = 2,048 tokens, D = 7,168, F = 2,048, E = 384 experts,
-top-6, balanced routing, BF16 operands with fp32 accumulation, forward +
-backward.  Inputs are resident in HBM before timing starts.  Useful work is
-6*R*D*F FLOPs forward and twice that backward (R = valid routes; padding and
-replay excluded), the Dist-MoE explainer's count (section 07).
+Workloads (all at T = 2,048 tokens, D = 7,168, F = 2,048, E = 384, top-6):
+  bf16_train_balanced  BF16, balanced routing, forward + backward (default)
+  bf16_fwd_balanced    BF16, balanced routing, forward only
+  bf16_train_zipf      BF16, Zipf(1.2) routing, forward + backward
+  mxfp8_train_shared   MXFP8 routed layer + one shared BF16 SwiGLU expert,
+                       forward + backward
+  mxfp8_ten_layer      ten MXFP8 layers (Zipf 0, 0.6, 1.0, 1.4 cycled), ten
+                       forwards then ten backwards in one byte-budgeted arena
+
+Inputs are resident in HBM before timing starts.  Useful work is 6*R*D*F
+FLOPs forward and twice that backward per routed layer (R = valid routes;
+padding and replay excluded), the Dist-MoE explainer's count (section 07);
+a shared expert adds 6*T*D*F forward and twice that backward.
 
 Prints ONE JSON line.  Also reports the dominant kernel against its roofline
-(per-kernel HIP-event timing over a second pass of the timed steps) and the
-CPU oracle timed on a bounded sample of the same workload.
+(per-kernel HIP-event timing over a second pass of the timed steps, on the
+library's launch stream) and the CPU oracle timed on a bounded sample.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 PEAK_HBM_GBS = 8000.0
-PEAK_BF16_TFLOPS = 2500.0
-PEAK_FP32_TFLOPS = 157.3
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "mixture_experts_routed_03_amd", "csrc")
 
 WORKLOADS = {
     # name: (config key, training)
     "bf16_train_balanced": ("bf16_fwd_balanced", True),
     "bf16_fwd_balanced": ("bf16_fwd_balanced", False),
     "bf16_train_zipf": ("bf16_train_zipf", True),
+    "mxfp8_train_shared": ("mxfp8_train_shared", True),
+    "mxfp8_ten_layer": ("mxfp8_ten_layer", True),
+}
+CPU_EXPERTS = {"bf16": 96, "mxfp8": 3}
+
+# Library timing name -> (kernel symbol in rocprofv3 traces, per precision;
+# source files that define it).
+SYMBOLS = {
+    "bf16": {
+        "w13_swiglu": ("moe::k_gemm_fwd<unsigned short, 0>", ["gemm_fwd.hip"]),
+        "w2_scatter": ("moe::k_gemm_fwd<unsigned short, 1>", ["gemm_fwd.hip"]),
+        "w2_dgrad_swiglu": ("moe::k_gemm_dgrad<0>", ["gemm_bwd.hip"]),
+        "w13_dgrad": ("moe::k_gemm_dgrad<1>", ["gemm_bwd.hip"]),
+        "w2_wgrad": ("moe::k_gemm_wgrad<unsigned short, 2>", ["gemm_bwd.hip"]),
+        "w13_wgrad": ("moe::k_gemm_wgrad<unsigned short, 13>", ["gemm_bwd.hip"]),
+    },
+    "mxfp8": {
+        "w13_swiglu": ("moe::k_mx_fwd<0>", ["gemm_mx.hip"]),
+        "w2_scatter": ("moe::k_mx_fwd<1>", ["gemm_mx.hip"]),
+        "w2_dgrad_swiglu": ("moe::k_mx_dgrad<0>", ["gemm_mx.hip"]),
+        "w13_dgrad": ("moe::k_mx_dgrad<1>", ["gemm_mx.hip"]),
+        "w2_wgrad": ("moe::k_mx_wgrad<unsigned short, 2>", ["gemm_mx.hip"]),
+        "w13_wgrad": ("moe::k_mx_wgrad<unsigned short, 13>", ["gemm_mx.hip"]),
+    },
 }
 
 
@@ -44,13 +80,246 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bf16_train_balanced", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-experts", type=int, default=24,
-                    help="experts in the CPU-oracle sample (all their routes)")
+    ap.add_argument("--cpu-experts", type=int, default=0,
+                    help="experts in the CPU-oracle sample (all their routes); 0 = default "
+                         "for the precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference kernel "
                          "for scaling hardware byte counters)")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+
+def alg_bytes(name, m):
+    """Minimum HBM bytes of one launch of kernel ``name`` for a layer with
+    metadata ``m`` (R valid routes, Rp rows padded to 32 per expert, ne
+    experts with rows, shapes, precision); None if not modelled.  Replay
+    kernels count only for a layer that replays, the forward's column
+    bundles only for a layer that saves."""
+    R, Rp, ne, T, K, D, F = m["R"], m["Rp"], m["ne"], m["T"], m["K"], m["D"], m["F"]
+    es, dwb, mx, rep = m["es"], m["dwb"], m["mx"], m["replay"]
+    if name.startswith("replay_"):
+        if not rep:
+            return 0
+        name = name[len("replay_"):]
+    elif name in ("bundle_x", "bundle_h2") and rep:
+        return 0
+
+    def q(n):  # E4M3 codes plus one E8M0 byte per 32 values
+        return n + n // 32
+
+    wb = (1 + 1 / 1024) if mx else es          # weight bytes per value (32x32 scales)
+    w13 = int(ne * 2 * F * D * wb)
+    w2 = int(ne * D * F * wb)
+    common = {
+        "route": T * K * 4 * 2 + R * 4 * 2,
+        "gather": T * D * es + R * D * es,
+        "combine": T * K * D * es + T * D * es + T * K * 8,
+        "combine_bwd": T * D * es + T * K * D * es + R * D * es + T * K * 8,
+        "dx_reduce": R * D * 4 + T * D * es,
+    }
+    if name in common:
+        return common[name]
+    if not mx:
+        return {
+            "w13_swiglu": w13 + R * D * es + R * 2 * F * es + R * F * es,
+            "w2_scatter": w2 + R * F * es + R * D * es,
+            "w2_dgrad_swiglu": w2 + R * D * es + 2 * R * 2 * F * es + R * F * es,
+            "w2_wgrad": ne * D * F * dwb + R * D * es + R * F * es,
+            "w13_dgrad": w13 + R * 2 * F * es + R * D * 4,
+            "w13_wgrad": ne * 2 * F * D * dwb + R * 2 * F * es + R * D * es,
+        }.get(name)
+    return {
+        "quant_x": R * D * 2 + q(R * D),
+        "bundle_x": R * D * 2 + q(Rp * D),
+        "w13_swiglu": w13 + q(R * D) + R * 2 * F * 2 + R * F * 2,
+        "bundle_h2": R * F * 2 + q(Rp * F),
+        "quant_h2": R * F * 2 + q(R * F),
+        "w2_scatter": w2 + q(R * F) + R * D * 2,
+        "quant_dh3": R * D * 2 + q(R * D),
+        "bundle_dh3": R * D * 2 + q(Rp * D),
+        "w2_dgrad_swiglu": w2 + q(R * D) + 2 * R * 2 * F * 2,
+        "w2_wgrad": ne * D * F * dwb + q(Rp * D) + q(Rp * F),
+        "quant_dh1": R * 2 * F * 2 + q(R * 2 * F),
+        "bundle_dh1": R * 2 * F * 2 + q(Rp * 2 * F),
+        "w13_dgrad": w13 + q(R * 2 * F) + R * D * 4,
+        "w13_wgrad": ne * 2 * F * D * dwb + q(Rp * 2 * F) + q(Rp * D),
+    }.get(name)
+
+
+def kernel_flops(name, m):
+    R, D, F = m["R"], m["D"], m["F"]
+    if name.startswith("replay_"):
+        if not m["replay"]:
+            return 0
+        name = name[len("replay_"):]
+    if name in ("w13_swiglu", "w13_dgrad", "w13_wgrad"):
+        return 2 * R * 2 * F * D
+    if name in ("w2_scatter", "w2_dgrad_swiglu", "w2_wgrad"):
+        return 2 * R * D * F
+    return None
+
+
+def src_hashes(files):
+    out = {}
+    for f in files + ["common.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            out[f] = hashlib.sha256(fh.read()).hexdigest()[:16]
+    return out
+
+
+def measured_traffic(workload, prec, kname):
+    """HBM bytes per launch of ``kname`` from the committed rocprofv3 counter
+    summary of this workload, if one exists and the kernel's sources are
+    unchanged since it was taken; else None."""
+    sym, files = SYMBOLS.get(prec, {}).get(kname, (None, None))
+    if sym is None:
+        return None
+    prof_dir = os.path.join(HERE, "profiles")
+    if not os.path.isdir(prof_dir):
+        return None
+    for fn in sorted(os.listdir(prof_dir)):
+        if not fn.startswith(workload + "_") or not fn.endswith(".md"):
+            continue
+        with open(os.path.join(prof_dir, fn)) as fh:
+            text = fh.read()
+        mt = re.search(r"```json\n(.*?)\n```", text, re.S)
+        if not mt:
+            continue
+        blob = json.loads(mt.group(1))
+        per = blob.get("traffic_bytes", {}).get(sym)
+        shas = blob.get("src_sha256_16", {})
+        if not per:
+            continue
+        now = src_hashes(files)
+        if any(shas.get(f) != h for f, h in now.items()):
+            return None
+        return int(sum(per) / len(per))
+    return None
+
+
+# ---------------------------------------------------------------- workloads
+
+def layer_meta(layer, rb, replay, T):
+    import numpy as np
+    counts = rb["counts"].astype(np.int64)
+    return {"R": int(rb["R"]), "Rp": int(rb["poffsets"][-1]), "ne": int((counts > 0).sum()),
+            "T": T, "K": layer.K, "D": layer.D, "F": layer.F,
+            "es": 4 if layer.prec == "f32" else 2,
+            "dwb": 4 if layer.dw_dtype.itemsize == 4 else 2,
+            "mx": layer.prec == "mxfp8", "replay": bool(replay),
+            "max_rows": int(counts.max()) if counts.size else 0}
+
+
+def setup(args, dev):
+    """Build the workload; returns (step, plans, meta_fn, useful_flops_fn,
+    cpu_fn, info) where plans maps a label to a MoeLayer whose per-kernel
+    timings are read, meta_fn() lists (label, per-layer metadata)."""
+    import torch
+
+    from mixture_experts_routed_03_amd import binding as B
+    from mixture_experts_routed_03_amd import workloads as wl
+
+    cfg_key, training = WORKLOADS[args.workload]
+    cfg = wl.CONFIGS[cfg_key]
+    T, D, F, E, K = cfg.T, cfg.D, cfg.F, cfg.E, cfg.K
+    bf = torch.bfloat16
+
+    if args.workload == "mxfp8_ten_layer":
+        L = cfg.layers
+        budget = wl.ten_layer_budget(cfg)
+        st = B.MoeStack(L, T, D, F, E, K, "mxfp8", arena_budget=budget, device=dev)
+        lays, preps = [], []
+        for l in range(L):
+            lay = wl.make_layer(cfg, l, device=dev)
+            preps.append(st.layer.prepare(lay["w13"], lay["w2"]))
+            if l == 0:   # the CPU-oracle sample's experts, in bf16 on the host
+                n_cpu = args.cpu_experts or CPU_EXPERTS["mxfp8"]
+                keep0 = {k: lay[k][:n_cpu].cpu() for k in ("w13", "w2")}
+            del lay["w13"], lay["w2"]
+            lays.append(lay)
+            torch.cuda.synchronize()
+        ys = [torch.empty((T, D), dtype=bf, device=dev) for _ in range(L)]
+        # one set of weight-gradient buffers, handed over after each layer's backward
+        dx = torch.empty((T, D), dtype=bf, device=dev)
+        dw13 = torch.empty((E, 2 * F, D), dtype=bf, device=dev)
+        dw2 = torch.empty((E, D, F), dtype=bf, device=dev)
+        ds = torch.empty((T, K), dtype=torch.float32, device=dev)
+
+        def step():
+            for l in range(L):
+                st.route(l, lays[l]["ids"])
+                st.forward(l, lays[l]["x"], None, None, lays[l]["scores"], ys[l],
+                           prepared=preps[l])
+            for l in reversed(range(L)):
+                st.backward(l, lays[l]["x"], lays[l]["scores"], lays[l]["dy"], None, None, dx,
+                            dw13, dw2, ds, prepared=preps[l])
+
+        def meta():
+            out = []
+            for l in range(L):
+                rb = st.readback(l, T)
+                out.append(("", layer_meta(st.layer, rb, st.status(l)[1], T)))
+            return out
+
+        def cpu():
+            lay0 = dict(lays[0], **keep0)
+            return cpu_baseline(lay0, cfg, True, n_cpu, "layer 0 of 10, ")
+
+        info = {"layers": L, "arena_budget_bytes": budget}
+        return step, {"": st.layer}, meta, cpu, info, cfg, training
+
+    lay = wl.make_layer(cfg, 0, device=dev, grads=training)
+    layer = B.MoeLayer(T, D, F, E, K, cfg.prec, training=training, device=dev)
+    if cfg.prec == "mxfp8":
+        layer.prepare(lay["w13"], lay["w2"])
+    act = layer.act_dtype
+    y = torch.empty((T, D), dtype=act, device=dev)
+    plans = {"": layer}
+    if training:
+        dx = torch.empty((T, D), dtype=act, device=dev)
+        dw13 = torch.empty((E, 2 * F, D), dtype=layer.dw_dtype, device=dev)
+        dw2 = torch.empty((E, D, F), dtype=layer.dw_dtype, device=dev)
+        dsc = torch.empty((T, K), dtype=torch.float32, device=dev)
+    shared = None
+    if cfg.shared_expert:
+        shared = B.MoeLayer(T, D, F, 1, 1, "bf16", training=training, device=dev)
+        plans["shared:"] = shared
+        sh_ids = torch.zeros((T, 1), dtype=torch.int32, device=dev)
+        sh_sc = torch.ones((T, 1), dtype=torch.float32, device=dev)
+        ysh = torch.empty((T, D), dtype=bf, device=dev)
+        dws13 = torch.empty_like(lay["w13_shared"])
+        dws2 = torch.empty_like(lay["w2_shared"])
+
+    def step():
+        if shared is not None:
+            shared.route(sh_ids)
+            shared.forward(lay["x"], lay["w13_shared"], lay["w2_shared"])
+            shared.combine(sh_sc, ysh)
+        layer.route(lay["ids"])
+        layer.forward(lay["x"], lay["w13"], lay["w2"])
+        layer.combine(lay["scores"], y, y_addend=ysh if shared is not None else None)
+        if training:
+            layer.backward(lay["x"], lay["scores"], lay["dy"], lay["w13"], lay["w2"], dx, dw13,
+                           dw2, dsc)
+            if shared is not None:
+                shared.backward(lay["x"], sh_sc, lay["dy"], lay["w13_shared"], lay["w2_shared"],
+                                dx, dws13, dws2, None, flags=B.BWD_ACCUMULATE_DX)
+
+    def meta():
+        out = [("", layer_meta(layer, layer.readback(T), layer.status()[1] if training else 0, T))]
+        if shared is not None:
+            out.append(("shared:", layer_meta(shared, shared.readback(T), shared.status()[1], T)))
+        return out
+
+    def cpu():
+        return cpu_baseline(lay, cfg, training,
+                            args.cpu_experts or CPU_EXPERTS["mxfp8" if cfg.prec == "mxfp8" else "bf16"],
+                            "routed experts only, " if shared is not None else "")
+
+    return step, plans, meta, cpu, {}, cfg, training
 
 
 def main():
@@ -61,44 +330,18 @@ def main():
               "parallelism over xGMI is a design note only). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from mixture_experts_routed_03_amd import binding as B
-    from mixture_experts_routed_03_amd import workloads as wl
 
-    cfg_key, training = WORKLOADS[args.workload]
-    cfg = wl.CONFIGS[cfg_key]
-    if args.workload == "bf16_train_zipf":
-        training = True
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    lay = wl.make_layer(cfg, 0, device=dev, grads=training)
-    T, D, F, E, K = cfg.T, cfg.D, cfg.F, cfg.E, cfg.K
-    layer = B.MoeLayer(T, D, F, E, K, cfg.prec, training=training, device=dev)
-    act = layer.act_dtype
-    y = torch.empty((T, D), dtype=act, device=dev)
-    if training:
-        dx = torch.empty((T, D), dtype=act, device=dev)
-        dw13 = torch.empty((E, 2 * F, D), dtype=layer.dw_dtype, device=dev)
-        dw2 = torch.empty((E, D, F), dtype=layer.dw_dtype, device=dev)
-        dsc = torch.empty((T, K), dtype=torch.float32, device=dev)
-
-    def step():
-        layer.route(lay["ids"])
-        layer.forward(lay["x"], lay["w13"], lay["w2"])
-        layer.combine(lay["scores"], y)
-        if training:
-            layer.backward(lay["x"], lay["scores"], lay["dy"], lay["w13"], lay["w2"], dx, dw13,
-                           dw2, dsc)
+    step, plans, meta_fn, cpu_fn, info, cfg, training = setup(args, dev)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    rb = layer.readback(T)
-    counts = rb["counts"].astype(np.int64)
-    R = int(rb["R"])
-    nonempty = int((counts > 0).sum())
+    metas = meta_fn()
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20) // 4
@@ -122,63 +365,66 @@ def main():
     ms_step = start.elapsed_time(stop) / args.steps
 
     # ---- second pass with per-kernel events (on the library's launch stream)
-    B.moe_timing_enable(layer.plan, True)
+    for p in plans.values():
+        B.moe_timing_enable(p.plan, True)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    ktimes = B.moe_timing_read(layer.plan)
-    B.moe_timing_enable(layer.plan, False)
+    ktimes = {}
+    for label, p in plans.items():
+        for name, (tot, n) in B.moe_timing_read(p.plan).items():
+            ktimes[label + name] = (tot, n)
+        B.moe_timing_enable(p.plan, False)
 
-    es = 2 if cfg.prec != "f32" else 4
-    fwd_flops = 6 * R * D * F
-    flops = fwd_flops * (3 if training else 1)
-    value = flops / (ms_step * 1e-3) / 1e12
+    mult = 3 if training else 1
+    useful = 0
+    for label, m in metas:
+        rows = m["R"]
+        useful += 6 * rows * m["D"] * m["F"] * mult
+    value = useful / (ms_step * 1e-3) / 1e12
 
-    # Algorithmic bytes per launch (what each kernel must move at minimum).
-    w13_b = nonempty * 2 * F * D * es
-    w2_b = nonempty * D * F * es
-    alg = {
-        "route": T * K * 4 * 2 + R * 4 * 2,
-        "gather": T * D * es + R * D * es,
-        "w13_swiglu": w13_b + R * D * es + R * 2 * F * es + R * F * es,
-        "w2_scatter": w2_b + R * F * es + R * D * es,
-        "combine": T * K * D * es + T * D * es + T * K * 8,
-        "combine_bwd": T * D * es + T * K * D * es + R * D * es + T * K * 8,
-        "w2_dgrad_swiglu": w2_b + R * D * es + R * 2 * F * es * 2,
-        "w2_wgrad": w2_b // es * (4 if layer.dw_dtype == torch.float32 else 2) + R * D * es
-        + R * 2 * F * es,
-        "w13_dgrad": w13_b + R * 2 * F * es + R * D * 4,
-        "w13_wgrad": w13_b // es * (4 if layer.dw_dtype == torch.float32 else 2)
-        + R * 2 * F * es + R * D * es,
-        "dx_reduce": R * D * 4 + T * D * es,
-    }
-    kflops = {"w13_swiglu": 2 * R * 2 * F * D, "w2_scatter": 2 * R * D * F,
-              "w2_dgrad_swiglu": 2 * R * D * F, "w2_wgrad": 2 * R * D * F,
-              "w13_dgrad": 2 * R * 2 * F * D, "w13_wgrad": 2 * R * 2 * F * D}
+    # per-kernel: algorithmic bytes and flops per step, time per step
     kernels = {}
-    for name, (tot, n) in ktimes.items():
+    for key, (tot, n) in ktimes.items():
         if n == 0:
             continue
-        avg = tot / n
-        ent = {"avg_ms": round(avg, 4), "launches": n}
-        if name in alg:
-            ent["GB/s"] = round(alg[name] / (avg * 1e-3) / 1e9, 1)
-            ent["alg_bytes"] = int(alg[name])
-        if name in kflops:
-            ent["TFLOP/s"] = round(kflops[name] / (avg * 1e-3) / 1e12, 2)
-        kernels[name] = ent
-    dom = max((k for k in kernels if k in alg), key=lambda k: kernels[k]["avg_ms"] *
-              kernels[k]["launches"])
-    ach = alg[dom] / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
-                "alg_bytes_per_launch": int(alg[dom])}
-    route_gbs = kernels.get("route", {}).get("GB/s")
+        label, name = (key.split(":", 1)[0] + ":", key.split(":", 1)[1]) if ":" in key else ("", key)
+        ms = tot / args.steps
+        ent = {"ms_per_step": round(ms, 4), "launches_per_step": n // args.steps,
+               "avg_ms": round(tot / n, 4)}
+        bsum, fsum, known = 0, 0, True
+        for lab, m in metas:
+            if lab != label:
+                continue
+            b = alg_bytes(name, m)
+            if b is None:
+                known = False
+                break
+            bsum += b
+            f = kernel_flops(name, m)
+            fsum += f or 0
+        if known:
+            ent["alg_bytes_per_step"] = int(bsum)
+            ent["GB/s"] = round(bsum / (ms * 1e-3) / 1e9, 1)
+            if fsum:
+                ent["TFLOP/s"] = round(fsum / (ms * 1e-3) / 1e12, 2)
+        kernels[key] = ent
+    dom = max((k for k in kernels if "GB/s" in kernels[k]), key=lambda k: kernels[k]["ms_per_step"])
+    dom_name = dom.split(":", 1)[-1]
+    n_launch = kernels[dom]["launches_per_step"]
+    alg_per_launch = kernels[dom]["alg_bytes_per_step"] / max(1, n_launch)
+    ach = kernels[dom]["GB/s"]
+    prec_dom = "bf16" if dom.startswith("shared:") else cfg.prec
+    traffic = measured_traffic(args.workload, prec_dom, dom_name)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": int(alg_per_launch),
+                "avg_launch_ms": kernels[dom]["avg_ms"]}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lay, cfg, training, args.cpu_experts)
+    cpu = None if args.no_cpu_baseline else cpu_fn()
 
+    m0 = metas[0][1]
+    prec = cfg.prec
     out = {
         "metric": "useful TFLOP/s/GPU MoE expert fwd+bwd (BF16, MXFP8); % MFMA peak; route GB/s",
         "value": round(value, 2),
@@ -190,14 +436,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.prec == "bf16" else cfg.prec,
-        "data": "synthetic (seeded; N(0,1) tokens, N(0,1/fan_in) weights, top-6 uniform routing)",
-        "config": {"workload": f"{args.workload}: T={T} D={D} F={F} E={E} K={K} "
-                               f"{'fwd+bwd' if training else 'fwd'}",
-                   "routes": R, "nonempty_experts": nonempty, "max_rows": int(counts.max()),
-                   "dw_dtype": "bf16" if layer.dw_dtype == torch.bfloat16 else "f32"},
-        "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
-        "route_GBps": route_gbs,
+        "dtype": prec,
+        "data": "synthetic (seeded; N(0,1) tokens, N(0,1/fan_in) weights, "
+                + ("Zipf-skewed" if cfg.zipf != (None,) else "balanced top-6") + " routing)",
+        "config": {"workload": f"{args.workload}: T={cfg.T} D={cfg.D} F={cfg.F} E={cfg.E} "
+                               f"K={cfg.K} {'fwd+bwd' if training else 'fwd'}"
+                               + (f", {info['layers']} layers" if "layers" in info else "")
+                               + (", + shared BF16 expert" if cfg.shared_expert else ""),
+                   "routes_per_layer": [m["R"] for lab, m in metas if lab == ""],
+                   "nonempty_experts": [m["ne"] for lab, m in metas if lab == ""],
+                   "max_rows": max(m["max_rows"] for lab, m in metas if lab == ""),
+                   "replayed_layers": [int(m["replay"]) for lab, m in metas if lab == ""],
+                   "dw_dtype": "bf16" if m0["dwb"] == 2 else "f32", **info},
+        "mfma_peak_frac": round(value / PEAK_TFLOPS[prec], 4),
+        "route_GBps": kernels.get("route", {}).get("GB/s"),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "kernels": kernels,
@@ -206,19 +458,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(lay, cfg, training, n_exp):
+def cpu_baseline(lay, cfg, training, n_exp, what=""):
     """The fp64 oracle, as it stands, on the routes of the first n_exp experts
     (all their tokens): forward (+ backward), wall time on the host cores."""
     import numpy as np
-    import torch
 
     from oracle import moe as om
+    from oracle import mx as omx
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    ora = omx if cfg.prec == "mxfp8" else om
     ids = lay["ids"].cpu().numpy()
     ids_s = np.where((ids >= 0) & (ids < n_exp), ids, -1).astype(np.int32)
     R_s = int((ids_s >= 0).sum())
@@ -227,15 +475,22 @@ def cpu_baseline(lay, cfg, training, n_exp):
     w13 = lay["w13"][:n_exp].cpu()
     w2 = lay["w2"][:n_exp].cpu()
     t0 = time.perf_counter()
-    y, cache = om.forward(x, ids_s, sc, w13, w2, keep=True)
+    y, cache = ora.forward(x, ids_s, sc, w13, w2, keep=True)
     if training:
-        om.backward(lay["dy"].cpu(), x, ids_s, sc, w13, w2, cache)
+        ora.backward(lay["dy"].cpu(), x, ids_s, sc, w13, w2, cache)
     dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
     flops = 6 * R_s * cfg.D * cfg.F * (3 if training else 1)
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"routes of experts 0..{n_exp - 1} ({R_s} of {int((ids >= 0).sum())} routes), "
-                      f"{'forward+backward' if training else 'forward'}, fp64 NumPy"}
+            "sample": f"{what}routes of experts 0..{n_exp - 1} ({R_s} of "
+                      f"{int((ids >= 0).sum())} routes), "
+                      f"{'forward+backward' if training else 'forward'}, fp64 NumPy"
+                      + (", quantization-faithful MXFP8" if cfg.prec == "mxfp8" else "")}
 
 
 if __name__ == "__main__":

@@ -367,3 +367,36 @@ class MoeLayer:
                 self.plan = None
         except Exception:
             pass
+
+
+class MoeStack:
+    """L routed-expert layers of one shape sharing one plan, one arena and
+    one scratch buffer: forwards in layer order, then backwards in reverse
+    order (each backward rewinds the arena to its layer's start)."""
+
+    def __init__(self, L, T_max, D, F, E, K, prec="mxfp8", dw_dtype=None, arena_budget=0,
+                 device="cuda"):
+        self.L = L
+        self.layer = MoeLayer(T_max, D, F, E, K, prec, dw_dtype, training=True, max_layers=L,
+                              arena_budget=arena_budget, device=device)
+        self.bufs = [self.layer.new_layer_buffers() for _ in range(L)]
+
+    def route(self, l, ids):
+        self.layer.route(ids, route_ws=self.bufs[l][0])
+
+    def forward(self, l, x, w13, w2, scores, y, prepared=None, y_addend=None):
+        rw, h3 = self.bufs[l]
+        self.layer.forward(x, w13, w2, layer=l, route_ws=rw, h3=h3, prepared=prepared)
+        self.layer.combine(scores, y, y_addend=y_addend, route_ws=rw, h3=h3)
+
+    def backward(self, l, x, scores, dy, w13, w2, dx, dw13, dw2, dscores=None, prepared=None,
+                 flags=0):
+        rw, h3 = self.bufs[l]
+        self.layer.backward(x, scores, dy, w13, w2, dx, dw13, dw2, dscores, layer=l, flags=flags,
+                            route_ws=rw, h3=h3, prepared=prepared)
+
+    def status(self, l):
+        return self.layer.status(route_ws=self.bufs[l][0])
+
+    def readback(self, l, T):
+        return self.layer.readback(T, route_ws=self.bufs[l][0])

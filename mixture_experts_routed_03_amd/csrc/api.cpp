@@ -150,8 +150,10 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
   hipError_t e = timed(p, tag, s, [&] { return launch_rowq(rx, p->R_max, s); });
   if (e != hipSuccess) return e;
   if (d.training) {
+    // A replaying layer's bundles are rebuilt in backward: the forward only
+    // writes them for a layer that saves.
     ColqArgs cx{hdr, offsets, poffsets, sc + L.x_rows, nullptr, nullptr, d.d, d.e,
-                -1, 0, 1, replay_only};
+                -1, 0, 1, replay_only ? 1 : 2};
     e = timed(p, replay_only ? "replay_bundle_x" : "bundle_x", s,
               [&] { return launch_colq(cx, p->Rp_max, s); });
     if (e != hipSuccess) return e;
@@ -165,7 +167,8 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
             [&] { return launch_mx_fwd(0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return e;
   if (d.training) {
-    ColqArgs ch{hdr, offsets, poffsets, sc + L.h2, nullptr, nullptr, d.f, d.e, -1, 2, 3, replay_only};
+    ColqArgs ch{hdr, offsets, poffsets, sc + L.h2, nullptr, nullptr, d.f, d.e, -1, 2, 3,
+                replay_only ? 1 : 2};
     e = timed(p, replay_only ? "replay_bundle_h2" : "bundle_h2", s,
               [&] { return launch_colq(ch, p->Rp_max, s); });
   }

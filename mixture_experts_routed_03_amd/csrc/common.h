@@ -148,7 +148,7 @@ struct ColqArgs {
   uint8_t* s;           // column-bundle exponents (sum_e N * Mp_e / 32 bytes)
   int N, E;
   int src_slot, q_slot, s_slot;
-  int replay_only;
+  int replay_only;      // 0 always, 1 only if the layer replays, 2 only if it saves
 };
 
 // Arguments of the device planner (one layer).

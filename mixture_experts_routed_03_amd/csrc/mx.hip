@@ -141,7 +141,9 @@ __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
 // bytes per row), writes 32 contiguous code bytes and one exponent.
 __global__ __launch_bounds__(256) void k_colq(ColqArgs a) {
   const RouteHdr* hdr = a.hdr;
-  if (a.replay_only && !hdr->rec.replay) return;
+  // replay_only: 1 = run only when the layer replays, 2 = only when it saves
+  if (a.replay_only == 1 && !hdr->rec.replay) return;
+  if (a.replay_only == 2 && hdr->rec.replay) return;
   const int gb = blockIdx.x;                 // 32-row block in the padded row space
   if (gb * 32 >= hdr->Rpad) return;
   const int col = blockIdx.y * 256 + threadIdx.x;

@@ -19,7 +19,8 @@ over the selected scores).  Recipe:
 * padding: exactly ``n_pad`` (token, slot) pairs, drawn uniformly without
   replacement, get id -1 and score 0.
 * dense tensors: N(0, std^2), rounded once to the storage dtype (round to
-  nearest even).  Weights use std = 1/sqrt(fan_in).
+  nearest even).  Weights use std = 1/sqrt(fan_in); each expert's matrix is
+  drawn from its own stream so one expert can be regenerated alone.
 
 CPU tensors come from NumPy PCG64; CUDA tensors from torch's device generator
 (much faster for the 34 GB of config-2 weights).  Either way a tensor is fully
@@ -118,6 +119,21 @@ def normal(shape, std: float, *, seed: int, dtype, device="cpu", chunk_rows: int
     return out
 
 
+def expert_normal(E, shape, std: float, *, seed: int, dtype, device="cpu", experts=None):
+    """Expert weights [E, *shape] ~ N(0, std^2), expert e drawn from its own
+    stream (seed, e), so any one expert can be regenerated alone.  With
+    ``experts`` only those experts are drawn (stacked in that order)."""
+    import torch
+
+    idx = range(E) if experts is None else list(experts)
+    out = torch.empty((len(idx),) + tuple(shape), dtype=dtype, device=torch.device(device))
+    for i, e in enumerate(idx):
+        ss = np.random.SeedSequence(entropy=seed, spawn_key=(int(e),))
+        es = int(ss.generate_state(2, dtype=np.uint64)[0] & np.uint64(0x7FFFFFFFFFFFFFFF))
+        out[i] = normal(shape, std, seed=es, dtype=dtype, device=device)
+    return out
+
+
 @dataclass(frozen=True)
 class Config:
     """One workload: layer shape, precision, routing recipe and phases."""
@@ -162,6 +178,15 @@ CONFIGS = {
 }
 
 
+def ten_layer_budget(cfg: Config) -> int:
+    """Arena budget of the ten-layer workload: 4.5 x the saved MXFP8 state of
+    one layer with R = T*K routes and R_pad = T*K + 16*E padded rows (x and
+    h2 column bundles with their exponents, BF16 h1), rounded up to 128 B."""
+    R, Rp, D, F = cfg.T * cfg.K, cfg.T * cfg.K + 16 * cfg.E, cfg.D, cfg.F
+    state = D * Rp + D * Rp // 32 + R * 2 * F * 2 + F * Rp + F * Rp // 32
+    return -(-int(4.5 * state) // 128) * 128
+
+
 def torch_dtype(prec: str):
     import torch
     return torch.float32 if prec == "f32" else torch.bfloat16
@@ -188,10 +213,8 @@ def make_layer(cfg: Config, layer: int = 0, device="cpu", *, T: int | None = Non
         "x": normal((T, cfg.D), 1.0, seed=stream_seed(cfg.seed, layer, "x"), dtype=dt, device=device),
     }
     if weights:
-        out["w13"] = normal((cfg.E, 2 * cfg.F, cfg.D), 1.0 / math.sqrt(cfg.D),
-                            seed=stream_seed(cfg.seed, layer, "w13"), dtype=dt, device=device)
-        out["w2"] = normal((cfg.E, cfg.D, cfg.F), 1.0 / math.sqrt(cfg.F),
-                           seed=stream_seed(cfg.seed, layer, "w2"), dtype=dt, device=device)
+        out["w13"] = layer_weight(cfg, layer, "w13", device)
+        out["w2"] = layer_weight(cfg, layer, "w2", device)
     if grads if grads is not None else cfg.training:
         out["dy"] = normal((T, cfg.D), 1.0, seed=stream_seed(cfg.seed, layer, "dy"), dtype=dt,
                            device=device)
@@ -203,6 +226,17 @@ def make_layer(cfg: Config, layer: int = 0, device="cpu", *, T: int | None = Non
                                   seed=stream_seed(cfg.seed, layer, "w2_shared"),
                                   dtype=torch.bfloat16, device=device)
     return out
+
+
+def layer_weight(cfg: Config, layer: int, name: str, device="cpu", experts=None):
+    """W13 [E, 2F, D] or W2 [E, D, F] of a layer (or the listed experts of it)."""
+    dt = torch_dtype(cfg.prec)
+    if name == "w13":
+        shape, std = (2 * cfg.F, cfg.D), 1.0 / math.sqrt(cfg.D)
+    else:
+        shape, std = (cfg.D, cfg.F), 1.0 / math.sqrt(cfg.F)
+    return expert_normal(cfg.E, shape, std, seed=stream_seed(cfg.seed, layer, name), dtype=dt,
+                         device=device, experts=experts)
 
 
 def scaled(cfg: Config, **kw) -> Config:

@@ -50,3 +50,20 @@ def decide(full_bytes, keep_bytes: int, capacity: int):
         flags.append(replay)
         cursor += int(keep_bytes) if replay else int(full)
     return flags, starts, tested
+
+
+def bf16_full_state_bytes(R: int, D: int, F: int, es: int = 2) -> int:
+    """This library's saved state of a BF16 (es = 2) or FP32 (es = 4) layer:
+    gathered x rows [R, D] and h1 [R, 2F], each aligned to 128 B (the route
+    outputs h3 live in the caller's slot buffer)."""
+    return align128(R * D * es) + align128(R * 2 * F * es)
+
+
+def mx_full_state_bytes(R: int, Rp: int, D: int, F: int) -> int:
+    """This library's saved state of an MXFP8 layer (explainer section 04:
+    MXFP8 full-save keeps the x and h2 column bundles and dense h1): x bundle
+    codes [D, Rp] and exponents [D, Rp/32], BF16 h1 [R, 2F], h2 bundle codes
+    [F, Rp] and exponents [F, Rp/32], each aligned to 128 B.  Rp = the rows
+    padded to 32 per expert."""
+    return (align128(D * Rp) + align128(D * Rp // 32) + align128(R * 2 * F * 2)
+            + align128(F * Rp) + align128(F * Rp // 32))

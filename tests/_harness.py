@@ -55,12 +55,34 @@ def check_route(got: dict, ids, E):
 
 
 def _expert_weights(lay, e, mx):
+    """fp64 weights of expert e (dequantized 32x32 MXFP8 values with mx);
+    memoized in lay["_wcache"] when the dict carries one."""
     from oracle import mx as omx
+    cache = lay.get("_wcache")
+    if cache is not None and (e, mx) in cache:
+        return cache[(e, mx)]
     w13 = om.as_f64(lay["w13"][e])
     w2 = om.as_f64(lay["w2"][e])
     if mx:
-        return omx.qdq_32x32(w13), omx.qdq_32x32(w2)
+        w13, w2 = omx.qdq_32x32(w13), omx.qdq_32x32(w2)
+    if cache is not None:
+        cache[(e, mx)] = (w13, w2)
     return w13, w2
+
+
+class RegenExperts:
+    """Stand-in for a layer's [E, ...] weight tensor whose device copy was
+    freed: expert e is drawn again from its own seeded stream (on the device
+    type it was first drawn on) when indexed."""
+
+    def __init__(self, cfg, layer, name, device="cuda"):
+        self.cfg, self.layer, self.name, self.device = cfg, layer, name, device
+        F, D = cfg.F, cfg.D
+        self.shape = (cfg.E, 2 * F, D) if name == "w13" else (cfg.E, D, F)
+
+    def __getitem__(self, e):
+        return wl.layer_weight(self.cfg, self.layer, self.name, self.device,
+                               experts=[int(e)])[0].cpu()
 
 
 def sampled_forward_ref(lay, tokens, mx=False):

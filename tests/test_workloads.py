@@ -40,3 +40,11 @@ def test_dense_tensors_are_seeded():
     lay = wl.make_layer(cfg)
     assert lay["x"].shape == (16, 256) and lay["w13"].shape == (8, 256, 256)
     assert lay["w2"].shape == (8, 256, 128) and lay["x"].dtype == torch.float32
+
+
+def test_single_expert_regenerates_alone():
+    cfg = wl.scaled(wl.CONFIGS["tiny_f32"], T=8)
+    full = wl.layer_weight(cfg, 2, "w13")
+    part = wl.layer_weight(cfg, 2, "w13", experts=[5, 1])
+    assert torch.equal(part[0], full[5]) and torch.equal(part[1], full[1])
+    assert not torch.equal(full[0], full[1])
