@@ -19,8 +19,9 @@ Workloads (all at T = 2,048 tokens, D = 7,168, F = 2,048, E = 384, top-6):
 
 Inputs are resident in HBM before timing starts.  Useful work is 6*R*D*F
 FLOPs forward and twice that backward per routed layer (R = valid routes;
-padding and replay excluded), the Dist-MoE explainer's count (section 07);
-a shared expert adds 6*T*D*F forward and twice that backward.
+padding, replay and shared experts excluded), the Dist-MoE explainer's count
+(section 07); the rate with the shared expert's 18*T*D*F counted is reported
+beside it.
 
 Prints ONE JSON line.  Also reports the dominant kernel against its roofline
 (per-kernel HIP-event timing over a second pass of the timed steps, on the
@@ -376,11 +377,12 @@ def main():
             ktimes[label + name] = (tot, n)
         B.moe_timing_enable(p.plan, False)
 
+    # Useful work: routed layers only (the Dist-MoE explainer's count, section
+    # 07, excludes shared experts, padding and replay); the shared expert's
+    # time stays in the step.
     mult = 3 if training else 1
-    useful = 0
-    for label, m in metas:
-        rows = m["R"]
-        useful += 6 * rows * m["D"] * m["F"] * mult
+    useful = sum(6 * m["R"] * m["D"] * m["F"] * mult for lab, m in metas if lab == "")
+    shared_flops = sum(6 * m["R"] * m["D"] * m["F"] * mult for lab, m in metas if lab != "")
     value = useful / (ms_step * 1e-3) / 1e12
 
     # per-kernel: algorithmic bytes and flops per step, time per step
@@ -449,6 +451,8 @@ def main():
                    "replayed_layers": [int(m["replay"]) for lab, m in metas if lab == ""],
                    "dw_dtype": "bf16" if m0["dwb"] == 2 else "f32", **info},
         "mfma_peak_frac": round(value / PEAK_TFLOPS[prec], 4),
+        "tflops_incl_shared_expert": (round((useful + shared_flops) / (ms_step * 1e-3) / 1e12, 2)
+                                      if shared_flops else None),
         "route_GBps": kernels.get("route", {}).get("GB/s"),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,

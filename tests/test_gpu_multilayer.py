@@ -83,7 +83,7 @@ def test_stacked_mx_layers_budget_and_parity(B, budget_factor):
     want_flags, want_starts, full = _oracle_plan(cfg, ids, budget)
     assert 0 < sum(want_flags) < cfg.layers or budget_factor < 1
     st, ys, grads = _run_stack(B, cfg, lays, budget)
-    free, fys, fgrads = _run_stack(B, cfg, lays, 1 << 40)
+    free, fys, fgrads = _run_stack(B, cfg, lays, sum(full))   # room for every layer
     for l in range(cfg.layers):
         status, replayed = st.status(l)
         assert status == 0
