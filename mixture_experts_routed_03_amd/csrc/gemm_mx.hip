@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   constexpr int kW = 128 * 128;      // weight stage: 128 rows x 128 E4M3 values
   constexpr int kA = kBM * 128;      // token stage: 64 rows x 128 values
   constexpr int kSc = kBM * 4;       // token scales of the stage: 4 blocks per row
-  constexpr int kStage = kW + kA + kSc;
+  constexpr int kStage = kW + kA + kSc + 16;   // + the weight scale dword of each wave
   __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,7 +134,6 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     const int mt = u - nt * mt_e;
     const int row0 = a.offsets[e] + mt * kBM;
     const int rows = min(kBM, a.offsets[e + 1] - row0);
-    const bool two = rows > 32;
 
     const uint8_t* wsrc[4];
 #pragma unroll
@@ -149,28 +148,26 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
                                 : nt * 128 + wave * 32;
     const uint32_t* wsc_src = reinterpret_cast<const uint32_t*>(
         a.sw + (int64_t(e) * (a.N / 32) + wrow0 / 32) * KB);
+    // Tile rows past the expert's last row re-read that row: every load is
+    // unconditional, and the extra output columns are never stored.
     const uint8_t* tsrc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = lrow + 32 * j;
-      tsrc[j] = r < rows ? a.qa + int64_t(row0 + r) * Kd + lc * 16 : nullptr;
-    }
+    for (int j = 0; j < 2; ++j)
+      tsrc[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kd + lc * 16;
     const uint32_t* tsc_src =
-        tid < rows ? reinterpret_cast<const uint32_t*>(a.sa + int64_t(row0 + tid) * KB) : nullptr;
+        reinterpret_cast<const uint32_t*>(a.sa + int64_t(row0 + min(tid & 63, rows - 1)) * KB);
 
     f32x16 acc0 = {}, acc1 = {};
     u32x4 R0[6], R1[6];
     uint32_t S0[2], S1[2];   // [0] weight scales of the wave, [1] token scales of row tid
-    uint32_t wsc[2];
     auto load = [&](u32x4* R, uint32_t* Sc, int s) {
       const int64_t off = int64_t(s) * 128;
 #pragma unroll
       for (int j = 0; j < 4; ++j) R[j] = *reinterpret_cast<const u32x4*>(wsrc[j] + off);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        R[4 + j] = tsrc[j] ? *reinterpret_cast<const u32x4*>(tsrc[j] + off) : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
       Sc[0] = wsc_src[s];
-      Sc[1] = tsc_src ? tsc_src[s] : 0x7f7f7f7fu;
+      Sc[1] = tsc_src[s];
     };
     auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
       char* base = lds + buf * kStage;
@@ -181,14 +178,17 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
       for (int j = 0; j < 2; ++j)
         *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
       if (tid < kBM) reinterpret_cast<uint32_t*>(base + kW + kA)[tid] = Sc[1];
-      wsc[buf] = Sc[0];
+      if (lane == 0) reinterpret_cast<uint32_t*>(base + kW + kA + kSc)[wave] = Sc[0];
     };
+    // Both 32-token halves are always multiplied: no accumulator depends on
+    // a branch inside the stage loop.
     auto compute = [&](int buf) {
       const char* wl = lds + buf * kStage;
       const char* tl = wl + kW;
       const uint32_t* tsc = reinterpret_cast<const uint32_t*>(tl + kA);
       const uint32_t ts0 = tsc[lr];
       const uint32_t ts1 = tsc[32 + lr];
+      const uint32_t wsc = tsc[kBM + wave];
       const int wrow = 32 * wave + lr;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -198,34 +198,33 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, cb));
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(tl + swz(lr, ca));
         const u32x4 b1 = *reinterpret_cast<const u32x4*>(tl + swz(lr, cb));
-        const int sa = byte_of(wsc[buf], blk);
+        const u32x4 d0 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, ca));
+        const u32x4 d1 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, cb));
+        const int sa = byte_of(wsc, blk);
         mfma_mx(acc0, a0, a1, b0, b1, sa, byte_of(ts0, blk));
-        if (two) {
-          const u32x4 d0 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, ca));
-          const u32x4 d1 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, cb));
-          mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
-        }
+        mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
       }
     };
 
+    // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
+    // s + 1 and R0 stage s + 2 (indices past the end repeat the last stage).
     load(R0, S0, 0);
-    if (S > 1) load(R1, S1, 1);
+    load(R1, S1, min(1, S - 1));
     store(R0, S0, 0);
-    if (S > 2) load(R0, S0, 2);
+    load(R0, S0, min(2, S - 1));
     lds_barrier();
-    for (int s = 0; s < S; s += 2) {
+    for (int s = 0; s + 1 < S; s += 2) {
       compute(0);
-      if (s + 1 < S) {
-        store(R1, S1, 1);
-        if (s + 3 < S) load(R1, S1, s + 3);
-      }
+      store(R1, S1, 1);
+      load(R1, S1, min(s + 3, S - 1));
       lds_barrier();
-      if (s + 1 >= S) break;
       compute(1);
-      if (s + 2 < S) {
-        store(R0, S0, 0);
-        if (s + 4 < S) load(R0, S0, s + 4);
-      }
+      store(R0, S0, 0);
+      load(R0, S0, min(s + 4, S - 1));
+      lds_barrier();
+    }
+    if (S & 1) {
+      compute(0);
       lds_barrier();
     }
 
@@ -309,7 +308,7 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
   constexpr int kW = 128 * 32 * 4;   // transposed weight stage: 128 columns x 128 values
   constexpr int kT = kBM * 128;      // token stage
   constexpr int kSc = kBM * 4;
-  constexpr int kStage = kW + kT + kSc;
+  constexpr int kStage = kW + kT + kSc + 16;   // + the weight scale dword of each wave
   __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -343,37 +342,33 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
     const int mt = u - nt * mt_e;
     const int row0 = a.offsets[e] + mt * kBM;
     const int rows = min(kBM, a.offsets[e + 1] - row0);
-    const bool two = rows > 32;
 
     const uint8_t* wsrc = a.qw + (int64_t(e) * Kd + 4 * kq) * N + nt * 128 + c16 * 16;
     // the wave's 32 output columns are one scale column block; 4 blocks along k per stage
     const uint8_t* wsc_src = a.sw + int64_t(e) * KB * (N / 32) + (nt * 128 + 32 * wave) / 32;
+    // Tile rows past the expert's last row re-read that row (outputs not stored).
     const uint8_t* tsrc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = lrow + 32 * j;
-      tsrc[j] = r < rows ? a.qa + int64_t(row0 + r) * Kd + lc * 16 : nullptr;
-    }
+    for (int j = 0; j < 2; ++j)
+      tsrc[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kd + lc * 16;
     const uint32_t* tsc_src =
-        tid < rows ? reinterpret_cast<const uint32_t*>(a.sa + int64_t(row0 + tid) * KB) : nullptr;
+        reinterpret_cast<const uint32_t*>(a.sa + int64_t(row0 + min(tid & 63, rows - 1)) * KB);
 
     f32x16 acc0 = {}, acc1 = {};
     u32x4 R0[6], R1[6];
     uint32_t S0[2], S1[2];
-    uint32_t wsc[2];
     auto load = [&](u32x4* R, uint32_t* Sc, int s) {
       const uint8_t* p = wsrc + int64_t(s) * 128 * N;
 #pragma unroll
       for (int i = 0; i < 4; ++i) R[i] = *reinterpret_cast<const u32x4*>(p + i * N);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        R[4 + j] = tsrc[j] ? *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128)
-                           : u32x4{0u, 0u, 0u, 0u};
+        R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
       uint32_t ws = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) ws |= uint32_t(wsc_src[int64_t(4 * s + i) * (N / 32)]) << (8 * i);
       Sc[0] = ws;
-      Sc[1] = tsc_src ? tsc_src[s] : 0x7f7f7f7fu;
+      Sc[1] = tsc_src[s];
     };
     auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
       uint32_t* la = reinterpret_cast<uint32_t*>(lds + buf * kStage);
@@ -388,7 +383,7 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
       if (tid < kBM) reinterpret_cast<uint32_t*>(lt + kT)[tid] = Sc[1];
-      wsc[buf] = Sc[0];
+      if (lane == 0) reinterpret_cast<uint32_t*>(lt + kT + kSc)[wave] = Sc[0];
     };
     auto compute = [&](int buf) {
       const char* la = lds + buf * kStage;
@@ -396,6 +391,7 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
       const uint32_t* tsc = reinterpret_cast<const uint32_t*>(lt + kT);
       const uint32_t ts0 = tsc[lr];
       const uint32_t ts1 = tsc[32 + lr];
+      const uint32_t wsc = tsc[kBM + wave];
       const int orow = 32 * wave + lr;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -405,34 +401,32 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + tsw_g(orow, gb) * 4);
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(lt + swz(lr, ga));
         const u32x4 b1 = *reinterpret_cast<const u32x4*>(lt + swz(lr, gb));
-        const int sa = byte_of(wsc[buf], blk);
+        const u32x4 d0 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, ga));
+        const u32x4 d1 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, gb));
+        const int sa = byte_of(wsc, blk);
         mfma_mx(acc0, a0, a1, b0, b1, sa, byte_of(ts0, blk));
-        if (two) {
-          const u32x4 d0 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, ga));
-          const u32x4 d1 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, gb));
-          mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
-        }
+        mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
       }
     };
 
+    // Same pipeline as the forward kernel.
     load(R0, S0, 0);
-    if (S > 1) load(R1, S1, 1);
+    load(R1, S1, min(1, S - 1));
     store(R0, S0, 0);
-    if (S > 2) load(R0, S0, 2);
+    load(R0, S0, min(2, S - 1));
     lds_barrier();
-    for (int s = 0; s < S; s += 2) {
+    for (int s = 0; s + 1 < S; s += 2) {
       compute(0);
-      if (s + 1 < S) {
-        store(R1, S1, 1);
-        if (s + 3 < S) load(R1, S1, s + 3);
-      }
+      store(R1, S1, 1);
+      load(R1, S1, min(s + 3, S - 1));
       lds_barrier();
-      if (s + 1 >= S) break;
       compute(1);
-      if (s + 2 < S) {
-        store(R0, S0, 0);
-        if (s + 4 < S) load(R0, S0, s + 4);
-      }
+      store(R0, S0, 0);
+      load(R0, S0, min(s + 4, S - 1));
+      lds_barrier();
+    }
+    if (S & 1) {
+      compute(0);
       lds_barrier();
     }
 
