@@ -196,6 +196,15 @@ __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __ex
 // barrier waits for this wave's LDS operations but not for its outstanding
 // global loads or stores: prefetched tiles stay in flight across it (a full
 // __syncthreads() drains every outstanding global access on gfx9).
+// A device address held in memory (the layer record) as a pointer the
+// compiler knows to be global: accesses through it become global rather than
+// flat instructions, and flat ones also count against the LDS wait counter,
+// which would make every LDS wait drain the outstanding prefetches.
+template <typename T>
+__device__ __forceinline__ T* global_ptr(uint64_t addr) {
+  return (T*)(T __attribute__((address_space(1)))*)(addr);
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();

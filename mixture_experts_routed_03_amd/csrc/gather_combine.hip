@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_gather(const u32x4* __restrict__ x, int
     if (row == 0 && lane == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(hdr->rec.x_rows) + row * row_chunks;
+  u32x4* dst = global_ptr<u32x4>(hdr->rec.x_rows) + row * row_chunks;
   const int64_t t = sorted_route[row] / K;
   const u32x4* src = x + t * row_chunks;
   for (int64_t i = lane; i < row_chunks; i += 64) dst[i] = src[i];

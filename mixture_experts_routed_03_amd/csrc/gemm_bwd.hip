@@ -39,6 +39,7 @@
 //    of one XCD write long contiguous runs of dW rows.
 //  * Persistent, XCD-aware grids as in the forward kernels.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
   const int chunk = (n_items + kXcds - 1) / kXcds;
   const int S = a.Kd / 64;
   const int64_t N = a.N;
-  const uint16_t* h1 = reinterpret_cast<const uint16_t*>(hdr->rec.h1);
+  const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
   for (int it = slot; it < chunk; it += per) {
     const int w = xcd * chunk + it;
@@ -144,18 +145,15 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
     const int mt = u - nt * mt_e;
     const int row0 = a.offsets[e] + mt * kBM;
     const int rows = min(kBM, a.offsets[e + 1] - row0);
-    const bool two = rows > 32;
 
     const uint16_t* wsrc = reinterpret_cast<const uint16_t*>(a.W) +
                            (int64_t(e) * a.Kd + 2 * kp) * N + nt * 128 + c16 * 8;
+    // Tile rows past the expert's last row re-read that row (outputs not stored).
     const char* tsrc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = lrow + 32 * j;
-      tsrc[j] = r < rows ? reinterpret_cast<const char*>(a.tok) +
-                               (int64_t(row0 + r) * a.Kd) * 2 + lc * 16
-                         : nullptr;
-    }
+    for (int j = 0; j < 2; ++j)
+      tsrc[j] = reinterpret_cast<const char*>(a.tok) +
+                int64_t(row0 + min(lrow + 32 * j, rows - 1)) * a.Kd * 2 + lc * 16;
 
     f32x16 acc0 = {}, acc1 = {};
     u32x4 R0[6], R1[6];
@@ -167,8 +165,7 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
       R[3] = *reinterpret_cast<const u32x4*>(p + 33 * N);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        R[4 + j] = tsrc[j] ? *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128)
-                           : u32x4{0u, 0u, 0u, 0u};
+        R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
     };
     auto store = [&](const u32x4* R, int buf) {
       uint32_t* la = reinterpret_cast<uint32_t*>(lds + buf * kStage);
@@ -183,7 +180,10 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
     };
-    auto compute = [&](int buf) {
+    // TWO: the tile has more than 32 rows (one loop copy per case, so no
+    // accumulator depends on a branch inside the stage loop).
+    auto compute = [&](int buf, auto two_c) {
+      constexpr bool TWO = decltype(two_c)::value;
       const char* la = lds + buf * kStage;
       const char* lt = la + kW;
       const int orow = 32 * wave + lr;
@@ -193,33 +193,39 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
         const u32x4 av = *reinterpret_cast<const u32x4*>(la + tsw_g(orow, g) * 4);
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(lt + swz(lr, g));
         mfma_bf16(acc0, av, b0);
-        if (two) {
+        if (TWO) {
           const u32x4 b1 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, g));
           mfma_bf16(acc1, av, b1);
         }
       }
     };
-
-    load(R0, 0);
-    if (S > 1) load(R1, 1);
-    store(R0, 0);
-    if (S > 2) load(R0, 2);
-    lds_barrier();
-    for (int s = 0; s < S; s += 2) {
-      compute(0);
-      if (s + 1 < S) {
+    // Pipeline as in the forward kernels: LDS buffer 0 holds stage s, R1
+    // stage s + 1 and R0 stage s + 2 (indices past the end repeat the last).
+    auto run = [&](auto two_c) {
+      load(R0, 0);
+      load(R1, min(1, S - 1));
+      store(R0, 0);
+      load(R0, min(2, S - 1));
+      lds_barrier();
+      for (int s = 0; s + 1 < S; s += 2) {
+        compute(0, two_c);
         store(R1, 1);
-        if (s + 3 < S) load(R1, s + 3);
-      }
-      lds_barrier();
-      if (s + 1 >= S) break;
-      compute(1);
-      if (s + 2 < S) {
+        load(R1, min(s + 3, S - 1));
+        lds_barrier();
+        compute(1, two_c);
         store(R0, 0);
-        if (s + 4 < S) load(R0, s + 4);
+        load(R0, min(s + 4, S - 1));
+        lds_barrier();
       }
-      lds_barrier();
-    }
+      if (S & 1) {
+        compute(0, two_c);
+        lds_barrier();
+      }
+    };
+    if (rows > 32)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
 
     // acc[b][v]: output column 32*wave + 8*(v/4) + 4*lh + v%4, token 32*b + lr
     const int col = nt * 128 + 32 * wave + 4 * lh;
@@ -291,8 +297,8 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   const int chunk = (n_items + kXcds - 1) / kXcds;
-  const uint16_t* asrc = reinterpret_cast<const uint16_t*>(a.arows ? a.arows
-                                                                   : (const void*)hdr->rec.x_rows);
+  const uint16_t* asrc = a.arows ? reinterpret_cast<const uint16_t*>(a.arows)
+                                 : global_ptr<const uint16_t>(hdr->rec.x_rows);
   const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(a.grad);
 
   struct Item {

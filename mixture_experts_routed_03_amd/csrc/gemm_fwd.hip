@@ -36,6 +36,8 @@
 //    m-tiles sharing a weight tile are adjacent.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -120,8 +122,8 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
   const RouteHdr* hdr = a.hdr;
   if (a.replay_only && !hdr->rec.replay) return;
   const int n_items = hdr->n_mt * a.NT;
-  const char* Abase = reinterpret_cast<const char*>(a.A ? a.A : (const void*)hdr->rec.x_rows);
-  T* out0 = reinterpret_cast<T*>(a.out0 ? a.out0 : (void*)hdr->rec.h1);
+  const char* Abase = a.A ? reinterpret_cast<const char*>(a.A) : global_ptr<const char>(hdr->rec.x_rows);
+  T* out0 = a.out0 ? reinterpret_cast<T*>(a.out0) : global_ptr<T>(hdr->rec.h1);
   T* out1 = reinterpret_cast<T*>(a.out1);
   const int64_t row_bytes = int64_t(a.Kd) * ES;
 
@@ -141,9 +143,10 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
     const int mt = u - nt * mt_e;
     const int row0 = a.offsets[e] + mt * kBM;
     const int rows = min(kBM, a.offsets[e + 1] - row0);
-    const bool two = rows > 32;
 
     // Global sources of this thread's four weight chunks and two token chunks.
+    // Tile rows past the expert's last row re-read that row: the loads are
+    // unconditional and the extra output columns are never stored.
     const char* wsrc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -154,10 +157,8 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
     }
     const char* tsrc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = lrow + 32 * j;
-      tsrc[j] = r < rows ? Abase + int64_t(row0 + r) * row_bytes + lc * 16 : nullptr;
-    }
+    for (int j = 0; j < 2; ++j)
+      tsrc[j] = Abase + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * row_bytes + lc * 16;
 
     f32x16 acc0 = {}, acc1 = {};
     u32x4 R0[6], R1[6];
@@ -166,8 +167,7 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) R[j] = *reinterpret_cast<const u32x4*>(wsrc[j] + off);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        R[4 + j] = tsrc[j] ? *reinterpret_cast<const u32x4*>(tsrc[j] + off) : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
     };
     auto store = [&](const u32x4* R, int buf) {
       char* base = lds + buf * kStage;
@@ -178,7 +178,10 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
       for (int j = 0; j < 2; ++j)
         *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
     };
-    auto compute = [&](int buf) {
+    // TWO (a compile-time flag per loop copy): the tile has more than 32
+    // rows, so the second 32-token half is multiplied too.
+    auto compute = [&](int buf, auto two_c) {
+      constexpr bool TWO = decltype(two_c)::value;
       const char* wl = lds + buf * kStage;
       const char* tl = wl + kW;
       const int wrow = 32 * wave + lr;
@@ -190,39 +193,40 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
           const int c = 4 * lh + q * kV + v;
           av[v] = *reinterpret_cast<const u32x4*>(wl + swz(wrow, c));
           b0[v] = *reinterpret_cast<const u32x4*>(tl + swz(lr, c));
+          if (TWO) b1[v] = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, c));
         }
         Mma<T>::step(acc0, av, b0);
-        if (two) {
-#pragma unroll
-          for (int v = 0; v < kV; ++v)
-            b1[v] = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, 4 * lh + q * kV + v));
-          Mma<T>::step(acc1, av, b1);
-        }
+        if (TWO) Mma<T>::step(acc1, av, b1);
       }
     };
 
-    // Pipeline: stage s computes from LDS while stages s+1 and s+2 are in
-    // flight in registers (stage k lives in R[k % 2] until stored).
-    load(R0, 0);
-    if (S > 1) load(R1, 1);
-    store(R0, 0);
-    if (S > 2) load(R0, 2);
-    lds_barrier();
-    for (int s = 0; s < S; s += 2) {
-      compute(0);
-      if (s + 1 < S) {
+    // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
+    // s + 1 and R0 stage s + 2 (indices past the end repeat the last stage).
+    auto run = [&](auto two_c) {
+      load(R0, 0);
+      load(R1, min(1, S - 1));
+      store(R0, 0);
+      load(R0, min(2, S - 1));
+      lds_barrier();
+      for (int s = 0; s + 1 < S; s += 2) {
+        compute(0, two_c);
         store(R1, 1);
-        if (s + 3 < S) load(R1, s + 3);
-      }
-      lds_barrier();
-      if (s + 1 >= S) break;
-      compute(1);
-      if (s + 2 < S) {
+        load(R1, min(s + 3, S - 1));
+        lds_barrier();
+        compute(1, two_c);
         store(R0, 0);
-        if (s + 4 < S) load(R0, s + 4);
+        load(R0, min(s + 4, S - 1));
+        lds_barrier();
       }
-      lds_barrier();
-    }
+      if (S & 1) {
+        compute(0, two_c);
+        lds_barrier();
+      }
+    };
+    if (rows > 32)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
 
     // ---------------------------------------------------------- epilogue
     // acc[b][v] is C[weight row 8*(v/4) + 4*lh + v%4][token 32*b + lr].

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   const RouteHdr* hdr = a.hdr;
   if (a.replay_only && !hdr->rec.replay) return;
   const int n_items = hdr->n_mt * a.NT;
-  uint16_t* out0 = reinterpret_cast<uint16_t*>(a.out0 ? a.out0 : (void*)hdr->rec.h1);
+  uint16_t* out0 = a.out0 ? reinterpret_cast<uint16_t*>(a.out0) : global_ptr<uint16_t>(hdr->rec.h1);
   uint16_t* out1 = reinterpret_cast<uint16_t*>(a.out1);
   const int Kd = a.Kd;
   const int KB = Kd / 32;           // scale bytes per row
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
   const int KB = Kd / 32;
   const int S = Kd / 128;
   const int64_t N = a.N;
-  const uint16_t* h1 = reinterpret_cast<const uint16_t*>(hdr->rec.h1);
+  const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
   for (int it = slot; it < chunk; it += per) {
     const int w = xcd * chunk + it;
@@ -503,8 +503,8 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   const int chunk = (n_items + kXcds - 1) / kXcds;
-  const uint8_t* qa = a.a_slot >= 0 ? reinterpret_cast<const uint8_t*>(rec_ptr_m(hdr, a.a_slot)) : a.qa;
-  const uint8_t* sa = a.a_slot >= 0 ? reinterpret_cast<const uint8_t*>(rec_ptr_m(hdr, a.a_slot + 1)) : a.sa;
+  const uint8_t* qa = a.a_slot >= 0 ? global_ptr<const uint8_t>(rec_ptr_m(hdr, a.a_slot)) : a.qa;
+  const uint8_t* sa = a.a_slot >= 0 ? global_ptr<const uint8_t>(rec_ptr_m(hdr, a.a_slot + 1)) : a.sa;
   const uint8_t* qb = a.qb;
   const uint8_t* sb = a.sb;
 

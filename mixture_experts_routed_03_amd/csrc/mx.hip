@@ -103,10 +103,10 @@ __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= hdr->R) return;
-  const uint16_t* src = reinterpret_cast<const uint16_t*>(
-      a.src_slot >= 0 ? (const void*)rec_ptr(hdr, a.src_slot) : a.src);
-  uint8_t* q = a.q_slot >= 0 ? reinterpret_cast<uint8_t*>(rec_ptr(hdr, a.q_slot)) : a.q;
-  uint8_t* s = a.s_slot >= 0 ? reinterpret_cast<uint8_t*>(rec_ptr(hdr, a.s_slot)) : a.s;
+  const uint16_t* src = a.src_slot >= 0 ? global_ptr<const uint16_t>(rec_ptr(hdr, a.src_slot))
+                                         : reinterpret_cast<const uint16_t*>(a.src);
+  uint8_t* q = a.q_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.q_slot)) : a.q;
+  uint8_t* s = a.s_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.s_slot)) : a.s;
   const int N = a.N;
   for (int c0 = lane * 8; c0 < N; c0 += 512) {
     const u32x4 raw = *reinterpret_cast<const u32x4*>(src + row * N + c0);
@@ -163,10 +163,10 @@ __global__ __launch_bounds__(256) void k_colq(ColqArgs a) {
   const int mb = (gb * 32 - pbase) / 32;     // block index inside the expert
   const int r0 = a.offsets[e] + mb * 32;
   const int rows = min(32, a.offsets[e + 1] - r0);
-  const uint16_t* src = reinterpret_cast<const uint16_t*>(
-      a.src_slot >= 0 ? (const void*)rec_ptr(hdr, a.src_slot) : a.src);
-  uint8_t* q = a.q_slot >= 0 ? reinterpret_cast<uint8_t*>(rec_ptr(hdr, a.q_slot)) : a.q;
-  uint8_t* s = a.s_slot >= 0 ? reinterpret_cast<uint8_t*>(rec_ptr(hdr, a.s_slot)) : a.s;
+  const uint16_t* src = a.src_slot >= 0 ? global_ptr<const uint16_t>(rec_ptr(hdr, a.src_slot))
+                                         : reinterpret_cast<const uint16_t*>(a.src);
+  uint8_t* q = a.q_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.q_slot)) : a.q;
+  uint8_t* s = a.s_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.s_slot)) : a.s;
   const int N = a.N;
   float v[32];
   float amax = 0.0f;
