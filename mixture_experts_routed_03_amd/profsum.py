@@ -76,18 +76,26 @@ def main(argv):
               f"Calibration: one plain {probe_mib} MiB device copy reads FETCH_SIZE = {fmax:.0f} KiB "
               f"and writes WRITE_SIZE = {wmax:.0f} KiB, so FETCH_SIZE is scaled by {f_scale:.3f} "
               f"and WRITE_SIZE by {w_scale:.3f} to get bytes.  Mean over the dispatches of each "
-              f"kernel.", "",
+              f"kernel that moved at least 1% of its largest dispatch's bytes (the others are "
+              f"replay launches that exit at once; the kernel-stats averages above include "
+              f"them).", "",
               "| kernel | dispatches | read GB | write GB |", "|---|---:|---:|---:|"]
     traffic = {}
     for k in sorted(F):
         if "moe::" not in k:
             continue
-        fv = sum(F[k]) / len(F[k]) * 1024 * f_scale
-        wl = W.get(k, [0.0])
-        wv = sum(wl) / len(wl) * 1024 * w_scale
+        fl, wl = F[k], W.get(k, [0.0] * len(F[k]))
+        if len(wl) != len(fl):
+            wl = [sum(wl) / len(wl)] * len(fl)
+        tot = [f * f_scale + w * w_scale for f, w in zip(fl, wl)]
+        # dispatches that exit at once (a replay kernel of a layer that saved
+        # its state) are left out of the mean
+        big = [i for i, t in enumerate(tot) if t >= 0.01 * max(tot)]
+        fv = sum(fl[i] for i in big) / len(big) * 1024 * f_scale
+        wv = sum(wl[i] for i in big) / len(big) * 1024 * w_scale
         if fv + wv < 1e6:
             continue
-        lines.append(f"| `{k}` | {len(F[k])} | {fv / 1e9:.3f} | {wv / 1e9:.3f} |")
+        lines.append(f"| `{k}` | {len(big)} of {len(fl)} | {fv / 1e9:.3f} | {wv / 1e9:.3f} |")
         traffic[k] = [round(fv + wv)]
     lines += ["", "Machine-readable (bytes per dispatch; source hashes of the kernels measured):",
               "", "```json",
