@@ -344,26 +344,43 @@ def main():
     torch.cuda.synchronize()
     metas = meta_fn()
 
+    copy_gbs = None
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20) // 4
         src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        c0.record()
         dst.copy_(src)  # reads and writes copy_probe_mb MiB each
+        c1.record()
         torch.cuda.synchronize()
+        copy_gbs = round(2 * n * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
         del src, dst
 
-    # ---- timed region: K steps, bracketed by synchronize on both sides
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed region: K steps, bracketed by synchronize on both sides; an
+    # event at each window boundary (up to 5 windows) gives window means
+    n_win = min(5, args.steps)
+    bounds = [round(i * args.steps / n_win) for i in range(n_win + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    torch.cuda.reset_peak_memory_stats()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
+    host = 0.0
+    evs[0].record()
+    w = 1
+    for i in range(args.steps):
+        h0 = time.perf_counter()
         step()
-    stop.record()
+        host += time.perf_counter() - h0
+        if i + 1 == bounds[w]:
+            evs[w].record()
+            w += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(stop) / args.steps
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    win_ms = [evs[i].elapsed_time(evs[i + 1]) / (bounds[i + 1] - bounds[i]) for i in range(n_win)]
+    peak_gib = torch.cuda.max_memory_allocated() / 2**30
 
     # ---- second pass with per-kernel events (on the library's launch stream)
     for p in plans.values():
@@ -423,6 +440,16 @@ def main():
                 "alg_bytes_per_launch": int(alg_per_launch),
                 "avg_launch_ms": kernels[dom]["avg_ms"]}
 
+    # Whole-step roofline: t* = max(useful FLOPs / MFMA peak, algorithmic
+    # bytes of every modelled kernel / HBM peak).
+    alg_step = sum(k.get("alg_bytes_per_step", 0) for k in kernels.values())
+    t_flop = useful / (PEAK_TFLOPS[cfg.prec] * 1e12) * 1e3
+    t_byte = alg_step / (PEAK_HBM_GBS * 1e9) * 1e3
+    step_roof = {"t_star_ms": round(max(t_flop, t_byte), 4),
+                 "bound": "hbm" if t_byte >= t_flop else "mfma",
+                 "alg_bytes_per_step": int(alg_step),
+                 "frac": round(max(t_flop, t_byte) / ms_step, 4)}
+
     cpu = None if args.no_cpu_baseline else cpu_fn()
 
     m0 = metas[0][1]
@@ -455,6 +482,12 @@ def main():
                                       if shared_flops else None),
         "route_GBps": kernels.get("route", {}).get("GB/s"),
         "wall_s_timed": round(wall, 3),
+        "window_ms_per_step": [round(v, 4) for v in win_ms],
+        "median_window_ms": round(sorted(win_ms)[len(win_ms) // 2], 4),
+        "host_enqueue_ms_per_step": round(host / args.steps * 1e3, 3),
+        "peak_device_GiB": round(peak_gib, 2),
+        "copy_probe_GBps": copy_gbs,
+        "step_roofline": step_roof,
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -228,4 +228,27 @@ template <> struct Elem<uint16_t> {
 // Number of XCDs of the MI355X; workgroups are dispatched round-robin over them.
 constexpr int kXcds = 8;
 
+// First weight-gradient work item of XCD x.  Items run expert-major, per_e
+// per expert; an item of expert e costs its 64-row contraction stages
+// (mtoff[e + 1] - mtoff[e]) plus one for storing its output tile, and the
+// XCDs receive equal shares of the total cost, so one hot expert does not
+// load a single XCD.  x = kXcds gives the item count.
+__device__ inline int xcd_first_item(const int32_t* __restrict__ mtoff, int E, int per_e, int x) {
+  const int64_t W = int64_t(per_e) * (mtoff[E] + E);
+  const int64_t T = W * x / kXcds;
+  int lo = 0, hi = E;  // the largest e with per_e * (mtoff[e] + e) <= T
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (int64_t(per_e) * (mtoff[mid] + mid) <= T)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  if (lo >= E) return E * per_e;
+  const int64_t P = int64_t(per_e) * (mtoff[lo] + lo);
+  const int64_t c = int64_t(mtoff[lo + 1] - mtoff[lo]) + 1;
+  const int64_t i = (T - P + c - 1) / c;
+  return int(min(int64_t(lo) * per_e + i, int64_t(E) * per_e));
+}
+
 }  // namespace moe

@@ -296,7 +296,8 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
-  const int chunk = (n_items + kXcds - 1) / kXcds;
+  const int first = xcd_first_item(a.mtoff, a.E, per_e, xcd);
+  const int last = xcd_first_item(a.mtoff, a.E, per_e, xcd + 1);
   const uint16_t* asrc = a.arows ? reinterpret_cast<const uint16_t*>(a.arows)
                                  : global_ptr<const uint16_t>(hdr->rec.x_rows);
   const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(a.grad);
@@ -304,14 +305,14 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
   struct Item {
     int e, ta, tb, r0, Me, S;
   };
-  // Work items of this workgroup are w = xcd*chunk + it for it = slot, slot +
-  // per, ...; (e, tb, ta) advance by carries instead of a division per item.
-  int w0 = xcd * chunk + slot;
+  // Work items of this workgroup are w = first + slot + i * per below last;
+  // (e, tb, ta) advance by carries instead of a division per item.
+  int w0 = first + slot;
   int ie = w0 / per_e;
   int irem = w0 - ie * per_e;
   int itb = irem / NA;
   int ita = irem - itb * NA;
-  const int wend = min(xcd * chunk + chunk, n_items);
+  const int wend = last;
   int wcur = w0;
   auto fill = [&](Item& t) {
     if (wcur >= wend) {

@@ -502,7 +502,8 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
-  const int chunk = (n_items + kXcds - 1) / kXcds;
+  const int first = xcd_first_item(a.mtoff, a.E, per_e, xcd);
+  const int last = xcd_first_item(a.mtoff, a.E, per_e, xcd + 1);
   const uint8_t* qa = a.a_slot >= 0 ? global_ptr<const uint8_t>(rec_ptr_m(hdr, a.a_slot)) : a.qa;
   const uint8_t* sa = a.a_slot >= 0 ? global_ptr<const uint8_t>(rec_ptr_m(hdr, a.a_slot + 1)) : a.sa;
   const uint8_t* qb = a.qb;
@@ -511,12 +512,12 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
   struct Item {
     int e, ta, tb, pb, mp, S;
   };
-  int w0 = xcd * chunk + slot;
+  int w0 = first + slot;
   int ie = w0 / per_e;
   int irem = w0 - ie * per_e;
   int itb = irem / NA;
   int ita = irem - itb * NA;
-  const int wend = min(xcd * chunk + chunk, n_items);
+  const int wend = last;
   int wcur = w0;
   auto fill = [&](Item& t) {
     if (wcur >= wend) {
