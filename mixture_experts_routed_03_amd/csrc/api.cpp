@@ -146,7 +146,8 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const char* tag = replay_only ? "replay_quant_x" : "quant_x";
   RowqArgs rx{hdr, sc + L.x_rows, reinterpret_cast<uint8_t*>(sc + L.qx),
-              reinterpret_cast<uint8_t*>(sc + L.sx), d.d, -1, -1, -1, replay_only};
+              reinterpret_cast<uint8_t*>(sc + L.sx), d.d, -1, -1, -1, replay_only,
+              int(p->R_max)};
   hipError_t e = timed(p, tag, s, [&] { return launch_rowq(rx, p->R_max, s); });
   if (e != hipSuccess) return e;
   if (d.training) {
@@ -162,7 +163,7 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
              reinterpret_cast<const uint8_t*>(sc + L.qx), reinterpret_cast<const uint8_t*>(sc + L.sx),
              reinterpret_cast<const uint8_t*>(w->q13), reinterpret_cast<const uint8_t*>(w->s13),
              nullptr, nullptr, nullptr, sc + L.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, 0, -1,
-             replay_only};
+             replay_only, int(p->R_max)};
   e = timed(p, replay_only ? "replay_w13" : "w13_swiglu", s,
             [&] { return launch_mx_fwd(0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return e;
@@ -198,7 +199,7 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const m
                               d.k, d.d, d.t_max, s);
   });
   if (e != hipSuccess) return MOE_ERR_HIP;
-  RowqArgs r3{hdr, sc + L.dh3, u8(L.qdh3), u8(L.sdh3), d.d, -1, -1, -1, 0};
+  RowqArgs r3{hdr, sc + L.dh3, u8(L.qdh3), u8(L.sdh3), d.d, -1, -1, -1, 0, int(p->R_max)};
   e = timed(p, "quant_dh3", s, [&] { return launch_rowq(r3, p->R_max, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   ColqArgs c3{hdr, offsets, poffsets, sc + L.dh3, u8(L.dh3cq), u8(L.dh3cs), d.d, d.e, -1, -1, -1, 0};
@@ -206,14 +207,15 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const m
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs dg2{hdr, offsets, poffsets, mtoff, sorted_route, u8(L.qdh3), u8(L.sdh3),
              reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
-             nullptr, nullptr, sc + L.dh1, nullptr, d.d, d.f, d.f, d.f / 128, d.e, 0, 0, -1, 0};
+             nullptr, nullptr, sc + L.dh1, nullptr, d.d, d.f, d.f, d.f / 128, d.e, 0, 0, -1, 0,
+             int(p->R_max)};
   e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_mx_dgrad(0, dg2, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs wg2{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
              u8(L.dh3cq), u8(L.dh3cs), g->dw2, nullptr, 0, 0, d.f, 0, d.e, d.f, d.d, 2, 0};
   e = timed(p, "w2_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 2, wg2, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
-  RowqArgs r1{hdr, sc + L.dh1, u8(L.qdh1), u8(L.sdh1), 2 * d.f, -1, -1, -1, 0};
+  RowqArgs r1{hdr, sc + L.dh1, u8(L.qdh1), u8(L.sdh1), 2 * d.f, -1, -1, -1, 0, int(p->R_max)};
   e = timed(p, "quant_dh1", s, [&] { return launch_rowq(r1, p->R_max, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   ColqArgs c1{hdr, offsets, poffsets, sc + L.dh1, u8(L.dh1cq), u8(L.dh1cs), 2 * d.f, d.e,
@@ -222,7 +224,8 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const m
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs dg13{hdr, offsets, poffsets, mtoff, sorted_route, u8(L.qdh1), u8(L.sdh1),
               reinterpret_cast<const uint8_t*>(w->q13), reinterpret_cast<const uint8_t*>(w->s13),
-              nullptr, nullptr, sc + L.dxr, nullptr, 2 * d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0};
+              nullptr, nullptr, sc + L.dxr, nullptr, 2 * d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
+              int(p->R_max)};
   e = timed(p, "w13_dgrad", s, [&] { return launch_mx_dgrad(1, dg13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs wg13{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
@@ -492,13 +495,14 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   // h2 -> 1x32 row blocks for the W2 GEMM
   RowqArgs rq{hdr, sc + L.h2, reinterpret_cast<uint8_t*>(sc + L.qh2),
-              reinterpret_cast<uint8_t*>(sc + L.sh2), d.f, -1, -1, -1, 0};
+              reinterpret_cast<uint8_t*>(sc + L.sh2), d.f, -1, -1, -1, 0, int(p->R_max)};
   e = timed(p, "quant_h2", s, [&] { return launch_rowq(rq, p->R_max, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs a2{hdr, offsets, poffsets, mtoff, sorted_route,
             reinterpret_cast<const uint8_t*>(sc + L.qh2), reinterpret_cast<const uint8_t*>(sc + L.sh2),
             reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
-            nullptr, nullptr, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0};
+            nullptr, nullptr, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
+            int(p->R_max)};
   return hip_status(timed(p, "w2_scatter", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); }));
 }
 

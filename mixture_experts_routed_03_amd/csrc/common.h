@@ -126,6 +126,7 @@ struct MxArgs {
   int a_ld, b_ld;       // WGRAD row lengths of A (= dW row length) and B (= dW rows)
   int a_slot;           // WGRAD: >= 0 takes A codes/exponents from record aux[a_slot], aux[a_slot+1]
   int replay_only;
+  int sa_rows;          // FPROP/DGRAD: row stride of the stage-grouped token exponents
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:
@@ -134,10 +135,13 @@ struct RowqArgs {
   const RouteHdr* hdr;
   const void* src;      // bf16 [R, N]
   uint8_t* q;           // [R, N]
-  uint8_t* s;           // [R, N/32]
+  uint8_t* s;           // exponents, see s_rows
   int N;
   int src_slot, q_slot, s_slot;
   int replay_only;
+  int s_rows;           // 0: exponents [R, N/32]; > 0: grouped by 128-column stage,
+                        // [N/128][s_rows][4] (a stage's exponents of consecutive rows
+                        // are consecutive dwords)
 };
 struct ColqArgs {
   const RouteHdr* hdr;

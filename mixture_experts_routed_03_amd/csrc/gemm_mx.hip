@@ -25,9 +25,10 @@
 //
 // MI355X design: the same coalesced, XOR-swizzled LDS staging as the BF16
 // kernels (128-byte row segments per stage; fp8 stages span 128 contraction
-// values).  DGRAD transposes the E4M3 weight tile in registers (a 4x4 byte
-// transpose of four rows with v_perm_b32) before writing it to LDS, so one
-// copy of the E4M3 weights serves forward and backward.
+// values).  DGRAD stages the E4M3 weight tile as it lies in memory (rows along
+// the contraction) and reads its MFMA operand with the gfx950 LDS transpose
+// read ds_read_b64_tr_b8, so one copy of the E4M3 weights serves forward and
+// backward with no register transpose.
 #include <algorithm>
 
 #include "common.h"
@@ -50,10 +51,6 @@ __device__ __forceinline__ void mfma_mx(f32x16& acc, u32x4 a0, u32x4 a1, u32x4 b
 __device__ __forceinline__ int byte_of(uint32_t w, int i) { return int((w >> (8 * i)) & 0xffu); }
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
-__device__ __forceinline__ int tsw(int o, int kq) {
-  return o * 32 + ((((kq >> 2) ^ o ^ (o >> 3)) & 7) << 2) + (kq & 3);
-}
-__device__ __forceinline__ int tsw_g(int o, int g) { return o * 32 + (((g ^ o ^ (o >> 3)) & 7) << 2); }
 // 64-byte rows (WGRAD): 16-byte chunk ch of row r
 __device__ __forceinline__ int swz64(int r, int ch) { return r * 64 + ((ch ^ ((r >> 2) & 3)) << 4); }
 
@@ -154,8 +151,8 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       tsrc[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kd + lc * 16;
-    const uint32_t* tsc_src =
-        reinterpret_cast<const uint32_t*>(a.sa + int64_t(row0 + min(tid & 63, rows - 1)) * KB);
+    // token exponents are grouped by stage: dword (s, row) at (s * sa_rows + row) * 4
+    const uint32_t* tsc_src = reinterpret_cast<const uint32_t*>(a.sa) + row0 + min(tid & 63, rows - 1);
 
     f32x16 acc0 = {}, acc1 = {};
     u32x4 R0[6], R1[6];
@@ -167,7 +164,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
       Sc[0] = wsc_src[s];
-      Sc[1] = tsc_src[s];
+      Sc[1] = tsc_src[int64_t(s) * a.sa_rows];
     };
     auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
       char* base = lds + buf * kStage;
@@ -290,22 +287,19 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
 }
 
 // ------------------------------------------------------------------ DGRAD
-// 4x4 byte transpose: out[j] = (r0.byte j, r1.byte j, r2.byte j, r3.byte j).
-__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
-                                             uint32_t* out) {
-  const uint32_t t01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
-  const uint32_t t23 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);  // r2.b0 r3.b0 r2.b1 r3.b1
-  const uint32_t u01 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
-  const uint32_t u23 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(u23, u01, 0x07060302u);
+// ds_read_b64_tr_b8 (gfx950), as measured: within each 16-lane group, the
+// lane with index 2j + hh supplies the address of row j of an 8-row block
+// (8 bytes: columns 8hh .. 8hh + 7 of a 16-column slab), and lane i receives
+// column i of the slab, rows 0..7 as bytes 0..7.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2*)((__attribute__((address_space(3))) char*)p));
 }
 
 template <int KIND>
 __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
-  constexpr int kW = 128 * 32 * 4;   // transposed weight stage: 128 columns x 128 values
+  constexpr int kW = 128 * 128;      // weight stage: 128 contraction rows x 128 columns
   constexpr int kT = kBM * 128;      // token stage
   constexpr int kSc = kBM * 4;
   constexpr int kStage = kW + kT + kSc + 16;   // + the weight scale dword of each wave
@@ -317,6 +311,11 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
   const int lh = lane >> 5;
   const int c16 = tid & 7;    // weight loader: 16-column chunk of a 128-byte row segment
   const int kq = tid >> 3;    // weight loader: rows 4kq .. 4kq+3 of the stage
+  // transpose reads of the weight operand: 16-lane group G covers columns
+  // 32*wave + 16*(G & 1) .. + 15 and contraction half G >> 1 (= lh)
+  const int tr_chunk = 2 * wave + ((lane >> 4) & 1);
+  const int tr_row = (lane & 15) >> 1;
+  const int tr_byte = 8 * (lane & 1);
   const int lc = tid & 7;
   const int lrow = tid >> 3;
 
@@ -344,15 +343,19 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
     const int rows = min(kBM, a.offsets[e + 1] - row0);
 
     const uint8_t* wsrc = a.qw + (int64_t(e) * Kd + 4 * kq) * N + nt * 128 + c16 * 16;
-    // the wave's 32 output columns are one scale column block; 4 blocks along k per stage
-    const uint8_t* wsc_src = a.sw + int64_t(e) * KB * (N / 32) + (nt * 128 + 32 * wave) / 32;
+    // Weight scales of the stage: 4 column blocks (one per wave) x 4 blocks
+    // along k.  Thread t loads the byte of column block (t >> 2) & 3 and k
+    // block t & 3 (one byte each, no register assembly); threads 0..15 put
+    // them in LDS, so wave w reads its four as one dword.
+    const uint8_t* wsc_src =
+        a.sw + int64_t(e) * KB * (N / 32) + (tid & 3) * (N / 32) + nt * 4 + ((tid >> 2) & 3);
     // Tile rows past the expert's last row re-read that row (outputs not stored).
     const uint8_t* tsrc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       tsrc[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kd + lc * 16;
-    const uint32_t* tsc_src =
-        reinterpret_cast<const uint32_t*>(a.sa + int64_t(row0 + min(tid & 63, rows - 1)) * KB);
+    // token exponents are grouped by stage: dword (s, row) at (s * sa_rows + row) * 4
+    const uint32_t* tsc_src = reinterpret_cast<const uint32_t*>(a.sa) + row0 + min(tid & 63, rows - 1);
 
     f32x16 acc0 = {}, acc1 = {};
     u32x4 R0[6], R1[6];
@@ -364,26 +367,18 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
-      uint32_t ws = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ws |= uint32_t(wsc_src[int64_t(4 * s + i) * (N / 32)]) << (8 * i);
-      Sc[0] = ws;
-      Sc[1] = tsc_src[s];
+      Sc[0] = wsc_src[int64_t(4 * s) * (N / 32)];
+      Sc[1] = tsc_src[int64_t(s) * a.sa_rows];
     };
     auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
-      uint32_t* la = reinterpret_cast<uint32_t*>(lds + buf * kStage);
+      char* lw = lds + buf * kStage;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t d[4];
-        transpose4x4(R[0][i], R[1][i], R[2][i], R[3][i], d);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) la[tsw(c16 * 16 + 4 * i + j, kq)] = d[j];
-      }
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(lw + swz(4 * kq + i, c16)) = R[i];
       char* lt = lds + buf * kStage + kW;
 #pragma unroll
       for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
       if (tid < kBM) reinterpret_cast<uint32_t*>(lt + kT)[tid] = Sc[1];
-      if (lane == 0) reinterpret_cast<uint32_t*>(lt + kT + kSc)[wave] = Sc[0];
+      if (tid < 16) reinterpret_cast<uint8_t*>(lt + kT + kSc)[tid] = uint8_t(Sc[0]);
     };
     auto compute = [&](int buf) {
       const char* la = lds + buf * kStage;
@@ -392,13 +387,22 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
       const uint32_t ts0 = tsc[lr];
       const uint32_t ts1 = tsc[32 + lr];
       const uint32_t wsc = tsc[kBM + wave];
-      const int orow = 32 * wave + lr;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int ga = 4 * q + lh, gb = 4 * q + 2 + lh;
         const int blk = 2 * q + lh;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(la + tsw_g(orow, ga) * 4);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + tsw_g(orow, gb) * 4);
+        // this lane's 32 operand bytes: contraction chunks ga and gb (16 rows
+        // each) of its output column, two 8-row transpose reads per chunk
+        i32x2 pc[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int row = 16 * (p < 2 ? ga : gb) + 8 * (p & 1) + tr_row;
+          pc[p] = lds_read_tr8(la + swz(row, tr_chunk) + tr_byte);
+        }
+        const u32x4 a0 = {uint32_t(pc[0][0]), uint32_t(pc[0][1]), uint32_t(pc[1][0]),
+                          uint32_t(pc[1][1])};
+        const u32x4 a1 = {uint32_t(pc[2][0]), uint32_t(pc[2][1]), uint32_t(pc[3][0]),
+                          uint32_t(pc[3][1])};
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(lt + swz(lr, ga));
         const u32x4 b1 = *reinterpret_cast<const u32x4*>(lt + swz(lr, gb));
         const u32x4 d0 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, ga));

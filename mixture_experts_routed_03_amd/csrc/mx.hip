@@ -131,7 +131,11 @@ __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
       out[h] = wv;
     }
     *reinterpret_cast<u32x2*>(q + row * N + c0) = out;
-    if ((lane & 3) == 0) s[row * (N / 32) + c0 / 32] = uint8_t(ex + 127);
+    if ((lane & 3) == 0) {
+      const int64_t si = a.s_rows ? (int64_t(c0 / 128) * a.s_rows + row) * 4 + (c0 / 32) % 4
+                                  : row * (N / 32) + c0 / 32;
+      s[si] = uint8_t(ex + 127);
+    }
   }
 }
 
