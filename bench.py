@@ -2,8 +2,9 @@
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-route (histogram, scan, stable permutation) -> expert forward (gather, W13
-grouped GEMM + SwiGLU, W2 grouped GEMM into route slots) -> combine, and for
+route (histogram, scan, stable permutation) -> expert forward (W13 grouped
+GEMM reading x rows through the permutation + SwiGLU, W2 grouped GEMM into
+route slots) -> combine, and for
 training workloads the backward (combine backward, W2 DGRAD + SwiGLU
 backward, W2/W13 WGRAD, W13 DGRAD, input-gradient reduction).  MXFP8
 workloads add the row quantizers and column bundles.
@@ -125,7 +126,7 @@ def alg_bytes(name, m):
         return common[name]
     if not mx:
         return {
-            "w13_swiglu": w13 + R * D * es + R * 2 * F * es + R * F * es,
+            "w13_swiglu": w13 + T * D * es + R * 2 * F * es + R * F * es,
             "w2_scatter": w2 + R * F * es + R * D * es,
             "w2_dgrad_swiglu": w2 + R * D * es + 2 * R * 2 * F * es + R * F * es,
             "w2_wgrad": ne * D * F * dwb + R * D * es + R * F * es,
@@ -133,8 +134,8 @@ def alg_bytes(name, m):
             "w13_wgrad": ne * 2 * F * D * dwb + R * 2 * F * es + R * D * es,
         }.get(name)
     return {
-        "quant_x": R * D * 2 + q(R * D),
-        "bundle_x": R * D * 2 + q(Rp * D),
+        "quant_x": T * D * 2 + q(R * D),
+        "bundle_x": T * D * 2 + q(Rp * D),
         "w13_swiglu": w13 + q(R * D) + R * 2 * F * 2 + R * F * 2,
         "bundle_h2": R * F * 2 + q(Rp * F),
         "quant_h2": R * F * 2 + q(R * F),

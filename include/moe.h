@@ -170,14 +170,17 @@ moe_status moe_mx_quantize(moe_plan_t plan, void* route_ws, const void* src, int
 moe_status moe_route(moe_plan_t plan, int64_t T, const int32_t* ids, void* route_ws,
                      hipStream_t stream);
 
-/* Expert forward of one layer (explainer section 02, staged form): gather
- * x rows in expert order, h1 = x W13^T with the SwiGLU epilogue, then
- * h3 = h2 W2^T stored bf16 (fp32 for F32 plans) into route slot
+/* Expert forward of one layer (explainer section 02, staged form): each
+ * expert's rows of x, gathered in expert order by the W13 kernel's loader
+ * (x[sorted_route[row] / K]), give h1 = x W13^T with the SwiGLU epilogue,
+ * then h3 = h2 W2^T stored bf16 (fp32 for F32 plans) into route slot
  * h3_slots[t*K + k].  Slots of padding routes are not written.  In training
  * the planner decides on the device whether this layer's state is saved in
  * the arena or rebuilt by backward (explainer section 04); layer is the
  * index of this layer in the stack (0 .. max_layers-1) and layer 0 starts
- * a new step (arena cursor 0).  x: [T,D]. arena may be null for inference. */
+ * a new step (arena cursor 0).  x: [T,D], read again by the backward (keep
+ * it until then).  arena may be null for inference.  A null x with routed
+ * rows sets MOE_STATUS_NULL_INPUT. */
 moe_status moe_expert_fwd(moe_plan_t plan, int32_t layer, void* route_ws, const void* x,
                           const moe_weights* w, void* h3_slots, void* arena, void* scratch,
                           hipStream_t stream);
@@ -220,8 +223,9 @@ moe_status moe_route_readback(moe_plan_t plan, void* route_ws, int32_t* counts,
                               int32_t* route_to_row, int32_t* R_out, hipStream_t stream);
 
 /* Device pointers of the layer's saved tensors inside scratch/arena, for
- * inspection by tests (synchronizes stream): gathered x rows [R,D] and h1
- * [R,2F] in the act dtype. */
+ * inspection by tests (synchronizes stream): *x_rows is always null (the
+ * gathered rows are never materialized: kernels read x through the
+ * permutation) and *h1 receives h1 [R,2F] in the act dtype. */
 moe_status moe_saved_ptrs(moe_plan_t plan, void* route_ws, void** x_rows, void** h1,
                           hipStream_t stream);
 

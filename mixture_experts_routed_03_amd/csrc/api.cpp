@@ -23,8 +23,7 @@ hipError_t launch_plan_decide(RouteHdr* hdr, const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_rewind(RouteHdr* hdr, void* arena, hipStream_t s);
 hipError_t launch_arena_reset(void* arena, hipStream_t s);
 hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
-                         const int32_t* sorted_route, int64_t R_max, int replay_only,
-                         hipStream_t s);
+                         const int32_t* sorted_route, void* dst, int64_t R_max, hipStream_t s);
 hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
                           const float* scores, const void* h3, const void* addend, void* y,
                           int K, int64_t D, int64_t T_max, uint32_t* status, hipStream_t s);
@@ -136,8 +135,8 @@ T* at(void* base, int64_t off) {
 // column bundle in training), the W13 grouped GEMM with the SwiGLU epilogue,
 // and the h2 column bundle in training.  replay_only = 1 runs the same
 // launches as backward's replay predicate.
-hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const moe_weights* w,
-                          int replay_only, int cus, hipStream_t s) {
+hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const void* x,
+                          const moe_weights* w, int replay_only, int cus, hipStream_t s) {
   const moe_desc& d = p->d;
   const ScratchLayout& L = p->sl;
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
@@ -145,16 +144,17 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const char* tag = replay_only ? "replay_quant_x" : "quant_x";
-  RowqArgs rx{hdr, sc + L.x_rows, reinterpret_cast<uint8_t*>(sc + L.qx),
+  // x rows are read through the permutation (the gather happens in the loaders)
+  RowqArgs rx{hdr, x, reinterpret_cast<uint8_t*>(sc + L.qx),
               reinterpret_cast<uint8_t*>(sc + L.sx), d.d, -1, -1, -1, replay_only,
-              int(p->R_max)};
+              int(p->R_max), sorted_route, d.k};
   hipError_t e = timed(p, tag, s, [&] { return launch_rowq(rx, p->R_max, s); });
   if (e != hipSuccess) return e;
   if (d.training) {
     // A replaying layer's bundles are rebuilt in backward: the forward only
     // writes them for a layer that saves.
-    ColqArgs cx{hdr, offsets, poffsets, sc + L.x_rows, nullptr, nullptr, d.d, d.e,
-                -1, 0, 1, replay_only ? 1 : 2};
+    ColqArgs cx{hdr, offsets, poffsets, x, nullptr, nullptr, d.d, d.e,
+                -1, 0, 1, replay_only ? 1 : 2, sorted_route, d.k};
     e = timed(p, replay_only ? "replay_bundle_x" : "bundle_x", s,
               [&] { return launch_colq(cx, p->Rp_max, s); });
     if (e != hipSuccess) return e;
@@ -180,9 +180,9 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
 // MXFP8 backward after the replay gather: replay of the quantized forward
 // state when needed, combine backward, both DGRADs on 1x32-quantized
 // gradients with the shared 32x32 weights, both WGRADs on column bundles.
-moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const moe_weights* w,
-                       const float* scores, const void* dy, const void* h3, void* arena,
-                       const moe_grads* g, uint32_t flags, int cus, hipStream_t s) {
+moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const void* x,
+                       const moe_weights* w, const float* scores, const void* dy, const void* h3,
+                       void* arena, const moe_grads* g, uint32_t flags, int cus, hipStream_t s) {
   const moe_desc& d = p->d;
   const ScratchLayout& L = p->sl;
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
@@ -192,7 +192,7 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const m
   const int32_t* route_to_row = at<int32_t>(ws, p->rl.route_to_row);
   const int dw_f32 = d.dw_dtype == MOE_DTYPE_F32;
   auto u8 = [&](int64_t off) { return reinterpret_cast<uint8_t*>(sc + off); };
-  hipError_t e = mx_forward_w13(p, hdr, ws, sc, w, 1, cus, s);
+  hipError_t e = mx_forward_w13(p, hdr, ws, sc, x, w, 1, cus, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = timed(p, "combine_bwd", s, [&] {
     return launch_combine_bwd(d.prec, hdr, route_to_row, scores, dy, h3, sc + L.dh3, g->dscores,
@@ -291,7 +291,6 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
     field = o;
     o = a256(o + bytes);
   };
-  take(S.x_rows, R * D * es);
   take(S.h1, R * 2 * F * es);
   take(S.h2, R * F * es);
   if (mx) {
@@ -305,6 +304,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
     take(S.h2cs, Rp / 32 * F);
   }
   if (d.training) {
+    if (!mx) take(S.x_rows, R * D * es);   // packed x rows for the W13 weight gradient
     take(S.dh3, R * D * es);
     take(S.dh1, R * 2 * F * es);
     take(S.dxr, R * D * 4);
@@ -324,7 +324,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   p->h3_bytes = std::max<int64_t>(a256(R * D * es), 256);
   p->state_max = mx ? align128(Rp * D) + align128(Rp / 32 * D) + align128(R * 2 * F * 2) +
                           align128(Rp * F) + align128(Rp / 32 * F)
-                    : align128(R * D * es) + align128(R * 2 * F * es);
+                    : align128(R * 2 * F * es);
   p->budget = d.arena_budget > 0 ? d.arena_budget : int64_t(d.max_layers) * p->state_max;
   p->arena_bytes = d.training ? kArenaHdrBytes + a256(p->budget) : kArenaHdrBytes;
   p->cus = 0;
@@ -354,6 +354,7 @@ moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
   if (!p || !buf || cap == 0) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
   const char* prec = d.prec == MOE_PREC_F32 ? "f32" : d.prec == MOE_PREC_BF16 ? "bf16" : "mxfp8";
+  const bool mx = d.prec == MOE_PREC_MXFP8;
   auto mib = [](int64_t b) { return double(b) / (1024.0 * 1024.0); };
   std::string s;
   char line[256];
@@ -371,8 +372,8 @@ moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
   std::snprintf(line, sizeof line, "  h3_slots   %10.2f MiB per layer [T*K, D]\n", mib(p->h3_bytes));
   s += line;
   std::snprintf(line, sizeof line,
-                "  scratch    %10.2f MiB shared: x_rows %.2f, h1 %.2f, h2 %.2f",
-                mib(p->sl.total), mib(p->sl.h1 - p->sl.x_rows), mib(p->sl.h2 - p->sl.h1),
+                "  scratch    %10.2f MiB shared: h1 %.2f, h2 %.2f",
+                mib(p->sl.total), mib(p->sl.h2 - p->sl.h1),
                 mib((d.training ? p->sl.dh3 : p->sl.total) - p->sl.h2));
   s += line;
   if (d.training) {
@@ -384,8 +385,9 @@ moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
   s += "\n";
   std::snprintf(line, sizeof line,
                 "  arena      %10.2f MiB: budget %.2f MiB, full layer state %.2f MiB at R_max "
-                "(x_rows + h1, 128-B aligned)\n",
-                mib(p->arena_bytes), mib(p->budget), mib(p->state_max));
+                "(%s, 128-B aligned)\n",
+                mib(p->arena_bytes), mib(p->budget), mib(p->state_max),
+                mx ? "x and h2 column bundles + h1" : "h1");
   s += line;
   std::snprintf(line, sizeof line,
                 "  planner: a layer replays iff cursor + full_state > budget (device decision "
@@ -466,7 +468,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   char* sc = reinterpret_cast<char*>(scratch);
   const ScratchLayout& L = p->sl;
   PlanArgs pa{layer, d.max_layers, d.training, p->es, d.d, d.f, p->budget,
-              uint64_t(d.training ? arena : nullptr), uint64_t(sc + L.x_rows), uint64_t(sc + L.h1),
+              uint64_t(d.training ? arena : nullptr), uint64_t(sc + L.h1),
               mx ? 1 : 0, 0,
               {mx ? uint64_t(sc + L.xcq) : 0, mx ? uint64_t(sc + L.xcs) : 0,
                mx ? uint64_t(sc + L.h2cq) : 0, mx ? uint64_t(sc + L.h2cs) : 0}};
@@ -476,13 +478,10 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
-  e = timed(p, "gather", s,
-            [&] { return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, p->R_max, 0, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
   const int cus = plan_cus(p);
   if (!mx) {
     FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
-                d.d, 2 * d.f, d.f, d.f / 64, d.e, 0};
+                d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -491,7 +490,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     return hip_status(timed(p, "w2_scatter", s,
                             [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
   }
-  e = mx_forward_w13(p, hdr, ws, sc, w, 0, cus, s);
+  e = mx_forward_w13(p, hdr, ws, sc, x, w, 0, cus, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   // h2 -> 1x32 row blocks for the W2 GEMM
   RowqArgs rq{hdr, sc + L.h2, reinterpret_cast<uint8_t*>(sc + L.qh2),
@@ -545,15 +544,11 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   float* dxr = reinterpret_cast<float*>(sc + p->sl.dxr);
   const int dw_f32 = d.dw_dtype == MOE_DTYPE_F32;
   hipError_t e;
-  // Replay (device predicate): rebuild gathered x and h1 in scratch when the
-  // forward did not save them.
-  e = timed(p, "replay_gather", s, [&] {
-    return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, p->R_max, 1, s);
-  });
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  if (mx) return mx_backward(p, hdr, ws, sc, w, scores, dy, h3, arena, g, flags, cus, s);
+  // Replay (device predicate): rebuild h1 in scratch from x when the forward
+  // did not save it.
+  if (mx) return mx_backward(p, hdr, ws, sc, x, w, scores, dy, h3, arena, g, flags, cus, s);
   FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
-              d.d, 2 * d.f, d.f, d.f / 64, d.e, 1};
+              d.d, 2 * d.f, d.f, d.f / 64, d.e, 1, x, d.k};
   e = timed(p, "replay_w13", s, [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = timed(p, "combine_bwd", s, [&] {
@@ -575,7 +570,12 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
               2 * d.f, d.d, d.f, d.d, d.e, d.d / 128, 0, 0};
   e = timed(p, "w13_dgrad", s, [&] { return launch_dgrad(1, b13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
-  BwdArgs bw13{hdr, offsets, mtoff, nullptr, nullptr, dh1, nullptr, g->dw13, nullptr,
+  // dW13's A rows: a packed copy of the x rows (its loads then stream)
+  e = timed(p, "gather", s, [&] {
+    return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, sc + p->sl.x_rows, p->R_max, s);
+  });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  BwdArgs bw13{hdr, offsets, mtoff, nullptr, nullptr, dh1, sc + p->sl.x_rows, g->dw13, nullptr,
                0, 0, d.f, d.d, d.e, 0, d.d, 2 * d.f};
   e = timed(p, "w13_wgrad", s, [&] { return launch_wgrad(dw_f32, 13, bw13, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;

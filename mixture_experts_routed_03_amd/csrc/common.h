@@ -77,7 +77,7 @@ struct FwdArgs {
   const int32_t* offsets;
   const int32_t* mtoff;
   const int32_t* sorted_route;
-  const void* A;    // token rows [R, Kd]; null = the layer record's x_rows
+  const void* A;    // token rows [R, Kd] (W2: h2); unused when x is set
   const void* W;    // [E, N, Kd]
   void* out0;       // W13: h1 [R, 2F] (null = record); W2: h3 slots [T*K, D]
   void* out1;       // W13: h2 [R, F]
@@ -87,6 +87,8 @@ struct FwdArgs {
   int NT;           // n-tiles per expert
   int E;
   int replay_only;  // 1: run only when the layer's forward chose replay
+  const void* x;    // W13: the caller's x [T, Kd]; packed row r reads x[sorted_route[r] / K]
+  int K;
 };
 
 // Arguments of the grouped backward GEMM launches.
@@ -97,7 +99,7 @@ struct BwdArgs {
   const void* W;        // DGRAD weight [E, Kd, N] (row = contraction index)
   const void* tok;      // DGRAD token operand rows [R, Kd] (dH3 or dH1)
   const void* grad;     // WGRAD gradient rows (dH3 [R, D] or dH1 [R, 2F])
-  const void* arows;    // WGRAD A-operand rows (h2 [R, F] or x rows [R, D]; null = record x rows)
+  const void* arows;    // WGRAD A-operand rows (h2 [R, F] or packed x rows [R, D])
   void* out;            // dH1 [R, 2F] / dXr [R, D] fp32 / dW2 [E, D, F] / dW13 [E, 2F, D]
   void* out2;           // W2 DGRAD: h2 [R, F] rebuilt from h1 for W2 WGRAD
   int Kd;               // DGRAD contraction length
@@ -142,6 +144,8 @@ struct RowqArgs {
   int s_rows;           // 0: exponents [R, N/32]; > 0: grouped by 128-column stage,
                         // [N/128][s_rows][4] (a stage's exponents of consecutive rows
                         // are consecutive dwords)
+  const int32_t* gather;  // non-null: source row r is src[gather[r] / K] (src = x [T, N])
+  int K;
 };
 struct ColqArgs {
   const RouteHdr* hdr;
@@ -153,6 +157,8 @@ struct ColqArgs {
   int N, E;
   int src_slot, q_slot, s_slot;
   int replay_only;      // 0 always, 1 only if the layer replays, 2 only if it saves
+  const int32_t* gather;  // non-null: source row r is src[gather[r] / K] (src = x [T, N])
+  int K;
 };
 
 // Arguments of the device planner (one layer).
@@ -160,8 +166,7 @@ struct PlanArgs {
   int32_t layer, max_layers, training, es, D, F;
   int64_t budget;
   uint64_t arena;           // device base of the arena (0 when none)
-  uint64_t scratch_x_rows;  // scratch regions used when state is not saved
-  uint64_t scratch_h1;
+  uint64_t scratch_h1;      // scratch regions used when state is not saved
   int32_t mx;               // MXFP8 layer: state = x/h2 column bundles + h1
   int32_t pad0;
   uint64_t scratch_aux[4];  // x bundle codes/exponents, h2 bundle codes/exponents

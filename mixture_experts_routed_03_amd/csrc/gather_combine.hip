@@ -1,5 +1,7 @@
-// Bandwidth-bound row kernels: gather x rows into expert order, combine the
-// K route outputs of each token, combine backward and the input-gradient sum.
+// Bandwidth-bound row kernels: combine the K route outputs of each token,
+// combine backward, the input-gradient sum, and a packed copy of the x rows
+// for the backward (the forward reads x through the permutation inside the
+// W13 kernel's loader).
 //
 // Dist-MoE explainer section 01: the expert kernel reads each route's source
 // row; results return to the route's slot (t*K + k) and the token owner
@@ -9,8 +11,10 @@
 // "Mixture of Experts: How Routing Becomes GPU Computation", section 2
 // (SwiGLU backward, weighted combine): dH = p dY and dp = <H, dY>.
 //
-// Layout: one wave per row; each lane moves 16-byte chunks, so a wave reads
-// 1 KiB contiguous per step (fully coalesced).
+// Layout: each lane moves 16-byte chunks of a row, so a wave reads 1 KiB
+// contiguous per step (fully coalesced).
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -57,24 +61,50 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// A[row] = x[sorted_route[row] / K] for row < R; destination from the
-// layer's planner record (arena or scratch).
+// Grid-stride element mapping: thread g handles 16-byte chunk (row, i) for
+// g = row * row_chunks + i, so every wave reads or writes 1 KiB contiguous
+// per step and all chunks of all rows are in flight at once (no per-row
+// serial loop); the grid is capped at a few waves per SIMD.
+__device__ __forceinline__ int64_t grid_thread() {
+  return int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+}
+__device__ __forceinline__ int64_t grid_threads() { return int64_t(gridDim.x) * blockDim.x; }
+
+// dst[row] = x[sorted_route[row] / K] for row < R (packed copy of the x rows
+// for the backward's W13 weight gradient, whose loads then stream).
 __global__ __launch_bounds__(256) void k_gather(const u32x4* __restrict__ x, int64_t row_chunks,
                                                 int K, const RouteHdr* __restrict__ hdr,
                                                 const int32_t* __restrict__ sorted_route,
-                                                int replay_only) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (replay_only && !hdr->rec.replay) return;
-  if (row >= hdr->R) return;
-  if (!x) {  // T > 0 needs x: report instead of faulting
-    if (row == 0 && lane == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
+                                                u32x4* __restrict__ dst) {
+  const int64_t n = int64_t(hdr->R) * row_chunks;
+  if (n == 0) return;
+  if (!x) {  // rows to copy need x: report instead of faulting
+    if (grid_thread() == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
-  u32x4* dst = global_ptr<u32x4>(hdr->rec.x_rows) + row * row_chunks;
-  const int64_t t = sorted_route[row] / K;
-  const u32x4* src = x + t * row_chunks;
-  for (int64_t i = lane; i < row_chunks; i += 64) dst[i] = src[i];
+  // four chunks per pass: their index loads, then their row loads, then
+  // the stores, so a pass waits for two round trips instead of eight
+  constexpr int U = 4;
+  const int64_t stride = grid_threads();
+  for (int64_t g0 = grid_thread(); g0 < n; g0 += U * stride) {
+    int64_t gi[U];
+    int32_t sr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      gi[u] = g0 + u * stride;
+      sr[u] = sorted_route[min(gi[u], n - 1) / row_chunks];
+    }
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = min(gi[u], n - 1);
+      const int64_t i = g - (g / row_chunks) * row_chunks;
+      v[u] = x[int64_t(sr[u] / K) * row_chunks + i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (gi[u] < n) dst[gi[u]] = v[u];
+  }
 }
 
 // y[t] = sum_k valid s[t,k] h3[t*K+k] (+ addend[t]), k ascending, fp32.
@@ -86,51 +116,62 @@ __global__ __launch_bounds__(256) void k_combine(const RouteHdr* __restrict__ hd
                                                  const u32x4* __restrict__ addend,
                                                  u32x4* __restrict__ y, int K, int64_t row_chunks,
                                                  uint32_t* __restrict__ status) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= hdr->T) return;
+  const int64_t n = int64_t(hdr->T) * row_chunks;
+  if (n == 0) return;
   if (!scores || !y) {
-    if (t == 0 && lane == 0) atomicOr(status, MOE_STATUS_NULL_INPUT);
+    if (grid_thread() == 0) atomicOr(status, MOE_STATUS_NULL_INPUT);
     return;
   }
-  float s[kMaxK];
-  bool v[kMaxK];
-  int bad = 0;
+  constexpr int nv = Vec16<T>::n;
+  for (int64_t g = grid_thread(); g < n; g += grid_threads()) {
+    const int64_t t = g / row_chunks;
+    const int64_t i = g - t * row_chunks;
+    // every slot chunk is loaded (in bounds even for padding routes, whose
+    // slots are never written) and padding is dropped by a select, so the K
+    // loads are independent
+    u32x4 hv[kMaxK];
+    float sk[kMaxK];
+    bool valid[kMaxK];
 #pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
-    if (k < K) {
-      v[k] = route_to_row[t * K + k] >= 0;
-      s[k] = scores[t * K + k];
-      bad |= (!v[k] && s[k] != 0.0f);
-    } else {
-      v[k] = false;
-      s[k] = 0.0f;
+    for (int k = 0; k < kMaxK; ++k) {
+      if (k < K) {
+        hv[k] = h3[(t * K + k) * row_chunks + i];
+        valid[k] = route_to_row[t * K + k] >= 0;
+        sk[k] = scores[t * K + k];
+      }
     }
-  }
-  if (bad && lane == 0) atomicOr(status, MOE_STATUS_PAD_SCORE);
-  constexpr int n = Vec16<T>::n;
-  for (int64_t i = lane; i < row_chunks; i += 64) {
-    float acc[n];
+    if (i == 0) {
+      bool bad = false;
 #pragma unroll
-    for (int j = 0; j < n; ++j) acc[j] = 0.0f;
-    for (int k = 0; k < K; ++k) {
-      if (!v[k]) continue;
-      float f[n];
-      Vec16<T>::unpack(h3[(t * K + k) * row_chunks + i], f);
+      for (int k = 0; k < kMaxK; ++k)
+        if (k < K) bad |= (!valid[k] && sk[k] != 0.0f);
+      if (bad) atomicOr(status, MOE_STATUS_PAD_SCORE);
+    }
+    float acc[nv];
 #pragma unroll
-      for (int j = 0; j < n; ++j) acc[j] += s[k] * f[j];
+    for (int j = 0; j < nv; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      if (k < K && valid[k]) {
+        float f[nv];
+        Vec16<T>::unpack(hv[k], f);
+#pragma unroll
+        for (int j = 0; j < nv; ++j) acc[j] += sk[k] * f[j];
+      }
     }
     if (addend) {
-      float f[n];
-      Vec16<T>::unpack(addend[t * row_chunks + i], f);
+      float f[nv];
+      Vec16<T>::unpack(addend[g], f);
 #pragma unroll
-      for (int j = 0; j < n; ++j) acc[j] += f[j];
+      for (int j = 0; j < nv; ++j) acc[j] += f[j];
     }
-    y[t * row_chunks + i] = Vec16<T>::pack(acc);
+    y[g] = Vec16<T>::pack(acc);
   }
 }
 
 // dh3[row(t,k)] = s[t,k] * dy[t];  dscores[t,k] = <h3_slot(t,k), dy[t]> (0 for padding).
+// One workgroup per token at a time (grid-stride over tokens): the threads
+// share the row's chunks, and the K dot products are reduced through LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict__ hdr,
                                                      const int32_t* __restrict__ route_to_row,
@@ -140,93 +181,133 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
                                                      u32x4* __restrict__ dh3,
                                                      float* __restrict__ dscores, int K,
                                                      int64_t row_chunks) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= hdr->T) return;
+  __shared__ float red[4][kMaxK];
+  const int n_tok = hdr->T;
+  if (n_tok == 0) return;
   if (!scores || !dy) {
-    if (t == 0 && lane == 0)
-      atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
+    if (grid_thread() == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
-  constexpr int n = Vec16<T>::n;
-  for (int k = 0; k < K; ++k) {
-    const int64_t r = t * K + k;
-    const int row = route_to_row[r];
-    if (row < 0) {
-      if (dscores && lane == 0) dscores[r] = 0.0f;
-      continue;
-    }
-    const float sk = scores[r];
-    float dot = 0.0f;
-    for (int64_t i = lane; i < row_chunks; i += 64) {
-      float g[n], h[n], o[n];
-      Vec16<T>::unpack(dy[t * row_chunks + i], g);
-      Vec16<T>::unpack(h3[r * row_chunks + i], h);
+  constexpr int nv = Vec16<T>::n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int64_t t = blockIdx.x; t < n_tok; t += gridDim.x) {
+    int rows[kMaxK];
+    float sk[kMaxK], dot[kMaxK];
 #pragma unroll
-      for (int j = 0; j < n; ++j) {
-        dot += h[j] * g[j];
-        o[j] = sk * g[j];
-      }
-      dh3[int64_t(row) * row_chunks + i] = Vec16<T>::pack(o);
+    for (int k = 0; k < kMaxK; ++k) {
+      rows[k] = k < K ? route_to_row[t * K + k] : -1;
+      sk[k] = k < K ? scores[t * K + k] : 0.0f;
+      dot[k] = 0.0f;
     }
-    dot = wave_sum(dot);
-    if (dscores && lane == 0) dscores[r] = dot;
+    for (int64_t i = tid; i < row_chunks; i += 256) {
+      float g[nv];
+      Vec16<T>::unpack(dy[t * row_chunks + i], g);
+      u32x4 hv[kMaxK];
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k)
+        if (k < K) hv[k] = h3[(t * K + k) * row_chunks + i];
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k) {
+        if (k < K && rows[k] >= 0) {
+          float h[nv], o[nv];
+          Vec16<T>::unpack(hv[k], h);
+#pragma unroll
+          for (int j = 0; j < nv; ++j) {
+            dot[k] += h[j] * g[j];
+            o[j] = sk[k] * g[j];
+          }
+          dh3[int64_t(rows[k]) * row_chunks + i] = Vec16<T>::pack(o);
+        }
+      }
+    }
+    if (dscores) {
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k) {
+        if (k < K) {
+          const float v = wave_sum(dot[k]);
+          if (lane == 0) red[wave][k] = v;
+        }
+      }
+      __syncthreads();
+      if (tid < K) {
+        const float v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+        dscores[t * K + tid] = route_to_row[t * K + tid] >= 0 ? v : 0.0f;
+      }
+      __syncthreads();
+    }
   }
 }
 
 // dx[t] (+)= sum over valid k, ascending, of dxr[row(t,k)] (fp32) -> act dtype.
+// Thread g handles 8 values: chunk i of token t (g = t * D/8 + i).
 template <typename T>
 __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ hdr,
                                                    const int32_t* __restrict__ route_to_row,
                                                    const float4* __restrict__ dxr,
                                                    T* __restrict__ dx, int K, int64_t D,
                                                    int accumulate) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= hdr->T) return;
+  const int64_t q8 = D / 8;
+  const int64_t n = int64_t(hdr->T) * q8;
+  if (n == 0) return;
   if (!dx) {
-    if (t == 0 && lane == 0)
-      atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
+    if (grid_thread() == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
-  int rows[kMaxK];
+  for (int64_t g = grid_thread(); g < n; g += grid_threads()) {
+    const int64_t t = g / q8;
+    const int64_t i = g - t * q8;
+    int rows[kMaxK];
+    float4 v0[kMaxK], v1[kMaxK];
 #pragma unroll
-  for (int k = 0; k < kMaxK; ++k) rows[k] = k < K ? route_to_row[t * K + k] : -1;
-  const int64_t q4 = D / 4;
-  for (int64_t i = lane; i < q4; i += 64) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-      if (rows[k] < 0) continue;
-      const float4 v = dxr[int64_t(rows[k]) * q4 + i];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+    for (int k = 0; k < kMaxK; ++k) {
+      if (k < K) {
+        rows[k] = route_to_row[t * K + k];
+        const float4* src = dxr + int64_t(max(rows[k], 0)) * (2 * q8) + 2 * i;
+        v0[k] = src[0];
+        v1[k] = src[1];
+      }
     }
-    T* o = dx + t * D + i * 4;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      if (k < K && rows[k] >= 0) {
+        acc[0] += v0[k].x;
+        acc[1] += v0[k].y;
+        acc[2] += v0[k].z;
+        acc[3] += v0[k].w;
+        acc[4] += v1[k].x;
+        acc[5] += v1[k].y;
+        acc[6] += v1[k].z;
+        acc[7] += v1[k].w;
+      }
+    }
+    T* o = dx + t * D + i * 8;
     if (accumulate) {
-      acc.x += Elem<T>::to_f(o[0]);
-      acc.y += Elem<T>::to_f(o[1]);
-      acc.z += Elem<T>::to_f(o[2]);
-      acc.w += Elem<T>::to_f(o[3]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += Elem<T>::to_f(o[j]);
     }
-    o[0] = Elem<T>::from_f(acc.x);
-    o[1] = Elem<T>::from_f(acc.y);
-    o[2] = Elem<T>::from_f(acc.z);
-    o[3] = Elem<T>::from_f(acc.w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = Elem<T>::from_f(acc[j]);
   }
 }
 
 // ------------------------------------------------------------ launchers
-static inline unsigned rows_grid(int64_t rows) { return unsigned((rows + 3) / 4); }
+// Element-mapped kernels: enough 256-thread workgroups for every chunk, capped
+// at 16 per CU of a 256-CU part (grid-stride loops cover the rest).
+static inline unsigned elem_grid(int64_t chunks) {
+  return unsigned(std::max<int64_t>(1, std::min<int64_t>((chunks + 255) / 256, 256 * 16)));
+}
+// One workgroup per token (grid-stride), capped at 8 per CU.
+static inline unsigned tok_grid(int64_t T) {
+  return unsigned(std::max<int64_t>(1, std::min<int64_t>(T, 256 * 8)));
+}
 
 hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
-                         const int32_t* sorted_route, int64_t R_max, int replay_only,
-                         hipStream_t s) {
+                         const int32_t* sorted_route, void* dst, int64_t R_max, hipStream_t s) {
   if (R_max == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gather, dim3(rows_grid(R_max)), dim3(256), 0, s,
+  hipLaunchKernelGGL(k_gather, dim3(elem_grid(R_max * (D * es / 16))), dim3(256), 0, s,
                      reinterpret_cast<const u32x4*>(x), D * es / 16, K, hdr, sorted_route,
-                     replay_only);
+                     reinterpret_cast<u32x4*>(dst));
   return hipGetLastError();
 }
 
@@ -235,12 +316,13 @@ hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to
                           int K, int64_t D, int64_t T_max, uint32_t* status, hipStream_t s) {
   if (T_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
-    hipLaunchKernelGGL(k_combine<float>, dim3(rows_grid(T_max)), dim3(256), 0, s, hdr,
+    hipLaunchKernelGGL(k_combine<float>, dim3(elem_grid(T_max * (D / 4))), dim3(256), 0, s, hdr,
                        route_to_row, scores, reinterpret_cast<const u32x4*>(h3),
                        reinterpret_cast<const u32x4*>(addend), reinterpret_cast<u32x4*>(y), K,
                        D / 4, status);
   else
-    hipLaunchKernelGGL(k_combine<uint16_t>, dim3(rows_grid(T_max)), dim3(256), 0, s, hdr,
+    hipLaunchKernelGGL(k_combine<uint16_t>, dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s,
+                       hdr,
                        route_to_row, scores, reinterpret_cast<const u32x4*>(h3),
                        reinterpret_cast<const u32x4*>(addend), reinterpret_cast<u32x4*>(y), K,
                        D / 8, status);
@@ -252,12 +334,12 @@ hipError_t launch_combine_bwd(int prec, const RouteHdr* hdr, const int32_t* rout
                               float* dscores, int K, int64_t D, int64_t T_max, hipStream_t s) {
   if (T_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
-    hipLaunchKernelGGL(k_combine_bwd<float>, dim3(rows_grid(T_max)), dim3(256), 0, s, hdr,
+    hipLaunchKernelGGL(k_combine_bwd<float>, dim3(tok_grid(T_max)), dim3(256), 0, s, hdr,
                        route_to_row, scores, reinterpret_cast<const u32x4*>(dy),
                        reinterpret_cast<const u32x4*>(h3), reinterpret_cast<u32x4*>(dh3),
                        dscores, K, D / 4);
   else
-    hipLaunchKernelGGL(k_combine_bwd<uint16_t>, dim3(rows_grid(T_max)), dim3(256), 0, s, hdr,
+    hipLaunchKernelGGL(k_combine_bwd<uint16_t>, dim3(tok_grid(T_max)), dim3(256), 0, s, hdr,
                        route_to_row, scores, reinterpret_cast<const u32x4*>(dy),
                        reinterpret_cast<const u32x4*>(h3), reinterpret_cast<u32x4*>(dh3),
                        dscores, K, D / 8);
@@ -269,11 +351,12 @@ hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_
                             int accumulate, hipStream_t s) {
   if (T_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
-    hipLaunchKernelGGL(k_dx_reduce<float>, dim3(rows_grid(T_max)), dim3(256), 0, s, hdr,
+    hipLaunchKernelGGL(k_dx_reduce<float>, dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s, hdr,
                        route_to_row, reinterpret_cast<const float4*>(dxr),
                        reinterpret_cast<float*>(dx), K, D, accumulate);
   else
-    hipLaunchKernelGGL(k_dx_reduce<uint16_t>, dim3(rows_grid(T_max)), dim3(256), 0, s, hdr,
+    hipLaunchKernelGGL(k_dx_reduce<uint16_t>, dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s,
+                       hdr,
                        route_to_row, reinterpret_cast<const float4*>(dxr),
                        reinterpret_cast<uint16_t*>(dx), K, D, accumulate);
   return hipGetLastError();

@@ -298,8 +298,7 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
   const int per = gridDim.x / kXcds;
   const int first = xcd_first_item(a.mtoff, a.E, per_e, xcd);
   const int last = xcd_first_item(a.mtoff, a.E, per_e, xcd + 1);
-  const uint16_t* asrc = a.arows ? reinterpret_cast<const uint16_t*>(a.arows)
-                                 : global_ptr<const uint16_t>(hdr->rec.x_rows);
+  const uint16_t* asrc = reinterpret_cast<const uint16_t*>(a.arows);
   const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(a.grad);
 
   struct Item {

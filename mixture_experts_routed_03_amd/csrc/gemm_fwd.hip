@@ -122,7 +122,14 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
   const RouteHdr* hdr = a.hdr;
   if (a.replay_only && !hdr->rec.replay) return;
   const int n_items = hdr->n_mt * a.NT;
-  const char* Abase = a.A ? reinterpret_cast<const char*>(a.A) : global_ptr<const char>(hdr->rec.x_rows);
+  // W13 reads the caller's x rows through the permutation (the gather is part
+  // of this loader); W2 reads packed h2 rows.
+  const char* Abase = reinterpret_cast<const char*>(MODE == 0 ? a.x : a.A);
+  if (MODE == 0 && !a.x) {  // rows to compute need x: report instead of faulting
+    if (n_items > 0 && blockIdx.x == 0 && threadIdx.x == 0)
+      atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
+    return;
+  }
   T* out0 = a.out0 ? reinterpret_cast<T*>(a.out0) : global_ptr<T>(hdr->rec.h1);
   T* out1 = reinterpret_cast<T*>(a.out1);
   const int64_t row_bytes = int64_t(a.Kd) * ES;
@@ -157,8 +164,11 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
     }
     const char* tsrc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      tsrc[j] = Abase + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * row_bytes + lc * 16;
+    for (int j = 0; j < 2; ++j) {
+      const int r = row0 + min(lrow + 32 * j, rows - 1);
+      const int64_t src = MODE == 0 ? a.sorted_route[r] / a.K : r;
+      tsrc[j] = Abase + src * row_bytes + lc * 16;
+    }
 
     f32x16 acc0 = {}, acc1 = {};
     u32x4 R0[6], R1[6];

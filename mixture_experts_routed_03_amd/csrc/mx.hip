@@ -107,9 +107,14 @@ __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
                                          : reinterpret_cast<const uint16_t*>(a.src);
   uint8_t* q = a.q_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.q_slot)) : a.q;
   uint8_t* s = a.s_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.s_slot)) : a.s;
+  if (!src) {  // rows to quantize need their source: report instead of faulting
+    if (row == 0 && lane == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
+    return;
+  }
   const int N = a.N;
+  const int64_t srow = a.gather ? a.gather[row] / a.K : row;
   for (int c0 = lane * 8; c0 < N; c0 += 512) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + row * N + c0);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + srow * N + c0);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -171,12 +176,18 @@ __global__ __launch_bounds__(256) void k_colq(ColqArgs a) {
                                          : reinterpret_cast<const uint16_t*>(a.src);
   uint8_t* q = a.q_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.q_slot)) : a.q;
   uint8_t* s = a.s_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.s_slot)) : a.s;
+  if (!src) {
+    if (gb == 0 && threadIdx.x == 0 && blockIdx.y == 0)
+      atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
+    return;
+  }
   const int N = a.N;
   float v[32];
   float amax = 0.0f;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    v[r] = r < rows ? bf16_to_f32(src[int64_t(r0 + r) * N + col]) : 0.0f;
+    const int64_t srow = a.gather ? a.gather[r0 + min(r, rows - 1)] / a.K : r0 + r;
+    v[r] = r < rows ? bf16_to_f32(src[srow * N + col]) : 0.0f;
     amax = fmaxf(amax, fabsf(v[r]));
   }
   const int ex = e8m0_exp(amax);

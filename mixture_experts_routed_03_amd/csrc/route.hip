@@ -43,21 +43,43 @@ __global__ __launch_bounds__(256) void k_route_hist(const int32_t* __restrict__ 
   if (threadIdx.x == 0) chunk_flags[c] = bad ? int32_t(MOE_STATUS_BAD_ID) : 0;
 }
 
-// Inclusive block scan of one int per thread (blockDim.x == 1024).
-__device__ int block_scan_incl(int v, int* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int add = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+// Inclusive scan of three ints per thread over a 1024-thread block: a
+// shuffle scan inside each wave, then a scan of the 16 wave totals.
+__device__ void block_scan3(int& a, int& b, int& c, int* sh /* [3][16] */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ua = __shfl_up(a, off, 64), ub = __shfl_up(b, off, 64), uc = __shfl_up(c, off, 64);
+    if (lane >= off) {
+      a += ua;
+      b += ub;
+      c += uc;
+    }
   }
-  int res = sh[tid];
+  if (lane == 63) {
+    sh[wave] = a;
+    sh[16 + wave] = b;
+    sh[32 + wave] = c;
+  }
   __syncthreads();
-  return res;
+  int pa = 0, pb = 0, pc = 0;
+  for (int w = 0; w < wave; ++w) {
+    pa += sh[w];
+    pb += sh[16 + w];
+    pc += sh[32 + w];
+  }
+  a += pa;
+  b += pb;
+  c += pc;
+  __syncthreads();
 }
+
+// Column sums of the chunk histograms and their rewrite into row bases read
+// 16 chunks at a time per expert (independent loads; threads of consecutive
+// experts read consecutive words).  Experts are handled in passes of 1024,
+// expert e = 1024 * pass + thread, with the running totals carried between
+// passes.
+constexpr int kScanBatch = 16;
 
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
                                                      const int32_t* __restrict__ chunk_flags,
@@ -67,72 +89,78 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
                                                      int32_t* __restrict__ poffsets,
                                                      int32_t* __restrict__ mtoff,
                                                      RouteHdr* __restrict__ hdr) {
-  __shared__ int sh[1024];
-  __shared__ int tot[3];
+  __shared__ int sh[48];
+  __shared__ int carry[3];
   __shared__ int red[2];
   const int tid = threadIdx.x;
-  // Each thread owns up to kMaxE/1024 = 4 consecutive experts.
-  constexpr int per = kMaxE / 1024;
-  int cnt[per];
-  int sc = 0, sp = 0, sm = 0, mx = 0;
-  for (int i = 0; i < per; ++i) {
-    const int e = tid * per + i;
-    int s = 0;
-    if (e < E)
-      for (int c = 0; c < nchunks; ++c) s += chunk_hist[int64_t(c) * E + e];
-    cnt[i] = s;
-    sc += s;
-    sp += (s + kMxBlock - 1) / kMxBlock * kMxBlock;
-    sm += (s + kBM - 1) / kBM;
-    mx = max(mx, s);
+  if (tid == 0) {
+    carry[0] = carry[1] = carry[2] = 0;
+    red[0] = red[1] = 0;
   }
-  const int ic = block_scan_incl(sc, sh);
-  const int ip = block_scan_incl(sp, sh);
-  const int im = block_scan_incl(sm, sh);
-  int oc = ic - sc, op = ip - sp, om = im - sm;
-  for (int i = 0; i < per; ++i) {
-    const int e = tid * per + i;
+  __syncthreads();
+  int mx = 0;
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int e = e0 + tid;
+    int s = 0;
     if (e < E) {
-      counts[e] = cnt[i];
+      for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j)
+          v[j] = chunk_hist[int64_t(min(c0 + j, nchunks - 1)) * E + e];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) s += c0 + j < nchunks ? v[j] : 0;
+      }
+    }
+    const int sp = (s + kMxBlock - 1) / kMxBlock * kMxBlock;
+    const int sm = (s + kBM - 1) / kBM;
+    mx = max(mx, s);
+    int ic = s, ip = sp, im = sm;
+    block_scan3(ic, ip, im, sh);
+    const int oc = carry[0] + ic - s, op = carry[1] + ip - sp, om = carry[2] + im - sm;
+    if (e < E) {
+      counts[e] = s;
       offsets[e] = oc;
       poffsets[e] = op;
       mtoff[e] = om;
       // chunk histograms -> row base of each (chunk, expert)
       int run = oc;
-      for (int c = 0; c < nchunks; ++c) {
-        const int h = chunk_hist[int64_t(c) * E + e];
-        chunk_hist[int64_t(c) * E + e] = run;
-        run += h;
+      for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j)
+          v[j] = chunk_hist[int64_t(min(c0 + j, nchunks - 1)) * E + e];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+          if (c0 + j < nchunks) {
+            chunk_hist[int64_t(c0 + j) * E + e] = run;
+            run += v[j];
+          }
+        }
       }
     }
-    oc += cnt[i];
-    op += (cnt[i] + kMxBlock - 1) / kMxBlock * kMxBlock;
-    om += (cnt[i] + kBM - 1) / kBM;
-  }
-  if (tid == 1023) {
-    tot[0] = ic;
-    tot[1] = ip;
-    tot[2] = im;
+    __syncthreads();   // every thread has read the carries of this pass
+    if (tid == 1023) {
+      carry[0] += ic;
+      carry[1] += ip;
+      carry[2] += im;
+    }
+    __syncthreads();
   }
   // status and max count
   int f = 0;
   for (int c = tid; c < nchunks; c += 1024) f |= chunk_flags[c];
-  if (tid == 0) {
-    red[0] = 0;
-    red[1] = 0;
-  }
-  __syncthreads();
   atomicOr(&red[0], f);
   atomicMax(&red[1], mx);
   __syncthreads();
   if (tid == 0) {
-    offsets[E] = tot[0];
-    poffsets[E] = tot[1];
-    mtoff[E] = tot[2];
+    offsets[E] = carry[0];
+    poffsets[E] = carry[1];
+    mtoff[E] = carry[2];
     hdr->T = T;
-    hdr->R = tot[0];
-    hdr->Rpad = tot[1];
-    hdr->n_mt = tot[2];
+    hdr->R = carry[0];
+    hdr->Rpad = carry[1];
+    hdr->n_mt = carry[2];
     hdr->status = uint32_t(red[0]);
     hdr->max_count = red[1];
     hdr->rec.done = 0;
@@ -176,9 +204,11 @@ __global__ void k_plan_decide(RouteHdr* __restrict__ hdr, PlanArgs a) {
   LayerRec& rec = hdr->rec;
   const int64_t R = hdr->R;
   const int64_t Rp = hdr->Rpad;
-  // Saved state of the layer.  BF16/FP32: gathered x rows and h1.  MXFP8
-  // (explainer section 04, MXFP8 full-save): x and h2 column bundles (codes +
-  // exponents) and dense h1; the gathered bf16 rows stay in scratch.
+  // Saved state of the layer.  BF16/FP32: h1 (explainer section 04 also
+  // lists the gathered x rows, which on one GPU are a copy of the caller's x:
+  // every kernel here reads x through the permutation instead).  MXFP8
+  // (section 04, MXFP8 full-save): x and h2 column bundles (codes +
+  // exponents) and dense h1.
   int64_t part[5] = {0, 0, 0, 0, 0};
   if (a.mx) {
     part[0] = align128(Rp * a.D);
@@ -187,14 +217,13 @@ __global__ void k_plan_decide(RouteHdr* __restrict__ hdr, PlanArgs a) {
     part[3] = align128(Rp * a.F);
     part[4] = align128(Rp / 32 * a.F);
   } else {
-    part[0] = align128(R * a.D * a.es);
     part[2] = align128(R * 2 * a.F * a.es);
   }
   const int64_t full = part[0] + part[1] + part[2] + part[3] + part[4];
   rec.layer = a.layer;
   rec.done = 1;
   auto to_scratch = [&]() {
-    rec.x_rows = a.scratch_x_rows;
+    rec.x_rows = 0;
     rec.h1 = a.scratch_h1;
     for (int i = 0; i < 4; ++i) rec.aux[i] = a.scratch_aux[i];
   };
@@ -219,17 +248,12 @@ __global__ void k_plan_decide(RouteHdr* __restrict__ hdr, PlanArgs a) {
   } else {
     rec.bytes = full;
     const uint64_t base = a.arena + uint64_t(kArenaHdrBytes) + uint64_t(cursor);
-    if (a.mx) {
-      rec.x_rows = a.scratch_x_rows;
-      rec.aux[0] = base;
-      rec.aux[1] = base + uint64_t(part[0]);
-      rec.h1 = base + uint64_t(part[0] + part[1]);
-      rec.aux[2] = rec.h1 + uint64_t(part[2]);
-      rec.aux[3] = rec.aux[2] + uint64_t(part[3]);
-    } else {
-      rec.x_rows = base;
-      rec.h1 = base + uint64_t(part[0]);
-    }
+    rec.x_rows = 0;
+    rec.aux[0] = base;
+    rec.aux[1] = base + uint64_t(part[0]);
+    rec.h1 = base + uint64_t(part[0] + part[1]);
+    rec.aux[2] = rec.h1 + uint64_t(part[2]);
+    rec.aux[3] = rec.aux[2] + uint64_t(part[3]);
   }
   ah->cursor = cursor + rec.bytes;
 }

@@ -54,9 +54,12 @@ def decide(full_bytes, keep_bytes: int, capacity: int):
 
 def bf16_full_state_bytes(R: int, D: int, F: int, es: int = 2) -> int:
     """This library's saved state of a BF16 (es = 2) or FP32 (es = 4) layer:
-    gathered x rows [R, D] and h1 [R, 2F], each aligned to 128 B (the route
-    outputs h3 live in the caller's slot buffer)."""
-    return align128(R * D * es) + align128(R * 2 * F * es)
+    h1 [R, 2F], aligned to 128 B.  Section 04 also lists the gathered x rows;
+    on one GPU they are a copy of the caller's x, which the backward reads
+    again through the permutation, and the route outputs h3 live in the
+    caller's slot buffer.  (D is kept for the signature of the other byte
+    terms.)"""
+    return align128(R * 2 * F * es)
 
 
 def mx_full_state_bytes(R: int, Rp: int, D: int, F: int) -> int:

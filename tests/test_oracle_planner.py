@@ -58,5 +58,7 @@ def test_mx_state_bytes_match_the_saved_tensors():
 
 
 def test_bf16_state_bytes():
-    assert planner.bf16_full_state_bytes(3, 128, 128) == 768 + 1536
-    assert planner.bf16_full_state_bytes(1, 128, 128, es=4) == 512 + 1024
+    """h1 [R, 2F] of the act dtype, rounded up to 128 B."""
+    assert planner.bf16_full_state_bytes(3, 128, 128) == 1536
+    assert planner.bf16_full_state_bytes(1, 128, 128, es=4) == 1024
+    assert planner.bf16_full_state_bytes(1, 128, 8) == 128   # 32 B -> one 128-B line
