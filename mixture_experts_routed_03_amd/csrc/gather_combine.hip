@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void k_gather(const u32x4* __restrict__ x, int
 }
 
 // y[t] = sum_k valid s[t,k] h3[t*K+k] (+ addend[t]), k ascending, fp32.
-template <typename T>
+// KM >= K bounds the per-thread route arrays (the launcher picks 2, 4, 8, 16).
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void k_combine(const RouteHdr* __restrict__ hdr,
                                                  const int32_t* __restrict__ route_to_row,
                                                  const float* __restrict__ scores,
@@ -123,17 +124,21 @@ __global__ __launch_bounds__(256) void k_combine(const RouteHdr* __restrict__ hd
     return;
   }
   constexpr int nv = Vec16<T>::n;
+  // with whole waves per row, a wave's token is uniform: its route and score
+  // reads become scalar loads
+  const bool wave_rows = row_chunks % 64 == 0;
   for (int64_t g = grid_thread(); g < n; g += grid_threads()) {
-    const int64_t t = g / row_chunks;
+    int64_t t = g / row_chunks;
+    if (wave_rows) t = __builtin_amdgcn_readfirstlane(int(t));
     const int64_t i = g - t * row_chunks;
     // every slot chunk is loaded (in bounds even for padding routes, whose
     // slots are never written) and padding is dropped by a select, so the K
     // loads are independent
-    u32x4 hv[kMaxK];
-    float sk[kMaxK];
-    bool valid[kMaxK];
+    u32x4 hv[KM];
+    float sk[KM];
+    bool valid[KM];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
+    for (int k = 0; k < KM; ++k) {
       if (k < K) {
         hv[k] = h3[(t * K + k) * row_chunks + i];
         valid[k] = route_to_row[t * K + k] >= 0;
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256) void k_combine(const RouteHdr* __restrict__ hd
     if (i == 0) {
       bool bad = false;
 #pragma unroll
-      for (int k = 0; k < kMaxK; ++k)
+      for (int k = 0; k < KM; ++k)
         if (k < K) bad |= (!valid[k] && sk[k] != 0.0f);
       if (bad) atomicOr(status, MOE_STATUS_PAD_SCORE);
     }
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(256) void k_combine(const RouteHdr* __restrict__ hd
 #pragma unroll
     for (int j = 0; j < nv; ++j) acc[j] = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
+    for (int k = 0; k < KM; ++k) {
       if (k < K && valid[k]) {
         float f[nv];
         Vec16<T>::unpack(hv[k], f);
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(256) void k_combine(const RouteHdr* __restrict__ hd
 // dh3[row(t,k)] = s[t,k] * dy[t];  dscores[t,k] = <h3_slot(t,k), dy[t]> (0 for padding).
 // One workgroup per token at a time (grid-stride over tokens): the threads
 // share the row's chunks, and the K dot products are reduced through LDS.
-template <typename T>
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict__ hdr,
                                                      const int32_t* __restrict__ route_to_row,
                                                      const float* __restrict__ scores,
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
                                                      u32x4* __restrict__ dh3,
                                                      float* __restrict__ dscores, int K,
                                                      int64_t row_chunks) {
-  __shared__ float red[4][kMaxK];
+  __shared__ float red[4][KM];
   const int n_tok = hdr->T;
   if (n_tok == 0) return;
   if (!scores || !dy) {
@@ -191,10 +196,10 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
   constexpr int nv = Vec16<T>::n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int64_t t = blockIdx.x; t < n_tok; t += gridDim.x) {
-    int rows[kMaxK];
-    float sk[kMaxK], dot[kMaxK];
+    int rows[KM];
+    float sk[KM], dot[KM];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
+    for (int k = 0; k < KM; ++k) {
       rows[k] = k < K ? route_to_row[t * K + k] : -1;
       sk[k] = k < K ? scores[t * K + k] : 0.0f;
       dot[k] = 0.0f;
@@ -202,12 +207,12 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
     for (int64_t i = tid; i < row_chunks; i += 256) {
       float g[nv];
       Vec16<T>::unpack(dy[t * row_chunks + i], g);
-      u32x4 hv[kMaxK];
+      u32x4 hv[KM];
 #pragma unroll
-      for (int k = 0; k < kMaxK; ++k)
+      for (int k = 0; k < KM; ++k)
         if (k < K) hv[k] = h3[(t * K + k) * row_chunks + i];
 #pragma unroll
-      for (int k = 0; k < kMaxK; ++k) {
+      for (int k = 0; k < KM; ++k) {
         if (k < K && rows[k] >= 0) {
           float h[nv], o[nv];
           Vec16<T>::unpack(hv[k], h);
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
     }
     if (dscores) {
 #pragma unroll
-      for (int k = 0; k < kMaxK; ++k) {
+      for (int k = 0; k < KM; ++k) {
         if (k < K) {
           const float v = wave_sum(dot[k]);
           if (lane == 0) red[wave][k] = v;
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
 
 // dx[t] (+)= sum over valid k, ascending, of dxr[row(t,k)] (fp32) -> act dtype.
 // Thread g handles 8 values: chunk i of token t (g = t * D/8 + i).
-template <typename T>
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ hdr,
                                                    const int32_t* __restrict__ route_to_row,
                                                    const float4* __restrict__ dxr,
@@ -253,13 +258,15 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ 
     if (grid_thread() == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
+  const bool wave_rows = q8 % 64 == 0;
   for (int64_t g = grid_thread(); g < n; g += grid_threads()) {
-    const int64_t t = g / q8;
+    int64_t t = g / q8;
+    if (wave_rows) t = __builtin_amdgcn_readfirstlane(int(t));
     const int64_t i = g - t * q8;
-    int rows[kMaxK];
-    float4 v0[kMaxK], v1[kMaxK];
+    int rows[KM];
+    float4 v0[KM], v1[KM];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
+    for (int k = 0; k < KM; ++k) {
       if (k < K) {
         rows[k] = route_to_row[t * K + k];
         const float4* src = dxr + int64_t(max(rows[k], 0)) * (2 * q8) + 2 * i;
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ 
     }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
+    for (int k = 0; k < KM; ++k) {
       if (k < K && rows[k] >= 0) {
         acc[0] += v0[k].x;
         acc[1] += v0[k].y;
@@ -293,9 +300,9 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ 
 
 // ------------------------------------------------------------ launchers
 // Element-mapped kernels: enough 256-thread workgroups for every chunk, capped
-// at 16 per CU of a 256-CU part (grid-stride loops cover the rest).
+// at 64 per CU of a 256-CU part (grid-stride loops cover larger calls).
 static inline unsigned elem_grid(int64_t chunks) {
-  return unsigned(std::max<int64_t>(1, std::min<int64_t>((chunks + 255) / 256, 256 * 16)));
+  return unsigned(std::max<int64_t>(1, std::min<int64_t>((chunks + 255) / 256, 256 * 64)));
 }
 // One workgroup per token (grid-stride), capped at 8 per CU.
 static inline unsigned tok_grid(int64_t T) {
@@ -311,21 +318,40 @@ hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr
   return hipGetLastError();
 }
 
+// Route-array bound of the K-dependent kernels: 2, 4, 8 or 16.
+#define MOE_DISPATCH_K(K, CALL)   \
+  do {                            \
+    if ((K) <= 2) {               \
+      constexpr int KM = 2;       \
+      CALL;                       \
+    } else if ((K) <= 4) {        \
+      constexpr int KM = 4;       \
+      CALL;                       \
+    } else if ((K) <= 8) {        \
+      constexpr int KM = 8;       \
+      CALL;                       \
+    } else {                      \
+      constexpr int KM = kMaxK;   \
+      CALL;                       \
+    }                             \
+  } while (0)
+
 hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
                           const float* scores, const void* h3, const void* addend, void* y,
                           int K, int64_t D, int64_t T_max, uint32_t* status, hipStream_t s) {
   if (T_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
-    hipLaunchKernelGGL(k_combine<float>, dim3(elem_grid(T_max * (D / 4))), dim3(256), 0, s, hdr,
-                       route_to_row, scores, reinterpret_cast<const u32x4*>(h3),
-                       reinterpret_cast<const u32x4*>(addend), reinterpret_cast<u32x4*>(y), K,
-                       D / 4, status);
+    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_combine<float, KM>), dim3(elem_grid(T_max * (D / 4))),
+                                         dim3(256), 0, s, hdr, route_to_row, scores,
+                                         reinterpret_cast<const u32x4*>(h3),
+                                         reinterpret_cast<const u32x4*>(addend),
+                                         reinterpret_cast<u32x4*>(y), K, D / 4, status));
   else
-    hipLaunchKernelGGL(k_combine<uint16_t>, dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s,
-                       hdr,
-                       route_to_row, scores, reinterpret_cast<const u32x4*>(h3),
-                       reinterpret_cast<const u32x4*>(addend), reinterpret_cast<u32x4*>(y), K,
-                       D / 8, status);
+    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_combine<uint16_t, KM>),
+                                         dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s, hdr,
+                                         route_to_row, scores, reinterpret_cast<const u32x4*>(h3),
+                                         reinterpret_cast<const u32x4*>(addend),
+                                         reinterpret_cast<u32x4*>(y), K, D / 8, status));
   return hipGetLastError();
 }
 
@@ -334,15 +360,17 @@ hipError_t launch_combine_bwd(int prec, const RouteHdr* hdr, const int32_t* rout
                               float* dscores, int K, int64_t D, int64_t T_max, hipStream_t s) {
   if (T_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
-    hipLaunchKernelGGL(k_combine_bwd<float>, dim3(tok_grid(T_max)), dim3(256), 0, s, hdr,
-                       route_to_row, scores, reinterpret_cast<const u32x4*>(dy),
-                       reinterpret_cast<const u32x4*>(h3), reinterpret_cast<u32x4*>(dh3),
-                       dscores, K, D / 4);
+    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_combine_bwd<float, KM>), dim3(tok_grid(T_max)),
+                                         dim3(256), 0, s, hdr, route_to_row, scores,
+                                         reinterpret_cast<const u32x4*>(dy),
+                                         reinterpret_cast<const u32x4*>(h3),
+                                         reinterpret_cast<u32x4*>(dh3), dscores, K, D / 4));
   else
-    hipLaunchKernelGGL(k_combine_bwd<uint16_t>, dim3(tok_grid(T_max)), dim3(256), 0, s, hdr,
-                       route_to_row, scores, reinterpret_cast<const u32x4*>(dy),
-                       reinterpret_cast<const u32x4*>(h3), reinterpret_cast<u32x4*>(dh3),
-                       dscores, K, D / 8);
+    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_combine_bwd<uint16_t, KM>), dim3(tok_grid(T_max)),
+                                         dim3(256), 0, s, hdr, route_to_row, scores,
+                                         reinterpret_cast<const u32x4*>(dy),
+                                         reinterpret_cast<const u32x4*>(h3),
+                                         reinterpret_cast<u32x4*>(dh3), dscores, K, D / 8));
   return hipGetLastError();
 }
 
@@ -351,15 +379,18 @@ hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_
                             int accumulate, hipStream_t s) {
   if (T_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
-    hipLaunchKernelGGL(k_dx_reduce<float>, dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s, hdr,
-                       route_to_row, reinterpret_cast<const float4*>(dxr),
-                       reinterpret_cast<float*>(dx), K, D, accumulate);
+    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_dx_reduce<float, KM>), dim3(elem_grid(T_max * (D / 8))),
+                                         dim3(256), 0, s, hdr, route_to_row,
+                                         reinterpret_cast<const float4*>(dxr),
+                                         reinterpret_cast<float*>(dx), K, D, accumulate));
   else
-    hipLaunchKernelGGL(k_dx_reduce<uint16_t>, dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s,
-                       hdr,
-                       route_to_row, reinterpret_cast<const float4*>(dxr),
-                       reinterpret_cast<uint16_t*>(dx), K, D, accumulate);
+    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_dx_reduce<uint16_t, KM>),
+                                         dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s, hdr,
+                                         route_to_row, reinterpret_cast<const float4*>(dxr),
+                                         reinterpret_cast<uint16_t*>(dx), K, D, accumulate));
   return hipGetLastError();
 }
+
+#undef MOE_DISPATCH_K
 
 }  // namespace moe

@@ -43,6 +43,8 @@ def _check_full(lay, outs, tol):
     (512, 384, 128, 16, 4, 1.3, 0, "bf16"),    # skew: multi-tile hot experts, empty experts
     (33, 512, 384, 40, 3, 0.5, 5, "f32"),      # most experts tiny or empty, fp32 dW
     (130, 128, 256, 3, 2, None, 0, "f32"),     # hot experts > 2 m-tiles, WGRAD > 4 stages
+    (70, 256, 128, 20, 12, 0.8, 9, "bf16"),    # K > 8: the widest route arrays
+    (40, 128, 128, 16, 16, None, 3, "bf16"),   # K = 16 (the maximum), every expert per token
 ])
 def test_bf16_backward_matches_oracle(B, T, D, F, E, K, zipf, n_pad, dw):
     banner(f"bf16 backward T={T} D={D} F={F} E={E} K={K} zipf={zipf} dW={dw}")

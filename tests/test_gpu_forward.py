@@ -73,6 +73,8 @@ def test_tiny_fp32_layer_matches_oracle(B):
     (512, 384, 128, 16, 4, 1.3, 0),      # skew: hot experts span several m-tiles, empty experts
     (64, 128, 128, 4, 1, None, 0),
     (33, 512, 384, 40, 3, 0.5, 5),       # more experts than rows per expert
+    (50, 256, 128, 24, 7, None, 11),      # K between the route-array bounds
+    (40, 128, 128, 16, 16, 1.1, 0),       # K = 16 (the maximum)
 ])
 def test_bf16_forward_matches_oracle(B, T, D, F, E, K, zipf, n_pad):
     banner(f"bf16 forward T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
