@@ -22,6 +22,8 @@ def B():
 @pytest.mark.parametrize("T,E,K,zipf,n_pad", [
     (256, 8, 2, None, 26), (2048, 384, 6, None, 0), (2048, 384, 6, 1.2, 0), (1, 4, 2, None, 0),
     (0, 4, 2, None, 0), (777, 64, 8, 0.8, 300), (5, 3, 3, None, 15),
+    (5000, 1500, 4, None, 0),             # E > 1024: the scan runs two passes over experts
+    (3000, 4096, 8, 1.0, 100),            # E = 4096, the largest expert count
 ])
 def test_route_bit_exact(B, T, E, K, zipf, n_pad):
     banner(f"route T={T} E={E} K={K} zipf={zipf} pad={n_pad}")
@@ -32,6 +34,19 @@ def test_route_bit_exact(B, T, E, K, zipf, n_pad):
     check_route(got, ids, E)
     st, _ = layer.status()
     assert st == 0
+
+
+def test_route_maximum_route_count(B):
+    """T*K = 2^24 routes (the plan's limit): 65,536 counting-sort chunks."""
+    T, E, K = 1 << 21, 16, 8
+    banner(f"route T={T} E={E} K={K} (2^24 routes)")
+    layer = B.MoeLayer(T, 128, 128, E, K, "bf16")
+    rng = np.random.default_rng(9)
+    ids = np.argsort(rng.random((T, E), dtype=np.float32), axis=1)[:, :K].astype(np.int32)
+    ids[rng.random((T, K)) < 0.01] = -1
+    layer.route(torch.from_numpy(ids).cuda())
+    check_route(layer.readback(T), ids, E)
+    assert layer.status()[0] == 0
 
 
 def test_route_bad_ids_flagged(B):
@@ -75,6 +90,7 @@ def test_tiny_fp32_layer_matches_oracle(B):
     (33, 512, 384, 40, 3, 0.5, 5),       # more experts than rows per expert
     (50, 256, 128, 24, 7, None, 11),      # K between the route-array bounds
     (40, 128, 128, 16, 16, 1.1, 0),       # K = 16 (the maximum)
+    (700, 128, 128, 2048, 4, None, 0),    # E > 1024, most experts with 0-3 rows
 ])
 def test_bf16_forward_matches_oracle(B, T, D, F, E, K, zipf, n_pad):
     banner(f"bf16 forward T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
