@@ -159,10 +159,12 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
     u32x4 R0[6], R1[6];
     auto load = [&](u32x4* R, int s) {
       const uint16_t* p = wsrc + int64_t(s) * 64 * N;
-      R[0] = *reinterpret_cast<const u32x4*>(p);
-      R[1] = *reinterpret_cast<const u32x4*>(p + N);
-      R[2] = *reinterpret_cast<const u32x4*>(p + 32 * N);
-      R[3] = *reinterpret_cast<const u32x4*>(p + 33 * N);
+      // weights stream through once: non-temporal loads keep them from
+      // evicting the token tiles the other n-tiles of this expert re-read
+      R[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+      R[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + N));
+      R[2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 32 * N));
+      R[3] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 33 * N));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);

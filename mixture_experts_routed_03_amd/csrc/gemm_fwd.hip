@@ -175,7 +175,8 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
     auto load = [&](u32x4* R, int s) {
       const int64_t off = int64_t(s) * 128;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) R[j] = *reinterpret_cast<const u32x4*>(wsrc[j] + off);
+      for (int j = 0; j < 4; ++j)   // weights: non-temporal (streamed once per m-tile)
+        R[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + off));
 #pragma unroll
       for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
     };

@@ -160,7 +160,8 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     auto load = [&](u32x4* R, uint32_t* Sc, int s) {
       const int64_t off = int64_t(s) * 128;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) R[j] = *reinterpret_cast<const u32x4*>(wsrc[j] + off);
+      for (int j = 0; j < 4; ++j)   // weights: non-temporal (streamed once per m-tile)
+        R[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + off));
 #pragma unroll
       for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
       Sc[0] = wsc_src[s];
@@ -363,7 +364,8 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
     auto load = [&](u32x4* R, uint32_t* Sc, int s) {
       const uint8_t* p = wsrc + int64_t(s) * 128 * N;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) R[i] = *reinterpret_cast<const u32x4*>(p + i * N);
+      for (int i = 0; i < 4; ++i)   // weights: non-temporal (streamed once per m-tile)
+        R[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * N));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
