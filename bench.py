@@ -12,6 +12,8 @@ workloads add the row quantizers and column bundles.
 Workloads (all at T = 2,048 tokens, D = 7,168, F = 2,048, E = 384, top-6):
   bf16_train_balanced  BF16, balanced routing, forward + backward (default)
   bf16_fwd_balanced    BF16, balanced routing, forward only
+  bf16_fwd_fused       the same with the combine fused into the W2 epilogue
+                       (fp32 atomics; inference form)
   bf16_train_zipf      BF16, Zipf(1.2) routing, forward + backward
   mxfp8_train_shared   MXFP8 routed layer + one shared BF16 SwiGLU expert,
                        forward + backward
@@ -48,6 +50,7 @@ WORKLOADS = {
     # name: (config key, training)
     "bf16_train_balanced": ("bf16_fwd_balanced", True),
     "bf16_fwd_balanced": ("bf16_fwd_balanced", False),
+    "bf16_fwd_fused": ("bf16_fwd_balanced", False),
     "bf16_train_zipf": ("bf16_train_zipf", True),
     "mxfp8_train_shared": ("mxfp8_train_shared", True),
     "mxfp8_ten_layer": ("mxfp8_ten_layer", True),
@@ -117,6 +120,8 @@ def alg_bytes(name, m):
     w2 = int(ne * D * F * wb)
     common = {
         "route": T * K * 4 * 2 + R * 4 * 2,
+        "zero_y32": T * D * 4,
+        "fused_finish": T * D * 4 + T * D * es + T * K * 8,
         "gather": T * D * es + R * D * es,
         "combine": T * K * D * es + T * D * es + T * K * 8,
         "combine_bwd": T * D * es + T * K * D * es + R * D * es + T * K * 8,
@@ -128,6 +133,7 @@ def alg_bytes(name, m):
         return {
             "w13_swiglu": w13 + T * D * es + R * 2 * F * es + R * F * es,
             "w2_scatter": w2 + R * F * es + R * D * es,
+            "w2_fused": w2 + R * F * es + T * D * 4 + R * 4,
             "w2_dgrad_swiglu": w2 + R * D * es + 2 * R * 2 * F * es + R * F * es,
             "w2_wgrad": ne * D * F * dwb + R * D * es + R * F * es,
             "w13_dgrad": w13 + R * 2 * F * es + R * D * 4,
@@ -140,6 +146,7 @@ def alg_bytes(name, m):
         "bundle_h2": R * F * 2 + q(Rp * F),
         "quant_h2": R * F * 2 + q(R * F),
         "w2_scatter": w2 + q(R * F) + R * D * 2,
+        "w2_fused": w2 + q(R * F) + T * D * 4 + R * 4,
         "quant_dh3": R * D * 2 + q(R * D),
         "bundle_dh3": R * D * 2 + q(Rp * D),
         "w2_dgrad_swiglu": w2 + q(R * D) + 2 * R * 2 * F * 2,
@@ -159,7 +166,7 @@ def kernel_flops(name, m):
         name = name[len("replay_"):]
     if name in ("w13_swiglu", "w13_dgrad", "w13_wgrad"):
         return 2 * R * 2 * F * D
-    if name in ("w2_scatter", "w2_dgrad_swiglu", "w2_wgrad"):
+    if name in ("w2_scatter", "w2_fused", "w2_dgrad_swiglu", "w2_wgrad"):
         return 2 * R * D * F
     return None
 
@@ -295,7 +302,14 @@ def setup(args, dev):
         dws13 = torch.empty_like(lay["w13_shared"])
         dws2 = torch.empty_like(lay["w2_shared"])
 
+    fused = args.workload == "bf16_fwd_fused"
+    y32 = torch.empty((T, D), dtype=torch.float32, device=dev) if fused else None
+
     def step():
+        if fused:
+            layer.route(lay["ids"])
+            layer.forward_fused(lay["x"], lay["w13"], lay["w2"], lay["scores"], y, y32=y32)
+            return
         if shared is not None:
             shared.route(sh_ids)
             shared.forward(lay["x"], lay["w13_shared"], lay["w2_shared"])

@@ -193,6 +193,22 @@ moe_status moe_combine(moe_plan_t plan, void* route_ws, const float* scores,
                        const void* h3_slots, const void* y_addend, void* y,
                        hipStream_t stream);
 
+/* Inference forward with the combine fused into the W2 epilogue (the FUSED
+ * mode of the explainer's section 05 kernels, where the expert kernel adds
+ * each route's weighted output into its token's row): like moe_expert_fwd
+ * followed by moe_combine, but every route's bf16-rounded (F32 plans: fp32)
+ * h3, times its score, is added into y32[t] (caller-owned fp32 [T,D]
+ * scratch, zeroed by this call) with hardware float atomics, then
+ * y = y32 (+ y_addend).  No route slots are written, so the order of the K
+ * additions per token is not fixed and y may differ from the slot combine
+ * in the last bits; use moe_combine where bit-reproducible outputs matter.
+ * Inference plans only (training = 0: nothing is kept for a backward,
+ * MOE_ERR_UNSUPPORTED otherwise).  scores: [T,K] fp32; a null scores or y
+ * with routed rows sets MOE_STATUS_NULL_INPUT. */
+moe_status moe_expert_fwd_fused(moe_plan_t plan, void* route_ws, const void* x,
+                                const float* scores, const moe_weights* w, float* y32,
+                                const void* y_addend, void* y, void* scratch, hipStream_t stream);
+
 /* Backward of one layer (blog section 2 SwiGLU backward, section 5): from
  * dy [T,D] computes dscores, W2 DGRAD with the SwiGLU backward epilogue,
  * W2 and W13 WGRAD, W13 DGRAD and the per-token sum of the K route input

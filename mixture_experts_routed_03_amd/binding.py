@@ -70,6 +70,7 @@ _SIGS = {
     "moe_route": [_P, ctypes.c_int64, _P, _P, _P],
     "moe_expert_fwd": [_P, ctypes.c_int32, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P, _P],
     "moe_combine": [_P, _P, _P, _P, _P, _P, _P],
+    "moe_expert_fwd_fused": [_P, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P, _P, _P],
     "moe_expert_bwd": [_P, ctypes.c_int32, _P, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P,
                        _P, ctypes.POINTER(moe_grads), ctypes.c_uint32, _P],
     "moe_read_status": [_P, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32), _P],
@@ -169,6 +170,14 @@ def moe_expert_fwd(plan, layer, route_ws, x, weights, h3_slots, arena, scratch, 
 def moe_combine(plan, route_ws, scores, h3_slots, y_addend, y, stream=None):
     _check(lib().moe_combine(plan, _ptr(route_ws), _ptr(scores), _ptr(h3_slots), _ptr(y_addend),
                              _ptr(y), _stream(stream)), "moe_combine")
+
+
+def moe_expert_fwd_fused(plan, route_ws, x, scores, weights, y32, y_addend, y, scratch,
+                         stream=None):
+    w = _weights(*weights)
+    _check(lib().moe_expert_fwd_fused(plan, _ptr(route_ws), _ptr(x), _ptr(scores),
+                                      ctypes.byref(w), _ptr(y32), _ptr(y_addend), _ptr(y),
+                                      _ptr(scratch), _stream(stream)), "moe_expert_fwd_fused")
 
 
 def moe_expert_bwd(plan, layer, route_ws, x, scores, dy, weights, h3_slots, arena, scratch,
@@ -311,6 +320,16 @@ class MoeLayer:
     def combine(self, scores, y, y_addend=None, route_ws=None, h3=None):
         moe_combine(self.plan, self.route_ws if route_ws is None else route_ws, scores,
                     self.h3 if h3 is None else h3, y_addend, y)
+
+    def forward_fused(self, x, w13, w2, scores, y, y_addend=None, y32=None, route_ws=None,
+                      prepared=None):
+        """Inference forward with the combine fused into the W2 epilogue
+        (fp32 atomics into y32, then y); returns y32."""
+        if y32 is None:
+            y32 = torch.empty((x.shape[0], self.D), dtype=torch.float32, device=self.device)
+        moe_expert_fwd_fused(self.plan, self.route_ws if route_ws is None else route_ws, x, scores,
+                             self._w(w13, w2, prepared), y32, y_addend, y, self.scratch)
+        return y32
 
     def backward(self, x, scores, dy, w13, w2, dx, dw13, dw2, dscores=None, layer=0, flags=0,
                  route_ws=None, h3=None, prepared=None):

@@ -24,6 +24,12 @@ hipError_t launch_plan_rewind(RouteHdr* hdr, void* arena, hipStream_t s);
 hipError_t launch_arena_reset(void* arena, hipStream_t s);
 hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
                          const int32_t* sorted_route, void* dst, int64_t R_max, hipStream_t s);
+hipError_t launch_zero_rows_f32(const RouteHdr* hdr, float* p, int64_t D, int64_t T_max,
+                                hipStream_t s);
+hipError_t launch_fused_finish(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
+                               const float* scores, const float* y32, const void* addend,
+                               void* y, int K, int64_t D, int64_t T_max, uint32_t* status,
+                               hipStream_t s);
 hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
                           const float* scores, const void* h3, const void* addend, void* y,
                           int K, int64_t D, int64_t T_max, uint32_t* status, hipStream_t s);
@@ -514,6 +520,69 @@ moe_status moe_combine(moe_plan_t p, void* ws, const float* scores, const void* 
   return hip_status(timed(p, "combine", s, [&] {
     return launch_combine(p->d.prec, hdr, at<int32_t>(ws, p->rl.route_to_row), scores, h3,
                           y_addend, y, p->d.k, p->d.d, p->d.t_max, &hdr->status, s);
+  }));
+}
+
+moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const float* scores,
+                                const moe_weights* w, float* y32, const void* y_addend, void* y,
+                                void* scratch, hipStream_t s) {
+  if (!p || !ws || !w || !scratch || !y32) return MOE_ERR_ARG;
+  const moe_desc& d = p->d;
+  if (d.training) return MOE_ERR_UNSUPPORTED;   // no route outputs are kept for a backward
+  const bool mx = d.prec == MOE_PREC_MXFP8;
+  if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;
+  if (!aligned16(x) || !aligned16(w->w13) || !aligned16(w->w2) || !aligned16(w->q13) ||
+      !aligned16(w->q2) || !aligned16(y32) || !aligned16(y) || !aligned16(y_addend) ||
+      !aligned16(scratch) || !aligned16(ws))
+    return MOE_ERR_ARG;
+  RouteHdr* hdr = hdr_of(ws);
+  char* sc = reinterpret_cast<char*>(scratch);
+  const ScratchLayout& L = p->sl;
+  PlanArgs pa{0, d.max_layers, 0, p->es, d.d, d.f, p->budget, 0, uint64_t(sc + L.h1), mx ? 1 : 0,
+              0, {mx ? uint64_t(sc + L.xcq) : 0, mx ? uint64_t(sc + L.xcs) : 0,
+                  mx ? uint64_t(sc + L.h2cq) : 0, mx ? uint64_t(sc + L.h2cs) : 0}};
+  hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
+  const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
+  const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
+  const int32_t* route_to_row = at<int32_t>(ws, p->rl.route_to_row);
+  const int cus = plan_cus(p);
+  if (!scores) {   // the W2 epilogue needs the scores: report, as the slot combine does
+    e = launch_fused_finish(d.prec, hdr, route_to_row, nullptr, y32, y_addend, y, d.k, d.d,
+                            d.t_max, &hdr->status, s);
+    return hip_status(e);
+  }
+  e = timed(p, "zero_y32", s, [&] { return launch_zero_rows_f32(hdr, y32, d.d, d.t_max, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (!mx) {
+    FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
+                d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
+    e = timed(p, "w13_swiglu", s,
+              [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    FwdArgs a2{hdr, offsets, mtoff, sorted_route, sc + L.h2, w->w2, nullptr, nullptr,
+               d.f, d.d, d.f, d.d / 128, d.e, 0, nullptr, d.k, scores, y32};
+    e = timed(p, "w2_fused", s, [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); });
+  } else {
+    e = mx_forward_w13(p, hdr, ws, sc, x, w, 0, cus, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    RowqArgs rq{hdr, sc + L.h2, reinterpret_cast<uint8_t*>(sc + L.qh2),
+                reinterpret_cast<uint8_t*>(sc + L.sh2), d.f, -1, -1, -1, 0, int(p->R_max)};
+    e = timed(p, "quant_h2", s, [&] { return launch_rowq(rq, p->R_max, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    MxArgs a2{hdr, offsets, poffsets, mtoff, sorted_route,
+              reinterpret_cast<const uint8_t*>(sc + L.qh2), reinterpret_cast<const uint8_t*>(sc + L.sh2),
+              reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
+              nullptr, nullptr, nullptr, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
+              int(p->R_max), scores, y32, d.k};
+    e = timed(p, "w2_fused", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); });
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(timed(p, "fused_finish", s, [&] {
+    return launch_fused_finish(d.prec, hdr, route_to_row, scores, y32, y_addend, y, d.k, d.d,
+                               d.t_max, &hdr->status, s);
   }));
 }
 

@@ -89,6 +89,10 @@ struct FwdArgs {
   int replay_only;  // 1: run only when the layer's forward chose replay
   const void* x;    // W13: the caller's x [T, Kd]; packed row r reads x[sorted_route[r] / K]
   int K;
+  // W2 FUSED combine: y32[t] += scores[route] * h3 (fp32 atomic add) instead
+  // of the slot store (y32 null: slots)
+  const float* scores;
+  float* y32;
 };
 
 // Arguments of the grouped backward GEMM launches.
@@ -129,6 +133,9 @@ struct MxArgs {
   int a_slot;           // WGRAD: >= 0 takes A codes/exponents from record aux[a_slot], aux[a_slot+1]
   int replay_only;
   int sa_rows;          // FPROP/DGRAD: row stride of the stage-grouped token exponents
+  const float* scores;  // W2 FUSED combine (see FwdArgs)
+  float* y32;
+  int K;
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:
@@ -205,6 +212,16 @@ __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __ex
 // barrier waits for this wave's LDS operations but not for its outstanding
 // global loads or stores: prefetched tiles stay in flight across it (a full
 // __syncthreads() drains every outstanding global access on gfx9).
+// FUSED combine: four consecutive fp32 outputs of one route, scaled by its
+// score, added into the token's fp32 row with hardware float atomics (the
+// summation order across routes is not fixed).
+__device__ __forceinline__ void fused_add4(float* y, float s, float a, float b, float c, float d) {
+  unsafeAtomicAdd(y + 0, s * a);
+  unsafeAtomicAdd(y + 1, s * b);
+  unsafeAtomicAdd(y + 2, s * c);
+  unsafeAtomicAdd(y + 3, s * d);
+}
+
 // A device address held in memory (the layer record) as a pointer the
 // compiler knows to be global: accesses through it become global rather than
 // flat instructions, and flat ones also count against the LDS wait counter,

@@ -174,6 +174,60 @@ __global__ __launch_bounds__(256) void k_combine(const RouteHdr* __restrict__ hd
   }
 }
 
+// FUSED combine, before the W2 kernel: y32 = 0 (a fill kernel, so the call
+// has no memset node when captured).
+__global__ __launch_bounds__(256) void k_zero_f32(const RouteHdr* __restrict__ hdr,
+                                                  float4* __restrict__ p, int64_t row4) {
+  const int64_t n4 = int64_t(hdr->T) * row4;
+  for (int64_t g = grid_thread(); g < n4; g += grid_threads()) p[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// FUSED combine, after the W2 kernel: y[t] = y32[t] (+ addend[t]) in the act
+// dtype; nonzero scores on padding routes are reported as in the slot combine.
+template <typename T>
+__global__ __launch_bounds__(256) void k_fused_finish(const RouteHdr* __restrict__ hdr,
+                                                      const int32_t* __restrict__ route_to_row,
+                                                      const float* __restrict__ scores,
+                                                      const float4* __restrict__ y32,
+                                                      const u32x4* __restrict__ addend,
+                                                      u32x4* __restrict__ y, int K,
+                                                      int64_t row_chunks,
+                                                      uint32_t* __restrict__ status) {
+  constexpr int nv = Vec16<T>::n;   // values per 16-byte output chunk
+  const int64_t n = int64_t(hdr->T) * row_chunks;
+  if (n == 0) return;
+  if (!scores || !y) {
+    if (grid_thread() == 0) atomicOr(status, MOE_STATUS_NULL_INPUT);
+    return;
+  }
+  for (int64_t g = grid_thread(); g < n; g += grid_threads()) {
+    const int64_t t = g / row_chunks;
+    const int64_t i = g - t * row_chunks;
+    if (i == 0) {
+      bool bad = false;
+      for (int k = 0; k < K; ++k)
+        bad |= route_to_row[t * K + k] < 0 && scores[t * K + k] != 0.0f;
+      if (bad) atomicOr(status, MOE_STATUS_PAD_SCORE);
+    }
+    float acc[nv];
+#pragma unroll
+    for (int j = 0; j < nv / 4; ++j) {
+      const float4 v = y32[g * (nv / 4) + j];
+      acc[4 * j] = v.x;
+      acc[4 * j + 1] = v.y;
+      acc[4 * j + 2] = v.z;
+      acc[4 * j + 3] = v.w;
+    }
+    if (addend) {
+      float f[nv];
+      Vec16<T>::unpack(addend[g], f);
+#pragma unroll
+      for (int j = 0; j < nv; ++j) acc[j] += f[j];
+    }
+    y[g] = Vec16<T>::pack(acc);
+  }
+}
+
 // dh3[row(t,k)] = s[t,k] * dy[t];  dscores[t,k] = <h3_slot(t,k), dy[t]> (0 for padding).
 // One workgroup per token at a time (grid-stride over tokens): the threads
 // share the row's chunks, and the K dot products are reduced through LDS.
@@ -352,6 +406,32 @@ hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to
                                          route_to_row, scores, reinterpret_cast<const u32x4*>(h3),
                                          reinterpret_cast<const u32x4*>(addend),
                                          reinterpret_cast<u32x4*>(y), K, D / 8, status));
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows_f32(const RouteHdr* hdr, float* p, int64_t D, int64_t T_max,
+                                hipStream_t s) {
+  if (T_max == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_f32, dim3(elem_grid(T_max * D / 4)), dim3(256), 0, s, hdr,
+                     reinterpret_cast<float4*>(p), D / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_finish(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
+                               const float* scores, const float* y32, const void* addend,
+                               void* y, int K, int64_t D, int64_t T_max, uint32_t* status,
+                               hipStream_t s) {
+  if (T_max == 0) return hipSuccess;
+  if (prec == MOE_PREC_F32)
+    hipLaunchKernelGGL(k_fused_finish<float>, dim3(elem_grid(T_max * (D / 4))), dim3(256), 0, s,
+                       hdr, route_to_row, scores, reinterpret_cast<const float4*>(y32),
+                       reinterpret_cast<const u32x4*>(addend), reinterpret_cast<u32x4*>(y), K,
+                       D / 4, status);
+  else
+    hipLaunchKernelGGL(k_fused_finish<uint16_t>, dim3(elem_grid(T_max * (D / 8))), dim3(256), 0,
+                       s, hdr, route_to_row, scores, reinterpret_cast<const float4*>(y32),
+                       reinterpret_cast<const u32x4*>(addend), reinterpret_cast<u32x4*>(y), K,
+                       D / 8, status);
   return hipGetLastError();
 }
 

@@ -295,10 +295,19 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
         const int m = 32 * b + lr;
         if (m < rows) {
           const int64_t slotr = a.sorted_route[row0 + m];
-          T* o = out0 + slotr * a.N + ncol;
+          if (a.y32) {
+            const float sc = a.scores[slotr];
+            float* o = a.y32 + (slotr / a.K) * a.N + ncol;
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            store4<T>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+            for (int g = 0; g < 4; ++g)
+              fused_add4(o + 8 * g, sc, Elem<T>::round(acc[4 * g]), Elem<T>::round(acc[4 * g + 1]),
+                         Elem<T>::round(acc[4 * g + 2]), Elem<T>::round(acc[4 * g + 3]));
+          } else {
+            T* o = out0 + slotr * a.N + ncol;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              store4<T>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+          }
         }
       }
     }

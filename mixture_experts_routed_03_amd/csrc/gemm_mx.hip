@@ -277,10 +277,20 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
         const int m = 32 * b + lr;
         if (m < rows) {
           const int64_t slotr = a.sorted_route[row0 + m];
-          uint16_t* o = out0 + slotr * a.N + ncol;
+          if (a.y32) {   // FUSED combine (h3 rounded to bf16 as the slots would hold it)
+            const float sc = a.scores[slotr];
+            float* o = a.y32 + (slotr / a.K) * a.N + ncol;
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            store4<uint16_t>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+            for (int g = 0; g < 4; ++g)
+              fused_add4(o + 8 * g, sc, round_bf16(acc[4 * g]), round_bf16(acc[4 * g + 1]),
+                         round_bf16(acc[4 * g + 2]), round_bf16(acc[4 * g + 3]));
+          } else {
+            uint16_t* o = out0 + slotr * a.N + ncol;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              store4<uint16_t>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
+                               acc[4 * g + 3]);
+          }
         }
       }
     }

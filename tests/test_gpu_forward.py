@@ -167,3 +167,47 @@ def test_full_size_bf16_forward_sampled(B):
     ref = sampled_forward_ref(lay, tokens)
     assert om.max_abs_rel(y[tokens], ref) < TOL["bf16"]
     assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("prec,T,D,F,E,K,zipf,n_pad", [
+    ("bf16", 300, 256, 256, 8, 2, None, 7),
+    ("bf16", 200, 384, 128, 12, 6, 1.2, 0),
+    ("f32", 256, 256, 128, 8, 2, None, 26),
+    ("mxfp8", 160, 256, 128, 6, 3, None, 5),
+])
+def test_fused_combine_matches_oracle(B, prec, T, D, F, E, K, zipf, n_pad):
+    """Combine fused into the W2 epilogue (fp32 atomics): same result as the
+    slot combine up to the order of the K additions per token."""
+    banner(f"fused combine {prec} T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
+    lay = make_inputs(T, D, F, E, K, prec, zipf=zipf, n_pad=n_pad, seed=T + 3)
+    ids = lay["ids"].clone(); sc = lay["scores"].clone()
+    ids[1] = -1; sc[1] = 0.0                      # an all-padded token
+    lay["ids"], lay["scores"] = ids, sc
+    layer = B.MoeLayer(T, D, F, E, K, prec)
+    y_slots = run_forward(layer, lay)
+    addend = torch.randn((T, D), generator=torch.Generator().manual_seed(5)).to(layer.act_dtype).cuda()
+    y = torch.empty_like(y_slots)
+    layer.route(lay["ids"])
+    layer.forward_fused(lay["x"], lay["w13"], lay["w2"], lay["scores"], y, y_addend=addend)
+    torch.cuda.synchronize()
+    if prec == "mxfp8":
+        from oracle import mx as omx
+        ref = omx.forward(lay["x"], ids, sc, lay["w13"].cpu(), lay["w2"].cpu())
+    else:
+        ref = oracle_forward(lay)
+    tol = TOL[prec]
+    assert om.max_abs_rel(y.float() - addend.float(), ref) < tol
+    assert torch.equal(y[1], addend[1])           # padding contributes exactly nothing
+    # against the slot combine: only the summation order differs
+    assert om.max_abs_rel(y.float() - addend.float(), y_slots) < (1e-5 if prec == "f32" else 1e-2)
+    assert layer.status()[0] == 0
+
+
+def test_fused_combine_needs_inference_plan(B):
+    layer = B.MoeLayer(8, 128, 128, 4, 2, "bf16", training=True)
+    x = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.MoeError) as ei:
+        layer.forward_fused(x, torch.zeros((4, 256, 128), dtype=torch.bfloat16, device="cuda"),
+                            torch.zeros((4, 128, 128), dtype=torch.bfloat16, device="cuda"),
+                            torch.zeros((8, 2), device="cuda"), torch.empty_like(x))
+    assert ei.value.code == 3
