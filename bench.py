@@ -19,6 +19,9 @@ Workloads (all at T = 2,048 tokens, D = 7,168, F = 2,048, E = 384, top-6):
                        forward + backward
   mxfp8_ten_layer      ten MXFP8 layers (Zipf 0, 0.6, 1.0, 1.4 cycled), ten
                        forwards then ten backwards in one byte-budgeted arena
+  ep8_share, ep64_share  the same 12,288 routed rows as one GPU's share under
+                       expert parallelism: 48 experts x ~256 rows, 6 x 2,048
+                       (BF16 forward + backward; compute-bound probes)
 
 Inputs are resident in HBM before timing starts.  Useful work is 6*R*D*F
 FLOPs forward and twice that backward per routed layer (R = valid routes;
@@ -54,6 +57,8 @@ WORKLOADS = {
     "bf16_train_zipf": ("bf16_train_zipf", True),
     "mxfp8_train_shared": ("mxfp8_train_shared", True),
     "mxfp8_ten_layer": ("mxfp8_ten_layer", True),
+    "ep8_share": ("ep8_share", True),
+    "ep64_share": ("ep64_share", True),
 }
 CPU_EXPERTS = {"bf16": 96, "mxfp8": 3}
 

@@ -175,6 +175,13 @@ CONFIGS = {
     "mxfp8_ten_layer": Config("mxfp8_ten_layer", 2048, 7168, 2048, 384, 6, "mxfp8",
                               zipf=(0.0, 0.6, 1.0, 1.4), training=True, layers=10,
                               note="ten MXFP8 layers, forwards then backwards, byte budget"),
+    # One GPU's share of the same routed rows (R = 12,288) under expert
+    # parallelism over 8 or 64 GPUs: 48 experts of ~256 rows, or 6 experts
+    # of 2,048 rows (every token routes to all six).
+    "ep8_share": Config("ep8_share", 2048, 7168, 2048, 48, 6, "bf16", training=True,
+                        note="EP8 share: 48 experts, ~256 rows each, BF16 forward+backward"),
+    "ep64_share": Config("ep64_share", 2048, 7168, 2048, 6, 6, "bf16", training=True,
+                         note="EP64 share: 6 experts, 2048 rows each, BF16 forward+backward"),
 }
 
 
