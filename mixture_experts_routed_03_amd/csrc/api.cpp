@@ -148,6 +148,7 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
   const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);  // FPROP/DGRAD m-tiles
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const char* tag = replay_only ? "replay_quant_x" : "quant_x";
   // x rows are read through the permutation (the gather happens in the loaders)
@@ -194,6 +195,7 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
   const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);  // FPROP/DGRAD m-tiles
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const int32_t* route_to_row = at<int32_t>(ws, p->rl.route_to_row);
   const int dw_f32 = d.dw_dtype == MOE_DTYPE_F32;
@@ -281,6 +283,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   L.offsets = o; o = a256(o + 4 * (E + 1));
   L.poffsets = o; o = a256(o + 4 * (E + 1));
   L.mtoff = o; o = a256(o + 4 * (E + 1));
+  L.gtoff = o; o = a256(o + 4 * (E + 1));
   L.chunk_hist = o; o = a256(o + 4 * L.nchunks * E);
   L.chunk_flags = o; o = a256(o + 4 * L.nchunks);
   L.sorted_route = o; o = a256(o + 4 * R);
@@ -483,16 +486,19 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
   const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);  // FPROP/DGRAD m-tiles
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const int cus = plan_cus(p);
   if (!mx) {
-    FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
+    FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
+    a13.stoff = mtoff;
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
-    FwdArgs a2{hdr, offsets, mtoff, sorted_route, sc + L.h2, w->w2, h3, nullptr,
+    FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + L.h2, w->w2, h3, nullptr,
                d.f, d.d, d.f, d.d / 128, d.e, 0};
+    a2.stoff = mtoff;
     return hip_status(timed(p, "w2_scatter", s,
                             [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
   }
@@ -546,6 +552,7 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
   const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);  // FPROP/DGRAD m-tiles
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const int32_t* route_to_row = at<int32_t>(ws, p->rl.route_to_row);
   const int cus = plan_cus(p);
@@ -557,13 +564,15 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
   e = timed(p, "zero_y32", s, [&] { return launch_zero_rows_f32(hdr, y32, d.d, d.t_max, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (!mx) {
-    FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
+    FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
+    a13.stoff = mtoff;
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
-    FwdArgs a2{hdr, offsets, mtoff, sorted_route, sc + L.h2, w->w2, nullptr, nullptr,
+    FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + L.h2, w->w2, nullptr, nullptr,
                d.f, d.d, d.f, d.d / 128, d.e, 0, nullptr, d.k, scores, y32};
+    a2.stoff = mtoff;
     e = timed(p, "w2_fused", s, [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); });
   } else {
     e = mx_forward_w13(p, hdr, ws, sc, x, w, 0, cus, s);
@@ -605,6 +614,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   char* sc = reinterpret_cast<char*>(scratch);
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);  // FPROP/DGRAD m-tiles
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const int32_t* route_to_row = at<int32_t>(ws, p->rl.route_to_row);
   const int cus = plan_cus(p);
@@ -616,8 +626,9 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   // Replay (device predicate): rebuild h1 in scratch from x when the forward
   // did not save it.
   if (mx) return mx_backward(p, hdr, ws, sc, x, w, scores, dy, h3, arena, g, flags, cus, s);
-  FwdArgs a13{hdr, offsets, mtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
+  FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
               d.d, 2 * d.f, d.f, d.f / 64, d.e, 1, x, d.k};
+  a13.stoff = mtoff;
   e = timed(p, "replay_w13", s, [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = timed(p, "combine_bwd", s, [&] {
@@ -627,16 +638,16 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   void* h2 = sc + p->sl.h2;
   // BwdArgs: hdr, offsets, mtoff, W, tok, grad, arows, out, out2, Kd, N, F, D, E, NT, a_ld, b_ld
-  BwdArgs b{hdr, offsets, mtoff, w->w2, dh3, nullptr, nullptr, dh1, h2,
-            d.d, d.f, d.f, d.d, d.e, d.f / 128, 0, 0};
+  BwdArgs b{hdr, offsets, gtoff, w->w2, dh3, nullptr, nullptr, dh1, h2,
+            d.d, d.f, d.f, d.d, d.e, d.f / 128, 0, 0, mtoff};
   e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_dgrad(0, b, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw2{hdr, offsets, mtoff, nullptr, nullptr, dh3, h2, g->dw2, nullptr,
               0, 0, d.f, d.d, d.e, 0, d.f, d.d};
   e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(dw_f32, 2, bw2, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
-  BwdArgs b13{hdr, offsets, mtoff, w->w13, dh1, nullptr, nullptr, dxr, nullptr,
-              2 * d.f, d.d, d.f, d.d, d.e, d.d / 128, 0, 0};
+  BwdArgs b13{hdr, offsets, gtoff, w->w13, dh1, nullptr, nullptr, dxr, nullptr,
+              2 * d.f, d.d, d.f, d.d, d.e, d.d / 128, 0, 0, mtoff};
   e = timed(p, "w13_dgrad", s, [&] { return launch_dgrad(1, b13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   // dW13's A rows: a packed copy of the x rows (its loads then stream)

@@ -10,7 +10,8 @@
 namespace moe {
 
 // ---------------------------------------------------------------- constants
-constexpr int kBM = 64;           // token rows per grouped-GEMM m-tile
+constexpr int kBM = 64;           // token rows per WGRAD contraction stage (and small m-tiles)
+constexpr int kBMX = 128;         // token rows of an FPROP/DGRAD m-tile of an expert with > kBM rows
 constexpr int kRankChunk = 256;   // routes per counting-sort chunk
 constexpr int kMxBlock = 32;      // MX block length (values per E8M0 scale)
 constexpr int kMaxE = 4096;
@@ -18,6 +19,9 @@ constexpr int kMaxK = 16;
 
 __host__ __device__ inline int64_t align_up(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
 __host__ __device__ inline int64_t align128(int64_t n) { return align_up(n, 128); }
+// Token rows per FPROP/DGRAD m-tile of an expert with c rows: a hot expert
+// takes 128-row tiles, so each weight tile is streamed once per 128 rows.
+__host__ __device__ inline int gemm_tile_rows(int c) { return c > kBM ? kBMX : kBM; }
 
 // ------------------------------------------------- per-layer planner record
 // Written on the device by the planner kernel during forward, read by every
@@ -40,7 +44,7 @@ struct RouteHdr {
   int32_t T;            // tokens of the call
   int32_t R;            // valid routes = packed rows
   int32_t Rpad;         // sum over experts of counts rounded up to 32
-  int32_t n_mt;         // m-tiles of kBM rows over all experts
+  int32_t n_mt;         // 64-row stages over all experts (sum of ceil(count / 64))
   uint32_t status;      // MOE_STATUS_* bits
   int32_t max_count;    // largest expert row count
   int32_t pad[10];
@@ -56,7 +60,7 @@ constexpr int64_t kArenaHdrBytes = 4096;  // data region starts here
 
 // Byte offsets inside a route workspace (host computed from the plan).
 struct RouteLayout {
-  int64_t hdr, counts, offsets, poffsets, mtoff, chunk_hist, chunk_flags,
+  int64_t hdr, counts, offsets, poffsets, mtoff, gtoff, chunk_hist, chunk_flags,
       sorted_route, route_to_row, total;
   int64_t nchunks;
 };
@@ -93,6 +97,7 @@ struct FwdArgs {
   // of the slot store (y32 null: slots)
   const float* scores;
   float* y32;
+  const int32_t* stoff;  // 64-row stage prefix (XCD work split, xcd_first_tile)
 };
 
 // Arguments of the grouped backward GEMM launches.
@@ -111,6 +116,7 @@ struct BwdArgs {
   int F, D, E;
   int NT;               // DGRAD n-tiles per expert
   int a_ld, b_ld;       // WGRAD row lengths of the A rows (= dW row length) and B rows (= dW rows)
+  const int32_t* stoff; // DGRAD: 64-row stage prefix (XCD work split); mtoff = the m-tile prefix
 };
 
 // Arguments of the MXFP8 grouped GEMM launches.
@@ -254,27 +260,50 @@ template <> struct Elem<uint16_t> {
 // Number of XCDs of the MI355X; workgroups are dispatched round-robin over them.
 constexpr int kXcds = 8;
 
-// First weight-gradient work item of XCD x.  Items run expert-major, per_e
-// per expert; an item of expert e costs its 64-row contraction stages
-// (mtoff[e + 1] - mtoff[e]) plus one for storing its output tile, and the
-// XCDs receive equal shares of the total cost, so one hot expert does not
-// load a single XCD.  x = kXcds gives the item count.
-__device__ inline int xcd_first_item(const int32_t* __restrict__ mtoff, int E, int per_e, int x) {
-  const int64_t W = int64_t(per_e) * (mtoff[E] + E);
+// Work split over the XCDs.  Units run expert-major, per_e per expert; a
+// unit of expert e costs (pre[e + 1] - pre[e]) + cw, and the XCDs receive
+// runs of units of equal total cost, so one hot expert does not load a
+// single XCD.  Returns the first unit of XCD x; x = kXcds gives the unit
+// count.
+//  * WGRAD: a unit is an output tile; pre = the 64-row stage prefix, cw = 1
+//    for storing the tile (experts with no rows still store zeros).
+//  * FPROP/DGRAD: a unit is a weight column (an n-tile of an expert with all
+//    its m-tiles, which run side by side and share that weight tile in L2);
+//    pre = the 64-row stage prefix, cw = 0.  Measured on a Zipf(1.2) load,
+//    a column of a hot expert costs about its token rows: adding a per-column
+//    weight cost only made the XCDs holding hot experts finish later.
+__device__ inline int xcd_first_unit(const int32_t* __restrict__ pre, int cw, int E, int per_e,
+                                     int x) {
+  auto prefix = [&](int e) { return int64_t(pre[e]) + int64_t(cw) * e; };
+  const int64_t W = int64_t(per_e) * prefix(E);
   const int64_t T = W * x / kXcds;
-  int lo = 0, hi = E;  // the largest e with per_e * (mtoff[e] + e) <= T
+  int lo = 0, hi = E;  // the largest e with per_e * prefix(e) <= T
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (int64_t(per_e) * (mtoff[mid] + mid) <= T)
+    if (int64_t(per_e) * prefix(mid) <= T)
       lo = mid;
     else
       hi = mid - 1;
   }
   if (lo >= E) return E * per_e;
-  const int64_t P = int64_t(per_e) * (mtoff[lo] + lo);
-  const int64_t c = int64_t(mtoff[lo + 1] - mtoff[lo]) + 1;
+  const int64_t P = int64_t(per_e) * prefix(lo);
+  // lo < E is the largest such e, so expert lo's units cost c >= 1 each
+  const int64_t c = prefix(lo + 1) - prefix(lo);
   const int64_t i = (T - P + c - 1) / c;
   return int(min(int64_t(lo) * per_e + i, int64_t(E) * per_e));
+}
+__device__ inline int xcd_first_item(const int32_t* __restrict__ mtoff, int E, int per_e, int x) {
+  return xcd_first_unit(mtoff, 1, E, per_e, x);
+}
+// First FPROP/DGRAD work item of XCD x: items run expert-major, then n-tile,
+// then m-tile (gtoff = the m-tile prefix, stoff = the 64-row stage prefix);
+// a weight column never straddles two XCDs.
+__device__ inline int xcd_first_tile(const int32_t* __restrict__ gtoff,
+                                     const int32_t* __restrict__ stoff, int E, int NT, int x) {
+  const int c = xcd_first_unit(stoff, 0, E, NT, x);
+  const int e = c / NT;
+  if (e >= E) return gtoff[E] * NT;
+  return gtoff[e] * NT + (c - e * NT) * (gtoff[e + 1] - gtoff[e]);
 }
 
 }  // namespace moe

@@ -109,10 +109,26 @@ __device__ __forceinline__ int tsw_g(int o, int g) { return o * 32 + (((g ^ o ^ 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
 
 // ------------------------------------------------------------------ DGRAD
+// Weight stage (contraction rows k, 256-byte rows of 128 output columns):
+// the 16-byte chunks of row k are XOR-swizzled by 4 (k & 3), so both the
+// row-wise 16-byte stores and the transpose reads (8 rows x 4 chunks per
+// instruction) touch every bank equally.
+__device__ __forceinline__ int wsw(int k, int c) { return k * 256 + ((c ^ ((k & 3) << 2)) << 4); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4j + q addresses row j,
+// columns 4q..4q+3 of a 4 x 16 bf16 block; lane i receives column i, rows
+// 0..3 (elements 0..3).
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 template <int KIND>
-__global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
-  constexpr int kW = 128 * 32 * 4;   // transposed weight stage: 128 columns x 64 values
-  constexpr int kT = kBM * 128;      // token stage: 64 rows x 64 values
+__global__ __launch_bounds__(256, 2) void k_gemm_dgrad(BwdArgs a) {
+  constexpr int kW = 64 * 256;       // weight stage: 64 contraction rows x 128 columns
+  constexpr int kT = kBMX * 128;     // token stage: up to 128 rows x 64 values
   constexpr int kStage = kW + kT;
   __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
   const int tid = threadIdx.x;
@@ -120,120 +136,126 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
   const int wave = tid >> 6;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int c16 = tid & 15;   // weight loader: 8-column chunk of a 256-byte row segment
-  const int kp = tid >> 4;    // weight loader: row pairs kp and kp + 16 of a stage
+  const int c16 = tid & 15;   // weight loader: 16-byte chunk of a 256-byte row segment
+  const int kp = tid >> 4;    // weight loader: contraction rows kp + 16 i
   const int lc = tid & 7;     // token loader: 16-byte chunk of a 128-byte row segment
   const int lrow = tid >> 3;  // token loader: tile row (+ 32 j)
+  // transpose reads of the weight operand: the 16-lane group (lane >> 4)
+  // covers output columns 32 wave + 16 ((lane >> 4) & 1) .. + 15 and
+  // contraction rows 8 lh .. 8 lh + 7 of each 16-row MFMA step
+  const int tr_row = 8 * lh + ((lane & 15) >> 2);
+  const int tr_chunk = 4 * wave + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_byte = 8 * (lane & 1);
 
   const RouteHdr* hdr = a.hdr;
-  const int n_items = hdr->n_mt * a.NT;
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
-  const int chunk = (n_items + kXcds - 1) / kXcds;
+  // a.mtoff is the m-tile prefix (128-row tiles for experts with more than
+  // 64 rows); the XCDs split the items by token rows
+  const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
+  const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
   const int S = a.Kd / 64;
   const int64_t N = a.N;
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
-  for (int it = slot; it < chunk; it += per) {
-    const int w = xcd * chunk + it;
-    if (w >= n_items) break;
+  for (int w = first + slot; w < last; w += per) {
     const int e = find_expert_b(a.mtoff, a.E, a.NT, w);
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;
     const int mt = u - nt * mt_e;
-    const int row0 = a.offsets[e] + mt * kBM;
-    const int rows = min(kBM, a.offsets[e + 1] - row0);
+    const int bm = gemm_tile_rows(a.offsets[e + 1] - a.offsets[e]);
+    const int row0 = a.offsets[e] + mt * bm;
+    const int rows = min(bm, a.offsets[e + 1] - row0);
 
     const uint16_t* wsrc = reinterpret_cast<const uint16_t*>(a.W) +
-                           (int64_t(e) * a.Kd + 2 * kp) * N + nt * 128 + c16 * 8;
+                           (int64_t(e) * a.Kd + kp) * N + nt * 128 + c16 * 8;
     // Tile rows past the expert's last row re-read that row (outputs not stored).
-    const char* tsrc[2];
+    const char* tsrc[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
       tsrc[j] = reinterpret_cast<const char*>(a.tok) +
                 int64_t(row0 + min(lrow + 32 * j, rows - 1)) * a.Kd * 2 + lc * 16;
 
-    f32x16 acc0 = {}, acc1 = {};
-    u32x4 R0[6], R1[6];
-    auto load = [&](u32x4* R, int s) {
+    f32x16 acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
+    u32x4 R0[8], R1[8];
+    // NB: 32-token blocks loaded and multiplied (1, 2 or 4; one loop copy
+    // each, so no accumulator depends on a branch inside the stage loop)
+    auto load = [&](u32x4* R, int s, auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
       const uint16_t* p = wsrc + int64_t(s) * 64 * N;
       // weights stream through once: non-temporal loads keep them from
       // evicting the token tiles the other n-tiles of this expert re-read
-      R[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-      R[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + N));
-      R[2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 32 * N));
-      R[3] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 33 * N));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i)
+        R[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 16 * i * N));
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
         R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
     };
-    auto store = [&](const u32x4* R, int buf) {
-      uint32_t* la = reinterpret_cast<uint32_t*>(lds + buf * kStage);
-      uint32_t d[8];
-      interleave8(R[0], R[1], d);
+    auto store = [&](const u32x4* R, int buf, auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
+      char* la = lds + buf * kStage;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) la[tsw(c16 * 8 + q, kp)] = d[q];
-      interleave8(R[2], R[3], d);
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(la + wsw(kp + 16 * i, c16)) = R[i];
+      char* lt = la + kW;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) la[tsw(c16 * 8 + q, kp + 16)] = d[q];
-      char* lt = lds + buf * kStage + kW;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
+      for (int j = 0; j < NB; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
     };
-    // TWO: the tile has more than 32 rows (one loop copy per case, so no
-    // accumulator depends on a branch inside the stage loop).
-    auto compute = [&](int buf, auto two_c) {
-      constexpr bool TWO = decltype(two_c)::value;
+    auto compute = [&](int buf, auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
       const char* la = lds + buf * kStage;
       const char* lt = la + kW;
-      const int orow = 32 * wave + lr;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int g = 2 * q + lh;
-        const u32x4 av = *reinterpret_cast<const u32x4*>(la + tsw_g(orow, g) * 4);
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lt + swz(lr, g));
-        mfma_bf16(acc0, av, b0);
-        if (TWO) {
-          const u32x4 b1 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, g));
-          mfma_bf16(acc1, av, b1);
-        }
+        const u32x2 lo = lds_read_tr16(la + wsw(16 * q + tr_row, tr_chunk) + tr_byte);
+        const u32x2 hi = lds_read_tr16(la + wsw(16 * q + tr_row + 4, tr_chunk) + tr_byte);
+        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+        u32x4 bv[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) bv[b] = *reinterpret_cast<const u32x4*>(lt + swz(32 * b + lr, g));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) mfma_bf16(acc[b], av, bv[b]);
       }
     };
     // Pipeline as in the forward kernels: LDS buffer 0 holds stage s, R1
     // stage s + 1 and R0 stage s + 2 (indices past the end repeat the last).
-    auto run = [&](auto two_c) {
-      load(R0, 0);
-      load(R1, min(1, S - 1));
-      store(R0, 0);
-      load(R0, min(2, S - 1));
+    auto run = [&](auto nb_c) {
+      load(R0, 0, nb_c);
+      load(R1, min(1, S - 1), nb_c);
+      store(R0, 0, nb_c);
+      load(R0, min(2, S - 1), nb_c);
       lds_barrier();
       for (int s = 0; s + 1 < S; s += 2) {
-        compute(0, two_c);
-        store(R1, 1);
-        load(R1, min(s + 3, S - 1));
+        compute(0, nb_c);
+        store(R1, 1, nb_c);
+        load(R1, min(s + 3, S - 1), nb_c);
         lds_barrier();
-        compute(1, two_c);
-        store(R0, 0);
-        load(R0, min(s + 4, S - 1));
+        compute(1, nb_c);
+        store(R0, 0, nb_c);
+        load(R0, min(s + 4, S - 1), nb_c);
         lds_barrier();
       }
       if (S & 1) {
-        compute(0, two_c);
+        compute(0, nb_c);
         lds_barrier();
       }
     };
-    if (rows > 32)
-      run(std::true_type{});
+    if (rows > 64)
+      run(std::integral_constant<int, 4>{});
+    else if (rows > 32)
+      run(std::integral_constant<int, 2>{});
     else
-      run(std::false_type{});
+      run(std::integral_constant<int, 1>{});
 
     // acc[b][v]: output column 32*wave + 8*(v/4) + 4*lh + v%4, token 32*b + lr
     const int col = nt * 128 + 32 * wave + 4 * lh;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const f32x16& acc = b ? acc1 : acc0;
+    for (int b = 0; b < 4; ++b) {
       const int m = 32 * b + lr;
       if (m >= rows) continue;
       const int64_t row = row0 + m;
@@ -250,7 +272,7 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
           load4_bf16(hr + F + j, uv);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float dh2 = acc[4 * g4 + i];
+            const float dh2 = acc[b][4 * g4 + i];
             const float sg = sigmoid_f(gv[i]);
             const float sl = silu_f(gv[i]);
             dg[i] = dh2 * uv[i] * (sg * (1.0f + gv[i] * (1.0f - sg)));
@@ -265,8 +287,8 @@ __global__ __launch_bounds__(256) void k_gemm_dgrad(BwdArgs a) {
         float* o = reinterpret_cast<float*>(a.out) + row * N;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-          store4<float>(o + col + 8 * g4, acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2],
-                        acc[4 * g4 + 3]);
+          store4<float>(o + col + 8 * g4, acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2],
+                        acc[b][4 * g4 + 3]);
       }
     }
   }

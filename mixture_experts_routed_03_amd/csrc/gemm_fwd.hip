@@ -24,16 +24,20 @@
 //    16-byte LDS reads.  Two further stages are in flight in registers
 //    (ring of two), so ~48 KiB per workgroup is outstanding while a stage
 //    computes.
-//  * Workgroup tile: 128 weight rows (4 waves x 32) x 64 token rows; each
-//    wave holds two 32x32 fp32 accumulators (v_mfma_f32_32x32x16_bf16, or
-//    v_mfma_f32_32x32x2f32 for fp32 operands).  A tile with <= 32 rows skips
-//    the second accumulator.  Within a stage, half h of a lane's operands
-//    covers chunks [4h, 4h+4) of the row segment: a permutation of the
-//    contraction applied identically to both operands.
-//  * Persistent grid, XCD-aware: work item w is run by a workgroup of XCD
-//    (w / chunk), so one XCD's L2 holds an expert's token rows while its
-//    n-tiles stream by; items are expert-major, then n-tile, then m-tile, so
-//    m-tiles sharing a weight tile are adjacent.
+//  * Workgroup tile: 128 weight rows (4 waves x 32) x 64 token rows, or x 128
+//    token rows for an expert with more than 64 rows (its weight tiles are
+//    then streamed once per 128 rows instead of once per 64).  Each wave
+//    holds one 32x32 fp32 accumulator per 32-token block
+//    (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x2f32 for fp32 operands);
+//    loop copies for 1, 2 and 4 blocks skip the blocks past the tile's last
+//    row.  Within a stage, half h of a lane's operands covers chunks
+//    [4h, 4h+4) of the row segment: a permutation of the contraction applied
+//    identically to both operands.
+//  * Persistent grid, XCD-aware: each XCD runs a contiguous run of work
+//    items, split by token rows (xcd_first_tile), so one XCD's L2 holds an
+//    expert's token rows while its n-tiles stream by; items are expert-major,
+//    then n-tile, then m-tile, so m-tiles sharing a weight tile run side by
+//    side.
 #include <algorithm>
 
 #include <type_traits>
@@ -103,10 +107,10 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ mtoff, in
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
 
 template <typename T, int MODE>
-__global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
   constexpr int ES = sizeof(T);
   constexpr int kW = 128 * 128;          // weight stage: 128 rows x 128 B
-  constexpr int kA = kBM * 128;          // token stage: 64 rows x 128 B
+  constexpr int kA = kBMX * 128;         // token stage: up to 128 rows x 128 B
   constexpr int kStage = kW + kA;
   constexpr int kSteps = 128 / ES / 16;  // MFMA k-steps (16 values) per stage
   constexpr int kV = Mma<T>::kV;         // 16-byte chunks per 8-value operand
@@ -121,7 +125,9 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
 
   const RouteHdr* hdr = a.hdr;
   if (a.replay_only && !hdr->rec.replay) return;
-  const int n_items = hdr->n_mt * a.NT;
+  // a.mtoff is the m-tile prefix: experts with more than 64 rows are cut
+  // into 128-row tiles, the others into one 64-row tile.
+  const int n_items = a.mtoff[a.E] * a.NT;
   // W13 reads the caller's x rows through the permutation (the gather is part
   // of this loader); W2 reads packed h2 rows.
   const char* Abase = reinterpret_cast<const char*>(MODE == 0 ? a.x : a.A);
@@ -137,23 +143,23 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
-  const int chunk = (n_items + kXcds - 1) / kXcds;
+  const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
+  const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
   const int S = int(row_bytes / 128);
 
-  for (int it = slot; it < chunk; it += per) {
-    const int w = xcd * chunk + it;
-    if (w >= n_items) break;
+  for (int w = first + slot; w < last; w += per) {
     const int e = find_expert(a.mtoff, a.E, a.NT, w);
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;
     const int mt = u - nt * mt_e;
-    const int row0 = a.offsets[e] + mt * kBM;
-    const int rows = min(kBM, a.offsets[e + 1] - row0);
+    const int bm = gemm_tile_rows(a.offsets[e + 1] - a.offsets[e]);
+    const int row0 = a.offsets[e] + mt * bm;
+    const int rows = min(bm, a.offsets[e + 1] - row0);
 
-    // Global sources of this thread's four weight chunks and two token chunks.
-    // Tile rows past the expert's last row re-read that row: the loads are
-    // unconditional and the extra output columns are never stored.
+    // Global sources of this thread's four weight chunks and four token
+    // chunks.  Tile rows past the expert's last row re-read that row: the
+    // loads are unconditional and the extra output columns are never stored.
     const char* wsrc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -162,121 +168,123 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
                                : nt * 128 + rho;
       wsrc[j] = reinterpret_cast<const char*>(a.W) + (int64_t(e) * a.N + wr) * row_bytes + lc * 16;
     }
-    const char* tsrc[2];
+    const char* tsrc[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int r = row0 + min(lrow + 32 * j, rows - 1);
       const int64_t src = MODE == 0 ? a.sorted_route[r] / a.K : r;
       tsrc[j] = Abase + src * row_bytes + lc * 16;
     }
 
-    f32x16 acc0 = {}, acc1 = {};
-    u32x4 R0[6], R1[6];
-    auto load = [&](u32x4* R, int s) {
+    f32x16 acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
+    u32x4 R0[8], R1[8];
+    // NB (a compile-time 32-row block count per loop copy: 1, 2 or 4) is the
+    // number of token blocks loaded and multiplied.
+    auto load = [&](u32x4* R, int s, auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
       const int64_t off = int64_t(s) * 128;
 #pragma unroll
       for (int j = 0; j < 4; ++j)   // weights: non-temporal (streamed once per m-tile)
         R[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + off));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
+      for (int j = 0; j < NB; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
     };
-    auto store = [&](const u32x4* R, int buf) {
+    auto store = [&](const u32x4* R, int buf, auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
       char* base = lds + buf * kStage;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         *reinterpret_cast<u32x4*>(base + swz(lrow + 32 * j, lc)) = R[j];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NB; ++j)
         *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
     };
-    // TWO (a compile-time flag per loop copy): the tile has more than 32
-    // rows, so the second 32-token half is multiplied too.
-    auto compute = [&](int buf, auto two_c) {
-      constexpr bool TWO = decltype(two_c)::value;
+    auto compute = [&](int buf, auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
       const char* wl = lds + buf * kStage;
       const char* tl = wl + kW;
       const int wrow = 32 * wave + lr;
 #pragma unroll
       for (int q = 0; q < kSteps; ++q) {
-        u32x4 av[kV], b0[kV], b1[kV];
+        u32x4 av[kV], bv[NB][kV];
 #pragma unroll
         for (int v = 0; v < kV; ++v) {
           const int c = 4 * lh + q * kV + v;
           av[v] = *reinterpret_cast<const u32x4*>(wl + swz(wrow, c));
-          b0[v] = *reinterpret_cast<const u32x4*>(tl + swz(lr, c));
-          if (TWO) b1[v] = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, c));
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            bv[b][v] = *reinterpret_cast<const u32x4*>(tl + swz(32 * b + lr, c));
         }
-        Mma<T>::step(acc0, av, b0);
-        if (TWO) Mma<T>::step(acc1, av, b1);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Mma<T>::step(acc[b], av, bv[b]);
       }
     };
 
     // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
     // s + 1 and R0 stage s + 2 (indices past the end repeat the last stage).
-    auto run = [&](auto two_c) {
-      load(R0, 0);
-      load(R1, min(1, S - 1));
-      store(R0, 0);
-      load(R0, min(2, S - 1));
+    auto run = [&](auto nb_c) {
+      load(R0, 0, nb_c);
+      load(R1, min(1, S - 1), nb_c);
+      store(R0, 0, nb_c);
+      load(R0, min(2, S - 1), nb_c);
       lds_barrier();
       for (int s = 0; s + 1 < S; s += 2) {
-        compute(0, two_c);
-        store(R1, 1);
-        load(R1, min(s + 3, S - 1));
+        compute(0, nb_c);
+        store(R1, 1, nb_c);
+        load(R1, min(s + 3, S - 1), nb_c);
         lds_barrier();
-        compute(1, two_c);
-        store(R0, 0);
-        load(R0, min(s + 4, S - 1));
+        compute(1, nb_c);
+        store(R0, 0, nb_c);
+        load(R0, min(s + 4, S - 1), nb_c);
         lds_barrier();
       }
       if (S & 1) {
-        compute(0, two_c);
+        compute(0, nb_c);
         lds_barrier();
       }
     };
-    if (rows > 32)
-      run(std::true_type{});
+    if (rows > 64)
+      run(std::integral_constant<int, 4>{});
+    else if (rows > 32)
+      run(std::integral_constant<int, 2>{});
     else
-      run(std::false_type{});
+      run(std::integral_constant<int, 1>{});
 
     // ---------------------------------------------------------- epilogue
     // acc[b][v] is C[weight row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
     if (MODE == 0) {
+      // h1 store, then SwiGLU: up waves (2,3) hand their rounded values to
+      // gate waves (0,1) through LDS, one 32-row block at a time.
       const int F = a.F;
       const int ncol = (wave < 2 ? 0 : F) + nt * 64 + (wave & 1) * 32 + 4 * lh;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const f32x16& acc = b ? acc1 : acc0;
-        const int m = 32 * b + lr;
-        if (m < rows) {
-          T* o = out0 + int64_t(row0 + m) * (2 * F) + ncol;
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            store4<T>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
-        }
-      }
-      // SwiGLU: up waves (2,3) hand their rounded values to gate waves (0,1).
+      const int jcol = nt * 64 + (wave & 1) * 32 + 4 * lh;
+      const int nbk = (rows + 31) >> 5;
       float* xch = reinterpret_cast<float*>(lds);
-      if (wave >= 2) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          xch[(((wave - 2) * 2 + 0) * 16 + v) * 64 + lane] = Elem<T>::round(acc0[v]);
-          xch[(((wave - 2) * 2 + 1) * 16 + v) * 64 + lane] = Elem<T>::round(acc1[v]);
-        }
-      }
-      lds_barrier();
-      if (wave < 2) {
-        const int jcol = nt * 64 + wave * 32 + 4 * lh;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const f32x16& acc = b ? acc1 : acc0;
+      for (int b = 0; b < 4; ++b) {
+        if (b < nbk) {
           const int m = 32 * b + lr;
           if (m < rows) {
+            T* o = out0 + int64_t(row0 + m) * (2 * F) + ncol;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              store4<T>(o + 8 * g, acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2],
+                        acc[b][4 * g + 3]);
+          }
+          if (wave >= 2) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              xch[((wave - 2) * 16 + v) * 64 + lane] = Elem<T>::round(acc[b][v]);
+          }
+          lds_barrier();
+          if (wave < 2 && m < rows) {
             float h[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const float g = Elem<T>::round(acc[v]);
-              const float up = xch[((wave * 2 + b) * 16 + v) * 64 + lane];
+              const float g = Elem<T>::round(acc[b][v]);
+              const float up = xch[(wave * 16 + v) * 64 + lane];
               h[v] = silu_f(g) * up;
             }
             T* o = out1 + int64_t(row0 + m) * F + jcol;
@@ -284,14 +292,13 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
             for (int g = 0; g < 4; ++g)
               store4<T>(o + 8 * g, h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
           }
+          lds_barrier();
         }
       }
-      lds_barrier();
     } else {
       const int ncol = nt * 128 + wave * 32 + 4 * lh;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const f32x16& acc = b ? acc1 : acc0;
+      for (int b = 0; b < 4; ++b) {
         const int m = 32 * b + lr;
         if (m < rows) {
           const int64_t slotr = a.sorted_route[row0 + m];
@@ -300,13 +307,15 @@ __global__ __launch_bounds__(256) void k_gemm_fwd(FwdArgs a) {
             float* o = a.y32 + (slotr / a.K) * a.N + ncol;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-              fused_add4(o + 8 * g, sc, Elem<T>::round(acc[4 * g]), Elem<T>::round(acc[4 * g + 1]),
-                         Elem<T>::round(acc[4 * g + 2]), Elem<T>::round(acc[4 * g + 3]));
+              fused_add4(o + 8 * g, sc, Elem<T>::round(acc[b][4 * g]),
+                         Elem<T>::round(acc[b][4 * g + 1]), Elem<T>::round(acc[b][4 * g + 2]),
+                         Elem<T>::round(acc[b][4 * g + 3]));
           } else {
             T* o = out0 + slotr * a.N + ncol;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-              store4<T>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+              store4<T>(o + 8 * g, acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2],
+                        acc[b][4 * g + 3]);
           }
         }
       }

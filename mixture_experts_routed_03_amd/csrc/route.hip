@@ -43,34 +43,33 @@ __global__ __launch_bounds__(256) void k_route_hist(const int32_t* __restrict__ 
   if (threadIdx.x == 0) chunk_flags[c] = bad ? int32_t(MOE_STATUS_BAD_ID) : 0;
 }
 
-// Inclusive scan of three ints per thread over a 1024-thread block: a
-// shuffle scan inside each wave, then a scan of the 16 wave totals.
-__device__ void block_scan3(int& a, int& b, int& c, int* sh /* [3][16] */) {
+// Inclusive scan of N ints per thread over a 1024-thread block: a shuffle
+// scan inside each wave, then a scan of the 16 wave totals.
+template <int N>
+__device__ void block_scan(int* v /* [N] */, int* sh /* [N][16] */) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int ua = __shfl_up(a, off, 64), ub = __shfl_up(b, off, 64), uc = __shfl_up(c, off, 64);
+    int u[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) u[j] = __shfl_up(v[j], off, 64);
     if (lane >= off) {
-      a += ua;
-      b += ub;
-      c += uc;
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[j] += u[j];
     }
   }
   if (lane == 63) {
-    sh[wave] = a;
-    sh[16 + wave] = b;
-    sh[32 + wave] = c;
+#pragma unroll
+    for (int j = 0; j < N; ++j) sh[16 * j + wave] = v[j];
   }
   __syncthreads();
-  int pa = 0, pb = 0, pc = 0;
+  int p[N] = {};
   for (int w = 0; w < wave; ++w) {
-    pa += sh[w];
-    pb += sh[16 + w];
-    pc += sh[32 + w];
+#pragma unroll
+    for (int j = 0; j < N; ++j) p[j] += sh[16 * j + w];
   }
-  a += pa;
-  b += pb;
-  c += pc;
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] += p[j];
   __syncthreads();
 }
 
@@ -88,13 +87,14 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
                                                      int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ poffsets,
                                                      int32_t* __restrict__ mtoff,
+                                                     int32_t* __restrict__ gtoff,
                                                      RouteHdr* __restrict__ hdr) {
-  __shared__ int sh[48];
-  __shared__ int carry[3];
+  __shared__ int sh[64];
+  __shared__ int carry[4];
   __shared__ int red[2];
   const int tid = threadIdx.x;
   if (tid == 0) {
-    carry[0] = carry[1] = carry[2] = 0;
+    carry[0] = carry[1] = carry[2] = carry[3] = 0;
     red[0] = red[1] = 0;
   }
   __syncthreads();
@@ -114,15 +114,19 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     }
     const int sp = (s + kMxBlock - 1) / kMxBlock * kMxBlock;
     const int sm = (s + kBM - 1) / kBM;
+    const int sg = (s + gemm_tile_rows(s) - 1) / gemm_tile_rows(s);
     mx = max(mx, s);
-    int ic = s, ip = sp, im = sm;
-    block_scan3(ic, ip, im, sh);
-    const int oc = carry[0] + ic - s, op = carry[1] + ip - sp, om = carry[2] + im - sm;
+    int v[4] = {s, sp, sm, sg};
+    block_scan<4>(v, sh);
+    const int ic = v[0], ip = v[1], im = v[2], ig = v[3];
+    const int oc = carry[0] + ic - s, op = carry[1] + ip - sp, om = carry[2] + im - sm,
+              og = carry[3] + ig - sg;
     if (e < E) {
       counts[e] = s;
       offsets[e] = oc;
       poffsets[e] = op;
       mtoff[e] = om;
+      gtoff[e] = og;
       // chunk histograms -> row base of each (chunk, expert)
       int run = oc;
       for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
@@ -144,6 +148,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
       carry[0] += ic;
       carry[1] += ip;
       carry[2] += im;
+      carry[3] += ig;
     }
     __syncthreads();
   }
@@ -157,6 +162,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     offsets[E] = carry[0];
     poffsets[E] = carry[1];
     mtoff[E] = carry[2];
+    gtoff[E] = carry[3];
     hdr->T = T;
     hdr->R = carry[0];
     hdr->Rpad = carry[1];
@@ -284,6 +290,7 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
                      reinterpret_cast<int32_t*>(ws + L.offsets),
                      reinterpret_cast<int32_t*>(ws + L.poffsets),
                      reinterpret_cast<int32_t*>(ws + L.mtoff),
+                     reinterpret_cast<int32_t*>(ws + L.gtoff),
                      reinterpret_cast<RouteHdr*>(ws + L.hdr));
   if (nchunks > 0)
     hipLaunchKernelGGL(k_route_rank, dim3(nchunks), dim3(256), 0, s, ids, n, E, hist,
