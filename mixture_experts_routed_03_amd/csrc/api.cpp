@@ -639,7 +639,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   void* h2 = sc + p->sl.h2;
   // BwdArgs: hdr, offsets, mtoff, W, tok, grad, arows, out, out2, Kd, N, F, D, E, NT, a_ld, b_ld
   BwdArgs b{hdr, offsets, gtoff, w->w2, dh3, nullptr, nullptr, dh1, h2,
-            d.d, d.f, d.f, d.d, d.e, d.f / 128, 0, 0, mtoff};
+            d.d, d.f, d.f, d.d, d.e, (d.f + 255) / 256, 0, 0, mtoff};
   e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_dgrad(0, b, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw2{hdr, offsets, mtoff, nullptr, nullptr, dh3, h2, g->dw2, nullptr,
@@ -647,7 +647,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(dw_f32, 2, bw2, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs b13{hdr, offsets, gtoff, w->w13, dh1, nullptr, nullptr, dxr, nullptr,
-              2 * d.f, d.d, d.f, d.d, d.e, d.d / 128, 0, 0, mtoff};
+              2 * d.f, d.d, d.f, d.d, d.e, (d.d + 255) / 256, 0, 0, mtoff};
   e = timed(p, "w13_dgrad", s, [&] { return launch_dgrad(1, b13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   // dW13's A rows: a packed copy of the x rows (its loads then stream)

@@ -109,11 +109,11 @@ __device__ __forceinline__ int tsw_g(int o, int g) { return o * 32 + (((g ^ o ^ 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
 
 // ------------------------------------------------------------------ DGRAD
-// Weight stage (contraction rows k, 256-byte rows of 128 output columns):
-// the 16-byte chunks of row k are XOR-swizzled by 4 (k & 3), so both the
+// Weight stage (contraction rows k, 512-byte rows of 256 output columns): the
+// 16-byte chunks of row k are XOR-swizzled by 4 (k & 3), so both the
 // row-wise 16-byte stores and the transpose reads (8 rows x 4 chunks per
-// instruction) touch every bank equally.
-__device__ __forceinline__ int wsw(int k, int c) { return k * 256 + ((c ^ ((k & 3) << 2)) << 4); }
+// instruction) spread evenly over the banks.
+__device__ __forceinline__ int wsw(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 // ds_read_b64_tr_b16: in each 16-lane group, lane 4j + q addresses row j,
@@ -125,9 +125,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Eight waves: 256 output columns (32 per wave) x up to 128 token rows.  A
+// 256-column tile reads 512-byte weight row segments, which HBM serves
+// faster than 256-byte ones, and shares each token stage among eight waves.
 template <int KIND>
-__global__ __launch_bounds__(256, 2) void k_gemm_dgrad(BwdArgs a) {
-  constexpr int kW = 64 * 256;       // weight stage: 64 contraction rows x 128 columns
+__global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
+  constexpr int kW = 64 * 512;       // weight stage: 64 contraction rows x 256 columns
   constexpr int kT = kBMX * 128;     // token stage: up to 128 rows x 64 values
   constexpr int kStage = kW + kT;
   __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
@@ -136,10 +139,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dgrad(BwdArgs a) {
   const int wave = tid >> 6;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int c16 = tid & 15;   // weight loader: 16-byte chunk of a 256-byte row segment
-  const int kp = tid >> 4;    // weight loader: contraction rows kp + 16 i
+  const int c32 = tid & 31;   // weight loader: 16-byte chunk of a 512-byte row segment
+  const int kp = tid >> 5;    // weight loader: contraction rows kp + 16 i
   const int lc = tid & 7;     // token loader: 16-byte chunk of a 128-byte row segment
-  const int lrow = tid >> 3;  // token loader: tile row (+ 32 j)
+  const int lrow = tid >> 3;  // token loader: tile row (+ 64 j)
   // transpose reads of the weight operand: the 16-lane group (lane >> 4)
   // covers output columns 32 wave + 16 ((lane >> 4) & 1) .. + 15 and
   // contraction rows 8 lh .. 8 lh + 7 of each 16-row MFMA step
@@ -168,22 +171,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dgrad(BwdArgs a) {
     const int bm = gemm_tile_rows(a.offsets[e + 1] - a.offsets[e]);
     const int row0 = a.offsets[e] + mt * bm;
     const int rows = min(bm, a.offsets[e + 1] - row0);
-
+    // The last tile of an N that is an odd multiple of 128 has 128 columns:
+    // the loads of its upper half re-read the lower half, and waves 4..7
+    // multiply them but store nothing.  Every load stays unconditional, so
+    // the stage loop has no branches.
+    const int ncols = min(256, int(N) - nt * 256);
+    const int wcol = c32 * 8 < ncols ? c32 * 8 : c32 * 8 - 128;
     const uint16_t* wsrc = reinterpret_cast<const uint16_t*>(a.W) +
-                           (int64_t(e) * a.Kd + kp) * N + nt * 128 + c16 * 8;
+                           (int64_t(e) * a.Kd + kp) * N + nt * 256 + wcol;
     // Tile rows past the expert's last row re-read that row (outputs not stored).
-    const char* tsrc[4];
+    const char* tsrc[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       tsrc[j] = reinterpret_cast<const char*>(a.tok) +
-                int64_t(row0 + min(lrow + 32 * j, rows - 1)) * a.Kd * 2 + lc * 16;
+                int64_t(row0 + min(lrow + 64 * j, rows - 1)) * a.Kd * 2 + lc * 16;
 
     f32x16 acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
-    u32x4 R0[8], R1[8];
-    // NB: 32-token blocks loaded and multiplied (1, 2 or 4; one loop copy
-    // each, so no accumulator depends on a branch inside the stage loop)
+    u32x4 R0[6], R1[6];
+    // NB: 32-token blocks multiplied (1, 2 or 4; one loop copy each, so no
+    // accumulator depends on a branch inside the stage loop); the token stage
+    // holds 64 rows per pass of the 512 threads (rows past the tile repeat its
+    // last row).
     auto load = [&](u32x4* R, int s, auto nb_c) {
       constexpr int NB = decltype(nb_c)::value;
       const uint16_t* p = wsrc + int64_t(s) * 64 * N;
@@ -193,17 +203,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dgrad(BwdArgs a) {
       for (int i = 0; i < 4; ++i)
         R[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 16 * i * N));
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < (NB + 3) / 4 + (NB == 4); ++j)
         R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
     };
     auto store = [&](const u32x4* R, int buf, auto nb_c) {
       constexpr int NB = decltype(nb_c)::value;
       char* la = lds + buf * kStage;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(la + wsw(kp + 16 * i, c16)) = R[i];
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(la + wsw(kp + 16 * i, c32)) = R[i];
       char* lt = la + kW;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
+      for (int j = 0; j < (NB + 3) / 4 + (NB == 4); ++j)
+        *reinterpret_cast<u32x4*>(lt + swz(lrow + 64 * j, lc)) = R[4 + j];
     };
     auto compute = [&](int buf, auto nb_c) {
       constexpr int NB = decltype(nb_c)::value;
@@ -251,9 +262,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dgrad(BwdArgs a) {
       run(std::integral_constant<int, 2>{});
     else
       run(std::integral_constant<int, 1>{});
+    if (32 * wave >= ncols) continue;
 
     // acc[b][v]: output column 32*wave + 8*(v/4) + 4*lh + v%4, token 32*b + lr
-    const int col = nt * 128 + 32 * wave + 4 * lh;
+    const int col = nt * 256 + 32 * wave + 4 * lh;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int m = 32 * b + lr;
@@ -460,11 +472,11 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
 // ------------------------------------------------------------------ launchers
 // Resident workgroups per CU of one kernel (queried once per kernel).
 template <int ID, typename K>
-static int occupancy(K kernel) {
+static int occupancy(K kernel, int threads = 256) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0)
       n = 1;
     per_cu = n;
   }
@@ -481,11 +493,11 @@ static unsigned persistent_grid(int per_cu, int64_t items, int cus) {
 hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hipStream_t s) {
   if (mt_max == 0) return hipSuccess;
   if (kind == 0) {
-    const unsigned g = persistent_grid(occupancy<0>(k_gemm_dgrad<0>), mt_max * a.NT, cus);
-    hipLaunchKernelGGL(k_gemm_dgrad<0>, dim3(g), dim3(256), 0, s, a);
+    const unsigned g = persistent_grid(occupancy<0>(k_gemm_dgrad<0>, 512), mt_max * a.NT, cus);
+    hipLaunchKernelGGL(k_gemm_dgrad<0>, dim3(g), dim3(512), 0, s, a);
   } else {
-    const unsigned g = persistent_grid(occupancy<1>(k_gemm_dgrad<1>), mt_max * a.NT, cus);
-    hipLaunchKernelGGL(k_gemm_dgrad<1>, dim3(g), dim3(256), 0, s, a);
+    const unsigned g = persistent_grid(occupancy<1>(k_gemm_dgrad<1>, 512), mt_max * a.NT, cus);
+    hipLaunchKernelGGL(k_gemm_dgrad<1>, dim3(g), dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
