@@ -148,7 +148,6 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
   const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
-  const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);  // FPROP/DGRAD m-tiles
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const char* tag = replay_only ? "replay_quant_x" : "quant_x";
   // x rows are read through the permutation (the gather happens in the loaders)
@@ -195,7 +194,6 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
   const int32_t* poffsets = at<int32_t>(ws, p->rl.poffsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
-  const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);  // FPROP/DGRAD m-tiles
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const int32_t* route_to_row = at<int32_t>(ws, p->rl.route_to_row);
   const int dw_f32 = d.dw_dtype == MOE_DTYPE_F32;
@@ -215,8 +213,9 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs dg2{hdr, offsets, poffsets, mtoff, sorted_route, u8(L.qdh3), u8(L.sdh3),
              reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
-             nullptr, nullptr, sc + L.dh1, nullptr, d.d, d.f, d.f, d.f / 128, d.e, 0, 0, -1, 0,
-             int(p->R_max)};
+             nullptr, nullptr, sc + L.dh1, nullptr, d.d, d.f, d.f, (d.f + 255) / 256, d.e, 0, 0,
+             -1, 0, int(p->R_max)};
+  dg2.stoff = mtoff;
   e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_mx_dgrad(0, dg2, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs wg2{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
@@ -232,8 +231,9 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs dg13{hdr, offsets, poffsets, mtoff, sorted_route, u8(L.qdh1), u8(L.sdh1),
               reinterpret_cast<const uint8_t*>(w->q13), reinterpret_cast<const uint8_t*>(w->s13),
-              nullptr, nullptr, sc + L.dxr, nullptr, 2 * d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
-              int(p->R_max)};
+              nullptr, nullptr, sc + L.dxr, nullptr, 2 * d.f, d.d, d.f, (d.d + 255) / 256, d.e, 0, 0,
+              -1, 0, int(p->R_max)};
+  dg13.stoff = mtoff;
   e = timed(p, "w13_dgrad", s, [&] { return launch_mx_dgrad(1, dg13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs wg13{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,

@@ -142,6 +142,7 @@ struct MxArgs {
   const float* scores;  // W2 FUSED combine (see FwdArgs)
   float* y32;
   int K;
+  const int32_t* stoff;  // DGRAD: 64-row stage prefix (XCD work split); mtoff = the m-tile prefix
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:

@@ -30,6 +30,7 @@
 // read ds_read_b64_tr_b8, so one copy of the E4M3 weights serves forward and
 // backward with no register transpose.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -308,43 +309,53 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
       (__attribute__((address_space(3))) i32x2*)((__attribute__((address_space(3))) char*)p));
 }
 
+// Weight stage of the DGRAD kernel: 128 contraction rows of 256 E4M3
+// columns; the 16-byte chunks of row r are XOR-swizzled by 2 (r & 7), so the
+// row-wise 16-byte stores and the transpose reads (8 + 8 rows x 2 chunks per
+// instruction) both spread evenly over the banks.
+__device__ __forceinline__ int wsw8(int r, int c) { return r * 256 + ((c ^ ((r & 7) << 1)) << 4); }
+
+// Eight waves: 256 output columns (32 per wave) x up to 64 token rows.
+// 256-byte weight row segments stream faster from HBM than 128-byte ones.
+// (A 128-row variant, four accumulators per wave, does not fit the 256
+// registers of two waves per SIMD without spilling.)
 template <int KIND>
-__global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
-  constexpr int kW = 128 * 128;      // weight stage: 128 contraction rows x 128 columns
-  constexpr int kT = kBM * 128;      // token stage
-  constexpr int kSc = kBM * 4;
-  constexpr int kStage = kW + kT + kSc + 16;   // + the weight scale dword of each wave
+__global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
+  constexpr int kW = 128 * 256;      // weight stage: 128 contraction rows x 256 columns
+  constexpr int kT = kBM * 128;      // token stage: up to 64 rows x 128 values
+  constexpr int kSc = kBM * 4;       // token exponents of the stage
+  constexpr int kStage = kW + kT + kSc + 32;   // + weight exponents: 8 column blocks x 4 k blocks
   __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int c16 = tid & 7;    // weight loader: 16-column chunk of a 128-byte row segment
-  const int kq = tid >> 3;    // weight loader: rows 4kq .. 4kq+3 of the stage
+  const int c16 = tid & 15;   // weight loader: 16-column chunk of a 256-byte row segment
+  const int kq = tid >> 4;    // weight loader: rows 4kq .. 4kq+3 of the stage
   // transpose reads of the weight operand: 16-lane group G covers columns
   // 32*wave + 16*(G & 1) .. + 15 and contraction half G >> 1 (= lh)
   const int tr_chunk = 2 * wave + ((lane >> 4) & 1);
   const int tr_row = (lane & 15) >> 1;
   const int tr_byte = 8 * (lane & 1);
   const int lc = tid & 7;
-  const int lrow = tid >> 3;
+  const int lrow = tid >> 3;  // token loader: tile row
 
   const RouteHdr* hdr = a.hdr;
-  const int n_items = hdr->n_mt * a.NT;
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
-  const int chunk = (n_items + kXcds - 1) / kXcds;
+  // 64-row m-tiles (a.mtoff = a.stoff); the XCDs split the items by token rows
+  const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
+  const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
   const int Kd = a.Kd;
   const int KB = Kd / 32;
   const int S = Kd / 128;
   const int64_t N = a.N;
+  const int NB32 = int(N / 32);
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
-  for (int it = slot; it < chunk; it += per) {
-    const int w = xcd * chunk + it;
-    if (w >= n_items) break;
+  for (int w = first + slot; w < last; w += per) {
     const int e = find_expert_m(a.mtoff, a.E, a.NT, w);
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
@@ -352,53 +363,59 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
     const int mt = u - nt * mt_e;
     const int row0 = a.offsets[e] + mt * kBM;
     const int rows = min(kBM, a.offsets[e + 1] - row0);
-
-    const uint8_t* wsrc = a.qw + (int64_t(e) * Kd + 4 * kq) * N + nt * 128 + c16 * 16;
-    // Weight scales of the stage: 4 column blocks (one per wave) x 4 blocks
-    // along k.  Thread t loads the byte of column block (t >> 2) & 3 and k
-    // block t & 3 (one byte each, no register assembly); threads 0..15 put
-    // them in LDS, so wave w reads its four as one dword.
-    const uint8_t* wsc_src =
-        a.sw + int64_t(e) * KB * (N / 32) + (tid & 3) * (N / 32) + nt * 4 + ((tid >> 2) & 3);
+    // The last tile of an N that is an odd multiple of 128 has 128 columns:
+    // its upper half re-reads the lower half, and waves 4..7 multiply it but
+    // store nothing (every load stays unconditional).
+    const int ncols = min(256, int(N) - nt * 256);
+    const int wcol = c16 * 16 < ncols ? c16 * 16 : c16 * 16 - 128;
+    const uint8_t* wsrc = a.qw + (int64_t(e) * Kd + 4 * kq) * N + nt * 256 + wcol;
+    // Weight exponents of the stage: 8 column blocks (one per wave) x 4
+    // blocks along k.  Thread t loads the byte of column block (t >> 2) & 7
+    // and k block t & 3; threads 0..31 put them in LDS, so wave w reads its
+    // four as one dword.
+    const int cb = min(nt * 8 + ((tid >> 2) & 7), NB32 - 1);
+    const uint8_t* wsc_src = a.sw + int64_t(e) * KB * NB32 + (tid & 3) * NB32 + cb;
     // Tile rows past the expert's last row re-read that row (outputs not stored).
-    const uint8_t* tsrc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      tsrc[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kd + lc * 16;
+    const uint8_t* tsrc = a.qa + int64_t(row0 + min(lrow, rows - 1)) * Kd + lc * 16;
     // token exponents are grouped by stage: dword (s, row) at (s * sa_rows + row) * 4
-    const uint32_t* tsc_src = reinterpret_cast<const uint32_t*>(a.sa) + row0 + min(tid & 63, rows - 1);
+    const uint32_t* tsc_src =
+        reinterpret_cast<const uint32_t*>(a.sa) + row0 + min(tid & (kBM - 1), rows - 1);
 
-    f32x16 acc0 = {}, acc1 = {};
-    u32x4 R0[6], R1[6];
+    f32x16 acc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[b] = f32x16{};
+    u32x4 R0[5], R1[5];
     uint32_t S0[2], S1[2];
-    auto load = [&](u32x4* R, uint32_t* Sc, int s) {
+    // NB: 32-token blocks multiplied (1 or 2; one loop copy each); the 512
+    // threads load all 64 rows of the token stage (rows past the tile repeat
+    // its last row).
+    auto load = [&](u32x4* R, uint32_t* Sc, int s, auto) {
       const uint8_t* p = wsrc + int64_t(s) * 128 * N;
 #pragma unroll
       for (int i = 0; i < 4; ++i)   // weights: non-temporal (streamed once per m-tile)
         R[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * N));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
-      Sc[0] = wsc_src[int64_t(4 * s) * (N / 32)];
+      R[4] = *reinterpret_cast<const u32x4*>(tsrc + int64_t(s) * 128);
+      Sc[0] = wsc_src[int64_t(4 * s) * NB32];
       Sc[1] = tsc_src[int64_t(s) * a.sa_rows];
     };
-    auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
+    auto store = [&](const u32x4* R, const uint32_t* Sc, int buf, auto) {
       char* lw = lds + buf * kStage;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(lw + swz(4 * kq + i, c16)) = R[i];
-      char* lt = lds + buf * kStage + kW;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lt + swz(lrow + 32 * j, lc)) = R[4 + j];
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(lw + wsw8(4 * kq + i, c16)) = R[i];
+      char* lt = lw + kW;
+      *reinterpret_cast<u32x4*>(lt + swz(lrow, lc)) = R[4];
       if (tid < kBM) reinterpret_cast<uint32_t*>(lt + kT)[tid] = Sc[1];
-      if (tid < 16) reinterpret_cast<uint8_t*>(lt + kT + kSc)[tid] = uint8_t(Sc[0]);
+      if (tid < 32) reinterpret_cast<uint8_t*>(lt + kT + kSc)[tid] = uint8_t(Sc[0]);
     };
-    auto compute = [&](int buf) {
+    auto compute = [&](int buf, auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
       const char* la = lds + buf * kStage;
       const char* lt = la + kW;
       const uint32_t* tsc = reinterpret_cast<const uint32_t*>(lt + kT);
-      const uint32_t ts0 = tsc[lr];
-      const uint32_t ts1 = tsc[32 + lr];
-      const uint32_t wsc = tsc[kBM + wave];
+      uint32_t ts[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ts[b] = tsc[32 * b + lr];
+      const uint32_t wsc = reinterpret_cast<const uint32_t*>(lt + kT + kSc)[wave];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int ga = 4 * q + lh, gb = 4 * q + 2 + lh;
@@ -409,47 +426,53 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int row = 16 * (p < 2 ? ga : gb) + 8 * (p & 1) + tr_row;
-          pc[p] = lds_read_tr8(la + swz(row, tr_chunk) + tr_byte);
+          pc[p] = lds_read_tr8(la + wsw8(row, tr_chunk) + tr_byte);
         }
         const u32x4 a0 = {uint32_t(pc[0][0]), uint32_t(pc[0][1]), uint32_t(pc[1][0]),
                           uint32_t(pc[1][1])};
         const u32x4 a1 = {uint32_t(pc[2][0]), uint32_t(pc[2][1]), uint32_t(pc[3][0]),
                           uint32_t(pc[3][1])};
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lt + swz(lr, ga));
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(lt + swz(lr, gb));
-        const u32x4 d0 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, ga));
-        const u32x4 d1 = *reinterpret_cast<const u32x4*>(lt + swz(32 + lr, gb));
         const int sa = byte_of(wsc, blk);
-        mfma_mx(acc0, a0, a1, b0, b1, sa, byte_of(ts0, blk));
-        mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const u32x4 b0 = *reinterpret_cast<const u32x4*>(lt + swz(32 * b + lr, ga));
+          const u32x4 b1 = *reinterpret_cast<const u32x4*>(lt + swz(32 * b + lr, gb));
+          mfma_mx(acc[b], a0, a1, b0, b1, sa, byte_of(ts[b], blk));
+        }
       }
     };
 
     // Same pipeline as the forward kernel.
-    load(R0, S0, 0);
-    load(R1, S1, min(1, S - 1));
-    store(R0, S0, 0);
-    load(R0, S0, min(2, S - 1));
-    lds_barrier();
-    for (int s = 0; s + 1 < S; s += 2) {
-      compute(0);
-      store(R1, S1, 1);
-      load(R1, S1, min(s + 3, S - 1));
+    auto run = [&](auto nb_c) {
+      load(R0, S0, 0, nb_c);
+      load(R1, S1, min(1, S - 1), nb_c);
+      store(R0, S0, 0, nb_c);
+      load(R0, S0, min(2, S - 1), nb_c);
       lds_barrier();
-      compute(1);
-      store(R0, S0, 0);
-      load(R0, S0, min(s + 4, S - 1));
-      lds_barrier();
-    }
-    if (S & 1) {
-      compute(0);
-      lds_barrier();
-    }
+      for (int s = 0; s + 1 < S; s += 2) {
+        compute(0, nb_c);
+        store(R1, S1, 1, nb_c);
+        load(R1, S1, min(s + 3, S - 1), nb_c);
+        lds_barrier();
+        compute(1, nb_c);
+        store(R0, S0, 0, nb_c);
+        load(R0, S0, min(s + 4, S - 1), nb_c);
+        lds_barrier();
+      }
+      if (S & 1) {
+        compute(0, nb_c);
+        lds_barrier();
+      }
+    };
+    if (rows > 32)
+      run(std::integral_constant<int, 2>{});
+    else
+      run(std::integral_constant<int, 1>{});
+    if (32 * wave >= ncols) continue;
 
-    const int col = nt * 128 + 32 * wave + 4 * lh;
+    const int col = nt * 256 + 32 * wave + 4 * lh;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const f32x16& acc = b ? acc1 : acc0;
       const int m = 32 * b + lr;
       if (m >= rows) continue;
       const int64_t row = row0 + m;
@@ -465,7 +488,7 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
           load4_bf16(hr + F + j, uv);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float dh2 = acc[4 * g4 + i];
+            const float dh2 = acc[b][4 * g4 + i];
             const float sg = sigmoid_f(gv[i]);
             dg[i] = dh2 * uv[i] * (sg * (1.0f + gv[i] * (1.0f - sg)));
             du[i] = dh2 * silu_f(gv[i]);
@@ -477,8 +500,8 @@ __global__ __launch_bounds__(256) void k_mx_dgrad(MxArgs a) {
         float* o = reinterpret_cast<float*>(a.out0) + row * N;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-          store4<float>(o + col + 8 * g4, acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2],
-                        acc[4 * g4 + 3]);
+          store4<float>(o + col + 8 * g4, acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2],
+                        acc[b][4 * g4 + 3]);
       }
     }
   }
@@ -658,11 +681,11 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
 
 // ------------------------------------------------------------------ launchers
 template <int ID, typename K>
-static int occupancy_m(K kernel) {
+static int occupancy_m(K kernel, int threads = 256) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0)
       n = 1;
     per_cu = n;
   }
@@ -693,12 +716,12 @@ hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, h
   if (mt_max == 0) return hipSuccess;
   if (kind == 0) {
     hipLaunchKernelGGL(k_mx_dgrad<0>,
-                       dim3(grid_m(occupancy_m<2>(k_mx_dgrad<0>), mt_max * a.NT, cus)), dim3(256),
-                       0, s, a);
+                       dim3(grid_m(occupancy_m<2>(k_mx_dgrad<0>, 512), mt_max * a.NT, cus)),
+                       dim3(512), 0, s, a);
   } else {
     hipLaunchKernelGGL(k_mx_dgrad<1>,
-                       dim3(grid_m(occupancy_m<3>(k_mx_dgrad<1>), mt_max * a.NT, cus)), dim3(256),
-                       0, s, a);
+                       dim3(grid_m(occupancy_m<3>(k_mx_dgrad<1>, 512), mt_max * a.NT, cus)),
+                       dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
