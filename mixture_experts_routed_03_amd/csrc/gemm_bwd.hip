@@ -21,20 +21,22 @@
 //                    dW13 = dH1^T X (a = D, b = 2F).
 //
 // MI355X design
-//  * Every global load is coalesced: sixteen consecutive lanes read one
-//    256-byte row segment.  Operands whose rows run along the contraction
-//    (DGRAD weights, both WGRAD operands) are transposed on their way into
-//    LDS: a thread holds the same 16-byte column chunk of two consecutive rows,
-//    interleaves them into eight (k, k+1) dwords and writes one dword per
-//    output column.  LDS rows hold 64 contraction values (32 dwords); their
-//    4-dword groups are XOR-swizzled with (o ^ o>>3) & 7 of the row o, which
-//    keeps these writes at most 2-way and the 16-byte MFMA operand reads
-//    conflict-free.
-//  * DGRAD: 128 output columns x 64 token rows per workgroup, 64 contraction
-//    values per stage, two more stages in flight in registers.
-//  * WGRAD: 128 x 128 outputs of one expert per work item, 64 token rows per
-//    stage; the next item's first stage is loaded while the current tile is
-//    staged through LDS and stored as whole 256/512-byte row segments.  Items
+//  * Every global load is coalesced: consecutive lanes read whole 128- to
+//    512-byte row segments.  Operands whose rows run along the contraction
+//    (DGRAD weights, both WGRAD operands) are stored into LDS as they lie in
+//    memory (16-byte stores, chunks XOR-swizzled per row) and read in MFMA
+//    operand layout with the gfx950 transpose read ds_read_b64_tr_b16: no
+//    register transpose.
+//  * DGRAD: eight waves, 256 output columns x up to 128 token rows per
+//    workgroup (128-row tiles for experts with more than 64 rows), 64
+//    contraction values per stage, two more stages in flight in registers.
+//    256 columns make the weight reads 512-byte row segments, which HBM
+//    serves faster than 256-byte ones.
+//  * WGRAD: eight waves, 128 dW rows x 256 dW columns of one expert per
+//    work item, 64 token rows per stage; the next item's first stage is
+//    loaded while the current tile is staged through LDS and stored as whole
+//    512-byte (bf16) or 1 KB (fp32) row segments, the write shape HBM takes
+//    fastest.  Items
 //    run expert-major with the output column tile fastest, so the workgroups
 //    of one XCD write long contiguous runs of dW rows.
 //  * Persistent, XCD-aware grids as in the forward kernels.
@@ -51,15 +53,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void mfma_bf16(f32x16& acc, u32x4 a, u32x4 b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-}
-
-// Interleave the bf16 halves of two rows: out[q] = (lo.half[q], hi.half[q]).
-__device__ __forceinline__ void interleave8(const u32x4& lo, const u32x4& hi, uint32_t* out) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = (lo[i] & 0xffffu) | (hi[i] << 16);
-    out[2 * i + 1] = (lo[i] >> 16) | (hi[i] & 0xffff0000u);
-  }
 }
 
 template <typename T>
@@ -97,13 +90,6 @@ __device__ __forceinline__ int find_expert_b(const int32_t* __restrict__ mtoff, 
   }
   return lo;
 }
-
-// Transposed tile: dword of contraction pair kpair in LDS row o, and the
-// first dword of 4-dword group g of row o.
-__device__ __forceinline__ int tsw(int o, int kpair) {
-  return o * 32 + ((((kpair >> 2) ^ o ^ (o >> 3)) & 7) << 2) + (kpair & 3);
-}
-__device__ __forceinline__ int tsw_g(int o, int g) { return o * 32 + (((g ^ o ^ (o >> 3)) & 7) << 2); }
 
 // Row tile (contraction contiguous): 128-byte rows, 16-byte chunks swizzled.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
@@ -308,27 +294,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
 
 // ------------------------------------------------------------------ WGRAD
 // TAG only separates the two launches in profiles (2: dW2, 13: dW13).
+// Work item: 128 dW rows x 256 dW columns of one expert on eight waves,
+// written as 512-byte (bf16) or 1 KB (fp32) row segments, which HBM takes
+// faster than 256-byte ones; per token row the item re-reads less operand
+// data than a 128 x 128 or 64 x 256 tile.  Wave w owns dW rows
+// 64 (w >> 2) .. + 63 and columns 64 (w & 3) .. + 63 of the tile: 2 x 2
+// accumulators of 32 x 32.  Both operand stages hold 64 token rows as they
+// lie in memory (A: 256 columns, 512-byte rows; B: 128 columns, 256-byte
+// rows; chunks XOR-swizzled by 4 (m & 3)) and are read with transpose reads.
+__device__ __forceinline__ int bsw(int m, int c) { return m * 256 + ((c ^ ((m & 3) << 2)) << 4); }
+
 template <typename TW, int TAG>
-__global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
-  constexpr int kOp = 128 * 32 * 4;                    // one transposed operand stage
-  constexpr int kRowB = 128 * int(sizeof(TW)) + 16;    // padded output-staging row
-  constexpr int kHalves = sizeof(TW) == 4 ? 2 : 1;     // fp32 tiles are staged in two halves
-  constexpr int kRowsPerPass = 128 / kHalves;
-  constexpr int kOut = kRowsPerPass * kRowB;
-  __shared__ __attribute__((aligned(16))) char lds[2 * kOp + kOut];
+__global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
+  constexpr int kA = 64 * 512;                         // A stage: 64 token rows x 256 columns
+  constexpr int kB = 64 * 256;                         // B stage: 64 token rows x 128 columns
+  constexpr int kRowB = 256 * int(sizeof(TW)) + 16;    // padded output-staging row
+  constexpr int kRowsPerPass = sizeof(TW) == 4 ? 32 : 64;
+  constexpr int kPasses = 128 / kRowsPerPass;
+  static_assert(kRowsPerPass * kRowB <= kA + kB, "output staging reuses the operand stages");
+  __shared__ __attribute__((aligned(16))) char lds[kA + kB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wa = wave & 3;    // 64-column block of the tile
+  const int wb = wave >> 2;   // 64-row block of the tile
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int c16 = tid & 15;   // loader: 8-column chunk of a 256-byte row segment
-  const int kp = tid >> 4;    // loader: row pairs kp and kp + 16 of a 64-row stage
+  const int c32 = tid & 31;   // A loader: 16-byte chunk of a 512-byte row segment
+  const int ar = tid >> 5;    // A loader: token rows ar + 16 i
+  const int c16 = tid & 15;   // B loader: 16-byte chunk of a 256-byte row segment
+  const int br = tid >> 4;    // B loader: token rows br + 32 j
+  // transpose reads: lane 4j + q of each 16-lane group addresses row j,
+  // columns 4q .. 4q + 3 of its group's 16 columns (16 (lane >> 4 & 1) on)
+  const int tr_row = 8 * lh + ((lane & 15) >> 2);
+  const int tr_c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_byte = 8 * (lane & 1);
 
-  const RouteHdr* hdr = a.hdr;
   const int a_ld = a.a_ld, b_ld = a.b_ld;
-  const int NA = a_ld / 128, NB = b_ld / 128;
+  const int NA = (a_ld + 255) / 256, NB = b_ld / 128;
   const int per_e = NA * NB;
-  const int n_items = a.E * per_e;
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
   const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(a.grad);
 
   struct Item {
-    int e, ta, tb, r0, Me, S;
+    int e, ta, tb, r0, Me, S, ncols;
   };
   // Work items of this workgroup are w = first + slot + i * per below last;
   // (e, tb, ta) advance by carries instead of a division per item.
@@ -360,6 +364,7 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
     t.r0 = a.offsets[ie];
     t.Me = a.offsets[ie + 1] - t.r0;
     t.S = (t.Me + 63) / 64;
+    t.ncols = min(256, a_ld - ita * 256);
     // advance to the next item of this workgroup
     wcur += per;
     ita += per;
@@ -372,34 +377,32 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
     }
   };
 
-  u32x4 R[8];  // one stage: rows 2kp, 2kp+1, 32+2kp, 33+2kp of A then B
+  // One stage in registers.  Token rows past the expert's last row are not
+  // read: their registers hold zeros, so they add nothing.  Columns past the
+  // end of a 128-column half tile re-read the first half.
+  u32x4 RA[4], RB[2];
   auto load = [&](const Item& t, int s) {
+    const int acol = t.ta * 256 + (c32 * 8 < t.ncols ? c32 * 8 : c32 * 8 - 128);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int m = s * 64 + 2 * kp + (h & 1) + (h >> 1) * 32;
-      if (m < t.Me) {
-        const int64_t row = t.r0 + m;
-        R[h] = *reinterpret_cast<const u32x4*>(asrc + row * a_ld + t.ta * 128 + c16 * 8);
-        R[4 + h] = *reinterpret_cast<const u32x4*>(bsrc + row * b_ld + t.tb * 128 + c16 * 8);
-      } else {
-        R[h] = u32x4{0u, 0u, 0u, 0u};
-        R[4 + h] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int m = s * 64 + ar + 16 * i;
+      RA[i] = u32x4{0u, 0u, 0u, 0u};
+      if (m < t.Me) RA[i] = *reinterpret_cast<const u32x4*>(asrc + int64_t(t.r0 + m) * a_ld + acol);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = s * 64 + br + 32 * j;
+      RB[j] = u32x4{0u, 0u, 0u, 0u};
+      if (m < t.Me)
+        RB[j] = *reinterpret_cast<const u32x4*>(bsrc + int64_t(t.r0 + m) * b_ld + t.tb * 128 +
+                                                c16 * 8);
     }
   };
   auto store = [&]() {
-    uint32_t* la = reinterpret_cast<uint32_t*>(lds);
-    uint32_t* lb = la + kOp / 4;
-    uint32_t d[8];
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      interleave8(R[2 * pp], R[2 * pp + 1], d);
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(lds + wsw(ar + 16 * i, c32)) = RA[i];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) la[tsw(c16 * 8 + q, kp + 16 * pp)] = d[q];
-      interleave8(R[4 + 2 * pp], R[5 + 2 * pp], d);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) lb[tsw(c16 * 8 + q, kp + 16 * pp)] = d[q];
-    }
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lds + kA + bsw(br + 32 * j, c16)) = RB[j];
   };
 
   Item cur, nxt;
@@ -407,9 +410,9 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
   if (cur.e >= 0 && cur.S > 0) load(cur, 0);
   while (cur.e >= 0) {
     fill(nxt);
-    f32x16 acc[4];
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    for (int i = 0; i < 4; ++i) acc[i >> 1][i & 1] = f32x16{};
     for (int s = 0; s < cur.S; ++s) {
       store();
       lds_barrier();
@@ -417,51 +420,69 @@ __global__ __launch_bounds__(256) void k_gemm_wgrad(BwdArgs a) {
         load(cur, s + 1);
       else if (nxt.e >= 0 && nxt.S > 0)
         load(nxt, 0);
-      const char* la = lds;
-      const char* lb = lds + kOp;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int g = 2 * q + lh;
-        const u32x4 av = *reinterpret_cast<const u32x4*>(la + tsw_g(32 * wave + lr, g) * 4);
+        u32x4 av[2], bv[2];
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const u32x4 bv = *reinterpret_cast<const u32x4*>(lb + tsw_g(32 * bb + lr, g) * 4);
-          mfma_bf16(acc[bb], av, bv);
+        for (int aa = 0; aa < 2; ++aa) {
+          const int ch = 8 * wa + 4 * aa + tr_c;
+          const u32x2 lo = lds_read_tr16(lds + wsw(16 * q + tr_row, ch) + tr_byte);
+          const u32x2 hi = lds_read_tr16(lds + wsw(16 * q + tr_row + 4, ch) + tr_byte);
+          av[aa] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int ch = 8 * wb + 4 * bb + tr_c;
+          const u32x2 lo = lds_read_tr16(lds + kA + bsw(16 * q + tr_row, ch) + tr_byte);
+          const u32x2 hi = lds_read_tr16(lds + kA + bsw(16 * q + tr_row + 4, ch) + tr_byte);
+          bv[bb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) mfma_bf16(acc[bb][aa], av[aa], bv[bb]);
       }
       lds_barrier();
     }
     if (cur.S == 0 && nxt.e >= 0 && nxt.S > 0) load(nxt, 0);
 
-    // acc[bb][v] = dW[b = tb*128 + 32*bb + lr][a = ta*128 + 32*wave + 8*(v/4) + 4*lh + v%4],
-    // staged through LDS and stored as whole row segments.
+    // acc[bb][aa][v] = dW[b = tb*128 + 64*wb + 32*bb + lr]
+    //                    [a = ta*256 + 64*wa + 32*aa + 8*(v/4) + 4*lh + v%4],
+    // staged through LDS (over the operand stages) in passes of
+    // kRowsPerPass rows and stored as whole row segments.
     TW* o = reinterpret_cast<TW*>(a.out) + (int64_t(cur.e) * b_ld + int64_t(cur.tb) * 128) * a_ld +
-            cur.ta * 128;
-    char* stg = lds + 2 * kOp;
+            cur.ta * 256;
 #pragma unroll
-    for (int h = 0; h < kHalves; ++h) {
+    for (int h = 0; h < kPasses; ++h) {
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        if (bb / (4 / kHalves) != h) continue;
-        const int rl = 32 * bb + lr - h * kRowsPerPass;
-        TW* rowp = reinterpret_cast<TW*>(stg + rl * kRowB) + 32 * wave + 4 * lh;
+      for (int bb = 0; bb < 2; ++bb) {
+        const int r = 64 * wb + 32 * bb;   // first tile row of this accumulator pair
+        if (r / kRowsPerPass != h) continue;
+        const int rl = r + lr - h * kRowsPerPass;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          store4<TW>(rowp + 8 * g4, acc[bb][4 * g4], acc[bb][4 * g4 + 1], acc[bb][4 * g4 + 2],
-                     acc[bb][4 * g4 + 3]);
+        for (int aa = 0; aa < 2; ++aa) {
+          TW* rowp = reinterpret_cast<TW*>(lds + rl * kRowB) + 64 * wa + 32 * aa + 4 * lh;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            store4<TW>(rowp + 8 * g4, acc[bb][aa][4 * g4], acc[bb][aa][4 * g4 + 1],
+                       acc[bb][aa][4 * g4 + 2], acc[bb][aa][4 * g4 + 3]);
+        }
       }
       lds_barrier();
-      constexpr int kChunksPerRow = 128 * int(sizeof(TW)) / 16;
+      constexpr int kChunksPerRow = 256 * int(sizeof(TW)) / 16;
       constexpr int kChunks = kRowsPerPass * kChunksPerRow;
+      const int live = cur.ncols * int(sizeof(TW)) / 16;   // chunks of a row inside dW
 #pragma unroll
-      for (int j = 0; j < kChunks / 256; ++j) {
-        const int i = tid + 256 * j;
+      for (int j = 0; j < kChunks / 512; ++j) {
+        const int i = tid + 512 * j;
         const int rl = i / kChunksPerRow, cc = i % kChunksPerRow;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * kRowB + cc * 16);
-        char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
-        // dW is written once and not read back here: stream it past the L2 so
-        // the expert's operand rows stay cached for the other tiles.
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+        if (cc < live) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(lds + rl * kRowB + cc * 16);
+          char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
+          // dW is written once and not read back here: stream it past the L2
+          // so the expert's operand rows stay cached for the other tiles.
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+        }
       }
       lds_barrier();
     }
@@ -505,12 +526,12 @@ hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hip
 // dW[e] = B_e^T A_e for every expert; dw_f32 selects the dW storage type;
 // tag names the launch (2: dW2, 13: dW13).
 hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s) {
-  const int64_t items = int64_t(a.E) * (a.a_ld / 128) * (a.b_ld / 128);
+  const int64_t items = int64_t(a.E) * ((a.a_ld + 255) / 256) * (a.b_ld / 128);
   if (items == 0) return hipSuccess;
 #define MOE_WG(TW, TAG, ID)                                                                  \
   do {                                                                                     \
-    const unsigned g = persistent_grid(occupancy<ID>(k_gemm_wgrad<TW, TAG>), items, cus);  \
-    hipLaunchKernelGGL((k_gemm_wgrad<TW, TAG>), dim3(g), dim3(256), 0, s, a);             \
+    const unsigned g = persistent_grid(occupancy<ID>(k_gemm_wgrad<TW, TAG>, 512), items, cus); \
+    hipLaunchKernelGGL((k_gemm_wgrad<TW, TAG>), dim3(g), dim3(512), 0, s, a);             \
   } while (0)
   if (dw_f32) {
     if (tag == 2)
