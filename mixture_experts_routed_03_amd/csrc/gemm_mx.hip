@@ -517,27 +517,33 @@ __device__ __forceinline__ uint64_t rec_ptr_m(const RouteHdr* h, int slot) {
   return h->rec.aux[slot];
 }
 
+// Work item: 128 dW rows x 256 dW columns of one expert on eight waves,
+// written as 512-byte (bf16) or 1 KB (fp32) row segments, which HBM takes
+// faster than 256-byte ones.  Wave w owns dW rows 64 (w >> 2) .. + 63 and
+// columns 64 (w & 3) .. + 63: 2 x 2 accumulators of 32 x 32.
 template <typename TW, int TAG>
-__global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
-  constexpr int kOp = 128 * 64;                        // one operand stage: 128 columns x 64 rows
-  constexpr int kRowB = 128 * int(sizeof(TW)) + 16;
-  constexpr int kHalves = sizeof(TW) == 4 ? 2 : 1;
-  constexpr int kRowsPerPass = 128 / kHalves;
+__global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
+  constexpr int kOpA = 256 * 64;                       // A stage: 256 columns x 64 rows
+  constexpr int kOpB = 128 * 64;                       // B stage: 128 columns x 64 rows
+  constexpr int kRowB = 256 * int(sizeof(TW)) + 16;    // padded output-staging row
+  constexpr int kRowsPerPass = sizeof(TW) == 4 ? 32 : 64;
+  constexpr int kPasses = 128 / kRowsPerPass;
   constexpr int kOut = kRowsPerPass * kRowB;
-  __shared__ __attribute__((aligned(16))) char lds[2 * kOp + kOut];
+  __shared__ __attribute__((aligned(16))) char lds[kOpA + kOpB + kOut];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wa = wave & 3;     // 64-column block of the tile
+  const int wb = wave >> 2;    // 64-row block of the tile
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const int ch = tid & 3;      // loader: 16-byte chunk of a 64-byte column segment
-  const int lrow = tid >> 2;   // loader: column (+ 64 j) of the 128-column tile
+  const int lcol = tid >> 2;   // loader: A columns lcol, lcol + 128; B column lcol
 
   const RouteHdr* hdr = a.hdr;
   const int a_ld = a.a_ld, b_ld = a.b_ld;
-  const int NA = a_ld / 128, NB = b_ld / 128;
+  const int NA = (a_ld + 255) / 256, NB = b_ld / 128;
   const int per_e = NA * NB;
-  const int n_items = a.E * per_e;
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
@@ -549,7 +555,7 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
   const uint8_t* sb = a.sb;
 
   struct Item {
-    int e, ta, tb, pb, mp, S;
+    int e, ta, tb, pb, mp, S, ncols;
   };
   int w0 = first + slot;
   int ie = w0 / per_e;
@@ -569,6 +575,7 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
     t.pb = a.poffsets[ie];
     t.mp = a.poffsets[ie + 1] - t.pb;
     t.S = (t.mp + 63) / 64;
+    t.ncols = min(256, a_ld - ita * 256);
     wcur += per;
     ita += per;
     while (ita >= NA) {
@@ -579,45 +586,46 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
       }
     }
   };
+  // A column of the tile, folded into the first half past a 128-column half
+  // tile's end (those columns are multiplied but never stored).
+  auto acol = [&](const Item& t, int c) { return t.ta * 256 + (c < t.ncols ? c : c - 128); };
 
-  u32x4 R[4];              // codes: A columns lrow, lrow+64; B columns lrow, lrow+64
-  uint32_t SA, SB[4];      // scales of this lane's MFMA rows for the stage
+  u32x4 R[3];              // codes: A columns lcol, lcol + 128; B column lcol
+  uint32_t SA[2], SB[2];   // exponents of this lane's MFMA rows for the stage
   auto load = [&](const Item& t, int s) {
     const int m0 = s * 64 + ch * 16;
     const bool in = m0 < t.mp;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = lrow + 64 * j;
+    for (int j = 0; j < 2; ++j)
       R[j] = in ? *reinterpret_cast<const u32x4*>(qa + int64_t(a_ld) * t.pb +
-                                                  int64_t(t.ta * 128 + c) * t.mp + m0)
+                                                  int64_t(acol(t, lcol + 128 * j)) * t.mp + m0)
                 : u32x4{0u, 0u, 0u, 0u};
-      R[2 + j] = in ? *reinterpret_cast<const u32x4*>(qb + int64_t(b_ld) * t.pb +
-                                                      int64_t(t.tb * 128 + c) * t.mp + m0)
-                    : u32x4{0u, 0u, 0u, 0u};
-    }
+    R[2] = in ? *reinterpret_cast<const u32x4*>(qb + int64_t(b_ld) * t.pb +
+                                                int64_t(t.tb * 128 + lcol) * t.mp + m0)
+              : u32x4{0u, 0u, 0u, 0u};
     const int mb = 2 * s + lh;   // MX block of this lane's half of the stage
     const int nmb = t.mp / 32;
-    if (mb < nmb) {
-      SA = sa[int64_t(a_ld) * (t.pb / 32) + int64_t(t.ta * 128 + 32 * wave + lr) * nmb + mb];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-        SB[bb] = sb[int64_t(b_ld) * (t.pb / 32) + int64_t(t.tb * 128 + 32 * bb + lr) * nmb + mb];
-    } else {
-      SA = 127;
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) SB[bb] = 127;
+    for (int i = 0; i < 2; ++i) {
+      SA[i] = 127;
+      SB[i] = 127;
+      if (mb < nmb) {
+        SA[i] = sa[int64_t(a_ld) * (t.pb / 32) + int64_t(acol(t, 64 * wa + 32 * i + lr)) * nmb + mb];
+        SB[i] = sb[int64_t(b_ld) * (t.pb / 32) + int64_t(t.tb * 128 + 64 * wb + 32 * i + lr) * nmb +
+                   mb];
+      }
     }
   };
-  uint32_t sa_cur = 127, sb_cur[4] = {127, 127, 127, 127};
+  uint32_t sa_cur[2] = {127, 127}, sb_cur[2] = {127, 127};
   auto store = [&]() {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<u32x4*>(lds + swz64(lrow + 64 * j, ch)) = R[j];
-      *reinterpret_cast<u32x4*>(lds + kOp + swz64(lrow + 64 * j, ch)) = R[2 + j];
-    }
-    sa_cur = SA;
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(lds + swz64(lcol + 128 * j, ch)) = R[j];
+    *reinterpret_cast<u32x4*>(lds + kOpA + swz64(lcol, ch)) = R[2];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) sb_cur[bb] = SB[bb];
+    for (int i = 0; i < 2; ++i) {
+      sa_cur[i] = SA[i];
+      sb_cur[i] = SB[i];
+    }
   };
 
   Item cur, nxt;
@@ -625,9 +633,9 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
   if (cur.e >= 0 && cur.S > 0) load(cur, 0);
   while (cur.e >= 0) {
     fill(nxt);
-    f32x16 acc[4];
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    for (int i = 0; i < 4; ++i) acc[i >> 1][i & 1] = f32x16{};
     for (int s = 0; s < cur.S; ++s) {
       store();
       lds_barrier();
@@ -635,43 +643,59 @@ __global__ __launch_bounds__(256) void k_mx_wgrad(MxArgs a) {
         load(cur, s + 1);
       else if (nxt.e >= 0 && nxt.S > 0)
         load(nxt, 0);
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(lds + swz64(32 * wave + lr, lh));
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(lds + swz64(32 * wave + lr, 2 + lh));
+      u32x4 a0[2], a1[2];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lds + kOp + swz64(32 * bb + lr, lh));
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(lds + kOp + swz64(32 * bb + lr, 2 + lh));
-        mfma_mx(acc[bb], a0, a1, b0, b1, int(sa_cur), int(sb_cur[bb]));
+      for (int aa = 0; aa < 2; ++aa) {
+        a0[aa] = *reinterpret_cast<const u32x4*>(lds + swz64(64 * wa + 32 * aa + lr, lh));
+        a1[aa] = *reinterpret_cast<const u32x4*>(lds + swz64(64 * wa + 32 * aa + lr, 2 + lh));
+      }
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lds + kOpA + swz64(64 * wb + 32 * bb + lr, lh));
+        const u32x4 b1 =
+            *reinterpret_cast<const u32x4*>(lds + kOpA + swz64(64 * wb + 32 * bb + lr, 2 + lh));
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+          mfma_mx(acc[bb][aa], a0[aa], a1[aa], b0, b1, int(sa_cur[aa]), int(sb_cur[bb]));
       }
       lds_barrier();
     }
     if (cur.S == 0 && nxt.e >= 0 && nxt.S > 0) load(nxt, 0);
 
+    // acc[bb][aa][v] = dW[b = tb*128 + 64*wb + 32*bb + lr]
+    //                    [a = ta*256 + 64*wa + 32*aa + 8*(v/4) + 4*lh + v%4]
     TW* o = reinterpret_cast<TW*>(a.out0) + (int64_t(cur.e) * b_ld + int64_t(cur.tb) * 128) * a_ld +
-            cur.ta * 128;
-    char* stg = lds + 2 * kOp;
+            cur.ta * 256;
+    char* stg = lds + kOpA + kOpB;
 #pragma unroll
-    for (int h = 0; h < kHalves; ++h) {
+    for (int h = 0; h < kPasses; ++h) {
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        if (bb / (4 / kHalves) != h) continue;
-        const int rl = 32 * bb + lr - h * kRowsPerPass;
-        TW* rowp = reinterpret_cast<TW*>(stg + rl * kRowB) + 32 * wave + 4 * lh;
+      for (int bb = 0; bb < 2; ++bb) {
+        const int r = 64 * wb + 32 * bb;   // first tile row of this accumulator pair
+        if (r / kRowsPerPass != h) continue;
+        const int rl = r + lr - h * kRowsPerPass;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          store4<TW>(rowp + 8 * g4, acc[bb][4 * g4], acc[bb][4 * g4 + 1], acc[bb][4 * g4 + 2],
-                     acc[bb][4 * g4 + 3]);
+        for (int aa = 0; aa < 2; ++aa) {
+          TW* rowp = reinterpret_cast<TW*>(stg + rl * kRowB) + 64 * wa + 32 * aa + 4 * lh;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            store4<TW>(rowp + 8 * g4, acc[bb][aa][4 * g4], acc[bb][aa][4 * g4 + 1],
+                       acc[bb][aa][4 * g4 + 2], acc[bb][aa][4 * g4 + 3]);
+        }
       }
       lds_barrier();
-      constexpr int kChunksPerRow = 128 * int(sizeof(TW)) / 16;
+      constexpr int kChunksPerRow = 256 * int(sizeof(TW)) / 16;
       constexpr int kChunks = kRowsPerPass * kChunksPerRow;
+      const int live = cur.ncols * int(sizeof(TW)) / 16;   // chunks of a row inside dW
 #pragma unroll
-      for (int j = 0; j < kChunks / 256; ++j) {
-        const int i = tid + 256 * j;
+      for (int j = 0; j < kChunks / 512; ++j) {
+        const int i = tid + 512 * j;
         const int rl = i / kChunksPerRow, cc = i % kChunksPerRow;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * kRowB + cc * 16);
-        char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+        if (cc < live) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * kRowB + cc * 16);
+          char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+        }
       }
       lds_barrier();
     }
@@ -728,12 +752,12 @@ hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, h
 
 // tag 2: dW2, 13: dW13
 hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStream_t s) {
-  const int64_t items = int64_t(a.E) * (a.a_ld / 128) * (a.b_ld / 128);
+  const int64_t items = int64_t(a.E) * ((a.a_ld + 255) / 256) * (a.b_ld / 128);
   if (items == 0) return hipSuccess;
 #define MOE_MXWG(TW, TAG, ID)                                                                 \
   do {                                                                                      \
-    const unsigned g = grid_m(occupancy_m<ID>(k_mx_wgrad<TW, TAG>), items, cus);            \
-    hipLaunchKernelGGL((k_mx_wgrad<TW, TAG>), dim3(g), dim3(256), 0, s, a);                 \
+    const unsigned g = grid_m(occupancy_m<ID>(k_mx_wgrad<TW, TAG>, 512), items, cus);       \
+    hipLaunchKernelGGL((k_mx_wgrad<TW, TAG>), dim3(g), dim3(512), 0, s, a);                 \
   } while (0)
   if (dw_f32) {
     if (tag == 2)
