@@ -261,6 +261,34 @@ template <> struct Elem<uint16_t> {
 // Number of XCDs of the MI355X; workgroups are dispatched round-robin over them.
 constexpr int kXcds = 8;
 
+// Expert of grouped-GEMM work item w: the largest e with mtoff[e] * NT <= w
+// (mtoff = the m-tile prefix, NT = n-tiles per expert).  A workgroup's items
+// only move forward, so from the expert of its previous item (e_prev >= 0) a
+// few steps forward usually find it; the first item (e_prev < 0), or one far
+// ahead, takes a binary search.  Each step is a dependent load, so this keeps
+// the chain of latencies before an item's first weight loads short.
+__device__ inline int item_expert(const int32_t* __restrict__ mtoff, int E, int NT, int w,
+                                  int e_prev) {
+  int lo = 0;
+  if (e_prev >= 0) {
+    lo = e_prev;
+#pragma unroll 1
+    for (int k = 0; k < 4; ++k) {
+      if (mtoff[lo + 1] * NT > w) return lo;
+      ++lo;
+    }
+  }
+  int hi = E;  // invariant: mtoff[lo] * NT <= w < mtoff[hi] * NT
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (mtoff[mid] * NT <= w)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
 // Work split over the XCDs.  Units run expert-major, per_e per expert; a
 // unit of expert e costs (pre[e + 1] - pre[e]) + cw, and the XCDs receive
 // runs of units of equal total cost, so one hot expert does not load a

@@ -78,19 +78,6 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
   f[3] = __uint_as_float(v[1] & 0xffff0000u);
 }
 
-__device__ __forceinline__ int find_expert_b(const int32_t* __restrict__ mtoff, int E, int NT,
-                                             int w) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (mtoff[mid] * NT <= w)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-
 // Row tile (contraction contiguous): 128-byte rows, 16-byte chunks swizzled.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
 
@@ -148,8 +135,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
   const int64_t N = a.N;
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
+  int e_prev = -1;  // expert of this workgroup's previous item
   for (int w = first + slot; w < last; w += per) {
-    const int e = find_expert_b(a.mtoff, a.E, a.NT, w);
+    const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
+    e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;

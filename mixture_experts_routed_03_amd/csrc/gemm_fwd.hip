@@ -86,20 +86,6 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
-// Finds the expert of work item w: the largest e with mtoff[e]*NT <= w.
-__device__ __forceinline__ int find_expert(const int32_t* __restrict__ mtoff, int E, int NT,
-                                           int w) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (mtoff[mid] * NT <= w)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-
 // LDS byte offset of 16-byte chunk c of tile row r (128-byte rows).  Chunks
 // are XOR-swizzled by (r ^ r>>3) & 7 so that both the row-wise writes (8 lanes
 // per row) and the MFMA-layout reads (32 rows, one chunk) are spread over all
@@ -147,8 +133,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
   const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
   const int S = int(row_bytes / 128);
 
+  int e_prev = -1;  // expert of this workgroup's previous item
   for (int w = first + slot; w < last; w += per) {
-    const int e = find_expert(a.mtoff, a.E, a.NT, w);
+    const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
+    e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;

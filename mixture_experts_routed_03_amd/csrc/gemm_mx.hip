@@ -55,19 +55,6 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ 
 // 64-byte rows (WGRAD): 16-byte chunk ch of row r
 __device__ __forceinline__ int swz64(int r, int ch) { return r * 64 + ((ch ^ ((r >> 2) & 3)) << 4); }
 
-__device__ __forceinline__ int find_expert_m(const int32_t* __restrict__ mtoff, int E, int NT,
-                                             int w) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (mtoff[mid] * NT <= w)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
 template <>
@@ -122,10 +109,12 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   const int chunk = (n_items + kXcds - 1) / kXcds;
   const int S = Kd / 128;
 
+  int e_prev = -1;  // expert of this workgroup's previous item
   for (int it = slot; it < chunk; it += per) {
     const int w = xcd * chunk + it;
     if (w >= n_items) break;
-    const int e = find_expert_m(a.mtoff, a.E, a.NT, w);
+    const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
+    e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;
@@ -355,8 +344,10 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
   const int NB32 = int(N / 32);
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
+  int e_prev = -1;  // expert of this workgroup's previous item
   for (int w = first + slot; w < last; w += per) {
-    const int e = find_expert_m(a.mtoff, a.E, a.NT, w);
+    const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
+    e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;
