@@ -77,6 +77,13 @@ typedef enum moe_dtype {
 
 /* moe_expert_bwd flags */
 #define MOE_BWD_ACCUMULATE_DX 0x1u  /* dx += result instead of dx = result */
+/* g->dw13 += result and g->dw2 += result instead of =: the in-place
+ * accumulation of weight gradients into the caller's parameter-gradient
+ * buffers that the explainer's API section lists among the training
+ * options (several micro-batches into one dW).  Each value is summed in fp32
+ * and rounded once to the dW type; experts with no rows keep their values.
+ * dW is then read as well as written. */
+#define MOE_BWD_ACCUMULATE_DW 0x2u
 
 /* Layer description.  Supported: D % 128 == 0, F % 128 == 0, 1 <= K <= 16,
  * K <= E <= 4096, 0 <= t_max <= 2^24 / K. */
@@ -215,6 +222,7 @@ moe_status moe_expert_fwd_fused(moe_plan_t plan, void* route_ws, const void* x,
  * gradients into g->dx.  Rebuilds the layer's state first when its forward
  * replayed.  Layers of a step must run in reverse forward order; each
  * backward rewinds the arena cursor to its layer's start. */
+/* flags: MOE_BWD_ACCUMULATE_DX | MOE_BWD_ACCUMULATE_DW; other bits -> MOE_ERR_ARG. */
 moe_status moe_expert_bwd(moe_plan_t plan, int32_t layer, void* route_ws, const void* x,
                           const float* scores, const void* dy, const moe_weights* w,
                           const void* h3_slots, void* arena, void* scratch,

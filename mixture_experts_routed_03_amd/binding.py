@@ -28,6 +28,7 @@ STATUS_PAD_SCORE = 0x2
 STATUS_ARENA = 0x4
 STATUS_NULL_INPUT = 0x8
 BWD_ACCUMULATE_DX = 0x1
+BWD_ACCUMULATE_DW = 0x2
 _ERRORS = {1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
            4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
 

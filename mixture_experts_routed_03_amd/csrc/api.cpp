@@ -220,6 +220,7 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs wg2{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
              u8(L.dh3cq), u8(L.dh3cs), g->dw2, nullptr, 0, 0, d.f, 0, d.e, d.f, d.d, 2, 0};
+  wg2.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
   e = timed(p, "w2_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 2, wg2, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   RowqArgs r1{hdr, sc + L.dh1, u8(L.qdh1), u8(L.sdh1), 2 * d.f, -1, -1, -1, 0, int(p->R_max)};
@@ -238,6 +239,7 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs wg13{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
               u8(L.dh1cq), u8(L.dh1cs), g->dw13, nullptr, 0, 0, d.f, 0, d.e, d.d, 2 * d.f, 0, 0};
+  wg13.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
   e = timed(p, "w13_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 13, wg13, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = timed(p, "dx_reduce", s, [&] {
@@ -600,6 +602,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
                           const void* h3, void* arena, void* scratch, const moe_grads* g,
                           uint32_t flags, hipStream_t s) {
   if (!p || !ws || !w || !g || !scratch || !h3) return MOE_ERR_ARG;
+  if (flags & ~(MOE_BWD_ACCUMULATE_DX | MOE_BWD_ACCUMULATE_DW)) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
   if (!d.training || d.prec == MOE_PREC_F32) return MOE_ERR_UNSUPPORTED;
   if (layer < 0 || layer >= d.max_layers) return MOE_ERR_ARG;
@@ -644,6 +647,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw2{hdr, offsets, mtoff, nullptr, nullptr, dh3, h2, g->dw2, nullptr,
               0, 0, d.f, d.d, d.e, 0, d.f, d.d};
+  bw2.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
   e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(dw_f32, 2, bw2, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs b13{hdr, offsets, gtoff, w->w13, dh1, nullptr, nullptr, dxr, nullptr,
@@ -657,6 +661,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw13{hdr, offsets, mtoff, nullptr, nullptr, dh1, sc + p->sl.x_rows, g->dw13, nullptr,
                0, 0, d.f, d.d, d.e, 0, d.d, 2 * d.f};
+  bw13.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
   e = timed(p, "w13_wgrad", s, [&] { return launch_wgrad(dw_f32, 13, bw13, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = timed(p, "dx_reduce", s, [&] {

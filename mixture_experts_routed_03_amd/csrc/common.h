@@ -117,6 +117,7 @@ struct BwdArgs {
   int NT;               // DGRAD n-tiles per expert
   int a_ld, b_ld;       // WGRAD row lengths of the A rows (= dW row length) and B rows (= dW rows)
   const int32_t* stoff; // DGRAD: 64-row stage prefix (XCD work split); mtoff = the m-tile prefix
+  int acc_dw;           // WGRAD: 1 = dW += result (fp32 sum, rounded once), 0 = dW = result
 };
 
 // Arguments of the MXFP8 grouped GEMM launches.
@@ -143,6 +144,7 @@ struct MxArgs {
   float* y32;
   int K;
   const int32_t* stoff;  // DGRAD: 64-row stage prefix (XCD work split); mtoff = the m-tile prefix
+  int acc_dw;            // WGRAD: 1 = dW += result (fp32 sum, rounded once), 0 = dW = result
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:
@@ -257,6 +259,29 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ uint16_t from_f(float v) { return f32_to_bf16(v); }
   static __device__ __forceinline__ float round(float v) { return round_bf16(v); }
 };
+
+// Weight-gradient copy-out: four fp32 results v added to the four dW values
+// at p (in-place accumulation: one rounding of old + v to the dW type).
+__device__ __forceinline__ void acc_store4(float* p, const float* v) {
+  typedef float f32x4_ __attribute__((ext_vector_type(4)));
+  f32x4_ o = *reinterpret_cast<const f32x4_*>(p);
+  o[0] += v[0];
+  o[1] += v[1];
+  o[2] += v[2];
+  o[3] += v[3];
+  __builtin_nontemporal_store(o, reinterpret_cast<f32x4_*>(p));
+}
+__device__ __forceinline__ void acc_store4(uint16_t* p, const float* v) {
+  typedef unsigned int u32x2_ __attribute__((ext_vector_type(2)));
+  u32x2_ o = *reinterpret_cast<const u32x2_*>(p);
+  const float a = __uint_as_float(o[0] << 16) + v[0];
+  const float b = __uint_as_float(o[0] & 0xffff0000u) + v[1];
+  const float c = __uint_as_float(o[1] << 16) + v[2];
+  const float d = __uint_as_float(o[1] & 0xffff0000u) + v[3];
+  o[0] = pack_bf16x2(a, b);
+  o[1] = pack_bf16x2(c, d);
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x2_*>(p));
+}
 
 // Number of XCDs of the MI355X; workgroups are dispatched round-robin over them.
 constexpr int kXcds = 8;

@@ -293,12 +293,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
 // rows; chunks XOR-swizzled by 4 (m & 3)) and are read with transpose reads.
 __device__ __forceinline__ int bsw(int m, int c) { return m * 256 + ((c ^ ((m & 3) << 2)) << 4); }
 
-template <typename TW, int TAG>
+// ACC: in-place accumulation (dW += result): the tile is staged in fp32 and
+// each copied-out value is added to the dW value it replaces, rounded once.
+template <typename TW, int TAG, int ACC>
 __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
+  typedef typename std::conditional<ACC != 0, float, TW>::type TS;   // staging type
   constexpr int kA = 64 * 512;                         // A stage: 64 token rows x 256 columns
   constexpr int kB = 64 * 256;                         // B stage: 64 token rows x 128 columns
-  constexpr int kRowB = 256 * int(sizeof(TW)) + 16;    // padded output-staging row
-  constexpr int kRowsPerPass = sizeof(TW) == 4 ? 32 : 64;
+  constexpr int kRowB = 256 * int(sizeof(TS)) + 16;    // padded output-staging row
+  constexpr int kRowsPerPass = sizeof(TS) == 4 ? 32 : 64;
   constexpr int kPasses = 128 / kRowsPerPass;
   static_assert(kRowsPerPass * kRowB <= kA + kB, "output staging reuses the operand stages");
   __shared__ __attribute__((aligned(16))) char lds[kA + kB];
@@ -450,27 +453,33 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
         const int rl = r + lr - h * kRowsPerPass;
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
-          TW* rowp = reinterpret_cast<TW*>(lds + rl * kRowB) + 64 * wa + 32 * aa + 4 * lh;
+          TS* rowp = reinterpret_cast<TS*>(lds + rl * kRowB) + 64 * wa + 32 * aa + 4 * lh;
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4)
-            store4<TW>(rowp + 8 * g4, acc[bb][aa][4 * g4], acc[bb][aa][4 * g4 + 1],
+            store4<TS>(rowp + 8 * g4, acc[bb][aa][4 * g4], acc[bb][aa][4 * g4 + 1],
                        acc[bb][aa][4 * g4 + 2], acc[bb][aa][4 * g4 + 3]);
         }
       }
       lds_barrier();
-      constexpr int kChunksPerRow = 256 * int(sizeof(TW)) / 16;
+      constexpr int kChunksPerRow = 256 * int(sizeof(TS)) / 16;
       constexpr int kChunks = kRowsPerPass * kChunksPerRow;
-      const int live = cur.ncols * int(sizeof(TW)) / 16;   // chunks of a row inside dW
+      const int live = cur.ncols * int(sizeof(TS)) / 16;   // chunks of a row inside dW
 #pragma unroll
       for (int j = 0; j < kChunks / 512; ++j) {
         const int i = tid + 512 * j;
         const int rl = i / kChunksPerRow, cc = i % kChunksPerRow;
         if (cc < live) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(lds + rl * kRowB + cc * 16);
-          char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
-          // dW is written once and not read back here: stream it past the L2
-          // so the expert's operand rows stay cached for the other tiles.
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+          if (ACC) {   // four fp32 results onto the four dW values they update
+            float f[4] = {__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                          __uint_as_float(v[3])};
+            acc_store4(o + int64_t(rl + h * kRowsPerPass) * a_ld + cc * 4, f);
+          } else {
+            char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
+            // dW is written once and not read back here: stream it past the
+            // L2 so the expert's operand rows stay cached for the other tiles.
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+          }
         }
       }
       lds_barrier();
@@ -512,26 +521,30 @@ hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hip
   return hipGetLastError();
 }
 
-// dW[e] = B_e^T A_e for every expert; dw_f32 selects the dW storage type;
-// tag names the launch (2: dW2, 13: dW13).
+// dW[e] = B_e^T A_e for every expert (a.acc_dw: dW[e] += it); dw_f32 selects
+// the dW storage type; tag names the launch (2: dW2, 13: dW13).
 hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s) {
   const int64_t items = int64_t(a.E) * ((a.a_ld + 255) / 256) * (a.b_ld / 128);
   if (items == 0) return hipSuccess;
-#define MOE_WG(TW, TAG, ID)                                                                  \
-  do {                                                                                     \
-    const unsigned g = persistent_grid(occupancy<ID>(k_gemm_wgrad<TW, TAG>, 512), items, cus); \
-    hipLaunchKernelGGL((k_gemm_wgrad<TW, TAG>), dim3(g), dim3(512), 0, s, a);             \
+#define MOE_WG(TW, TAG, ACC, ID)                                                                \
+  do {                                                                                        \
+    const unsigned g =                                                                        \
+        persistent_grid(occupancy<ID>(k_gemm_wgrad<TW, TAG, ACC>, 512), items, cus);          \
+    hipLaunchKernelGGL((k_gemm_wgrad<TW, TAG, ACC>), dim3(g), dim3(512), 0, s, a);           \
   } while (0)
+  const int acc = a.acc_dw ? 1 : 0;
   if (dw_f32) {
-    if (tag == 2)
-      MOE_WG(float, 2, 2);
-    else
-      MOE_WG(float, 13, 3);
+    if (tag == 2) {
+      if (acc) MOE_WG(float, 2, 1, 6); else MOE_WG(float, 2, 0, 2);
+    } else {
+      if (acc) MOE_WG(float, 13, 1, 7); else MOE_WG(float, 13, 0, 3);
+    }
   } else {
-    if (tag == 2)
-      MOE_WG(uint16_t, 2, 4);
-    else
-      MOE_WG(uint16_t, 13, 5);
+    if (tag == 2) {
+      if (acc) MOE_WG(uint16_t, 2, 1, 8); else MOE_WG(uint16_t, 2, 0, 4);
+    } else {
+      if (acc) MOE_WG(uint16_t, 13, 1, 9); else MOE_WG(uint16_t, 13, 0, 5);
+    }
   }
 #undef MOE_WG
   return hipGetLastError();

@@ -512,12 +512,15 @@ __device__ __forceinline__ uint64_t rec_ptr_m(const RouteHdr* h, int slot) {
 // written as 512-byte (bf16) or 1 KB (fp32) row segments, which HBM takes
 // faster than 256-byte ones.  Wave w owns dW rows 64 (w >> 2) .. + 63 and
 // columns 64 (w & 3) .. + 63: 2 x 2 accumulators of 32 x 32.
-template <typename TW, int TAG>
+// ACC: in-place accumulation (dW += result): the tile is staged in fp32 and
+// each copied-out value is added to the dW value it replaces, rounded once.
+template <typename TW, int TAG, int ACC>
 __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
+  typedef typename std::conditional<ACC != 0, float, TW>::type TS;   // staging type
   constexpr int kOpA = 256 * 64;                       // A stage: 256 columns x 64 rows
   constexpr int kOpB = 128 * 64;                       // B stage: 128 columns x 64 rows
-  constexpr int kRowB = 256 * int(sizeof(TW)) + 16;    // padded output-staging row
-  constexpr int kRowsPerPass = sizeof(TW) == 4 ? 32 : 64;
+  constexpr int kRowB = 256 * int(sizeof(TS)) + 16;    // padded output-staging row
+  constexpr int kRowsPerPass = sizeof(TS) == 4 ? 32 : 64;
   constexpr int kPasses = 128 / kRowsPerPass;
   constexpr int kOut = kRowsPerPass * kRowB;
   __shared__ __attribute__((aligned(16))) char lds[kOpA + kOpB + kOut];
@@ -667,25 +670,31 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
         const int rl = r + lr - h * kRowsPerPass;
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
-          TW* rowp = reinterpret_cast<TW*>(stg + rl * kRowB) + 64 * wa + 32 * aa + 4 * lh;
+          TS* rowp = reinterpret_cast<TS*>(stg + rl * kRowB) + 64 * wa + 32 * aa + 4 * lh;
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4)
-            store4<TW>(rowp + 8 * g4, acc[bb][aa][4 * g4], acc[bb][aa][4 * g4 + 1],
+            store4<TS>(rowp + 8 * g4, acc[bb][aa][4 * g4], acc[bb][aa][4 * g4 + 1],
                        acc[bb][aa][4 * g4 + 2], acc[bb][aa][4 * g4 + 3]);
         }
       }
       lds_barrier();
-      constexpr int kChunksPerRow = 256 * int(sizeof(TW)) / 16;
+      constexpr int kChunksPerRow = 256 * int(sizeof(TS)) / 16;
       constexpr int kChunks = kRowsPerPass * kChunksPerRow;
-      const int live = cur.ncols * int(sizeof(TW)) / 16;   // chunks of a row inside dW
+      const int live = cur.ncols * int(sizeof(TS)) / 16;   // chunks of a row inside dW
 #pragma unroll
       for (int j = 0; j < kChunks / 512; ++j) {
         const int i = tid + 512 * j;
         const int rl = i / kChunksPerRow, cc = i % kChunksPerRow;
         if (cc < live) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * kRowB + cc * 16);
-          char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+          if (ACC) {   // four fp32 results onto the four dW values they update
+            float f[4] = {__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                          __uint_as_float(v[3])};
+            acc_store4(o + int64_t(rl + h * kRowsPerPass) * a_ld + cc * 4, f);
+          } else {
+            char* dst = reinterpret_cast<char*>(o + int64_t(rl + h * kRowsPerPass) * a_ld) + cc * 16;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+          }
         }
       }
       lds_barrier();
@@ -745,21 +754,24 @@ hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, h
 hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStream_t s) {
   const int64_t items = int64_t(a.E) * ((a.a_ld + 255) / 256) * (a.b_ld / 128);
   if (items == 0) return hipSuccess;
-#define MOE_MXWG(TW, TAG, ID)                                                                 \
+#define MOE_MXWG(TW, TAG, ACC, ID)                                                            \
   do {                                                                                      \
-    const unsigned g = grid_m(occupancy_m<ID>(k_mx_wgrad<TW, TAG>, 512), items, cus);       \
-    hipLaunchKernelGGL((k_mx_wgrad<TW, TAG>), dim3(g), dim3(512), 0, s, a);                 \
+    const unsigned g = grid_m(occupancy_m<ID>(k_mx_wgrad<TW, TAG, ACC>, 512), items, cus);  \
+    hipLaunchKernelGGL((k_mx_wgrad<TW, TAG, ACC>), dim3(g), dim3(512), 0, s, a);           \
   } while (0)
+  const int acc = a.acc_dw ? 1 : 0;
   if (dw_f32) {
-    if (tag == 2)
-      MOE_MXWG(float, 2, 4);
-    else
-      MOE_MXWG(float, 13, 5);
+    if (tag == 2) {
+      if (acc) MOE_MXWG(float, 2, 1, 8); else MOE_MXWG(float, 2, 0, 4);
+    } else {
+      if (acc) MOE_MXWG(float, 13, 1, 9); else MOE_MXWG(float, 13, 0, 5);
+    }
   } else {
-    if (tag == 2)
-      MOE_MXWG(uint16_t, 2, 6);
-    else
-      MOE_MXWG(uint16_t, 13, 7);
+    if (tag == 2) {
+      if (acc) MOE_MXWG(uint16_t, 2, 1, 10); else MOE_MXWG(uint16_t, 2, 0, 6);
+    } else {
+      if (acc) MOE_MXWG(uint16_t, 13, 1, 11); else MOE_MXWG(uint16_t, 13, 0, 7);
+    }
   }
 #undef MOE_MXWG
   return hipGetLastError();

@@ -108,15 +108,19 @@ def sampled_forward_ref(lay, tokens, mx=False):
     return np.stack([out[t] for t in tokens])
 
 
-def run_train(layer, lay, dw_f32=False, dx_init=None, flags=0):
-    """Forward + backward on the current stream; returns y, dx, dw13, dw2, dscores."""
+def run_train(layer, lay, dw_f32=False, dx_init=None, flags=0, dw_init=None):
+    """Forward + backward on the current stream; returns y, dx, dw13, dw2, dscores
+    (dw_init: starting dW13, dW2 for MOE_BWD_ACCUMULATE_DW)."""
     T = lay["x"].shape[0]
     dev = layer.device
     y = run_forward(layer, lay)
     dx = (torch.empty((T, layer.D), dtype=layer.act_dtype, device=dev) if dx_init is None
           else dx_init.clone())
-    dw13 = torch.empty((layer.E, 2 * layer.F, layer.D), dtype=layer.dw_dtype, device=dev)
-    dw2 = torch.empty((layer.E, layer.D, layer.F), dtype=layer.dw_dtype, device=dev)
+    if dw_init is None:
+        dw13 = torch.empty((layer.E, 2 * layer.F, layer.D), dtype=layer.dw_dtype, device=dev)
+        dw2 = torch.empty((layer.E, layer.D, layer.F), dtype=layer.dw_dtype, device=dev)
+    else:
+        dw13, dw2 = dw_init[0].clone(), dw_init[1].clone()
     ds = torch.empty((T, layer.K), dtype=torch.float32, device=dev)
     layer.backward(lay["x"], lay["scores"], lay["dy"], lay["w13"], lay["w2"], dx, dw13, dw2, ds,
                    flags=flags)

@@ -1,0 +1,99 @@
+"""GPU parity of in-place weight-gradient accumulation (MOE_BWD_ACCUMULATE_DW,
+the optional accumulation of weight gradients into the caller's parameter
+gradient buffers listed in the Dist-MoE explainer's API section): starting
+from a random dW, the backward must leave dW_start + dW, with dW the oracle's
+weight gradient of the step (summed in fp32, rounded once), and must leave the
+dW of experts without rows bit-for-bit unchanged."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as om
+from oracle import mx as omx
+from tests._harness import TOL, banner, make_inputs, run_train
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_routed_03_amd import binding
+    binding.lib()
+    assert torch.cuda.is_available()
+    return binding
+
+
+def _start(layer, seed, scale):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    E, F, D = layer.E, layer.F, layer.D
+    w13 = (torch.randn((E, 2 * F, D), generator=g) * scale).to(layer.dw_dtype).cuda()
+    w2 = (torch.randn((E, D, F), generator=g) * scale).to(layer.dw_dtype).cuda()
+    return w13, w2
+
+
+def _empty_last_expert(lay):
+    """Route no token to the last expert (its routes become padding, score 0)."""
+    E = lay["w13"].shape[0]
+    ids, sc = lay["ids"].clone(), lay["scores"].clone()
+    pad = ids == E - 1
+    ids[pad] = -1
+    sc[pad] = 0.0
+    lay["ids"], lay["scores"] = ids, sc
+
+
+def _check(dw13, dw2, start, rdw13, rdw2, counts, tol):
+    for e in range(len(counts)):
+        if counts[e] == 0:
+            assert torch.equal(dw13[e], start[0][e]) and torch.equal(dw2[e], start[1][e]), e
+        else:
+            assert om.max_abs_rel(dw13[e], om.as_f64(start[0][e]) + rdw13[e]) < tol, e
+            assert om.max_abs_rel(dw2[e], om.as_f64(start[1][e]) + rdw2[e]) < tol, e
+
+
+@pytest.mark.parametrize("T,D,F,E,K,zipf,dw", [
+    (200, 384, 256, 9, 2, 1.3, "bf16"),   # D = 3 x 128: half 256-column dW13 tiles; empty experts
+    (130, 256, 384, 4, 2, None, "f32"),   # F = 3 x 128: half dW2 tiles; fp32 dW
+])
+def test_bf16_accumulate_dw(B, T, D, F, E, K, zipf, dw):
+    banner(f"bf16 dW accumulate T={T} D={D} F={F} E={E} K={K} zipf={zipf} dW={dw}")
+    lay = make_inputs(T, D, F, E, K, "bf16", zipf=zipf, seed=T + 3, training=True)
+    _empty_last_expert(lay)
+    layer = B.MoeLayer(T, D, F, E, K, "bf16", dw_dtype=dw, training=True)
+    start = _start(layer, T, 0.05)
+    _, _, dw13, dw2, _ = run_train(layer, lay, flags=B.BWD_ACCUMULATE_DW, dw_init=start)
+    torch.cuda.synchronize()
+    assert layer.status()[0] == 0
+    _, cache = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(),
+                          lay["w2"].cpu(), keep=True)
+    _, rdw13, rdw2, _ = om.backward(lay["dy"], lay["x"], lay["ids"], lay["scores"],
+                                    lay["w13"].cpu(), lay["w2"].cpu(), cache)
+    counts = cache["route"]["counts"]
+    assert counts[E - 1] == 0
+    _check(dw13, dw2, start, rdw13, rdw2, counts, TOL["bf16"])
+
+
+def test_mx_accumulate_dw(B):
+    T, D, F, E, K = 160, 384, 256, 7, 2
+    banner(f"mxfp8 dW accumulate T={T} D={D} F={F} E={E} K={K}")
+    lay = make_inputs(T, D, F, E, K, "mxfp8", zipf=1.4, seed=41, training=True)
+    _empty_last_expert(lay)
+    layer = B.MoeLayer(T, D, F, E, K, "mxfp8", training=True)
+    start = _start(layer, 41, 0.05)
+    _, _, dw13, dw2, _ = run_train(layer, lay, flags=B.BWD_ACCUMULATE_DW, dw_init=start)
+    torch.cuda.synchronize()
+    assert layer.status()[0] == 0
+    ids, sc = lay["ids"].cpu().numpy(), lay["scores"]
+    _, cache = omx.forward(lay["x"], ids, sc, lay["w13"].cpu(), lay["w2"].cpu(), keep=True)
+    _, rdw13, rdw2, _ = omx.backward(lay["dy"], lay["x"], ids, sc, lay["w13"].cpu(),
+                                     lay["w2"].cpu(), cache)
+    counts = np.bincount(ids[ids >= 0], minlength=E)
+    assert counts[E - 1] == 0
+    _check(dw13, dw2, start, rdw13, rdw2, counts, TOL["mxfp8"])
+
+
+def test_unknown_backward_flag_rejected(B):
+    T, D, F, E, K = 16, 128, 128, 2, 1
+    lay = make_inputs(T, D, F, E, K, "bf16", seed=2, training=True)
+    layer = B.MoeLayer(T, D, F, E, K, "bf16", training=True)
+    with pytest.raises(B.MoeError):
+        run_train(layer, lay, flags=0x4)
