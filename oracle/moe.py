@@ -105,33 +105,73 @@ def silu_grad(z: np.ndarray) -> np.ndarray:
     return s * (1.0 + z * (1.0 - s))
 
 
-def expert_ffn(x_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray):
+# Clamped SwiGLU.  The Dist-MoE explainer's API section lists "plain and
+# clamped SwiGLU" without a formula; the reading taken here is the plainest
+# one: before the activation the gate is clamped from above and the up
+# projection to [-L, L], h2 = SiLU(min(g, L)) * clamp(u, -L, L), and a
+# clamped value passes no gradient (dg = 0 where g > L, du = 0 where |u| > L).
+# Each clamp is a decision at a threshold, so it is taken on the values the
+# kernel decides on: ``decide`` = (g, u) as stored in the activation dtype
+# (default: g, u themselves).  limit None or 0 is the plain SwiGLU.
+#   ([DM] s.08 "Supported modes"; SiLU and its derivative from [GG] s.1, s.2.)
+
+def _clamped(g, u, limit, decide):
+    if not limit:
+        return g, u, np.ones_like(g, dtype=bool), np.ones_like(u, dtype=bool)
+    gd, ud = (g, u) if decide is None else decide
+    g_in = ~(gd > limit)
+    u_in = ~((ud > limit) | (ud < -limit))
+    gc = np.where(g_in, g, limit)
+    uc = np.where(u_in, u, np.where(ud > limit, limit, -limit))
+    return gc, uc, g_in, u_in
+
+
+def swiglu(g, u, limit=None, decide=None):
+    """h2 = SiLU(g) * u ([DM] s.02), clamped as above when ``limit`` is set."""
+    gc, uc, _, _ = _clamped(g, u, limit, decide)
+    return silu(gc) * uc
+
+
+def swiglu_backward(g, u, dh2, limit=None, decide=None):
+    """(dg, du) of h2 = swiglu(g, u): dg = dh2 * u * silu'(g), du = dh2 * SiLU(g)
+    ([GG] s.2 SwiGLU backward), on the clamped values, zero where clamped."""
+    gc, uc, g_in, u_in = _clamped(g, u, limit, decide)
+    dg = np.where(g_in, dh2 * uc * silu_grad(gc), 0.0)
+    du = np.where(u_in, dh2 * silu(gc), 0.0)
+    return dg, du
+
+
+def expert_ffn(x_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray, limit=None, act=None):
     """One expert on its rows: h1 = x W13^T = [g | u], h2 = SiLU(g) * u, h3 = h2 W2^T.
 
     x_rows [M, D], w13 [2F, D] (gate rows first), w2 [D, F]; all float64.
+    ``limit``: clamped SwiGLU (see above), its clamp decisions taken on
+    act(h1), the activation dtype's rounding (None: h1 itself).
     """
     F = w2.shape[1]
     h1 = x_rows @ w13.T
     g, u = h1[:, :F], h1[:, F:]
-    h2 = silu(g) * u
+    dec = None if act is None else (act(g), act(u))
+    h2 = swiglu(g, u, limit, dec)
     h3 = h2 @ w2.T
     return h1, h2, h3
 
 
-def expert_ffn_backward(x_rows, w13, w2, h1, dh3):
+def expert_ffn_backward(x_rows, w13, w2, h1, dh3, limit=None, act=None):
     """Gradients of one expert given dL/dh3 for its rows.
 
     dh2 = dh3 W2; dW2 = dh3^T h2; dg = dh2 * u * silu'(g); du = dh2 * SiLU(g);
     dh1 = [dg | du]; dx = dh1 W13; dW13 = dh1^T x  ([GG] s.2, grouped GEMM
-    backward for C = A B^T: dA = dC B, dB = dC^T A).
+    backward for C = A B^T: dA = dC B, dB = dC^T A).  ``limit``/``act`` as in
+    expert_ffn.
     """
     F = w2.shape[1]
     g, u = h1[:, :F], h1[:, F:]
-    h2 = silu(g) * u
+    dec = None if act is None else (act(g), act(u))
+    h2 = swiglu(g, u, limit, dec)
     dh2 = dh3 @ w2
     dw2 = dh3.T @ h2
-    dg = dh2 * u * silu_grad(g)
-    du = dh2 * silu(g)
+    dg, du = swiglu_backward(g, u, dh2, limit, dec)
     dh1 = np.concatenate([dg, du], axis=1)
     dx = dh1 @ w13
     dw13 = dh1.T @ x_rows
@@ -142,12 +182,13 @@ def expert_ffn_backward(x_rows, w13, w2, h1, dh3):
 # Whole layer
 # --------------------------------------------------------------------------
 
-def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False):
+def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None, act=None):
     """Y[t] = sum over valid k (ascending) of scores[t,k] * h3(t,k) (+ y_addend).
 
     Returns Y [T, D] float64 and, with ``keep``, a cache for ``backward``
     holding the routing metadata, per-row h1, h2 and the route outputs
-    H3S [T*K, D] (zero rows for padding).
+    H3S [T*K, D] (zero rows for padding).  ``limit``/``act``: clamped SwiGLU
+    (see expert_ffn).
     """
     X = as_f64(x)
     S = as_f64(scores)
@@ -167,13 +208,13 @@ def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False):
             continue
         routes = rt["sorted_route"][a:b]
         xe = X[routes // K]
-        h1, h2, h3 = expert_ffn(xe, as_f64(w13[e]), as_f64(w2[e]))
+        h1, h2, h3 = expert_ffn(xe, as_f64(w13[e]), as_f64(w2[e]), limit, act)
         H1[a:b], H2[a:b], H3S[routes] = h1, h2, h3
     Y = combine(H3S, S, ids_a, E)
     if y_addend is not None:
         Y = Y + as_f64(y_addend)
     if keep:
-        return Y, dict(route=rt, H1=H1, H2=H2, H3S=H3S, K=K, E=E)
+        return Y, dict(route=rt, H1=H1, H2=H2, H3S=H3S, K=K, E=E, limit=limit, act=act)
     return Y
 
 
@@ -222,7 +263,8 @@ def backward(dy, x, ids, scores, w13, w2, cache):
         routes = rt["sorted_route"][a:b]
         xe = X[routes // K]
         dxe, dw13e, dw2e, _ = expert_ffn_backward(xe, as_f64(w13[e]), as_f64(w2[e]),
-                                                  cache["H1"][a:b], dH3S[routes])
+                                                  cache["H1"][a:b], dH3S[routes],
+                                                  cache.get("limit"), cache.get("act"))
         dW13[e], dW2[e] = dw13e, dw2e
         dXr[routes] = dxe
     for k in range(K):

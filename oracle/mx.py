@@ -147,35 +147,35 @@ def qdq_32x32(w: np.ndarray) -> np.ndarray:
 # the MXFP8 path feeds to a block-scaled GEMM, fp64 everywhere else.
 # --------------------------------------------------------------------------
 
-def expert_ffn_mx(x_rows, w13q, w2q):
+def expert_ffn_mx(x_rows, w13q, w2q, limit=None):
     """Forward.  x rows (BF16) quantized 1x32 along D after the gather; h1
-    stored BF16; h2 = SiLU(g) * u from it, rounded to BF16 and quantized 1x32
-    along F for the W2 GEMM.  ``w13q``/``w2q`` are 32x32-block dequantized
-    weights.  Returns h1 (BF16 values), h2 (BF16 values) and h3."""
-    from .moe import silu
+    stored BF16; h2 = SiLU(g) * u from it (clamped SwiGLU with ``limit``, see
+    oracle.moe.swiglu), rounded to BF16 and quantized 1x32 along F for the W2
+    GEMM.  ``w13q``/``w2q`` are 32x32-block dequantized weights.  Returns h1
+    (BF16 values), h2 (BF16 values) and h3."""
+    from .moe import swiglu
     F = w2q.shape[1]
     h1 = bf16_round(qdq_rows(x_rows) @ w13q.T)
     g, u = h1[:, :F], h1[:, F:]
-    h2 = bf16_round(silu(g) * u)
+    h2 = bf16_round(swiglu(g, u, limit))
     h3 = qdq_rows(h2) @ w2q.T
     return h1, h2, h3
 
 
-def expert_ffn_backward_mx(x_rows, w13q, w2q, h1, dh3):
+def expert_ffn_backward_mx(x_rows, w13q, w2q, h1, dh3, limit=None):
     """Backward.  ``h1`` is the stored BF16 h1, ``dh3`` the route gradient
     (rounded to BF16 here).  DGRAD operands are quantized along their
     contraction axis (dh3 1x32 along D, dh1 1x32 along 2F) and use the same
     32x32 weight values; WGRAD operands are column bundles (32x1 down the
-    expert's rows) of dh3, h2, dh1 and x."""
-    from .moe import silu, silu_grad
+    expert's rows) of dh3, h2, dh1 and x.  ``limit``: clamped SwiGLU."""
+    from .moe import swiglu, swiglu_backward
     F = w2q.shape[1]
     g, u = h1[:, :F], h1[:, F:]
-    h2 = bf16_round(silu(g) * u)
+    h2 = bf16_round(swiglu(g, u, limit))
     dh3 = bf16_round(dh3)
     dh2 = qdq_rows(dh3) @ w2q
     dw2 = qdq_cols(dh3).T @ qdq_cols(h2)
-    dg = dh2 * u * silu_grad(g)
-    du = dh2 * silu(g)
+    dg, du = swiglu_backward(g, u, dh2, limit)
     dh1 = bf16_round(np.concatenate([dg, du], axis=1))
     dx = qdq_rows(dh1) @ w13q
     dw13 = qdq_cols(dh1).T @ qdq_cols(x_rows)
@@ -225,9 +225,9 @@ def quantize_cols(v):
 # Whole layer, quantization-faithful (same routing and combine as moe.py)
 # --------------------------------------------------------------------------
 
-def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False):
+def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None):
     """MXFP8 layer forward: weights in 32x32 blocks, activations per the
-    expert functions above; combine in fp64."""
+    expert functions above; combine in fp64.  ``limit``: clamped SwiGLU."""
     from . import moe
     X = moe.as_f64(x)
     S = moe.as_f64(scores)
@@ -245,13 +245,13 @@ def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False):
             continue
         routes = rt["sorted_route"][a:b]
         h1, _, h3 = expert_ffn_mx(X[routes // K], qdq_32x32(moe.as_f64(w13[e])),
-                                  qdq_32x32(moe.as_f64(w2[e])))
+                                  qdq_32x32(moe.as_f64(w2[e])), limit)
         H1[a:b], H3S[routes] = h1, h3
     Y = moe.combine(H3S, S, ids_a, E)
     if y_addend is not None:
         Y = Y + moe.as_f64(y_addend)
     if keep:
-        return Y, dict(route=rt, H1=H1, H3S=H3S, K=K, E=E)
+        return Y, dict(route=rt, H1=H1, H3S=H3S, K=K, E=E, limit=limit)
     return Y
 
 
@@ -283,7 +283,7 @@ def backward(dy, x, ids, scores, w13, w2, cache):
         routes = rt["sorted_route"][a:b]
         dxe, dw13e, dw2e, _ = expert_ffn_backward_mx(
             X[routes // K], qdq_32x32(moe.as_f64(w13[e])), qdq_32x32(moe.as_f64(w2[e])),
-            cache["H1"][a:b], dH3S[routes])
+            cache["H1"][a:b], dH3S[routes], cache.get("limit"))
         dW13[e], dW2[e] = dw13e, dw2e
         dXr[routes] = dxe
     for k in range(K):

@@ -156,3 +156,75 @@ def test_max_abs_rel_metric():
     assert moe.max_abs_rel(np.array([1.0, 2.5]), np.array([1.0, 2.0])) == 0.25
     assert moe.max_abs_rel(np.zeros(3), np.zeros(3)) == 0.0
     assert moe.max_abs_rel(np.ones(3), np.zeros(3)) == float("inf")
+
+
+# ---------------------------------------------------------------- clamped SwiGLU
+# (the reading of "clamped SwiGLU" in the Dist-MoE explainer's API section:
+# h2 = SiLU(min(g, L)) * clamp(u, -L, L), no gradient through a clamped value)
+
+def test_clamped_swiglu_worked_values():
+    L = 1.0
+    g = np.array([3.0, 0.5, -2.0, 3.0])
+    u = np.array([-5.0, 0.25, 4.0, 0.5])
+    s1 = 1.0 / (1.0 + np.exp(-1.0))                     # sigmoid(1)
+    s05 = 1.0 / (1.0 + np.exp(-0.5))
+    sm2 = 1.0 / (1.0 + np.exp(2.0))
+    want = np.array([-1.0 * s1,                          # g -> 1, u -> -1
+                     0.5 * s05 * 0.25,                   # inside: plain SwiGLU
+                     -2.0 * sm2 * 1.0,                   # u -> +1 (g below the limit)
+                     1.0 * s1 * 0.5])                    # g -> 1 only
+    np.testing.assert_allclose(moe.swiglu(g, u, L), want, rtol=1e-15)
+    dg, du = moe.swiglu_backward(g, u, np.ones(4), L)
+    np.testing.assert_array_equal(dg[[0, 3]], 0.0)       # clamped gate: no gradient
+    np.testing.assert_array_equal(du[[0, 2]], 0.0)       # clamped up: no gradient
+    np.testing.assert_allclose(dg[1], 0.25 * moe.silu_grad(np.array([0.5]))[0], rtol=1e-15)
+    np.testing.assert_allclose(du[1], 0.5 * s05, rtol=1e-15)
+    np.testing.assert_allclose(du[3], s1, rtol=1e-15)    # d/du of SiLU(1) * u
+
+
+def test_clamped_swiglu_limits_and_decisions():
+    rng = np.random.default_rng(3)
+    g, u = rng.standard_normal(1000) * 3, rng.standard_normal(1000) * 3
+    np.testing.assert_array_equal(moe.swiglu(g, u, 1e30), moe.swiglu(g, u))
+    np.testing.assert_array_equal(moe.swiglu(g, u, 0), moe.swiglu(g, u))   # 0 = plain
+    # the clamp decisions follow ``decide`` (the stored activation), the
+    # values the computation: just above the limit in fp64, at it when stored
+    gg, uu = np.array([1.0 + 1e-9]), np.array([-(1.0 + 1e-9)])
+    h = moe.swiglu(gg, uu, 1.0, decide=(np.array([1.0]), np.array([-1.0])))
+    np.testing.assert_allclose(h, moe.silu(gg) * uu, rtol=1e-15)
+    assert moe.swiglu(gg, uu, 1.0)[0] == moe.silu(np.array([1.0]))[0] * -1.0
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_clamped_backward_matches_finite_differences(seed):
+    rng = np.random.default_rng(10 + seed)
+    T, D, F, E, K = 4, 8, 4, 3, 2
+    x, ids, s, w13, w2 = _rand_layer(rng, T, D, F, E, K, pad=1)
+    dy = rng.standard_normal((T, D))
+    _, cache = moe.forward(x, ids, s, w13, w2, keep=True)
+    L = float(np.median(np.abs(cache["H1"])))            # clamps about half the values
+    g, u = cache["H1"][:, :F], cache["H1"][:, F:]
+    assert 0.2 < np.mean((g > L) | (np.abs(u) > L)) < 0.95
+
+    def loss(x_, s_, w13_, w2_):
+        return float(np.sum(moe.forward(x_, ids, s_, w13_, w2_, limit=L) * dy))
+
+    _, cache = moe.forward(x, ids, s, w13, w2, keep=True, limit=L)
+    dx, dw13, dw2, ds = moe.backward(dy, x, ids, s, w13, w2, cache)
+    h = 1e-7
+    for name, arr, grad in (("x", x, dx), ("w13", w13, dw13), ("w2", w2, dw2), ("s", s, ds)):
+        fd = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            args = {"x": x, "s": s, "w13": w13, "w2": w2}
+            p = arr.copy(); p[i] += h
+            m = arr.copy(); m[i] -= h
+            args_p = dict(args); args_p[name] = p
+            args_m = dict(args); args_m[name] = m
+            fd[i] = (loss(args_p["x"], args_p["s"], args_p["w13"], args_p["w2"])
+                     - loss(args_m["x"], args_m["s"], args_m["w13"], args_m["w2"])) / (2 * h)
+        if name == "s":
+            fd = np.where(ids >= 0, fd, 0.0)
+        err = np.max(np.abs(grad - fd)) / max(np.max(np.abs(fd)), 1e-300)
+        assert err < 1e-5, (name, err)
