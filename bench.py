@@ -57,6 +57,7 @@ WORKLOADS = {
     "bf16_train_zipf": ("bf16_train_zipf", True),
     "mxfp8_train_shared": ("mxfp8_train_shared", True),
     "mxfp8_ten_layer": ("mxfp8_ten_layer", True),
+    "bf16_train_clamped": ("bf16_train_clamped", True),
     "ep8_share": ("ep8_share", True),
     "ep64_share": ("ep64_share", True),
 }
@@ -286,7 +287,8 @@ def setup(args, dev):
         return step, {"": st.layer}, meta, cpu, info, cfg, training
 
     lay = wl.make_layer(cfg, 0, device=dev, grads=training)
-    layer = B.MoeLayer(T, D, F, E, K, cfg.prec, training=training, device=dev)
+    layer = B.MoeLayer(T, D, F, E, K, cfg.prec, training=training, device=dev,
+                       swiglu_limit=cfg.swiglu_limit)
     if cfg.prec == "mxfp8":
         layer.prepare(lay["w13"], lay["w2"])
     act = layer.act_dtype
@@ -502,7 +504,9 @@ def main():
         "config": {"workload": f"{args.workload}: T={cfg.T} D={cfg.D} F={cfg.F} E={cfg.E} "
                                f"K={cfg.K} {'fwd+bwd' if training else 'fwd'}"
                                + (f", {info['layers']} layers" if "layers" in info else "")
-                               + (", + shared BF16 expert" if cfg.shared_expert else ""),
+                               + (", + shared BF16 expert" if cfg.shared_expert else "")
+                               + (f", SwiGLU clamped at {cfg.swiglu_limit:g}"
+                                  if cfg.swiglu_limit else ""),
                    "routes_per_layer": [m["R"] for lab, m in metas if lab == ""],
                    "nonempty_experts": [m["ne"] for lab, m in metas if lab == ""],
                    "max_rows": max(m["max_rows"] for lab, m in metas if lab == ""),
@@ -542,8 +546,12 @@ def cpu_baseline(lay, cfg, training, n_exp, what=""):
     sc = lay["scores"].cpu()
     w13 = lay["w13"][:n_exp].cpu()
     w2 = lay["w2"][:n_exp].cpu()
+    clamp = {}
+    if cfg.swiglu_limit:
+        clamp = {"limit": cfg.swiglu_limit} if cfg.prec == "mxfp8" else \
+            {"limit": cfg.swiglu_limit, "act": omx.bf16_round}
     t0 = time.perf_counter()
-    y, cache = ora.forward(x, ids_s, sc, w13, w2, keep=True)
+    y, cache = ora.forward(x, ids_s, sc, w13, w2, keep=True, **clamp)
     if training:
         ora.backward(lay["dy"].cpu(), x, ids_s, sc, w13, w2, cache)
     dt = time.perf_counter() - t0

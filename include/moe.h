@@ -99,6 +99,12 @@ typedef struct moe_desc {
   int32_t max_layers;       /* layers whose saved state shares one arena (>= 1) */
   int64_t arena_budget;     /* bytes of saved state the arena may hold;
                                0 = enough to save every layer at R = t_max*K */
+  float swiglu_limit;       /* 0: plain SwiGLU.  L > 0: clamped SwiGLU (named
+                               in the explainer's section 08 without a
+                               formula; read here as h2 = SiLU(min(g, L)) *
+                               clamp(u, -L, L), no gradient through a clamped
+                               value, the clamps decided on h1 as stored).
+                               Negative or non-finite -> MOE_ERR_ARG. */
 } moe_desc;
 
 /* Byte sizes of the caller-owned buffers (all 256-byte aligned). */

@@ -43,7 +43,8 @@ class moe_desc(ctypes.Structure):
     _fields_ = [("t_max", ctypes.c_int64), ("d", ctypes.c_int32), ("f", ctypes.c_int32),
                 ("e", ctypes.c_int32), ("k", ctypes.c_int32), ("prec", ctypes.c_int32),
                 ("dw_dtype", ctypes.c_int32), ("training", ctypes.c_int32),
-                ("max_layers", ctypes.c_int32), ("arena_budget", ctypes.c_int64)]
+                ("max_layers", ctypes.c_int32), ("arena_budget", ctypes.c_int64),
+                ("swiglu_limit", ctypes.c_float)]
 
 
 class moe_sizes(ctypes.Structure):
@@ -127,11 +128,12 @@ def _stream(stream=None):
 # ------------------------------------------------------------------ C entry points
 
 def moe_plan_create(t_max, d, f, e, k, prec="bf16", dw_dtype=None, training=False,
-                    max_layers=1, arena_budget=0):
+                    max_layers=1, arena_budget=0, swiglu_limit=0.0):
     if dw_dtype is None:
         dw_dtype = "f32" if prec == "f32" else "bf16"
     desc = moe_desc(int(t_max), int(d), int(f), int(e), int(k), PREC[prec], DTYPE[dw_dtype],
-                    int(bool(training)), int(max_layers), int(arena_budget))
+                    int(bool(training)), int(max_layers), int(arena_budget),
+                    float(swiglu_limit))
     h = _P()
     _check(lib().moe_plan_create(ctypes.byref(desc), ctypes.byref(h)), "moe_plan_create")
     return h
@@ -266,15 +268,16 @@ class MoeLayer:
     """
 
     def __init__(self, T_max, D, F, E, K, prec="bf16", dw_dtype=None, training=False,
-                 max_layers=1, arena_budget=0, device="cuda"):
+                 max_layers=1, arena_budget=0, device="cuda", swiglu_limit=0.0):
         self.T_max, self.D, self.F, self.E, self.K = T_max, D, F, E, K
+        self.swiglu_limit = swiglu_limit
         self.prec, self.training, self.max_layers = prec, training, max_layers
         self.device = torch.device(device)
         self.act_dtype = torch.float32 if prec == "f32" else torch.bfloat16
         self.dw_dtype = (torch.float32 if (dw_dtype or ("f32" if prec == "f32" else "bf16")) == "f32"
                          else torch.bfloat16)
         self.plan = moe_plan_create(T_max, D, F, E, K, prec, dw_dtype, training, max_layers,
-                                    arena_budget)
+                                    arena_budget, swiglu_limit)
         self.sizes = moe_plan_sizes(self.plan)
         self.scratch = _bytes(self.sizes["scratch"], self.device)
         self.arena = _bytes(self.sizes["arena"], self.device) if training else None

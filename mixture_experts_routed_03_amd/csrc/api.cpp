@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -141,6 +142,11 @@ T* at(void* base, int64_t off) {
 // column bundle in training), the W13 grouped GEMM with the SwiGLU epilogue,
 // and the h2 column bundle in training.  replay_only = 1 runs the same
 // launches as backward's replay predicate.
+// Clamped SwiGLU limit for the kernels (+inf: the plain SwiGLU).
+static float swiglu_limit(const moe_plan_s* p) {
+  return p->d.swiglu_limit > 0.0f ? p->d.swiglu_limit : INFINITY;
+}
+
 hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const void* x,
                           const moe_weights* w, int replay_only, int cus, hipStream_t s) {
   const moe_desc& d = p->d;
@@ -170,6 +176,7 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
              reinterpret_cast<const uint8_t*>(w->q13), reinterpret_cast<const uint8_t*>(w->s13),
              nullptr, nullptr, nullptr, sc + L.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, 0, -1,
              replay_only, int(p->R_max)};
+  a13.limit = swiglu_limit(p);
   e = timed(p, replay_only ? "replay_w13" : "w13_swiglu", s,
             [&] { return launch_mx_fwd(0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return e;
@@ -215,6 +222,7 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
              reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
              nullptr, nullptr, sc + L.dh1, nullptr, d.d, d.f, d.f, (d.f + 255) / 256, d.e, 0, 0,
              -1, 0, int(p->R_max)};
+  dg2.limit = swiglu_limit(p);
   dg2.stoff = mtoff;
   e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_mx_dgrad(0, dg2, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -266,6 +274,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   if (d.dw_dtype != MOE_DTYPE_F32 && d.dw_dtype != MOE_DTYPE_BF16) return MOE_ERR_ARG;
   if (d.prec == MOE_PREC_F32 && d.dw_dtype != MOE_DTYPE_F32) return MOE_ERR_ARG;
   if (d.max_layers < 1 || d.arena_budget < 0) return MOE_ERR_ARG;
+  if (!(d.swiglu_limit >= 0.0f) || !(d.swiglu_limit < INFINITY)) return MOE_ERR_ARG;
 
   moe_plan_s* p = new (std::nothrow) moe_plan_s();
   if (!p) return MOE_ERR_ARG;
@@ -374,6 +383,11 @@ moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
                 (long long)d.t_max, d.d, d.f, d.e, d.k, prec,
                 d.dw_dtype == MOE_DTYPE_F32 ? "f32" : "bf16", d.training, d.max_layers);
   s += line;
+  if (d.swiglu_limit > 0.0f) {
+    std::snprintf(line, sizeof line, "  SwiGLU clamped at L=%g (gate <= L, |up| <= L)\n",
+                  double(d.swiglu_limit));
+    s += line;
+  }
   std::snprintf(line, sizeof line, "  routed rows R <= %lld, m-tiles <= %lld (%d rows each)\n",
                 (long long)p->R_max, (long long)p->mt_max, kBM);
   s += line;
@@ -495,6 +509,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     a13.stoff = mtoff;
+    a13.limit = swiglu_limit(p);
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -569,6 +584,7 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
     FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     a13.stoff = mtoff;
+    a13.limit = swiglu_limit(p);
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -632,6 +648,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
               d.d, 2 * d.f, d.f, d.f / 64, d.e, 1, x, d.k};
   a13.stoff = mtoff;
+  a13.limit = swiglu_limit(p);
   e = timed(p, "replay_w13", s, [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = timed(p, "combine_bwd", s, [&] {
@@ -643,6 +660,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   // BwdArgs: hdr, offsets, mtoff, W, tok, grad, arows, out, out2, Kd, N, F, D, E, NT, a_ld, b_ld
   BwdArgs b{hdr, offsets, gtoff, w->w2, dh3, nullptr, nullptr, dh1, h2,
             d.d, d.f, d.f, d.d, d.e, (d.f + 255) / 256, 0, 0, mtoff};
+  b.limit = swiglu_limit(p);
   e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_dgrad(0, b, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw2{hdr, offsets, mtoff, nullptr, nullptr, dh3, h2, g->dw2, nullptr,

@@ -98,6 +98,7 @@ struct FwdArgs {
   const float* scores;
   float* y32;
   const int32_t* stoff;  // 64-row stage prefix (XCD work split, xcd_first_tile)
+  float limit;           // W13: clamped SwiGLU limit (+inf: plain)
 };
 
 // Arguments of the grouped backward GEMM launches.
@@ -118,6 +119,7 @@ struct BwdArgs {
   int a_ld, b_ld;       // WGRAD row lengths of the A rows (= dW row length) and B rows (= dW rows)
   const int32_t* stoff; // DGRAD: 64-row stage prefix (XCD work split); mtoff = the m-tile prefix
   int acc_dw;           // WGRAD: 1 = dW += result (fp32 sum, rounded once), 0 = dW = result
+  float limit;          // W2 DGRAD: clamped SwiGLU limit (+inf: plain)
 };
 
 // Arguments of the MXFP8 grouped GEMM launches.
@@ -145,6 +147,7 @@ struct MxArgs {
   int K;
   const int32_t* stoff;  // DGRAD: 64-row stage prefix (XCD work split); mtoff = the m-tile prefix
   int acc_dw;            // WGRAD: 1 = dW += result (fp32 sum, rounded once), 0 = dW = result
+  float limit;           // W13 FPROP / W2 DGRAD: clamped SwiGLU limit (+inf: plain)
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:
@@ -259,6 +262,14 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ uint16_t from_f(float v) { return f32_to_bf16(v); }
   static __device__ __forceinline__ float round(float v) { return round_bf16(v); }
 };
+
+// Clamped SwiGLU (limit L; L = +inf is the plain SwiGLU): the gate is
+// clamped from above and the up projection to [-L, L] before SiLU(g) * u.
+// Written as comparisons, so a NaN passes through unchanged.
+__device__ __forceinline__ float clamp_gate(float g, float L) { return g > L ? L : g; }
+__device__ __forceinline__ float clamp_up(float u, float L) {
+  return u > L ? L : (u < -L ? -L : u);
+}
 
 // Weight-gradient copy-out: four fp32 results v added to the four dW values
 // at p (in-place accumulation: one rounding of old + v to the dW type).

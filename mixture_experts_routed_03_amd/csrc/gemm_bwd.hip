@@ -260,11 +260,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float dh2 = acc[b][4 * g4 + i];
-            const float sg = sigmoid_f(gv[i]);
-            const float sl = silu_f(gv[i]);
-            dg[i] = dh2 * uv[i] * (sg * (1.0f + gv[i] * (1.0f - sg)));
-            du[i] = dh2 * sl;
-            hv[i] = sl * uv[i];
+            // clamped SwiGLU backward: no gradient through a clamped value
+            const float L = a.limit;
+            const float gc = clamp_gate(gv[i], L), uc = clamp_up(uv[i], L);
+            const float sg = sigmoid_f(gc);
+            const float sl = silu_f(gc);
+            dg[i] = gv[i] > L ? 0.0f : dh2 * uc * (sg * (1.0f + gc * (1.0f - sg)));
+            du[i] = (uv[i] > L || uv[i] < -L) ? 0.0f : dh2 * sl;
+            hv[i] = sl * uc;
           }
           store4<uint16_t>(o + j, dg[0], dg[1], dg[2], dg[3]);
           store4<uint16_t>(o + F + j, du[0], du[1], du[2], du[3]);

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
             for (int v = 0; v < 16; ++v) {
               const float g = Elem<T>::round(acc[b][v]);
               const float up = xch[(wave * 16 + v) * 64 + lane];
-              h[v] = silu_f(g) * up;
+              h[v] = silu_f(clamp_gate(g, a.limit)) * clamp_up(up, a.limit);
             }
             T* o = out1 + int64_t(row0 + m) * F + jcol;
 #pragma unroll

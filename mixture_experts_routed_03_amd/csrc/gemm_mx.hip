@@ -250,7 +250,8 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
             float h[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              h[v] = silu_f(round_bf16(acc[v])) * xch[((wave * 2 + b) * 16 + v) * 64 + lane];
+              h[v] = silu_f(clamp_gate(round_bf16(acc[v]), a.limit)) *
+                     clamp_up(xch[((wave * 2 + b) * 16 + v) * 64 + lane], a.limit);
             uint16_t* o = out1 + int64_t(row0 + m) * F + jcol;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
@@ -480,9 +481,12 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float dh2 = acc[b][4 * g4 + i];
-            const float sg = sigmoid_f(gv[i]);
-            dg[i] = dh2 * uv[i] * (sg * (1.0f + gv[i] * (1.0f - sg)));
-            du[i] = dh2 * silu_f(gv[i]);
+            // clamped SwiGLU backward: no gradient through a clamped value
+            const float L = a.limit;
+            const float gc = clamp_gate(gv[i], L), uc = clamp_up(uv[i], L);
+            const float sg = sigmoid_f(gc);
+            dg[i] = gv[i] > L ? 0.0f : dh2 * uc * (sg * (1.0f + gc * (1.0f - sg)));
+            du[i] = (uv[i] > L || uv[i] < -L) ? 0.0f : dh2 * silu_f(gc);
           }
           store4<uint16_t>(o + j, dg[0], dg[1], dg[2], dg[3]);
           store4<uint16_t>(o + F + j, du[0], du[1], du[2], du[3]);

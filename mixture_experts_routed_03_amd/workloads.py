@@ -152,6 +152,7 @@ class Config:
     shared_expert: bool = False
     seed: int = 0
     note: str = ""
+    swiglu_limit: float = 0.0      # > 0: clamped SwiGLU at this limit
 
     @property
     def n_pad(self) -> int:
@@ -178,6 +179,10 @@ CONFIGS = {
     # One GPU's share of the same routed rows (R = 12,288) under expert
     # parallelism over 8 or 64 GPUs: 48 experts of ~256 rows, or 6 experts
     # of 2,048 rows (every token routes to all six).
+    "bf16_train_clamped": Config("bf16_train_clamped", 2048, 7168, 2048, 384, 6, "bf16",
+                                 training=True, swiglu_limit=1.0,
+                                 note="balanced BF16 training layer with the SwiGLU clamped at "
+                                      "1.0 (about a third of h1 clamped)"),
     "ep8_share": Config("ep8_share", 2048, 7168, 2048, 48, 6, "bf16", training=True,
                         note="EP8 share: 48 experts, ~256 rows each, BF16 forward+backward"),
     "ep64_share": Config("ep64_share", 2048, 7168, 2048, 6, 6, "bf16", training=True,

@@ -68,6 +68,23 @@ def test_plan_rejects_bad_args(b):
     assert ei.value.code == 1
 
 
+@pytest.mark.parametrize("limit", [-1.0, float("inf"), float("nan")])
+def test_plan_rejects_bad_swiglu_limit(b, limit):
+    with pytest.raises(b.MoeError):
+        b.moe_plan_create(16, 256, 128, 8, 2, "bf16", swiglu_limit=limit)
+
+
+def test_plan_explains_clamped_swiglu(b):
+    plain = b.moe_plan_create(16, 256, 128, 8, 2, "bf16")
+    clamped = b.moe_plan_create(16, 256, 128, 8, 2, "bf16", swiglu_limit=7.0)
+    try:
+        assert "clamped" not in b.moe_plan_explain(plain)
+        assert "SwiGLU clamped at L=7" in b.moe_plan_explain(clamped)
+    finally:
+        b.moe_plan_destroy(plain)
+        b.moe_plan_destroy(clamped)
+
+
 def test_calls_reject_before_enqueue(b):
     """Host-detectable errors return before any launch (null stream, no GPU)."""
     plan = b.moe_plan_create(16, 256, 128, 8, 2, "bf16")

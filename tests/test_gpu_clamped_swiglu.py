@@ -1,0 +1,118 @@
+"""GPU parity of the clamped SwiGLU (named in the Dist-MoE explainer's
+section 08 "Supported modes"; read as h2 = SiLU(min(g, L)) * clamp(u, -L, L)
+with no gradient through a clamped value, the clamps decided on h1 as the
+kernel stores it: bf16), through the C ABI against the fp64 oracle.  The limit
+is the median |h1| of the oracle's forward, so about half of the gate and up
+values are clamped."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as om
+from oracle import mx as omx
+from tests._harness import TOL, banner, make_inputs, run_forward, run_train
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_routed_03_amd import binding
+    binding.lib()
+    assert torch.cuda.is_available()
+    return binding
+
+
+def _limit(lay):
+    _, cache = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(),
+                          lay["w2"].cpu(), keep=True)
+    return float(np.median(np.abs(cache["H1"])))
+
+
+def _check_train(lay, outs, limit, mx, tol):
+    y, dx, dw13, dw2, ds = outs
+    torch.cuda.synchronize()
+    if mx:
+        ids = lay["ids"].cpu().numpy()
+        ry, cache = omx.forward(lay["x"], ids, lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                                keep=True, limit=limit)
+        rdx, rdw13, rdw2, rds = omx.backward(lay["dy"], lay["x"], ids, lay["scores"],
+                                             lay["w13"].cpu(), lay["w2"].cpu(), cache)
+    else:
+        ry, cache = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(),
+                               lay["w2"].cpu(), keep=True, limit=limit, act=omx.bf16_round)
+        rdx, rdw13, rdw2, rds = om.backward(lay["dy"], lay["x"], lay["ids"], lay["scores"],
+                                            lay["w13"].cpu(), lay["w2"].cpu(), cache)
+    F = lay["w2"].shape[2]
+    h1 = cache["H1"]
+    frac = np.mean(np.concatenate([(h1[:, :F] > limit).ravel(), (np.abs(h1[:, F:]) > limit).ravel()]))
+    assert 0.3 < frac < 0.7, frac
+    assert om.max_abs_rel(y, ry) < tol
+    assert om.max_abs_rel(dx, rdx) < tol
+    assert om.max_abs_rel(ds, rds) < tol
+    counts = cache["route"]["counts"]
+    for e in range(len(counts)):
+        if counts[e]:
+            assert om.max_abs_rel(dw13[e], rdw13[e]) < tol, e
+            assert om.max_abs_rel(dw2[e], rdw2[e]) < tol, e
+    # the plain SwiGLU gives a different answer on the same inputs
+    assert om.max_abs_rel(y, om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(),
+                                        lay["w2"].cpu())) > 5 * tol
+
+
+@pytest.mark.parametrize("T,D,F,E,K,zipf", [
+    (200, 256, 256, 6, 2, None),
+    (150, 384, 128, 9, 3, 1.2),   # multi-tile hot expert, D = 3 x 128
+])
+def test_bf16_clamped_swiglu_train(B, T, D, F, E, K, zipf):
+    banner(f"bf16 clamped SwiGLU T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
+    lay = make_inputs(T, D, F, E, K, "bf16", zipf=zipf, seed=T + 13, training=True)
+    L = _limit(lay)
+    layer = B.MoeLayer(T, D, F, E, K, "bf16", training=True, swiglu_limit=L)
+    _check_train(lay, run_train(layer, lay), L, False, TOL["bf16"])
+    assert layer.status()[0] == 0
+
+
+def test_mx_clamped_swiglu_train(B):
+    T, D, F, E, K = 160, 256, 256, 5, 2
+    banner(f"mxfp8 clamped SwiGLU T={T} D={D} F={F} E={E} K={K}")
+    lay = make_inputs(T, D, F, E, K, "mxfp8", seed=77, training=True)
+    L = _limit(lay)
+    layer = B.MoeLayer(T, D, F, E, K, "mxfp8", training=True, swiglu_limit=L)
+    _check_train(lay, run_train(layer, lay), L, True, TOL["mxfp8"])
+    assert layer.status()[0] == 0
+
+
+def test_bf16_clamped_swiglu_fused_inference(B):
+    T, D, F, E, K = 128, 256, 128, 8, 2
+    banner("bf16 clamped SwiGLU, fused inference")
+    lay = make_inputs(T, D, F, E, K, "bf16", seed=5)
+    L = _limit(lay)
+    layer = B.MoeLayer(T, D, F, E, K, "bf16", swiglu_limit=L)
+    layer.route(lay["ids"])
+    y = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    layer.forward_fused(lay["x"], lay["w13"], lay["w2"], lay["scores"], y)
+    torch.cuda.synchronize()
+    ry = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                    limit=L, act=omx.bf16_round)
+    assert om.max_abs_rel(y, ry) < TOL["bf16"]
+    y2 = run_forward(layer, lay)                      # the slot path agrees
+    torch.cuda.synchronize()
+    assert om.max_abs_rel(y2, ry) < TOL["bf16"]
+
+
+def test_clamped_replay_matches_saved_state(B):
+    """A layer that replays its forward in backward (no arena room) rebuilds
+    the clamped state bit for bit."""
+    T, D, F, E, K = 120, 256, 256, 5, 2
+    banner("clamped SwiGLU replay vs save")
+    lay = make_inputs(T, D, F, E, K, "bf16", seed=8, training=True)
+    L = _limit(lay)
+    saved = B.MoeLayer(T, D, F, E, K, "bf16", training=True, swiglu_limit=L)
+    a = [t.clone() for t in run_train(saved, lay)]
+    replay = B.MoeLayer(T, D, F, E, K, "bf16", training=True, swiglu_limit=L, arena_budget=128)
+    b = run_train(replay, lay)
+    torch.cuda.synchronize()
+    assert saved.status()[1] == 0 and replay.status()[1] == 1
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
