@@ -95,6 +95,9 @@ def parse():
                     help="experts in the CPU-oracle sample (all their routes); 0 = default "
                          "for the precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--width", type=int, default=0,
+                    help="expert width F for a width sweep (default: the workload's F; "
+                         "a multiple of 128)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference kernel "
                          "for scaling hardware byte counters)")
@@ -239,6 +242,10 @@ def setup(args, dev):
 
     cfg_key, training = WORKLOADS[args.workload]
     cfg = wl.CONFIGS[cfg_key]
+    if args.width:
+        if args.width % 128:
+            raise SystemExit("--width must be a multiple of 128")
+        cfg = wl.scaled(cfg, F=args.width)
     T, D, F, E, K = cfg.T, cfg.D, cfg.F, cfg.E, cfg.K
     bf = torch.bfloat16
 
@@ -457,7 +464,8 @@ def main():
     alg_per_launch = kernels[dom]["alg_bytes_per_step"] / max(1, n_launch)
     ach = kernels[dom]["GB/s"]
     prec_dom = "bf16" if dom.startswith("shared:") else cfg.prec
-    traffic = measured_traffic(args.workload, prec_dom, dom_name)
+    # counters were taken at each workload's own width
+    traffic = None if args.width else measured_traffic(args.workload, prec_dom, dom_name)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": int(alg_per_launch),
