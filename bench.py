@@ -58,6 +58,9 @@ WORKLOADS = {
     "mxfp8_train_shared": ("mxfp8_train_shared", True),
     "mxfp8_ten_layer": ("mxfp8_ten_layer", True),
     "bf16_train_clamped": ("bf16_train_clamped", True),
+    "bf16_decode_t1": ("bf16_decode_t1", False),
+    "bf16_decode_t8": ("bf16_decode_t8", False),
+    "bf16_decode_t64": ("bf16_decode_t64", False),
     "ep8_share": ("ep8_share", True),
     "ep64_share": ("ep64_share", True),
 }

@@ -183,6 +183,12 @@ CONFIGS = {
                                  training=True, swiglu_limit=1.0,
                                  note="balanced BF16 training layer with the SwiGLU clamped at "
                                       "1.0 (about a third of h1 clamped)"),
+    "bf16_decode_t1": Config("bf16_decode_t1", 1, 7168, 2048, 384, 6, "bf16",
+                             note="decode step: one token, six routed experts (one row each)"),
+    "bf16_decode_t8": Config("bf16_decode_t8", 8, 7168, 2048, 384, 6, "bf16",
+                             note="decode step: eight tokens, about one row per active expert"),
+    "bf16_decode_t64": Config("bf16_decode_t64", 64, 7168, 2048, 384, 6, "bf16",
+                              note="decode step: 64 tokens, about one row per expert"),
     "ep8_share": Config("ep8_share", 2048, 7168, 2048, 48, 6, "bf16", training=True,
                         note="EP8 share: 48 experts, ~256 rows each, BF16 forward+backward"),
     "ep64_share": Config("ep64_share", 2048, 7168, 2048, 6, 6, "bf16", training=True,
