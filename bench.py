@@ -58,6 +58,8 @@ WORKLOADS = {
     "mxfp8_train_shared": ("mxfp8_train_shared", True),
     "mxfp8_ten_layer": ("mxfp8_ten_layer", True),
     "bf16_train_clamped": ("bf16_train_clamped", True),
+    "mxfp8_fwd_balanced": ("mxfp8_fwd_balanced", False),
+    "mxfp8_fwd_1x32": ("mxfp8_fwd_1x32", False),
     "bf16_decode_t1": ("bf16_decode_t1", False),
     "bf16_decode_t8": ("bf16_decode_t8", False),
     "bf16_decode_t64": ("bf16_decode_t64", False),
@@ -298,7 +300,7 @@ def setup(args, dev):
 
     lay = wl.make_layer(cfg, 0, device=dev, grads=training)
     layer = B.MoeLayer(T, D, F, E, K, cfg.prec, training=training, device=dev,
-                       swiglu_limit=cfg.swiglu_limit)
+                       swiglu_limit=cfg.swiglu_limit, mx_w1x32=cfg.mx_w1x32)
     if cfg.prec == "mxfp8":
         layer.prepare(lay["w13"], lay["w2"])
     act = layer.act_dtype
@@ -557,10 +559,10 @@ def cpu_baseline(lay, cfg, training, n_exp, what=""):
     sc = lay["scores"].cpu()
     w13 = lay["w13"][:n_exp].cpu()
     w2 = lay["w2"][:n_exp].cpu()
-    clamp = {}
+    clamp = {"w1x32": True} if cfg.mx_w1x32 else {}
     if cfg.swiglu_limit:
-        clamp = {"limit": cfg.swiglu_limit} if cfg.prec == "mxfp8" else \
-            {"limit": cfg.swiglu_limit, "act": omx.bf16_round}
+        clamp.update({"limit": cfg.swiglu_limit} if cfg.prec == "mxfp8" else
+                     {"limit": cfg.swiglu_limit, "act": omx.bf16_round})
     t0 = time.perf_counter()
     y, cache = ora.forward(x, ids_s, sc, w13, w2, keep=True, **clamp)
     if training:

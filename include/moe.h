@@ -79,7 +79,7 @@ typedef enum moe_dtype {
 #define MOE_BWD_ACCUMULATE_DX 0x1u  /* dx += result instead of dx = result */
 /* g->dw13 += result and g->dw2 += result instead of =: the in-place
  * accumulation of weight gradients into the caller's parameter-gradient
- * buffers that the explainer's API section lists among the training
+ * buffers that the explainer's Supported modes section lists among the training
  * options (several micro-batches into one dW).  Each value is summed in fp32
  * and rounded once to the dW type; experts with no rows keep their values.
  * dW is then read as well as written. */
@@ -105,6 +105,12 @@ typedef struct moe_desc {
                                clamp(u, -L, L), no gradient through a clamped
                                value, the clamps decided on h1 as stored).
                                Negative or non-finite -> MOE_ERR_ARG. */
+  int32_t mx_w1x32;         /* MXFP8 inference plans: 1 = weights prepared in
+                               1x32 blocks (one E8M0 exponent per 32 values of
+                               a weight row along the contraction, the
+                               explainer's inference preparation); 0 = 32x32
+                               blocks (training-compatible).  1 with a
+                               training or non-MXFP8 plan -> MOE_ERR_ARG. */
 } moe_desc;
 
 /* Byte sizes of the caller-owned buffers (all 256-byte aligned). */

@@ -44,7 +44,7 @@ class moe_desc(ctypes.Structure):
                 ("e", ctypes.c_int32), ("k", ctypes.c_int32), ("prec", ctypes.c_int32),
                 ("dw_dtype", ctypes.c_int32), ("training", ctypes.c_int32),
                 ("max_layers", ctypes.c_int32), ("arena_budget", ctypes.c_int64),
-                ("swiglu_limit", ctypes.c_float)]
+                ("swiglu_limit", ctypes.c_float), ("mx_w1x32", ctypes.c_int32)]
 
 
 class moe_sizes(ctypes.Structure):
@@ -128,12 +128,12 @@ def _stream(stream=None):
 # ------------------------------------------------------------------ C entry points
 
 def moe_plan_create(t_max, d, f, e, k, prec="bf16", dw_dtype=None, training=False,
-                    max_layers=1, arena_budget=0, swiglu_limit=0.0):
+                    max_layers=1, arena_budget=0, swiglu_limit=0.0, mx_w1x32=False):
     if dw_dtype is None:
         dw_dtype = "f32" if prec == "f32" else "bf16"
     desc = moe_desc(int(t_max), int(d), int(f), int(e), int(k), PREC[prec], DTYPE[dw_dtype],
                     int(bool(training)), int(max_layers), int(arena_budget),
-                    float(swiglu_limit))
+                    float(swiglu_limit), int(bool(mx_w1x32)))
     h = _P()
     _check(lib().moe_plan_create(ctypes.byref(desc), ctypes.byref(h)), "moe_plan_create")
     return h
@@ -268,16 +268,17 @@ class MoeLayer:
     """
 
     def __init__(self, T_max, D, F, E, K, prec="bf16", dw_dtype=None, training=False,
-                 max_layers=1, arena_budget=0, device="cuda", swiglu_limit=0.0):
+                 max_layers=1, arena_budget=0, device="cuda", swiglu_limit=0.0,
+                 mx_w1x32=False):
         self.T_max, self.D, self.F, self.E, self.K = T_max, D, F, E, K
-        self.swiglu_limit = swiglu_limit
+        self.swiglu_limit, self.mx_w1x32 = swiglu_limit, bool(mx_w1x32)
         self.prec, self.training, self.max_layers = prec, training, max_layers
         self.device = torch.device(device)
         self.act_dtype = torch.float32 if prec == "f32" else torch.bfloat16
         self.dw_dtype = (torch.float32 if (dw_dtype or ("f32" if prec == "f32" else "bf16")) == "f32"
                          else torch.bfloat16)
         self.plan = moe_plan_create(T_max, D, F, E, K, prec, dw_dtype, training, max_layers,
-                                    arena_budget, swiglu_limit)
+                                    arena_budget, swiglu_limit, mx_w1x32)
         self.sizes = moe_plan_sizes(self.plan)
         self.scratch = _bytes(self.sizes["scratch"], self.device)
         self.arena = _bytes(self.sizes["arena"], self.device) if training else None
@@ -285,13 +286,20 @@ class MoeLayer:
         self.prepared = None
 
     def prepare(self, w13, w2):
-        """MXFP8: quantize bf16 weights once into E4M3 + 32x32 E8M0 scales."""
+        """MXFP8: quantize bf16 weights once into E4M3 + E8M0 scales, in 32x32
+        blocks, or (mx_w1x32 plans) 1x32 blocks along each weight row with
+        the exponents grouped by 128-value stage: s13 [D/128, E*2F, 4],
+        s2 [F/128, E*D, 4]."""
         E, D, F = self.E, self.D, self.F
         u8 = dict(dtype=torch.uint8, device=self.device)
         q13 = torch.empty((E, 2 * F, D), **u8)
-        s13 = torch.empty((E, 2 * F // 32, D // 32), **u8)
         q2 = torch.empty((E, D, F), **u8)
-        s2 = torch.empty((E, D // 32, F // 32), **u8)
+        if self.mx_w1x32:
+            s13 = torch.empty((D // 128, E * 2 * F, 4), **u8)
+            s2 = torch.empty((F // 128, E * D, 4), **u8)
+        else:
+            s13 = torch.empty((E, 2 * F // 32, D // 32), **u8)
+            s2 = torch.empty((E, D // 32, F // 32), **u8)
         moe_prepare_weights(self.plan, w13, w2, q13, s13, q2, s2)
         self.prepared = (q13, s13, q2, s2)
         return self.prepared

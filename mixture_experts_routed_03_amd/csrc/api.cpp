@@ -177,6 +177,8 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
              nullptr, nullptr, nullptr, sc + L.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, 0, -1,
              replay_only, int(p->R_max)};
   a13.limit = swiglu_limit(p);
+  a13.w1x32 = d.mx_w1x32;
+  a13.sw_rows = d.e * 2 * d.f;
   e = timed(p, replay_only ? "replay_w13" : "w13_swiglu", s,
             [&] { return launch_mx_fwd(0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return e;
@@ -275,6 +277,8 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   if (d.prec == MOE_PREC_F32 && d.dw_dtype != MOE_DTYPE_F32) return MOE_ERR_ARG;
   if (d.max_layers < 1 || d.arena_budget < 0) return MOE_ERR_ARG;
   if (!(d.swiglu_limit >= 0.0f) || !(d.swiglu_limit < INFINITY)) return MOE_ERR_ARG;
+  if (d.mx_w1x32 != 0 && (d.mx_w1x32 != 1 || d.prec != MOE_PREC_MXFP8 || d.training))
+    return MOE_ERR_ARG;
 
   moe_plan_s* p = new (std::nothrow) moe_plan_s();
   if (!p) return MOE_ERR_ARG;
@@ -363,9 +367,10 @@ moe_status moe_plan_sizes(moe_plan_t p, moe_sizes* s) {
   if (p->d.prec == MOE_PREC_MXFP8) {
     const int64_t E = p->d.e, D = p->d.d, F = p->d.f;
     s->q13 = size_t(a256(E * 2 * F * D));
-    s->s13 = size_t(a256(E * 2 * F * D / 1024));
+    // 32x32 blocks: one exponent per 1024 values; 1x32: one per 32
+    s->s13 = size_t(a256(E * 2 * F * D / (p->d.mx_w1x32 ? 32 : 1024)));
     s->q2 = size_t(a256(E * D * F));
-    s->s2 = size_t(a256(E * D * F / 1024));
+    s->s2 = size_t(a256(E * D * F / (p->d.mx_w1x32 ? 32 : 1024)));
   }
   return MOE_OK;
 }
@@ -441,6 +446,20 @@ moe_status moe_prepare_weights(moe_plan_t p, const void* w13, const void* w2, vo
   if (p->d.prec != MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
   if (!w13 || !w2 || !q13 || !s13 || !q2 || !s2) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
+  if (d.mx_w1x32) {
+    // 1x32 blocks: the row quantizer over the weight rows [E*N, Kd], its
+    // exponents grouped by 128-value stage ([Kd/128][E*N] dwords)
+    auto prep = [&](const void* w, void* q, void* sc, int64_t rows, int kd) {
+      RowqArgs r{nullptr, w, reinterpret_cast<uint8_t*>(q), reinterpret_cast<uint8_t*>(sc), kd,
+                 -1, -1, -1, 0, int(rows), nullptr, 0, rows};
+      return launch_rowq(r, rows, s);
+    };
+    hipError_t e = timed(p, "prep_w13", s,
+                         [&] { return prep(w13, q13, s13, int64_t(d.e) * 2 * d.f, d.d); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(
+        timed(p, "prep_w2", s, [&] { return prep(w2, q2, s2, int64_t(d.e) * d.d, d.f); }));
+  }
   hipError_t e = timed(p, "prep_w13", s, [&] {
     return launch_prep_w(w13, q13, s13, d.e, 2 * d.f, d.d, s);
   });
@@ -531,6 +550,8 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
             reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
             nullptr, nullptr, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
             int(p->R_max)};
+  a2.w1x32 = d.mx_w1x32;
+  a2.sw_rows = d.e * d.d;
   return hip_status(timed(p, "w2_scatter", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); }));
 }
 
@@ -604,6 +625,8 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
               reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
               nullptr, nullptr, nullptr, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
               int(p->R_max), scores, y32, d.k};
+    a2.w1x32 = d.mx_w1x32;
+    a2.sw_rows = d.e * d.d;
     e = timed(p, "w2_fused", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); });
   }
   if (e != hipSuccess) return MOE_ERR_HIP;

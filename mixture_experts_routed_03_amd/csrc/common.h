@@ -148,6 +148,9 @@ struct MxArgs {
   const int32_t* stoff;  // DGRAD: 64-row stage prefix (XCD work split); mtoff = the m-tile prefix
   int acc_dw;            // WGRAD: 1 = dW += result (fp32 sum, rounded once), 0 = dW = result
   float limit;           // W13 FPROP / W2 DGRAD: clamped SwiGLU limit (+inf: plain)
+  int w1x32;             // FPROP: weights in 1x32 blocks, exponents grouped by 128-value
+                         // stage: dword (s, e*N + n) of [Kd/128][sw_rows] (see k_rowq)
+  int sw_rows;           // E * N for w1x32
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:
@@ -165,6 +168,7 @@ struct RowqArgs {
                         // are consecutive dwords)
   const int32_t* gather;  // non-null: source row r is src[gather[r] / K] (src = x [T, N])
   int K;
+  int64_t rows;         // > 0: rows to quantize (hdr unused); 0: the route header's R
 };
 struct ColqArgs {
   const RouteHdr* hdr;

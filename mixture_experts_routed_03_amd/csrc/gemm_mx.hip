@@ -81,12 +81,17 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
 }
 
 // ------------------------------------------------------------------ forward
-template <int MODE>
+// W1: weights prepared in 1x32 blocks (inference): every weight row has its
+// own exponent per 32 values, so each lane takes the exponents of its own
+// row (one dword per stage, staged through LDS like the token exponents)
+// instead of the wave's 32x32-block exponents.
+template <int MODE, int W1>
 __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   constexpr int kW = 128 * 128;      // weight stage: 128 rows x 128 E4M3 values
   constexpr int kA = kBM * 128;      // token stage: 64 rows x 128 values
   constexpr int kSc = kBM * 4;       // token scales of the stage: 4 blocks per row
-  constexpr int kStage = kW + kA + kSc + 16;   // + the weight scale dword of each wave
+  // + the weight exponents: one dword per wave (32x32) or per weight row (1x32)
+  constexpr int kStage = kW + kA + kSc + (W1 ? 128 * 4 : 16);
   __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,8 +138,13 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     // the 32 weight rows of this wave form one 32-row scale block
     const int wrow0 = MODE == 0 ? ((wave < 2 ? 0 : a.F) + nt * 64 + (wave & 1) * 32)
                                 : nt * 128 + wave * 32;
-    const uint32_t* wsc_src = reinterpret_cast<const uint32_t*>(
-        a.sw + (int64_t(e) * (a.N / 32) + wrow0 / 32) * KB);
+    // 1x32: thread tid < 128 fetches the exponent dword of tile row tid
+    const int wr1 = MODE == 0 ? ((tid & 127) < 64 ? nt * 64 + (tid & 63)
+                                                  : a.F + nt * 64 + (tid & 63))
+                              : nt * 128 + (tid & 127);
+    const uint32_t* wsc_src =
+        W1 ? reinterpret_cast<const uint32_t*>(a.sw) + int64_t(e) * a.N + wr1
+           : reinterpret_cast<const uint32_t*>(a.sw + (int64_t(e) * (a.N / 32) + wrow0 / 32) * KB);
     // Tile rows past the expert's last row re-read that row: every load is
     // unconditional, and the extra output columns are never stored.
     const uint8_t* tsrc[2];
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
         R[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + off));
 #pragma unroll
       for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
-      Sc[0] = wsc_src[s];
+      Sc[0] = W1 ? wsc_src[int64_t(s) * a.sw_rows] : wsc_src[s];
       Sc[1] = tsc_src[int64_t(s) * a.sa_rows];
     };
     auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
@@ -166,7 +176,11 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
       for (int j = 0; j < 2; ++j)
         *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
       if (tid < kBM) reinterpret_cast<uint32_t*>(base + kW + kA)[tid] = Sc[1];
-      if (lane == 0) reinterpret_cast<uint32_t*>(base + kW + kA + kSc)[wave] = Sc[0];
+      if (W1) {
+        if (tid < 128) reinterpret_cast<uint32_t*>(base + kW + kA + kSc)[tid] = Sc[0];
+      } else if (lane == 0) {
+        reinterpret_cast<uint32_t*>(base + kW + kA + kSc)[wave] = Sc[0];
+      }
     };
     // Both 32-token halves are always multiplied: no accumulator depends on
     // a branch inside the stage loop.
@@ -176,7 +190,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
       const uint32_t* tsc = reinterpret_cast<const uint32_t*>(tl + kA);
       const uint32_t ts0 = tsc[lr];
       const uint32_t ts1 = tsc[32 + lr];
-      const uint32_t wsc = tsc[kBM + wave];
+      const uint32_t wsc = W1 ? tsc[kBM + 32 * wave + lr] : tsc[kBM + wave];
       const int wrow = 32 * wave + lr;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -729,13 +743,16 @@ static unsigned grid_m(int per_cu, int64_t items, int cus) {
 // mode 0: W13 (+ SwiGLU), 1: W2 -> slots
 hipError_t launch_mx_fwd(int mode, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s) {
   if (mt_max == 0) return hipSuccess;
+#define MOE_MXF(M, W, ID)                                                                   \
+  hipLaunchKernelGGL((k_mx_fwd<M, W>),                                                     \
+                     dim3(grid_m(occupancy_m<ID>(k_mx_fwd<M, W>), mt_max * a.NT, cus)), \
+                     dim3(256), 0, s, a)
   if (mode == 0) {
-    hipLaunchKernelGGL(k_mx_fwd<0>, dim3(grid_m(occupancy_m<0>(k_mx_fwd<0>), mt_max * a.NT, cus)),
-                       dim3(256), 0, s, a);
+    if (a.w1x32) MOE_MXF(0, 1, 12); else MOE_MXF(0, 0, 0);
   } else {
-    hipLaunchKernelGGL(k_mx_fwd<1>, dim3(grid_m(occupancy_m<1>(k_mx_fwd<1>), mt_max * a.NT, cus)),
-                       dim3(256), 0, s, a);
+    if (a.w1x32) MOE_MXF(1, 1, 13); else MOE_MXF(1, 0, 1);
   }
+#undef MOE_MXF
   return hipGetLastError();
 }
 

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
   if (a.replay_only && !hdr->rec.replay) return;
   const int lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= hdr->R) return;
+  if (row >= (a.rows > 0 ? a.rows : int64_t(hdr->R))) return;
   const uint16_t* src = a.src_slot >= 0 ? global_ptr<const uint16_t>(rec_ptr(hdr, a.src_slot))
                                          : reinterpret_cast<const uint16_t*>(a.src);
   uint8_t* q = a.q_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.q_slot)) : a.q;

@@ -153,6 +153,7 @@ class Config:
     seed: int = 0
     note: str = ""
     swiglu_limit: float = 0.0      # > 0: clamped SwiGLU at this limit
+    mx_w1x32: bool = False         # MXFP8 inference with 1x32-block prepared weights
 
     @property
     def n_pad(self) -> int:
@@ -183,6 +184,10 @@ CONFIGS = {
                                  training=True, swiglu_limit=1.0,
                                  note="balanced BF16 training layer with the SwiGLU clamped at "
                                       "1.0 (about a third of h1 clamped)"),
+    "mxfp8_fwd_balanced": Config("mxfp8_fwd_balanced", 2048, 7168, 2048, 384, 6, "mxfp8",
+                                 note="MXFP8 inference forward, 32x32-block weights"),
+    "mxfp8_fwd_1x32": Config("mxfp8_fwd_1x32", 2048, 7168, 2048, 384, 6, "mxfp8", mx_w1x32=True,
+                             note="MXFP8 inference forward, 1x32-block weights"),
     "bf16_decode_t1": Config("bf16_decode_t1", 1, 7168, 2048, 384, 6, "bf16",
                              note="decode step: one token, six routed experts (one row each)"),
     "bf16_decode_t8": Config("bf16_decode_t8", 8, 7168, 2048, 384, 6, "bf16",

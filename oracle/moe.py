@@ -105,8 +105,8 @@ def silu_grad(z: np.ndarray) -> np.ndarray:
     return s * (1.0 + z * (1.0 - s))
 
 
-# Clamped SwiGLU.  The Dist-MoE explainer's API section lists "plain and
-# clamped SwiGLU" without a formula; the reading taken here is the plainest
+# Clamped SwiGLU.  The Dist-MoE explainer's Supported modes section names a
+# clamped SwiGLU beside the plain one, without a formula; the reading taken here is the plainest
 # one: before the activation the gate is clamped from above and the up
 # projection to [-L, L], h2 = SiLU(min(g, L)) * clamp(u, -L, L), and a
 # clamped value passes no gradient (dg = 0 where g > L, du = 0 where |u| > L).

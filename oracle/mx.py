@@ -225,9 +225,12 @@ def quantize_cols(v):
 # Whole layer, quantization-faithful (same routing and combine as moe.py)
 # --------------------------------------------------------------------------
 
-def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None):
-    """MXFP8 layer forward: weights in 32x32 blocks, activations per the
-    expert functions above; combine in fp64.  ``limit``: clamped SwiGLU."""
+def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None, w1x32=False):
+    """MXFP8 layer forward: weights in 32x32 blocks (``w1x32``: 1x32 blocks
+    along each weight row, the inference preparation the Dist-MoE explainer's
+    Supported modes section names beside the training-compatible 32x32), activations per
+    the expert functions above; combine in fp64.  ``limit``: clamped SwiGLU."""
+    wq = qdq_rows if w1x32 else qdq_32x32
     from . import moe
     X = moe.as_f64(x)
     S = moe.as_f64(scores)
@@ -244,8 +247,8 @@ def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None):
         if a == b:
             continue
         routes = rt["sorted_route"][a:b]
-        h1, _, h3 = expert_ffn_mx(X[routes // K], qdq_32x32(moe.as_f64(w13[e])),
-                                  qdq_32x32(moe.as_f64(w2[e])), limit)
+        h1, _, h3 = expert_ffn_mx(X[routes // K], wq(moe.as_f64(w13[e])),
+                                  wq(moe.as_f64(w2[e])), limit)
         H1[a:b], H3S[routes] = h1, h3
     Y = moe.combine(H3S, S, ids_a, E)
     if y_addend is not None:

@@ -85,6 +85,22 @@ def test_plan_explains_clamped_swiglu(b):
         b.moe_plan_destroy(clamped)
 
 
+def test_plan_1x32_weights_only_for_mxfp8_inference(b):
+    for kw in (dict(prec="bf16"), dict(prec="mxfp8", training=True)):
+        with pytest.raises(b.MoeError):
+            b.moe_plan_create(16, 256, 128, 8, 2, mx_w1x32=True, **kw)
+    p32 = b.moe_plan_create(16, 256, 128, 8, 2, "mxfp8")
+    p1 = b.moe_plan_create(16, 256, 128, 8, 2, "mxfp8", mx_w1x32=True)
+    try:
+        s32, s1 = b.moe_plan_sizes(p32), b.moe_plan_sizes(p1)
+        assert s1["q13"] == s32["q13"] == 8 * 256 * 256
+        assert s32["s13"] == 8 * 256 * 256 // 1024 and s1["s13"] == 8 * 256 * 256 // 32
+        assert s1["s2"] == 8 * 256 * 128 // 32
+    finally:
+        b.moe_plan_destroy(p32)
+        b.moe_plan_destroy(p1)
+
+
 def test_calls_reject_before_enqueue(b):
     """Host-detectable errors return before any launch (null stream, no GPU)."""
     plan = b.moe_plan_create(16, 256, 128, 8, 2, "bf16")

@@ -1,0 +1,58 @@
+"""MXFP8 inference with weights prepared in 1x32 blocks (one E8M0 exponent
+per 32 values of a weight row along the contraction: the inference
+preparation the Dist-MoE explainer's Supported modes section names beside the
+training-compatible 32x32 blocks).  Preparation bit-exact against the oracle's
+row quantizer; forward (slot and FUSED combine) against the
+quantization-faithful oracle with 1x32 weights."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as om
+from oracle import mx as omx
+from tests._harness import TOL, banner, make_inputs, run_forward
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_routed_03_amd import binding
+    binding.lib()
+    assert torch.cuda.is_available()
+    return binding
+
+
+def _check_prepared(q, s, w):
+    """q [E, N, Kd] codes; s [Kd/128, E*N, 4] exponents + 127 (stage-grouped)."""
+    E, N, Kd = w.shape
+    rq, re = omx.quantize_rows(om.as_f64(w).reshape(E * N, Kd))
+    np.testing.assert_array_equal(q.cpu().numpy().reshape(E * N, Kd), rq)
+    got = s.cpu().numpy().astype(np.int64)                  # [Kd/128, E*N, 4]
+    got = got.transpose(1, 0, 2).reshape(E * N, Kd // 32)    # [E*N, Kd/32]
+    np.testing.assert_array_equal(got, re + 127)
+
+
+@pytest.mark.parametrize("T,D,F,E,K,zipf,n_pad", [
+    (300, 256, 256, 8, 2, None, 7),
+    (200, 384, 128, 10, 3, 1.3, 0),     # skew, D = 3 x 128, empty experts likely
+])
+def test_mx_1x32_forward_matches_oracle(B, T, D, F, E, K, zipf, n_pad):
+    banner(f"mx 1x32 forward T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
+    lay = make_inputs(T, D, F, E, K, "mxfp8", zipf=zipf, n_pad=n_pad, seed=T + 17)
+    layer = B.MoeLayer(T, D, F, E, K, "mxfp8", mx_w1x32=True)
+    q13, s13, q2, s2 = layer.prepare(lay["w13"], lay["w2"])
+    torch.cuda.synchronize()
+    _check_prepared(q13, s13, lay["w13"])
+    _check_prepared(q2, s2, lay["w2"])
+    y = run_forward(layer, lay)
+    torch.cuda.synchronize()
+    ref = omx.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                      w1x32=True)
+    assert om.max_abs_rel(y, ref) < TOL["mxfp8"]
+    assert layer.status()[0] == 0
+    # the FUSED combine reads the same prepared weights
+    yf = torch.empty_like(y)
+    layer.forward_fused(lay["x"], lay["w13"], lay["w2"], lay["scores"], yf)
+    torch.cuda.synchronize()
+    assert om.max_abs_rel(yf, ref) < TOL["mxfp8"]
