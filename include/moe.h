@@ -79,8 +79,8 @@ typedef enum moe_dtype {
 #define MOE_BWD_ACCUMULATE_DX 0x1u  /* dx += result instead of dx = result */
 /* g->dw13 += result and g->dw2 += result instead of =: the in-place
  * accumulation of weight gradients into the caller's parameter-gradient
- * buffers that the explainer's Supported modes section lists among the training
- * options (several micro-batches into one dW).  Each value is summed in fp32
+ * buffers that the explainx.ai post on Dist-MoE lists under Supported modes
+ * among the training options (several micro-batches into one dW).  Each value is summed in fp32
  * and rounded once to the dW type; experts with no rows keep their values.
  * dW is then read as well as written. */
 #define MOE_BWD_ACCUMULATE_DW 0x2u
@@ -100,15 +100,16 @@ typedef struct moe_desc {
   int64_t arena_budget;     /* bytes of saved state the arena may hold;
                                0 = enough to save every layer at R = t_max*K */
   float swiglu_limit;       /* 0: plain SwiGLU.  L > 0: clamped SwiGLU (named
-                               in the explainer's section 08 without a
-                               formula; read here as h2 = SiLU(min(g, L)) *
+                               under Supported modes in the explainx.ai
+                               post on Dist-MoE, no formula; read here as h2 = SiLU(min(g, L)) *
                                clamp(u, -L, L), no gradient through a clamped
                                value, the clamps decided on h1 as stored).
                                Negative or non-finite -> MOE_ERR_ARG. */
   int32_t mx_w1x32;         /* MXFP8 inference plans: 1 = weights prepared in
                                1x32 blocks (one E8M0 exponent per 32 values of
                                a weight row along the contraction, the
-                               explainer's inference preparation); 0 = 32x32
+                               inference preparation of the explainx.ai
+                               post's Supported modes); 0 = 32x32
                                blocks (training-compatible).  1 with a
                                training or non-MXFP8 plan -> MOE_ERR_ARG. */
 } moe_desc;

@@ -105,15 +105,16 @@ def silu_grad(z: np.ndarray) -> np.ndarray:
     return s * (1.0 + z * (1.0 - s))
 
 
-# Clamped SwiGLU.  The Dist-MoE explainer's Supported modes section names a
-# clamped SwiGLU beside the plain one, without a formula; the reading taken here is the plainest
+# Clamped SwiGLU.  The Supported modes section of the explainx.ai post "Meta
+# Dist-MoE: Open-Source Fused MoE Kernels for Blackwell" names a clamped SwiGLU
+# beside the plain one, without a formula; the reading taken here is the plainest
 # one: before the activation the gate is clamped from above and the up
 # projection to [-L, L], h2 = SiLU(min(g, L)) * clamp(u, -L, L), and a
 # clamped value passes no gradient (dg = 0 where g > L, du = 0 where |u| > L).
 # Each clamp is a decision at a threshold, so it is taken on the values the
 # kernel decides on: ``decide`` = (g, u) as stored in the activation dtype
 # (default: g, u themselves).  limit None or 0 is the plain SwiGLU.
-#   ([DM] s.08 "Supported modes"; SiLU and its derivative from [GG] s.1, s.2.)
+#   (SiLU and its derivative from [GG] s.1, s.2.)
 
 def _clamped(g, u, limit, decide):
     if not limit:

@@ -227,8 +227,8 @@ def quantize_cols(v):
 
 def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None, w1x32=False):
     """MXFP8 layer forward: weights in 32x32 blocks (``w1x32``: 1x32 blocks
-    along each weight row, the inference preparation the Dist-MoE explainer's
-    Supported modes section names beside the training-compatible 32x32), activations per
+    along each weight row, the inference preparation that the Supported modes
+    section of the explainx.ai post on Dist-MoE names beside the training-compatible 32x32), activations per
     the expert functions above; combine in fp64.  ``limit``: clamped SwiGLU."""
     wq = qdq_rows if w1x32 else qdq_32x32
     from . import moe

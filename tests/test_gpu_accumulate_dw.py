@@ -1,6 +1,6 @@
 """GPU parity of in-place weight-gradient accumulation (MOE_BWD_ACCUMULATE_DW,
 the optional accumulation of weight gradients into the caller's parameter
-gradient buffers listed in the Dist-MoE explainer's Supported modes section): starting
+gradient buffers listed under Supported modes in the explainx.ai post on Dist-MoE): starting
 from a random dW, the backward must leave dW_start + dW, with dW the oracle's
 weight gradient of the step (summed in fp32, rounded once), and must leave the
 dW of experts without rows bit-for-bit unchanged."""

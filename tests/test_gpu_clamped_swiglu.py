@@ -1,5 +1,5 @@
-"""GPU parity of the clamped SwiGLU (named in the Dist-MoE explainer's
-section 08 "Supported modes"; read as h2 = SiLU(min(g, L)) * clamp(u, -L, L)
+"""GPU parity of the clamped SwiGLU (named under Supported modes in the
+explainx.ai post on Dist-MoE; read as h2 = SiLU(min(g, L)) * clamp(u, -L, L)
 with no gradient through a clamped value, the clamps decided on h1 as the
 kernel stores it: bf16), through the C ABI against the fp64 oracle.  The limit
 is the median |h1| of the oracle's forward, so about half of the gate and up

@@ -1,6 +1,6 @@
 """MXFP8 inference with weights prepared in 1x32 blocks (one E8M0 exponent
 per 32 values of a weight row along the contraction: the inference
-preparation the Dist-MoE explainer's Supported modes section names beside the
+preparation the explainx.ai post on Dist-MoE names in Supported modes beside the
 training-compatible 32x32 blocks).  Preparation bit-exact against the oracle's
 row quantizer; forward (slot and FUSED combine) against the
 quantization-faithful oracle with 1x32 weights."""

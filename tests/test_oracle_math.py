@@ -159,7 +159,7 @@ def test_max_abs_rel_metric():
 
 
 # ---------------------------------------------------------------- clamped SwiGLU
-# (the reading of the clamped SwiGLU named in the Dist-MoE explainer's Supported modes section:
+# (the reading of the clamped SwiGLU named under Supported modes in the explainx.ai post on Dist-MoE:
 # h2 = SiLU(min(g, L)) * clamp(u, -L, L), no gradient through a clamped value)
 
 def test_clamped_swiglu_worked_values():
