@@ -45,7 +45,7 @@ import sys
 import time
 
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "f32": 157.3}
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "mixture_experts_routed_03_amd", "csrc")
 
@@ -60,13 +60,14 @@ WORKLOADS = {
     "bf16_train_clamped": ("bf16_train_clamped", True),
     "mxfp8_fwd_balanced": ("mxfp8_fwd_balanced", False),
     "mxfp8_fwd_1x32": ("mxfp8_fwd_1x32", False),
+    "mxfp4_fwd_balanced": ("mxfp4_fwd_balanced", False),
     "bf16_decode_t1": ("bf16_decode_t1", False),
     "bf16_decode_t8": ("bf16_decode_t8", False),
     "bf16_decode_t64": ("bf16_decode_t64", False),
     "ep8_share": ("ep8_share", True),
     "ep64_share": ("ep64_share", True),
 }
-CPU_EXPERTS = {"bf16": 96, "mxfp8": 3}
+CPU_EXPERTS = {"bf16": 96, "mxfp8": 3, "mxfp4": 3}
 
 # Library timing name -> (kernel symbol in rocprofv3 traces, per precision;
 # source files that define it).
@@ -86,6 +87,10 @@ SYMBOLS = {
         "w13_dgrad": ("moe::k_mx_dgrad<1>", ["gemm_mx.hip"]),
         "w2_wgrad": ("moe::k_mx_wgrad<unsigned short, 2>", ["gemm_mx.hip"]),
         "w13_wgrad": ("moe::k_mx_wgrad<unsigned short, 13>", ["gemm_mx.hip"]),
+    },
+    "mxfp4": {
+        "w13_swiglu": ("moe::k_mx_fwd<0, 1, 1>", ["gemm_mx.hip"]),
+        "w2_scatter": ("moe::k_mx_fwd<1, 1, 1>", ["gemm_mx.hip"]),
     },
 }
 
@@ -119,6 +124,7 @@ def alg_bytes(name, m):
     bundles only for a layer that saves."""
     R, Rp, ne, T, K, D, F = m["R"], m["Rp"], m["ne"], m["T"], m["K"], m["D"], m["F"]
     es, dwb, mx, rep = m["es"], m["dwb"], m["mx"], m["replay"]
+    ab, wb = m["ab"], m["wb"]     # bytes per quantized activation / weight value
     if name.startswith("replay_"):
         if not rep:
             return 0
@@ -126,10 +132,9 @@ def alg_bytes(name, m):
     elif name in ("bundle_x", "bundle_h2") and rep:
         return 0
 
-    def q(n):  # E4M3 codes plus one E8M0 byte per 32 values
-        return n + n // 32
+    def q(n):  # E4M3 (or packed E2M1) codes plus one E8M0 byte per 32 values
+        return int(n * ab) + n // 32
 
-    wb = (1 + 1 / 1024) if mx else es          # weight bytes per value (32x32 scales)
     w13 = int(ne * 2 * F * D * wb)
     w2 = int(ne * D * F * wb)
     common = {
@@ -232,7 +237,13 @@ def layer_meta(layer, rb, replay, T):
             "T": T, "K": layer.K, "D": layer.D, "F": layer.F,
             "es": 4 if layer.prec == "f32" else 2,
             "dwb": 4 if layer.dw_dtype.itemsize == 4 else 2,
-            "mx": layer.prec == "mxfp8", "replay": bool(replay),
+            "mx": layer.prec in ("mxfp8", "mxfp4"), "replay": bool(replay),
+            # bytes per value of quantized activations and of weights (codes +
+            # exponents: 32x32 blocks one per 1024 values, 1x32 one per 32)
+            "ab": 0.5 if layer.prec == "mxfp4" else 1.0,
+            "wb": (0.5 + 1 / 32 if layer.prec == "mxfp4" else
+                   1 + 1 / 32 if layer.mx_w1x32 else 1 + 1 / 1024)
+                  if layer.prec in ("mxfp8", "mxfp4") else (4 if layer.prec == "f32" else 2),
             "max_rows": int(counts.max()) if counts.size else 0}
 
 
@@ -301,7 +312,7 @@ def setup(args, dev):
     lay = wl.make_layer(cfg, 0, device=dev, grads=training)
     layer = B.MoeLayer(T, D, F, E, K, cfg.prec, training=training, device=dev,
                        swiglu_limit=cfg.swiglu_limit, mx_w1x32=cfg.mx_w1x32)
-    if cfg.prec == "mxfp8":
+    if cfg.prec in ("mxfp8", "mxfp4"):
         layer.prepare(lay["w13"], lay["w2"])
     act = layer.act_dtype
     y = torch.empty((T, D), dtype=act, device=dev)
@@ -351,7 +362,7 @@ def setup(args, dev):
 
     def cpu():
         return cpu_baseline(lay, cfg, training,
-                            args.cpu_experts or CPU_EXPERTS["mxfp8" if cfg.prec == "mxfp8" else "bf16"],
+                            args.cpu_experts or CPU_EXPERTS.get(cfg.prec, CPU_EXPERTS["bf16"]),
                             "routed experts only, " if shared is not None else "")
 
     return step, plans, meta, cpu, {}, cfg, training
@@ -550,8 +561,9 @@ def cpu_baseline(lay, cfg, training, n_exp, what=""):
 
     from oracle import moe as om
     from oracle import mx as omx
+    from oracle import mxfp4 as o4
 
-    ora = omx if cfg.prec == "mxfp8" else om
+    ora = {"mxfp8": omx, "mxfp4": o4}.get(cfg.prec, om)
     ids = lay["ids"].cpu().numpy()
     ids_s = np.where((ids >= 0) & (ids < n_exp), ids, -1).astype(np.int32)
     R_s = int((ids_s >= 0).sum())
@@ -561,11 +573,14 @@ def cpu_baseline(lay, cfg, training, n_exp, what=""):
     w2 = lay["w2"][:n_exp].cpu()
     clamp = {"w1x32": True} if cfg.mx_w1x32 else {}
     if cfg.swiglu_limit:
-        clamp.update({"limit": cfg.swiglu_limit} if cfg.prec == "mxfp8" else
+        clamp.update({"limit": cfg.swiglu_limit} if cfg.prec in ("mxfp8", "mxfp4") else
                      {"limit": cfg.swiglu_limit, "act": omx.bf16_round})
+    if cfg.prec != "mxfp4":
+        clamp["keep"] = True
     t0 = time.perf_counter()
-    y, cache = ora.forward(x, ids_s, sc, w13, w2, keep=True, **clamp)
+    out = ora.forward(x, ids_s, sc, w13, w2, **clamp)
     if training:
+        y, cache = out
         ora.backward(lay["dy"].cpu(), x, ids_s, sc, w13, w2, cache)
     dt = time.perf_counter() - t0
     try:
@@ -579,7 +594,8 @@ def cpu_baseline(lay, cfg, training, n_exp, what=""):
             "sample": f"{what}routes of experts 0..{n_exp - 1} ({R_s} of "
                       f"{int((ids >= 0).sum())} routes), "
                       f"{'forward+backward' if training else 'forward'}, fp64 NumPy"
-                      + (", quantization-faithful MXFP8" if cfg.prec == "mxfp8" else "")}
+                      + (f", quantization-faithful {cfg.prec.upper()}"
+                         if cfg.prec in ("mxfp8", "mxfp4") else "")}
 
 
 if __name__ == "__main__":

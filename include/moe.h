@@ -25,7 +25,8 @@
  * Conventions for every call
  *  - All tensors are contiguous, row-major, in device memory (HBM) unless a
  *    parameter says "host".  Activations and weights are float32 for
- *    MOE_PREC_F32 and bfloat16 for MOE_PREC_BF16 / MOE_PREC_MXFP8.
+ *    MOE_PREC_F32 and bfloat16 for MOE_PREC_BF16 / MOE_PREC_MXFP8 /
+ *    MOE_PREC_MXFP4.
  *  - The caller owns every buffer and allocates it with the sizes reported
  *    by moe_plan_sizes; the library never allocates or frees device memory
  *    and keeps no pointer after a call returns.
@@ -61,7 +62,14 @@ typedef enum moe_status {
 typedef enum moe_prec {
   MOE_PREC_F32 = 0,         /* fp32 operands, fp32 MFMA */
   MOE_PREC_BF16 = 1,        /* bf16 operands, fp32 accumulation */
-  MOE_PREC_MXFP8 = 2        /* E4M3 operands with E8M0 scales per 32 values */
+  MOE_PREC_MXFP8 = 2,       /* E4M3 operands with E8M0 scales per 32 values */
+  MOE_PREC_MXFP4 = 3        /* inference only: E2M1 operands (two per byte, low
+                               nibble first) with E8M0 scales per 32 values,
+                               weights prepared in 1x32 blocks; D and F
+                               multiples of 256.  The OCP-MX counterpart of the
+                               4-bit inference mode of the Dist-MoE explainer
+                               (section 02; section 08's support table: 4-bit
+                               is inference-only with prepared weights). */
 } moe_prec;
 
 typedef enum moe_dtype {
@@ -86,7 +94,9 @@ typedef enum moe_dtype {
 #define MOE_BWD_ACCUMULATE_DW 0x2u
 
 /* Layer description.  Supported: D % 128 == 0, F % 128 == 0, 1 <= K <= 16,
- * K <= E <= 4096, 0 <= t_max <= 2^24 / K. */
+ * K <= E <= 4096, 0 <= t_max <= 2^24 / K (else MOE_ERR_SHAPE).  MXFP4:
+ * D % 256 == 0 and F % 256 == 0 (else MOE_ERR_SHAPE), training 0 (else
+ * MOE_ERR_ARG). */
 typedef struct moe_desc {
   int64_t t_max;            /* most tokens any call will pass */
   int32_t d;                /* token width D */
@@ -111,7 +121,8 @@ typedef struct moe_desc {
                                inference preparation of the explainx.ai
                                post's Supported modes); 0 = 32x32
                                blocks (training-compatible).  1 with a
-                               training or non-MXFP8 plan -> MOE_ERR_ARG. */
+                               training or non-MXFP8 plan -> MOE_ERR_ARG
+                               (MXFP4 weights are always 1x32: leave 0). */
 } moe_desc;
 
 /* Byte sizes of the caller-owned buffers (all 256-byte aligned). */
@@ -166,7 +177,11 @@ void moe_plan_destroy(moe_plan_t plan);
 /* MXFP8 weight preparation (explainer section 02: static weights use 32x32
  * blocks so forward and input-gradient GEMMs share the E4M3 values).  Reads
  * w13/w2 (bf16), writes q13/s13/q2/s2.  Done once per weight update; it is
- * not part of a timed step. */
+ * not part of a timed step.  With mx_w1x32 (MXFP8) and for MXFP4 plans the
+ * weight rows are quantized in 1x32 blocks along the contraction: codes
+ * q13 [E, 2F, D] (MXFP4: [E, 2F, D/2] packed E2M1), exponents grouped by
+ * stage, s13 [D/G][E*2F][G/32] with G = 128 (MXFP8) or 256 (MXFP4), and
+ * likewise q2/s2 over [E*D, F].  Other precisions -> MOE_ERR_UNSUPPORTED. */
 moe_status moe_prepare_weights(moe_plan_t plan, const void* w13, const void* w2,
                                void* q13, void* s13, void* q2, void* s2,
                                hipStream_t stream);
@@ -178,7 +193,10 @@ moe_status moe_prepare_weights(moe_plan_t plan, const void* w13, const void* w2,
  * counts[e] rounded up to 32 -> for expert e, q[n*poffsets[e] + c*Mp_e + m]
  * and sc[n*poffsets[e]/32 + c*Mp_e/32 + m/32]; pad rows are +0.  E8M0 byte =
  * e + 127 where e is the smallest integer with amax <= 448 * 2^e (clamped to
- * [-127, 127]); E4M3 values are rounded to nearest even. */
+ * [-127, 127]); E4M3 values are rounded to nearest even.  kind 2 (MXFP4): 1x32
+ * row blocks -> q [R, n/2] E2M1 codes (value 2i in the low nibble of byte i),
+ * sc [R, n/32], e the smallest integer with amax <= 6 * 2^e, E2M1 values
+ * rounded to nearest even.  Other kinds -> MOE_ERR_ARG. */
 moe_status moe_mx_quantize(moe_plan_t plan, void* route_ws, const void* src, int32_t n,
                            int32_t kind, void* q, void* sc, hipStream_t stream);
 

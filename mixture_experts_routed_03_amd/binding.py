@@ -21,7 +21,7 @@ import torch  # noqa: F401  (loads the HIP runtime first)
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-PREC = {"f32": 0, "bf16": 1, "mxfp8": 2}
+PREC = {"f32": 0, "bf16": 1, "mxfp8": 2, "mxfp4": 3}
 DTYPE = {"f32": 0, "bf16": 1}
 STATUS_BAD_ID = 0x1
 STATUS_PAD_SCORE = 0x2
@@ -289,9 +289,19 @@ class MoeLayer:
         """MXFP8: quantize bf16 weights once into E4M3 + E8M0 scales, in 32x32
         blocks, or (mx_w1x32 plans) 1x32 blocks along each weight row with
         the exponents grouped by 128-value stage: s13 [D/128, E*2F, 4],
-        s2 [F/128, E*D, 4]."""
+        s2 [F/128, E*D, 4].  MXFP4: packed E2M1 codes q13 [E, 2F, D/2],
+        q2 [E, D, F/2], 1x32 exponents grouped by 256-value stage:
+        s13 [D/256, E*2F, 8], s2 [F/256, E*D, 8]."""
         E, D, F = self.E, self.D, self.F
         u8 = dict(dtype=torch.uint8, device=self.device)
+        if self.prec == "mxfp4":
+            q13 = torch.empty((E, 2 * F, D // 2), **u8)
+            q2 = torch.empty((E, D, F // 2), **u8)
+            s13 = torch.empty((D // 256, E * 2 * F, 8), **u8)
+            s2 = torch.empty((F // 256, E * D, 8), **u8)
+            moe_prepare_weights(self.plan, w13, w2, q13, s13, q2, s2)
+            self.prepared = (q13, s13, q2, s2)
+            return self.prepared
         q13 = torch.empty((E, 2 * F, D), **u8)
         q2 = torch.empty((E, D, F), **u8)
         if self.mx_w1x32:
@@ -306,9 +316,9 @@ class MoeLayer:
 
     def _w(self, w13, w2, prepared=None):
         prep = prepared if prepared is not None else self.prepared
-        if self.prec == "mxfp8":
+        if self.prec in ("mxfp8", "mxfp4"):
             if prep is None:
-                raise RuntimeError("MXFP8 layer: call prepare(w13, w2) first")
+                raise RuntimeError("block-scaled layer: call prepare(w13, w2) first")
             return (w13, w2) + tuple(prep)
         return (w13, w2)
 
@@ -350,13 +360,14 @@ class MoeLayer:
                        self.arena, self.scratch, dx, dw13, dw2, dscores, flags)
 
     def quantize(self, src, kind, route_ws=None):
-        """MXFP8 codes of bf16 rows src [R, n]: kind 0 = 1x32 row blocks,
-        1 = per-expert column bundles (see moe_mx_quantize)."""
+        """Block-scaled codes of bf16 rows src [R, n]: kind 0 = MXFP8 1x32
+        row blocks, 1 = MXFP8 per-expert column bundles, 2 = MXFP4 1x32 row
+        blocks (packed E2M1) (see moe_mx_quantize)."""
         n = src.shape[1]
         rb = self.readback(self.T_max, route_ws)
-        if kind == 0:
+        if kind in (0, 2):
             R = src.shape[0]
-            q = torch.zeros((R, n), dtype=torch.uint8, device=self.device)
+            q = torch.zeros((R, n // 2 if kind == 2 else n), dtype=torch.uint8, device=self.device)
             sc = torch.zeros((R, n // 32), dtype=torch.uint8, device=self.device)
         else:
             Rp = int(rb["poffsets"][-1])

@@ -157,9 +157,11 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
   const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
   const char* tag = replay_only ? "replay_quant_x" : "quant_x";
   // x rows are read through the permutation (the gather happens in the loaders)
+  const int fp4 = d.prec == MOE_PREC_MXFP4;
   RowqArgs rx{hdr, x, reinterpret_cast<uint8_t*>(sc + L.qx),
               reinterpret_cast<uint8_t*>(sc + L.sx), d.d, -1, -1, -1, replay_only,
               int(p->R_max), sorted_route, d.k};
+  rx.fp4 = fp4;
   hipError_t e = timed(p, tag, s, [&] { return launch_rowq(rx, p->R_max, s); });
   if (e != hipSuccess) return e;
   if (d.training) {
@@ -177,7 +179,8 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
              nullptr, nullptr, nullptr, sc + L.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, 0, -1,
              replay_only, int(p->R_max)};
   a13.limit = swiglu_limit(p);
-  a13.w1x32 = d.mx_w1x32;
+  a13.w1x32 = d.mx_w1x32 || fp4;
+  a13.fp4 = fp4;
   a13.sw_rows = d.e * 2 * d.f;
   e = timed(p, replay_only ? "replay_w13" : "w13_swiglu", s,
             [&] { return launch_mx_fwd(0, a13, p->mt_max, cus, s); });
@@ -271,8 +274,11 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   if (d.t_max < 0 || d.k < 1 || d.k > kMaxK || d.e < d.k || d.e > kMaxE || d.d <= 0 ||
       d.f <= 0 || d.d % 128 || d.f % 128 || d.t_max * d.k > (int64_t(1) << 24))
     return MOE_ERR_SHAPE;
-  if (d.prec != MOE_PREC_F32 && d.prec != MOE_PREC_BF16 && d.prec != MOE_PREC_MXFP8)
+  if (d.prec != MOE_PREC_F32 && d.prec != MOE_PREC_BF16 && d.prec != MOE_PREC_MXFP8 &&
+      d.prec != MOE_PREC_MXFP4)
     return MOE_ERR_ARG;
+  if (d.prec == MOE_PREC_MXFP4 && (d.d % 256 || d.f % 256)) return MOE_ERR_SHAPE;
+  if (d.prec == MOE_PREC_MXFP4 && d.training) return MOE_ERR_ARG;
   if (d.dw_dtype != MOE_DTYPE_F32 && d.dw_dtype != MOE_DTYPE_BF16) return MOE_ERR_ARG;
   if (d.prec == MOE_PREC_F32 && d.dw_dtype != MOE_DTYPE_F32) return MOE_ERR_ARG;
   if (d.max_layers < 1 || d.arena_budget < 0) return MOE_ERR_ARG;
@@ -289,6 +295,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   p->Rp_max = align_up(p->R_max + 31 * std::min<int64_t>(d.e, p->R_max), 32);
   const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es, Rp = p->Rp_max;
   const bool mx = d.prec == MOE_PREC_MXFP8;
+  const bool fp4 = d.prec == MOE_PREC_MXFP4;   // inference only: no column bundles
 
   RouteLayout& L = p->rl;
   L.nchunks = (R + kRankChunk - 1) / kRankChunk;
@@ -327,6 +334,12 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
     take(S.h2cq, Rp * F);
     take(S.h2cs, Rp / 32 * F);
   }
+  if (fp4) {
+    take(S.qx, R * D / 2);
+    take(S.sx, R * D / 32);
+    take(S.qh2, R * F / 2);
+    take(S.sh2, R * F / 32);
+  }
   if (d.training) {
     if (!mx) take(S.x_rows, R * D * es);   // packed x rows for the W13 weight gradient
     take(S.dh3, R * D * es);
@@ -364,13 +377,15 @@ moe_status moe_plan_sizes(moe_plan_t p, moe_sizes* s) {
   s->h3_slots = size_t(p->h3_bytes);
   s->arena = size_t(p->arena_bytes);
   s->layer_state_max = size_t(p->state_max);
-  if (p->d.prec == MOE_PREC_MXFP8) {
+  if (p->d.prec == MOE_PREC_MXFP8 || p->d.prec == MOE_PREC_MXFP4) {
     const int64_t E = p->d.e, D = p->d.d, F = p->d.f;
-    s->q13 = size_t(a256(E * 2 * F * D));
+    const int64_t per_byte = p->d.prec == MOE_PREC_MXFP4 ? 2 : 1;
+    const int64_t per_exp = p->d.prec == MOE_PREC_MXFP4 || p->d.mx_w1x32 ? 32 : 1024;
     // 32x32 blocks: one exponent per 1024 values; 1x32: one per 32
-    s->s13 = size_t(a256(E * 2 * F * D / (p->d.mx_w1x32 ? 32 : 1024)));
-    s->q2 = size_t(a256(E * D * F));
-    s->s2 = size_t(a256(E * D * F / (p->d.mx_w1x32 ? 32 : 1024)));
+    s->q13 = size_t(a256(E * 2 * F * D / per_byte));
+    s->s13 = size_t(a256(E * 2 * F * D / per_exp));
+    s->q2 = size_t(a256(E * D * F / per_byte));
+    s->s2 = size_t(a256(E * D * F / per_exp));
   }
   return MOE_OK;
 }
@@ -378,7 +393,10 @@ moe_status moe_plan_sizes(moe_plan_t p, moe_sizes* s) {
 moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
   if (!p || !buf || cap == 0) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
-  const char* prec = d.prec == MOE_PREC_F32 ? "f32" : d.prec == MOE_PREC_BF16 ? "bf16" : "mxfp8";
+  const char* prec = d.prec == MOE_PREC_F32    ? "f32"
+                     : d.prec == MOE_PREC_BF16 ? "bf16"
+                     : d.prec == MOE_PREC_MXFP8 ? "mxfp8"
+                                                : "mxfp4";
   const bool mx = d.prec == MOE_PREC_MXFP8;
   auto mib = [](int64_t b) { return double(b) / (1024.0 * 1024.0); };
   std::string s;
@@ -443,15 +461,17 @@ void moe_plan_destroy(moe_plan_t p) {
 moe_status moe_prepare_weights(moe_plan_t p, const void* w13, const void* w2, void* q13,
                                void* s13, void* q2, void* s2, hipStream_t s) {
   if (!p) return MOE_ERR_ARG;
-  if (p->d.prec != MOE_PREC_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (p->d.prec != MOE_PREC_MXFP8 && p->d.prec != MOE_PREC_MXFP4) return MOE_ERR_UNSUPPORTED;
   if (!w13 || !w2 || !q13 || !s13 || !q2 || !s2) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
-  if (d.mx_w1x32) {
+  const int fp4 = d.prec == MOE_PREC_MXFP4;
+  if (d.mx_w1x32 || fp4) {
     // 1x32 blocks: the row quantizer over the weight rows [E*N, Kd], its
-    // exponents grouped by 128-value stage ([Kd/128][E*N] dwords)
+    // exponents grouped by stage ([Kd/128][E*N] dwords; MXFP4 [Kd/256][E*N]
+    // pairs of dwords)
     auto prep = [&](const void* w, void* q, void* sc, int64_t rows, int kd) {
       RowqArgs r{nullptr, w, reinterpret_cast<uint8_t*>(q), reinterpret_cast<uint8_t*>(sc), kd,
-                 -1, -1, -1, 0, int(rows), nullptr, 0, rows};
+                 -1, -1, -1, 0, int(rows), nullptr, 0, rows, fp4};
       return launch_rowq(r, rows, s);
     };
     hipError_t e = timed(p, "prep_w13", s,
@@ -474,9 +494,10 @@ moe_status moe_mx_quantize(moe_plan_t p, void* ws, const void* src, int32_t n, i
   if (!p || !ws || !src || !q || !sc) return MOE_ERR_ARG;
   if (n <= 0 || n % 128) return MOE_ERR_SHAPE;
   RouteHdr* hdr = hdr_of(ws);
-  if (kind == 0) {
+  if (kind == 0 || kind == 2) {
     RowqArgs r{hdr, src, reinterpret_cast<uint8_t*>(q), reinterpret_cast<uint8_t*>(sc), n,
                -1, -1, -1, 0};
+    r.fp4 = kind == 2;
     return hip_status(launch_rowq(r, p->R_max, s));
   }
   if (kind == 1) {
@@ -501,7 +522,9 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
                           hipStream_t s) {
   if (!p || !ws || !w || !h3 || !scratch) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
-  const bool mx = d.prec == MOE_PREC_MXFP8;
+  const bool mx8 = d.prec == MOE_PREC_MXFP8;
+  const bool fp4 = d.prec == MOE_PREC_MXFP4;
+  const bool mx = mx8 || fp4;
   if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;
   if (layer < 0 || layer >= d.max_layers) return MOE_ERR_ARG;
   if (!aligned16(x) || !aligned16(w->w13) || !aligned16(w->w2) || !aligned16(w->q13) ||
@@ -513,9 +536,9 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   const ScratchLayout& L = p->sl;
   PlanArgs pa{layer, d.max_layers, d.training, p->es, d.d, d.f, p->budget,
               uint64_t(d.training ? arena : nullptr), uint64_t(sc + L.h1),
-              mx ? 1 : 0, 0,
-              {mx ? uint64_t(sc + L.xcq) : 0, mx ? uint64_t(sc + L.xcs) : 0,
-               mx ? uint64_t(sc + L.h2cq) : 0, mx ? uint64_t(sc + L.h2cs) : 0}};
+              mx8 ? 1 : 0, 0,
+              {mx8 ? uint64_t(sc + L.xcq) : 0, mx8 ? uint64_t(sc + L.xcs) : 0,
+               mx8 ? uint64_t(sc + L.h2cq) : 0, mx8 ? uint64_t(sc + L.h2cs) : 0}};
   hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
@@ -543,6 +566,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   // h2 -> 1x32 row blocks for the W2 GEMM
   RowqArgs rq{hdr, sc + L.h2, reinterpret_cast<uint8_t*>(sc + L.qh2),
               reinterpret_cast<uint8_t*>(sc + L.sh2), d.f, -1, -1, -1, 0, int(p->R_max)};
+  rq.fp4 = fp4;
   e = timed(p, "quant_h2", s, [&] { return launch_rowq(rq, p->R_max, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs a2{hdr, offsets, poffsets, mtoff, sorted_route,
@@ -550,7 +574,8 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
             reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
             nullptr, nullptr, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
             int(p->R_max)};
-  a2.w1x32 = d.mx_w1x32;
+  a2.w1x32 = d.mx_w1x32 || fp4;
+  a2.fp4 = fp4;
   a2.sw_rows = d.e * d.d;
   return hip_status(timed(p, "w2_scatter", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); }));
 }
@@ -573,7 +598,9 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
   if (!p || !ws || !w || !scratch || !y32) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
   if (d.training) return MOE_ERR_UNSUPPORTED;   // no route outputs are kept for a backward
-  const bool mx = d.prec == MOE_PREC_MXFP8;
+  const bool mx8 = d.prec == MOE_PREC_MXFP8;
+  const bool fp4 = d.prec == MOE_PREC_MXFP4;
+  const bool mx = mx8 || fp4;
   if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;
   if (!aligned16(x) || !aligned16(w->w13) || !aligned16(w->w2) || !aligned16(w->q13) ||
       !aligned16(w->q2) || !aligned16(y32) || !aligned16(y) || !aligned16(y_addend) ||
@@ -582,9 +609,9 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
   RouteHdr* hdr = hdr_of(ws);
   char* sc = reinterpret_cast<char*>(scratch);
   const ScratchLayout& L = p->sl;
-  PlanArgs pa{0, d.max_layers, 0, p->es, d.d, d.f, p->budget, 0, uint64_t(sc + L.h1), mx ? 1 : 0,
-              0, {mx ? uint64_t(sc + L.xcq) : 0, mx ? uint64_t(sc + L.xcs) : 0,
-                  mx ? uint64_t(sc + L.h2cq) : 0, mx ? uint64_t(sc + L.h2cs) : 0}};
+  PlanArgs pa{0, d.max_layers, 0, p->es, d.d, d.f, p->budget, 0, uint64_t(sc + L.h1), mx8 ? 1 : 0,
+              0, {mx8 ? uint64_t(sc + L.xcq) : 0, mx8 ? uint64_t(sc + L.xcs) : 0,
+                  mx8 ? uint64_t(sc + L.h2cq) : 0, mx8 ? uint64_t(sc + L.h2cs) : 0}};
   hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
@@ -618,6 +645,7 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
     if (e != hipSuccess) return MOE_ERR_HIP;
     RowqArgs rq{hdr, sc + L.h2, reinterpret_cast<uint8_t*>(sc + L.qh2),
                 reinterpret_cast<uint8_t*>(sc + L.sh2), d.f, -1, -1, -1, 0, int(p->R_max)};
+    rq.fp4 = fp4;
     e = timed(p, "quant_h2", s, [&] { return launch_rowq(rq, p->R_max, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
     MxArgs a2{hdr, offsets, poffsets, mtoff, sorted_route,
@@ -625,7 +653,8 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
               reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
               nullptr, nullptr, nullptr, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
               int(p->R_max), scores, y32, d.k};
-    a2.w1x32 = d.mx_w1x32;
+    a2.w1x32 = d.mx_w1x32 || fp4;
+    a2.fp4 = fp4;
     a2.sw_rows = d.e * d.d;
     e = timed(p, "w2_fused", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); });
   }

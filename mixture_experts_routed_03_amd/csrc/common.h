@@ -151,6 +151,8 @@ struct MxArgs {
   int w1x32;             // FPROP: weights in 1x32 blocks, exponents grouped by 128-value
                          // stage: dword (s, e*N + n) of [Kd/128][sw_rows] (see k_rowq)
   int sw_rows;           // E * N for w1x32
+  int fp4;               // FPROP: E2M1 operands (two per byte) with 1x32 weight blocks;
+                         // exponents grouped by 256-value stage, [Kd/256][rows][8]
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:
@@ -169,6 +171,8 @@ struct RowqArgs {
   const int32_t* gather;  // non-null: source row r is src[gather[r] / K] (src = x [T, N])
   int K;
   int64_t rows;         // > 0: rows to quantize (hdr unused); 0: the route header's R
+  int fp4;              // 1: E2M1 codes, two per byte (q is [R, N/2]); grouped exponents
+                        // then come per 256-column stage, [N/256][s_rows][8]
 };
 struct ColqArgs {
   const RouteHdr* hdr;

@@ -49,6 +49,16 @@ __device__ __forceinline__ void mfma_mx(f32x16& acc, u32x4 a0, u32x4 a1, u32x4 b
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
 }
 
+// E2M1 x E2M1 (cbsz = blgp = 4): a 4-bit operand fills four registers, so
+// the upper half of each 8-register operand is not read.  Lane (r, h) holds
+// MX block h of the 64-value step (32 values, low nibble first) and supplies
+// that block's scale (measured on gfx950).
+__device__ __forceinline__ void mfma_fp4(f32x16& acc, u32x4 a0, u32x4 b0, int sa, int sb) {
+  const i32x8 a = {int(a0[0]), int(a0[1]), int(a0[2]), int(a0[3]), 0, 0, 0, 0};
+  const i32x8 b = {int(b0[0]), int(b0[1]), int(b0[2]), int(b0[3]), 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 4, 4, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ int byte_of(uint32_t w, int i) { return int((w >> (8 * i)) & 0xffu); }
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
@@ -85,13 +95,18 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
 // own exponent per 32 values, so each lane takes the exponents of its own
 // row (one dword per stage, staged through LDS like the token exponents)
 // instead of the wave's 32x32-block exponents.
-template <int MODE, int W1>
+// FP4 (needs W1): E2M1 operands, two per byte.  A stage is still 128 bytes
+// of every row, now 256 values = 8 MX blocks = four MFMAs per accumulator,
+// with 8 exponent bytes per row.
+template <int MODE, int W1, int FP4>
 __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
-  constexpr int kW = 128 * 128;      // weight stage: 128 rows x 128 E4M3 values
-  constexpr int kA = kBM * 128;      // token stage: 64 rows x 128 values
-  constexpr int kSc = kBM * 4;       // token scales of the stage: 4 blocks per row
+  static_assert(!FP4 || W1, "4-bit weights come in 1x32 blocks");
+  constexpr int kW = 128 * 128;      // weight stage: 128 rows x 128 bytes
+  constexpr int kA = kBM * 128;      // token stage: 64 rows x 128 bytes
+  constexpr int kXb = FP4 ? 8 : 4;   // exponent bytes per row and stage
+  constexpr int kSc = kBM * kXb;     // token scales of the stage
   // + the weight exponents: one dword per wave (32x32) or per weight row (1x32)
-  constexpr int kStage = kW + kA + kSc + (W1 ? 128 * 4 : 16);
+  constexpr int kStage = kW + kA + kSc + (W1 ? 128 * kXb : 16);
   __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,11 +123,12 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   uint16_t* out1 = reinterpret_cast<uint16_t*>(a.out1);
   const int Kd = a.Kd;
   const int KB = Kd / 32;           // scale bytes per row
+  const int Kb = FP4 ? Kd / 2 : Kd; // code bytes per row
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   const int chunk = (n_items + kXcds - 1) / kXcds;
-  const int S = Kd / 128;
+  const int S = Kb / 128;
 
   int e_prev = -1;  // expert of this workgroup's previous item
   for (int it = slot; it < chunk; it += per) {
@@ -133,7 +149,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
       const int rho = lrow + 32 * j;
       const int wr = MODE == 0 ? (rho < 64 ? nt * 64 + rho : a.F + nt * 64 + rho - 64)
                                : nt * 128 + rho;
-      wsrc[j] = a.qw + (int64_t(e) * a.N + wr) * Kd + lc * 16;
+      wsrc[j] = a.qw + (int64_t(e) * a.N + wr) * Kb + lc * 16;
     }
     // the 32 weight rows of this wave form one 32-row scale block
     const int wrow0 = MODE == 0 ? ((wave < 2 ? 0 : a.F) + nt * 64 + (wave & 1) * 32)
@@ -143,20 +159,24 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
                                                   : a.F + nt * 64 + (tid & 63))
                               : nt * 128 + (tid & 127);
     const uint32_t* wsc_src =
-        W1 ? reinterpret_cast<const uint32_t*>(a.sw) + int64_t(e) * a.N + wr1
+        W1 ? reinterpret_cast<const uint32_t*>(a.sw) + (int64_t(e) * a.N + wr1) * (kXb / 4)
            : reinterpret_cast<const uint32_t*>(a.sw + (int64_t(e) * (a.N / 32) + wrow0 / 32) * KB);
     // Tile rows past the expert's last row re-read that row: every load is
     // unconditional, and the extra output columns are never stored.
     const uint8_t* tsrc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      tsrc[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kd + lc * 16;
-    // token exponents are grouped by stage: dword (s, row) at (s * sa_rows + row) * 4
-    const uint32_t* tsc_src = reinterpret_cast<const uint32_t*>(a.sa) + row0 + min(tid & 63, rows - 1);
+      tsrc[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kb + lc * 16;
+    // token exponents are grouped by stage: the kXb bytes of (s, row) at
+    // (s * sa_rows + row) * kXb
+    const uint32_t* tsc_src =
+        reinterpret_cast<const uint32_t*>(a.sa) + int64_t(row0 + min(tid & 63, rows - 1)) * (kXb / 4);
 
     f32x16 acc0 = {}, acc1 = {};
     u32x4 R0[6], R1[6];
-    uint32_t S0[2], S1[2];   // [0] weight scales of the wave, [1] token scales of row tid
+    // [0..1] weight scales (of the wave, or of tile row tid with W1), [2..3]
+    // token scales of row tid; the second dword of each only with FP4
+    uint32_t S0[4], S1[4];
     auto load = [&](u32x4* R, uint32_t* Sc, int s) {
       const int64_t off = int64_t(s) * 128;
 #pragma unroll
@@ -164,8 +184,18 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
         R[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + off));
 #pragma unroll
       for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
-      Sc[0] = W1 ? wsc_src[int64_t(s) * a.sw_rows] : wsc_src[s];
-      Sc[1] = tsc_src[int64_t(s) * a.sa_rows];
+      if (FP4) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w2 = *reinterpret_cast<const u32x2*>(wsc_src + int64_t(s) * a.sw_rows * 2);
+        const u32x2 t2 = *reinterpret_cast<const u32x2*>(tsc_src + int64_t(s) * a.sa_rows * 2);
+        Sc[0] = w2[0];
+        Sc[1] = w2[1];
+        Sc[2] = t2[0];
+        Sc[3] = t2[1];
+      } else {
+        Sc[0] = W1 ? wsc_src[int64_t(s) * a.sw_rows] : wsc_src[s];
+        Sc[2] = tsc_src[int64_t(s) * a.sa_rows];
+      }
     };
     auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
       char* base = lds + buf * kStage;
@@ -175,11 +205,24 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
-      if (tid < kBM) reinterpret_cast<uint32_t*>(base + kW + kA)[tid] = Sc[1];
-      if (W1) {
-        if (tid < 128) reinterpret_cast<uint32_t*>(base + kW + kA + kSc)[tid] = Sc[0];
-      } else if (lane == 0) {
-        reinterpret_cast<uint32_t*>(base + kW + kA + kSc)[wave] = Sc[0];
+      uint32_t* ts = reinterpret_cast<uint32_t*>(base + kW + kA);
+      uint32_t* ws = reinterpret_cast<uint32_t*>(base + kW + kA + kSc);
+      if (FP4) {
+        if (tid < kBM) {
+          ts[2 * tid] = Sc[2];
+          ts[2 * tid + 1] = Sc[3];
+        }
+        if (tid < 128) {
+          ws[2 * tid] = Sc[0];
+          ws[2 * tid + 1] = Sc[1];
+        }
+      } else {
+        if (tid < kBM) ts[tid] = Sc[2];
+        if (W1) {
+          if (tid < 128) ws[tid] = Sc[0];
+        } else if (lane == 0) {
+          ws[wave] = Sc[0];
+        }
       }
     };
     // Both 32-token halves are always multiplied: no accumulator depends on
@@ -188,10 +231,27 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
       const char* wl = lds + buf * kStage;
       const char* tl = wl + kW;
       const uint32_t* tsc = reinterpret_cast<const uint32_t*>(tl + kA);
+      const uint32_t* wscl = reinterpret_cast<const uint32_t*>(tl + kA + kSc);
+      const int wrow = 32 * wave + lr;
+      if (FP4) {
+        // lane (r, h) multiplies 16-byte chunk 2q + h of its rows: MX block
+        // 2q + h of the stage, whose exponent is byte (2q + h) of the row's 8
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = 2 * q + lh;
+          const int dw = q >> 1, by = c & 3;
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, c));
+          const u32x4 b0 = *reinterpret_cast<const u32x4*>(tl + swz(lr, c));
+          const u32x4 d0 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, c));
+          const int sa = byte_of(wscl[2 * wrow + dw], by);
+          mfma_fp4(acc0, a0, b0, sa, byte_of(tsc[2 * lr + dw], by));
+          mfma_fp4(acc1, a0, d0, sa, byte_of(tsc[2 * (32 + lr) + dw], by));
+        }
+        return;
+      }
       const uint32_t ts0 = tsc[lr];
       const uint32_t ts1 = tsc[32 + lr];
-      const uint32_t wsc = W1 ? tsc[kBM + 32 * wave + lr] : tsc[kBM + wave];
-      const int wrow = 32 * wave + lr;
+      const uint32_t wsc = W1 ? wscl[wrow] : wscl[wave];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int ca = 4 * q + lh, cb = 4 * q + 2 + lh;
@@ -743,14 +803,14 @@ static unsigned grid_m(int per_cu, int64_t items, int cus) {
 // mode 0: W13 (+ SwiGLU), 1: W2 -> slots
 hipError_t launch_mx_fwd(int mode, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s) {
   if (mt_max == 0) return hipSuccess;
-#define MOE_MXF(M, W, ID)                                                                   \
-  hipLaunchKernelGGL((k_mx_fwd<M, W>),                                                     \
-                     dim3(grid_m(occupancy_m<ID>(k_mx_fwd<M, W>), mt_max * a.NT, cus)), \
+#define MOE_MXF(M, W, P, ID)                                                                   \
+  hipLaunchKernelGGL((k_mx_fwd<M, W, P>),                                                     \
+                     dim3(grid_m(occupancy_m<ID>(k_mx_fwd<M, W, P>), mt_max * a.NT, cus)), \
                      dim3(256), 0, s, a)
   if (mode == 0) {
-    if (a.w1x32) MOE_MXF(0, 1, 12); else MOE_MXF(0, 0, 0);
+    if (a.fp4) MOE_MXF(0, 1, 1, 14); else if (a.w1x32) MOE_MXF(0, 1, 0, 12); else MOE_MXF(0, 0, 0, 0);
   } else {
-    if (a.w1x32) MOE_MXF(1, 1, 13); else MOE_MXF(1, 0, 1);
+    if (a.fp4) MOE_MXF(1, 1, 1, 15); else if (a.w1x32) MOE_MXF(1, 1, 0, 13); else MOE_MXF(1, 0, 0, 1);
   }
 #undef MOE_MXF
   return hipGetLastError();

@@ -7,6 +7,7 @@
 //
 //   k_prep_w : W [E, N, K] bf16 -> q [E, N, K] e4m3, s [E, N/32, K/32] e8m0
 //   k_rowq   : rows [R, N] bf16 -> q [R, N], s [R, N/32]           (1x32)
+//              (MXFP4: q [R, N/2], two E2M1 codes per byte)
 //   k_colq   : rows [R, N] bf16 -> per expert e, q^T [N, Mp_e] and
 //              s^T [N, Mp_e/32] at offsets N*poffsets[e] and N*poffsets[e]/32,
 //              Mp_e = counts[e] rounded up to 32, pad rows quantized as 0.
@@ -60,6 +61,39 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
 
 __device__ __forceinline__ float ldexp_i(float v, int e) { return ldexpf(v, e); }
 
+// MXFP4 (OCP MX E2M1 with E8M0 block scales): e = the smallest integer with
+// amax <= 6 * 2^e, clamped to [-127, 127] (-127 for an all-zero block).
+__device__ __forceinline__ int e8m0_exp_fp4(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int p;
+  const float m = frexpf(amax, &p);  // 6 = 0.75 * 2^3
+  const int e = m <= 0.75f ? p - 3 : p - 2;
+  return min(127, max(-127, e));
+}
+
+// E2M1 code of v (bias 1: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), nearest,
+// ties to the even code; magnitudes above 6 saturate.  The grid spacing is
+// 0.5 below 2, 1 in [2, 4) and 2 above, and every binade edge lies on the
+// grid, so rounding a / spacing to the nearest even integer rounds to the
+// grid (both scalings are exact).
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  const float a = fminf(fabsf(v), 6.0f);
+  float q;
+  uint32_t code;
+  if (a < 2.0f) {
+    q = __builtin_rintf(a * 2.0f);            // 0..4 half-units
+    code = uint32_t(q);                       // 0, 0.5, 1, 1.5 -> codes 0..3; 2.0 -> 4
+  } else if (a < 4.0f) {
+    q = __builtin_rintf(a);                   // 2..4
+    code = uint32_t(q) + 2u;                  // 2 -> 4, 3 -> 5, 4 -> 6
+  } else {
+    q = __builtin_rintf(a * 0.5f);            // 2..3
+    code = uint32_t(q) + 4u;                  // 4 -> 6, 6 -> 7
+  }
+  return sign | code;
+}
+
 // ------------------------------------------------------------------ weights
 // One workgroup per (expert, 32-row block, 256 columns): thread = column.
 __global__ __launch_bounds__(256) void k_prep_w(const uint16_t* __restrict__ w,
@@ -96,7 +130,9 @@ __device__ __forceinline__ uint64_t rec_ptr(const RouteHdr* h, int slot) {
 }
 
 // Lane = 8 consecutive values; 4 lanes = one block.  A wave covers 512
-// values of a row per step.
+// values of a row per step.  FP4: E2M1 codes, value 2i in the low nibble of
+// byte i (the order in which the scaled MFMA reads a 4-bit operand).
+template <int FP4>
 __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
   const RouteHdr* hdr = a.hdr;
   if (a.replay_only && !hdr->rec.replay) return;
@@ -126,18 +162,26 @@ __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    const int ex = e8m0_exp(amax);
-    u32x2 out;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    const int ex = FP4 ? e8m0_exp_fp4(amax) : e8m0_exp(amax);
+    if (FP4) {
       uint32_t wv = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wv |= e4m3_rne(ldexp_i(v[4 * h + i], -ex)) << (8 * i);
-      out[h] = wv;
+      for (int i = 0; i < 8; ++i) wv |= e2m1_rne(ldexp_i(v[i], -ex)) << (4 * i);
+      *reinterpret_cast<uint32_t*>(q + row * (N / 2) + c0 / 2) = wv;
+    } else {
+      u32x2 out;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv |= e4m3_rne(ldexp_i(v[4 * h + i], -ex)) << (8 * i);
+        out[h] = wv;
+      }
+      *reinterpret_cast<u32x2*>(q + row * N + c0) = out;
     }
-    *reinterpret_cast<u32x2*>(q + row * N + c0) = out;
     if ((lane & 3) == 0) {
-      const int64_t si = a.s_rows ? (int64_t(c0 / 128) * a.s_rows + row) * 4 + (c0 / 32) % 4
+      constexpr int G = FP4 ? 256 : 128;     // values per stage of the grouped layout
+      const int64_t si = a.s_rows ? (int64_t(c0 / G) * a.s_rows + row) * (G / 32) + (c0 / 32) % (G / 32)
                                   : row * (N / 32) + c0 / 32;
       s[si] = uint8_t(ex + 127);
     }
@@ -219,7 +263,10 @@ hipError_t launch_prep_w(const void* w, void* q, void* s, int E, int N, int K, h
 
 hipError_t launch_rowq(const RowqArgs& a, int64_t R_max, hipStream_t st) {
   if (R_max == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rowq, dim3(unsigned((R_max + 3) / 4)), dim3(256), 0, st, a);
+  if (a.fp4)
+    hipLaunchKernelGGL(k_rowq<1>, dim3(unsigned((R_max + 3) / 4)), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_rowq<0>, dim3(unsigned((R_max + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -144,7 +144,7 @@ class Config:
     F: int
     E: int
     K: int
-    prec: str                      # "f32" | "bf16" | "mxfp8"
+    prec: str                      # "f32" | "bf16" | "mxfp8" | "mxfp4" (inference)
     zipf: tuple = (None,)          # per-layer routing: None = uniform top-K, else Zipf exponent
     pad_frac: float = 0.0
     training: bool = False
@@ -188,6 +188,8 @@ CONFIGS = {
                                  note="MXFP8 inference forward, 32x32-block weights"),
     "mxfp8_fwd_1x32": Config("mxfp8_fwd_1x32", 2048, 7168, 2048, 384, 6, "mxfp8", mx_w1x32=True,
                              note="MXFP8 inference forward, 1x32-block weights"),
+    "mxfp4_fwd_balanced": Config("mxfp4_fwd_balanced", 2048, 7168, 2048, 384, 6, "mxfp4",
+                                 note="MXFP4 inference forward: E2M1 activations and 1x32 weights"),
     "bf16_decode_t1": Config("bf16_decode_t1", 1, 7168, 2048, 384, 6, "bf16",
                              note="decode step: one token, six routed experts (one row each)"),
     "bf16_decode_t8": Config("bf16_decode_t8", 8, 7168, 2048, 384, 6, "bf16",

@@ -30,7 +30,7 @@ def run_forward(layer, lay, y_addend=None):
     """route -> expert_fwd -> combine on the current stream; returns y."""
     T = lay["x"].shape[0]
     y = torch.empty((T, layer.D), dtype=layer.act_dtype, device=layer.device)
-    if layer.prec == "mxfp8" and layer.prepared is None:
+    if layer.prec in ("mxfp8", "mxfp4") and layer.prepared is None:
         layer.prepare(lay["w13"], lay["w2"])
     layer.route(lay["ids"])
     layer.forward(lay["x"], lay["w13"], lay["w2"])

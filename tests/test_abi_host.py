@@ -101,6 +101,29 @@ def test_plan_1x32_weights_only_for_mxfp8_inference(b):
         b.moe_plan_destroy(p1)
 
 
+def test_plan_mxfp4_inference_only_and_sizes(b):
+    """MXFP4 plans: inference only, D and F multiples of 256, weights in 1x32
+    blocks of packed E2M1 (half a byte per value, one exponent per 32)."""
+    with pytest.raises(b.MoeError):
+        b.moe_plan_create(16, 256, 256, 8, 2, "mxfp4", training=True)
+    for D, F in ((384, 256), (256, 384)):
+        with pytest.raises(b.MoeError):
+            b.moe_plan_create(16, D, F, 8, 2, "mxfp4")
+    with pytest.raises(b.MoeError):
+        b.moe_plan_create(16, 256, 256, 8, 2, "mxfp4", mx_w1x32=True)
+    p = b.moe_plan_create(16, 512, 256, 8, 2, "mxfp4")
+    try:
+        s = b.moe_plan_sizes(p)
+        assert s["q13"] == 8 * 512 * 512 // 2 and s["s13"] == 8 * 512 * 512 // 32
+        assert s["q2"] == 8 * 512 * 256 // 2 and s["s2"] == 8 * 512 * 256 // 32
+        assert "prec=mxfp4" in b.moe_plan_explain(p)
+        L = b.lib()
+        # quantizer kinds are 0, 1 and 2 (MXFP4 rows)
+        assert L.moe_mx_quantize(p, 256, 256, 256, 3, 256, 256, None) == 1
+    finally:
+        b.moe_plan_destroy(p)
+
+
 def test_calls_reject_before_enqueue(b):
     """Host-detectable errors return before any launch (null stream, no GPU)."""
     plan = b.moe_plan_create(16, 256, 128, 8, 2, "bf16")

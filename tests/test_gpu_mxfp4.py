@@ -1,0 +1,140 @@
+"""MXFP4 inference through the C ABI: E2M1 activations and weights with one
+E8M0 scale per 32 values along the contraction (the OCP-MX counterpart of the
+Dist-MoE explainer's 4-bit inference mode, section 02; weights prepared in
+1x32 blocks as the explainx.ai post's Supported modes names for inference).
+The quantizers are bit-exact against the oracle's codes; the layer (slot and
+FUSED combine) matches the quantization-faithful MXFP4 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_routed_03_amd import workloads as wl
+from oracle import moe as om
+from oracle import mxfp4 as o4
+from tests._harness import TOL, banner, make_inputs, run_forward
+
+pytestmark = pytest.mark.gpu
+
+TOL4 = TOL["mxfp8"]
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_routed_03_amd import binding
+    binding.lib()
+    assert torch.cuda.is_available()
+    return binding
+
+
+def _wide(shape, seed):
+    """bf16 values over many binades, exact zeros, tiny values, and blocks
+    whose scaled values sit exactly on E2M1 rounding ties."""
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randn(shape, generator=g) * torch.exp(3 * torch.randn(shape, generator=g))
+    v[..., 5] = 0.0
+    v.view(-1)[::97] *= 1e-30
+    ties = torch.tensor([6.0, 5.0, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25, -5.0, -0.25, 0.1, 4.0,
+                         -2.5, 1.0, 0.5, 3.0] * 2)
+    v[0, :32] = ties * 4.0
+    if shape[1] >= 64:
+        v[1, 32:64] = ties * 2.0 ** -20
+    return v.to(torch.bfloat16)
+
+
+def _check_prepared(q, s, w):
+    """q [E, N, Kd/2] packed E2M1; s [Kd/256, E*N, 8] exponents + 127."""
+    E, N, Kd = w.shape
+    rq, re = o4.quantize_rows_fp4(om.as_f64(w).reshape(E * N, Kd))
+    np.testing.assert_array_equal(q.cpu().numpy().reshape(E * N, Kd // 2), rq)
+    got = s.cpu().numpy().astype(np.int64).transpose(1, 0, 2).reshape(E * N, Kd // 32)
+    np.testing.assert_array_equal(got, re + 127)
+
+
+def test_fp4_row_quantizer_bit_exact(B):
+    banner("mxfp4 row quantizer")
+    T, E, K, n = 120, 6, 2, 512
+    layer = B.MoeLayer(T, n, 256, E, K, "mxfp4")
+    ids, _ = wl.make_routing(T, E, K, zipf_s=1.5, seed=4)
+    ids[3, 1] = -1
+    layer.route(torch.from_numpy(ids).cuda())
+    rt = om.route(ids, E)
+    src = _wide((rt["R"], n), 3).cuda()
+    q, sc, _ = layer.quantize(src, 2)
+    torch.cuda.synchronize()
+    rq, re = o4.quantize_rows_fp4(om.as_f64(src))
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    np.testing.assert_array_equal(sc.cpu().numpy().astype(np.int64), re + 127)
+
+
+def test_fp4_weight_prep_bit_exact(B):
+    banner("mxfp4 weight prep")
+    E, D, F = 3, 512, 256
+    layer = B.MoeLayer(16, D, F, E, 2, "mxfp4")
+    w13 = torch.stack([_wide((2 * F, D), 10 + e) for e in range(E)]).cuda()
+    w2 = torch.stack([_wide((D, F), 20 + e) for e in range(E)]).cuda()
+    q13, s13, q2, s2 = layer.prepare(w13, w2)
+    torch.cuda.synchronize()
+    _check_prepared(q13, s13, w13)
+    _check_prepared(q2, s2, w2)
+
+
+@pytest.mark.parametrize("T,D,F,E,K,zipf,n_pad", [
+    (300, 256, 256, 8, 2, None, 7),      # ragged m-tiles, one stage per W2 row
+    (200, 768, 512, 10, 3, 1.3, 0),      # skew: hot experts over several tiles, empty experts
+    (40, 512, 256, 16, 16, None, 3),     # K = 16, every expert per token
+    (1, 256, 256, 4, 2, None, 0),        # a single token
+])
+def test_mxfp4_forward_matches_oracle(B, T, D, F, E, K, zipf, n_pad):
+    banner(f"mxfp4 forward T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
+    lay = make_inputs(T, D, F, E, K, "bf16", zipf=zipf, n_pad=n_pad, seed=T + 29)
+    layer = B.MoeLayer(T, D, F, E, K, "mxfp4")
+    q13, s13, q2, s2 = layer.prepare(lay["w13"], lay["w2"])
+    torch.cuda.synchronize()
+    _check_prepared(q13, s13, lay["w13"])
+    _check_prepared(q2, s2, lay["w2"])
+    y = run_forward(layer, lay)
+    torch.cuda.synchronize()
+    ref = o4.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(), lay["w2"].cpu())
+    assert om.max_abs_rel(y, ref) < TOL4
+    assert layer.status()[0] == 0
+    add = torch.randn_like(y)
+    yf = torch.empty_like(y)
+    layer.forward_fused(lay["x"], lay["w13"], lay["w2"], lay["scores"], yf, y_addend=add)
+    torch.cuda.synchronize()
+    assert om.max_abs_rel(yf, ref + om.as_f64(add)) < TOL4
+
+
+def test_mxfp4_clamped_swiglu(B):
+    banner("mxfp4 forward, clamped SwiGLU")
+    T, D, F, E, K = 150, 512, 256, 6, 2
+    lay = make_inputs(T, D, F, E, K, "bf16", seed=77)
+    layer = B.MoeLayer(T, D, F, E, K, "mxfp4", swiglu_limit=0.5)
+    y = run_forward(layer, lay)
+    torch.cuda.synchronize()
+    ref = o4.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                     limit=0.5)
+    assert om.max_abs_rel(y, ref) < TOL4
+
+
+def test_mxfp4_full_size_sampled(B):
+    """T=2048, D=7168, F=2048, E=384, K=6, balanced routing: every output of
+    four tokens against the oracle, one route at a time (each row's blocks
+    are its own, so a route's h3 needs only its row and its expert)."""
+    cfg = wl.CONFIGS["mxfp4_fwd_balanced"]
+    banner("full-size mxfp4 forward, sampled tokens")
+    lay = wl.make_layer(cfg, 0, device="cuda")
+    layer = B.MoeLayer(cfg.T, cfg.D, cfg.F, cfg.E, cfg.K, "mxfp4")
+    y = run_forward(layer, lay)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    ids = lay["ids"].cpu().numpy()
+    s = lay["scores"].cpu().numpy().astype(np.float64)
+    tokens = [0, 777, 2047]
+    for t in tokens:
+        ref = np.zeros(cfg.D)
+        for k in range(cfg.K):
+            e = int(ids[t, k])
+            w13 = o4.qdq_rows_fp4(om.as_f64(lay["w13"][e]))
+            w2 = o4.qdq_rows_fp4(om.as_f64(lay["w2"][e]))
+            ref += s[t, k] * o4.expert_ffn_mxfp4(om.as_f64(lay["x"][t:t + 1]), w13, w2)[2][0]
+        assert om.max_abs_rel(y[t], ref) < TOL4, t
