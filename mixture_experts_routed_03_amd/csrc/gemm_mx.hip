@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   constexpr int kSc = kBM * kXb;     // token scales of the stage
   // + the weight exponents: one dword per wave (32x32) or per weight row (1x32)
   constexpr int kStage = kW + kA + kSc + (W1 ? 128 * kXb : 16);
-  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+  constexpr int kXch = 2 * 2 * 16 * 64 * 4;   // SwiGLU epilogue: up halves of two waves
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStage + (MODE == 0 ? kXch : 0)];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -130,10 +131,16 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   const int chunk = (n_items + kXcds - 1) / kXcds;
   const int S = Kb / 128;
 
+  // Operand sources of one work item (an m-tile of an expert x 128 weight rows).
+  struct Item {
+    int e, nt, row0, rows;
+    const uint8_t* w[4];     // weight rows of this thread (4 x 16 bytes per stage)
+    const uint8_t* t[2];     // token rows
+    const uint32_t* ws;      // weight exponents
+    const uint32_t* ts;      // token exponents
+  };
   int e_prev = -1;  // expert of this workgroup's previous item
-  for (int it = slot; it < chunk; it += per) {
-    const int w = xcd * chunk + it;
-    if (w >= n_items) break;
+  auto setup = [&](int w, Item& I) {
     const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
     e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
@@ -142,153 +149,190 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     const int mt = u - nt * mt_e;
     const int row0 = a.offsets[e] + mt * kBM;
     const int rows = min(kBM, a.offsets[e + 1] - row0);
-
-    const uint8_t* wsrc[4];
+    I.e = e;
+    I.nt = nt;
+    I.row0 = row0;
+    I.rows = rows;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rho = lrow + 32 * j;
       const int wr = MODE == 0 ? (rho < 64 ? nt * 64 + rho : a.F + nt * 64 + rho - 64)
                                : nt * 128 + rho;
-      wsrc[j] = a.qw + (int64_t(e) * a.N + wr) * Kb + lc * 16;
+      I.w[j] = a.qw + (int64_t(e) * a.N + wr) * Kb + lc * 16;
     }
     // the 32 weight rows of this wave form one 32-row scale block
     const int wrow0 = MODE == 0 ? ((wave < 2 ? 0 : a.F) + nt * 64 + (wave & 1) * 32)
                                 : nt * 128 + wave * 32;
-    // 1x32: thread tid < 128 fetches the exponent dword of tile row tid
+    // 1x32: thread tid < 128 fetches the exponents of tile row tid
     const int wr1 = MODE == 0 ? ((tid & 127) < 64 ? nt * 64 + (tid & 63)
                                                   : a.F + nt * 64 + (tid & 63))
                               : nt * 128 + (tid & 127);
-    const uint32_t* wsc_src =
-        W1 ? reinterpret_cast<const uint32_t*>(a.sw) + (int64_t(e) * a.N + wr1) * (kXb / 4)
-           : reinterpret_cast<const uint32_t*>(a.sw + (int64_t(e) * (a.N / 32) + wrow0 / 32) * KB);
+    I.ws = W1 ? reinterpret_cast<const uint32_t*>(a.sw) + (int64_t(e) * a.N + wr1) * (kXb / 4)
+              : reinterpret_cast<const uint32_t*>(a.sw + (int64_t(e) * (a.N / 32) + wrow0 / 32) * KB);
     // Tile rows past the expert's last row re-read that row: every load is
     // unconditional, and the extra output columns are never stored.
-    const uint8_t* tsrc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      tsrc[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kb + lc * 16;
+      I.t[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kb + lc * 16;
     // token exponents are grouped by stage: the kXb bytes of (s, row) at
     // (s * sa_rows + row) * kXb
-    const uint32_t* tsc_src =
-        reinterpret_cast<const uint32_t*>(a.sa) + int64_t(row0 + min(tid & 63, rows - 1)) * (kXb / 4);
+    I.ts = reinterpret_cast<const uint32_t*>(a.sa) + int64_t(row0 + min(tid & 63, rows - 1)) * (kXb / 4);
+  };
 
-    f32x16 acc0 = {}, acc1 = {};
-    u32x4 R0[6], R1[6];
-    // [0..1] weight scales (of the wave, or of tile row tid with W1), [2..3]
-    // token scales of row tid; the second dword of each only with FP4
-    uint32_t S0[4], S1[4];
-    auto load = [&](u32x4* R, uint32_t* Sc, int s) {
-      const int64_t off = int64_t(s) * 128;
+  u32x4 R0[6], R1[6];
+  // [0..1] weight scales (of the wave, or of tile row tid with W1), [2..3]
+  // token scales of row tid; the second dword of each only with FP4
+  uint32_t S0[4], S1[4];
+  Item cur, nxt;
+  bool cross = false;   // loads past the current item's last stage fetch the next item's
+  // Stage idx of the current item; idx >= S is stage idx - S of the next item
+  // (without a next item: the current item's last stage, never used).
+  auto load = [&](u32x4* R, uint32_t* Sc, int idx) {
+    const bool nx = idx >= S;
+    const int st = nx ? (cross ? idx - S : S - 1) : idx;
+    const bool use_n = nx && cross;
+    const int64_t off = int64_t(st) * 128;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)   // weights: non-temporal (streamed once per m-tile)
-        R[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + off));
+    for (int j = 0; j < 4; ++j)   // weights: non-temporal (streamed once per m-tile)
+      R[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>((use_n ? nxt.w[j] : cur.w[j]) + off));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
-      if (FP4) {
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 w2 = *reinterpret_cast<const u32x2*>(wsc_src + int64_t(s) * a.sw_rows * 2);
-        const u32x2 t2 = *reinterpret_cast<const u32x2*>(tsc_src + int64_t(s) * a.sa_rows * 2);
-        Sc[0] = w2[0];
-        Sc[1] = w2[1];
-        Sc[2] = t2[0];
-        Sc[3] = t2[1];
-      } else {
-        Sc[0] = W1 ? wsc_src[int64_t(s) * a.sw_rows] : wsc_src[s];
-        Sc[2] = tsc_src[int64_t(s) * a.sa_rows];
+    for (int j = 0; j < 2; ++j)
+      R[4 + j] = *reinterpret_cast<const u32x4*>((use_n ? nxt.t[j] : cur.t[j]) + off);
+    const uint32_t* wsp = use_n ? nxt.ws : cur.ws;
+    const uint32_t* tsp = use_n ? nxt.ts : cur.ts;
+    if (FP4) {
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 w2 = *reinterpret_cast<const u32x2*>(wsp + int64_t(st) * a.sw_rows * 2);
+      const u32x2 t2 = *reinterpret_cast<const u32x2*>(tsp + int64_t(st) * a.sa_rows * 2);
+      Sc[0] = w2[0];
+      Sc[1] = w2[1];
+      Sc[2] = t2[0];
+      Sc[3] = t2[1];
+    } else {
+      Sc[0] = W1 ? wsp[int64_t(st) * a.sw_rows] : wsp[st];
+      Sc[2] = tsp[int64_t(st) * a.sa_rows];
+    }
+  };
+  auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
+    char* base = lds + buf * kStage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(base + swz(lrow + 32 * j, lc)) = R[j];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
+    uint32_t* ts = reinterpret_cast<uint32_t*>(base + kW + kA);
+    uint32_t* ws = reinterpret_cast<uint32_t*>(base + kW + kA + kSc);
+    if (FP4) {
+      if (tid < kBM) {
+        ts[2 * tid] = Sc[2];
+        ts[2 * tid + 1] = Sc[3];
       }
-    };
-    auto store = [&](const u32x4* R, const uint32_t* Sc, int buf) {
-      char* base = lds + buf * kStage;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4*>(base + swz(lrow + 32 * j, lc)) = R[j];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        *reinterpret_cast<u32x4*>(base + kW + swz(lrow + 32 * j, lc)) = R[4 + j];
-      uint32_t* ts = reinterpret_cast<uint32_t*>(base + kW + kA);
-      uint32_t* ws = reinterpret_cast<uint32_t*>(base + kW + kA + kSc);
-      if (FP4) {
-        if (tid < kBM) {
-          ts[2 * tid] = Sc[2];
-          ts[2 * tid + 1] = Sc[3];
-        }
-        if (tid < 128) {
-          ws[2 * tid] = Sc[0];
-          ws[2 * tid + 1] = Sc[1];
-        }
-      } else {
-        if (tid < kBM) ts[tid] = Sc[2];
-        if (W1) {
-          if (tid < 128) ws[tid] = Sc[0];
-        } else if (lane == 0) {
-          ws[wave] = Sc[0];
-        }
+      if (tid < 128) {
+        ws[2 * tid] = Sc[0];
+        ws[2 * tid + 1] = Sc[1];
       }
-    };
-    // Both 32-token halves are always multiplied: no accumulator depends on
-    // a branch inside the stage loop.
-    auto compute = [&](int buf) {
-      const char* wl = lds + buf * kStage;
-      const char* tl = wl + kW;
-      const uint32_t* tsc = reinterpret_cast<const uint32_t*>(tl + kA);
-      const uint32_t* wscl = reinterpret_cast<const uint32_t*>(tl + kA + kSc);
-      const int wrow = 32 * wave + lr;
-      if (FP4) {
-        // lane (r, h) multiplies 16-byte chunk 2q + h of its rows: MX block
-        // 2q + h of the stage, whose exponent is byte (2q + h) of the row's 8
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = 2 * q + lh;
-          const int dw = q >> 1, by = c & 3;
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, c));
-          const u32x4 b0 = *reinterpret_cast<const u32x4*>(tl + swz(lr, c));
-          const u32x4 d0 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, c));
-          const int sa = byte_of(wscl[2 * wrow + dw], by);
-          mfma_fp4(acc0, a0, b0, sa, byte_of(tsc[2 * lr + dw], by));
-          mfma_fp4(acc1, a0, d0, sa, byte_of(tsc[2 * (32 + lr) + dw], by));
-        }
-        return;
+    } else {
+      if (tid < kBM) ts[tid] = Sc[2];
+      if (W1) {
+        if (tid < 128) ws[tid] = Sc[0];
+      } else if (lane == 0) {
+        ws[wave] = Sc[0];
       }
-      const uint32_t ts0 = tsc[lr];
-      const uint32_t ts1 = tsc[32 + lr];
-      const uint32_t wsc = W1 ? wscl[wrow] : wscl[wave];
+    }
+  };
+  f32x16 acc0, acc1;
+  // Both 32-token halves are always multiplied: no accumulator depends on
+  // a branch inside the stage loop.
+  auto compute = [&](int buf) {
+    const char* wl = lds + buf * kStage;
+    const char* tl = wl + kW;
+    const uint32_t* tsc = reinterpret_cast<const uint32_t*>(tl + kA);
+    const uint32_t* wscl = reinterpret_cast<const uint32_t*>(tl + kA + kSc);
+    const int wrow = 32 * wave + lr;
+    if (FP4) {
+      // lane (r, h) multiplies 16-byte chunk 2q + h of its rows: MX block
+      // 2q + h of the stage, whose exponent is byte (2q + h) of the row's 8
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int ca = 4 * q + lh, cb = 4 * q + 2 + lh;
-        const int blk = 2 * q + lh;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, ca));
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, cb));
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(tl + swz(lr, ca));
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(tl + swz(lr, cb));
-        const u32x4 d0 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, ca));
-        const u32x4 d1 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, cb));
-        const int sa = byte_of(wsc, blk);
-        mfma_mx(acc0, a0, a1, b0, b1, sa, byte_of(ts0, blk));
-        mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
+      for (int q = 0; q < 4; ++q) {
+        const int c = 2 * q + lh;
+        const int dw = q >> 1, by = c & 3;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, c));
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(tl + swz(lr, c));
+        const u32x4 d0 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, c));
+        const int sa = byte_of(wscl[2 * wrow + dw], by);
+        mfma_fp4(acc0, a0, b0, sa, byte_of(tsc[2 * lr + dw], by));
+        mfma_fp4(acc1, a0, d0, sa, byte_of(tsc[2 * (32 + lr) + dw], by));
       }
-    };
+      return;
+    }
+    const uint32_t ts0 = tsc[lr];
+    const uint32_t ts1 = tsc[32 + lr];
+    const uint32_t wsc = W1 ? wscl[wrow] : wscl[wave];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int ca = 4 * q + lh, cb = 4 * q + 2 + lh;
+      const int blk = 2 * q + lh;
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, ca));
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(wl + swz(wrow, cb));
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(tl + swz(lr, ca));
+      const u32x4 b1 = *reinterpret_cast<const u32x4*>(tl + swz(lr, cb));
+      const u32x4 d0 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, ca));
+      const u32x4 d1 = *reinterpret_cast<const u32x4*>(tl + swz(32 + lr, cb));
+      const int sa = byte_of(wsc, blk);
+      mfma_mx(acc0, a0, a1, b0, b1, sa, byte_of(ts0, blk));
+      mfma_mx(acc1, a0, a1, d0, d1, sa, byte_of(ts1, blk));
+    }
+  };
+
+  // Items of this workgroup: it = slot, slot + per, ... within its XCD's chunk.
+  auto valid = [&](int it) { return it < chunk && xcd * chunk + it < n_items; };
+  if (!valid(slot)) return;
+  setup(xcd * chunk + slot, cur);
+  bool primed = false;  // buffer 0 / R1 / R0 already hold stages 0 / 1 / 2 of cur
+  for (int it = slot;;) {
+    const int itn = it + per;
+    // Prefetch across items needs three stages per item (the three stages in
+    // flight at an item's end must all belong to the next item).
+    cross = valid(itn) && S >= 3;
+    if (cross) setup(xcd * chunk + itn, nxt);
+    acc0 = f32x16{};
+    acc1 = f32x16{};
 
     // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
-    // s + 1 and R0 stage s + 2 (indices past the end repeat the last stage).
-    load(R0, S0, 0);
-    load(R1, S1, min(1, S - 1));
-    store(R0, S0, 0);
-    load(R0, S0, min(2, S - 1));
-    lds_barrier();
+    // s + 1 and R0 stage s + 2.
+    if (!primed) {
+      load(R0, S0, 0);
+      load(R1, S1, 1);
+      store(R0, S0, 0);
+      load(R0, S0, 2);
+      lds_barrier();
+    }
     for (int s = 0; s + 1 < S; s += 2) {
       compute(0);
       store(R1, S1, 1);
-      load(R1, S1, min(s + 3, S - 1));
+      load(R1, S1, s + 3);
       lds_barrier();
       compute(1);
       store(R0, S0, 0);
-      load(R0, S0, min(s + 4, S - 1));
+      load(R0, S0, s + 4);
       lds_barrier();
     }
     if (S & 1) {
       compute(0);
       lds_barrier();
+      if (cross) {   // R1, R0 hold stages 0, 1 of the next item
+        store(R1, S1, 0);
+#pragma unroll
+        for (int j = 0; j < 6; ++j) R1[j] = R0[j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S1[j] = S0[j];
+        load(R0, S0, S + 2);
+        lds_barrier();
+      }
     }
+    const int nt = cur.nt, row0 = cur.row0, rows = cur.rows;
 
     // Epilogue (as the BF16 kernels): acc[b][v] = C[row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
     if (MODE == 0) {
@@ -305,7 +349,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
             store4<uint16_t>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
         }
       }
-      float* xch = reinterpret_cast<float*>(lds);
+      float* xch = reinterpret_cast<float*>(lds + 2 * kStage);  // not the stage buffers
       if (wave >= 2) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -359,6 +403,15 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
         }
       }
     }
+    if (!cross) {
+      if (!valid(itn)) break;
+      setup(xcd * chunk + itn, cur);
+      primed = false;
+    } else {
+      cur = nxt;
+      primed = true;
+    }
+    it = itn;
   }
 }
 

@@ -36,6 +36,7 @@ def _check_prepared(q, s, w):
 @pytest.mark.parametrize("T,D,F,E,K,zipf,n_pad", [
     (300, 256, 256, 8, 2, None, 7),
     (200, 384, 128, 10, 3, 1.3, 0),     # skew, D = 3 x 128, empty experts likely
+    (1024, 768, 640, 16, 4, None, 0),   # several items per workgroup: prefetch across items
 ])
 def test_mx_1x32_forward_matches_oracle(B, T, D, F, E, K, zipf, n_pad):
     banner(f"mx 1x32 forward T={T} D={D} F={F} E={E} K={K} zipf={zipf}")

@@ -83,6 +83,7 @@ def test_fp4_weight_prep_bit_exact(B):
     (200, 768, 512, 10, 3, 1.3, 0),      # skew: hot experts over several tiles, empty experts
     (40, 512, 256, 16, 16, None, 3),     # K = 16, every expert per token
     (1, 256, 256, 4, 2, None, 0),        # a single token
+    (1024, 1280, 768, 16, 4, 1.0, 11),  # several items per workgroup: prefetch across items (odd stage counts)
 ])
 def test_mxfp4_forward_matches_oracle(B, T, D, F, E, K, zipf, n_pad):
     banner(f"mxfp4 forward T={T} D={D} F={F} E={E} K={K} zipf={zipf}")

@@ -79,6 +79,7 @@ def test_row_and_column_quantizers_bit_exact(B):
     (300, 256, 256, 8, 2, None, 7),
     (200, 384, 128, 10, 3, 1.3, 0),
     (64, 128, 256, 3, 1, None, 0),
+    (1024, 896, 640, 16, 4, 1.0, 11),   # several items per workgroup: prefetch across items (odd stage counts)
 ])
 def test_mx_forward_matches_oracle(B, T, D, F, E, K, zipf, n_pad):
     banner(f"mx forward T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
