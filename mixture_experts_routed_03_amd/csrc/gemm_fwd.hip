@@ -170,12 +170,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
     u32x4 R0[8], R1[8];
     // NB (a compile-time 32-row block count per loop copy: 1, 2 or 4) is the
     // number of token blocks loaded and multiplied.
+    // Stages past the end (the pipeline's last two loads) are never used:
+    // their weight loads read token rows, which sit in L2, instead of
+    // re-reading the last weight stage (a non-temporal line that HBM would
+    // have to supply again).
     auto load = [&](u32x4* R, int s, auto nb_c) {
       constexpr int NB = decltype(nb_c)::value;
-      const int64_t off = int64_t(s) * 128;
+      const bool past = s >= S;
+      const int64_t off = int64_t(past ? S - 1 : s) * 128;
 #pragma unroll
       for (int j = 0; j < 4; ++j)   // weights: non-temporal (streamed once per m-tile)
-        R[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + off));
+        R[j] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>((past ? tsrc[j] : wsrc[j]) + off));
 #pragma unroll
       for (int j = 0; j < NB; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
     };
@@ -211,21 +217,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
     };
 
     // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
-    // s + 1 and R0 stage s + 2 (indices past the end repeat the last stage).
+    // s + 1 and R0 stage s + 2.
     auto run = [&](auto nb_c) {
       load(R0, 0, nb_c);
-      load(R1, min(1, S - 1), nb_c);
+      load(R1, 1, nb_c);
       store(R0, 0, nb_c);
-      load(R0, min(2, S - 1), nb_c);
+      load(R0, 2, nb_c);
       lds_barrier();
       for (int s = 0; s + 1 < S; s += 2) {
         compute(0, nb_c);
         store(R1, 1, nb_c);
-        load(R1, min(s + 3, S - 1), nb_c);
+        load(R1, s + 3, nb_c);
         lds_barrier();
         compute(1, nb_c);
         store(R0, 0, nb_c);
-        load(R0, min(s + 4, S - 1), nb_c);
+        load(R0, s + 4, nb_c);
         lds_barrier();
       }
       if (S & 1) {
