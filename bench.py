@@ -77,16 +77,20 @@ SYMBOLS = {
         "w2_scatter": ("moe::k_gemm_fwd<unsigned short, 1>", ["gemm_fwd.hip"]),
         "w2_dgrad_swiglu": ("moe::k_gemm_dgrad<0>", ["gemm_bwd.hip"]),
         "w13_dgrad": ("moe::k_gemm_dgrad<1>", ["gemm_bwd.hip"]),
-        "w2_wgrad": ("moe::k_gemm_wgrad<unsigned short, 2>", ["gemm_bwd.hip"]),
-        "w13_wgrad": ("moe::k_gemm_wgrad<unsigned short, 13>", ["gemm_bwd.hip"]),
+        "w2_wgrad": ("moe::k_gemm_wgrad<unsigned short, 2, 0>", ["gemm_bwd.hip"]),
+        "w13_wgrad": ("moe::k_gemm_wgrad<unsigned short, 13, 0>", ["gemm_bwd.hip"]),
     },
     "mxfp8": {
-        "w13_swiglu": ("moe::k_mx_fwd<0>", ["gemm_mx.hip"]),
-        "w2_scatter": ("moe::k_mx_fwd<1>", ["gemm_mx.hip"]),
+        "w13_swiglu": ("moe::k_mx_fwd<0, 0, 0>", ["gemm_mx.hip"]),
+        "w2_scatter": ("moe::k_mx_fwd<1, 0, 0>", ["gemm_mx.hip"]),
         "w2_dgrad_swiglu": ("moe::k_mx_dgrad<0>", ["gemm_mx.hip"]),
         "w13_dgrad": ("moe::k_mx_dgrad<1>", ["gemm_mx.hip"]),
-        "w2_wgrad": ("moe::k_mx_wgrad<unsigned short, 2>", ["gemm_mx.hip"]),
-        "w13_wgrad": ("moe::k_mx_wgrad<unsigned short, 13>", ["gemm_mx.hip"]),
+        "w2_wgrad": ("moe::k_mx_wgrad<unsigned short, 2, 0>", ["gemm_mx.hip"]),
+        "w13_wgrad": ("moe::k_mx_wgrad<unsigned short, 13, 0>", ["gemm_mx.hip"]),
+    },
+    "mxfp8_1x32": {
+        "w13_swiglu": ("moe::k_mx_fwd<0, 1, 0>", ["gemm_mx.hip"]),
+        "w2_scatter": ("moe::k_mx_fwd<1, 1, 0>", ["gemm_mx.hip"]),
     },
     "mxfp4": {
         "w13_swiglu": ("moe::k_mx_fwd<0, 1, 1>", ["gemm_mx.hip"]),
@@ -481,7 +485,8 @@ def main():
     ach = kernels[dom]["GB/s"]
     prec_dom = "bf16" if dom.startswith("shared:") else cfg.prec
     # counters were taken at each workload's own width
-    traffic = None if args.width else measured_traffic(args.workload, prec_dom, dom_name)
+    sym_key = "mxfp8_1x32" if prec_dom == "mxfp8" and cfg.mx_w1x32 else prec_dom
+    traffic = None if args.width else measured_traffic(args.workload, sym_key, dom_name)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": int(alg_per_launch),
