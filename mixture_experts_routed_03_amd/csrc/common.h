@@ -47,7 +47,11 @@ struct RouteHdr {
   int32_t n_mt;         // 64-row stages over all experts (sum of ceil(count / 64))
   uint32_t status;      // MOE_STATUS_* bits
   int32_t max_count;    // largest expert row count
-  int32_t pad[10];
+  // Work queues of the persistent GEMM launches: per XCD, the next item
+  // ticket [0, 8) and the count of workgroups that found the queue empty
+  // [8, 16).  Zeroed by routing; the last workgroup of a launch to finish
+  // on an XCD zeroes that XCD's pair again for the next launch.
+  uint32_t wq[16];
   LayerRec rec;
 };
 static_assert(sizeof(RouteHdr) <= 512, "route header must fit its slot");
@@ -304,6 +308,24 @@ __device__ __forceinline__ void acc_store4(uint16_t* p, const float* v) {
 
 // Number of XCDs of the MI355X; workgroups are dispatched round-robin over them.
 constexpr int kXcds = 8;
+
+// Per-XCD work queue of a persistent GEMM launch (RouteHdr::wq): the
+// workgroups of an XCD take that XCD's items in order, each the next free one
+// when it is ready, so items that share a weight tile (the m-tiles of one
+// expert and n-tile) run side by side even when item costs differ.  Called by
+// one thread of the workgroup.
+__device__ __forceinline__ int wq_take(const RouteHdr* hdr, int xcd) {
+  return int(atomicAdd(const_cast<uint32_t*>(&hdr->wq[xcd]), 1u));
+}
+// A workgroup that found its XCD's queue empty: the last of the XCD's `per`
+// workgroups re-arms the queue for the next launch.
+__device__ __forceinline__ void wq_finish(const RouteHdr* hdr, int xcd, int per) {
+  uint32_t* wq = const_cast<uint32_t*>(hdr->wq);
+  if (atomicAdd(&wq[kXcds + xcd], 1u) == uint32_t(per - 1)) {
+    atomicExch(&wq[xcd], 0u);
+    atomicExch(&wq[kXcds + xcd], 0u);
+  }
+}
 
 // Expert of grouped-GEMM work item w: the largest e with mtoff[e] * NT <= w
 // (mtoff = the m-tile prefix, NT = n-tiles per expert).  A workgroup's items

@@ -125,7 +125,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
 
   const RouteHdr* hdr = a.hdr;
   const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   // a.mtoff is the m-tile prefix (128-row tiles for experts with more than
   // 64 rows); the XCDs split the items by token rows
@@ -135,8 +134,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
   const int64_t N = a.N;
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
+  // items [first, last) of this XCD come from its work queue, in order
+  __shared__ int s_next;
+  if (tid == 0) s_next = wq_take(hdr, xcd);
+  lds_barrier();
   int e_prev = -1;  // expert of this workgroup's previous item
-  for (int w = first + slot; w < last; w += per) {
+  for (int w = first + s_next; w < last;) {
     const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
     e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
@@ -169,14 +172,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
     // accumulator depends on a branch inside the stage loop); the token stage
     // holds 64 rows per pass of the 512 threads (rows past the tile repeat its
     // last row).
-    auto load = [&](u32x4* R, int s, auto nb_c) {
+    auto load = [&](u32x4* R, int s, auto nb_c, auto tm_c) {
       constexpr int NB = decltype(nb_c)::value;
+      constexpr bool TM = decltype(tm_c)::value;
       const uint16_t* p = wsrc + int64_t(s) * 64 * N;
       // weights stream through once: non-temporal loads keep them from
       // evicting the token tiles the other n-tiles of this expert re-read
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        R[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 16 * i * N));
+      for (int i = 0; i < 4; ++i) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(p + 16 * i * N);
+        if constexpr (TM)
+          R[i] = *src;
+        else
+          R[i] = __builtin_nontemporal_load(src);
+      }
 #pragma unroll
       for (int j = 0; j < (NB + 3) / 4 + (NB == 4); ++j)
         R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
@@ -210,20 +219,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
     };
     // Pipeline as in the forward kernels: LDS buffer 0 holds stage s, R1
     // stage s + 1 and R0 stage s + 2 (indices past the end repeat the last).
-    auto run = [&](auto nb_c) {
-      load(R0, 0, nb_c);
-      load(R1, min(1, S - 1), nb_c);
+    auto run = [&](auto nb_c, auto tm_c) {
+      load(R0, 0, nb_c, tm_c);
+      load(R1, min(1, S - 1), nb_c, tm_c);
       store(R0, 0, nb_c);
-      load(R0, min(2, S - 1), nb_c);
+      load(R0, min(2, S - 1), nb_c, tm_c);
       lds_barrier();
       for (int s = 0; s + 1 < S; s += 2) {
         compute(0, nb_c);
         store(R1, 1, nb_c);
-        load(R1, min(s + 3, S - 1), nb_c);
+        load(R1, min(s + 3, S - 1), nb_c, tm_c);
         lds_barrier();
         compute(1, nb_c);
         store(R0, 0, nb_c);
-        load(R0, min(s + 4, S - 1), nb_c);
+        load(R0, min(s + 4, S - 1), nb_c, tm_c);
         lds_barrier();
       }
       if (S & 1) {
@@ -231,18 +240,30 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
         lds_barrier();
       }
     };
-    if (rows > 64)
-      run(std::integral_constant<int, 4>{});
-    else if (rows > 32)
-      run(std::integral_constant<int, 2>{});
+    // An expert cut into several m-tiles re-reads its weight tiles once per
+    // m-tile; those items run side by side on one XCD, so its weights are
+    // loaded with the default (L2-allocating) policy to serve the sibling
+    // tiles from L2.  A single-tile expert streams its weights non-temporally.
+    auto go = [&](auto tm_c) {
+      if (rows > 64)
+        run(std::integral_constant<int, 4>{}, tm_c);
+      else if (rows > 32)
+        run(std::integral_constant<int, 2>{}, tm_c);
+      else
+        run(std::integral_constant<int, 1>{}, tm_c);
+    };
+    if (mt_e > 1)
+      go(std::true_type{});
     else
-      run(std::integral_constant<int, 1>{});
-    if (32 * wave >= ncols) continue;
+      go(std::false_type{});
+    // the next item, taken while this one's epilogue runs
+    int taken = 0;
+    if (tid == 0) taken = wq_take(hdr, xcd);
 
     // acc[b][v]: output column 32*wave + 8*(v/4) + 4*lh + v%4, token 32*b + lr
     const int col = nt * 256 + 32 * wave + 4 * lh;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < 4 && 32 * wave < ncols; ++b) {
       const int m = 32 * b + lr;
       if (m >= rows) continue;
       const int64_t row = row0 + m;
@@ -281,7 +302,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
                         acc[b][4 * g4 + 3]);
       }
     }
+    if (tid == 0) s_next = taken;
+    lds_barrier();
+    w = first + s_next;
   }
+  if (tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // ------------------------------------------------------------------ WGRAD

@@ -127,14 +127,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
   const int64_t row_bytes = int64_t(a.Kd) * ES;
 
   const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
   const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
   const int S = int(row_bytes / 128);
 
+  // items [first, last) of this XCD come from its work queue, in order
+  __shared__ int s_next;
+  if (tid == 0) s_next = wq_take(hdr, xcd);
+  lds_barrier();
   int e_prev = -1;  // expert of this workgroup's previous item
-  for (int w = first + slot; w < last; w += per) {
+  for (int w = first + s_next; w < last;) {
     const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
     e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
@@ -174,14 +177,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
     // their weight loads read token rows, which sit in L2, instead of
     // re-reading the last weight stage (a non-temporal line that HBM would
     // have to supply again).
-    auto load = [&](u32x4* R, int s, auto nb_c) {
+    auto load = [&](u32x4* R, int s, auto nb_c, auto tm_c) {
       constexpr int NB = decltype(nb_c)::value;
+      constexpr bool TM = decltype(tm_c)::value;
       const bool past = s >= S;
       const int64_t off = int64_t(past ? S - 1 : s) * 128;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)   // weights: non-temporal (streamed once per m-tile)
-        R[j] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>((past ? tsrc[j] : wsrc[j]) + off));
+      for (int j = 0; j < 4; ++j) {   // weights: non-temporal unless TM (see below)
+        const u32x4* src = reinterpret_cast<const u32x4*>((past ? tsrc[j] : wsrc[j]) + off);
+        if constexpr (TM)
+          R[j] = *src;
+        else
+          R[j] = __builtin_nontemporal_load(src);
+      }
 #pragma unroll
       for (int j = 0; j < NB; ++j) R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + off);
     };
@@ -218,20 +226,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
 
     // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
     // s + 1 and R0 stage s + 2.
-    auto run = [&](auto nb_c) {
-      load(R0, 0, nb_c);
-      load(R1, 1, nb_c);
+    auto run = [&](auto nb_c, auto tm_c) {
+      load(R0, 0, nb_c, tm_c);
+      load(R1, 1, nb_c, tm_c);
       store(R0, 0, nb_c);
-      load(R0, 2, nb_c);
+      load(R0, 2, nb_c, tm_c);
       lds_barrier();
       for (int s = 0; s + 1 < S; s += 2) {
         compute(0, nb_c);
         store(R1, 1, nb_c);
-        load(R1, s + 3, nb_c);
+        load(R1, s + 3, nb_c, tm_c);
         lds_barrier();
         compute(1, nb_c);
         store(R0, 0, nb_c);
-        load(R0, s + 4, nb_c);
+        load(R0, s + 4, nb_c, tm_c);
         lds_barrier();
       }
       if (S & 1) {
@@ -239,12 +247,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
         lds_barrier();
       }
     };
-    if (rows > 64)
-      run(std::integral_constant<int, 4>{});
-    else if (rows > 32)
-      run(std::integral_constant<int, 2>{});
+    // An expert cut into several m-tiles re-reads its weight tiles once per
+    // m-tile; those items run side by side on one XCD, so its weights are
+    // loaded with the default (L2-allocating) policy to serve the sibling
+    // tiles from L2.  A single-tile expert streams its weights non-temporally.
+    auto go = [&](auto tm_c) {
+      if (rows > 64)
+        run(std::integral_constant<int, 4>{}, tm_c);
+      else if (rows > 32)
+        run(std::integral_constant<int, 2>{}, tm_c);
+      else
+        run(std::integral_constant<int, 1>{}, tm_c);
+    };
+    if (mt_e > 1)
+      go(std::true_type{});
     else
-      run(std::integral_constant<int, 1>{});
+      go(std::false_type{});
+
+    // the next item, taken while this one's epilogue runs
+    int taken = 0;
+    if (tid == 0) taken = wq_take(hdr, xcd);
 
     // ---------------------------------------------------------- epilogue
     // acc[b][v] is C[weight row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
@@ -314,7 +336,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
         }
       }
     }
+    if (tid == 0) s_next = taken;
+    lds_barrier();
+    w = first + s_next;
   }
+  if (tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // Persistent grid size: a multiple of the XCD count, at most the upper bound

@@ -171,6 +171,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     hdr->max_count = red[1];
     hdr->rec.done = 0;
   }
+  if (tid < 2 * kXcds) hdr->wq[tid] = 0u;
 }
 
 __global__ __launch_bounds__(256) void k_route_rank(const int32_t* __restrict__ ids, int64_t n,
