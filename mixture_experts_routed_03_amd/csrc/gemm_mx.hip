@@ -126,7 +126,6 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   const int KB = Kd / 32;           // scale bytes per row
   const int Kb = FP4 ? Kd / 2 : Kd; // code bytes per row
   const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   const int chunk = (n_items + kXcds - 1) / kXcds;
   const int S = Kb / 128;
@@ -286,13 +285,20 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     }
   };
 
-  // Items of this workgroup: it = slot, slot + per, ... within its XCD's chunk.
+  // Items of this XCD's chunk come from its work queue, in order; a
+  // workgroup holds two tickets (its current and next item) and takes the
+  // one after while an item's epilogue runs.
   auto valid = [&](int it) { return it < chunk && xcd * chunk + it < n_items; };
-  if (!valid(slot)) return;
-  setup(xcd * chunk + slot, cur);
+  __shared__ int s_q[2];
+  if (tid == 0) {
+    s_q[0] = wq_take(hdr, xcd);
+    s_q[1] = wq_take(hdr, xcd);
+  }
+  lds_barrier();
+  int it = s_q[0], itn = s_q[1];
+  if (valid(it)) setup(xcd * chunk + it, cur);
   bool primed = false;  // buffer 0 / R1 / R0 already hold stages 0 / 1 / 2 of cur
-  for (int it = slot;;) {
-    const int itn = it + per;
+  for (; valid(it);) {
     // Prefetch across items needs three stages per item (the three stages in
     // flight at an item's end must all belong to the next item).
     cross = valid(itn) && S >= 3;
@@ -333,6 +339,8 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
       }
     }
     const int nt = cur.nt, row0 = cur.row0, rows = cur.rows;
+    int taken = 0;
+    if (tid == 0) taken = wq_take(hdr, xcd);
 
     // Epilogue (as the BF16 kernels): acc[b][v] = C[row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
     if (MODE == 0) {
@@ -403,16 +411,19 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
         }
       }
     }
+    if (tid == 0) s_q[0] = taken;
+    lds_barrier();
     if (!cross) {
-      if (!valid(itn)) break;
-      setup(xcd * chunk + itn, cur);
+      if (valid(itn)) setup(xcd * chunk + itn, cur);
       primed = false;
     } else {
       cur = nxt;
       primed = true;
     }
     it = itn;
+    itn = s_q[0];
   }
+  if (tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // ------------------------------------------------------------------ DGRAD
@@ -460,7 +471,6 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
 
   const RouteHdr* hdr = a.hdr;
   const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
   // 64-row m-tiles (a.mtoff = a.stoff); the XCDs split the items by token rows
   const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
@@ -472,8 +482,12 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
   const int NB32 = int(N / 32);
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
+  // items [first, last) of this XCD come from its work queue, in order
+  __shared__ int s_next;
+  if (tid == 0) s_next = wq_take(hdr, xcd);
+  lds_barrier();
   int e_prev = -1;  // expert of this workgroup's previous item
-  for (int w = first + slot; w < last; w += per) {
+  for (int w = first + s_next; w < last;) {
     const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
     e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
@@ -587,11 +601,13 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
       run(std::integral_constant<int, 2>{});
     else
       run(std::integral_constant<int, 1>{});
-    if (32 * wave >= ncols) continue;
+    // the next item, taken while this one's epilogue runs
+    int taken = 0;
+    if (tid == 0) taken = wq_take(hdr, xcd);
 
     const int col = nt * 256 + 32 * wave + 4 * lh;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2 && 32 * wave < ncols; ++b) {
       const int m = 32 * b + lr;
       if (m >= rows) continue;
       const int64_t row = row0 + m;
@@ -626,7 +642,11 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
                         acc[b][4 * g4 + 3]);
       }
     }
+    if (tid == 0) s_next = taken;
+    lds_barrier();
+    w = first + s_next;
   }
+  if (tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // ------------------------------------------------------------------ WGRAD
