@@ -189,49 +189,75 @@ __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
 }
 
 // ------------------------------------------------------------------ column bundles (32x1)
-// One workgroup per (32-row block of the padded row space, 256 columns):
-// thread = column; reads 32 rows down its column (a wave reads 128 contiguous
-// bytes per row), writes 32 contiguous code bytes and one exponent.
+// One workgroup per (32-row block of the padded row space, 256 columns).  The
+// block's rows are loaded row-wise with 16-byte loads (32 lanes per 512-byte
+// row segment) into LDS; then each thread takes one column, reads its 32
+// values from LDS, and writes 32 contiguous code bytes and one exponent.
 __global__ __launch_bounds__(256) void k_colq(ColqArgs a) {
+  constexpr int kRow = 256 + 8;              // LDS row pitch (bf16), 16-byte aligned
+  __shared__ __attribute__((aligned(16))) uint16_t tile[32 * kRow];
+  __shared__ int s_lo, s_e;
   const RouteHdr* hdr = a.hdr;
   // replay_only: 1 = run only when the layer replays, 2 = only when it saves
   if (a.replay_only == 1 && !hdr->rec.replay) return;
   if (a.replay_only == 2 && hdr->rec.replay) return;
   const int gb = blockIdx.x;                 // 32-row block in the padded row space
-  if (gb * 32 >= hdr->Rpad) return;
-  const int col = blockIdx.y * 256 + threadIdx.x;
-  if (col >= a.N) return;
-  // expert of this block: the largest e with poffsets[e] <= 32*gb
-  int lo = 0, hi = a.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.poffsets[mid] <= gb * 32)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  const int e = lo;
-  const int pbase = a.poffsets[e];
-  const int mp = a.poffsets[e + 1] - pbase;
-  const int mb = (gb * 32 - pbase) / 32;     // block index inside the expert
-  const int r0 = a.offsets[e] + mb * 32;
-  const int rows = min(32, a.offsets[e + 1] - r0);
+  const int key = gb * 32;
+  if (key >= hdr->Rpad) return;
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.y * 256;
+  const int N = a.N;
   const uint16_t* src = a.src_slot >= 0 ? global_ptr<const uint16_t>(rec_ptr(hdr, a.src_slot))
                                          : reinterpret_cast<const uint16_t*>(a.src);
   uint8_t* q = a.q_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.q_slot)) : a.q;
   uint8_t* s = a.s_slot >= 0 ? global_ptr<uint8_t>(rec_ptr(hdr, a.s_slot)) : a.s;
   if (!src) {
-    if (gb == 0 && threadIdx.x == 0 && blockIdx.y == 0)
+    if (gb == 0 && tid == 0 && blockIdx.y == 0)
       atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
-  const int N = a.N;
+  // Expert of this block: the largest e < E with poffsets[e] <= key, found by
+  // two rounds of parallel probes instead of a chain of dependent loads.
+  const int E = a.E;
+  const int step = (E + 255) / 256;
+  if (tid == 0) {
+    s_lo = 0;
+    s_e = 0;
+  }
+  __syncthreads();
+  if (tid * step < E && a.poffsets[tid * step] <= key) atomicMax(&s_lo, tid * step);
+  __syncthreads();
+  const int lo = s_lo;
+  if (tid < step && lo + tid < E && a.poffsets[lo + tid] <= key) atomicMax(&s_e, lo + tid);
+  __syncthreads();
+  const int e = s_e;
+  const int pbase = a.poffsets[e];
+  const int mp = a.poffsets[e + 1] - pbase;
+  const int mb = (key - pbase) / 32;         // block index inside the expert
+  const int r0 = a.offsets[e] + mb * 32;
+  const int rows = min(32, a.offsets[e + 1] - r0);
+
+  // rows r = t/32 + 8j, 16-byte chunk t%32; rows past the expert's end are zero
+  const int cc = tid & 31;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = (tid >> 5) + 8 * j;
+    const int col = c0 + 8 * cc;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < rows && col < N) {
+      const int64_t srow = a.gather ? a.gather[r0 + r] / a.K : r0 + r;
+      v = *reinterpret_cast<const u32x4*>(src + srow * N + col);
+    }
+    *reinterpret_cast<u32x4*>(tile + r * kRow + 8 * cc) = v;
+  }
+  __syncthreads();
+  const int col = c0 + tid;
+  if (col >= N) return;
   float v[32];
   float amax = 0.0f;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    const int64_t srow = a.gather ? a.gather[r0 + min(r, rows - 1)] / a.K : r0 + r;
-    v[r] = r < rows ? bf16_to_f32(src[srow * N + col]) : 0.0f;
+    v[r] = bf16_to_f32(tile[r * kRow + tid]);
     amax = fmaxf(amax, fabsf(v[r]));
   }
   const int ex = e8m0_exp(amax);
