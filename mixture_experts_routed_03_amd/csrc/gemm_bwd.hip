@@ -135,11 +135,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
   // items [first, last) of this XCD come from its work queue, in order
+  // (with skewed routing: when some expert spans several m-tiles; otherwise
+  // dealt statically, slot, slot + per, ..., which costs no atomics)
+  const bool dyn = hdr->max_count > kBMX;
+  const int slot = blockIdx.x / kXcds;
   __shared__ int s_next;
-  if (tid == 0) s_next = wq_take(hdr, xcd);
+  if (dyn && tid == 0) s_next = wq_take(hdr, xcd);
   lds_barrier();
   int e_prev = -1;  // expert of this workgroup's previous item
-  for (int w = first + s_next; w < last;) {
+  for (int w = dyn ? first + s_next : first + slot; w < last;) {
     const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
     e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
       go(std::false_type{});
     // the next item, taken while this one's epilogue runs
     int taken = 0;
-    if (tid == 0) taken = wq_take(hdr, xcd);
+    if (dyn && tid == 0) taken = wq_take(hdr, xcd);
 
     // acc[b][v]: output column 32*wave + 8*(v/4) + 4*lh + v%4, token 32*b + lr
     const int col = nt * 256 + 32 * wave + 4 * lh;
@@ -302,11 +306,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
                         acc[b][4 * g4 + 3]);
       }
     }
-    if (tid == 0) s_next = taken;
-    lds_barrier();
-    w = first + s_next;
+    if (dyn) {
+      if (tid == 0) s_next = taken;
+      lds_barrier();
+      w = first + s_next;
+    } else {
+      w += per;
+    }
   }
-  if (tid == 0) wq_finish(hdr, xcd, per);
+  if (dyn && tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // ------------------------------------------------------------------ WGRAD

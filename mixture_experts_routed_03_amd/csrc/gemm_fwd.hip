@@ -133,11 +133,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
   const int S = int(row_bytes / 128);
 
   // items [first, last) of this XCD come from its work queue, in order
+  // (with skewed routing: when some expert spans several m-tiles; otherwise
+  // dealt statically, slot, slot + per, ..., which costs no atomics)
+  const bool dyn = hdr->max_count > kBMX;
+  const int slot = blockIdx.x / kXcds;
   __shared__ int s_next;
-  if (tid == 0) s_next = wq_take(hdr, xcd);
+  if (dyn && tid == 0) s_next = wq_take(hdr, xcd);
   lds_barrier();
   int e_prev = -1;  // expert of this workgroup's previous item
-  for (int w = first + s_next; w < last;) {
+  for (int w = dyn ? first + s_next : first + slot; w < last;) {
     const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
     e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
 
     // the next item, taken while this one's epilogue runs
     int taken = 0;
-    if (tid == 0) taken = wq_take(hdr, xcd);
+    if (dyn && tid == 0) taken = wq_take(hdr, xcd);
 
     // ---------------------------------------------------------- epilogue
     // acc[b][v] is C[weight row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
@@ -336,11 +340,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
         }
       }
     }
-    if (tid == 0) s_next = taken;
-    lds_barrier();
-    w = first + s_next;
+    if (dyn) {
+      if (tid == 0) s_next = taken;
+      lds_barrier();
+      w = first + s_next;
+    } else {
+      w += per;
+    }
   }
-  if (tid == 0) wq_finish(hdr, xcd, per);
+  if (dyn && tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // Persistent grid size: a multiple of the XCD count, at most the upper bound

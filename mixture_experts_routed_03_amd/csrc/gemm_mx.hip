@@ -285,17 +285,21 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     }
   };
 
-  // Items of this XCD's chunk come from its work queue, in order; a
-  // workgroup holds two tickets (its current and next item) and takes the
-  // one after while an item's epilogue runs.
+  // Items of this XCD's chunk come from its work queue, in order, when some
+  // expert spans several m-tiles (skewed routing); a workgroup then holds two
+  // tickets (its current and next item) and takes the one after while an
+  // item's epilogue runs.  Otherwise they are dealt statically (slot,
+  // slot + per, ...), which costs no atomics.
   auto valid = [&](int it) { return it < chunk && xcd * chunk + it < n_items; };
+  const bool dyn = hdr->max_count > kBM;
+  const int slot = blockIdx.x / kXcds;
   __shared__ int s_q[2];
-  if (tid == 0) {
+  if (dyn && tid == 0) {
     s_q[0] = wq_take(hdr, xcd);
     s_q[1] = wq_take(hdr, xcd);
   }
   lds_barrier();
-  int it = s_q[0], itn = s_q[1];
+  int it = dyn ? s_q[0] : slot, itn = dyn ? s_q[1] : slot + per;
   if (valid(it)) setup(xcd * chunk + it, cur);
   bool primed = false;  // buffer 0 / R1 / R0 already hold stages 0 / 1 / 2 of cur
   for (; valid(it);) {
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     }
     const int nt = cur.nt, row0 = cur.row0, rows = cur.rows;
     int taken = 0;
-    if (tid == 0) taken = wq_take(hdr, xcd);
+    if (dyn && tid == 0) taken = wq_take(hdr, xcd);
 
     // Epilogue (as the BF16 kernels): acc[b][v] = C[row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
     if (MODE == 0) {
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
         }
       }
     }
-    if (tid == 0) s_q[0] = taken;
+    if (dyn && tid == 0) s_q[0] = taken;
     lds_barrier();
     if (!cross) {
       if (valid(itn)) setup(xcd * chunk + itn, cur);
@@ -421,9 +425,9 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
       primed = true;
     }
     it = itn;
-    itn = s_q[0];
+    itn = dyn ? s_q[0] : itn + per;
   }
-  if (tid == 0) wq_finish(hdr, xcd, per);
+  if (dyn && tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // ------------------------------------------------------------------ DGRAD
@@ -483,11 +487,15 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
   // items [first, last) of this XCD come from its work queue, in order
+  // (with skewed routing: when some expert spans several m-tiles; otherwise
+  // dealt statically, slot, slot + per, ..., which costs no atomics)
+  const bool dyn = hdr->max_count > kBM;
+  const int slot = blockIdx.x / kXcds;
   __shared__ int s_next;
-  if (tid == 0) s_next = wq_take(hdr, xcd);
+  if (dyn && tid == 0) s_next = wq_take(hdr, xcd);
   lds_barrier();
   int e_prev = -1;  // expert of this workgroup's previous item
-  for (int w = first + s_next; w < last;) {
+  for (int w = dyn ? first + s_next : first + slot; w < last;) {
     const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
     e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
@@ -603,7 +611,7 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
       run(std::integral_constant<int, 1>{});
     // the next item, taken while this one's epilogue runs
     int taken = 0;
-    if (tid == 0) taken = wq_take(hdr, xcd);
+    if (dyn && tid == 0) taken = wq_take(hdr, xcd);
 
     const int col = nt * 256 + 32 * wave + 4 * lh;
 #pragma unroll
@@ -642,11 +650,15 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
                         acc[b][4 * g4 + 3]);
       }
     }
-    if (tid == 0) s_next = taken;
-    lds_barrier();
-    w = first + s_next;
+    if (dyn) {
+      if (tid == 0) s_next = taken;
+      lds_barrier();
+      w = first + s_next;
+    } else {
+      w += per;
+    }
   }
-  if (tid == 0) wq_finish(hdr, xcd, per);
+  if (dyn && tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // ------------------------------------------------------------------ WGRAD

@@ -9,7 +9,8 @@
 // built on the GPU - which is what happens here, with no host sync.
 // Dist-MoE explainer section 01: id -1 disables a route.
 //
-// Deterministic counting sort in three launches:
+// Deterministic counting sort in three launches (one for small calls, see
+// k_route_small):
 //   hist : one workgroup per chunk of 256 routes, LDS atomics -> chunk_hist[c][e]
 //   scan : one workgroup; counts[e] = sum_c chunk_hist[c][e], exclusive scans
 //          of counts, of counts rounded up to 32 and of m-tiles; the chunk
@@ -200,6 +201,107 @@ __global__ __launch_bounds__(256) void k_route_rank(const int32_t* __restrict__ 
   route_to_row[r] = row;
 }
 
+// Up to kSmallRoutes routes (decode steps): the whole counting sort in one
+// launch of one workgroup.  The ids sit in LDS; counts come from LDS atomics
+// (their order does not matter, only their sums); offsets from the same
+// block scan as k_route_scan; a route's row is its expert's offset plus the
+// number of earlier routes of that expert (the stable order).  Writes the
+// same outputs as the three launches (no chunk histograms).
+constexpr int kSmallRoutes = 1024;
+
+__global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict__ ids, int n,
+                                                      int E, int T,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ poffsets,
+                                                      int32_t* __restrict__ mtoff,
+                                                      int32_t* __restrict__ gtoff,
+                                                      int32_t* __restrict__ sorted_route,
+                                                      int32_t* __restrict__ route_to_row,
+                                                      RouteHdr* __restrict__ hdr) {
+  __shared__ int32_t sid[kSmallRoutes];
+  __shared__ int32_t cnt[kMaxE];   // counts, then each expert's first row
+  __shared__ int sh[64];
+  __shared__ int carry[4];
+  __shared__ int s_mx;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  if (tid == 0) {
+    carry[0] = carry[1] = carry[2] = carry[3] = 0;
+    s_mx = 0;
+  }
+  int bad = 0;
+  int id = -1;
+  if (tid < n) {
+    id = ids[tid];
+    if (id < -1 || id >= E) {
+      bad = 1;
+      id = -1;
+    }
+  }
+  sid[tid] = id;
+  __syncthreads();
+  if (id >= 0) atomicAdd(&cnt[id], 1);
+  bad = __syncthreads_or(bad);
+  int mx = 0;
+  for (int e0 = 0; e0 < E; e0 += 1024) {
+    const int e = e0 + tid;
+    const int s = e < E ? cnt[e] : 0;
+    const int sp = (s + kMxBlock - 1) / kMxBlock * kMxBlock;
+    const int sm = (s + kBM - 1) / kBM;
+    const int sg = (s + gemm_tile_rows(s) - 1) / gemm_tile_rows(s);
+    mx = max(mx, s);
+    int v[4] = {s, sp, sm, sg};
+    block_scan<4>(v, sh);
+    const int ic = v[0], ip = v[1], im = v[2], ig = v[3];
+    const int oc = carry[0] + ic - s;
+    if (e < E) {
+      counts[e] = s;
+      offsets[e] = oc;
+      poffsets[e] = carry[1] + ip - sp;
+      mtoff[e] = carry[2] + im - sm;
+      gtoff[e] = carry[3] + ig - sg;
+      cnt[e] = oc;
+    }
+    __syncthreads();   // every thread has read the carries of this pass
+    if (tid == 1023) {
+      carry[0] += ic;
+      carry[1] += ip;
+      carry[2] += im;
+      carry[3] += ig;
+    }
+    __syncthreads();
+  }
+  if (tid < n) {
+    if (id < 0) {
+      route_to_row[tid] = -1;
+    } else {
+      // earlier routes of the same expert (every lane reads the same word per step)
+      int rank = 0;
+      for (int q = 0; q < tid; ++q) rank += (sid[q] == id);
+      const int row = cnt[id] + rank;
+      sorted_route[row] = tid;
+      route_to_row[tid] = row;
+    }
+  }
+  atomicMax(&s_mx, mx);
+  __syncthreads();
+  if (tid == 0) {
+    offsets[E] = carry[0];
+    poffsets[E] = carry[1];
+    mtoff[E] = carry[2];
+    gtoff[E] = carry[3];
+    hdr->T = T;
+    hdr->R = carry[0];
+    hdr->Rpad = carry[1];
+    hdr->n_mt = carry[2];
+    hdr->status = bad ? uint32_t(MOE_STATUS_BAD_ID) : 0u;
+    hdr->max_count = s_mx;
+    hdr->rec.done = 0;
+  }
+  if (tid < 2 * kXcds) hdr->wq[tid] = 0u;
+}
+
 // ------------------------------------------------------------ planner
 // Dist-MoE explainer section 04: before saving a layer's full state the
 // planner replays instead when saved bytes + this layer's full state +
@@ -280,6 +382,18 @@ __global__ void k_arena_reset(uint64_t arena) {
 hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
                         const RouteLayout& L, hipStream_t s) {
   const int64_t n = T * K;
+  if (n <= kSmallRoutes && E <= kMaxE) {
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, ids, int(n), E, int(T),
+                       reinterpret_cast<int32_t*>(ws + L.counts),
+                       reinterpret_cast<int32_t*>(ws + L.offsets),
+                       reinterpret_cast<int32_t*>(ws + L.poffsets),
+                       reinterpret_cast<int32_t*>(ws + L.mtoff),
+                       reinterpret_cast<int32_t*>(ws + L.gtoff),
+                       reinterpret_cast<int32_t*>(ws + L.sorted_route),
+                       reinterpret_cast<int32_t*>(ws + L.route_to_row),
+                       reinterpret_cast<RouteHdr*>(ws + L.hdr));
+    return hipGetLastError();
+  }
   const int nchunks = int((n + kRankChunk - 1) / kRankChunk);
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.chunk_hist);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.chunk_flags);

@@ -24,6 +24,9 @@ def B():
     (0, 4, 2, None, 0), (777, 64, 8, 0.8, 300), (5, 3, 3, None, 15),
     (5000, 1500, 4, None, 0),             # E > 1024: the scan runs two passes over experts
     (3000, 4096, 8, 1.0, 100),            # E = 4096, the largest expert count
+    (128, 2048, 8, None, 10),             # 1,024 routes: the one-launch path, two scan passes
+    (205, 4096, 5, 1.0, 0),               # 1,025 routes: just past the one-launch path
+    (64, 384, 6, None, 0), (170, 384, 6, 1.3, 9),   # decode-sized calls
 ])
 def test_route_bit_exact(B, T, E, K, zipf, n_pad):
     banner(f"route T={T} E={E} K={K} zipf={zipf} pad={n_pad}")
