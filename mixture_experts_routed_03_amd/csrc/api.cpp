@@ -24,7 +24,7 @@ hipError_t launch_plan_decide(RouteHdr* hdr, const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_rewind(RouteHdr* hdr, void* arena, hipStream_t s);
 hipError_t launch_arena_reset(void* arena, hipStream_t s);
 hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
-                         const int32_t* sorted_route, void* dst, int64_t R_max, hipStream_t s);
+                         const int32_t* route_to_row, void* dst, int64_t T_max, hipStream_t s);
 hipError_t launch_zero_rows_f32(const RouteHdr* hdr, float* p, int64_t D, int64_t T_max,
                                 hipStream_t s);
 hipError_t launch_fused_finish(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
@@ -726,7 +726,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   // dW13's A rows: a packed copy of the x rows (its loads then stream)
   e = timed(p, "gather", s, [&] {
-    return launch_gather(x, d.d, p->es, d.k, hdr, sorted_route, sc + p->sl.x_rows, p->R_max, s);
+    return launch_gather(x, d.d, p->es, d.k, hdr, route_to_row, sc + p->sl.x_rows, d.t_max, s);
   });
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw13{hdr, offsets, mtoff, nullptr, nullptr, dh1, sc + p->sl.x_rows, g->dw13, nullptr,

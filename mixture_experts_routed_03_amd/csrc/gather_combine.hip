@@ -20,6 +20,7 @@
 namespace moe {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Vec16;  // 16 bytes of T as floats
@@ -70,40 +71,36 @@ __device__ __forceinline__ int64_t grid_thread() {
 }
 __device__ __forceinline__ int64_t grid_threads() { return int64_t(gridDim.x) * blockDim.x; }
 
-// dst[row] = x[sorted_route[row] / K] for row < R (packed copy of the x rows
-// for the backward's W13 weight gradient, whose loads then stream).
+// dst[route_to_row[t*K + k]] = x[t] for every valid route (t, k): the packed
+// x rows of the backward's W13 weight gradient, whose loads then stream.
+// Thread g reads 16-byte chunk i of token t once (g = t * row_chunks + i) and
+// writes it to the rows of the token's valid routes; rows [0, R) are exactly
+// the valid routes, so every row is written once and x is read once.
+template <int KM>
 __global__ __launch_bounds__(256) void k_gather(const u32x4* __restrict__ x, int64_t row_chunks,
                                                 int K, const RouteHdr* __restrict__ hdr,
-                                                const int32_t* __restrict__ sorted_route,
+                                                const int32_t* __restrict__ route_to_row,
                                                 u32x4* __restrict__ dst) {
-  const int64_t n = int64_t(hdr->R) * row_chunks;
-  if (n == 0) return;
+  const int64_t n = int64_t(hdr->T) * row_chunks;
+  if (n == 0 || hdr->R == 0) return;
   if (!x) {  // rows to copy need x: report instead of faulting
     if (grid_thread() == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
-  // four chunks per pass: their index loads, then their row loads, then
-  // the stores, so a pass waits for two round trips instead of eight
-  constexpr int U = 4;
-  const int64_t stride = grid_threads();
-  for (int64_t g0 = grid_thread(); g0 < n; g0 += U * stride) {
-    int64_t gi[U];
-    int32_t sr[U];
+  // with whole waves per row, a wave's token is uniform: its route reads
+  // become scalar loads
+  const bool wave_rows = row_chunks % 64 == 0;
+  for (int64_t g = grid_thread(); g < n; g += grid_threads()) {
+    int64_t t = g / row_chunks;
+    if (wave_rows) t = __builtin_amdgcn_readfirstlane(int(t));
+    const int64_t i = g - t * row_chunks;
+    int rows[KM];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      gi[u] = g0 + u * stride;
-      sr[u] = sorted_route[min(gi[u], n - 1) / row_chunks];
-    }
-    u32x4 v[U];
+    for (int k = 0; k < KM; ++k) rows[k] = k < K ? route_to_row[t * K + k] : -1;
+    const u32x4 v = x[g];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t g = min(gi[u], n - 1);
-      const int64_t i = g - (g / row_chunks) * row_chunks;
-      v[u] = x[int64_t(sr[u] / K) * row_chunks + i];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (gi[u] < n) dst[gi[u]] = v[u];
+    for (int k = 0; k < KM; ++k)
+      if (rows[k] >= 0) dst[int64_t(rows[k]) * row_chunks + i] = v;
   }
 }
 
@@ -298,57 +295,86 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
 }
 
 // dx[t] (+)= sum over valid k, ascending, of dxr[row(t,k)] (fp32) -> act dtype.
-// Thread g handles 8 values: chunk i of token t (g = t * D/8 + i).
+// Thread g handles 4 values: float4 chunk i of token t (g = t * D/4 + i), so
+// each of a wave's K row loads is 1 KiB contiguous and its store 512 bytes
+// (bf16) or 1 KiB (fp32).
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* f);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float* f) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  f[0] = v.x;
+  f[1] = v.y;
+  f[2] = v.z;
+  f[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* f) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+  f[0] = __uint_as_float(v[0] << 16);
+  f[1] = __uint_as_float(v[0] & 0xffff0000u);
+  f[2] = __uint_as_float(v[1] << 16);
+  f[3] = __uint_as_float(v[1] & 0xffff0000u);
+}
+template <typename T>
+__device__ __forceinline__ void put4(T* p, const float* f);
+template <>
+__device__ __forceinline__ void put4<float>(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+}
+template <>
+__device__ __forceinline__ void put4<uint16_t>(uint16_t* p, const float* f) {
+  u32x2 v;
+  v[0] = pack_bf16x2(f[0], f[1]);
+  v[1] = pack_bf16x2(f[2], f[3]);
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+
 template <typename T, int KM>
 __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ hdr,
                                                    const int32_t* __restrict__ route_to_row,
                                                    const float4* __restrict__ dxr,
                                                    T* __restrict__ dx, int K, int64_t D,
                                                    int accumulate) {
-  const int64_t q8 = D / 8;
-  const int64_t n = int64_t(hdr->T) * q8;
+  const int64_t q4 = D / 4;
+  const int64_t n = int64_t(hdr->T) * q4;
   if (n == 0) return;
   if (!dx) {
     if (grid_thread() == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
-  const bool wave_rows = q8 % 64 == 0;
+  const bool wave_rows = q4 % 64 == 0;
   for (int64_t g = grid_thread(); g < n; g += grid_threads()) {
-    int64_t t = g / q8;
+    int64_t t = g / q4;
     if (wave_rows) t = __builtin_amdgcn_readfirstlane(int(t));
-    const int64_t i = g - t * q8;
+    const int64_t i = g - t * q4;
     int rows[KM];
-    float4 v0[KM], v1[KM];
+    float4 v[KM];
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
       if (k < K) {
         rows[k] = route_to_row[t * K + k];
-        const float4* src = dxr + int64_t(max(rows[k], 0)) * (2 * q8) + 2 * i;
-        v0[k] = src[0];
-        v1[k] = src[1];
+        v[k] = dxr[int64_t(max(rows[k], 0)) * q4 + i];
       }
     }
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
       if (k < K && rows[k] >= 0) {
-        acc[0] += v0[k].x;
-        acc[1] += v0[k].y;
-        acc[2] += v0[k].z;
-        acc[3] += v0[k].w;
-        acc[4] += v1[k].x;
-        acc[5] += v1[k].y;
-        acc[6] += v1[k].z;
-        acc[7] += v1[k].w;
+        acc[0] += v[k].x;
+        acc[1] += v[k].y;
+        acc[2] += v[k].z;
+        acc[3] += v[k].w;
       }
     }
-    T* o = dx + t * D + i * 8;
+    T* o = dx + t * D + i * 4;
     if (accumulate) {
+      float f[4];
+      load4<T>(o, f);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += Elem<T>::to_f(o[j]);
+      for (int j = 0; j < 4; ++j) acc[j] += f[j];
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = Elem<T>::from_f(acc[j]);
+    put4<T>(o, acc);
   }
 }
 
@@ -361,15 +387,6 @@ static inline unsigned elem_grid(int64_t chunks) {
 // One workgroup per token (grid-stride), capped at 8 per CU.
 static inline unsigned tok_grid(int64_t T) {
   return unsigned(std::max<int64_t>(1, std::min<int64_t>(T, 256 * 8)));
-}
-
-hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
-                         const int32_t* sorted_route, void* dst, int64_t R_max, hipStream_t s) {
-  if (R_max == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gather, dim3(elem_grid(R_max * (D * es / 16))), dim3(256), 0, s,
-                     reinterpret_cast<const u32x4*>(x), D * es / 16, K, hdr, sorted_route,
-                     reinterpret_cast<u32x4*>(dst));
-  return hipGetLastError();
 }
 
 // Route-array bound of the K-dependent kernels: 2, 4, 8 or 16.
@@ -389,6 +406,16 @@ hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr
       CALL;                       \
     }                             \
   } while (0)
+
+hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
+                         const int32_t* route_to_row, void* dst, int64_t T_max, hipStream_t s) {
+  if (T_max == 0) return hipSuccess;
+  const int64_t rc = D * es / 16;
+  MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_gather<KM>), dim3(elem_grid(T_max * rc)), dim3(256), 0,
+                                       s, reinterpret_cast<const u32x4*>(x), rc, K, hdr,
+                                       route_to_row, reinterpret_cast<u32x4*>(dst)));
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
                           const float* scores, const void* h3, const void* addend, void* y,
@@ -459,13 +486,13 @@ hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_
                             int accumulate, hipStream_t s) {
   if (T_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
-    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_dx_reduce<float, KM>), dim3(elem_grid(T_max * (D / 8))),
+    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_dx_reduce<float, KM>), dim3(elem_grid(T_max * (D / 4))),
                                          dim3(256), 0, s, hdr, route_to_row,
                                          reinterpret_cast<const float4*>(dxr),
                                          reinterpret_cast<float*>(dx), K, D, accumulate));
   else
     MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_dx_reduce<uint16_t, KM>),
-                                         dim3(elem_grid(T_max * (D / 8))), dim3(256), 0, s, hdr,
+                                         dim3(elem_grid(T_max * (D / 4))), dim3(256), 0, s, hdr,
                                          route_to_row, reinterpret_cast<const float4*>(dxr),
                                          reinterpret_cast<uint16_t*>(dx), K, D, accumulate));
   return hipGetLastError();

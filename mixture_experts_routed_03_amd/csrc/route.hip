@@ -74,12 +74,15 @@ __device__ void block_scan(int* v /* [N] */, int* sh /* [N][16] */) {
   __syncthreads();
 }
 
-// Column sums of the chunk histograms and their rewrite into row bases read
-// 16 chunks at a time per expert (independent loads; threads of consecutive
-// experts read consecutive words).  Experts are handled in passes of 1024,
+// Column sums of the chunk histograms and their rewrite into row bases: with
+// at most kScanRegs chunks an expert's column is loaded into registers in one
+// round trip and rewritten from them; larger calls read 16 chunks at a time
+// per expert, twice (independent loads; threads of consecutive experts read
+// consecutive words).  Experts are handled in passes of 1024,
 // expert e = 1024 * pass + thread, with the running totals carried between
 // passes.
 constexpr int kScanBatch = 16;
+constexpr int kScanRegs = 64;
 
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
                                                      const int32_t* __restrict__ chunk_flags,
@@ -98,12 +101,25 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     carry[0] = carry[1] = carry[2] = carry[3] = 0;
     red[0] = red[1] = 0;
   }
+  // chunk status words, loaded first so they are in flight with the columns
+  int f = 0;
+  for (int c = tid; c < nchunks; c += 1024) f |= chunk_flags[c];
   __syncthreads();
+  // up to kScanRegs chunks (16,384 routes): an expert's whole column is loaded
+  // into registers at once, read once and rewritten from the registers
+  const bool regs = nchunks <= kScanRegs;
   int mx = 0;
   for (int e0 = 0; e0 < E; e0 += 1024) {
     const int e = e0 + tid;
     int s = 0;
-    if (e < E) {
+    int col[kScanRegs];
+    if (e < E && regs) {
+#pragma unroll
+      for (int j = 0; j < kScanRegs; ++j)
+        col[j] = j < nchunks ? chunk_hist[int64_t(j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanRegs; ++j) s += col[j];
+    } else if (e < E) {
       for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
         int v[kScanBatch];
 #pragma unroll
@@ -130,7 +146,16 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
       gtoff[e] = og;
       // chunk histograms -> row base of each (chunk, expert)
       int run = oc;
-      for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      if (regs) {
+#pragma unroll
+        for (int j = 0; j < kScanRegs; ++j) {
+          if (j < nchunks) {
+            chunk_hist[int64_t(j) * E + e] = run;
+            run += col[j];
+          }
+        }
+      }
+      for (int c0 = 0; !regs && c0 < nchunks; c0 += kScanBatch) {
         int v[kScanBatch];
 #pragma unroll
         for (int j = 0; j < kScanBatch; ++j)
@@ -154,8 +179,6 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     __syncthreads();
   }
   // status and max count
-  int f = 0;
-  for (int c = tid; c < nchunks; c += 1024) f |= chunk_flags[c];
   atomicOr(&red[0], f);
   atomicMax(&red[1], mx);
   __syncthreads();
