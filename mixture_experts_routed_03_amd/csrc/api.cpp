@@ -60,6 +60,7 @@ struct moe_plan_s {
   int64_t R_max;          // t_max * K
   int64_t Rp_max;         // upper bound on rows padded to 32 per expert
   int64_t mt_max;         // upper bound on m-tiles
+  bool hot;               // BF16 forward: hot experts on the 256 x 256 MFMA tiles
   RouteLayout rl;
   ScratchLayout sl;
   int64_t h3_bytes;
@@ -135,6 +136,15 @@ hipError_t timed(moe_plan_s* p, const char* name, hipStream_t s, Fn&& fn) {
 template <typename T>
 T* at(void* base, int64_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
+// BF16 forward split (plans with hot set): cold experts stay on the
+// streaming tiles, experts with many rows take the 256 x 256 MFMA tiles.
+static void use_hot(const moe_plan_s* p, void* ws, FwdArgs& a) {
+  if (!p->hot) return;
+  a.cstoff = at<int32_t>(ws, p->rl.cstoff);
+  a.ctoff = at<int32_t>(ws, p->rl.ctoff);
+  a.hotoff = at<int32_t>(ws, p->rl.hotoff);
 }
 
 
@@ -293,6 +303,13 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   p->R_max = d.t_max * d.k;
   p->mt_max = std::min<int64_t>(p->R_max, (p->R_max + kBM - 1) / kBM + d.e);
   p->Rp_max = align_up(p->R_max + 31 * std::min<int64_t>(d.e, p->R_max), 32);
+  {
+    // the hot-expert kernel addresses an expert's weights and the token rows
+    // with 32-bit byte offsets and stores 256-column W2 tiles
+    const int64_t lim = int64_t(1) << 32;
+    p->hot = d.prec == MOE_PREC_BF16 && d.d % 256 == 0 && 2 * d.f * d.d * 2 < lim &&
+             d.t_max * d.d * 2 < lim && p->R_max * d.f * 2 < lim;
+  }
   const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es, Rp = p->Rp_max;
   const bool mx = d.prec == MOE_PREC_MXFP8;
   const bool fp4 = d.prec == MOE_PREC_MXFP4;   // inference only: no column bundles
@@ -306,6 +323,11 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   L.poffsets = o; o = a256(o + 4 * (E + 1));
   L.mtoff = o; o = a256(o + 4 * (E + 1));
   L.gtoff = o; o = a256(o + 4 * (E + 1));
+  // cstoff, ctoff, hotoff: one region, written by routing as split[3][E + 1]
+  L.cstoff = o;
+  L.ctoff = o + 4 * (E + 1);
+  L.hotoff = o + 8 * (E + 1);
+  o = a256(o + 12 * (E + 1));
   L.chunk_hist = o; o = a256(o + 4 * L.nchunks * E);
   L.chunk_flags = o; o = a256(o + 4 * L.nchunks);
   L.sorted_route = o; o = a256(o + 4 * R);
@@ -551,6 +573,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     a13.stoff = mtoff;
+    use_hot(p, ws, a13);
     a13.limit = swiglu_limit(p);
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
@@ -558,6 +581,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + L.h2, w->w2, h3, nullptr,
                d.f, d.d, d.f, d.d / 128, d.e, 0};
     a2.stoff = mtoff;
+    use_hot(p, ws, a2);
     return hip_status(timed(p, "w2_scatter", s,
                             [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
   }
@@ -632,6 +656,7 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
     FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     a13.stoff = mtoff;
+    use_hot(p, ws, a13);
     a13.limit = swiglu_limit(p);
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
@@ -639,6 +664,7 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
     FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + L.h2, w->w2, nullptr, nullptr,
                d.f, d.d, d.f, d.d / 128, d.e, 0, nullptr, d.k, scores, y32};
     a2.stoff = mtoff;
+    use_hot(p, ws, a2);
     e = timed(p, "w2_fused", s, [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); });
   } else {
     e = mx_forward_w13(p, hdr, ws, sc, x, w, 0, cus, s);
@@ -700,6 +726,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
               d.d, 2 * d.f, d.f, d.f / 64, d.e, 1, x, d.k};
   a13.stoff = mtoff;
+  use_hot(p, ws, a13);
   a13.limit = swiglu_limit(p);
   e = timed(p, "replay_w13", s, [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -22,6 +22,12 @@ __host__ __device__ inline int64_t align128(int64_t n) { return align_up(n, 128)
 // Token rows per FPROP/DGRAD m-tile of an expert with c rows: a hot expert
 // takes 128-row tiles, so each weight tile is streamed once per 128 rows.
 __host__ __device__ inline int gemm_tile_rows(int c) { return c > kBM ? kBMX : kBM; }
+// BF16 forward: an expert with at least kHotRows rows is MFMA-bound (its
+// weight tiles are reused by many token rows) and runs on 256 x 256 tiles
+// (k_gemm_hot); the others stream their weights on the tiles above.
+constexpr int kHotRows = 256;
+constexpr int kBMH = 256;         // token rows of a hot-expert m-tile
+__host__ __device__ inline bool hot_expert(int c) { return c >= kHotRows; }
 
 // ------------------------------------------------- per-layer planner record
 // Written on the device by the planner kernel during forward, read by every
@@ -66,6 +72,9 @@ constexpr int64_t kArenaHdrBytes = 4096;  // data region starts here
 struct RouteLayout {
   int64_t hdr, counts, offsets, poffsets, mtoff, gtoff, chunk_hist, chunk_flags,
       sorted_route, route_to_row, total;
+  // BF16 forward split: the cold experts' 64-row stage and m-tile prefixes
+  // (hot experts count 0) and the hot experts' 256-row m-tile prefix
+  int64_t cstoff, ctoff, hotoff;
   int64_t nchunks;
 };
 
@@ -103,6 +112,11 @@ struct FwdArgs {
   float* y32;
   const int32_t* stoff;  // 64-row stage prefix (XCD work split, xcd_first_tile)
   float limit;           // W13: clamped SwiGLU limit (+inf: plain)
+  // BF16 only (null: every expert on the streaming tiles): the cold experts'
+  // m-tile and stage prefixes and the hot experts' 256-row m-tile prefix
+  const int32_t* ctoff;
+  const int32_t* cstoff;
+  const int32_t* hotoff;
 };
 
 // Arguments of the grouped backward GEMM launches.

@@ -375,13 +375,31 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int64_t mt_max, int cus, hipStr
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_hot(int mode, const FwdArgs& a, int64_t items_max, int cus,
+                           hipStream_t s);
+
 // mode 0: W13 + SwiGLU (out0 = h1 or null, out1 = h2); mode 1: W2 -> slots.
+// BF16 with a.hotoff: the cold experts' items (prefixes ctoff / cstoff) on
+// the streaming tiles, then the hot experts' 256 x 256 tiles (k_gemm_hot;
+// each hot expert has at most as many 256-row tiles as 128-row ones, so
+// mt_max bounds them too).
 hipError_t launch_gemm_fwd(int prec, int mode, const FwdArgs& a, int64_t mt_max, int cus,
                            hipStream_t s) {
   if (mt_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
     return mode == 0 ? launch_fwd_t<float, 0>(a, mt_max, cus, s)
                      : launch_fwd_t<float, 1>(a, mt_max, cus, s);
+  if (a.hotoff) {
+    FwdArgs c = a;
+    c.mtoff = a.ctoff;
+    c.stoff = a.cstoff;
+    const hipError_t e = mode == 0 ? launch_fwd_t<uint16_t, 0>(c, mt_max, cus, s)
+                                   : launch_fwd_t<uint16_t, 1>(c, mt_max, cus, s);
+    if (e != hipSuccess) return e;
+    FwdArgs h = a;
+    h.NT = mode == 0 ? a.F / 128 : a.N / 256;
+    return launch_gemm_hot(mode, h, mt_max * h.NT, cus, s);
+  }
   return mode == 0 ? launch_fwd_t<uint16_t, 0>(a, mt_max, cus, s)
                    : launch_fwd_t<uint16_t, 1>(a, mt_max, cus, s);
 }

@@ -84,6 +84,23 @@ __device__ void block_scan(int* v /* [N] */, int* sh /* [N][16] */) {
 constexpr int kScanBatch = 16;
 constexpr int kScanRegs = 64;
 
+// The per-expert terms whose exclusive prefixes routing writes, for an
+// expert with s rows: rows (offsets), rows rounded up to 32 (poffsets),
+// 64-row stages (mtoff), FPROP/DGRAD m-tiles (gtoff), then the BF16 forward
+// split: stages and m-tiles of cold experts (cstoff, ctoff) and 256-row
+// m-tiles of hot experts (hotoff).
+constexpr int kScans = 7;
+__device__ __forceinline__ void scan_terms(int s, int* v) {
+  const bool hot = hot_expert(s);
+  v[0] = s;
+  v[1] = (s + kMxBlock - 1) / kMxBlock * kMxBlock;
+  v[2] = (s + kBM - 1) / kBM;
+  v[3] = (s + gemm_tile_rows(s) - 1) / gemm_tile_rows(s);
+  v[4] = hot ? 0 : v[2];
+  v[5] = hot ? 0 : v[3];
+  v[6] = hot ? (s + kBMH - 1) / kBMH : 0;
+}
+
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
                                                      const int32_t* __restrict__ chunk_flags,
                                                      int nchunks, int E, int T,
@@ -92,15 +109,14 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
                                                      int32_t* __restrict__ poffsets,
                                                      int32_t* __restrict__ mtoff,
                                                      int32_t* __restrict__ gtoff,
+                                                     int32_t* __restrict__ split,
                                                      RouteHdr* __restrict__ hdr) {
-  __shared__ int sh[64];
-  __shared__ int carry[4];
+  __shared__ int sh[16 * kScans];
+  __shared__ int carry[kScans];
   __shared__ int red[2];
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    carry[0] = carry[1] = carry[2] = carry[3] = 0;
-    red[0] = red[1] = 0;
-  }
+  if (tid < kScans) carry[tid] = 0;
+  if (tid == 0) red[0] = red[1] = 0;
   // chunk status words, loaded first so they are in flight with the columns
   int f = 0;
   for (int c = tid; c < nchunks; c += 1024) f |= chunk_flags[c];
@@ -129,21 +145,26 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
         for (int j = 0; j < kScanBatch; ++j) s += c0 + j < nchunks ? v[j] : 0;
       }
     }
-    const int sp = (s + kMxBlock - 1) / kMxBlock * kMxBlock;
-    const int sm = (s + kBM - 1) / kBM;
-    const int sg = (s + gemm_tile_rows(s) - 1) / gemm_tile_rows(s);
+    int v[kScans];
+    scan_terms(s, v);
     mx = max(mx, s);
-    int v[4] = {s, sp, sm, sg};
-    block_scan<4>(v, sh);
-    const int ic = v[0], ip = v[1], im = v[2], ig = v[3];
-    const int oc = carry[0] + ic - s, op = carry[1] + ip - sp, om = carry[2] + im - sm,
-              og = carry[3] + ig - sg;
+    block_scan<kScans>(v, sh);
+    int o[kScans];
+    {
+      int t[kScans];
+      scan_terms(s, t);
+#pragma unroll
+      for (int j = 0; j < kScans; ++j) o[j] = carry[j] + v[j] - t[j];
+    }
+    const int oc = o[0];
     if (e < E) {
       counts[e] = s;
       offsets[e] = oc;
-      poffsets[e] = op;
-      mtoff[e] = om;
-      gtoff[e] = og;
+      poffsets[e] = o[1];
+      mtoff[e] = o[2];
+      gtoff[e] = o[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) split[j * (E + 1) + e] = o[4 + j];
       // chunk histograms -> row base of each (chunk, expert)
       int run = oc;
       if (regs) {
@@ -171,10 +192,8 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     }
     __syncthreads();   // every thread has read the carries of this pass
     if (tid == 1023) {
-      carry[0] += ic;
-      carry[1] += ip;
-      carry[2] += im;
-      carry[3] += ig;
+#pragma unroll
+      for (int j = 0; j < kScans; ++j) carry[j] += v[j];
     }
     __syncthreads();
   }
@@ -187,6 +206,8 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     poffsets[E] = carry[1];
     mtoff[E] = carry[2];
     gtoff[E] = carry[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) split[j * (E + 1) + E] = carry[4 + j];
     hdr->T = T;
     hdr->R = carry[0];
     hdr->Rpad = carry[1];
@@ -239,20 +260,19 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
                                                       int32_t* __restrict__ poffsets,
                                                       int32_t* __restrict__ mtoff,
                                                       int32_t* __restrict__ gtoff,
+                                                      int32_t* __restrict__ split,
                                                       int32_t* __restrict__ sorted_route,
                                                       int32_t* __restrict__ route_to_row,
                                                       RouteHdr* __restrict__ hdr) {
   __shared__ int32_t sid[kSmallRoutes];
   __shared__ int32_t cnt[kMaxE];   // counts, then each expert's first row
-  __shared__ int sh[64];
-  __shared__ int carry[4];
+  __shared__ int sh[16 * kScans];
+  __shared__ int carry[kScans];
   __shared__ int s_mx;
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
-  if (tid == 0) {
-    carry[0] = carry[1] = carry[2] = carry[3] = 0;
-    s_mx = 0;
-  }
+  if (tid < kScans) carry[tid] = 0;
+  if (tid == 0) s_mx = 0;
   int bad = 0;
   int id = -1;
   if (tid < n) {
@@ -270,28 +290,32 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
   for (int e0 = 0; e0 < E; e0 += 1024) {
     const int e = e0 + tid;
     const int s = e < E ? cnt[e] : 0;
-    const int sp = (s + kMxBlock - 1) / kMxBlock * kMxBlock;
-    const int sm = (s + kBM - 1) / kBM;
-    const int sg = (s + gemm_tile_rows(s) - 1) / gemm_tile_rows(s);
+    int v[kScans];
+    scan_terms(s, v);
     mx = max(mx, s);
-    int v[4] = {s, sp, sm, sg};
-    block_scan<4>(v, sh);
-    const int ic = v[0], ip = v[1], im = v[2], ig = v[3];
-    const int oc = carry[0] + ic - s;
+    block_scan<kScans>(v, sh);
+    int o[kScans];
+    {
+      int t[kScans];
+      scan_terms(s, t);
+#pragma unroll
+      for (int j = 0; j < kScans; ++j) o[j] = carry[j] + v[j] - t[j];
+    }
+    const int oc = o[0];
     if (e < E) {
       counts[e] = s;
       offsets[e] = oc;
-      poffsets[e] = carry[1] + ip - sp;
-      mtoff[e] = carry[2] + im - sm;
-      gtoff[e] = carry[3] + ig - sg;
+      poffsets[e] = o[1];
+      mtoff[e] = o[2];
+      gtoff[e] = o[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) split[j * (E + 1) + e] = o[4 + j];
       cnt[e] = oc;
     }
     __syncthreads();   // every thread has read the carries of this pass
     if (tid == 1023) {
-      carry[0] += ic;
-      carry[1] += ip;
-      carry[2] += im;
-      carry[3] += ig;
+#pragma unroll
+      for (int j = 0; j < kScans; ++j) carry[j] += v[j];
     }
     __syncthreads();
   }
@@ -314,6 +338,8 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
     poffsets[E] = carry[1];
     mtoff[E] = carry[2];
     gtoff[E] = carry[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) split[j * (E + 1) + E] = carry[4 + j];
     hdr->T = T;
     hdr->R = carry[0];
     hdr->Rpad = carry[1];
@@ -412,6 +438,7 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
                        reinterpret_cast<int32_t*>(ws + L.poffsets),
                        reinterpret_cast<int32_t*>(ws + L.mtoff),
                        reinterpret_cast<int32_t*>(ws + L.gtoff),
+                       reinterpret_cast<int32_t*>(ws + L.cstoff),
                        reinterpret_cast<int32_t*>(ws + L.sorted_route),
                        reinterpret_cast<int32_t*>(ws + L.route_to_row),
                        reinterpret_cast<RouteHdr*>(ws + L.hdr));
@@ -429,6 +456,7 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
                      reinterpret_cast<int32_t*>(ws + L.poffsets),
                      reinterpret_cast<int32_t*>(ws + L.mtoff),
                      reinterpret_cast<int32_t*>(ws + L.gtoff),
+                     reinterpret_cast<int32_t*>(ws + L.cstoff),
                      reinterpret_cast<RouteHdr*>(ws + L.hdr));
   if (nchunks > 0)
     hipLaunchKernelGGL(k_route_rank, dim3(nchunks), dim3(256), 0, s, ids, n, E, hist,

@@ -1,0 +1,133 @@
+"""GPU parity of the BF16 forward when experts are hot (at least 256 rows):
+those experts run on the 256 x 256 MFMA tiles, the others on the
+weight-streaming tiles, through the C ABI against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as om
+from oracle import mx as omx
+from tests._harness import (TOL, banner, check_route, make_inputs, oracle_forward, run_forward,
+                            run_train)
+
+pytestmark = pytest.mark.gpu
+
+HOT = 256   # rows from which an expert takes the large tiles
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_routed_03_amd import binding
+    binding.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return binding
+
+
+def _counts(lay, E):
+    ids = lay["ids"].cpu().numpy()
+    return np.bincount(ids[ids >= 0].ravel(), minlength=E)
+
+
+# (T, D, F, E, K, zipf, n_pad): every case has hot experts; the comments say
+# which tile shapes they reach
+CASES = [
+    (1024, 512, 256, 4, 2, None, 0),     # all hot, ~512 rows: whole 256-row m-tiles, 2 n-tiles each
+    (1500, 256, 384, 6, 3, 1.2, 9),      # uneven hot experts (368-1348 rows), F = 3 x 128, padded routes
+    (600, 256, 256, 1, 1, None, 0),      # one expert, 600 rows: last m-tile 88 rows (waves with 2, 1, 0 live blocks)
+    (900, 768, 128, 3, 1, 0.6, 0),       # a cold expert beside hot ones (256 and 436 rows), D = 3 x 256
+]
+
+
+@pytest.mark.parametrize("T,D,F,E,K,zipf,n_pad", CASES)
+def test_hot_forward_matches_oracle(B, T, D, F, E, K, zipf, n_pad):
+    banner(f"hot bf16 forward T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
+    lay = make_inputs(T, D, F, E, K, "bf16", zipf=zipf, n_pad=n_pad, seed=T + 11)
+    assert _counts(lay, E).max() >= HOT
+    layer = B.MoeLayer(T, D, F, E, K, "bf16")
+    y = run_forward(layer, lay)
+    torch.cuda.synchronize()
+    check_route(layer.readback(T), lay["ids"].cpu().numpy(), E)
+    ref, cache = oracle_forward(lay, keep=True)
+    assert om.max_abs_rel(y, ref) < TOL["bf16"]
+    assert torch.isfinite(y.float()).all()
+    # h1 in packed row order, written by both tile kinds
+    _, h1p = layer.saved_ptrs()
+    R = cache["route"]["R"]
+    h1 = layer.view(h1p, (R, 2 * F), torch.bfloat16)
+    assert om.max_abs_rel(h1, cache["H1"]) < TOL["bf16"]
+    assert layer.status()[0] == 0
+
+
+def test_hot_forward_deterministic(B):
+    banner("hot forward determinism")
+    T, D, F, E, K = 800, 256, 256, 3, 2
+    lay = make_inputs(T, D, F, E, K, "bf16", seed=5)
+    layer = B.MoeLayer(T, D, F, E, K, "bf16")
+    y1 = run_forward(layer, lay).clone()
+    y2 = run_forward(layer, lay).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_hot_fused_combine_matches_oracle(B):
+    banner("hot fused combine")
+    T, D, F, E, K = 1200, 512, 128, 5, 2
+    lay = make_inputs(T, D, F, E, K, "bf16", zipf=1.0, seed=21)
+    assert _counts(lay, E).max() >= HOT
+    layer = B.MoeLayer(T, D, F, E, K, "bf16")
+    y_slots = run_forward(layer, lay).clone()
+    addend = torch.randn((T, D), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16).cuda()
+    y = torch.empty_like(y_slots)
+    layer.route(lay["ids"])
+    layer.forward_fused(lay["x"], lay["w13"], lay["w2"], lay["scores"], y, y_addend=addend)
+    torch.cuda.synchronize()
+    ref = oracle_forward(lay)
+    assert om.max_abs_rel(y.float() - addend.float(), ref) < TOL["bf16"]
+    assert om.max_abs_rel(y.float() - addend.float(), y_slots) < 1e-2
+    assert layer.status()[0] == 0
+
+
+def test_hot_training_matches_oracle(B):
+    """Forward h1 from the large tiles feeds the backward (dX, dW13, dW2, dS)."""
+    banner("hot bf16 training")
+    T, D, F, E, K = 700, 256, 256, 4, 2
+    lay = make_inputs(T, D, F, E, K, "bf16", zipf=0.8, seed=17, training=True)
+    assert _counts(lay, E).max() >= HOT
+    layer = B.MoeLayer(T, D, F, E, K, "bf16", training=True)
+    y, dx, dw13, dw2, ds = run_train(layer, lay)
+    torch.cuda.synchronize()
+    ref_y, cache = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(),
+                              lay["w2"].cpu(), keep=True)
+    rdx, rdw13, rdw2, rds = om.backward(lay["dy"], lay["x"], lay["ids"], lay["scores"],
+                                        lay["w13"].cpu(), lay["w2"].cpu(), cache)
+    tol = TOL["bf16"]
+    assert om.max_abs_rel(y, ref_y) < tol
+    assert om.max_abs_rel(dx, rdx) < tol
+    assert om.max_abs_rel(ds, rds) < tol
+    for e in range(E):
+        assert om.max_abs_rel(dw13[e], rdw13[e]) < tol, e
+        assert om.max_abs_rel(dw2[e], rdw2[e]) < tol, e
+    assert layer.status() == (0, 0)
+
+
+def test_hot_replay_and_clamp_match_saved_state(B):
+    """A layer that replays its forward in backward rebuilds h1 with the same
+    large tiles bit for bit; the clamped SwiGLU epilogue matches the oracle."""
+    banner("hot replay + clamped SwiGLU")
+    T, D, F, E, K = 640, 256, 256, 2, 1
+    lay = make_inputs(T, D, F, E, K, "bf16", seed=8, training=True)
+    assert _counts(lay, E).max() >= HOT
+    _, c0 = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                       keep=True)
+    L = float(np.median(np.abs(c0["H1"])))
+    saved = B.MoeLayer(T, D, F, E, K, "bf16", training=True, swiglu_limit=L)
+    a = [t.clone() for t in run_train(saved, lay)]
+    replay = B.MoeLayer(T, D, F, E, K, "bf16", training=True, swiglu_limit=L, arena_budget=128)
+    b = run_train(replay, lay)
+    torch.cuda.synchronize()
+    assert saved.status()[1] == 0 and replay.status()[1] == 1
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    ry, _ = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                       keep=True, limit=L, act=omx.bf16_round)
+    assert om.max_abs_rel(a[0], ry) < TOL["bf16"]
