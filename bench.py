@@ -544,7 +544,14 @@ def main():
         "mfma_peak_frac": round(value / PEAK_TFLOPS[prec], 4),
         "tflops_incl_shared_expert": (round((useful + shared_flops) / (ms_step * 1e-3) / 1e12, 2)
                                       if shared_flops else None),
+        # routing itself moves ~0.2 MB (ids in, permutation out): its time is
+        # launch latency, so it is reported in microseconds beside its GB/s;
+        # the bandwidth-bound half of the router is the permuted-row gather
+        # (inside the W13 loader in the forward, a kernel of its own in the
+        # BF16 backward)
         "route_GBps": kernels.get("route", {}).get("GB/s"),
+        "route_us": (round(kernels["route"]["avg_ms"] * 1e3, 1) if "route" in kernels else None),
+        "gather_GBps": kernels.get("gather", {}).get("GB/s"),
         "wall_s_timed": round(wall, 3),
         "window_ms_per_step": [round(v, 4) for v in win_ms],
         "median_window_ms": round(sorted(win_ms)[len(win_ms) // 2], 4),

@@ -749,6 +749,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs b13{hdr, offsets, gtoff, w->w13, dh1, nullptr, nullptr, dxr, nullptr,
               2 * d.f, d.d, d.f, d.d, d.e, (d.d + 255) / 256, 0, 0, mtoff};
+  b13.row_slot = sorted_route;
   e = timed(p, "w13_dgrad", s, [&] { return launch_dgrad(1, b13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   // dW13's A rows: a packed copy of the x rows (its loads then stream)

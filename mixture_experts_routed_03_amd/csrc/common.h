@@ -138,6 +138,7 @@ struct BwdArgs {
   const int32_t* stoff; // DGRAD: 64-row stage prefix (XCD work split); mtoff = the m-tile prefix
   int acc_dw;           // WGRAD: 1 = dW += result (fp32 sum, rounded once), 0 = dW = result
   float limit;          // W2 DGRAD: clamped SwiGLU limit (+inf: plain)
+  const int32_t* row_slot;  // W13 DGRAD: dXr row r goes to slot row_slot[r] (the route t*K+k)
 };
 
 // Arguments of the MXFP8 grouped GEMM launches.

@@ -294,10 +294,11 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const RouteHdr* __restrict_
   }
 }
 
-// dx[t] (+)= sum over valid k, ascending, of dxr[row(t,k)] (fp32) -> act dtype.
-// Thread g handles 4 values: float4 chunk i of token t (g = t * D/4 + i), so
-// each of a wave's K row loads is 1 KiB contiguous and its store 512 bytes
-// (bf16) or 1 KiB (fp32).
+// dx[t] (+)= sum over valid k, ascending, of dxr[t*K + k] (fp32) -> act dtype.
+// The W13 DGRAD stores each route's fp32 row at its slot t*K + k, so a
+// token's K rows are one contiguous run.  Each thread handles 4 values per
+// step, so each of a wave's K row loads is 1 KiB contiguous and its store
+// 512 bytes (bf16) or 1 KiB (fp32).
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float* f);
 template <>
@@ -336,45 +337,44 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ 
                                                    const float4* __restrict__ dxr,
                                                    T* __restrict__ dx, int K, int64_t D,
                                                    int accumulate) {
-  const int64_t q4 = D / 4;
-  const int64_t n = int64_t(hdr->T) * q4;
-  if (n == 0) return;
+  const int n_tok = hdr->T;
+  if (n_tok == 0) return;
   if (!dx) {
     if (grid_thread() == 0) atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_NULL_INPUT);
     return;
   }
-  const bool wave_rows = q4 % 64 == 0;
-  for (int64_t g = grid_thread(); g < n; g += grid_threads()) {
-    int64_t t = g / q4;
-    if (wave_rows) t = __builtin_amdgcn_readfirstlane(int(t));
-    const int64_t i = g - t * q4;
-    int rows[KM];
-    float4 v[KM];
+  const int64_t q4 = D / 4;
+  // one workgroup per token at a time: the token's route flags are uniform
+  // (scalar loads) and its K slot rows stream by in 4 KiB steps
+  for (int64_t t = blockIdx.x; t < n_tok; t += gridDim.x) {
+    bool valid[KM];
 #pragma unroll
-    for (int k = 0; k < KM; ++k) {
-      if (k < K) {
-        rows[k] = route_to_row[t * K + k];
-        v[k] = dxr[int64_t(max(rows[k], 0)) * q4 + i];
+    for (int k = 0; k < KM; ++k) valid[k] = k < K && route_to_row[t * K + k] >= 0;
+    const float4* src = dxr + t * K * q4;
+    T* o = dx + t * D;
+    for (int64_t i = threadIdx.x; i < q4; i += 256) {
+      float4 v[KM];
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (k < K) v[k] = src[k * q4 + i];   // a padding slot is read but not added
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        if (valid[k]) {
+          acc[0] += v[k].x;
+          acc[1] += v[k].y;
+          acc[2] += v[k].z;
+          acc[3] += v[k].w;
+        }
       }
-    }
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      if (accumulate) {
+        float f[4];
+        load4<T>(o + 4 * i, f);
 #pragma unroll
-    for (int k = 0; k < KM; ++k) {
-      if (k < K && rows[k] >= 0) {
-        acc[0] += v[k].x;
-        acc[1] += v[k].y;
-        acc[2] += v[k].z;
-        acc[3] += v[k].w;
+        for (int j = 0; j < 4; ++j) acc[j] += f[j];
       }
+      put4<T>(o + 4 * i, acc);
     }
-    T* o = dx + t * D + i * 4;
-    if (accumulate) {
-      float f[4];
-      load4<T>(o, f);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += f[j];
-    }
-    put4<T>(o, acc);
   }
 }
 
@@ -486,13 +486,13 @@ hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_
                             int accumulate, hipStream_t s) {
   if (T_max == 0) return hipSuccess;
   if (prec == MOE_PREC_F32)
-    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_dx_reduce<float, KM>), dim3(elem_grid(T_max * (D / 4))),
+    MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_dx_reduce<float, KM>), dim3(tok_grid(T_max)),
                                          dim3(256), 0, s, hdr, route_to_row,
                                          reinterpret_cast<const float4*>(dxr),
                                          reinterpret_cast<float*>(dx), K, D, accumulate));
   else
     MOE_DISPATCH_K(K, hipLaunchKernelGGL((k_dx_reduce<uint16_t, KM>),
-                                         dim3(elem_grid(T_max * (D / 4))), dim3(256), 0, s, hdr,
+                                         dim3(tok_grid(T_max)), dim3(256), 0, s, hdr,
                                          route_to_row, reinterpret_cast<const float4*>(dxr),
                                          reinterpret_cast<uint16_t*>(dx), K, D, accumulate));
   return hipGetLastError();

@@ -15,7 +15,8 @@
 //                    epilogue -> dH1 = [dG | dU] (bf16); also writes
 //                    h2 = SiLU(g) * u rebuilt from h1 (the forward formula) for
 //                    the W2 weight gradient.
-//   k_gemm_dgrad<1>: dXr = dH1_e W13_e (contraction over 2F) -> fp32 rows.
+//   k_gemm_dgrad<1>: dXr = dH1_e W13_e (contraction over 2F) -> fp32 rows,
+//                    each stored at its route slot t*K + k.
 //   k_gemm_wgrad:    dW_e[b][a] = sum over the expert's rows m of
 //                    B[m][b] A[m][a]: dW2 = dH3^T H2 (a = F, b = D) and
 //                    dW13 = dH1^T X (a = D, b = 2F).
@@ -299,7 +300,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
           if (h2o) store4<uint16_t>(h2o + row * F + j, hv[0], hv[1], hv[2], hv[3]);
         }
       } else {
-        float* o = reinterpret_cast<float*>(a.out) + row * N;
+        // dXr rows go to their route slots, so the input-gradient sum reads
+        // each token's K rows as one contiguous run
+        float* o = reinterpret_cast<float*>(a.out) + int64_t(a.row_slot[row]) * N;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
           store4<float>(o + col + 8 * g4, acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2],

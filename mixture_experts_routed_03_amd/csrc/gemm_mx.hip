@@ -13,7 +13,8 @@
 //   k_mx_fwd<0>: h1 = Xq W13q^T per expert (+ SwiGLU epilogue -> h1, h2 bf16)
 //   k_mx_fwd<1>: h3 = H2q W2q^T per expert -> route slots (bf16)
 //   k_mx_dgrad<0>: dH2 = dH3q W2q (contraction over D) + SwiGLU backward -> dH1
-//   k_mx_dgrad<1>: dXr = dH1q W13q (contraction over 2F) -> fp32 rows
+//   k_mx_dgrad<1>: dXr = dH1q W13q (contraction over 2F) -> fp32 rows at
+//                  their route slots t*K + k
 //   k_mx_wgrad:  dW[b][a] = sum_m B[m][b] A[m][a] from column bundles
 //
 // MFMA operand layout (measured on gfx950): one MFMA covers 64 contraction
@@ -643,7 +644,8 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
           store4<uint16_t>(o + F + j, du[0], du[1], du[2], du[3]);
         }
       } else {
-        float* o = reinterpret_cast<float*>(a.out0) + row * N;
+        // dXr rows go to their route slots (contiguous K rows per token)
+        float* o = reinterpret_cast<float*>(a.out0) + int64_t(a.sorted_route[row]) * N;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
           store4<float>(o + col + 8 * g4, acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2],

@@ -131,3 +131,39 @@ def test_hot_replay_and_clamp_match_saved_state(B):
     ry, _ = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
                        keep=True, limit=L, act=omx.bf16_round)
     assert om.max_abs_rel(a[0], ry) < TOL["bf16"]
+
+
+def test_hot_sized_experts_on_streaming_tiles_bf16(B):
+    """Experts of 256+ rows in a BF16 plan whose D is not a multiple of 256:
+    every expert stays on the streaming tiles; forward and backward still
+    match the oracle."""
+    T, D, F, E, K = 800, 384, 128, 3, 2
+    banner(f"hot-sized experts, streaming tiles bf16 T={T} D={D} F={F} E={E} K={K}")
+    lay = make_inputs(T, D, F, E, K, "bf16", seed=T + 2, training=True)
+    assert _counts(lay, E).min() >= HOT
+    layer = B.MoeLayer(T, D, F, E, K, "bf16", training=True)
+    y, dx, dw13, dw2, ds = run_train(layer, lay)
+    torch.cuda.synchronize()
+    ref_y, cache = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(),
+                              lay["w2"].cpu(), keep=True)
+    rdx, rdw13, rdw2, rds = om.backward(lay["dy"], lay["x"], lay["ids"], lay["scores"],
+                                        lay["w13"].cpu(), lay["w2"].cpu(), cache)
+    tol = TOL["bf16"]
+    assert om.max_abs_rel(y, ref_y) < tol
+    assert om.max_abs_rel(dx, rdx) < tol
+    assert om.max_abs_rel(ds, rds) < tol
+    for e in range(E):
+        assert om.max_abs_rel(dw13[e], rdw13[e]) < tol, e
+        assert om.max_abs_rel(dw2[e], rdw2[e]) < tol, e
+
+
+def test_hot_sized_experts_fp32_forward(B):
+    """FP32 plans (forward only) never take the large BF16 tiles."""
+    T, D, F, E, K = 600, 256, 128, 2, 1
+    banner(f"hot-sized experts, fp32 forward T={T} D={D} F={F} E={E} K={K}")
+    lay = make_inputs(T, D, F, E, K, "f32", seed=T + 2)
+    assert _counts(lay, E).min() >= HOT
+    layer = B.MoeLayer(T, D, F, E, K, "f32")
+    y = run_forward(layer, lay)
+    torch.cuda.synchronize()
+    assert om.max_abs_rel(y, oracle_forward(lay)) < TOL["f32"]
