@@ -189,10 +189,13 @@ __global__ __launch_bounds__(256) void k_rowq(RowqArgs a) {
 }
 
 // ------------------------------------------------------------------ column bundles (32x1)
-// One workgroup per (32-row block of the padded row space, 256 columns).  The
-// block's rows are loaded row-wise with 16-byte loads (32 lanes per 512-byte
-// row segment) into LDS; then each thread takes one column, reads its 32
-// values from LDS, and writes 32 contiguous code bytes and one exponent.
+// One workgroup per (32-row block of the padded row space, 1,024 columns),
+// one 256-column tile at a time.  A tile's rows are loaded row-wise with
+// 16-byte loads (32 lanes per 512-byte row segment) into LDS; then each
+// thread takes one column, reads its 32 values from LDS, and writes 32
+// contiguous code bytes and one exponent.
+constexpr int kColTiles = 4;   // 256-column tiles per k_colq workgroup
+
 __global__ __launch_bounds__(256) void k_colq(ColqArgs a) {
   constexpr int kRow = 256 + 8;              // LDS row pitch (bf16), 16-byte aligned
   __shared__ __attribute__((aligned(16))) uint16_t tile[32 * kRow];
@@ -205,7 +208,6 @@ __global__ __launch_bounds__(256) void k_colq(ColqArgs a) {
   const int key = gb * 32;
   if (key >= hdr->Rpad) return;
   const int tid = threadIdx.x;
-  const int c0 = blockIdx.y * 256;
   const int N = a.N;
   const uint16_t* src = a.src_slot >= 0 ? global_ptr<const uint16_t>(rec_ptr(hdr, a.src_slot))
                                          : reinterpret_cast<const uint16_t*>(a.src);
@@ -237,45 +239,64 @@ __global__ __launch_bounds__(256) void k_colq(ColqArgs a) {
   const int r0 = a.offsets[e] + mb * 32;
   const int rows = min(32, a.offsets[e + 1] - r0);
 
-  // rows r = t/32 + 8j, 16-byte chunk t%32; rows past the expert's end are zero
+  // Column tiles of 256: this workgroup covers kColTiles of them with one
+  // expert lookup; the next tile's rows are loaded while this one is
+  // quantized.  Rows r = t/32 + 8j, 16-byte chunk t%32; rows past the
+  // expert's end are zero.
   const int cc = tid & 31;
+  u32x4 v8[4];
+  auto load = [&](int c0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (tid >> 5) + 8 * j;
-    const int col = c0 + 8 * cc;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < rows && col < N) {
-      const int64_t srow = a.gather ? a.gather[r0 + r] / a.K : r0 + r;
-      v = *reinterpret_cast<const u32x4*>(src + srow * N + col);
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid >> 5) + 8 * j;
+      const int col = c0 + 8 * cc;
+      v8[j] = u32x4{0u, 0u, 0u, 0u};
+      if (r < rows && col < N) {
+        const int64_t srow = a.gather ? a.gather[r0 + r] / a.K : r0 + r;
+        v8[j] = *reinterpret_cast<const u32x4*>(src + srow * N + col);
+      }
     }
-    *reinterpret_cast<u32x4*>(tile + r * kRow + 8 * cc) = v;
-  }
-  __syncthreads();
-  const int col = c0 + tid;
-  if (col >= N) return;
-  float v[32];
-  float amax = 0.0f;
+  };
+  const int cbase = blockIdx.y * (256 * kColTiles);
+  load(cbase);
+  for (int ct = 0; ct < kColTiles; ++ct) {
+    const int c0 = cbase + 256 * ct;
+    if (c0 >= N) break;   // uniform
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    v[r] = bf16_to_f32(tile[r * kRow + tid]);
-    amax = fmaxf(amax, fabsf(v[r]));
-  }
-  const int ex = e8m0_exp(amax);
-  u32x4 o0, o1;
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid >> 5) + 8 * j;
+      *reinterpret_cast<u32x4*>(tile + r * kRow + 8 * cc) = v8[j];
+    }
+    __syncthreads();
+    if (ct + 1 < kColTiles && c0 + 256 < N) load(c0 + 256);
+    const int col = c0 + tid;
+    if (col < N) {
+      float v[32];
+      float amax = 0.0f;
 #pragma unroll
-  for (int w4 = 0; w4 < 8; ++w4) {
-    uint32_t wv = 0;
+      for (int r = 0; r < 32; ++r) {
+        v[r] = bf16_to_f32(tile[r * kRow + tid]);
+        amax = fmaxf(amax, fabsf(v[r]));
+      }
+      const int ex = e8m0_exp(amax);
+      u32x4 o0, o1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv |= e4m3_rne(ldexp_i(v[4 * w4 + i], -ex)) << (8 * i);
-    if (w4 < 4)
-      o0[w4] = wv;
-    else
-      o1[w4 - 4] = wv;
+      for (int w4 = 0; w4 < 8; ++w4) {
+        uint32_t wv = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv |= e4m3_rne(ldexp_i(v[4 * w4 + i], -ex)) << (8 * i);
+        if (w4 < 4)
+          o0[w4] = wv;
+        else
+          o1[w4 - 4] = wv;
+      }
+      uint8_t* qd = q + int64_t(N) * pbase + int64_t(col) * mp + mb * 32;
+      *reinterpret_cast<u32x4*>(qd) = o0;
+      *reinterpret_cast<u32x4*>(qd + 16) = o1;
+      s[int64_t(N) * (pbase / 32) + int64_t(col) * (mp / 32) + mb] = uint8_t(ex + 127);
+    }
+    __syncthreads();   // the tile is rewritten by the next column tile
   }
-  uint8_t* qd = q + int64_t(N) * pbase + int64_t(col) * mp + mb * 32;
-  *reinterpret_cast<u32x4*>(qd) = o0;
-  *reinterpret_cast<u32x4*>(qd + 16) = o1;
-  s[int64_t(N) * (pbase / 32) + int64_t(col) * (mp / 32) + mb] = uint8_t(ex + 127);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -298,7 +319,8 @@ hipError_t launch_rowq(const RowqArgs& a, int64_t R_max, hipStream_t st) {
 
 hipError_t launch_colq(const ColqArgs& a, int64_t Rpad_max, hipStream_t st) {
   if (Rpad_max == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_colq, dim3(unsigned(Rpad_max / 32), unsigned((a.N + 255) / 256)),
+  hipLaunchKernelGGL(k_colq,
+                     dim3(unsigned(Rpad_max / 32), unsigned((a.N + 256 * kColTiles - 1) / (256 * kColTiles))),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }
