@@ -35,6 +35,8 @@ CASES = [
     (1500, 256, 384, 6, 3, 1.2, 9),      # uneven hot experts (368-1348 rows), F = 3 x 128, padded routes
     (600, 256, 256, 1, 1, None, 0),      # one expert, 600 rows: last m-tile 88 rows (waves with 2, 1, 0 live blocks)
     (900, 768, 128, 3, 1, 0.6, 0),       # a cold expert beside hot ones (256 and 436 rows), D = 3 x 256
+    (5000, 256, 128, 1500, 4, 1.2, 0),   # E > 1024: the split prefixes carried across scan passes
+    (400, 256, 128, 2, 2, None, 0),      # 800 routes: the one-launch routing path writes the split
 ]
 
 
