@@ -123,6 +123,17 @@ typedef struct moe_desc {
                                blocks (training-compatible).  1 with a
                                training or non-MXFP8 plan -> MOE_ERR_ARG
                                (MXFP4 weights are always 1x32: leave 0). */
+  int32_t hot_tiles;        /* BF16 forward tiling of experts with 256 or more
+                               rows (their GEMMs reuse each weight tile over
+                               hundreds of rows, so they are bound by the
+                               matrix cores, not by reading weights):
+                               0 = automatic (256 x 256 MFMA tiles when the
+                               call could give them at least three work items
+                               per four compute units), 1 = always those
+                               tiles, 2 = never (every expert on the
+                               weight-streaming tiles).  Results agree within
+                               rounding either way.  Ignored by other
+                               precisions; other values -> MOE_ERR_ARG. */
 } moe_desc;
 
 /* Byte sizes of the caller-owned buffers (all 256-byte aligned). */

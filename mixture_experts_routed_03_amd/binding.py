@@ -44,7 +44,8 @@ class moe_desc(ctypes.Structure):
                 ("e", ctypes.c_int32), ("k", ctypes.c_int32), ("prec", ctypes.c_int32),
                 ("dw_dtype", ctypes.c_int32), ("training", ctypes.c_int32),
                 ("max_layers", ctypes.c_int32), ("arena_budget", ctypes.c_int64),
-                ("swiglu_limit", ctypes.c_float), ("mx_w1x32", ctypes.c_int32)]
+                ("swiglu_limit", ctypes.c_float), ("mx_w1x32", ctypes.c_int32),
+                ("hot_tiles", ctypes.c_int32)]
 
 
 class moe_sizes(ctypes.Structure):
@@ -127,13 +128,18 @@ def _stream(stream=None):
 
 # ------------------------------------------------------------------ C entry points
 
+HOT_TILES = {"auto": 0, "always": 1, "never": 2}
+
+
 def moe_plan_create(t_max, d, f, e, k, prec="bf16", dw_dtype=None, training=False,
-                    max_layers=1, arena_budget=0, swiglu_limit=0.0, mx_w1x32=False):
+                    max_layers=1, arena_budget=0, swiglu_limit=0.0, mx_w1x32=False,
+                    hot_tiles="auto"):
     if dw_dtype is None:
         dw_dtype = "f32" if prec == "f32" else "bf16"
+    ht = HOT_TILES[hot_tiles] if isinstance(hot_tiles, str) else int(hot_tiles)
     desc = moe_desc(int(t_max), int(d), int(f), int(e), int(k), PREC[prec], DTYPE[dw_dtype],
                     int(bool(training)), int(max_layers), int(arena_budget),
-                    float(swiglu_limit), int(bool(mx_w1x32)))
+                    float(swiglu_limit), int(bool(mx_w1x32)), ht)
     h = _P()
     _check(lib().moe_plan_create(ctypes.byref(desc), ctypes.byref(h)), "moe_plan_create")
     return h
@@ -269,7 +275,7 @@ class MoeLayer:
 
     def __init__(self, T_max, D, F, E, K, prec="bf16", dw_dtype=None, training=False,
                  max_layers=1, arena_budget=0, device="cuda", swiglu_limit=0.0,
-                 mx_w1x32=False):
+                 mx_w1x32=False, hot_tiles="auto"):
         self.T_max, self.D, self.F, self.E, self.K = T_max, D, F, E, K
         self.swiglu_limit, self.mx_w1x32 = swiglu_limit, bool(mx_w1x32)
         self.prec, self.training, self.max_layers = prec, training, max_layers
@@ -278,7 +284,7 @@ class MoeLayer:
         self.dw_dtype = (torch.float32 if (dw_dtype or ("f32" if prec == "f32" else "bf16")) == "f32"
                          else torch.bfloat16)
         self.plan = moe_plan_create(T_max, D, F, E, K, prec, dw_dtype, training, max_layers,
-                                    arena_budget, swiglu_limit, mx_w1x32)
+                                    arena_budget, swiglu_limit, mx_w1x32, hot_tiles)
         self.sizes = moe_plan_sizes(self.plan)
         self.scratch = _bytes(self.sizes["scratch"], self.device)
         self.arena = _bytes(self.sizes["arena"], self.device) if training else None

@@ -140,8 +140,14 @@ T* at(void* base, int64_t off) {
 
 // BF16 forward split (plans with hot set): cold experts stay on the
 // streaming tiles, experts with many rows take the 256 x 256 MFMA tiles.
-static void use_hot(const moe_plan_s* p, void* ws, FwdArgs& a) {
+// In automatic mode the large tiles are used only when the call could give
+// them at least three items per four compute units (R_max / 256 m-tiles times the GEMM's
+// 256-wide n-tiles): a lone expert of 2,048 rows, such as a shared expert,
+// gives the W13 GEMM 128 items and runs faster on the streaming tiles.
+static void use_hot(moe_plan_s* p, void* ws, FwdArgs& a, int mode /* 0: W13, 1: W2 */) {
   if (!p->hot) return;
+  const int64_t nt = mode == 0 ? p->d.f / 128 : p->d.d / 256;
+  if (p->d.hot_tiles == 0 && 4 * (p->R_max / kBMH) * nt < 3 * int64_t(plan_cus(p))) return;
   a.cstoff = at<int32_t>(ws, p->rl.cstoff);
   a.ctoff = at<int32_t>(ws, p->rl.ctoff);
   a.hotoff = at<int32_t>(ws, p->rl.hotoff);
@@ -295,6 +301,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   if (!(d.swiglu_limit >= 0.0f) || !(d.swiglu_limit < INFINITY)) return MOE_ERR_ARG;
   if (d.mx_w1x32 != 0 && (d.mx_w1x32 != 1 || d.prec != MOE_PREC_MXFP8 || d.training))
     return MOE_ERR_ARG;
+  if (d.hot_tiles < 0 || d.hot_tiles > 2) return MOE_ERR_ARG;
 
   moe_plan_s* p = new (std::nothrow) moe_plan_s();
   if (!p) return MOE_ERR_ARG;
@@ -307,8 +314,8 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
     // the hot-expert kernel addresses an expert's weights and the token rows
     // with 32-bit byte offsets and stores 256-column W2 tiles
     const int64_t lim = int64_t(1) << 32;
-    p->hot = d.prec == MOE_PREC_BF16 && d.d % 256 == 0 && 2 * d.f * d.d * 2 < lim &&
-             d.t_max * d.d * 2 < lim && p->R_max * d.f * 2 < lim;
+    p->hot = d.prec == MOE_PREC_BF16 && d.hot_tiles != 2 && d.d % 256 == 0 &&
+             2 * d.f * d.d * 2 < lim && d.t_max * d.d * 2 < lim && p->R_max * d.f * 2 < lim;
   }
   const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es, Rp = p->Rp_max;
   const bool mx = d.prec == MOE_PREC_MXFP8;
@@ -436,6 +443,13 @@ moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
   std::snprintf(line, sizeof line, "  routed rows R <= %lld, m-tiles <= %lld (%d rows each)\n",
                 (long long)p->R_max, (long long)p->mt_max, kBM);
   s += line;
+  if (d.prec == MOE_PREC_BF16) {
+    static const char* kHot[] = {"automatic", "always", "never"};
+    std::snprintf(line, sizeof line,
+                  "  experts with >= %d rows: 256 x 256 MFMA forward tiles %s%s\n", kHotRows,
+                  kHot[d.hot_tiles], p->hot ? "" : " (not with this shape)");
+    s += line;
+  }
   std::snprintf(line, sizeof line, "  route_ws   %10.2f MiB per layer (metadata + planner record)\n",
                 mib(p->rl.total));
   s += line;
@@ -573,7 +587,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     a13.stoff = mtoff;
-    use_hot(p, ws, a13);
+    use_hot(p, ws, a13, 0);
     a13.limit = swiglu_limit(p);
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
@@ -581,7 +595,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + L.h2, w->w2, h3, nullptr,
                d.f, d.d, d.f, d.d / 128, d.e, 0};
     a2.stoff = mtoff;
-    use_hot(p, ws, a2);
+    use_hot(p, ws, a2, 1);
     return hip_status(timed(p, "w2_scatter", s,
                             [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
   }
@@ -656,7 +670,7 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
     FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     a13.stoff = mtoff;
-    use_hot(p, ws, a13);
+    use_hot(p, ws, a13, 0);
     a13.limit = swiglu_limit(p);
     e = timed(p, "w13_swiglu", s,
               [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
@@ -664,7 +678,7 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
     FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + L.h2, w->w2, nullptr, nullptr,
                d.f, d.d, d.f, d.d / 128, d.e, 0, nullptr, d.k, scores, y32};
     a2.stoff = mtoff;
-    use_hot(p, ws, a2);
+    use_hot(p, ws, a2, 1);
     e = timed(p, "w2_fused", s, [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); });
   } else {
     e = mx_forward_w13(p, hdr, ws, sc, x, w, 0, cus, s);
@@ -726,7 +740,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
               d.d, 2 * d.f, d.f, d.f / 64, d.e, 1, x, d.k};
   a13.stoff = mtoff;
-  use_hot(p, ws, a13);
+  use_hot(p, ws, a13, 0);
   a13.limit = swiglu_limit(p);
   e = timed(p, "replay_w13", s, [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;

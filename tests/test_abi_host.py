@@ -68,6 +68,27 @@ def test_plan_rejects_bad_args(b):
     assert ei.value.code == 1
 
 
+def test_plan_hot_tiles_option(b):
+    for bad in (-1, 3):
+        with pytest.raises(b.MoeError) as ei:
+            b.moe_plan_create(16, 256, 128, 8, 2, "bf16", hot_tiles=bad)
+        assert ei.value.code == 1
+    for mode, word in (("auto", "automatic"), ("always", "always"), ("never", "never")):
+        p = b.moe_plan_create(16, 256, 128, 8, 2, "bf16", hot_tiles=mode)
+        try:
+            text = b.moe_plan_explain(p)
+            assert f"MFMA forward tiles {word}" in text
+            # D = 256 allows the large tiles; "never" switches them off
+            assert ("not with this shape" in text) == (mode == "never")
+        finally:
+            b.moe_plan_destroy(p)
+    p = b.moe_plan_create(16, 384, 128, 8, 2, "bf16", hot_tiles="always")   # D % 256 != 0
+    try:
+        assert "not with this shape" in b.moe_plan_explain(p)
+    finally:
+        b.moe_plan_destroy(p)
+
+
 @pytest.mark.parametrize("limit", [-1.0, float("inf"), float("nan")])
 def test_plan_rejects_bad_swiglu_limit(b, limit):
     with pytest.raises(b.MoeError):
