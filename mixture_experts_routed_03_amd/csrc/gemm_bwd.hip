@@ -37,9 +37,13 @@
 //    work item, 64 token rows per stage; the next item's first stage is
 //    loaded while the current tile is staged through LDS and stored as whole
 //    512-byte (bf16) or 1 KB (fp32) row segments, the write shape HBM takes
-//    fastest.  Items
-//    run expert-major with the output column tile fastest, so the workgroups
-//    of one XCD write long contiguous runs of dW rows.
+//    fastest.  Items run expert-major.  dW13 (14 KB rows at D = 7,168) takes
+//    them with the output column tile fastest, so the workgroups of one XCD
+//    write long contiguous runs of dW rows; dW2, whose rows have a
+//    power-of-two byte pitch at F = 1,024 ... 4,096, takes them with the
+//    128-row band fastest, so the concurrent workgroups write one column
+//    segment of many bands: at F = 2,048 that wrote 5.9 instead of 5.1 TB/s
+//    (column-fastest reached 5.75 TB/s only at the 6 KB pitch of F = 3,072).
 //  * Persistent, XCD-aware grids as in the forward kernels.
 #include <algorithm>
 #include <type_traits>
@@ -380,8 +384,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
   int w0 = first + slot;
   int ie = w0 / per_e;
   int irem = w0 - ie * per_e;
-  int itb = irem / NA;
-  int ita = irem - itb * NA;
+  // dW2 (rows of F values: a power-of-two byte pitch at the usual widths)
+  // takes its items with the 128-row band tb fastest, dW13 with the column
+  // tile ta fastest: the order that writes fastest for each (see the loop
+  // below).
+  constexpr bool kBandFast = TAG == 2;
+  int itb = kBandFast ? irem % NB : irem / NA;
+  int ita = kBandFast ? irem / NB : irem - itb * NA;
   const int wend = last;
   int wcur = w0;
   auto fill = [&](Item& t) {
@@ -398,12 +407,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
     t.ncols = min(256, a_ld - ita * 256);
     // advance to the next item of this workgroup
     wcur += per;
-    ita += per;
-    while (ita >= NA) {
-      ita -= NA;
-      if (++itb == NB) {
-        itb = 0;
-        ++ie;
+    if (kBandFast) {
+      itb += per;
+      while (itb >= NB) {
+        itb -= NB;
+        if (++ita == NA) {
+          ita = 0;
+          ++ie;
+        }
+      }
+    } else {
+      ita += per;
+      while (ita >= NA) {
+        ita -= NA;
+        if (++itb == NB) {
+          itb = 0;
+          ++ie;
+        }
       }
     }
   };

@@ -719,8 +719,13 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
   int w0 = first + slot;
   int ie = w0 / per_e;
   int irem = w0 - ie * per_e;
-  int itb = irem / NA;
-  int ita = irem - itb * NA;
+  // dW2 (rows of F values: a power-of-two byte pitch at the usual widths)
+  // takes its items with the 128-row band tb fastest, dW13 with the column
+  // tile ta fastest: the order that writes fastest for each (see the loop
+  // below).
+  constexpr bool kBandFast = TAG == 2;
+  int itb = kBandFast ? irem % NB : irem / NA;
+  int ita = kBandFast ? irem / NB : irem - itb * NA;
   const int wend = last;
   int wcur = w0;
   auto fill = [&](Item& t) {
@@ -736,12 +741,23 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
     t.S = (t.mp + 63) / 64;
     t.ncols = min(256, a_ld - ita * 256);
     wcur += per;
-    ita += per;
-    while (ita >= NA) {
-      ita -= NA;
-      if (++itb == NB) {
-        itb = 0;
-        ++ie;
+    if (kBandFast) {
+      itb += per;
+      while (itb >= NB) {
+        itb -= NB;
+        if (++ita == NA) {
+          ita = 0;
+          ++ie;
+        }
+      }
+    } else {
+      ita += per;
+      while (ita >= NA) {
+        ita -= NA;
+        if (++itb == NB) {
+          itb = 0;
+          ++ie;
+        }
       }
     }
   };
