@@ -181,9 +181,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
     // accumulator depends on a branch inside the stage loop); the token stage
     // holds 64 rows per pass of the 512 threads (rows past the tile repeat its
     // last row).
+    // W2 rows (the contraction of the W2 DGRAD) are F values apart, a
+    // power-of-two byte pitch at the usual widths, and the n-tiles of one
+    // expert run side by side: each starts its contraction at its own
+    // offset, nt * S / NT stages, so at any moment they read different row
+    // bands instead of the same one (the sum's order is fixed per item).
+    const int rot = KIND == 0 ? int(int64_t(nt) * S / a.NT) : 0;
     auto load = [&](u32x4* R, int s, auto nb_c, auto tm_c) {
       constexpr int NB = decltype(nb_c)::value;
       constexpr bool TM = decltype(tm_c)::value;
+      s += rot;
+      if (s >= S) s -= S;
       const uint16_t* p = wsrc + int64_t(s) * 64 * N;
       // weights stream through once: non-temporal loads keep them from
       // evicting the token tiles the other n-tiles of this expert re-read
