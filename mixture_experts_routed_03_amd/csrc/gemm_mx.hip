@@ -531,7 +531,13 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
     // NB: 32-token blocks multiplied (1 or 2; one loop copy each); the 512
     // threads load all 64 rows of the token stage (rows past the tile repeat
     // its last row).
+    // W2 DGRAD: each n-tile starts its contraction at nt * S / NT stages, so
+    // the n-tiles of an expert read different bands of W2's power-of-two
+    // pitch rows at any moment (the sum's order is fixed per item).
+    const int rot = KIND == 0 ? int(int64_t(nt) * S / a.NT) : 0;
     auto load = [&](u32x4* R, uint32_t* Sc, int s, auto) {
+      s += rot;
+      if (s >= S) s -= S;
       const uint8_t* p = wsrc + int64_t(s) * 128 * N;
 #pragma unroll
       for (int i = 0; i < 4; ++i)   // weights: non-temporal (streamed once per m-tile)
