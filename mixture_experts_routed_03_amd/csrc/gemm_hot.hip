@@ -33,7 +33,7 @@
 //    each wave owns 64 gate and the matching 64 up rows, so the SwiGLU
 //    epilogue works on its own accumulators.
 //  * Token rows past an expert's last row re-read that row (unconditional
-//    loads); a wave whose 128 token rows are partly or wholly past the end
+//    loads); a wave whose 64 token rows are partly or wholly past the end
 //    skips the MFMAs of its dead 32-row blocks (a wave-uniform branch).
 //  * Persistent grid of one workgroup per CU; each XCD runs a contiguous run
 //    of items ordered expert-major, then n-tile, then m-tile, so the m-tiles
