@@ -1,17 +1,22 @@
 """MXFP8 codecs and the quantization-faithful MXFP8 expert path (test infrastructure).
 
 Source: "Dist-MoE - Speed-of-light distributed Mixture-of-Experts kernels",
-section 02 "Expert Computation and Tensor Precision":
-  * E4M3 has 4 exponent bits and 3 fraction bits; its largest finite
-    magnitude is 448.  E8M0 encodes a power-of-two scale in one byte.
-  * MXFP8 stores E4M3 values with one E8M0 scale per 32 logical values; the
-    producer picks the scale, rounds the values and publishes both.
-  * forward GEMMs contract over features, so activation rows carry scales
-    along that axis (1x32); weight gradients contract over token rows and use
-    a separately quantized column bundle (32x1 down the rows); static weights
-    use 32x32 blocks, so forward and input-gradient GEMMs share the same
-    values with two scale orientations.
-  * MXFP8 training quantizes the BF16 rows after the gather.
+section 02 "Expert Computation and Tensor Precision".  What that section
+fixes, restated:
+  * the element format E4M3 (one sign bit, a 4-bit exponent and a 3-bit
+    fraction) tops out at 448; the scale format E8M0 is a single byte that
+    holds a power of two;
+  * an MXFP8 tensor is E4M3 data plus one E8M0 scale for every 32
+    consecutive logical values, and whoever produces the tensor chooses the
+    scale, rounds the data with it and hands out both;
+  * the scale axis follows the contraction: forward GEMMs sum over features,
+    so activation rows are scaled in 1x32 runs along the features; weight
+    gradients sum over token rows, so they read a column bundle quantized in
+    32x1 runs down the rows; prepared weights use 32x32 tiles, whose data is
+    shared by the forward and input-gradient GEMMs, each reading the scale
+    in its own orientation;
+  * in training the rows are quantized after the gather, from their BF16
+    form.
 
 Readings taken where the page is silent (each is a choice, listed in the
 design notes):
@@ -147,36 +152,50 @@ def qdq_32x32(w: np.ndarray) -> np.ndarray:
 # the MXFP8 path feeds to a block-scaled GEMM, fp64 everywhere else.
 # --------------------------------------------------------------------------
 
-def expert_ffn_mx(x_rows, w13q, w2q, limit=None):
+def _identity(v):
+    return v
+
+
+def expert_ffn_mx(x_rows, w13q, w2q, limit=None, act=bf16_round):
     """Forward.  x rows (BF16) quantized 1x32 along D after the gather; h1
     stored BF16; h2 = SiLU(g) * u from it (clamped SwiGLU with ``limit``, see
     oracle.moe.swiglu), rounded to BF16 and quantized 1x32 along F for the W2
     GEMM.  ``w13q``/``w2q`` are 32x32-block dequantized weights.  Returns h1
-    (BF16 values), h2 (BF16 values) and h3."""
+    (BF16 values), h2 (BF16 values) and h3.
+
+    ``act`` is the rounding applied where an intermediate is materialized
+    before it is quantized (h1, h2): BF16 by default (the reading above);
+    ``act=None`` keeps them in fp64, the reading in which only the block
+    quantizers round (used to show that the BF16 rounding points are not
+    what makes a comparison pass)."""
     from .moe import swiglu
+    act = act or _identity
     F = w2q.shape[1]
-    h1 = bf16_round(qdq_rows(x_rows) @ w13q.T)
+    h1 = act(qdq_rows(x_rows) @ w13q.T)
     g, u = h1[:, :F], h1[:, F:]
-    h2 = bf16_round(swiglu(g, u, limit))
+    h2 = act(swiglu(g, u, limit))
     h3 = qdq_rows(h2) @ w2q.T
     return h1, h2, h3
 
 
-def expert_ffn_backward_mx(x_rows, w13q, w2q, h1, dh3, limit=None):
+def expert_ffn_backward_mx(x_rows, w13q, w2q, h1, dh3, limit=None, act=bf16_round):
     """Backward.  ``h1`` is the stored BF16 h1, ``dh3`` the route gradient
     (rounded to BF16 here).  DGRAD operands are quantized along their
     contraction axis (dh3 1x32 along D, dh1 1x32 along 2F) and use the same
     32x32 weight values; WGRAD operands are column bundles (32x1 down the
-    expert's rows) of dh3, h2, dh1 and x.  ``limit``: clamped SwiGLU."""
+    expert's rows) of dh3, h2, dh1 and x.  ``limit``: clamped SwiGLU.
+    ``act``: rounding of the materialized intermediates (h2, dh3, dh1), as
+    in ``expert_ffn_mx``."""
     from .moe import swiglu, swiglu_backward
+    act = act or _identity
     F = w2q.shape[1]
     g, u = h1[:, :F], h1[:, F:]
-    h2 = bf16_round(swiglu(g, u, limit))
-    dh3 = bf16_round(dh3)
+    h2 = act(swiglu(g, u, limit))
+    dh3 = act(dh3)
     dh2 = qdq_rows(dh3) @ w2q
     dw2 = qdq_cols(dh3).T @ qdq_cols(h2)
     dg, du = swiglu_backward(g, u, dh2, limit)
-    dh1 = bf16_round(np.concatenate([dg, du], axis=1))
+    dh1 = act(np.concatenate([dg, du], axis=1))
     dx = qdq_rows(dh1) @ w13q
     dw13 = qdq_cols(dh1).T @ qdq_cols(x_rows)
     return dx, dw13, dw2, dh1
@@ -225,11 +244,13 @@ def quantize_cols(v):
 # Whole layer, quantization-faithful (same routing and combine as moe.py)
 # --------------------------------------------------------------------------
 
-def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None, w1x32=False):
+def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None, w1x32=False,
+            act=bf16_round):
     """MXFP8 layer forward: weights in 32x32 blocks (``w1x32``: 1x32 blocks
     along each weight row, the inference preparation that the Supported modes
     section of the explainx.ai post on Dist-MoE names beside the training-compatible 32x32), activations per
-    the expert functions above; combine in fp64.  ``limit``: clamped SwiGLU."""
+    the expert functions above; combine in fp64.  ``limit``: clamped SwiGLU.
+    ``act``: rounding of materialized intermediates (BF16; None = none)."""
     wq = qdq_rows if w1x32 else qdq_32x32
     from . import moe
     X = moe.as_f64(x)
@@ -248,13 +269,13 @@ def forward(x, ids, scores, w13, w2, *, y_addend=None, keep=False, limit=None, w
             continue
         routes = rt["sorted_route"][a:b]
         h1, _, h3 = expert_ffn_mx(X[routes // K], wq(moe.as_f64(w13[e])),
-                                  wq(moe.as_f64(w2[e])), limit)
+                                  wq(moe.as_f64(w2[e])), limit, act)
         H1[a:b], H3S[routes] = h1, h3
     Y = moe.combine(H3S, S, ids_a, E)
     if y_addend is not None:
         Y = Y + moe.as_f64(y_addend)
     if keep:
-        return Y, dict(route=rt, H1=H1, H3S=H3S, K=K, E=E, limit=limit)
+        return Y, dict(route=rt, H1=H1, H3S=H3S, K=K, E=E, limit=limit, act=act)
     return Y
 
 
@@ -286,7 +307,7 @@ def backward(dy, x, ids, scores, w13, w2, cache):
         routes = rt["sorted_route"][a:b]
         dxe, dw13e, dw2e, _ = expert_ffn_backward_mx(
             X[routes // K], qdq_32x32(moe.as_f64(w13[e])), qdq_32x32(moe.as_f64(w2[e])),
-            cache["H1"][a:b], dH3S[routes], cache.get("limit"))
+            cache["H1"][a:b], dH3S[routes], cache.get("limit"), cache.get("act", bf16_round))
         dW13[e], dW2[e] = dw13e, dw2e
         dXr[routes] = dxe
     for k in range(K):

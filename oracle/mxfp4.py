@@ -124,18 +124,21 @@ def unpack_e2m1(packed) -> np.ndarray:
     return out
 
 
-def expert_ffn_mxfp4(x_rows, w13q, w2q, limit=None):
+def expert_ffn_mxfp4(x_rows, w13q, w2q, limit=None, act=bf16_round):
     """One expert's forward with MXFP4 operands.  ``w13q``/``w2q`` are the
-    dequantized 1x32-block E2M1 weights.  Returns h1, h2 (BF16 values) and h3."""
+    dequantized 1x32-block E2M1 weights.  Returns h1, h2 (BF16 values) and h3.
+    ``act``: rounding of the materialized h1 and h2 (BF16; None = none)."""
     from .moe import swiglu
+    act = act or (lambda v: v)
     F = w2q.shape[1]
-    h1 = bf16_round(qdq_rows_fp4(x_rows) @ w13q.T)
-    h2 = bf16_round(swiglu(h1[:, :F], h1[:, F:], limit))
+    h1 = act(qdq_rows_fp4(x_rows) @ w13q.T)
+    h2 = act(swiglu(h1[:, :F], h1[:, F:], limit))
     h3 = qdq_rows_fp4(h2) @ w2q.T
     return h1, h2, h3
 
 
-def forward(x, ids, scores, w13, w2, *, y_addend=None, limit=None, experts=None):
+def forward(x, ids, scores, w13, w2, *, y_addend=None, limit=None, experts=None,
+            act=bf16_round):
     """MXFP4 layer forward (inference): weights quantized 1x32 along their
     contraction axis, activations per ``expert_ffn_mxfp4``, routing and the
     fp64 combine of the BF16 layer.  ``experts``: optional subset of experts
@@ -155,7 +158,7 @@ def forward(x, ids, scores, w13, w2, *, y_addend=None, limit=None, experts=None)
             continue
         routes = rt["sorted_route"][a:b]
         _, _, h3 = expert_ffn_mxfp4(X[routes // K], qdq_rows_fp4(moe.as_f64(w13[e])),
-                                    qdq_rows_fp4(moe.as_f64(w2[e])), limit)
+                                    qdq_rows_fp4(moe.as_f64(w2[e])), limit, act)
         H3S[routes] = h3
     Y = moe.combine(H3S, S, ids_a, E)
     if y_addend is not None:

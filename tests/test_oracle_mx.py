@@ -97,12 +97,14 @@ def test_mx_path_reduces_to_exact_path_without_rounding(monkeypatch):
     M, D, F = 7, 64, 32
     x = rng.standard_normal((M, D)); w13 = rng.standard_normal((2 * F, D)); w2 = rng.standard_normal((D, F))
     dh3 = rng.standard_normal((M, D))
-    for name in ("qdq_rows", "qdq_cols", "bf16_round"):
+    for name in ("qdq_rows", "qdq_cols"):
         monkeypatch.setattr(mx, name, lambda v: np.asarray(v, dtype=np.float64))
-    h1, h2, h3 = mx.expert_ffn_mx(x, w13, w2)
+    # act=None: the switch that drops the BF16 rounding of materialized
+    # intermediates; with the block quantizers off too, nothing rounds
+    h1, h2, h3 = mx.expert_ffn_mx(x, w13, w2, act=None)
     r1, r2, r3 = moe.expert_ffn(x, w13, w2)
     np.testing.assert_allclose(h3, r3, rtol=1e-12, atol=1e-12)
-    got = mx.expert_ffn_backward_mx(x, w13, w2, h1, dh3)
+    got = mx.expert_ffn_backward_mx(x, w13, w2, h1, dh3, act=None)
     ref = moe.expert_ffn_backward(x, w13, w2, r1, dh3)
     for a, b in zip(got, ref):
         np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-11)
@@ -144,9 +146,9 @@ def test_mx_layer_reduces_to_fp64_layer_without_rounding(monkeypatch):
     x = rng.standard_normal((T, D)); w13 = rng.standard_normal((E, 2 * F, D))
     w2 = rng.standard_normal((E, D, F)); ids = np.array([[0, 1], [1, 2], [2, -1], [0, 2], [1, 0], [-1, -1]])
     s = rng.random((T, K)); s[ids < 0] = 0; dy = rng.standard_normal((T, D))
-    for name in ("qdq_rows", "qdq_cols", "qdq_32x32", "bf16_round"):
+    for name in ("qdq_rows", "qdq_cols", "qdq_32x32"):
         monkeypatch.setattr(mx, name, lambda v: np.asarray(v, dtype=np.float64))
-    y, c = mx.forward(x, ids, s, w13, w2, keep=True)
+    y, c = mx.forward(x, ids, s, w13, w2, keep=True, act=None)
     ry, rc = moe.forward(x, ids, s, w13, w2, keep=True)
     np.testing.assert_allclose(y, ry, rtol=1e-12, atol=1e-12)
     for a, b in zip(mx.backward(dy, x, ids, s, w13, w2, c), moe.backward(dy, x, ids, s, w13, w2, rc)):
@@ -173,3 +175,28 @@ def test_bf16_round_matches_library_conversion():
     ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
     got = mx.bf16_round(x.astype(np.float64))
     np.testing.assert_array_equal(got, ref)
+
+
+def test_mx_bf16_rounding_points_are_load_bearing():
+    """The two readings of the rounding points (BF16 materialization before
+    each quantizer, or none) are not interchangeable at the MXFP8 tolerance:
+    moving h2 by one BF16 rounding pushes a few percent of its values across
+    an E4M3 rounding boundary, and each such value then moves by a whole
+    E4M3 step (6-12 %).  Over ten seeds the two readings' h3 differ by 2-5e-2
+    max-abs-rel, most of the 6e-2 bound, while each stays within the bound of
+    the unquantized-activation product.  So the oracle must quantize the same
+    BF16 values the kernels store; the GPU tests report their distance to
+    both readings."""
+    errs, errq = [], []
+    for seed in range(11, 21):
+        rng = np.random.default_rng(seed)
+        M, D, F = 48, 256, 128
+        x = rng.standard_normal((M, D))
+        w13 = mx.qdq_32x32(rng.standard_normal((2 * F, D)) / 16)
+        w2 = mx.qdq_32x32(rng.standard_normal((D, F)) / np.sqrt(F))
+        a = mx.expert_ffn_mx(x, w13, w2)[2]
+        b = mx.expert_ffn_mx(x, w13, w2, act=None)[2]
+        errs.append(moe.max_abs_rel(a, b))
+        errq.append(moe.max_abs_rel(a, moe.expert_ffn(x, w13, w2)[2]))
+    assert 1e-2 < min(errs) and max(errs) < 6e-2
+    assert max(errq) < 6e-2
