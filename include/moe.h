@@ -93,10 +93,15 @@ typedef enum moe_dtype {
  * dW is then read as well as written. */
 #define MOE_BWD_ACCUMULATE_DW 0x2u
 
-/* Layer description.  Supported: D % 128 == 0, F % 128 == 0, 1 <= K <= 16,
- * K <= E <= 4096, 0 <= t_max <= 2^24 / K (else MOE_ERR_SHAPE).  MXFP4:
- * D % 256 == 0 and F % 256 == 0 (else MOE_ERR_SHAPE), training 0 (else
- * MOE_ERR_ARG). */
+/* Layer description.  Supported: D % 128 == 0, F % 128 == 0, D and F at
+ * most 65,536, 1 <= K <= 16, 1 <= E <= 4096, 0 <= t_max <= 2^24 / K (else
+ * MOE_ERR_SHAPE).  K may exceed E: a token may name one expert in several
+ * slots, and each such slot is an independent route.  E is bounded by the
+ * router, which keeps one counter per expert in on-chip LDS per 256-route
+ * chunk (at the pages' expert size, D = 7,168 and F = 2,048, 4,096 BF16
+ * experts would already need 360 GB of weights, more than one GPU holds).
+ * MXFP4: D % 256 == 0 and F % 256 == 0 (else MOE_ERR_SHAPE), training 0
+ * (else MOE_ERR_ARG). */
 typedef struct moe_desc {
   int64_t t_max;            /* most tokens any call will pass */
   int32_t d;                /* token width D */
@@ -172,10 +177,25 @@ typedef struct moe_grads {
 } moe_grads;
 
 /* Validate a description and build a host-side plan (no device work).
- * *out receives a handle owned by the library; free it with moe_plan_destroy. */
+ * The Dist-MoE explainer's section 08 (public API) and the explainx.ai post's
+ * list of key design points describe a context that owns the layer's buffers
+ * and is reused sequentially, never reentrantly; on one GPU that context
+ * becomes this plan plus caller-owned buffers sized from it.  Section 03
+ * (memory planning) gives the sizing rules: one layer's saved state counted
+ * with align128 byte terms, one scratch region shared by every call and
+ * sized for the largest temporary layout.  desc: host pointer, read only;
+ * *out receives a handle owned by the library (free it with
+ * moe_plan_destroy).  MOE_ERR_ARG for a null pointer or an option outside
+ * its set, MOE_ERR_SHAPE for shapes outside the limits above. */
 moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out);
 
-/* Buffer sizes for a plan (host only). */
+/* Byte sizes of every caller-owned buffer of a plan (host only; sizes is a
+ * host out-parameter).  Explainer section 03: the activation arena holds
+ * saved state up to the budget (a soft limit: a layer that does not fit
+ * replays), scratch holds the largest single call's temporaries (a hard
+ * limit, here guaranteed by sizing it for t_max routes), and each layer's
+ * routing metadata and route-output slots are separate.  MOE_ERR_ARG for a
+ * null plan or sizes. */
 moe_status moe_plan_sizes(moe_plan_t plan, moe_sizes* sizes);
 
 /* Human-readable breakdown of the plan's buffers into buf (host, NUL
@@ -242,10 +262,16 @@ moe_status moe_combine(moe_plan_t plan, void* route_ws, const float* scores,
                        const void* h3_slots, const void* y_addend, void* y,
                        hipStream_t stream);
 
-/* Inference forward with the combine fused into the W2 epilogue (the FUSED
- * mode of the explainer's section 05 kernels, where the expert kernel adds
- * each route's weighted output into its token's row): like moe_expert_fwd
- * followed by moe_combine, but every route's bf16-rounded (F32 plans: fp32)
+/* Inference forward with the combine fused into the W2 epilogue: the
+ * score-weighted scatter-add of every route's output into its token's row,
+ * the combine that "Mixture of Experts: How Routing Becomes GPU Computation"
+ * writes as an index_add_ of weighted expert outputs into the original token
+ * rows (section 2, selected-expert forward), done inside the W2 kernel
+ * instead of as a separate pass.  (The Dist-MoE explainer's own W2 epilogue,
+ * section 05, stores each route's result to its return slot and leaves the
+ * weighted sum to the token owner; moe_expert_fwd + moe_combine is that
+ * form.)  Like moe_expert_fwd followed by moe_combine, but every route's
+ * bf16-rounded (F32 plans: fp32)
  * h3, times its score, is added into y32[t] (caller-owned fp32 [T,D]
  * scratch, zeroed by this call) with hardware float atomics, then
  * y = y32 (+ y_addend).  No route slots are written, so the order of the K
@@ -272,12 +298,22 @@ moe_status moe_expert_bwd(moe_plan_t plan, int32_t layer, void* route_ws, const 
 
 /* Synchronizes stream and returns the sticky MOE_STATUS_* bits of route_ws
  * (host out-parameter) together with, when not null, the layer's planner
- * decision (*replayed = 1 when its forward chose replay). */
+ * decision (*replayed = 1 when its forward chose replay).  The explainx.ai
+ * post's list of key design points has invalid ids and overflowing scratch
+ * end in a device trap that invalidates the whole context; here the kernels
+ * record such conditions as sticky bits and carry on (bad ids act as padding,
+ * scratch cannot overflow because it is sized for t_max routes), and this
+ * call is the one place that reads them back.  MOE_ERR_ARG for a null
+ * route_ws or status, MOE_ERR_HIP if the copy or the wait fails. */
 moe_status moe_read_status(void* route_ws, uint32_t* status, int32_t* replayed,
                            hipStream_t stream);
 
-/* Rewind the arena to empty (after an aborted step, when no backward still
- * needs a saved state). */
+/* Rewind the arena to empty, for a step that was abandoned between its
+ * forwards and backwards.  The Dist-MoE explainer's section 06 (pipeline
+ * liveness and slot reuse) allows resetting state after an aborted schedule
+ * only once no backward still owns it; the caller guarantees that (no
+ * pending moe_expert_bwd of this arena).  Enqueued on stream; MOE_ERR_ARG for
+ * a null plan or arena. */
 moe_status moe_arena_reset(moe_plan_t plan, void* arena, hipStream_t stream);
 
 /* Routing results of route_ws copied to host memory (synchronizes stream):

@@ -287,8 +287,12 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   if (!desc || !out) return MOE_ERR_ARG;
   *out = nullptr;
   const moe_desc& d = *desc;
-  if (d.t_max < 0 || d.k < 1 || d.k > kMaxK || d.e < d.k || d.e > kMaxE || d.d <= 0 ||
-      d.f <= 0 || d.d % 128 || d.f % 128 || d.t_max * d.k > (int64_t(1) << 24))
+  // K may exceed E: duplicate ids inside a token are independent routes.
+  // D and F are bounded so that every per-row index the kernels form in 32
+  // bits (row lengths, stage counts, E * 2F weight rows) stays in range.
+  if (d.t_max < 0 || d.k < 1 || d.k > kMaxK || d.e < 1 || d.e > kMaxE || d.d <= 0 ||
+      d.f <= 0 || d.d > kMaxWidth || d.f > kMaxWidth || d.d % 128 || d.f % 128 ||
+      d.t_max * d.k > (int64_t(1) << 24))
     return MOE_ERR_SHAPE;
   if (d.prec != MOE_PREC_F32 && d.prec != MOE_PREC_BF16 && d.prec != MOE_PREC_MXFP8 &&
       d.prec != MOE_PREC_MXFP4)
@@ -315,7 +319,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
     // with 32-bit byte offsets and stores 256-column W2 tiles
     const int64_t lim = int64_t(1) << 32;
     p->hot = d.prec == MOE_PREC_BF16 && d.hot_tiles != 2 && d.d % 256 == 0 &&
-             2 * d.f * d.d * 2 < lim && d.t_max * d.d * 2 < lim && p->R_max * d.f * 2 < lim;
+             int64_t(4) * d.f * d.d < lim && d.t_max * d.d * 2 < lim && p->R_max * d.f * 2 < lim;
   }
   const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es, Rp = p->Rp_max;
   const bool mx = d.prec == MOE_PREC_MXFP8;

@@ -14,8 +14,14 @@ constexpr int kBM = 64;           // token rows per WGRAD contraction stage (and
 constexpr int kBMX = 128;         // token rows of an FPROP/DGRAD m-tile of an expert with > kBM rows
 constexpr int kRankChunk = 256;   // routes per counting-sort chunk
 constexpr int kMxBlock = 32;      // MX block length (values per E8M0 scale)
+// Experts per plan.  Routing keeps one counter per expert in LDS for each
+// 256-route chunk (16 KiB at 4,096) and the one-workgroup decode router holds
+// E counters too; 4,096 experts is ten times the pages' largest count (384),
+// and at their expert size (D = 7,168, F = 2,048) 4,096 bf16 experts would
+// already need 360 GB of weights, more than one GPU's 288 GB of HBM.
 constexpr int kMaxE = 4096;
 constexpr int kMaxK = 16;
+constexpr int kMaxWidth = 65536;  // largest D and F
 
 __host__ __device__ inline int64_t align_up(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
 __host__ __device__ inline int64_t align128(int64_t n) { return align_up(n, 128); }

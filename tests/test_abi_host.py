@@ -49,7 +49,8 @@ def test_plan_sizes_and_explain(b):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(d=100), dict(f=64), dict(k=0), dict(k=17), dict(e=5000), dict(e=1, k=2), dict(t_max=-1),
+    dict(d=100), dict(f=64), dict(k=0), dict(k=17), dict(e=5000), dict(e=0), dict(t_max=-1),
+    dict(d=65536 + 128), dict(f=65536 + 128),
 ])
 def test_plan_rejects_bad_shapes(b, kw):
     args = dict(t_max=16, d=256, f=128, e=8, k=2)
@@ -161,3 +162,26 @@ def test_calls_reject_before_enqueue(b):
     assert L.moe_expert_bwd(plan, 0, 256, 256, 256, 256, ctypes.byref(w), 256, 256, 256,
                             ctypes.byref(g), 0, null) == 3    # inference plan has no backward
     b.moe_plan_destroy(plan)
+
+
+def test_plan_accepts_k_above_e(b):
+    """Duplicate ids inside a token are independent routes, so K > E is a
+    legal plan (every token then names some expert twice)."""
+    p = b.moe_plan_create(16, 256, 128, 2, 6, "bf16", training=True)
+    try:
+        assert "E=2 K=6" in b.moe_plan_explain(p)
+    finally:
+        b.moe_plan_destroy(p)
+
+
+def test_plan_hot_tiles_need_32bit_offsets(b):
+    """The hot-expert tiles address one expert's W13 with 32-bit byte
+    offsets: 2F x D bf16 values must span less than 4 GiB.  At F = D = 32,768
+    that is exactly 4 GiB, so the large tiles stay off (the bound is computed
+    in 64 bits; in 32 bits 2 * F * D * 2 wraps to 0)."""
+    for f, on in ((16384, True), (32768, False)):
+        p = b.moe_plan_create(16, 32768, f, 8, 2, "bf16", hot_tiles="always")
+        try:
+            assert ("not with this shape" in b.moe_plan_explain(p)) != on, f
+        finally:
+            b.moe_plan_destroy(p)
