@@ -10,11 +10,12 @@ backward, W2/W13 WGRAD, W13 DGRAD, input-gradient reduction).  MXFP8
 workloads add the row quantizers and column bundles.
 
 Workloads (all at T = 2,048 tokens, D = 7,168, F = 2,048, E = 384, top-6):
-  bf16_train_balanced  BF16, balanced routing, forward + backward (default)
+  bf16_train_zipf      BF16, Zipf(1.2) routing, forward + backward (default:
+                       the stated BF16 forward + backward configuration)
+  bf16_train_balanced  BF16, balanced routing, forward + backward
   bf16_fwd_balanced    BF16, balanced routing, forward only
   bf16_fwd_fused       the same with the combine fused into the W2 epilogue
                        (fp32 atomics; inference form)
-  bf16_train_zipf      BF16, Zipf(1.2) routing, forward + backward
   mxfp8_train_shared   MXFP8 routed layer + one shared BF16 SwiGLU expert,
                        forward + backward
   mxfp8_ten_layer      ten MXFP8 layers (Zipf 0, 0.6, 1.0, 1.4 cycled), ten
@@ -31,13 +32,16 @@ beside it.
 
 Prints ONE JSON line.  Also reports the dominant kernel against its roofline
 (per-kernel HIP-event timing over a second pass of the timed steps, on the
-library's launch stream) and the CPU oracle timed on a bounded sample.
+library's launch stream; beside it the average duration of the same kernel in
+the committed rocprofv3 summary of this workload), the bandwidth-bound row
+kernels timed cold (a third pass in which the library writes a 1 GiB buffer
+before each kernel, outside its events, evicting the 256 MiB Infinity Cache),
+and the CPU oracle timed on a bounded sample.
 """
 
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -69,12 +73,15 @@ WORKLOADS = {
 }
 CPU_EXPERTS = {"bf16": 96, "mxfp8": 3, "mxfp4": 3}
 
-# Library timing name -> (kernel symbol in rocprofv3 traces, per precision;
-# source files that define it).
+# Library timing name -> (kernel symbols in rocprofv3 traces, per precision;
+# source files that define them).  A timing slot may cover several launches
+# (the BF16 forward GEMMs: streaming tiles, then the hot experts' tiles).
 SYMBOLS = {
     "bf16": {
-        "w13_swiglu": ("moe::k_gemm_fwd<unsigned short, 0>", ["gemm_fwd.hip"]),
-        "w2_scatter": ("moe::k_gemm_fwd<unsigned short, 1>", ["gemm_fwd.hip"]),
+        "w13_swiglu": (["moe::k_gemm_fwd<unsigned short, 0>", "moe::k_gemm_hot<0>"],
+                       ["gemm_fwd.hip", "gemm_hot.hip"]),
+        "w2_scatter": (["moe::k_gemm_fwd<unsigned short, 1>", "moe::k_gemm_hot<1>"],
+                       ["gemm_fwd.hip", "gemm_hot.hip"]),
         "w2_dgrad_swiglu": ("moe::k_gemm_dgrad<0>", ["gemm_bwd.hip"]),
         "w13_dgrad": ("moe::k_gemm_dgrad<1>", ["gemm_bwd.hip"]),
         "w2_wgrad": ("moe::k_gemm_wgrad<unsigned short, 2, 0>", ["gemm_bwd.hip"]),
@@ -104,7 +111,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bf16_train_balanced", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="bf16_train_zipf", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-experts", type=int, default=0,
                     help="experts in the CPU-oracle sample (all their routes); 0 = default "
                          "for the precision")
@@ -115,6 +122,9 @@ def parse():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference kernel "
                          "for scaling hardware byte counters)")
+    ap.add_argument("--cold-steps", type=int, default=3,
+                    help="steps of the cold-cache pass (row kernels timed after an Infinity "
+                         "Cache flush); 0 = skip")
     return ap.parse_args()
 
 
@@ -194,24 +204,21 @@ def kernel_flops(name, m):
     return None
 
 
-def src_hashes(files):
-    out = {}
-    for f in files + ["common.h"]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            out[f] = hashlib.sha256(fh.read()).hexdigest()[:16]
-    return out
-
-
-def measured_traffic(workload, prec, kname):
-    """HBM bytes per launch of ``kname`` from the committed rocprofv3 counter
-    summary of this workload, if one exists and the kernel's sources are
-    unchanged since it was taken; else None."""
-    sym, files = SYMBOLS.get(prec, {}).get(kname, (None, None))
-    if sym is None:
-        return None
+def measured_profile(workload, prec, kname):
+    """(HBM bytes per launch, average launch microseconds) of timing slot
+    ``kname`` from the committed rocprofv3 summary of this workload, summed
+    over the slot's kernels, if the summary exists and the code of those
+    kernels (comments ignored) is unchanged since it was taken; else
+    (None, None)."""
+    from mixture_experts_routed_03_amd.profsum import source_hashes
+    syms, files = SYMBOLS.get(prec, {}).get(kname, (None, None))
+    if syms is None:
+        return None, None
+    if isinstance(syms, str):
+        syms = [syms]
     prof_dir = os.path.join(HERE, "profiles")
     if not os.path.isdir(prof_dir):
-        return None
+        return None, None
     for fn in sorted(os.listdir(prof_dir)):
         if not fn.startswith(workload + "_") or not fn.endswith(".md"):
             continue
@@ -221,15 +228,17 @@ def measured_traffic(workload, prec, kname):
         if not mt:
             continue
         blob = json.loads(mt.group(1))
-        per = blob.get("traffic_bytes", {}).get(sym)
-        shas = blob.get("src_sha256_16", {})
-        if not per:
-            continue
-        now = src_hashes(files)
+        shas = blob.get("src_code_sha256_16", {})
+        now = source_hashes(files + ["common.h"])
         if any(shas.get(f) != h for f, h in now.items()):
-            return None
-        return int(sum(per) / len(per))
-    return None
+            return None, None
+        traffic = [blob.get("traffic_bytes", {}).get(s) for s in syms]
+        avg = [blob.get("avg_us_working", {}).get(s) for s in syms]
+        tb = (int(sum(sum(t) / len(t) for t in traffic if t))
+              if traffic[0] else None)
+        us = round(sum(a for a in avg if a), 2) if avg[0] else None
+        return tb, us
+    return None, None
 
 
 # ---------------------------------------------------------------- workloads
@@ -443,6 +452,32 @@ def main():
             ktimes[label + name] = (tot, n)
         B.moe_timing_enable(p.plan, False)
 
+    # ---- third pass: the same steps with the Infinity Cache flushed before
+    # every kernel (outside its events); the row kernels' cold rates
+    cold = {}
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for p in plans.values():
+            B.moe_timing_enable(p.plan, True)
+            B.moe_timing_flush(p.plan, flush)
+        for _ in range(args.cold_steps):
+            step()
+        torch.cuda.synchronize()
+        for label, p in plans.items():
+            if label:
+                B.moe_timing_enable(p.plan, False)
+                B.moe_timing_flush(p.plan, None)
+                continue
+            for name, (tot, n) in B.moe_timing_read(p.plan).items():
+                if name in ("route", "gather", "combine", "combine_bwd", "dx_reduce") and n:
+                    bsum = sum(alg_bytes(name, m) for lab, m in metas if lab == "")
+                    ms = tot / args.cold_steps
+                    cold[name] = {"us": round(tot / n * 1e3, 1),
+                                  "GB/s": round(bsum / (ms * 1e-3) / 1e9, 1)}
+            B.moe_timing_enable(p.plan, False)
+            B.moe_timing_flush(p.plan, None)
+        del flush
+
     # Useful work: routed layers only (the Dist-MoE explainer's count, section
     # 07, excludes shared experts, padding and replay); the shared expert's
     # time stays in the step.
@@ -486,11 +521,16 @@ def main():
     prec_dom = "bf16" if dom.startswith("shared:") else cfg.prec
     # counters were taken at each workload's own width
     sym_key = "mxfp8_1x32" if prec_dom == "mxfp8" and cfg.mx_w1x32 else prec_dom
-    traffic = None if args.width else measured_traffic(args.workload, sym_key, dom_name)
+    traffic, prof_us = ((None, None) if args.width else
+                        measured_profile(args.workload, sym_key, dom_name))
     roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": int(alg_per_launch),
-                "avg_launch_ms": kernels[dom]["avg_ms"]}
+                "avg_launch_ms": kernels[dom]["avg_ms"],
+                # the same kernel's average working-dispatch duration in the
+                # committed rocprofv3 summary of this workload (null when its
+                # code changed since)
+                "profile_avg_launch_ms": None if prof_us is None else round(prof_us / 1e3, 4)}
     # A kernel whose useful FLOPs take longer at the MFMA peak than its bytes
     # at the HBM peak (many rows per expert) is reported against the MFMA peak.
     tfl = kernels[dom].get("TFLOP/s")
@@ -552,6 +592,9 @@ def main():
         "route_GBps": kernels.get("route", {}).get("GB/s"),
         "route_us": (round(kernels["route"]["avg_ms"] * 1e3, 1) if "route" in kernels else None),
         "gather_GBps": kernels.get("gather", {}).get("GB/s"),
+        # bandwidth-bound row kernels with the Infinity Cache flushed before
+        # each launch (per-launch microseconds, algorithmic GB/s)
+        "row_kernels_cold": cold or None,
         "wall_s_timed": round(wall, 3),
         "window_ms_per_step": [round(v, 4) for v in win_ms],
         "median_window_ms": round(sorted(win_ms)[len(win_ms) // 2], 4),

@@ -339,6 +339,16 @@ moe_status moe_saved_ptrs(moe_plan_t plan, void* route_ws, void** x_rows, void**
  * launch count.  moe_timing_enable(plan, 0) stops recording and clears the
  * totals. */
 moe_status moe_timing_enable(moe_plan_t plan, int32_t enable);
+/* Benchmark only: while timing is enabled and buf is non-null, every timed
+ * kernel is preceded, outside its events, by a write of bytes bytes of buf
+ * (caller-owned device memory, 16-byte aligned), so that the kernel reads
+ * its inputs from HBM and not from the 256 MiB memory-side Infinity Cache.
+ * The Dist-MoE explainer's section 07 times whole steps in steady state; a
+ * cold-cache timing of each bandwidth-bound row kernel (routing, gather,
+ * combine, combine backward, input-gradient sum) shows whether its rate is
+ * an HBM rate.  buf = null turns it off.  MOE_ERR_ARG for a null plan or a
+ * misaligned or too small buffer. */
+moe_status moe_timing_flush(moe_plan_t plan, void* buf, size_t bytes);
 moe_status moe_timing_read(moe_plan_t plan, int32_t idx, char* name, size_t cap,
                            double* total_ms, int64_t* launches);
 

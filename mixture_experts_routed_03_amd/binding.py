@@ -82,6 +82,7 @@ _SIGS = {
     "moe_saved_ptrs": [_P, _P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P],
     "moe_mx_quantize": [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P],
     "moe_timing_enable": [_P, ctypes.c_int32],
+    "moe_timing_flush": [_P, _P, ctypes.c_size_t],
     "moe_timing_read": [_P, ctypes.c_int32, ctypes.c_char_p, ctypes.c_size_t,
                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
 }
@@ -245,6 +246,14 @@ def moe_mx_quantize(plan, route_ws, src, n, kind, q, sc, stream=None):
 
 def moe_timing_enable(plan, enable=True):
     _check(lib().moe_timing_enable(plan, int(bool(enable))), "moe_timing_enable")
+
+
+def moe_timing_flush(plan, buf, nbytes=None):
+    """Benchmark only: write ``buf`` (a device tensor; None = off) before each
+    timed kernel, outside its events (see moe.h)."""
+    n = 0 if buf is None else (int(nbytes) if nbytes is not None
+                               else buf.numel() * buf.element_size())
+    _check(lib().moe_timing_flush(plan, _ptr(buf), n), "moe_timing_flush")
 
 
 def moe_timing_read(plan) -> dict:

@@ -27,6 +27,7 @@ hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr
                          const int32_t* route_to_row, void* dst, int64_t T_max, hipStream_t s);
 hipError_t launch_zero_rows_f32(const RouteHdr* hdr, float* p, int64_t D, int64_t T_max,
                                 hipStream_t s);
+hipError_t launch_flush(void* p, int64_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_fused_finish(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
                                const float* scores, const float* y32, const void* addend,
                                void* y, int K, int64_t D, int64_t T_max, uint32_t* status,
@@ -75,6 +76,9 @@ struct moe_plan_s {
     int64_t launches = 0;
   };
   bool timing = false;
+  void* flush_buf = nullptr;   // benchmark: written before each timed kernel
+  int64_t flush_bytes = 0;
+  uint32_t flush_count = 0;
   std::vector<TimerSlot> slots;
   std::vector<hipEvent_t> pool;
 };
@@ -119,12 +123,19 @@ moe_plan_s::TimerSlot& timer_slot(moe_plan_s* p, const char* name) {
 }
 
 // Runs one launcher; when timing is on, brackets it with events on stream s.
+// With a flush buffer set (moe_timing_flush), each timed launch is preceded,
+// outside its events, by a write of that buffer.
 template <class Fn>
 hipError_t timed(moe_plan_s* p, const char* name, hipStream_t s, Fn&& fn) {
   if (!p->timing) return fn();
   hipEvent_t a = take_event(p), b = take_event(p);
   if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, s);
+  hipError_t e = hipSuccess;
+  if (p->flush_buf) {
+    e = launch_flush(p->flush_buf, p->flush_bytes, ++p->flush_count, s);
+    if (e != hipSuccess) return e;
+  }
+  e = hipEventRecord(a, s);
   if (e != hipSuccess) return e;
   e = fn();
   if (e != hipSuccess) return e;
@@ -856,6 +867,13 @@ moe_status moe_timing_enable(moe_plan_t p, int32_t enable) {
     p->slots.clear();
   }
   p->timing = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_timing_flush(moe_plan_t p, void* buf, size_t bytes) {
+  if (!p || (buf && (!aligned16(buf) || bytes < 16))) return MOE_ERR_ARG;
+  p->flush_buf = buf;
+  p->flush_bytes = buf ? int64_t(bytes) : 0;
   return MOE_OK;
 }
 

@@ -436,6 +436,21 @@ hipError_t launch_combine(int prec, const RouteHdr* hdr, const int32_t* route_to
   return hipGetLastError();
 }
 
+// Benchmark helper: writes n16 16-byte chunks of p, so that data read next
+// comes from HBM rather than from the memory-side Infinity Cache (256 MiB on
+// MI355X), which a write of more than its size evicts.
+__global__ __launch_bounds__(256) void k_flush(u32x4* __restrict__ p, int64_t n16, uint32_t v) {
+  for (int64_t g = grid_thread(); g < n16; g += grid_threads())
+    __builtin_nontemporal_store(u32x4{v, v, v, v}, p + g);
+}
+
+hipError_t launch_flush(void* p, int64_t bytes, uint32_t v, hipStream_t s) {
+  if (bytes < 16) return hipSuccess;
+  hipLaunchKernelGGL(k_flush, dim3(elem_grid(bytes / 16)), dim3(256), 0, s,
+                     reinterpret_cast<u32x4*>(p), bytes / 16, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero_rows_f32(const RouteHdr* hdr, float* p, int64_t D, int64_t T_max,
                                 hipStream_t s) {
   if (T_max == 0) return hipSuccess;
