@@ -22,6 +22,7 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
                         const RouteLayout& L, hipStream_t s);
 hipError_t launch_plan_decide(RouteHdr* hdr, const PlanArgs& a, hipStream_t s);
 hipError_t launch_plan_rewind(RouteHdr* hdr, void* arena, hipStream_t s);
+hipError_t launch_plan_enter_bwd(RouteHdr* hdr, const PlanArgs& a, hipStream_t s);
 hipError_t launch_arena_reset(void* arena, hipStream_t s);
 hipError_t launch_gather(const void* x, int64_t D, int es, int K, const RouteHdr* hdr,
                          const int32_t* route_to_row, void* dst, int64_t T_max, hipStream_t s);
@@ -172,6 +173,19 @@ static void use_hot(moe_plan_s* p, void* ws, FwdArgs& a, int mode /* 0: W13, 1: 
 // Clamped SwiGLU limit for the kernels (+inf: the plain SwiGLU).
 static float swiglu_limit(const moe_plan_s* p) {
   return p->d.swiglu_limit > 0.0f ? p->d.swiglu_limit : INFINITY;
+}
+
+// Planner arguments of a layer call: the scratch regions a replaying layer's
+// state lives in (and the arena it is saved in otherwise).
+PlanArgs plan_args(const moe_plan_s* p, int32_t layer, int training, void* arena, char* sc) {
+  const moe_desc& d = p->d;
+  const ScratchLayout& L = p->sl;
+  const bool mx8 = d.prec == MOE_PREC_MXFP8;
+  return PlanArgs{layer, d.max_layers, training, p->es, d.d, d.f, p->budget,
+                  uint64_t(training ? arena : nullptr), uint64_t(sc + L.h1),
+                  mx8 ? 1 : 0, 0,
+                  {mx8 ? uint64_t(sc + L.xcq) : 0, mx8 ? uint64_t(sc + L.xcs) : 0,
+                   mx8 ? uint64_t(sc + L.h2cq) : 0, mx8 ? uint64_t(sc + L.h2cs) : 0}};
 }
 
 hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const void* x,
@@ -585,11 +599,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   RouteHdr* hdr = hdr_of(ws);
   char* sc = reinterpret_cast<char*>(scratch);
   const ScratchLayout& L = p->sl;
-  PlanArgs pa{layer, d.max_layers, d.training, p->es, d.d, d.f, p->budget,
-              uint64_t(d.training ? arena : nullptr), uint64_t(sc + L.h1),
-              mx8 ? 1 : 0, 0,
-              {mx8 ? uint64_t(sc + L.xcq) : 0, mx8 ? uint64_t(sc + L.xcs) : 0,
-               mx8 ? uint64_t(sc + L.h2cq) : 0, mx8 ? uint64_t(sc + L.h2cs) : 0}};
+  const PlanArgs pa = plan_args(p, layer, d.training, arena, sc);
   hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
@@ -645,26 +655,36 @@ moe_status moe_combine(moe_plan_t p, void* ws, const float* scores, const void* 
   }));
 }
 
-moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const float* scores,
-                                const moe_weights* w, float* y32, const void* y_addend, void* y,
-                                void* scratch, hipStream_t s) {
-  if (!p || !ws || !w || !scratch || !y32) return MOE_ERR_ARG;
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of the fused inference forward (nothing enqueued).
+moe_status fused_check(moe_plan_s* p, void* ws, const void* x, const moe_weights* w,
+                       const void* y_addend, void* y) {
+  if (!p || !ws || !w) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
   if (d.training) return MOE_ERR_UNSUPPORTED;   // no route outputs are kept for a backward
-  const bool mx8 = d.prec == MOE_PREC_MXFP8;
-  const bool fp4 = d.prec == MOE_PREC_MXFP4;
-  const bool mx = mx8 || fp4;
+  const bool mx = d.prec == MOE_PREC_MXFP8 || d.prec == MOE_PREC_MXFP4;
   if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;
   if (!aligned16(x) || !aligned16(w->w13) || !aligned16(w->w2) || !aligned16(w->q13) ||
-      !aligned16(w->q2) || !aligned16(y32) || !aligned16(y) || !aligned16(y_addend) ||
-      !aligned16(scratch) || !aligned16(ws))
+      !aligned16(w->q2) || !aligned16(y) || !aligned16(y_addend) || !aligned16(ws))
     return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+// The fused inference forward on a given scratch buffer and fp32 row buffer
+// (arguments already checked).
+moe_status fused_forward(moe_plan_s* p, void* ws, const void* x, const float* scores,
+                         const moe_weights* w, float* y32, const void* y_addend, void* y,
+                         void* scratch, hipStream_t s) {
+  const moe_desc& d = p->d;
+  const bool fp4 = d.prec == MOE_PREC_MXFP4;
+  const bool mx = d.prec == MOE_PREC_MXFP8 || fp4;
   RouteHdr* hdr = hdr_of(ws);
   char* sc = reinterpret_cast<char*>(scratch);
   const ScratchLayout& L = p->sl;
-  PlanArgs pa{0, d.max_layers, 0, p->es, d.d, d.f, p->budget, 0, uint64_t(sc + L.h1), mx8 ? 1 : 0,
-              0, {mx8 ? uint64_t(sc + L.xcq) : 0, mx8 ? uint64_t(sc + L.xcs) : 0,
-                  mx8 ? uint64_t(sc + L.h2cq) : 0, mx8 ? uint64_t(sc + L.h2cs) : 0}};
+  const PlanArgs pa = plan_args(p, 0, 0, nullptr, sc);
   hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
@@ -720,6 +740,19 @@ moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const flo
   }));
 }
 
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_fwd_fused(moe_plan_t p, void* ws, const void* x, const float* scores,
+                                const moe_weights* w, float* y32, const void* y_addend, void* y,
+                                void* scratch, hipStream_t s) {
+  if (!scratch || !y32 || !aligned16(scratch) || !aligned16(y32)) return MOE_ERR_ARG;
+  const moe_status st = fused_check(p, ws, x, w, y_addend, y);
+  if (st != MOE_OK) return st;
+  return fused_forward(p, ws, x, scores, w, y32, y_addend, y, scratch, s);
+}
+
 moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
                           const float* scores, const void* dy, const moe_weights* w,
                           const void* h3, void* arena, void* scratch, const moe_grads* g,
@@ -749,6 +782,13 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   float* dxr = reinterpret_cast<float*>(sc + p->sl.dxr);
   const int dw_f32 = d.dw_dtype == MOE_DTYPE_F32;
   hipError_t e;
+  // A layer whose forward did not run since its routing is reported and
+  // rebuilt from x like a replaying layer.
+  {
+    const PlanArgs pa = plan_args(p, layer, 1, arena, sc);
+    e = timed(p, "plan_bwd", s, [&] { return launch_plan_enter_bwd(hdr, pa, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   // Replay (device predicate): rebuild h1 in scratch from x when the forward
   // did not save it.
   if (mx) return mx_backward(p, hdr, ws, sc, x, w, scores, dy, h3, arena, g, flags, cus, s);

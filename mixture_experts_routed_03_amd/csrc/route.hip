@@ -416,6 +416,26 @@ __global__ void k_plan_decide(RouteHdr* __restrict__ hdr, PlanArgs a) {
   ah->cursor = cursor + rec.bytes;
 }
 
+// First launch of a backward.  If no forward of this layer ran since its
+// routing (rec.done == 0), the record's pointers are not this call's: report
+// it (MOE_STATUS_ARENA) and turn the layer into a replaying one, so that the
+// backward rebuilds its forward state from x in scratch, as for a layer the
+// planner chose to replay, instead of reading through stale pointers.
+__global__ void k_plan_enter_bwd(RouteHdr* __restrict__ hdr, PlanArgs a) {
+  if (threadIdx.x != 0) return;
+  LayerRec& rec = hdr->rec;
+  if (rec.done) return;
+  hdr->status |= MOE_STATUS_ARENA;
+  rec.start = a.arena ? reinterpret_cast<ArenaHdr*>(a.arena)->cursor : 0;
+  rec.bytes = 0;
+  rec.replay = 1;
+  rec.layer = a.layer;
+  rec.x_rows = 0;
+  rec.h1 = a.scratch_h1;
+  for (int i = 0; i < 4; ++i) rec.aux[i] = a.scratch_aux[i];
+  rec.done = 1;
+}
+
 // Backward rewinds the cursor to the layer's start (reverse layer order).
 __global__ void k_plan_rewind(RouteHdr* __restrict__ hdr, uint64_t arena) {
   if (threadIdx.x != 0) return;
@@ -467,6 +487,11 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
 
 hipError_t launch_plan_decide(RouteHdr* hdr, const PlanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_plan_decide, dim3(1), dim3(64), 0, s, hdr, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_enter_bwd(RouteHdr* hdr, const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_plan_enter_bwd, dim3(1), dim3(64), 0, s, hdr, a);
   return hipGetLastError();
 }
 
