@@ -85,6 +85,14 @@ class RegenExperts:
                                experts=[int(e)])[0].cpu()
 
 
+def full_size_tokens(T, n=32, seed=0):
+    """n distinct tokens of a T-token call: the first, the last and n - 2
+    drawn uniformly without replacement from the rest (seeded)."""
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, T - 1), size=min(n, T) - 2, replace=False)
+    return sorted({0, T - 1, *[int(t) for t in mid]})
+
+
 def sampled_forward_ref(lay, tokens, mx=False):
     """Oracle Y for selected tokens only, one expert's weights at a time."""
     from oracle import mx as omx
@@ -99,6 +107,8 @@ def sampled_forward_ref(lay, tokens, mx=False):
             e = int(ids[t, k])
             if 0 <= e < E:
                 by_e.setdefault(e, []).append((t, k))
+    if "_wcache" in lay:
+        prefetch_expert_weights(lay, list(by_e), mx)
     for e, lst in sorted(by_e.items()):
         w13, w2 = _expert_weights(lay, e, mx)
         xr = om.as_f64(X[[t for t, _ in lst]])
@@ -154,6 +164,8 @@ def sampled_backward_ref(lay, tokens, experts, mx=False):
     for e in experts:
         for t, k in zip(*np.nonzero(ids == e)):
             work.setdefault(int(e), set()).add((int(t), int(k)))
+    if "_wcache" in lay:
+        prefetch_expert_weights(lay, list(work), mx)
     for e, routes in sorted(work.items()):
         routes = sorted(routes, key=lambda tk: tk[0] * ids.shape[1] + tk[1])
         w13, w2 = _expert_weights(lay, e, mx)
@@ -173,3 +185,118 @@ def sampled_backward_ref(lay, tokens, experts, mx=False):
                 ds[t][k] = float(h3[i] @ dyr[i])
     return (np.stack([dx[t] for t in tokens]), np.stack([ds[t] for t in tokens]),
             np.stack([dw13[e] for e in experts]), np.stack([dw2[e] for e in experts]))
+
+
+# ----------------------------------------------------------- designed MX scales
+# Gaussian weights give almost every 32x32 block the same E8M0 exponent, so a
+# kernel that reads the wrong block's scale would still look right.  These
+# helpers multiply each block by a power of two that depends on the block's
+# position (and the expert), non-symmetrically in the two block indices, so
+# every scale read meets several distinct exponents in both orientations.
+
+def block_exponents(n_blocks, k_blocks, e=0):
+    """Exponent of the (bn, bk) 32x32 block of expert e: (3 bn + 5 bk + e) mod 7 - 3."""
+    bn = np.arange(n_blocks)[:, None]
+    bk = np.arange(k_blocks)[None, :]
+    return (3 * bn + 5 * bk + e) % 7 - 3
+
+
+def _pow2_blocks(n, k, e, device):
+    ex = block_exponents(n // 32, k // 32, e)
+    f = np.repeat(np.repeat(np.ldexp(1.0, ex), 32, 0), 32, 1)
+    return torch.from_numpy(f.astype(np.float32)).to(device)
+
+
+def apply_designed_scales(lay, row_jitter=False):
+    """In place: weights scaled per 32x32 block (pattern above, offset by the
+    expert and by 1 for W2), x and dY scaled per 32 columns and per run of 48
+    tokens.  row_jitter: also scale weight row n by 2^((n mod 3) - 1), so
+    weights quantized in 1x32 blocks get a different exponent in neighbouring
+    rows.  All factors are powers of two, so bf16 values stay exact."""
+    w13, w2 = lay["w13"], lay["w2"]
+    E, N13, D = w13.shape
+    F = w2.shape[2]
+    dev = w13.device
+
+    def jit(n):
+        v = np.ldexp(1.0, np.arange(n) % 3 - 1) if row_jitter else np.ones(n)
+        return torch.from_numpy(v.astype(np.float32)).to(dev)[:, None]
+
+    for e in range(E):
+        w13[e] = (w13[e].float() * _pow2_blocks(N13, D, e, dev) * jit(N13)).to(w13.dtype)
+        w2[e] = (w2[e].float() * _pow2_blocks(D, F, e + 1, dev) * jit(D)).to(w2.dtype)
+
+    def rows_cols(t, a, b):
+        T, n = t.shape
+        col = np.ldexp(1.0, (a * (np.arange(n) // 32)) % 5 - 2)
+        row = np.ldexp(1.0, (np.arange(T) // 48 + b) % 3 - 1)
+        f = torch.from_numpy((row[:, None] * col[None, :]).astype(np.float32)).to(t.device)
+        return (t.float() * f).to(t.dtype)
+
+    lay["x"] = rows_cols(lay["x"], 3, 0)
+    if "dy" in lay:
+        lay["dy"] = rows_cols(lay["dy"], 2, 1)
+    return lay
+
+
+def distinct_block_exponents(w, rows=32, cols=32):
+    """Distinct E8M0 exponents (oracle rule) over the 32x32 blocks of w [N, K]."""
+    from oracle import mx as omx
+    a = om.as_f64(w)
+    N, K = a.shape
+    b = np.abs(a.reshape(N // rows, rows, K // cols, cols)).max(axis=(1, 3))
+    return set(np.unique(omx.e8m0_exponent(b)).tolist())
+
+
+def blockwise_max_abs_rel(got, ref, rb=32, cb=32):
+    """max over (rb x cb) blocks of max|got - ref| / max|ref| inside the block
+    (blocks whose reference is all zero must match exactly and count 0)."""
+    g = om.as_f64(got)
+    r = np.asarray(ref, dtype=np.float64)
+    if g.ndim == 1:
+        g, r = g[None, :], r[None, :]
+    M, N = r.shape
+    worst = 0.0
+    for i in range(0, M, rb):
+        for j in range(0, N, cb):
+            rr = r[i:i + rb, j:j + cb]
+            d = np.max(np.abs(g[i:i + rb, j:j + cb] - rr))
+            m = np.max(np.abs(rr))
+            if m == 0.0:
+                assert d == 0.0
+                continue
+            worst = max(worst, d / m)
+    return worst
+
+
+def report(name, **errs):
+    """Print achieved errors next to the bound they are checked against."""
+    parts = ", ".join(f"{k}={v:.2e}" for k, v in errs.items())
+    print(f"[err] {name}: {parts}", flush=True)
+
+
+def prefetch_expert_weights(lay, experts, mx, workers=None):
+    """Fill lay["_wcache"] for ``experts`` using a thread pool (NumPy's
+    element-wise passes release the GIL, so the 32x32 dequantization of
+    full-size expert weights runs in parallel)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    cache = lay.setdefault("_wcache", {})
+    todo = [int(e) for e in sorted(set(experts)) if (int(e), mx) not in cache]
+    if not todo:
+        return
+    n = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    # copy each expert's weights to the host first (one device sync per tensor)
+    host = {e: (lay["w13"][e].cpu(), lay["w2"][e].cpu()) for e in todo}
+
+    def one(e):
+        from oracle import mx as omx
+        w13 = om.as_f64(host[e][0])
+        w2 = om.as_f64(host[e][1])
+        if mx:
+            w13, w2 = omx.qdq_32x32(w13), omx.qdq_32x32(w2)
+        return e, (w13, w2)
+
+    with ThreadPoolExecutor(n) as ex:
+        for e, w in ex.map(one, todo):
+            cache[(e, mx)] = w

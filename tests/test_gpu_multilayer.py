@@ -11,7 +11,7 @@ from mixture_experts_routed_03_amd import workloads as wl
 from oracle import moe as om
 from oracle import mx as omx
 from oracle import planner
-from tests._harness import (TOL, RegenExperts, banner, sampled_backward_ref,
+from tests._harness import (TOL, RegenExperts, banner, report, sampled_backward_ref,
                             sampled_forward_ref)
 
 pytestmark = pytest.mark.gpu
@@ -163,14 +163,24 @@ def test_full_size_ten_layer_mxfp8_step_sampled(B):
         torch.cuda.synchronize()
         ref = dict(lay, w13=RegenExperts(cfg, l, "w13"), w2=RegenExperts(cfg, l, "w2"),
                    _wcache={})
-        t = [int(np.flatnonzero((ids[l] >= 0).all(axis=1))[(37 * l) % 100])]
+        full = np.flatnonzero((ids[l] >= 0).all(axis=1))
+        t = sorted({int(full[(37 * l + 101 * j) % len(full)]) for j in range(4)})
         tol = TOL["mxfp8"]
-        assert om.max_abs_rel(ys[l][t], sampled_forward_ref(ref, t, mx=True)) < tol, l
+        # the coldest expert of the first sampled token, and on the skewed
+        # layers (Zipf 1.0 and 1.4) the hottest expert of the layer, whose
+        # weight gradients contract over thousands of rows in multi-tile items
         experts = [int(min(ids[l][t[0]], key=lambda e: rt["counts"][e]))]
+        if cfg.zipf_for(l) in (1.0, 1.4):
+            experts.append(int(np.argmax(rt["counts"])))
         rdx, rds, rdw13, rdw2 = sampled_backward_ref(ref, t, experts, mx=True)
-        assert om.max_abs_rel(dx[t], rdx) < tol, l
-        assert om.max_abs_rel(ds[t], rds) < tol, l
-        assert om.max_abs_rel(dw13[experts[0]], rdw13[0]) < tol, l
-        assert om.max_abs_rel(dw2[experts[0]], rdw2[0]) < tol, l
+        errs = dict(y=om.max_abs_rel(ys[l][t], sampled_forward_ref(ref, t, mx=True)),
+                    dx=om.max_abs_rel(dx[t], rdx), ds=om.max_abs_rel(ds[t], rds))
+        for i, e in enumerate(experts):
+            errs[f"dw13[{e}]"] = om.max_abs_rel(dw13[e], rdw13[i])
+            errs[f"dw2[{e}]"] = om.max_abs_rel(dw2[e], rdw2[i])
+        report(f"ten-layer layer {l} zipf={cfg.zipf_for(l)}, tokens {t}, experts "
+               f"{[(e, int(rt['counts'][e])) for e in experts]} (bound 6e-2)", **errs)
+        for k, v in errs.items():
+            assert v < tol, (l, k)
         for v in (ys[l], dx, ds):
             assert torch.isfinite(v.float()).all()

@@ -8,8 +8,8 @@ import torch
 from mixture_experts_routed_03_amd import workloads as wl
 from oracle import moe as om
 from oracle import mx as omx
-from tests._harness import (TOL, banner, make_inputs, run_forward, run_train,
-                            sampled_backward_ref, sampled_forward_ref)
+from tests._harness import (TOL, banner, full_size_tokens, make_inputs, report, run_forward,
+                            run_train, sampled_backward_ref, sampled_forward_ref)
 
 pytestmark = pytest.mark.gpu
 
@@ -166,20 +166,23 @@ def test_full_size_mxfp8_train_with_shared_expert_sampled(B):
     shared.backward(lay["x"], sh_sc, lay["dy"], lay["w13_shared"], lay["w2_shared"], dx, dws13,
                     dws2, None, flags=B.BWD_ACCUMULATE_DX)
     torch.cuda.synchronize()
-    tokens = [0, 3, 999, 2047]
+    tokens = full_size_tokens(T, seed=4)
+    lay["_wcache"] = {}
     sh = om.as_f64(lay["w13_shared"][0]), om.as_f64(lay["w2_shared"][0])
     xs = om.as_f64(lay["x"][tokens])
     h1s, _, h3s = om.expert_ffn(xs, *sh)
     ref_y = sampled_forward_ref(lay, tokens, mx=True) + h3s
-    assert om.max_abs_rel(y[tokens], ref_y) < TOL["mxfp8"]
     counts = np.bincount(lay["ids"].cpu().numpy().reshape(-1), minlength=E)
     experts = [int(np.argmax(counts)), int(np.argmin(counts)), 17, 200]
     rdx, rds, rdw13, rdw2 = sampled_backward_ref(lay, tokens, experts, mx=True)
     dxs, _, _, _ = om.expert_ffn_backward(xs, *sh, h1s, om.as_f64(lay["dy"][tokens]))
-    assert om.max_abs_rel(dx[tokens], rdx + dxs) < TOL["mxfp8"]
-    assert om.max_abs_rel(ds[tokens], rds) < TOL["mxfp8"]
+    errs = dict(y=om.max_abs_rel(y[tokens], ref_y), dx=om.max_abs_rel(dx[tokens], rdx + dxs),
+                ds=om.max_abs_rel(ds[tokens], rds))
     for i, e in enumerate(experts):
-        assert om.max_abs_rel(dw13[e], rdw13[i]) < TOL["mxfp8"], e
-        assert om.max_abs_rel(dw2[e], rdw2[i]) < TOL["mxfp8"], e
+        errs[f"dw13[{e}]"] = om.max_abs_rel(dw13[e], rdw13[i])
+        errs[f"dw2[{e}]"] = om.max_abs_rel(dw2[e], rdw2[i])
+    report(f"full-size mxfp8 + shared, {len(tokens)} tokens (bound 6e-2)", **errs)
+    for k, v in errs.items():
+        assert v < TOL["mxfp8"], k
     for t in (y, dx, dw13, dw2, ds):
         assert torch.isfinite(t.float()).all()
