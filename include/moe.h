@@ -284,6 +284,24 @@ moe_status moe_expert_fwd_fused(moe_plan_t plan, void* route_ws, const void* x,
                                 const float* scores, const moe_weights* w, float* y32,
                                 const void* y_addend, void* y, void* scratch, hipStream_t stream);
 
+/* Allocation-free variant of moe_expert_fwd_fused, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and results minus
+ * y32 and scratch: the fused forward's scratch and its fp32 accumulation
+ * rows live in a 64 MiB array inside the library, one per GPU, held until the
+ * process ends.  The plan must fit it: moe_plan_sizes(plan).scratch and
+ * t_max * D * 4 bytes of fp32 rows, each rounded up to 256 bytes, at most
+ * 64 MiB together (else MOE_ERR_WORKSPACE, before anything is enqueued; for
+ * example the BF16 layer at D = 7,168, F = 2,048, K = 6 fits up to t_max =
+ * 655 tokens).  Every call on one GPU shares that array and it keeps the
+ * last call's contents (this call clears what must start at zero), so calls
+ * that overlap on one GPU - on two streams, or from two threads - race; keep
+ * them ordered on one stream.  No hipMalloc, hipFree or allocating library
+ * call is made. */
+moe_status moe_expert_fwd_fused_noalloc(moe_plan_t plan, void* route_ws, const void* x,
+                                        const float* scores, const moe_weights* w,
+                                        const void* y_addend, void* y, hipStream_t stream);
+
 /* Backward of one layer (blog section 2 SwiGLU backward, section 5): from
  * dy [T,D] computes dscores, W2 DGRAD with the SwiGLU backward epilogue,
  * W2 and W13 WGRAD, W13 DGRAD and the per-token sum of the K route input

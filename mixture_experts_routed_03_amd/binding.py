@@ -74,6 +74,7 @@ _SIGS = {
     "moe_expert_fwd": [_P, ctypes.c_int32, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P, _P],
     "moe_combine": [_P, _P, _P, _P, _P, _P, _P],
     "moe_expert_fwd_fused": [_P, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P, _P, _P],
+    "moe_expert_fwd_fused_noalloc": [_P, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P],
     "moe_expert_bwd": [_P, ctypes.c_int32, _P, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P,
                        _P, ctypes.POINTER(moe_grads), ctypes.c_uint32, _P],
     "moe_read_status": [_P, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32), _P],
@@ -188,6 +189,13 @@ def moe_expert_fwd_fused(plan, route_ws, x, scores, weights, y32, y_addend, y, s
     _check(lib().moe_expert_fwd_fused(plan, _ptr(route_ws), _ptr(x), _ptr(scores),
                                       ctypes.byref(w), _ptr(y32), _ptr(y_addend), _ptr(y),
                                       _ptr(scratch), _stream(stream)), "moe_expert_fwd_fused")
+
+
+def moe_expert_fwd_fused_noalloc(plan, route_ws, x, scores, weights, y_addend, y, stream=None):
+    w = _weights(*weights)
+    _check(lib().moe_expert_fwd_fused_noalloc(plan, _ptr(route_ws), _ptr(x), _ptr(scores),
+                                              ctypes.byref(w), _ptr(y_addend), _ptr(y),
+                                              _stream(stream)), "moe_expert_fwd_fused_noalloc")
 
 
 def moe_expert_bwd(plan, layer, route_ws, x, scores, dy, weights, h3_slots, arena, scratch,

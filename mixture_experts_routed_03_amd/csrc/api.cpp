@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <utility>
@@ -910,6 +911,10 @@ moe_status moe_timing_enable(moe_plan_t p, int32_t enable) {
   return MOE_OK;
 }
 
+moe_status moe_expert_fwd_fused_noalloc(moe_plan_t p, void* ws, const void* x,
+                                        const float* scores, const moe_weights* w,
+                                        const void* y_addend, void* y, hipStream_t s);
+
 moe_status moe_timing_flush(moe_plan_t p, void* buf, size_t bytes) {
   if (!p || (buf && (!aligned16(buf) || bytes < 16))) return MOE_ERR_ARG;
   p->flush_buf = buf;
@@ -945,3 +950,62 @@ moe_status moe_timing_read(moe_plan_t p, int32_t idx, char* name, size_t cap, do
 }
 
 }  // extern "C"
+
+// ------------------------------------------------- allocation-free inference
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid hipMalloc):
+// moe_expert_fwd_fused_noalloc keeps the fused forward's scratch and its fp32
+// accumulation rows in this array instead of caller buffers.  Each GPU the
+// library runs on holds its own copy until the process ends, and every call
+// on that GPU shares it: calls that overlap on one GPU race.  In host code
+// the name `scratch` is only a host-side stand-in; the device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+namespace {
+
+constexpr size_t kNoAllocBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+// This GPU's copy of `scratch` (the device of stream s; the current device
+// for the null stream), looked up with that device current.
+moe_status noalloc_base(hipStream_t s, char** out) {
+  int dev = -1;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 ||
+      dev >= kMaxDevices)
+    return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MOE_ERR_HIP;
+    if (e != hipSuccess || !ptr) return MOE_ERR_HIP;
+    g_noalloc_ptr[dev] = ptr;
+  }
+  *out = reinterpret_cast<char*>(g_noalloc_ptr[dev]);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_expert_fwd_fused_noalloc(moe_plan_t p, void* ws, const void* x,
+                                                   const float* scores, const moe_weights* w,
+                                                   const void* y_addend, void* y,
+                                                   hipStream_t s) {
+  moe_status st = fused_check(p, ws, x, w, y_addend, y);
+  if (st != MOE_OK) return st;
+  // scratch layout of the plan, then the fp32 rows [t_max, D]
+  const int64_t sc_bytes = a256(p->sl.total);
+  const int64_t y32_bytes = a256(p->d.t_max * p->d.d * 4);
+  if (sc_bytes + y32_bytes > int64_t(kNoAllocBytes)) return MOE_ERR_WORKSPACE;
+  char* base = nullptr;
+  st = noalloc_base(s, &base);
+  if (st != MOE_OK) return st;
+  return fused_forward(p, ws, x, scores, w, reinterpret_cast<float*>(base + sc_bytes), y_addend,
+                       y, base, s);
+}
