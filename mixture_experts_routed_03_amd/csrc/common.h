@@ -327,6 +327,31 @@ __device__ __forceinline__ void acc_store4(uint16_t* p, const float* v) {
   __builtin_nontemporal_store(o, reinterpret_cast<u32x2_*>(p));
 }
 
+// Weight-gradient tile of item i of one expert (NA column tiles x NB row
+// bands of dW; the kernels pass hot only for dW13).  The items an XCD runs at once are consecutive, so their
+// order decides how much operand data they share.  An expert with many rows
+// (hot: its operand rows do not stay in L2 between passes over its tiles)
+// takes blocks of 4 column tiles x 8 row bands: 32 concurrent items read 4
+// column strips of A and 8 row bands of B instead of every column strip of
+// A for one band.  Other experts keep the order that writes dW fastest: the
+// row band fastest (band_fast, dW2) or the column tile fastest (dW13).
+constexpr int kWgBlockA = 4, kWgBlockB = 8;
+__device__ __forceinline__ void wgrad_tile(int i, int NA, int NB, bool hot, bool band_fast,
+                                           int& ta, int& tb) {
+  if (hot && NA % kWgBlockA == 0 && NB % kWgBlockB == 0) {
+    const int blk = i / (kWgBlockA * kWgBlockB), wi = i % (kWgBlockA * kWgBlockB);
+    const int nA = NA / kWgBlockA;
+    ta = (blk % nA) * kWgBlockA + wi % kWgBlockA;
+    tb = (blk / nA) * kWgBlockB + wi / kWgBlockA;
+  } else if (band_fast) {
+    tb = i % NB;
+    ta = i / NB;
+  } else {
+    ta = i % NA;
+    tb = i / NA;
+  }
+}
+
 // Number of XCDs of the MI355X; workgroups are dispatched round-robin over them.
 constexpr int kXcds = 8;
 

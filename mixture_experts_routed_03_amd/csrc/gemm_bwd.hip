@@ -44,6 +44,12 @@
 //    128-row band fastest, so the concurrent workgroups write one column
 //    segment of many bands: at F = 2,048 that wrote 5.9 instead of 5.1 TB/s
 //    (column-fastest reached 5.75 TB/s only at the 6 KB pitch of F = 3,072).
+//    In dW13 an expert with 256 or more rows, whose operand rows do not
+//    stay in L2 between passes over its tiles, takes blocks of 4 column
+//    tiles x 8 row bands instead (wgrad_tile), so the items an XCD runs at
+//    once share operand rows: at Zipf(1.2) the launch read 0.72 instead of
+//    2.75 GB, in the same time.  (dW2 keeps its order: blocks there read
+//    0.45 instead of 0.82 GB but wrote 3% slower.)
 //  * Persistent, XCD-aware grids as in the forward kernels.
 #include <algorithm>
 #include <type_traits>
@@ -387,53 +393,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
   struct Item {
     int e, ta, tb, r0, Me, S, ncols;
   };
-  // Work items of this workgroup are w = first + slot + i * per below last;
-  // (e, tb, ta) advance by carries instead of a division per item.
-  int w0 = first + slot;
-  int ie = w0 / per_e;
-  int irem = w0 - ie * per_e;
-  // dW2 (rows of F values: a power-of-two byte pitch at the usual widths)
-  // takes its items with the 128-row band tb fastest, dW13 with the column
-  // tile ta fastest: the order that writes fastest for each (see the loop
-  // below).
-  constexpr bool kBandFast = TAG == 2;
-  int itb = kBandFast ? irem % NB : irem / NA;
-  int ita = kBandFast ? irem / NB : irem - itb * NA;
-  const int wend = last;
-  int wcur = w0;
+  // Work items of this workgroup: w = first + slot + i * per below last.
+  int wcur = first + slot;
   auto fill = [&](Item& t) {
-    if (wcur >= wend) {
+    if (wcur >= last) {
       t.e = -1;
       return;
     }
-    t.e = ie;
-    t.ta = ita;
-    t.tb = itb;
-    t.r0 = a.offsets[ie];
-    t.Me = a.offsets[ie + 1] - t.r0;
-    t.S = (t.Me + 63) / 64;
-    t.ncols = min(256, a_ld - ita * 256);
-    // advance to the next item of this workgroup
+    const int w = wcur;
     wcur += per;
-    if (kBandFast) {
-      itb += per;
-      while (itb >= NB) {
-        itb -= NB;
-        if (++ita == NA) {
-          ita = 0;
-          ++ie;
-        }
-      }
-    } else {
-      ita += per;
-      while (ita >= NA) {
-        ita -= NA;
-        if (++itb == NB) {
-          itb = 0;
-          ++ie;
-        }
-      }
-    }
+    const int e = w / per_e;
+    t.e = e;
+    t.r0 = a.offsets[e];
+    t.Me = a.offsets[e + 1] - t.r0;
+    t.S = (t.Me + 63) / 64;
+    int ta, tb;
+    wgrad_tile(w - e * per_e, NA, NB, TAG == 13 && hot_expert(t.Me), TAG == 2, ta, tb);
+    t.ta = ta;
+    t.tb = tb;
+    t.ncols = min(256, a_ld - ta * 256);
   };
 
   // One stage in registers.  Token rows past the expert's last row are not

@@ -722,50 +722,25 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
   struct Item {
     int e, ta, tb, pb, mp, S, ncols;
   };
-  int w0 = first + slot;
-  int ie = w0 / per_e;
-  int irem = w0 - ie * per_e;
-  // dW2 (rows of F values: a power-of-two byte pitch at the usual widths)
-  // takes its items with the 128-row band tb fastest, dW13 with the column
-  // tile ta fastest: the order that writes fastest for each (see the loop
-  // below).
-  constexpr bool kBandFast = TAG == 2;
-  int itb = kBandFast ? irem % NB : irem / NA;
-  int ita = kBandFast ? irem / NB : irem - itb * NA;
-  const int wend = last;
-  int wcur = w0;
+  // Work items of this workgroup: w = first + slot + i * per below last.
+  int wcur = first + slot;
   auto fill = [&](Item& t) {
-    if (wcur >= wend) {
+    if (wcur >= last) {
       t.e = -1;
       return;
     }
-    t.e = ie;
-    t.ta = ita;
-    t.tb = itb;
-    t.pb = a.poffsets[ie];
-    t.mp = a.poffsets[ie + 1] - t.pb;
-    t.S = (t.mp + 63) / 64;
-    t.ncols = min(256, a_ld - ita * 256);
+    const int w = wcur;
     wcur += per;
-    if (kBandFast) {
-      itb += per;
-      while (itb >= NB) {
-        itb -= NB;
-        if (++ita == NA) {
-          ita = 0;
-          ++ie;
-        }
-      }
-    } else {
-      ita += per;
-      while (ita >= NA) {
-        ita -= NA;
-        if (++itb == NB) {
-          itb = 0;
-          ++ie;
-        }
-      }
-    }
+    const int e = w / per_e;
+    t.e = e;
+    t.pb = a.poffsets[e];
+    t.mp = a.poffsets[e + 1] - t.pb;
+    t.S = (t.mp + 63) / 64;
+    int ta, tb;
+    wgrad_tile(w - e * per_e, NA, NB, TAG == 13 && hot_expert(t.mp), TAG == 2, ta, tb);
+    t.ta = ta;
+    t.tb = tb;
+    t.ncols = min(256, a_ld - ta * 256);
   };
   // A column of the tile, folded into the first half past a 128-column half
   // tile's end (those columns are multiplied but never stored).
