@@ -352,21 +352,26 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ 
     for (int k = 0; k < KM; ++k) valid[k] = k < K && route_to_row[t * K + k] >= 0;
     const float4* src = dxr + t * K * q4;
     T* o = dx + t * D;
-    for (int64_t i = threadIdx.x; i < q4; i += 256) {
-      float4 v[KM];
+    // two chunks per thread per step, so 2K loads are in flight; the slot
+    // rows are read exactly once, so the loads do not allocate in L2
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const f32x4_t* src4 = reinterpret_cast<const f32x4_t*>(src);
+    auto sum = [&](int64_t i) {
+      f32x4_t v[KM];
 #pragma unroll
       for (int k = 0; k < KM; ++k)
-        if (k < K) v[k] = src[k * q4 + i];   // a padding slot is read but not added
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (k < K) v[k] = __builtin_nontemporal_load(src4 + k * q4 + i);   // padding read, not added
+      return [=](float* acc) {
 #pragma unroll
-      for (int k = 0; k < KM; ++k) {
-        if (valid[k]) {
-          acc[0] += v[k].x;
-          acc[1] += v[k].y;
-          acc[2] += v[k].z;
-          acc[3] += v[k].w;
+        for (int k = 0; k < KM; ++k) {
+          if (valid[k]) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] += v[k][j];
+          }
         }
-      }
+      };
+    };
+    auto finish = [&](int64_t i, float* acc) {
       if (accumulate) {
         float f[4];
         load4<T>(o + 4 * i, f);
@@ -374,6 +379,21 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const RouteHdr* __restrict__ 
         for (int j = 0; j < 4; ++j) acc[j] += f[j];
       }
       put4<T>(o + 4 * i, acc);
+    };
+    int64_t i = threadIdx.x;
+    for (; i + 256 < q4; i += 512) {
+      const auto a0 = sum(i);
+      const auto a1 = sum(i + 256);
+      float acc0[4] = {0.f, 0.f, 0.f, 0.f}, acc1[4] = {0.f, 0.f, 0.f, 0.f};
+      a0(acc0);
+      a1(acc1);
+      finish(i, acc0);
+      finish(i + 256, acc1);
+    }
+    if (i < q4) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      sum(i)(acc);
+      finish(i, acc);
     }
   }
 }

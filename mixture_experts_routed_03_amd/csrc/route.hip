@@ -9,8 +9,10 @@
 // built on the GPU - which is what happens here, with no host sync.
 // Dist-MoE explainer section 01: id -1 disables a route.
 //
-// Deterministic counting sort in three launches (one for small calls, see
-// k_route_small):
+// Deterministic counting sort.  Up to 1,024 routes (decode): one workgroup
+// of one launch (k_route_small); up to 32,768 routes: one launch of one
+// workgroup per 256-route chunk that needs nothing from the others
+// (k_route_chunked); larger calls, three launches:
 //   hist : one workgroup per chunk of 256 routes, LDS atomics -> chunk_hist[c][e]
 //   scan : one workgroup; counts[e] = sum_c chunk_hist[c][e], exclusive scans
 //          of counts, of counts rounded up to 32 and of m-tiles; the chunk
@@ -74,15 +76,13 @@ __device__ void block_scan(int* v /* [N] */, int* sh /* [N][16] */) {
   __syncthreads();
 }
 
-// Column sums of the chunk histograms and their rewrite into row bases: with
-// at most kScanRegs chunks an expert's column is loaded into registers in one
-// round trip and rewritten from them; larger calls read 16 chunks at a time
-// per expert, twice (independent loads; threads of consecutive experts read
-// consecutive words).  Experts are handled in passes of 1024,
+// Column sums of the chunk histograms and their rewrite into row bases
+// (calls above kChunkedRoutes routes): each thread reads its expert's column
+// 16 chunks at a time, twice (independent loads; threads of consecutive
+// experts read consecutive words).  Experts are handled in passes of 1024,
 // expert e = 1024 * pass + thread, with the running totals carried between
 // passes.
 constexpr int kScanBatch = 16;
-constexpr int kScanRegs = 64;
 
 // The per-expert terms whose exclusive prefixes routing writes, for an
 // expert with s rows: rows (offsets), rows rounded up to 32 (poffsets),
@@ -121,21 +121,11 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   int f = 0;
   for (int c = tid; c < nchunks; c += 1024) f |= chunk_flags[c];
   __syncthreads();
-  // up to kScanRegs chunks (16,384 routes): an expert's whole column is loaded
-  // into registers at once, read once and rewritten from the registers
-  const bool regs = nchunks <= kScanRegs;
   int mx = 0;
   for (int e0 = 0; e0 < E; e0 += 1024) {
     const int e = e0 + tid;
     int s = 0;
-    int col[kScanRegs];
-    if (e < E && regs) {
-#pragma unroll
-      for (int j = 0; j < kScanRegs; ++j)
-        col[j] = j < nchunks ? chunk_hist[int64_t(j) * E + e] : 0;
-#pragma unroll
-      for (int j = 0; j < kScanRegs; ++j) s += col[j];
-    } else if (e < E) {
+    if (e < E) {
       for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
         int v[kScanBatch];
 #pragma unroll
@@ -167,16 +157,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
       for (int j = 0; j < 3; ++j) split[j * (E + 1) + e] = o[4 + j];
       // chunk histograms -> row base of each (chunk, expert)
       int run = oc;
-      if (regs) {
-#pragma unroll
-        for (int j = 0; j < kScanRegs; ++j) {
-          if (j < nchunks) {
-            chunk_hist[int64_t(j) * E + e] = run;
-            run += col[j];
-          }
-        }
-      }
-      for (int c0 = 0; !regs && c0 < nchunks; c0 += kScanBatch) {
+      for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
         int v[kScanBatch];
 #pragma unroll
         for (int j = 0; j < kScanBatch; ++j)
@@ -351,6 +332,176 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
   if (tid < 2 * kXcds) hdr->wq[tid] = 0u;
 }
 
+// Inclusive scan of N ints per thread over a 256-thread block (4 waves).
+template <int N>
+__device__ void block_scan256(int* v /* [N] */, int* sh /* [N][4] */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int u[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) u[j] = __shfl_up(v[j], off, 64);
+    if (lane >= off) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[j] += u[j];
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) sh[4 * j + wave] = v[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    if (w < wave) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[j] += sh[4 * j + w];
+    }
+  }
+  __syncthreads();
+}
+
+// Calls of kSmallRoutes + 1 .. kChunkedRoutes routes (training and prefill
+// steps): the whole counting sort in one launch, one 256-thread workgroup
+// per 256-route chunk, with no communication between workgroups.  Every
+// workgroup reads all the ids (at most 128 KiB; after the first workgroup
+// they come from L2) and counts in LDS, with integer atomics (exact in any
+// order), each expert's routes in all chunks and in the chunks before its
+// own.  It then scans the per-expert terms itself (each thread a run of
+// consecutive experts) and ranks its own chunk's routes as k_route_rank
+// does; workgroup 0 publishes counts, prefixes and the header.  Same
+// outputs as the three-launch path, which stays for larger calls (each
+// workgroup's read of every id would grow with the square of the call).
+constexpr int kChunkedRoutes = 32768;
+
+__global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict__ ids, int n,
+                                                       int E, int T,
+                                                       int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ poffsets,
+                                                       int32_t* __restrict__ mtoff,
+                                                       int32_t* __restrict__ gtoff,
+                                                       int32_t* __restrict__ split,
+                                                       int32_t* __restrict__ sorted_route,
+                                                       int32_t* __restrict__ route_to_row,
+                                                       RouteHdr* __restrict__ hdr) {
+  extern __shared__ int32_t cnt[];   // [E] routes per expert, then [E] routes before this chunk
+  int32_t* tot = cnt;
+  int32_t* pre = cnt + E;
+  __shared__ int32_t sid[kRankChunk];
+  __shared__ int sh[4 * kScans];
+  __shared__ int s_mx;
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kRankChunk) {
+    tot[e] = 0;
+    pre[e] = 0;
+  }
+  if (tid == 0) s_mx = 0;
+  __syncthreads();
+  const int mine = c * kRankChunk + tid;   // this thread's route of the chunk
+  const int before = c * kRankChunk;       // routes of the earlier chunks
+  int my_id = -1, bad = 0;
+  constexpr int kBatch = 8;                // independent loads in flight per thread
+  for (int r0 = 0; r0 < n; r0 += kRankChunk * kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int r = r0 + kRankChunk * k + tid;
+      v[k] = r < n ? ids[r] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int r = r0 + kRankChunk * k + tid;
+      const int id = v[k];
+      const bool valid = id >= 0 && id < E;
+      if (id < -1 || id >= E) bad = 1;
+      if (valid) {
+        atomicAdd(&tot[id], 1);
+        if (r < before) atomicAdd(&pre[id], 1);
+      }
+      if (r == mine) my_id = valid ? id : -1;
+    }
+  }
+  bad = __syncthreads_or(bad);   // also: every count is in
+
+  // exclusive prefixes over experts; thread t owns experts [t ept, t ept + ept)
+  const int ept = (E + kRankChunk - 1) / kRankChunk;
+  const int e0 = tid * ept;
+  int own[kScans] = {}, mx = 0;
+  for (int i = 0; i < ept; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      int v[kScans];
+      scan_terms(tot[e], v);
+#pragma unroll
+      for (int j = 0; j < kScans; ++j) own[j] += v[j];
+      mx = max(mx, tot[e]);
+    }
+  }
+  int run[kScans];
+#pragma unroll
+  for (int j = 0; j < kScans; ++j) run[j] = own[j];
+  block_scan256<kScans>(run, sh);   // inclusive
+#pragma unroll
+  for (int j = 0; j < kScans; ++j) run[j] -= own[j];
+  for (int i = 0; i < ept; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int s = tot[e];
+      if (c == 0) {
+        counts[e] = s;
+        offsets[e] = run[0];
+        poffsets[e] = run[1];
+        mtoff[e] = run[2];
+        gtoff[e] = run[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) split[j * (E + 1) + e] = run[4 + j];
+      }
+      pre[e] += run[0];   // this chunk's first row of expert e
+      int v[kScans];
+      scan_terms(s, v);
+#pragma unroll
+      for (int j = 0; j < kScans; ++j) run[j] += v[j];
+    }
+  }
+  atomicMax(&s_mx, mx);
+  sid[tid] = mine < n ? my_id : -1;
+  __syncthreads();
+  if (mine < n) {
+    if (my_id < 0) {
+      route_to_row[mine] = -1;
+    } else {
+      // earlier routes of the same expert in this chunk (every lane reads the
+      // same LDS word per step)
+      int rank = 0;
+      for (int q = 0; q < tid; ++q) rank += (sid[q] == my_id);
+      const int row = pre[my_id] + rank;
+      sorted_route[row] = mine;
+      route_to_row[mine] = row;
+    }
+  }
+  if (c == 0) {
+    // the last thread's running prefixes are the totals
+    if (tid == kRankChunk - 1) {
+      offsets[E] = run[0];
+      poffsets[E] = run[1];
+      mtoff[E] = run[2];
+      gtoff[E] = run[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) split[j * (E + 1) + E] = run[4 + j];
+      hdr->T = T;
+      hdr->R = run[0];
+      hdr->Rpad = run[1];
+      hdr->n_mt = run[2];
+      hdr->status = bad ? uint32_t(MOE_STATUS_BAD_ID) : 0u;
+      hdr->max_count = s_mx;
+      hdr->rec.done = 0;
+    }
+    if (tid < 2 * kXcds) hdr->wq[tid] = 0u;
+  }
+}
+
 // ------------------------------------------------------------ planner
 // Dist-MoE explainer section 04: before saving a layer's full state the
 // planner replays instead when saved bytes + this layer's full state +
@@ -465,6 +616,20 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
     return hipGetLastError();
   }
   const int nchunks = int((n + kRankChunk - 1) / kRankChunk);
+  if (n <= kChunkedRoutes) {
+    hipLaunchKernelGGL(k_route_chunked, dim3(nchunks), dim3(kRankChunk), 2 * E * sizeof(int32_t),
+                       s, ids, int(n), E, int(T),
+                       reinterpret_cast<int32_t*>(ws + L.counts),
+                       reinterpret_cast<int32_t*>(ws + L.offsets),
+                       reinterpret_cast<int32_t*>(ws + L.poffsets),
+                       reinterpret_cast<int32_t*>(ws + L.mtoff),
+                       reinterpret_cast<int32_t*>(ws + L.gtoff),
+                       reinterpret_cast<int32_t*>(ws + L.cstoff),
+                       reinterpret_cast<int32_t*>(ws + L.sorted_route),
+                       reinterpret_cast<int32_t*>(ws + L.route_to_row),
+                       reinterpret_cast<RouteHdr*>(ws + L.hdr));
+    return hipGetLastError();
+  }
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.chunk_hist);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.chunk_flags);
   if (nchunks > 0)
