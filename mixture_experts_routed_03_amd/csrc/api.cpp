@@ -64,6 +64,7 @@ struct moe_plan_s {
   int64_t Rp_max;         // upper bound on rows padded to 32 per expert
   int64_t mt_max;         // upper bound on m-tiles
   bool hot;               // BF16 forward: hot experts on the 256 x 256 MFMA tiles
+  int ks13, ks2;          // forward split-K factors of the W13 and W2 GEMMs (1: none)
   RouteLayout rl;
   ScratchLayout sl;
   int64_t h3_bytes;
@@ -166,6 +167,13 @@ static void use_hot(moe_plan_s* p, void* ws, FwdArgs& a, int mode /* 0: W13, 1: 
   a.hotoff = at<int32_t>(ws, p->rl.hotoff);
 }
 
+
+// Split-K arguments of a BF16/FP32 forward GEMM launch (mode 0: W13, 1: W2).
+static void set_split(const moe_plan_s* p, FwdArgs& a, int mode, char* sc) {
+  a.ksplit = mode == 0 ? p->ks13 : p->ks2;
+  a.part = a.ksplit > 1 ? reinterpret_cast<float*>(sc + p->sl.part) : nullptr;
+  a.part_rows = p->R_max;
+}
 
 // MXFP8 forward up to h2 (after the gather): x rows -> 1x32 blocks (and the x
 // column bundle in training), the W13 grouped GEMM with the SwiGLU epilogue,
@@ -350,6 +358,38 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es, Rp = p->Rp_max;
   const bool mx = d.prec == MOE_PREC_MXFP8;
   const bool fp4 = d.prec == MOE_PREC_MXFP4;   // inference only: no column bundles
+  {
+    // Split-K of the BF16/FP32 forward GEMMs ("Mixture of Experts: How
+    // Routing Becomes GPU Computation", section 6): considered when even the
+    // plan's upper bound on work items (m-tiles x n-tiles) gives the 256 CUs
+    // of gfx950 fewer than two items each, which is decode (a handful of
+    // rows, one per expert).  The streaming kernel keeps two workgroups per
+    // CU, so 512 items run at once: the factor (1..8, at least 4 stages of
+    // 128 bytes per part) is the one whose item count fills its last round
+    // of 512 best, the smaller on ties within 2% (at one token and the
+    // 7168 x 2048 layer: W13 192 items x 8 = 3 full rounds, W2 336 x 3 =
+    // 1,008 of 1,024).  A plan that may put experts on the hot-expert tiles
+    // does not split.
+    const bool may_hot = p->hot && (d.hot_tiles == 1 || 4 * (R / kBMH) * (F / 128) >= 3 * 256 ||
+                                    4 * (R / kBMH) * (D / 256) >= 3 * 256);
+    auto factor = [&](int64_t items, int64_t stages) {
+      constexpr int64_t kSlots = 2 * 256;
+      if (mx || fp4 || may_hot || items >= kSlots || items == 0) return 1;
+      int best = 1;
+      double best_fill = 0.0;
+      for (int ks = 1; ks <= 8 && stages / ks >= 4; ++ks) {
+        const int64_t n = items * ks;
+        const double fill = double(n) / double((n + kSlots - 1) / kSlots * kSlots);
+        if (fill > best_fill + 0.02) {
+          best = ks;
+          best_fill = fill;
+        }
+      }
+      return best;
+    };
+    p->ks13 = factor(p->mt_max * (F / 64), D * es / 128);
+    p->ks2 = factor(p->mt_max * (D / 128), F * es / 128);
+  }
 
   RouteLayout& L = p->rl;
   L.nchunks = (R + kRankChunk - 1) / kRankChunk;
@@ -383,6 +423,8 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   };
   take(S.h1, R * 2 * F * es);
   take(S.h2, R * F * es);
+  if (p->ks13 > 1 || p->ks2 > 1)
+    take(S.part, std::max<int64_t>(p->ks13 * R * 2 * F, p->ks2 * R * D) * 4);
   if (mx) {
     take(S.qx, R * D);
     take(S.sx, R * D / 32);
@@ -473,6 +515,12 @@ moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
   std::snprintf(line, sizeof line, "  routed rows R <= %lld, m-tiles <= %lld (%d rows each)\n",
                 (long long)p->R_max, (long long)p->mt_max, kBM);
   s += line;
+  if (p->ks13 > 1 || p->ks2 > 1) {
+    std::snprintf(line, sizeof line,
+                  "  forward split-K: W13 x%d, W2 x%d (fp32 partial tiles, ordered second pass)\n",
+                  p->ks13, p->ks2);
+    s += line;
+  }
   if (d.prec == MOE_PREC_BF16) {
     static const char* kHot[] = {"automatic", "always", "never"};
     std::snprintf(line, sizeof line,
@@ -613,6 +661,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     a13.stoff = mtoff;
+    set_split(p, a13, 0, sc);
     use_hot(p, ws, a13, 0);
     a13.limit = swiglu_limit(p);
     e = timed(p, "w13_swiglu", s,
@@ -621,6 +670,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
     FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + L.h2, w->w2, h3, nullptr,
                d.f, d.d, d.f, d.d / 128, d.e, 0};
     a2.stoff = mtoff;
+    set_split(p, a2, 1, sc);
     use_hot(p, ws, a2, 1);
     return hip_status(timed(p, "w2_scatter", s,
                             [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); }));
@@ -706,6 +756,7 @@ moe_status fused_forward(moe_plan_s* p, void* ws, const void* x, const float* sc
     FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + L.h2,
                 d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
     a13.stoff = mtoff;
+    set_split(p, a13, 0, sc);
     use_hot(p, ws, a13, 0);
     a13.limit = swiglu_limit(p);
     e = timed(p, "w13_swiglu", s,
@@ -714,6 +765,7 @@ moe_status fused_forward(moe_plan_s* p, void* ws, const void* x, const float* sc
     FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + L.h2, w->w2, nullptr, nullptr,
                d.f, d.d, d.f, d.d / 128, d.e, 0, nullptr, d.k, scores, y32};
     a2.stoff = mtoff;
+    set_split(p, a2, 1, sc);
     use_hot(p, ws, a2, 1);
     e = timed(p, "w2_fused", s, [&] { return launch_gemm_fwd(d.prec, 1, a2, p->mt_max, cus, s); });
   } else {
@@ -796,6 +848,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
               d.d, 2 * d.f, d.f, d.f / 64, d.e, 1, x, d.k};
   a13.stoff = mtoff;
+  set_split(p, a13, 0, sc);
   use_hot(p, ws, a13, 0);
   a13.limit = swiglu_limit(p);
   e = timed(p, "replay_w13", s, [&] { return launch_gemm_fwd(d.prec, 0, a13, p->mt_max, cus, s); });

@@ -68,6 +68,7 @@ struct RouteHdr {
 };
 static_assert(sizeof(RouteHdr) <= 512, "route header must fit its slot");
 
+
 struct ArenaHdr {
   int64_t cursor;       // next free byte of the data region
   int64_t pad[31];
@@ -91,6 +92,7 @@ struct ScratchLayout {
   // MXFP8: row-quantized operands (codes, exponents) and column bundles
   int64_t qx, sx, qh2, sh2, xcq, xcs, h2cq, h2cs;
   int64_t qdh3, sdh3, dh3cq, dh3cs, qdh1, sdh1, dh1cq, dh1cs;
+  int64_t part;   // split-K partial tiles of the forward GEMMs (plans that split)
   int64_t total;
 };
 
@@ -123,6 +125,14 @@ struct FwdArgs {
   const int32_t* ctoff;
   const int32_t* cstoff;
   const int32_t* hotoff;
+  // Split-K (streaming tiles only; <= 1: none).  Each output tile's stage
+  // loop is cut into ksplit contiguous ranges run as separate items; item k
+  // stores its fp32 partial tile to part[k][row][column] (part_rows rows per
+  // part, columns as in h1 / the W2 output), and a second launch adds the
+  // parts in order k = 0, 1, ... before the epilogue.
+  int ksplit;
+  float* part;
+  int64_t part_rows;
 };
 
 // Arguments of the grouped backward GEMM launches.

@@ -92,7 +92,8 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
 // banks.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
 
-template <typename T, int MODE>
+// SPLIT: the split-K instantiation (a.ksplit parts per output tile).
+template <typename T, int MODE, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
   constexpr int ES = sizeof(T);
   constexpr int kW = 128 * 128;          // weight stage: 128 rows x 128 B
@@ -112,8 +113,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
   const RouteHdr* hdr = a.hdr;
   if (a.replay_only && !hdr->rec.replay) return;
   // a.mtoff is the m-tile prefix: experts with more than 64 rows are cut
-  // into 128-row tiles, the others into one 64-row tile.
-  const int n_items = a.mtoff[a.E] * a.NT;
+  // into 128-row tiles, the others into one 64-row tile.  With split-K each
+  // output tile is ks consecutive items, one per range of stages.
+  const int ks = SPLIT ? a.ksplit : 1;
+  const int n_items = a.mtoff[a.E] * a.NT * ks;
   // W13 reads the caller's x rows through the permutation (the gather is part
   // of this loader); W2 reads packed h2 rows.
   const char* Abase = reinterpret_cast<const char*>(MODE == 0 ? a.x : a.A);
@@ -128,9 +131,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
 
   const int xcd = blockIdx.x % kXcds;
   const int per = gridDim.x / kXcds;
-  const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
-  const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
-  const int S = int(row_bytes / 128);
+  const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd) * ks;
+  const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1) * ks;
+  const int S_all = int(row_bytes / 128);
 
   // items [first, last) of this XCD come from its work queue, in order
   // (with skewed routing: when some expert spans several m-tiles; otherwise
@@ -142,10 +145,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
   lds_barrier();
   int e_prev = -1;  // expert of this workgroup's previous item
   for (int w = dyn ? first + s_next : first + slot; w < last;) {
-    const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
+    const int wt = ks > 1 ? w / ks : w;   // output tile
+    const int kp = w - wt * ks;           // its stage range: [s0, s0 + S)
+    const int s0 = int(int64_t(kp) * S_all / ks);
+    const int S = int(int64_t(kp + 1) * S_all / ks) - s0;
+    const int e = item_expert(a.mtoff, a.E, a.NT, wt, e_prev);
     e_prev = e;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
-    const int u = w - a.mtoff[e] * a.NT;
+    const int u = wt - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;
     const int mt = u - nt * mt_e;
     const int bm = gemm_tile_rows(a.offsets[e + 1] - a.offsets[e]);
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
       constexpr int NB = decltype(nb_c)::value;
       constexpr bool TM = decltype(tm_c)::value;
       const bool past = s >= S;
-      const int64_t off = int64_t(past ? S - 1 : s) * 128;
+      const int64_t off = int64_t(s0 + (past ? S - 1 : s)) * 128;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {   // weights: non-temporal unless TM (see below)
         const u32x4* src = reinterpret_cast<const u32x4*>((past ? tsrc[j] : wsrc[j]) + off);
@@ -274,7 +281,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
 
     // ---------------------------------------------------------- epilogue
     // acc[b][v] is C[weight row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
-    if (MODE == 0) {
+    if (SPLIT) {
+      // Split-K ("Mixture of Experts: How Routing Becomes GPU Computation",
+      // section 6): this part's fp32 tile, columns as the complete tile
+      // would be stored; k_fwd_splitk_finish adds the parts.
+      const int ncol = MODE == 0 ? (wave < 2 ? 0 : a.F) + nt * 64 + (wave & 1) * 32 + 4 * lh
+                                 : nt * 128 + wave * 32 + 4 * lh;
+      float* P = a.part + (int64_t(kp) * a.part_rows + row0) * a.N + ncol;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int m = 32 * b + lr;
+        if (m < rows) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            store4<float>(P + int64_t(m) * a.N + 8 * g, acc[b][4 * g], acc[b][4 * g + 1],
+                          acc[b][4 * g + 2], acc[b][4 * g + 3]);
+        }
+      }
+    } else if (MODE == 0) {
       // h1 store, then SwiGLU: up waves (2,3) hand their rounded values to
       // gate waves (0,1) through LDS, one 32-row block at a time.
       const int F = a.F;
@@ -351,6 +375,81 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fwd(FwdArgs a) {
   if (dyn && tid == 0) wq_finish(hdr, xcd, per);
 }
 
+// Second pass of a split-K forward GEMM ("Mixture of Experts: How Routing
+// Becomes GPU Computation", section 6, Split-K: the partial results of one
+// output tile are added by a separate reduction kernel).  A thread handles
+// four adjacent output columns of one packed row: its loads of all parts are
+// issued together, then added in order k = 0, 1, ..., so the result does not
+// depend on scheduling.  The epilogue is the one of the single-pass kernel:
+// W13 rounds g and u to T, stores h1 = [g | u] and h2 = SiLU(g) * u; W2
+// stores the row into its route slot, or adds score * row into y32 (FUSED
+// combine).
+constexpr int kMaxSplit = 8;
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void k_fwd_splitk_finish(FwdArgs a) {
+  const RouteHdr* hdr = a.hdr;
+  if (a.replay_only && !hdr->rec.replay) return;
+  const int ks = a.ksplit;
+  const int64_t R = hdr->R;
+  const int cols = (MODE == 0 ? a.F : a.N) / 4;   // 4-column groups per row
+  const int64_t n = R * cols;
+  const int64_t pstride = a.part_rows * a.N;
+  T* h1 = MODE == 0 ? (a.out0 ? reinterpret_cast<T*>(a.out0) : global_ptr<T>(hdr->rec.h1))
+                    : nullptr;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / cols;
+    const int c = int(i - r * cols) * 4;
+    const float* P = a.part + r * a.N + c;
+    constexpr int NV = MODE == 0 ? 2 : 1;   // W13: gate and up columns
+    float4 q[kMaxSplit][NV];
+#pragma unroll
+    for (int k = 0; k < kMaxSplit; ++k) {
+      if (k < ks) {
+#pragma unroll
+        for (int h = 0; h < NV; ++h)
+          q[k][h] = *reinterpret_cast<const float4*>(P + k * pstride + h * a.F);
+      }
+    }
+    float v[NV][4] = {};
+#pragma unroll
+    for (int k = 0; k < kMaxSplit; ++k) {
+      if (k < ks) {
+#pragma unroll
+        for (int h = 0; h < NV; ++h) {
+          v[h][0] += q[k][h].x;
+          v[h][1] += q[k][h].y;
+          v[h][2] += q[k][h].z;
+          v[h][3] += q[k][h].w;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < NV; ++h) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[h][j] = Elem<T>::round(v[h][j]);
+    }
+    if constexpr (MODE == 0) {
+      T* o = h1 + r * (2 * a.F) + c;
+      store4<T>(o, v[0][0], v[0][1], v[0][2], v[0][3]);
+      store4<T>(o + a.F, v[1][0], v[1][1], v[1][2], v[1][3]);
+      float hh[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        hh[j] = silu_f(clamp_gate(v[0][j], a.limit)) * clamp_up(v[1][j], a.limit);
+      store4<T>(reinterpret_cast<T*>(a.out1) + r * a.F + c, hh[0], hh[1], hh[2], hh[3]);
+    } else {
+      const int64_t slotr = a.sorted_route[r];
+      if (a.y32)
+        fused_add4(a.y32 + (slotr / a.K) * a.N + c, a.scores[slotr], v[0][0], v[0][1], v[0][2],
+                   v[0][3]);
+      else
+        store4<T>(reinterpret_cast<T*>(a.out0) + slotr * a.N + c, v[0][0], v[0][1], v[0][2],
+                  v[0][3]);
+    }
+  }
+}
+
 // Persistent grid size: a multiple of the XCD count, at most the upper bound
 // on work items.
 static unsigned fwd_grid(int64_t items_max, int cus, int per_cu) {
@@ -364,14 +463,25 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int64_t mt_max, int cus, hipStr
   static int per_cu = 0;  // resident workgroups per CU (same on every gfx950 device)
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_fwd<T, MODE>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gemm_fwd<T, MODE, false>, 256, 0) !=
             hipSuccess ||
         n <= 0)
       n = 1;
     per_cu = n;
   }
-  const unsigned g = fwd_grid(mt_max * a.NT, cus, per_cu);
-  hipLaunchKernelGGL((k_gemm_fwd<T, MODE>), dim3(g), dim3(256), 0, s, a);
+  const int ks = a.ksplit > 1 ? a.ksplit : 1;
+  const unsigned g = fwd_grid(mt_max * a.NT * ks, cus, per_cu);
+  if (ks > 1) {
+    if (ks > kMaxSplit) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm_fwd<T, MODE, true>), dim3(g), dim3(256), 0, s, a);
+    // rows <= part_rows; one thread per 4 output columns of a row
+    const int64_t cols = (MODE == 0 ? a.F : a.N) / 4;
+    const int64_t blocks = std::min<int64_t>((a.part_rows * cols + 255) / 256, int64_t(cus) * 8);
+    hipLaunchKernelGGL((k_fwd_splitk_finish<T, MODE>), dim3(unsigned(std::max<int64_t>(blocks, 1))),
+                       dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_gemm_fwd<T, MODE, false>), dim3(g), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -391,6 +501,7 @@ hipError_t launch_gemm_fwd(int prec, int mode, const FwdArgs& a, int64_t mt_max,
                      : launch_fwd_t<float, 1>(a, mt_max, cus, s);
   if (a.hotoff) {
     FwdArgs c = a;
+    c.ksplit = 1;   // the finish pass would cover the hot experts' rows too
     c.mtoff = a.ctoff;
     c.stoff = a.cstoff;
     const hipError_t e = mode == 0 ? launch_fwd_t<uint16_t, 0>(c, mt_max, cus, s)

@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
   extern __shared__ int32_t cnt[];   // [E] routes per expert, then [E] routes before this chunk
   int32_t* tot = cnt;
   int32_t* pre = cnt + E;
-  __shared__ int32_t sid[kRankChunk];
+  __shared__ __align__(16) int32_t sid[kRankChunk];
   __shared__ int sh[4 * kScans];
   __shared__ int s_mx;
   const int c = blockIdx.x;
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
   const int mine = c * kRankChunk + tid;   // this thread's route of the chunk
   const int before = c * kRankChunk;       // routes of the earlier chunks
   int my_id = -1, bad = 0;
-  constexpr int kBatch = 8;                // independent loads in flight per thread
+  constexpr int kBatch = 48;   // independent loads in flight per thread (12,288 routes: one batch)
   for (int r0 = 0; r0 < n; r0 += kRankChunk * kBatch) {
     int v[kBatch];
 #pragma unroll
@@ -416,14 +416,15 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
       const int id = v[k];
       const bool valid = id >= 0 && id < E;
       if (id < -1 || id >= E) bad = 1;
-      if (valid) {
-        atomicAdd(&tot[id], 1);
-        if (r < before) atomicAdd(&pre[id], 1);
-      }
+      // one LDS atomic per route: earlier chunks count into pre, the rest
+      // into tot, and tot becomes the total below
+      if (valid) atomicAdd(r < before ? &pre[id] : &tot[id], 1);
       if (r == mine) my_id = valid ? id : -1;
     }
   }
   bad = __syncthreads_or(bad);   // also: every count is in
+  for (int e = tid; e < E; e += kRankChunk) tot[e] += pre[e];
+  __syncthreads();
 
   // exclusive prefixes over experts; thread t owns experts [t ept, t ept + ept)
   const int ept = (E + kRankChunk - 1) / kRankChunk;
@@ -473,9 +474,14 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
       route_to_row[mine] = -1;
     } else {
       // earlier routes of the same expert in this chunk (every lane reads the
-      // same LDS word per step)
+      // same four LDS words per step)
       int rank = 0;
-      for (int q = 0; q < tid; ++q) rank += (sid[q] == my_id);
+      const int4* s4 = reinterpret_cast<const int4*>(sid);
+      for (int q = 0; q < (tid >> 2); ++q) {
+        const int4 v = s4[q];
+        rank += (v.x == my_id) + (v.y == my_id) + (v.z == my_id) + (v.w == my_id);
+      }
+      for (int q = tid & ~3; q < tid; ++q) rank += (sid[q] == my_id);
       const int row = pre[my_id] + rank;
       sorted_route[row] = mine;
       route_to_row[mine] = row;

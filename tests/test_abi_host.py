@@ -185,3 +185,28 @@ def test_plan_hot_tiles_need_32bit_offsets(b):
             assert ("not with this shape" in b.moe_plan_explain(p)) != on, f
         finally:
             b.moe_plan_destroy(p)
+
+
+@pytest.mark.parametrize("t_max,D,F,E,K,prec,expect", [
+    (1, 7168, 2048, 384, 6, "bf16", (8, 3)),     # decode, one token: 192 x 8 and 336 x 3 items
+    (8, 7168, 2048, 384, 6, "bf16", None),       # 1,536 W13 items: no split
+    (2048, 7168, 2048, 384, 6, "bf16", None),
+    (3, 1024, 512, 8, 2, "bf16", (4, 2)),        # 4 stages per part (the minimum)
+    (4, 896, 640, 5, 2, "bf16", (3, 2)),         # 14 stages as 4 + 5 + 5; 10 as 5 + 5
+    (4, 768, 384, 5, 2, "f32", (6, 3)),
+    (1, 7168, 2048, 384, 6, "mxfp8", None),      # block-scaled paths do not split
+])
+def test_plan_forward_split_k_choice(b, t_max, D, F, E, K, prec, expect):
+    """Split-K is chosen from the plan's upper bound on forward work items:
+    below two per CU of the 256, the factor in 1..8 (each part keeping >= 4
+    stages of 128 bytes) whose items fill their last round of 512 resident
+    workgroups best, the smaller on near-ties."""
+    p = b.moe_plan_create(t_max, D, F, E, K, prec)
+    try:
+        txt = b.moe_plan_explain(p)
+        if expect is None:
+            assert "split-K" not in txt
+        else:
+            assert f"forward split-K: W13 x{expect[0]}, W2 x{expect[1]}" in txt, txt
+    finally:
+        b.moe_plan_destroy(p)
