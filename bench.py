@@ -78,10 +78,15 @@ CPU_EXPERTS = {"bf16": 96, "mxfp8": 3, "mxfp4": 3}
 # (the BF16 forward GEMMs: streaming tiles, then the hot experts' tiles).
 SYMBOLS = {
     "bf16": {
-        "w13_swiglu": (["moe::k_gemm_fwd<unsigned short, 0>", "moe::k_gemm_hot<0>"],
+        "w13_swiglu": (["moe::k_gemm_fwd<unsigned short, 0, false>", "moe::k_gemm_hot<0>",
+                        "moe::k_gemm_fwd<unsigned short, 0, true>",
+                        "moe::k_fwd_splitk_finish<unsigned short, 0>"],
                        ["gemm_fwd.hip", "gemm_hot.hip"]),
-        "w2_scatter": (["moe::k_gemm_fwd<unsigned short, 1>", "moe::k_gemm_hot<1>"],
+        "w2_scatter": (["moe::k_gemm_fwd<unsigned short, 1, false>", "moe::k_gemm_hot<1>",
+                        "moe::k_gemm_fwd<unsigned short, 1, true>",
+                        "moe::k_fwd_splitk_finish<unsigned short, 1>"],
                        ["gemm_fwd.hip", "gemm_hot.hip"]),
+        "mega_fwd": ("moe::k_gemm_mega<unsigned short>", ["gemm_fwd.hip"]),
         "w2_dgrad_swiglu": ("moe::k_gemm_dgrad<0>", ["gemm_bwd.hip"]),
         "w13_dgrad": ("moe::k_gemm_dgrad<1>", ["gemm_bwd.hip"]),
         "w2_wgrad": ("moe::k_gemm_wgrad<unsigned short, 2, 0>", ["gemm_bwd.hip"]),
@@ -116,6 +121,8 @@ def parse():
                     help="experts in the CPU-oracle sample (all their routes); 0 = default "
                          "for the precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pipeline", choices=("staged", "mega"), default="staged",
+                    help="BF16 expert forward: two launches (W13, W2) or one fused (Mega) launch")
     ap.add_argument("--width", type=int, default=0,
                     help="expert width F for a width sweep (default: the workload's F; "
                          "a multiple of 128)")
@@ -166,6 +173,8 @@ def alg_bytes(name, m):
         return {
             "w13_swiglu": w13 + T * D * es + R * 2 * F * es + R * F * es,
             "w2_scatter": w2 + R * F * es + R * D * es,
+            # fused: x rows, h1 and h2 written, h3 slots; h2 is read back from L2
+            "mega_fwd": w13 + w2 + T * D * es + R * 2 * F * es + R * F * es + R * D * es,
             "w2_fused": w2 + R * F * es + T * D * 4 + R * 4,
             "w2_dgrad_swiglu": w2 + R * D * es + 2 * R * 2 * F * es + R * F * es,
             "w2_wgrad": ne * D * F * dwb + R * D * es + R * F * es,
@@ -199,6 +208,8 @@ def kernel_flops(name, m):
         name = name[len("replay_"):]
     if name in ("w13_swiglu", "w13_dgrad", "w13_wgrad"):
         return 2 * R * 2 * F * D
+    if name == "mega_fwd":
+        return 6 * R * D * F
     if name in ("w2_scatter", "w2_fused", "w2_dgrad_swiglu", "w2_wgrad"):
         return 2 * R * D * F
     return None
@@ -358,7 +369,10 @@ def setup(args, dev):
             shared.forward(lay["x"], lay["w13_shared"], lay["w2_shared"])
             shared.combine(sh_sc, ysh)
         layer.route(lay["ids"])
-        layer.forward(lay["x"], lay["w13"], lay["w2"])
+        if args.pipeline == "mega":
+            layer.forward_mega(lay["x"], lay["w13"], lay["w2"])
+        else:
+            layer.forward(lay["x"], lay["w13"], lay["w2"])
         layer.combine(lay["scores"], y, y_addend=ysh if shared is not None else None)
         if training:
             layer.backward(lay["x"], lay["scores"], lay["dy"], lay["w13"], lay["w2"], dx, dw13,
@@ -575,7 +589,8 @@ def main():
                                + (f", {info['layers']} layers" if "layers" in info else "")
                                + (", + shared BF16 expert" if cfg.shared_expert else "")
                                + (f", SwiGLU clamped at {cfg.swiglu_limit:g}"
-                                  if cfg.swiglu_limit else ""),
+                                  if cfg.swiglu_limit else "")
+                               + (", fused (Mega) forward" if args.pipeline == "mega" else ""),
                    "routes_per_layer": [m["R"] for lab, m in metas if lab == ""],
                    "nonempty_experts": [m["ne"] for lab, m in metas if lab == ""],
                    "max_rows": max(m["max_rows"] for lab, m in metas if lab == ""),

@@ -82,6 +82,7 @@ typedef enum moe_dtype {
 #define MOE_STATUS_PAD_SCORE  0x2u  /* nonzero score on an id -1 route: ignored */
 #define MOE_STATUS_ARENA      0x4u  /* backward of a layer whose forward state is gone */
 #define MOE_STATUS_NULL_INPUT 0x8u  /* null x/scores/dy for a call with rows: rows skipped */
+#define MOE_STATUS_SYNC_TIMEOUT 0x10u /* fused forward: a W2 tile stopped waiting for its h2 rows */
 
 /* moe_expert_bwd flags */
 #define MOE_BWD_ACCUMULATE_DX 0x1u  /* dx += result instead of dx = result */
@@ -253,6 +254,24 @@ moe_status moe_route(moe_plan_t plan, int64_t T, const int32_t* ids, void* route
 moe_status moe_expert_fwd(moe_plan_t plan, int32_t layer, void* route_ws, const void* x,
                           const moe_weights* w, void* h3_slots, void* arena, void* scratch,
                           hipStream_t stream);
+
+/* The same expert forward as one fused (Mega) launch (explainer section 05,
+ * "Kernel Pipelines: Staged and Mega": the W13 and W2 work records share
+ * one persistent grid, and per-chunk counters in HBM let a W2 record start
+ * once the h2 rows it reads are complete).  Arguments, outputs, planner
+ * behaviour and MOE_STATUS_NULL_INPUT as moe_expert_fwd; h3_slots and the
+ * saved or scratch h1 are bit-identical to moe_expert_fwd's where that one
+ * runs every expert on the streaming tiles without split-K (the same tiles
+ * and epilogues, only scheduled together).  Chunks are experts: each XCD
+ * owns a contiguous range of experts and runs their W13 and W2 records
+ * from its own queue, so h2 rows are handed over inside one L2.  All experts
+ * use the streaming 128 x 128 tiles (no hot-expert tiles, no split-K).
+ * BF16 and F32 plans (MOE_ERR_UNSUPPORTED for block-scaled plans).  A W2
+ * record that waited too long for its rows (it cannot happen while the
+ * grid runs to completion) sets MOE_STATUS_SYNC_TIMEOUT. */
+moe_status moe_expert_fwd_mega(moe_plan_t plan, int32_t layer, void* route_ws, const void* x,
+                               const moe_weights* w, void* h3_slots, void* arena,
+                               void* scratch, hipStream_t stream);
 
 /* Token-owner combine (explainer section 01): y[t] = sum over valid k,
  * ascending, of scores[t,k] * h3_slots[t*K+k] in fp32, plus y_addend[t]

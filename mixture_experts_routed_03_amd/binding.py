@@ -27,6 +27,7 @@ STATUS_BAD_ID = 0x1
 STATUS_PAD_SCORE = 0x2
 STATUS_ARENA = 0x4
 STATUS_NULL_INPUT = 0x8
+STATUS_SYNC_TIMEOUT = 0x10
 BWD_ACCUMULATE_DX = 0x1
 BWD_ACCUMULATE_DW = 0x2
 _ERRORS = {1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
@@ -72,6 +73,8 @@ _SIGS = {
     "moe_prepare_weights": [_P, _P, _P, _P, _P, _P, _P, _P],
     "moe_route": [_P, ctypes.c_int64, _P, _P, _P],
     "moe_expert_fwd": [_P, ctypes.c_int32, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P, _P],
+    "moe_expert_fwd_mega": [_P, ctypes.c_int32, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P,
+                            _P],
     "moe_combine": [_P, _P, _P, _P, _P, _P, _P],
     "moe_expert_fwd_fused": [_P, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P, _P, _P],
     "moe_expert_fwd_fused_noalloc": [_P, _P, _P, _P, ctypes.POINTER(moe_weights), _P, _P, _P],
@@ -176,6 +179,14 @@ def moe_expert_fwd(plan, layer, route_ws, x, weights, h3_slots, arena, scratch, 
     _check(lib().moe_expert_fwd(plan, int(layer), _ptr(route_ws), _ptr(x), ctypes.byref(w),
                                 _ptr(h3_slots), _ptr(arena), _ptr(scratch), _stream(stream)),
            "moe_expert_fwd")
+
+
+def moe_expert_fwd_mega(plan, layer, route_ws, x, weights, h3_slots, arena, scratch,
+                        stream=None):
+    w = weights if isinstance(weights, moe_weights) else _weights(*weights)
+    _check(lib().moe_expert_fwd_mega(plan, int(layer), _ptr(route_ws), _ptr(x), ctypes.byref(w),
+                                     _ptr(h3_slots), _ptr(arena), _ptr(scratch),
+                                     _stream(stream)), "moe_expert_fwd_mega")
 
 
 def moe_combine(plan, route_ws, scores, h3_slots, y_addend, y, stream=None):
@@ -361,6 +372,12 @@ class MoeLayer:
         moe_expert_fwd(self.plan, layer, self.route_ws if route_ws is None else route_ws, x,
                        self._w(w13, w2, prepared), self.h3 if h3 is None else h3, self.arena,
                        self.scratch)
+
+    def forward_mega(self, x, w13, w2, layer=0, route_ws=None, h3=None):
+        """The expert forward as one fused (Mega) launch; same outputs as forward."""
+        moe_expert_fwd_mega(self.plan, layer, self.route_ws if route_ws is None else route_ws, x,
+                            self._w(w13, w2, None), self.h3 if h3 is None else h3, self.arena,
+                            self.scratch)
 
     def combine(self, scores, y, y_addend=None, route_ws=None, h3=None):
         moe_combine(self.plan, self.route_ws if route_ws is None else route_ws, scores,

@@ -43,6 +43,8 @@ hipError_t launch_combine_bwd(int prec, const RouteHdr* hdr, const int32_t* rout
 hipError_t launch_dx_reduce(int prec, const RouteHdr* hdr, const int32_t* route_to_row,
                             const float* dxr, void* dx, int K, int64_t D, int64_t T_max,
                             int accumulate, hipStream_t s);
+hipError_t launch_gemm_mega(int prec, const FwdArgs& a13, const FwdArgs& a2, uint32_t* msync,
+                            int look, int64_t mt_max, int cus, hipStream_t s);
 hipError_t launch_gemm_fwd(int prec, int mode, const FwdArgs& a, int64_t mt_max, int cus,
                            hipStream_t s);
 hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hipStream_t s);
@@ -409,6 +411,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   L.chunk_flags = o; o = a256(o + 4 * L.nchunks);
   L.sorted_route = o; o = a256(o + 4 * R);
   L.route_to_row = o; o = a256(o + 4 * R);
+  L.msync = o; o = a256(o + 4 * (kXcds + E));
   L.total = o;
 
   ScratchLayout& S = p->sl;
@@ -631,20 +634,75 @@ moe_status moe_route(moe_plan_t p, int64_t T, const int32_t* ids, void* ws, hipS
   }));
 }
 
-moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
-                          const moe_weights* w, void* h3, void* arena, void* scratch,
-                          hipStream_t s) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks shared by the staged and the fused (Mega) expert forward.
+moe_status fwd_args_check(moe_plan_s* p, int32_t layer, void* ws, const void* x,
+                          const moe_weights* w, void* h3, void* arena, void* scratch) {
   if (!p || !ws || !w || !h3 || !scratch) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
-  const bool mx8 = d.prec == MOE_PREC_MXFP8;
-  const bool fp4 = d.prec == MOE_PREC_MXFP4;
-  const bool mx = mx8 || fp4;
+  const bool mx = d.prec == MOE_PREC_MXFP8 || d.prec == MOE_PREC_MXFP4;
   if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;
   if (layer < 0 || layer >= d.max_layers) return MOE_ERR_ARG;
   if (!aligned16(x) || !aligned16(w->w13) || !aligned16(w->w2) || !aligned16(w->q13) ||
       !aligned16(w->q2) || !aligned16(h3) || !aligned16(scratch) || !aligned16(ws))
     return MOE_ERR_ARG;
   if (d.training && arena && !aligned16(arena)) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+// W2 records of expert j - kMegaLook follow the W13 records of expert j in
+// the fused forward's queues (measured at T=2048, D=7168, F=2048, E=384,
+// K=6: a lookahead of 1 expert leaves W2 records waiting, 6.06 ms; 2 and 4
+// give 5.88 and 5.86 ms).
+constexpr int kMegaLook = 4;
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_fwd_mega(moe_plan_t p, int32_t layer, void* ws, const void* x,
+                               const moe_weights* w, void* h3, void* arena, void* scratch,
+                               hipStream_t s) {
+  const moe_status st = fwd_args_check(p, layer, ws, x, w, h3, arena, scratch);
+  if (st != MOE_OK) return st;
+  const moe_desc& d = p->d;
+  if (d.prec == MOE_PREC_MXFP8 || d.prec == MOE_PREC_MXFP4) return MOE_ERR_UNSUPPORTED;
+  RouteHdr* hdr = hdr_of(ws);
+  char* sc = reinterpret_cast<char*>(scratch);
+  PlanArgs pa = plan_args(p, layer, d.training, arena, sc);
+  pa.zero = uint64_t(reinterpret_cast<uintptr_t>(at<uint32_t>(ws, p->rl.msync)));
+  pa.zero_n = kXcds + d.e;
+  hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
+  const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
+  const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);
+  const int32_t* sorted_route = at<int32_t>(ws, p->rl.sorted_route);
+  FwdArgs a13{hdr, offsets, gtoff, sorted_route, nullptr, w->w13, nullptr, sc + p->sl.h2,
+              d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, x, d.k};
+  a13.stoff = mtoff;
+  a13.limit = swiglu_limit(p);
+  FwdArgs a2{hdr, offsets, gtoff, sorted_route, sc + p->sl.h2, w->w2, h3, nullptr,
+             d.f, d.d, d.f, d.d / 128, d.e, 0};
+  a2.stoff = mtoff;
+  return hip_status(timed(p, "mega_fwd", s, [&] {
+    return launch_gemm_mega(d.prec, a13, a2, at<uint32_t>(ws, p->rl.msync), kMegaLook, p->mt_max,
+                            plan_cus(p), s);
+  }));
+}
+
+moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
+                          const moe_weights* w, void* h3, void* arena, void* scratch,
+                          hipStream_t s) {
+  const moe_status st = fwd_args_check(p, layer, ws, x, w, h3, arena, scratch);
+  if (st != MOE_OK) return st;
+  const moe_desc& d = p->d;
+  const bool mx8 = d.prec == MOE_PREC_MXFP8;
+  const bool fp4 = d.prec == MOE_PREC_MXFP4;
+  const bool mx = mx8 || fp4;
   RouteHdr* hdr = hdr_of(ws);
   char* sc = reinterpret_cast<char*>(scratch);
   const ScratchLayout& L = p->sl;

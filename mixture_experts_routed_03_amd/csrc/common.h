@@ -79,6 +79,9 @@ constexpr int64_t kArenaHdrBytes = 4096;  // data region starts here
 struct RouteLayout {
   int64_t hdr, counts, offsets, poffsets, mtoff, gtoff, chunk_hist, chunk_flags,
       sorted_route, route_to_row, total;
+  // Fused (Mega) forward: kXcds work-queue tickets, then one W13-tile
+  // completion counter per expert (uint32, zeroed before each fused call)
+  int64_t msync;
   // BF16 forward split: the cold experts' 64-row stage and m-tile prefixes
   // (hot experts count 0) and the hot experts' 256-row m-tile prefix
   int64_t cstoff, ctoff, hotoff;
@@ -232,6 +235,9 @@ struct PlanArgs {
   int32_t mx;               // MXFP8 layer: state = x/h2 column bundles + h1
   int32_t pad0;
   uint64_t scratch_aux[4];  // x bundle codes/exponents, h2 bundle codes/exponents
+  uint64_t zero;            // words [zero, zero + 4 zero_n) set to 0 first (0: none)
+  int32_t zero_n;
+  int32_t pad1;
 };
 
 // ------------------------------------------------------------ device utils
@@ -285,6 +291,10 @@ template <typename T>
 __device__ __forceinline__ T* global_ptr(uint64_t addr) {
   return (T*)(T __attribute__((address_space(1)))*)(addr);
 }
+
+// s_waitcnt immediate that waits for every outstanding vector memory
+// operation of the wave (vmcnt 0; expcnt and lgkmcnt left at their maxima).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -370,6 +380,14 @@ constexpr int kXcds = 8;
 // when it is ready, so items that share a weight tile (the m-tiles of one
 // expert and n-tile) run side by side even when item costs differ.  Called by
 // one thread of the workgroup.
+// The XCD (accelerator complex die) this workgroup runs on, read from the
+// hardware register XCC_ID (bits [3:0]) rather than assumed from blockIdx.
+__device__ __forceinline__ int hw_xcd() {
+  constexpr int kXccIdReg = 20;   // HW_REG_XCC_ID
+  const unsigned v = __builtin_amdgcn_s_getreg(kXccIdReg | (0 << 6) | ((4 - 1) << 11));
+  return int(v % kXcds);
+}
+
 __device__ __forceinline__ int wq_take(const RouteHdr* hdr, int xcd) {
   return int(atomicAdd(const_cast<uint32_t*>(&hdr->wq[xcd]), 1u));
 }

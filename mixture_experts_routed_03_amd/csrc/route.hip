@@ -515,6 +515,10 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
 // that replays keeps only its replay input (here none: x stays with the
 // caller).  Equality saves.  Layer 0 starts the step at cursor 0.
 __global__ void k_plan_decide(RouteHdr* __restrict__ hdr, PlanArgs a) {
+  if (a.zero) {
+    uint32_t* z = reinterpret_cast<uint32_t*>(a.zero);
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) z[i] = 0u;
+  }
   if (threadIdx.x != 0) return;
   LayerRec& rec = hdr->rec;
   const int64_t R = hdr->R;
