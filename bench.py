@@ -93,20 +93,20 @@ SYMBOLS = {
         "w13_wgrad": ("moe::k_gemm_wgrad<unsigned short, 13, 0>", ["gemm_bwd.hip"]),
     },
     "mxfp8": {
-        "w13_swiglu": ("moe::k_mx_fwd<0, 0, 0>", ["gemm_mx.hip"]),
-        "w2_scatter": ("moe::k_mx_fwd<1, 0, 0>", ["gemm_mx.hip"]),
-        "w2_dgrad_swiglu": ("moe::k_mx_dgrad<0>", ["gemm_mx.hip"]),
-        "w13_dgrad": ("moe::k_mx_dgrad<1>", ["gemm_mx.hip"]),
-        "w2_wgrad": ("moe::k_mx_wgrad<unsigned short, 2, 0>", ["gemm_mx.hip"]),
-        "w13_wgrad": ("moe::k_mx_wgrad<unsigned short, 13, 0>", ["gemm_mx.hip"]),
+        "w13_swiglu": ("moe::k_mx_fwd<0, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
+        "w2_scatter": ("moe::k_mx_fwd<1, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
+        "w2_dgrad_swiglu": ("moe::k_mx_dgrad<0>", ["gemm_mx.hip", "mxq.h"]),
+        "w13_dgrad": ("moe::k_mx_dgrad<1>", ["gemm_mx.hip", "mxq.h"]),
+        "w2_wgrad": ("moe::k_mx_wgrad<unsigned short, 2, 0>", ["gemm_mx.hip", "mxq.h"]),
+        "w13_wgrad": ("moe::k_mx_wgrad<unsigned short, 13, 0>", ["gemm_mx.hip", "mxq.h"]),
     },
     "mxfp8_1x32": {
-        "w13_swiglu": ("moe::k_mx_fwd<0, 1, 0>", ["gemm_mx.hip"]),
-        "w2_scatter": ("moe::k_mx_fwd<1, 1, 0>", ["gemm_mx.hip"]),
+        "w13_swiglu": ("moe::k_mx_fwd<0, 1, 0>", ["gemm_mx.hip", "mxq.h"]),
+        "w2_scatter": ("moe::k_mx_fwd<1, 1, 0>", ["gemm_mx.hip", "mxq.h"]),
     },
     "mxfp4": {
-        "w13_swiglu": ("moe::k_mx_fwd<0, 1, 1>", ["gemm_mx.hip"]),
-        "w2_scatter": ("moe::k_mx_fwd<1, 1, 1>", ["gemm_mx.hip"]),
+        "w13_swiglu": ("moe::k_mx_fwd<0, 1, 1>", ["gemm_mx.hip", "mxq.h"]),
+        "w2_scatter": ("moe::k_mx_fwd<1, 1, 1>", ["gemm_mx.hip", "mxq.h"]),
     },
 }
 
@@ -146,7 +146,8 @@ def alg_bytes(name, m):
     R, Rp, ne, T, K, D, F = m["R"], m["Rp"], m["ne"], m["T"], m["K"], m["D"], m["F"]
     es, dwb, mx, rep = m["es"], m["dwb"], m["mx"], m["replay"]
     ab, wb = m["ab"], m["wb"]     # bytes per quantized activation / weight value
-    if name.startswith("replay_"):
+    replay = name.startswith("replay_")
+    if replay:
         if not rep:
             return 0
         name = name[len("replay_"):]
@@ -155,6 +156,9 @@ def alg_bytes(name, m):
 
     def q(n):  # E4M3 (or packed E2M1) codes plus one E8M0 byte per 32 values
         return int(n * ab) + n // 32
+
+    if replay and mx and name == "w13_swiglu":   # rebuilds h1 and bf16 h2 only
+        return int(ne * 2 * F * D * wb) + q(R * D) + R * 2 * F * 2 + R * F * 2
 
     w13 = int(ne * 2 * F * D * wb)
     w2 = int(ne * D * F * wb)
@@ -184,7 +188,9 @@ def alg_bytes(name, m):
     return {
         "quant_x": T * D * 2 + q(R * D),
         "bundle_x": T * D * 2 + q(Rp * D),
-        "w13_swiglu": w13 + q(R * D) + R * 2 * F * 2 + R * F * 2,
+        # h1, the h2 row blocks (quantized in the epilogue) and, in training,
+        # bf16 h2 for its column bundle
+        "w13_swiglu": w13 + q(R * D) + R * 2 * F * 2 + q(R * F) + (R * F * 2 if m["train"] else 0),
         "bundle_h2": R * F * 2 + q(Rp * F),
         "quant_h2": R * F * 2 + q(R * F),
         "w2_scatter": w2 + q(R * F) + R * D * 2,
@@ -258,6 +264,7 @@ def layer_meta(layer, rb, replay, T):
     import numpy as np
     counts = rb["counts"].astype(np.int64)
     return {"R": int(rb["R"]), "Rp": int(rb["poffsets"][-1]), "ne": int((counts > 0).sum()),
+            "train": bool(layer.training),
             "T": T, "K": layer.K, "D": layer.D, "F": layer.F,
             "es": 4 if layer.prec == "f32" else 2,
             "dwb": 4 if layer.dw_dtype.itemsize == 4 else 2,

@@ -266,9 +266,10 @@ moe_status moe_expert_fwd(moe_plan_t plan, int32_t layer, void* route_ws, const 
  * owns a contiguous range of experts and runs their W13 and W2 records
  * from its own queue, so h2 rows are handed over inside one L2.  All experts
  * use the streaming 128 x 128 tiles (no hot-expert tiles, no split-K).
- * BF16 and F32 plans (MOE_ERR_UNSUPPORTED for block-scaled plans).  A W2
- * record that waited too long for its rows (it cannot happen while the
- * grid runs to completion) sets MOE_STATUS_SYNC_TIMEOUT. */
+ * Block-scaled plans (MXFP8 32x32 or 1x32 weights, MXFP4) hand over the h2
+ * rows as the 1x32 blocks the W13 epilogue quantizes them into, as in the
+ * staged forward.  A W2 record that waited too long for its rows (it cannot
+ * happen while the grid runs to completion) sets MOE_STATUS_SYNC_TIMEOUT. */
 moe_status moe_expert_fwd_mega(moe_plan_t plan, int32_t layer, void* route_ws, const void* x,
                                const moe_weights* w, void* h3_slots, void* arena,
                                void* scratch, hipStream_t stream);

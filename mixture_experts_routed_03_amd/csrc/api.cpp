@@ -52,6 +52,8 @@ hipError_t launch_prep_w(const void* w, void* q, void* s, int E, int N, int K, h
 hipError_t launch_rowq(const RowqArgs& a, int64_t R_max, hipStream_t st);
 hipError_t launch_colq(const ColqArgs& a, int64_t Rpad_max, hipStream_t st);
 hipError_t launch_mx_fwd(int mode, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s);
+hipError_t launch_mx_mega(const MxArgs& a13, const MxArgs& a2, uint32_t* msync, int look,
+                          int64_t mt_max, int cus, hipStream_t s);
 hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s);
 hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStream_t s);
 hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s);
@@ -199,8 +201,36 @@ PlanArgs plan_args(const moe_plan_s* p, int32_t layer, int training, void* arena
                    mx8 ? uint64_t(sc + L.h2cq) : 0, mx8 ? uint64_t(sc + L.h2cs) : 0}};
 }
 
+// W2 records of expert j - kMegaLook follow the W13 records of expert j in
+// the fused forward's queues (measured at T=2048, D=7168, F=2048, E=384,
+// K=6: a lookahead of 1 expert leaves W2 records waiting, 6.06 ms; 2 and 4
+// give 5.88 and 5.86 ms).
+constexpr int kMegaLook = 4;
+
+// Arguments of the block-scaled W2 FPROP: h2 row blocks x W2 -> route slots
+// h3 (or, with y32, the FUSED combine).
+MxArgs mx_w2_args(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const moe_weights* w,
+                  void* h3, const float* scores, float* y32) {
+  const moe_desc& d = p->d;
+  const ScratchLayout& L = p->sl;
+  const int fp4 = d.prec == MOE_PREC_MXFP4;
+  MxArgs a2{hdr, at<int32_t>(ws, p->rl.offsets), at<int32_t>(ws, p->rl.poffsets),
+            at<int32_t>(ws, p->rl.mtoff), at<int32_t>(ws, p->rl.sorted_route),
+            reinterpret_cast<const uint8_t*>(sc + L.qh2), reinterpret_cast<const uint8_t*>(sc + L.sh2),
+            reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
+            nullptr, nullptr, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
+            int(p->R_max), scores, y32, d.k};
+  a2.w1x32 = d.mx_w1x32 || fp4;
+  a2.fp4 = fp4;
+  a2.sw_rows = d.e * d.d;
+  return a2;
+}
+
+// With mega (the W2 arguments) the W13 GEMM runs as the fused (Mega) launch
+// together with the W2 records, msync its tickets and counters.
 hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const void* x,
-                          const moe_weights* w, int replay_only, int cus, hipStream_t s) {
+                          const moe_weights* w, int replay_only, int cus, hipStream_t s,
+                          const MxArgs* mega = nullptr, uint32_t* msync = nullptr) {
   const moe_desc& d = p->d;
   const ScratchLayout& L = p->sl;
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
@@ -228,14 +258,26 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
   MxArgs a13{hdr, offsets, poffsets, mtoff, sorted_route,
              reinterpret_cast<const uint8_t*>(sc + L.qx), reinterpret_cast<const uint8_t*>(sc + L.sx),
              reinterpret_cast<const uint8_t*>(w->q13), reinterpret_cast<const uint8_t*>(w->s13),
-             nullptr, nullptr, nullptr, sc + L.h2, d.d, 2 * d.f, d.f, d.f / 64, d.e, 0, 0, -1,
-             replay_only, int(p->R_max)};
+             nullptr, nullptr, nullptr, d.training ? sc + L.h2 : nullptr, d.d, 2 * d.f, d.f,
+             d.f / 64, d.e, 0, 0, -1, replay_only, int(p->R_max)};
   a13.limit = swiglu_limit(p);
   a13.w1x32 = d.mx_w1x32 || fp4;
   a13.fp4 = fp4;
   a13.sw_rows = d.e * 2 * d.f;
-  e = timed(p, replay_only ? "replay_w13" : "w13_swiglu", s,
-            [&] { return launch_mx_fwd(0, a13, p->mt_max, cus, s); });
+  if (!replay_only) {
+    // h2 rows -> 1x32 blocks for the W2 GEMM, in the epilogue (bf16 h2 is
+    // kept only in training, for its column bundle)
+    a13.q_out = reinterpret_cast<uint8_t*>(sc + L.qh2);
+    a13.s_out = reinterpret_cast<uint8_t*>(sc + L.sh2);
+    a13.q_rows = int(p->R_max);
+  }
+  if (mega)
+    e = timed(p, "mega_fwd", s, [&] {
+      return launch_mx_mega(a13, *mega, msync, kMegaLook, p->mt_max, cus, s);
+    });
+  else
+    e = timed(p, replay_only ? "replay_w13" : "w13_swiglu", s,
+              [&] { return launch_mx_fwd(0, a13, p->mt_max, cus, s); });
   if (e != hipSuccess) return e;
   if (d.training) {
     ColqArgs ch{hdr, offsets, poffsets, sc + L.h2, nullptr, nullptr, d.f, d.e, -1, 2, 3,
@@ -653,11 +695,6 @@ moe_status fwd_args_check(moe_plan_s* p, int32_t layer, void* ws, const void* x,
   return MOE_OK;
 }
 
-// W2 records of expert j - kMegaLook follow the W13 records of expert j in
-// the fused forward's queues (measured at T=2048, D=7168, F=2048, E=384,
-// K=6: a lookahead of 1 expert leaves W2 records waiting, 6.06 ms; 2 and 4
-// give 5.88 and 5.86 ms).
-constexpr int kMegaLook = 4;
 
 }  // namespace
 
@@ -669,14 +706,18 @@ moe_status moe_expert_fwd_mega(moe_plan_t p, int32_t layer, void* ws, const void
   const moe_status st = fwd_args_check(p, layer, ws, x, w, h3, arena, scratch);
   if (st != MOE_OK) return st;
   const moe_desc& d = p->d;
-  if (d.prec == MOE_PREC_MXFP8 || d.prec == MOE_PREC_MXFP4) return MOE_ERR_UNSUPPORTED;
   RouteHdr* hdr = hdr_of(ws);
   char* sc = reinterpret_cast<char*>(scratch);
+  uint32_t* msync = at<uint32_t>(ws, p->rl.msync);
   PlanArgs pa = plan_args(p, layer, d.training, arena, sc);
-  pa.zero = uint64_t(reinterpret_cast<uintptr_t>(at<uint32_t>(ws, p->rl.msync)));
+  pa.zero = uint64_t(reinterpret_cast<uintptr_t>(msync));
   pa.zero_n = kXcds + d.e;
   hipError_t e = timed(p, "plan", s, [&] { return launch_plan_decide(hdr, pa, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (d.prec == MOE_PREC_MXFP8 || d.prec == MOE_PREC_MXFP4) {
+    const MxArgs a2 = mx_w2_args(p, hdr, ws, sc, w, h3, nullptr, nullptr);
+    return hip_status(mx_forward_w13(p, hdr, ws, sc, x, w, 0, plan_cus(p), s, &a2, msync));
+  }
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
   const int32_t* mtoff = at<int32_t>(ws, p->rl.mtoff);
   const int32_t* gtoff = at<int32_t>(ws, p->rl.gtoff);
@@ -735,20 +776,7 @@ moe_status moe_expert_fwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   }
   e = mx_forward_w13(p, hdr, ws, sc, x, w, 0, cus, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  // h2 -> 1x32 row blocks for the W2 GEMM
-  RowqArgs rq{hdr, sc + L.h2, reinterpret_cast<uint8_t*>(sc + L.qh2),
-              reinterpret_cast<uint8_t*>(sc + L.sh2), d.f, -1, -1, -1, 0, int(p->R_max)};
-  rq.fp4 = fp4;
-  e = timed(p, "quant_h2", s, [&] { return launch_rowq(rq, p->R_max, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  MxArgs a2{hdr, offsets, poffsets, mtoff, sorted_route,
-            reinterpret_cast<const uint8_t*>(sc + L.qh2), reinterpret_cast<const uint8_t*>(sc + L.sh2),
-            reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
-            nullptr, nullptr, h3, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
-            int(p->R_max)};
-  a2.w1x32 = d.mx_w1x32 || fp4;
-  a2.fp4 = fp4;
-  a2.sw_rows = d.e * d.d;
+  const MxArgs a2 = mx_w2_args(p, hdr, ws, sc, w, h3, nullptr, nullptr);
   return hip_status(timed(p, "w2_scatter", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); }));
 }
 
@@ -829,19 +857,7 @@ moe_status fused_forward(moe_plan_s* p, void* ws, const void* x, const float* sc
   } else {
     e = mx_forward_w13(p, hdr, ws, sc, x, w, 0, cus, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    RowqArgs rq{hdr, sc + L.h2, reinterpret_cast<uint8_t*>(sc + L.qh2),
-                reinterpret_cast<uint8_t*>(sc + L.sh2), d.f, -1, -1, -1, 0, int(p->R_max)};
-    rq.fp4 = fp4;
-    e = timed(p, "quant_h2", s, [&] { return launch_rowq(rq, p->R_max, s); });
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    MxArgs a2{hdr, offsets, poffsets, mtoff, sorted_route,
-              reinterpret_cast<const uint8_t*>(sc + L.qh2), reinterpret_cast<const uint8_t*>(sc + L.sh2),
-              reinterpret_cast<const uint8_t*>(w->q2), reinterpret_cast<const uint8_t*>(w->s2),
-              nullptr, nullptr, nullptr, nullptr, d.f, d.d, d.f, d.d / 128, d.e, 0, 0, -1, 0,
-              int(p->R_max), scores, y32, d.k};
-    a2.w1x32 = d.mx_w1x32 || fp4;
-    a2.fp4 = fp4;
-    a2.sw_rows = d.e * d.d;
+    const MxArgs a2 = mx_w2_args(p, hdr, ws, sc, w, nullptr, scores, y32);
     e = timed(p, "w2_fused", s, [&] { return launch_mx_fwd(1, a2, p->mt_max, cus, s); });
   }
   if (e != hipSuccess) return MOE_ERR_HIP;

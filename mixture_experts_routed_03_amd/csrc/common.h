@@ -191,6 +191,12 @@ struct MxArgs {
   int sw_rows;           // E * N for w1x32
   int fp4;               // FPROP: E2M1 operands (two per byte) with 1x32 weight blocks;
                          // exponents grouped by 256-value stage, [Kd/256][rows][8]
+  // W13 FPROP: h2 rows quantized in the epilogue (null: none), as k_rowq
+  // writes them: codes [R, F] (E2M1 with fp4: [R, F/2]) and exponents grouped
+  // by stage with q_rows rows (the W2 FPROP's token operand)
+  uint8_t* q_out;
+  uint8_t* s_out;
+  int q_rows;
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:

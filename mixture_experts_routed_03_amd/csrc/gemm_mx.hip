@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "mxq.h"
 
 namespace moe {
 
@@ -99,8 +100,15 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
 // FP4 (needs W1): E2M1 operands, two per byte.  A stage is still 128 bytes
 // of every row, now 256 values = 8 MX blocks = four MFMAs per accumulator,
 // with 8 exponent bytes per row.
+// MODE 2: the fused (Mega) forward: the W13 records of a and the W2 records
+// of a2 from per-XCD queues with per-expert readiness counters in msync, the
+// hand-off described at k_gemm_mega (gemm_fwd.hip).  Prefetch into the next
+// record crosses into a W2 record only once its h2 rows are complete;
+// otherwise the record waits for them before its first loads.
+constexpr int kMxMegaSpin = 1 << 22;   // polls (each followed by a short sleep)
+
 template <int MODE, int W1, int FP4>
-__global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
+__global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a, MxArgs a2, uint32_t* msync, int look) {
   static_assert(!FP4 || W1, "4-bit weights come in 1x32 blocks");
   constexpr int kW = 128 * 128;      // weight stage: 128 rows x 128 bytes
   constexpr int kA = kBM * 128;      // token stage: 64 rows x 128 bytes
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   // + the weight exponents: one dword per wave (32x32) or per weight row (1x32)
   constexpr int kStage = kW + kA + kSc + (W1 ? 128 * kXb : 16);
   constexpr int kXch = 2 * 2 * 16 * 64 * 4;   // SwiGLU epilogue: up halves of two waves
-  __shared__ __attribute__((aligned(16))) char lds[2 * kStage + (MODE == 0 ? kXch : 0)];
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStage + (MODE != 1 ? kXch : 0)];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -123,17 +131,37 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   const int n_items = hdr->n_mt * a.NT;
   uint16_t* out0 = a.out0 ? reinterpret_cast<uint16_t*>(a.out0) : global_ptr<uint16_t>(hdr->rec.h1);
   uint16_t* out1 = reinterpret_cast<uint16_t*>(a.out1);
+  const MxArgs& b2 = MODE == 2 ? a2 : a;   // the W2 records' arguments
+  uint16_t* h3 = reinterpret_cast<uint16_t*>(b2.out0);
   const int Kd = a.Kd;
   const int KB = Kd / 32;           // scale bytes per row
   const int Kb = FP4 ? Kd / 2 : Kd; // code bytes per row
-  const int xcd = blockIdx.x % kXcds;
+  const int xcd = MODE == 2 ? hw_xcd() : blockIdx.x % kXcds;
   const int per = gridDim.x / kXcds;
   const int chunk = (n_items + kXcds - 1) / kXcds;
-  const int S = Kb / 128;
+  const int S_fix = Kb / 128;       // stages per item (MODE 0 / 1)
+
+  // MODE 2: this XCD's experts [e_lo, e_lo + ne) and its queue: block j =
+  // the W13 records of expert e_lo + j, then the W2 records of expert
+  // e_lo + j - look; mstart(j) = records before block j
+  const int32_t* gt = a.mtoff;
+  uint32_t* ticket = msync + xcd;
+  uint32_t* ready = msync + kXcds;
+  int e_lo = 0, ne = 0, total = 0;
+  if (MODE == 2) {
+    e_lo = xcd_first_unit(gt, 0, a.E, 1, xcd);
+    ne = xcd_first_unit(gt, 0, a.E, 1, xcd + 1) - e_lo;
+    total = (gt[e_lo + ne] - gt[e_lo]) * (a.NT + a2.NT);
+  }
+  auto mstart = [&](int j) {
+    const int p = min(j, ne), q = max(0, min(j - look, ne));
+    return (gt[e_lo + p] - gt[e_lo]) * a.NT + (gt[e_lo + q] - gt[e_lo]) * a2.NT;
+  };
+  int j_lo = 0;   // tickets only grow, so blocks only move forward
 
   // Operand sources of one work item (an m-tile of an expert x 128 weight rows).
   struct Item {
-    int e, nt, row0, rows;
+    int md, S, e, nt, row0, rows;
     const uint8_t* w[4];     // weight rows of this thread (4 x 16 bytes per stage)
     const uint8_t* t[2];     // token rows
     const uint32_t* ws;      // weight exponents
@@ -141,14 +169,36 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   };
   int e_prev = -1;  // expert of this workgroup's previous item
   auto setup = [&](int w, Item& I) {
-    const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
-    e_prev = e;
+    int md = MODE, e, u;
+    if (MODE == 2) {
+      int hi = ne + look;   // mstart(j_lo) <= w < mstart(hi) = total
+      while (hi - j_lo > 1) {
+        const int mid = (j_lo + hi) >> 1;
+        if (mstart(mid) <= w)
+          j_lo = mid;
+        else
+          hi = mid;
+      }
+      u = w - mstart(j_lo);
+      const int c13 = j_lo < ne ? (gt[e_lo + j_lo + 1] - gt[e_lo + j_lo]) * a.NT : 0;
+      md = u < c13 ? 0 : 1;
+      e = md == 0 ? e_lo + j_lo : e_lo + j_lo - look;
+      if (md) u -= c13;
+    } else {
+      e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
+      e_prev = e;
+      u = w - a.mtoff[e] * a.NT;
+    }
+    const MxArgs& A = md == 1 ? b2 : a;
+    const int Kbi = FP4 ? A.Kd / 2 : A.Kd;
+    const int KBi = A.Kd / 32;
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
-    const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;
     const int mt = u - nt * mt_e;
     const int row0 = a.offsets[e] + mt * kBM;
     const int rows = min(kBM, a.offsets[e + 1] - row0);
+    I.md = md;
+    I.S = MODE == 2 ? Kbi / 128 : S_fix;
     I.e = e;
     I.nt = nt;
     I.row0 = row0;
@@ -156,28 +206,30 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rho = lrow + 32 * j;
-      const int wr = MODE == 0 ? (rho < 64 ? nt * 64 + rho : a.F + nt * 64 + rho - 64)
-                               : nt * 128 + rho;
-      I.w[j] = a.qw + (int64_t(e) * a.N + wr) * Kb + lc * 16;
+      const int wr = md == 0 ? (rho < 64 ? nt * 64 + rho : A.F + nt * 64 + rho - 64)
+                             : nt * 128 + rho;
+      I.w[j] = A.qw + (int64_t(e) * A.N + wr) * Kbi + lc * 16;
     }
     // the 32 weight rows of this wave form one 32-row scale block
-    const int wrow0 = MODE == 0 ? ((wave < 2 ? 0 : a.F) + nt * 64 + (wave & 1) * 32)
-                                : nt * 128 + wave * 32;
+    const int wrow0 = md == 0 ? ((wave < 2 ? 0 : A.F) + nt * 64 + (wave & 1) * 32)
+                              : nt * 128 + wave * 32;
     // 1x32: thread tid < 128 fetches the exponents of tile row tid
-    const int wr1 = MODE == 0 ? ((tid & 127) < 64 ? nt * 64 + (tid & 63)
-                                                  : a.F + nt * 64 + (tid & 63))
-                              : nt * 128 + (tid & 127);
-    I.ws = W1 ? reinterpret_cast<const uint32_t*>(a.sw) + (int64_t(e) * a.N + wr1) * (kXb / 4)
-              : reinterpret_cast<const uint32_t*>(a.sw + (int64_t(e) * (a.N / 32) + wrow0 / 32) * KB);
+    const int wr1 = md == 0 ? ((tid & 127) < 64 ? nt * 64 + (tid & 63)
+                                                : A.F + nt * 64 + (tid & 63))
+                            : nt * 128 + (tid & 127);
+    I.ws = W1 ? reinterpret_cast<const uint32_t*>(A.sw) + (int64_t(e) * A.N + wr1) * (kXb / 4)
+              : reinterpret_cast<const uint32_t*>(A.sw + (int64_t(e) * (A.N / 32) + wrow0 / 32) * KBi);
     // Tile rows past the expert's last row re-read that row: every load is
     // unconditional, and the extra output columns are never stored.
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      I.t[j] = a.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kb + lc * 16;
+      I.t[j] = A.qa + int64_t(row0 + min(lrow + 32 * j, rows - 1)) * Kbi + lc * 16;
     // token exponents are grouped by stage: the kXb bytes of (s, row) at
     // (s * sa_rows + row) * kXb
-    I.ts = reinterpret_cast<const uint32_t*>(a.sa) + int64_t(row0 + min(tid & 63, rows - 1)) * (kXb / 4);
+    I.ts = reinterpret_cast<const uint32_t*>(A.sa) + int64_t(row0 + min(tid & 63, rows - 1)) * (kXb / 4);
   };
+  // MODE 2 (W1 weights): the exponent rows of the W13 and W2 weights differ
+  auto sw_rows = [&](const Item& I) { return MODE == 2 && I.md == 1 ? b2.sw_rows : a.sw_rows; };
 
   u32x4 R0[6], R1[6];
   // [0..1] weight scales (of the wave, or of tile row tid with W1), [2..3]
@@ -188,6 +240,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   // Stage idx of the current item; idx >= S is stage idx - S of the next item
   // (without a next item: the current item's last stage, never used).
   auto load = [&](u32x4* R, uint32_t* Sc, int idx) {
+    const int S = cur.S;
     const bool nx = idx >= S;
     const int st = nx ? (cross ? idx - S : S - 1) : idx;
     const bool use_n = nx && cross;
@@ -203,14 +256,14 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     const uint32_t* tsp = use_n ? nxt.ts : cur.ts;
     if (FP4) {
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 w2 = *reinterpret_cast<const u32x2*>(wsp + int64_t(st) * a.sw_rows * 2);
+      const u32x2 w2 = *reinterpret_cast<const u32x2*>(wsp + int64_t(st) * sw_rows(use_n ? nxt : cur) * 2);
       const u32x2 t2 = *reinterpret_cast<const u32x2*>(tsp + int64_t(st) * a.sa_rows * 2);
       Sc[0] = w2[0];
       Sc[1] = w2[1];
       Sc[2] = t2[0];
       Sc[3] = t2[1];
     } else {
-      Sc[0] = W1 ? wsp[int64_t(st) * a.sw_rows] : wsp[st];
+      Sc[0] = W1 ? wsp[int64_t(st) * sw_rows(use_n ? nxt : cur)] : wsp[st];
       Sc[2] = tsp[int64_t(st) * a.sa_rows];
     }
   };
@@ -291,29 +344,57 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
   // tickets (its current and next item) and takes the one after while an
   // item's epilogue runs.  Otherwise they are dealt statically (slot,
   // slot + per, ...), which costs no atomics.
-  auto valid = [&](int it) { return it < chunk && xcd * chunk + it < n_items; };
-  const bool dyn = hdr->max_count > kBM;
+  auto valid = [&](int it) {
+    return MODE == 2 ? it < total : (it < chunk && xcd * chunk + it < n_items);
+  };
+  auto index = [&](int it) { return MODE == 2 ? it : xcd * chunk + it; };
+  auto take = [&]() { return MODE == 2 ? int(atomicAdd(ticket, 1u)) : wq_take(hdr, xcd); };
+  // MODE 2: W13 records of expert e, which its W2 records wait for
+  auto need = [&](int e) { return uint32_t((gt[e + 1] - gt[e]) * a.NT); };
+  const bool dyn = MODE == 2 || hdr->max_count > kBM;
   const int slot = blockIdx.x / kXcds;
   __shared__ int s_q[2];
+  __shared__ int s_ok;
   if (dyn && tid == 0) {
-    s_q[0] = wq_take(hdr, xcd);
-    s_q[1] = wq_take(hdr, xcd);
+    s_q[0] = take();
+    s_q[1] = take();
   }
   lds_barrier();
   int it = dyn ? s_q[0] : slot, itn = dyn ? s_q[1] : slot + per;
-  if (valid(it)) setup(xcd * chunk + it, cur);
+  if (valid(it)) setup(index(it), cur);
   bool primed = false;  // buffer 0 / R1 / R0 already hold stages 0 / 1 / 2 of cur
   for (; valid(it);) {
+    const int S = cur.S;
     // Prefetch across items needs three stages per item (the three stages in
     // flight at an item's end must all belong to the next item).
     cross = valid(itn) && S >= 3;
-    if (cross) setup(xcd * chunk + itn, nxt);
+    if (cross) {
+      setup(index(itn), nxt);
+      if (MODE == 2) {
+        cross = nxt.S >= 3;
+        if (nxt.md == 1) {   // a W2 record: only with its h2 rows complete
+          if (tid == 0) s_ok = atomicAdd(&ready[nxt.e], 0u) >= need(nxt.e);
+          lds_barrier();
+          cross = cross && s_ok;
+        }
+      }
+    }
     acc0 = f32x16{};
     acc1 = f32x16{};
 
     // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
     // s + 1 and R0 stage s + 2.
     if (!primed) {
+      if (MODE == 2 && cur.md == 1) {   // wait (bounded) for the h2 rows
+        if (tid == 0) {
+          int n = 0;
+          while (atomicAdd(&ready[cur.e], 0u) < need(cur.e) && ++n < kMxMegaSpin)
+            __builtin_amdgcn_s_sleep(4);
+          if (n >= kMxMegaSpin)
+            atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_SYNC_TIMEOUT);
+        }
+        lds_barrier();
+      }
       load(R0, S0, 0);
       load(R1, S1, 1);
       store(R0, S0, 0);
@@ -345,10 +426,11 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     }
     const int nt = cur.nt, row0 = cur.row0, rows = cur.rows;
     int taken = 0;
-    if (dyn && tid == 0) taken = wq_take(hdr, xcd);
+    if (dyn && tid == 0) taken = take();
 
     // Epilogue (as the BF16 kernels): acc[b][v] = C[row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
-    if (MODE == 0) {
+    const int md = MODE == 2 ? cur.md : MODE;
+    if (md == 0) {
       const int F = a.F;
       const int ncol = (wave < 2 ? 0 : F) + nt * 64 + (wave & 1) * 32 + 4 * lh;
 #pragma unroll
@@ -381,16 +463,61 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
             float h[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              h[v] = silu_f(clamp_gate(round_bf16(acc[v]), a.limit)) *
-                     clamp_up(xch[((wave * 2 + b) * 16 + v) * 64 + lane], a.limit);
-            uint16_t* o = out1 + int64_t(row0 + m) * F + jcol;
+              h[v] = round_bf16(silu_f(clamp_gate(round_bf16(acc[v]), a.limit)) *
+                                clamp_up(xch[((wave * 2 + b) * 16 + v) * 64 + lane], a.limit));
+            if (out1) {
+              uint16_t* o = out1 + int64_t(row0 + m) * F + jcol;
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-              store4<uint16_t>(o + 8 * g, h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
+              for (int g = 0; g < 4; ++g)
+                store4<uint16_t>(o + 8 * g, h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
+            }
+            if (a.q_out) {
+              // The wave's 32 columns are one 1x32 block of the h2 row: lane
+              // (r, 0) holds block values 8g + i, lane (r, 1) values 8g + 4 + i
+              // (g, i < 4); amax over both, then k_rowq's encoding.
+              float amax = 0.0f;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(h[v]));
+              amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+              const int64_t row = row0 + m;
+              const int c0 = nt * 64 + wave * 32;   // the block's first column
+              if (FP4) {
+                const int ex = e8m0_exp_fp4(amax);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  uint32_t wv = 0;
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) wv |= e2m1_rne(ldexp_i(h[4 * g + i], -ex)) << (4 * i);
+                  *reinterpret_cast<uint16_t*>(a.q_out + row * (F / 2) + (jcol + 8 * g) / 2) =
+                      uint16_t(wv);
+                }
+                if (lh == 0)
+                  a.s_out[(int64_t(c0 / 256) * a.q_rows + row) * 8 + (c0 / 32) % 8] =
+                      uint8_t(ex + 127);
+              } else {
+                const int ex = e8m0_exp(amax);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  uint32_t wv = 0;
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) wv |= e4m3_rne(ldexp_i(h[4 * g + i], -ex)) << (8 * i);
+                  *reinterpret_cast<uint32_t*>(a.q_out + row * F + jcol + 8 * g) = wv;
+                }
+                if (lh == 0)
+                  a.s_out[(int64_t(c0 / 128) * a.q_rows + row) * 4 + (c0 / 32) % 4] =
+                      uint8_t(ex + 127);
+              }
+            }
           }
         }
       }
       lds_barrier();
+      if (MODE == 2) {   // this record's stores complete in L2, then counted
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (tid == 0) atomicAdd(&ready[cur.e], 1u);
+      }
     } else {
       const int ncol = nt * 128 + wave * 32 + 4 * lh;
 #pragma unroll
@@ -398,16 +525,16 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
         const f32x16& acc = b ? acc1 : acc0;
         const int m = 32 * b + lr;
         if (m < rows) {
-          const int64_t slotr = a.sorted_route[row0 + m];
-          if (a.y32) {   // FUSED combine (h3 rounded to bf16 as the slots would hold it)
-            const float sc = a.scores[slotr];
-            float* o = a.y32 + (slotr / a.K) * a.N + ncol;
+          const int64_t slotr = b2.sorted_route[row0 + m];
+          if (b2.y32) {   // FUSED combine (h3 rounded to bf16 as the slots would hold it)
+            const float sc = b2.scores[slotr];
+            float* o = b2.y32 + (slotr / b2.K) * b2.N + ncol;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
               fused_add4(o + 8 * g, sc, round_bf16(acc[4 * g]), round_bf16(acc[4 * g + 1]),
                          round_bf16(acc[4 * g + 2]), round_bf16(acc[4 * g + 3]));
           } else {
-            uint16_t* o = out0 + slotr * a.N + ncol;
+            uint16_t* o = h3 + slotr * b2.N + ncol;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
               store4<uint16_t>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
@@ -419,7 +546,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     if (dyn && tid == 0) s_q[0] = taken;
     lds_barrier();
     if (!cross) {
-      if (valid(itn)) setup(xcd * chunk + itn, cur);
+      if (valid(itn)) setup(index(itn), cur);
       primed = false;
     } else {
       cur = nxt;
@@ -428,7 +555,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a) {
     it = itn;
     itn = dyn ? s_q[0] : itn + per;
   }
-  if (dyn && tid == 0) wq_finish(hdr, xcd, per);
+  if (MODE != 2 && dyn && tid == 0) wq_finish(hdr, xcd, per);
 }
 
 // ------------------------------------------------------------------ DGRAD
@@ -890,13 +1017,28 @@ hipError_t launch_mx_fwd(int mode, const MxArgs& a, int64_t mt_max, int cus, hip
 #define MOE_MXF(M, W, P, ID)                                                                   \
   hipLaunchKernelGGL((k_mx_fwd<M, W, P>),                                                     \
                      dim3(grid_m(occupancy_m<ID>(k_mx_fwd<M, W, P>), mt_max * a.NT, cus)), \
-                     dim3(256), 0, s, a)
+                     dim3(256), 0, s, a, a, nullptr, 0)
   if (mode == 0) {
     if (a.fp4) MOE_MXF(0, 1, 1, 14); else if (a.w1x32) MOE_MXF(0, 1, 0, 12); else MOE_MXF(0, 0, 0, 0);
   } else {
     if (a.fp4) MOE_MXF(1, 1, 1, 15); else if (a.w1x32) MOE_MXF(1, 1, 0, 13); else MOE_MXF(1, 0, 0, 1);
   }
 #undef MOE_MXF
+  return hipGetLastError();
+}
+
+// Fused (Mega) MX forward: a13 = the W13 records' arguments, a2 = the W2
+// records'; msync = tickets and per-expert counters, zeroed before the call.
+hipError_t launch_mx_mega(const MxArgs& a13, const MxArgs& a2, uint32_t* msync, int look,
+                          int64_t mt_max, int cus, hipStream_t s) {
+  if (mt_max == 0) return hipSuccess;
+  const int64_t items = mt_max * (a13.NT + a2.NT);
+#define MOE_MXM(W, P, ID)                                                                     \
+  hipLaunchKernelGGL((k_mx_fwd<2, W, P>),                                                     \
+                     dim3(grid_m(occupancy_m<ID>(k_mx_fwd<2, W, P>), items, cus)),           \
+                     dim3(256), 0, s, a13, a2, msync, look)
+  if (a13.fp4) MOE_MXM(1, 1, 18); else if (a13.w1x32) MOE_MXM(1, 0, 17); else MOE_MXM(0, 0, 16);
+#undef MOE_MXM
   return hipGetLastError();
 }
 
