@@ -10,9 +10,9 @@
 // Dist-MoE explainer section 01: id -1 disables a route.
 //
 // Deterministic counting sort.  Up to 1,024 routes (decode): one workgroup
-// of one launch (k_route_small); up to 32,768 routes: one launch of one
-// workgroup per 256-route chunk that needs nothing from the others
-// (k_route_chunked); larger calls, three launches:
+// of one launch (k_route_small); up to 32,768 routes and 2,560 experts: one
+// launch of one workgroup per 256-route chunk that needs nothing from the
+// others (k_route_chunked); larger calls, three launches:
 //   hist : one workgroup per chunk of 256 routes, LDS atomics -> chunk_hist[c][e]
 //   scan : one workgroup; counts[e] = sum_c chunk_hist[c][e], exclusive scans
 //          of counts, of counts rounded up to 32 and of m-tiles; the chunk
@@ -368,11 +368,15 @@ __device__ void block_scan256(int* v /* [N] */, int* sh /* [N][4] */) {
 // they come from L2) and counts in LDS, with integer atomics (exact in any
 // order), each expert's routes in all chunks and in the chunks before its
 // own.  It then scans the per-expert terms itself (each thread a run of
-// consecutive experts) and ranks its own chunk's routes as k_route_rank
-// does; workgroup 0 publishes counts, prefixes and the header.  Same
-// outputs as the three-launch path, which stays for larger calls (each
-// workgroup's read of every id would grow with the square of the call).
+// consecutive experts) and ranks its own chunk's routes: a route's rank is
+// the count of its expert's routes in the chunk's earlier waves (LDS
+// counters) plus the earlier lanes of its own wave with that expert;
+// workgroup 0 publishes counts, prefixes and the header.  Same outputs as
+// the three-launch path, which stays for larger calls (each workgroup's
+// read of every id would grow with the square of the call) and for more
+// experts than its LDS counters fit.
 constexpr int kChunkedRoutes = 32768;
+constexpr int kChunkedMaxE = 2560;   // 6 E counters in LDS, within 64 KiB
 
 __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict__ ids, int n,
                                                        int E, int T,
@@ -385,18 +389,18 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
                                                        int32_t* __restrict__ sorted_route,
                                                        int32_t* __restrict__ route_to_row,
                                                        RouteHdr* __restrict__ hdr) {
-  extern __shared__ int32_t cnt[];   // [E] routes per expert, then [E] routes before this chunk
+  // [E] routes per expert, [E] routes before this chunk, then [4][E] the
+  // chunk's routes per expert in each of its four waves
+  extern __shared__ int32_t cnt[];
   int32_t* tot = cnt;
   int32_t* pre = cnt + E;
+  int32_t* wcnt = cnt + 2 * E;
   __shared__ __align__(16) int32_t sid[kRankChunk];
   __shared__ int sh[4 * kScans];
   __shared__ int s_mx;
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kRankChunk) {
-    tot[e] = 0;
-    pre[e] = 0;
-  }
+  for (int e = tid; e < 6 * E; e += kRankChunk) cnt[e] = 0;
   if (tid == 0) s_mx = 0;
   __syncthreads();
   const int mine = c * kRankChunk + tid;   // this thread's route of the chunk
@@ -422,6 +426,7 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
       if (r == mine) my_id = valid ? id : -1;
     }
   }
+  if (my_id >= 0) atomicAdd(&wcnt[(tid >> 6) * E + my_id], 1);
   bad = __syncthreads_or(bad);   // also: every count is in
   for (int e = tid; e < E; e += kRankChunk) tot[e] += pre[e];
   __syncthreads();
@@ -473,11 +478,14 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
     if (my_id < 0) {
       route_to_row[mine] = -1;
     } else {
-      // earlier routes of the same expert in this chunk (every lane reads the
-      // same four LDS words per step)
+      // earlier routes of the same expert in this chunk: those of the earlier
+      // waves (counted), then the earlier lanes of this wave (every lane reads
+      // the same four LDS words per step)
+      const int w = tid >> 6;
       int rank = 0;
+      for (int u = 0; u < w; ++u) rank += wcnt[u * E + my_id];
       const int4* s4 = reinterpret_cast<const int4*>(sid);
-      for (int q = 0; q < (tid >> 2); ++q) {
+      for (int q = w * 16; q < (tid >> 2); ++q) {
         const int4 v = s4[q];
         rank += (v.x == my_id) + (v.y == my_id) + (v.z == my_id) + (v.w == my_id);
       }
@@ -626,8 +634,8 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
     return hipGetLastError();
   }
   const int nchunks = int((n + kRankChunk - 1) / kRankChunk);
-  if (n <= kChunkedRoutes) {
-    hipLaunchKernelGGL(k_route_chunked, dim3(nchunks), dim3(kRankChunk), 2 * E * sizeof(int32_t),
+  if (n <= kChunkedRoutes && E <= kChunkedMaxE) {
+    hipLaunchKernelGGL(k_route_chunked, dim3(nchunks), dim3(kRankChunk), 6 * E * sizeof(int32_t),
                        s, ids, int(n), E, int(T),
                        reinterpret_cast<int32_t*>(ws + L.counts),
                        reinterpret_cast<int32_t*>(ws + L.offsets),
