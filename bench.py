@@ -251,9 +251,11 @@ def measured_profile(workload, prec, kname):
             return None, None
         traffic = [blob.get("traffic_bytes", {}).get(s) for s in syms]
         avg = [blob.get("avg_us_working", {}).get(s) for s in syms]
+        if not any(avg):   # a summary of another pipeline of this workload
+            continue
         tb = (int(sum(sum(t) / len(t) for t in traffic if t))
-              if traffic[0] else None)
-        us = round(sum(a for a in avg if a), 2) if avg[0] else None
+              if any(traffic) else None)
+        us = round(sum(a for a in avg if a), 2)
         return tb, us
     return None, None
 
