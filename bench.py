@@ -94,6 +94,7 @@ SYMBOLS = {
     },
     "mxfp8": {
         "w13_swiglu": ("moe::k_mx_fwd<0, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
+        "mega_fwd": ("moe::k_mx_fwd<2, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
         "w2_scatter": ("moe::k_mx_fwd<1, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
         "w2_dgrad_swiglu": ("moe::k_mx_dgrad<0>", ["gemm_mx.hip", "mxq.h"]),
         "w13_dgrad": ("moe::k_mx_dgrad<1>", ["gemm_mx.hip", "mxq.h"]),
@@ -191,6 +192,9 @@ def alg_bytes(name, m):
         # h1, the h2 row blocks (quantized in the epilogue) and, in training,
         # bf16 h2 for its column bundle
         "w13_swiglu": w13 + q(R * D) + R * 2 * F * 2 + q(R * F) + (R * F * 2 if m["train"] else 0),
+        # fused (Mega) forward: both GEMMs' operands and outputs, h2 handed over in L2
+        "mega_fwd": (w13 + w2 + q(R * D) + R * 2 * F * 2 + q(R * F)
+                     + (R * F * 2 if m["train"] else 0) + R * D * 2),
         "bundle_h2": R * F * 2 + q(Rp * F),
         "quant_h2": R * F * 2 + q(R * F),
         "w2_scatter": w2 + q(R * F) + R * D * 2,
