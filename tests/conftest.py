@@ -33,7 +33,8 @@ def _poison_workspaces():
         return
     from mixture_experts_routed_03_amd import binding as B
     M = B.MoeLayer
-    orig = {n: getattr(M, n) for n in ("route", "forward", "combine", "forward_fused", "backward")}
+    orig = {n: getattr(M, n) for n in ("route", "forward", "forward_mega", "combine",
+                                       "forward_fused", "backward")}
     byte = POISON
 
     def route(self, ids, route_ws=None):
@@ -46,6 +47,13 @@ def _poison_workspaces():
         if self.arena is not None and layer == 0:      # a new step: no saved state yet
             _fill(self.arena[4096:], byte)
         return orig["forward"](self, x, w13, w2, layer, route_ws, h3, prepared)
+
+    def forward_mega(self, x, w13, w2, layer=0, route_ws=None, h3=None):
+        _fill(self.scratch, byte)
+        _fill(self.h3 if h3 is None else h3, byte)
+        if self.arena is not None and layer == 0:
+            _fill(self.arena[4096:], byte)
+        return orig["forward_mega"](self, x, w13, w2, layer, route_ws, h3)
 
     def combine(self, scores, y, y_addend=None, route_ws=None, h3=None):
         if y_addend is None or y_addend.data_ptr() != y.data_ptr():
@@ -73,8 +81,8 @@ def _poison_workspaces():
         return orig["backward"](self, x, scores, dy, w13, w2, dx, dw13, dw2, dscores, layer,
                                 flags, route_ws, h3, prepared)
 
-    for n, f in (("route", route), ("forward", forward), ("combine", combine),
-                 ("forward_fused", forward_fused), ("backward", backward)):
+    for n, f in (("route", route), ("forward", forward), ("forward_mega", forward_mega),
+                 ("combine", combine), ("forward_fused", forward_fused), ("backward", backward)):
         setattr(M, n, f)
     print(f"[poison] workspaces and outputs filled with 0x{byte:02X} before each call", flush=True)
     yield
