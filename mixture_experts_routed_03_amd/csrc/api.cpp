@@ -172,6 +172,17 @@ static void use_hot(moe_plan_s* p, void* ws, FwdArgs& a, int mode /* 0: W13, 1: 
 }
 
 
+// BF16 weight gradients: experts with at least kHotWgRows rows take the
+// 256 x 256 tiles of k_wgrad_hot unless the plan keeps every expert on the
+// streaming tiles (hot_tiles = never) or no call can have such an expert
+// (launch_wgrad also requires bf16 dW, no accumulation and widths that are
+// multiples of 256).
+static void hot_wgrad(const moe_plan_s* p, void* ws, BwdArgs& a) {
+  if (p->d.prec != MOE_PREC_BF16 || p->d.hot_tiles == 2 || p->R_max < kHotWgRows) return;
+  a.cst = at<int32_t>(ws, p->rl.cwoff);
+  a.hot_wg = 1;
+}
+
 // Split-K arguments of a BF16/FP32 forward GEMM launch (mode 0: W13, 1: W2).
 static void set_split(const moe_plan_s* p, FwdArgs& a, int mode, char* sc) {
   a.ksplit = mode == 0 ? p->ks13 : p->ks2;
@@ -444,11 +455,12 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   L.poffsets = o; o = a256(o + 4 * (E + 1));
   L.mtoff = o; o = a256(o + 4 * (E + 1));
   L.gtoff = o; o = a256(o + 4 * (E + 1));
-  // cstoff, ctoff, hotoff: one region, written by routing as split[3][E + 1]
+  // cstoff, ctoff, hotoff, cwoff: one region, written by routing as split[4][E + 1]
   L.cstoff = o;
   L.ctoff = o + 4 * (E + 1);
   L.hotoff = o + 8 * (E + 1);
-  o = a256(o + 12 * (E + 1));
+  L.cwoff = o + 12 * (E + 1);
+  o = a256(o + 16 * (E + 1));
   L.chunk_hist = o; o = a256(o + 4 * L.nchunks * E);
   L.chunk_flags = o; o = a256(o + 4 * L.nchunks);
   L.sorted_route = o; o = a256(o + 4 * R);
@@ -572,6 +584,13 @@ moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
                   "  experts with >= %d rows: 256 x 256 MFMA forward tiles %s%s\n", kHotRows,
                   kHot[d.hot_tiles], p->hot ? "" : " (not with this shape)");
     s += line;
+    if (d.training && d.hot_tiles != 2 && p->R_max >= kHotWgRows) {
+      std::snprintf(line, sizeof line,
+                    "  experts with >= %d rows: 256 x 256 MFMA weight-gradient tiles "
+                    "(bf16 dW, widths multiples of 256)\n",
+                    kHotWgRows);
+      s += line;
+    }
   }
   std::snprintf(line, sizeof line, "  route_ws   %10.2f MiB per layer (metadata + planner record)\n",
                 mib(p->rl.total));
@@ -942,6 +961,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   BwdArgs bw2{hdr, offsets, mtoff, nullptr, nullptr, dh3, h2, g->dw2, nullptr,
               0, 0, d.f, d.d, d.e, 0, d.f, d.d};
   bw2.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
+  hot_wgrad(p, ws, bw2);
   e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(dw_f32, 2, bw2, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs b13{hdr, offsets, gtoff, w->w13, dh1, nullptr, nullptr, dxr, nullptr,
@@ -957,6 +977,7 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   BwdArgs bw13{hdr, offsets, mtoff, nullptr, nullptr, dh1, sc + p->sl.x_rows, g->dw13, nullptr,
                0, 0, d.f, d.d, d.e, 0, d.d, 2 * d.f};
   bw13.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
+  hot_wgrad(p, ws, bw13);
   e = timed(p, "w13_wgrad", s, [&] { return launch_wgrad(dw_f32, 13, bw13, cus, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = timed(p, "dx_reduce", s, [&] {

@@ -34,6 +34,14 @@ __host__ __device__ inline int gemm_tile_rows(int c) { return c > kBM ? kBMX : k
 constexpr int kHotRows = 256;
 constexpr int kBMH = 256;         // token rows of a hot-expert m-tile
 __host__ __device__ inline bool hot_expert(int c) { return c >= kHotRows; }
+// BF16 weight gradients: an expert with at least kHotWgRows rows runs on
+// k_wgrad_hot's 256 x 256 tiles, the others on k_gemm_wgrad's streaming
+// tiles.  Measured on MI355X: with 32 stages of 64 rows per tile (2,048-row
+// experts) the large tiles took the W13 weight gradient from 0.90 to 0.81 ms;
+// with 4-5 stages (256-row experts) they made the W2 one slower (0.65 to
+// 0.72 ms), the tile's output stores weighing as much as its multiplies.
+constexpr int kHotWgRows = 512;
+__host__ __device__ inline bool hot_wgrad_expert(int c) { return c >= kHotWgRows; }
 
 // ------------------------------------------------- per-layer planner record
 // Written on the device by the planner kernel during forward, read by every
@@ -83,8 +91,9 @@ struct RouteLayout {
   // completion counter per expert (uint32, zeroed before each fused call)
   int64_t msync;
   // BF16 forward split: the cold experts' 64-row stage and m-tile prefixes
-  // (hot experts count 0) and the hot experts' 256-row m-tile prefix
-  int64_t cstoff, ctoff, hotoff;
+  // (hot experts count 0) and the hot experts' 256-row m-tile prefix; BF16
+  // WGRAD split: the 64-row stage prefix of the experts below kHotWgRows rows
+  int64_t cstoff, ctoff, hotoff, cwoff;
   int64_t nchunks;
 };
 
@@ -158,6 +167,12 @@ struct BwdArgs {
   int acc_dw;           // WGRAD: 1 = dW += result (fp32 sum, rounded once), 0 = dW = result
   float limit;          // W2 DGRAD: clamped SwiGLU limit (+inf: plain)
   const int32_t* row_slot;  // W13 DGRAD: dXr row r goes to slot row_slot[r] (the route t*K+k)
+  // WGRAD with hot_wg = 1 (bf16 dW, no accumulation, a_ld and b_ld multiples
+  // of 256): experts of kHotWgRows rows or more run on k_wgrad_hot's 256 x 256
+  // tiles; cst = routing's 64-row stage prefix of the other experts (those
+  // count 0)
+  const int32_t* cst;
+  int hot_wg;
 };
 
 // Arguments of the MXFP8 grouped GEMM launches.
@@ -381,11 +396,6 @@ __device__ __forceinline__ void wgrad_tile(int i, int NA, int NB, bool hot, bool
 // Number of XCDs of the MI355X; workgroups are dispatched round-robin over them.
 constexpr int kXcds = 8;
 
-// Per-XCD work queue of a persistent GEMM launch (RouteHdr::wq): the
-// workgroups of an XCD take that XCD's items in order, each the next free one
-// when it is ready, so items that share a weight tile (the m-tiles of one
-// expert and n-tile) run side by side even when item costs differ.  Called by
-// one thread of the workgroup.
 // The XCD (accelerator complex die) this workgroup runs on, read from the
 // hardware register XCC_ID (bits [3:0]) rather than assumed from blockIdx.
 __device__ __forceinline__ int hw_xcd() {
@@ -394,6 +404,11 @@ __device__ __forceinline__ int hw_xcd() {
   return int(v % kXcds);
 }
 
+// Per-XCD work queue of a persistent GEMM launch (RouteHdr::wq): the
+// workgroups of an XCD take that XCD's items in order, each the next free one
+// when it is ready, so items that share a weight tile (the m-tiles of one
+// expert and n-tile) run side by side even when item costs differ.  Called by
+// one thread of the workgroup.
 __device__ __forceinline__ int wq_take(const RouteHdr* hdr, int xcd) {
   return int(atomicAdd(const_cast<uint32_t*>(&hdr->wq[xcd]), 1u));
 }

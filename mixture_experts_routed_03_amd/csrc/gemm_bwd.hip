@@ -60,6 +60,8 @@ namespace moe {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
 
 __device__ __forceinline__ void mfma_bf16(f32x16& acc, u32x4 a, u32x4 b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -385,8 +387,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
-  const int first = xcd_first_item(a.mtoff, a.E, per_e, xcd);
-  const int last = xcd_first_item(a.mtoff, a.E, per_e, xcd + 1);
+  // with hot_wg the experts of kHotWgRows rows or more are k_wgrad_hot's:
+  // split by the cold experts' stages (theirs count 0, plus 1 per item)
+  const int32_t* cost = a.hot_wg ? a.cst : a.mtoff;
+  const int first = xcd_first_item(cost, a.E, per_e, xcd);
+  const int last = xcd_first_item(cost, a.E, per_e, xcd + 1);
   const uint16_t* asrc = reinterpret_cast<const uint16_t*>(a.arows);
   const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(a.grad);
 
@@ -396,13 +401,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
   // Work items of this workgroup: w = first + slot + i * per below last.
   int wcur = first + slot;
   auto fill = [&](Item& t) {
-    if (wcur >= last) {
-      t.e = -1;
-      return;
+    int e = 0;
+    for (;;) {   // with hot_wg, step over the hot experts' items
+      if (wcur >= last) {
+        t.e = -1;
+        return;
+      }
+      e = wcur / per_e;
+      if (!a.hot_wg || !hot_wgrad_expert(a.offsets[e + 1] - a.offsets[e])) break;
+      wcur += ((e + 1) * per_e - wcur + per - 1) / per * per;
     }
     const int w = wcur;
     wcur += per;
-    const int e = w / per_e;
     t.e = e;
     t.r0 = a.offsets[e];
     t.Me = a.offsets[e + 1] - t.r0;
@@ -533,6 +543,250 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------ WGRAD, hot experts
+// An expert with at least kHotWgRows rows contracts its weight gradient over
+// hundreds to thousands of token rows: MFMA-bound work ("Mixture of Experts:
+// How Routing Becomes GPU Computation", section 1 arithmetic intensity), for
+// which the 128 x 256 streaming tile (one stage in flight, 4 MFMAs per wave
+// per 16-row step) is the wrong shape.  Here a work item is a 256 x 256 dW
+// tile: eight waves, wave (wa, wb) owning dW rows 128 wb .. + 127 and
+// columns 64 wa .. + 63 as 4 x 2 fp32 accumulators of
+// v_mfma_f32_32x32x16_bf16 (8 MFMAs per wave per 16-row step).  A stage is
+// 64 token rows of both operands (256 columns each, 512-byte rows: 64 KiB),
+// moved by the gfx950 direct global-to-LDS load (global_load_lds_dwordx4: a
+// wave instruction fills two 512-byte LDS rows, each lane fetching the
+// global chunk that the row's XOR swizzle puts at its slot), into one of two
+// LDS buffers while the other multiplies; the operands are read in MFMA
+// layout with ds_read_b64_tr_b16 as in k_gemm_wgrad.  Token rows past the
+// expert's end are loaded clamped and their B rows zeroed in LDS before the
+// last stage multiplies, so they add nothing.  The tile is staged through
+// LDS in four passes of 64 rows and written as whole 512-byte row segments,
+// non-temporally.  Items: the hot experts' tiles, split over the XCDs by
+// their 64-row stage counts, 4 x 8 blocks of tiles where the grid allows
+// (wgrad_tile); k_gemm_wgrad skips these experts (BwdArgs::hot_wg).
+template <int TAG>
+__global__ __launch_bounds__(512, 1) void k_wgrad_hot(BwdArgs a) {
+  constexpr int kOp = 64 * 512;   // one operand's stage: 64 token rows x 256 columns
+  constexpr int kPitch = 512 + 16;   // output-staging row (bf16), padded
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * kOp];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * kOp];
+  static_assert(64 * kPitch <= 2 * kOp, "a 64-row output pass fits one buffer");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wa = wave & 3;    // 64-column block of the tile
+  const int wb = wave >> 2;   // 128-row block of the tile
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int tr_row = 8 * lh + ((lane & 15) >> 2);
+  const int tr_c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_byte = 8 * (lane & 1);
+
+  const int a_ld = a.a_ld, b_ld = a.b_ld;
+  const int NA = a_ld / 256, NB = b_ld / 256;
+  const int per_e = NA * NB;
+  // hot experts' 64-row stages before expert e (routing's cold prefix counts them 0)
+  auto hs = [&](int e) { return a.mtoff[e] - a.cst[e]; };
+  const int E = a.E;
+  if (hs(E) == 0) return;
+  // XCD split: units (expert-major, per_e per expert) of equal total stage cost
+  auto first_unit = [&](int x) {
+    const int64_t W = int64_t(per_e) * hs(E);
+    const int64_t T = W * x / kXcds;
+    int lo = 0, hi = E;   // the largest e with per_e * hs(e) <= T
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (int64_t(per_e) * hs(mid) <= T)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    if (lo >= E) return E * per_e;
+    const int64_t c = hs(lo + 1) - hs(lo);   // >= 1: lo is the largest such e
+    const int64_t i = (T - int64_t(per_e) * hs(lo) + c - 1) / c;
+    return int(min(int64_t(lo) * per_e + i, int64_t(E) * per_e));
+  };
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per = gridDim.x / kXcds;
+  const int first = first_unit(xcd), last = first_unit(xcd + 1);
+  const char* asrc = reinterpret_cast<const char*>(a.arows);
+  const char* bsrc = reinterpret_cast<const char*>(a.grad);
+  // loader roles: waves 0-3 fill the A stage, 4-7 the B stage; wave v & 3
+  // covers stage rows 16 (v & 3) .. + 15, instruction i rows 2 i, 2 i + 1 of
+  // those (lanes 0-31 / 32-63), lane slot chunk lane & 31
+  const bool aload = wave < 4;
+  const int vq = wave & 3;
+  const int ldr = 16 * vq + lh;        // stage row of instruction 0 (+ 2 i)
+  const int lchunk = lane & 31;
+
+  // this workgroup's units are w0, w0 + per, ...: the first of them, from
+  // w on, that belongs to a hot expert (last: none)
+  auto next_hot = [&](int w) {
+    while (w < last) {
+      const int e = w / per_e;
+      if (hot_wgrad_expert(a.offsets[e + 1] - a.offsets[e])) return w;
+      // the next hot expert (the smallest e2 > e with hot stages)
+      const int h1 = hs(e + 1);
+      int lo = e + 1, hi = E;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (hs(mid + 1) > h1)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      if (lo >= E) return last;
+      w += (lo * per_e - w + per - 1) / per * per;
+    }
+    return last;
+  };
+  struct Item {
+    int e, ta, tb, Me, S;
+    const char* gbase;   // this lane's operand (A or B) at the tile's first token row
+    int64_t ld2;         // its row pitch in bytes
+  };
+  auto decode = [&](int w, Item& t) {
+    const int e = w / per_e;
+    const int r0 = a.offsets[e];
+    t.e = e;
+    t.Me = a.offsets[e + 1] - r0;
+    t.S = (t.Me + 63) / 64;
+    wgrad_tile(w - e * per_e, NA, NB, true, false, t.ta, t.tb);
+    t.gbase = aload ? asrc + (int64_t(r0) * a_ld + t.ta * 256) * 2
+                    : bsrc + (int64_t(r0) * b_ld + t.tb * 256) * 2;
+    t.ld2 = int64_t(aload ? a_ld : b_ld) * 2;
+  };
+  auto issue = [&](const Item& t, char* buf, int s) {
+    char* dst = buf + (aload ? 0 : kOp) + 16 * vq * 512;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = ldr + 2 * i;                      // stage row
+      const int m = min(64 * s + k, t.Me - 1);         // token row, clamped
+      const int gc = lchunk ^ ((k & 3) << 2);          // global chunk at this slot
+      __builtin_amdgcn_global_load_lds((gbl_void*)(t.gbase + int64_t(m) * t.ld2 + gc * 16),
+                                       (lds_void*)(dst + i * 1024), 16, 0, 0);
+    }
+  };
+
+  Item cur, nxt;
+  int w = next_hot(first + slot);
+  bool pre = false;   // stage 0 of cur already issued into lds1
+  while (w < last) {
+    decode(w, cur);
+    const int S = cur.S;
+    const int tail = cur.Me - 64 * (S - 1);   // live rows of the last stage
+    // zero the B rows of the last stage past the expert's end (after its loads landed)
+    auto zero_tail = [&](char* buf) {
+      char* bb = buf + kOp;
+      for (int i = tid; i < (64 - tail) * 32; i += 512)
+        *reinterpret_cast<u32x4*>(bb + (tail + i / 32) * 512 + (i % 32) * 16) = u32x4{0u, 0u, 0u, 0u};
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    auto compute = [&](const char* buf) {
+      const char* la = buf;
+      const char* lb = buf + kOp;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 av[2], bv[4];
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          const int ch = 8 * wa + 4 * aa + tr_c;
+          const u32x2 lo = lds_read_tr16(la + wsw(16 * q + tr_row, ch) + tr_byte);
+          const u32x2 hi = lds_read_tr16(la + wsw(16 * q + tr_row + 4, ch) + tr_byte);
+          av[aa] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int ch = 16 * wb + 4 * bb + tr_c;
+          const u32x2 lo = lds_read_tr16(lb + wsw(16 * q + tr_row, ch) + tr_byte);
+          const u32x2 hi = lds_read_tr16(lb + wsw(16 * q + tr_row + 4, ch) + tr_byte);
+          bv[bb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa) mfma_bf16(acc[bb][aa], av[aa], bv[bb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // stage s multiplies from one buffer while stage s + 1 streams into the
+    // other; each step ends when this wave's loads have landed and every
+    // wave is past its MFMAs (the last stage's tail rows are zeroed between).
+    // Stage 0 sits in lds1 when the previous item prefetched it.
+    char* b0 = pre ? lds1 : lds0;
+    char* b1 = pre ? lds0 : lds1;
+    if (!pre) issue(cur, b0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (S == 1 && tail < 64) {
+      zero_tail(b0);
+      __syncthreads();
+    }
+    for (int s = 0; s < S; ++s) {
+      char* cb = (s & 1) ? b1 : b0;
+      char* nb = (s & 1) ? b0 : b1;
+      if (s + 1 < S) issue(cur, nb, s + 1);
+      compute(cb);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (s + 2 == S && tail < 64) {
+        zero_tail(nb);
+        __syncthreads();
+      }
+    }
+    // the next item's first stage streams into lds1 while this tile is
+    // staged out through lds0 (both free after the last barrier)
+    const int wn = next_hot(w + per);
+    pre = wn < last;
+    if (pre) {
+      decode(wn, nxt);
+      issue(nxt, lds1, 0);
+    }
+
+    // acc[bb][aa][v] = dW[b = tb*256 + 128 wb + 32 bb + lr]
+    //                    [a = ta*256 + 64 wa + 32 aa + 8 (v/4) + 4 lh + v%4],
+    // staged in four passes of 64 rows through lds0
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) +
+                  (int64_t(cur.e) * b_ld + int64_t(cur.tb) * 256) * a_ld + cur.ta * 256;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int r = 128 * wb + 32 * bb;   // first tile row of this accumulator row block
+        if (r / 64 != h) continue;
+        const int rl = r + lr - 64 * h;
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          uint16_t* rowp = reinterpret_cast<uint16_t*>(lds0 + rl * kPitch) + 64 * wa + 32 * aa + 4 * lh;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            store4<uint16_t>(rowp + 8 * g4, acc[bb][aa][4 * g4], acc[bb][aa][4 * g4 + 1],
+                             acc[bb][aa][4 * g4 + 2], acc[bb][aa][4 * g4 + 3]);
+        }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {   // 64 rows x 32 chunks of 16 bytes
+        const int i = tid + 512 * j;
+        const int rl = i / 32, cc = i % 32;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds0 + rl * kPitch + cc * 16);
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4*>(o + int64_t(rl + 64 * h) * a_ld + cc * 8));
+      }
+      lds_barrier();
+    }
+    w = wn;
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 // Resident workgroups per CU of one kernel (queried once per kernel).
 template <int ID, typename K>
@@ -568,9 +822,14 @@ hipError_t launch_dgrad(int kind, const BwdArgs& a, int64_t mt_max, int cus, hip
 
 // dW[e] = B_e^T A_e for every expert (a.acc_dw: dW[e] += it); dw_f32 selects
 // the dW storage type; tag names the launch (2: dW2, 13: dW13).
-hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s) {
-  const int64_t items = int64_t(a.E) * ((a.a_ld + 255) / 256) * (a.b_ld / 128);
+hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& args, int cus, hipStream_t s) {
+  const int64_t items = int64_t(args.E) * ((args.a_ld + 255) / 256) * (args.b_ld / 128);
   if (items == 0) return hipSuccess;
+  // the hot experts go to k_wgrad_hot only where it applies; otherwise every
+  // expert stays on k_gemm_wgrad
+  BwdArgs a = args;
+  a.hot_wg = (args.hot_wg && args.cst && !dw_f32 && !args.acc_dw && args.a_ld % 256 == 0 &&
+              args.b_ld % 256 == 0) ? 1 : 0;
 #define MOE_WG(TW, TAG, ACC, ID)                                                                \
   do {                                                                                        \
     const unsigned g =                                                                        \
@@ -592,6 +851,13 @@ hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStrea
     }
   }
 #undef MOE_WG
+  if (a.hot_wg) {   // the hot experts' 256 x 256 tiles
+    const unsigned g = persistent_grid(1, int64_t(cus), cus);
+    if (tag == 2)
+      hipLaunchKernelGGL(k_wgrad_hot<2>, dim3(g), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_wgrad_hot<13>, dim3(g), dim3(512), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -88,8 +88,9 @@ constexpr int kScanBatch = 16;
 // expert with s rows: rows (offsets), rows rounded up to 32 (poffsets),
 // 64-row stages (mtoff), FPROP/DGRAD m-tiles (gtoff), then the BF16 forward
 // split: stages and m-tiles of cold experts (cstoff, ctoff) and 256-row
-// m-tiles of hot experts (hotoff).
-constexpr int kScans = 7;
+// m-tiles of hot experts (hotoff), then the BF16 WGRAD split: stages of the
+// experts below kHotWgRows rows (cwoff).
+constexpr int kScans = 8;
 __device__ __forceinline__ void scan_terms(int s, int* v) {
   const bool hot = hot_expert(s);
   v[0] = s;
@@ -99,6 +100,7 @@ __device__ __forceinline__ void scan_terms(int s, int* v) {
   v[4] = hot ? 0 : v[2];
   v[5] = hot ? 0 : v[3];
   v[6] = hot ? (s + kBMH - 1) / kBMH : 0;
+  v[7] = hot_wgrad_expert(s) ? 0 : v[2];
 }
 
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
       mtoff[e] = o[2];
       gtoff[e] = o[3];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) split[j * (E + 1) + e] = o[4 + j];
+      for (int j = 0; j < kScans - 4; ++j) split[j * (E + 1) + e] = o[4 + j];
       // chunk histograms -> row base of each (chunk, expert)
       int run = oc;
       for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     mtoff[E] = carry[2];
     gtoff[E] = carry[3];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) split[j * (E + 1) + E] = carry[4 + j];
+    for (int j = 0; j < kScans - 4; ++j) split[j * (E + 1) + E] = carry[4 + j];
     hdr->T = T;
     hdr->R = carry[0];
     hdr->Rpad = carry[1];
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
       mtoff[e] = o[2];
       gtoff[e] = o[3];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) split[j * (E + 1) + e] = o[4 + j];
+      for (int j = 0; j < kScans - 4; ++j) split[j * (E + 1) + e] = o[4 + j];
       cnt[e] = oc;
     }
     __syncthreads();   // every thread has read the carries of this pass
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
     mtoff[E] = carry[2];
     gtoff[E] = carry[3];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) split[j * (E + 1) + E] = carry[4 + j];
+    for (int j = 0; j < kScans - 4; ++j) split[j * (E + 1) + E] = carry[4 + j];
     hdr->T = T;
     hdr->R = carry[0];
     hdr->Rpad = carry[1];
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
         mtoff[e] = run[2];
         gtoff[e] = run[3];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) split[j * (E + 1) + e] = run[4 + j];
+        for (int j = 0; j < kScans - 4; ++j) split[j * (E + 1) + e] = run[4 + j];
       }
       pre[e] += run[0];   // this chunk's first row of expert e
       int v[kScans];
@@ -503,7 +505,7 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
       mtoff[E] = run[2];
       gtoff[E] = run[3];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) split[j * (E + 1) + E] = run[4 + j];
+      for (int j = 0; j < kScans - 4; ++j) split[j * (E + 1) + E] = run[4 + j];
       hdr->T = T;
       hdr->R = run[0];
       hdr->Rpad = run[1];

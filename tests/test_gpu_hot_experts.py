@@ -15,6 +15,7 @@ from tests._harness import (TOL, banner, check_route, make_inputs, oracle_forwar
 pytestmark = pytest.mark.gpu
 
 HOT = 256   # rows from which an expert takes the large tiles
+HOT_WG = 512   # rows from which its BF16 weight gradients take them
 
 
 @pytest.fixture(scope="module")
@@ -189,3 +190,37 @@ def test_tile_modes_agree(B):
     torch.cuda.synchronize()
     assert torch.equal(ys["auto"], ys["never"])
     assert om.max_abs_rel(ys["always"].float(), ys["never"].float()) < 1e-2
+
+
+@pytest.mark.parametrize("T,D,F,E,K,zipf", [
+    (1200, 512, 256, 5, 2, 1.0),    # 865 and 574 rows on the 256 x 256 tiles; 413, 301, 247 streaming
+    (1500, 256, 384, 6, 3, 1.2),    # dW13 of four experts on them; dW2 (rows of F = 384 values) streaming
+    (2000, 512, 256, 3, 1, None),   # every expert on them, ~670 rows (last stage partly past the end)
+])
+def test_hot_weight_gradient_tiles_equal_streaming(B, T, D, F, E, K, zipf):
+    """BF16 weight gradients of experts with 512+ rows run on 256 x 256
+    tiles (k_wgrad_hot) in automatic mode, those of smaller experts and the
+    forward of these small calls on the streaming tiles; "never" keeps every
+    weight gradient on the streaming tiles.  Both contract the same token
+    rows in the same 16-row MFMA steps, so every gradient is bit-identical;
+    against the oracle within the BF16 bound."""
+    banner(f"hot weight-gradient tiles T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
+    lay = make_inputs(T, D, F, E, K, "bf16", zipf=zipf, seed=T + 31, training=True)
+    counts = _counts(lay, E)
+    assert counts.max() >= HOT_WG
+    outs = {}
+    for mode in ("auto", "never"):
+        layer = B.MoeLayer(T, D, F, E, K, "bf16", training=True, hot_tiles=mode)
+        outs[mode] = [t.clone() for t in run_train(layer, lay)]
+        torch.cuda.synchronize()
+        assert layer.status() == (0, 0)
+    for name, u, v in zip(("y", "dx", "dw13", "dw2", "ds"), outs["auto"], outs["never"]):
+        assert torch.equal(u, v), name
+    _, cache = om.forward(lay["x"], lay["ids"], lay["scores"], lay["w13"].cpu(),
+                          lay["w2"].cpu(), keep=True)
+    _, rdw13, rdw2, _ = om.backward(lay["dy"], lay["x"], lay["ids"], lay["scores"],
+                                    lay["w13"].cpu(), lay["w2"].cpu(), cache)
+    dw13, dw2 = outs["auto"][2], outs["auto"][3]
+    for e in range(E):
+        assert om.max_abs_rel(dw13[e], rdw13[e]) < TOL["bf16"], e
+        assert om.max_abs_rel(dw2[e], rdw2[e]) < TOL["bf16"], e
