@@ -87,10 +87,14 @@ SYMBOLS = {
                         "moe::k_fwd_splitk_finish<unsigned short, 1>"],
                        ["gemm_fwd.hip", "gemm_hot.hip"]),
         "mega_fwd": ("moe::k_gemm_mega<unsigned short>", ["gemm_fwd.hip"]),
+        "w2_bwd_mega": ("moe::k_bwd_mega<0, unsigned short, 0>", ["gemm_bwd.hip"]),
+        "w13_bwd_mega": ("moe::k_bwd_mega<1, unsigned short, 0>", ["gemm_bwd.hip"]),
         "w2_dgrad_swiglu": ("moe::k_gemm_dgrad<0>", ["gemm_bwd.hip"]),
         "w13_dgrad": ("moe::k_gemm_dgrad<1>", ["gemm_bwd.hip"]),
-        "w2_wgrad": ("moe::k_gemm_wgrad<unsigned short, 2, 0>", ["gemm_bwd.hip"]),
-        "w13_wgrad": ("moe::k_gemm_wgrad<unsigned short, 13, 0>", ["gemm_bwd.hip"]),
+        "w2_wgrad": (["moe::k_gemm_wgrad<unsigned short, 2, 0>", "moe::k_wgrad_hot<2>"],
+                     ["gemm_bwd.hip"]),
+        "w13_wgrad": (["moe::k_gemm_wgrad<unsigned short, 13, 0>", "moe::k_wgrad_hot<13>"],
+                      ["gemm_bwd.hip"]),
     },
     "mxfp8": {
         "w13_swiglu": ("moe::k_mx_fwd<0, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
@@ -123,7 +127,8 @@ def parse():
                          "for the precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pipeline", choices=("staged", "mega"), default="staged",
-                    help="BF16 expert forward: two launches (W13, W2) or one fused (Mega) launch")
+                    help="expert forward: two launches (W13, W2) or one fused (Mega) launch; "
+                         "BF16 training: also the fused backward (one launch per projection)")
     ap.add_argument("--width", type=int, default=0,
                     help="expert width F for a width sweep (default: the workload's F; "
                          "a multiple of 128)")
@@ -185,6 +190,11 @@ def alg_bytes(name, m):
             "w2_wgrad": ne * D * F * dwb + R * D * es + R * F * es,
             "w13_dgrad": w13 + R * 2 * F * es + R * D * 4,
             "w13_wgrad": ne * 2 * F * D * dwb + R * 2 * F * es + R * D * es,
+            # fused backward: the h2 rows W2 DGRAD rebuilds are read back from
+            # L2; dH1 and the x rows are counted once
+            "w2_bwd_mega": (w2 + R * D * es + 2 * R * 2 * F * es + R * F * es
+                            + ne * D * F * dwb),
+            "w13_bwd_mega": w13 + R * 2 * F * es + R * D * 4 + ne * 2 * F * D * dwb + R * D * es,
         }.get(name)
     return {
         "quant_x": T * D * 2 + q(R * D),
@@ -220,6 +230,10 @@ def kernel_flops(name, m):
         return 2 * R * 2 * F * D
     if name == "mega_fwd":
         return 6 * R * D * F
+    if name == "w2_bwd_mega":
+        return 4 * R * D * F
+    if name == "w13_bwd_mega":
+        return 8 * R * D * F
     if name in ("w2_scatter", "w2_fused", "w2_dgrad_swiglu", "w2_wgrad"):
         return 2 * R * D * F
     return None
@@ -371,6 +385,8 @@ def setup(args, dev):
 
     fused = args.workload == "bf16_fwd_fused"
     y32 = torch.empty((T, D), dtype=torch.float32, device=dev) if fused else None
+    # the fused backward exists for BF16 plans
+    bwd_flags = B.BWD_MEGA if args.pipeline == "mega" and cfg.prec == "bf16" else 0
 
     def step():
         if fused:
@@ -389,7 +405,7 @@ def setup(args, dev):
         layer.combine(lay["scores"], y, y_addend=ysh if shared is not None else None)
         if training:
             layer.backward(lay["x"], lay["scores"], lay["dy"], lay["w13"], lay["w2"], dx, dw13,
-                           dw2, dsc)
+                           dw2, dsc, flags=bwd_flags)
             if shared is not None:
                 shared.backward(lay["x"], sh_sc, lay["dy"], lay["w13_shared"], lay["w2_shared"],
                                 dx, dws13, dws2, None, flags=B.BWD_ACCUMULATE_DX)
@@ -603,7 +619,9 @@ def main():
                                + (", + shared BF16 expert" if cfg.shared_expert else "")
                                + (f", SwiGLU clamped at {cfg.swiglu_limit:g}"
                                   if cfg.swiglu_limit else "")
-                               + (", fused (Mega) forward" if args.pipeline == "mega" else ""),
+                               + ((", fused (Mega) forward and backward"
+                                   if training and prec == "bf16" else ", fused (Mega) forward")
+                                  if args.pipeline == "mega" else ""),
                    "routes_per_layer": [m["R"] for lab, m in metas if lab == ""],
                    "nonempty_experts": [m["ne"] for lab, m in metas if lab == ""],
                    "max_rows": max(m["max_rows"] for lab, m in metas if lab == ""),

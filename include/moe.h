@@ -82,7 +82,8 @@ typedef enum moe_dtype {
 #define MOE_STATUS_PAD_SCORE  0x2u  /* nonzero score on an id -1 route: ignored */
 #define MOE_STATUS_ARENA      0x4u  /* backward of a layer whose forward state is gone */
 #define MOE_STATUS_NULL_INPUT 0x8u  /* null x/scores/dy for a call with rows: rows skipped */
-#define MOE_STATUS_SYNC_TIMEOUT 0x10u /* fused forward: a W2 tile stopped waiting for its h2 rows */
+#define MOE_STATUS_SYNC_TIMEOUT 0x10u /* fused forward or backward: a record stopped waiting
+                                         for the rows it reads */
 
 /* moe_expert_bwd flags */
 #define MOE_BWD_ACCUMULATE_DX 0x1u  /* dx += result instead of dx = result */
@@ -93,6 +94,14 @@ typedef enum moe_dtype {
  * and rounded once to the dW type; experts with no rows keep their values.
  * dW is then read as well as written. */
 #define MOE_BWD_ACCUMULATE_DW 0x2u
+/* The fused (Mega) backward of the Dist-MoE explainer, section 05: each
+ * projection's DGRAD and WGRAD work records run in one persistent grid, each
+ * expert's DGRAD tile range next to its WGRAD range (two launches: W2, then
+ * W13).  Results are bit-identical to the staged backward (the same tiles,
+ * summed in the same order).  BF16 plans only (MXFP8: MOE_ERR_UNSUPPORTED).
+ * The W2 launch's dW2 records wait, bounded, for the h2 rows its DGRAD
+ * records rebuild; a wait that runs out sets MOE_STATUS_SYNC_TIMEOUT. */
+#define MOE_BWD_MEGA 0x4u
 
 /* Layer description.  Supported: D % 128 == 0, F % 128 == 0, D and F at
  * most 65,536, 1 <= K <= 16, 1 <= E <= 4096, 0 <= t_max <= 2^24 / K (else
@@ -334,7 +343,8 @@ moe_status moe_expert_fwd_fused_noalloc(moe_plan_t plan, void* route_ws, const v
  * gradients into g->dx.  Rebuilds the layer's state first when its forward
  * replayed.  Layers of a step must run in reverse forward order; each
  * backward rewinds the arena cursor to its layer's start. */
-/* flags: MOE_BWD_ACCUMULATE_DX | MOE_BWD_ACCUMULATE_DW; other bits -> MOE_ERR_ARG. */
+/* flags: MOE_BWD_ACCUMULATE_DX | MOE_BWD_ACCUMULATE_DW | MOE_BWD_MEGA; other bits ->
+ * MOE_ERR_ARG. */
 moe_status moe_expert_bwd(moe_plan_t plan, int32_t layer, void* route_ws, const void* x,
                           const float* scores, const void* dy, const moe_weights* w,
                           const void* h3_slots, void* arena, void* scratch,

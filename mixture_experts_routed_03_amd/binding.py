@@ -30,6 +30,7 @@ STATUS_NULL_INPUT = 0x8
 STATUS_SYNC_TIMEOUT = 0x10
 BWD_ACCUMULATE_DX = 0x1
 BWD_ACCUMULATE_DW = 0x2
+BWD_MEGA = 0x4
 _ERRORS = {1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
            4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
 

@@ -57,6 +57,8 @@ hipError_t launch_mx_mega(const MxArgs& a13, const MxArgs& a2, uint32_t* msync, 
 hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s);
 hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStream_t s);
 hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s);
+hipError_t launch_bwd_mega(int kind, int dw_f32, const BwdArgs& dg, const BwdArgs& wg,
+                           uint32_t* tickets, uint32_t* ready, int cus, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -217,6 +219,8 @@ PlanArgs plan_args(const moe_plan_s* p, int32_t layer, int training, void* arena
 // K=6: a lookahead of 1 expert leaves W2 records waiting, 6.06 ms; 2 and 4
 // give 5.88 and 5.86 ms).
 constexpr int kMegaLook = 4;
+// Counters of the fused W2 backward: one per expert and 256-column block of F.
+inline int msync_blocks(int F) { return (F + 255) / 256; }
 
 // Arguments of the block-scaled W2 FPROP: h2 row blocks x W2 -> route slots
 // h3 (or, with y32, the FUSED combine).
@@ -465,7 +469,7 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
   L.chunk_flags = o; o = a256(o + 4 * L.nchunks);
   L.sorted_route = o; o = a256(o + 4 * R);
   L.route_to_row = o; o = a256(o + 4 * R);
-  L.msync = o; o = a256(o + 4 * (kXcds + E));
+  L.msync = o; o = a256(o + 4 * (2 * kXcds + int64_t(E) * msync_blocks(d.f)));
   L.total = o;
 
   ScratchLayout& S = p->sl;
@@ -904,9 +908,11 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
                           const void* h3, void* arena, void* scratch, const moe_grads* g,
                           uint32_t flags, hipStream_t s) {
   if (!p || !ws || !w || !g || !scratch || !h3) return MOE_ERR_ARG;
-  if (flags & ~(MOE_BWD_ACCUMULATE_DX | MOE_BWD_ACCUMULATE_DW)) return MOE_ERR_ARG;
+  if (flags & ~(MOE_BWD_ACCUMULATE_DX | MOE_BWD_ACCUMULATE_DW | MOE_BWD_MEGA)) return MOE_ERR_ARG;
   const moe_desc& d = p->d;
   if (!d.training || d.prec == MOE_PREC_F32) return MOE_ERR_UNSUPPORTED;
+  const bool mega = (flags & MOE_BWD_MEGA) != 0;
+  if (mega && d.prec != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
   if (layer < 0 || layer >= d.max_layers) return MOE_ERR_ARG;
   const bool mx = d.prec == MOE_PREC_MXFP8;
   if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;
@@ -930,8 +936,13 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   hipError_t e;
   // A layer whose forward did not run since its routing is reported and
   // rebuilt from x like a replaying layer.
+  uint32_t* msync = at<uint32_t>(ws, p->rl.msync);
   {
-    const PlanArgs pa = plan_args(p, layer, 1, arena, sc);
+    PlanArgs pa = plan_args(p, layer, 1, arena, sc);
+    if (mega) {   // the fused launches' tickets and counters
+      pa.zero = uint64_t(reinterpret_cast<uintptr_t>(msync));
+      pa.zero_n = 2 * kXcds + d.e * msync_blocks(d.f);
+    }
     e = timed(p, "plan_bwd", s, [&] { return launch_plan_enter_bwd(hdr, pa, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -956,30 +967,50 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   BwdArgs b{hdr, offsets, gtoff, w->w2, dh3, nullptr, nullptr, dh1, h2,
             d.d, d.f, d.f, d.d, d.e, (d.f + 255) / 256, 0, 0, mtoff};
   b.limit = swiglu_limit(p);
-  e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_dgrad(0, b, p->mt_max, cus, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw2{hdr, offsets, mtoff, nullptr, nullptr, dh3, h2, g->dw2, nullptr,
               0, 0, d.f, d.d, d.e, 0, d.f, d.d};
   bw2.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
-  hot_wgrad(p, ws, bw2);
-  e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(dw_f32, 2, bw2, cus, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs b13{hdr, offsets, gtoff, w->w13, dh1, nullptr, nullptr, dxr, nullptr,
               2 * d.f, d.d, d.f, d.d, d.e, (d.d + 255) / 256, 0, 0, mtoff};
   b13.row_slot = sorted_route;
-  e = timed(p, "w13_dgrad", s, [&] { return launch_dgrad(1, b13, p->mt_max, cus, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  // dW13's A rows: a packed copy of the x rows (its loads then stream)
-  e = timed(p, "gather", s, [&] {
-    return launch_gather(x, d.d, p->es, d.k, hdr, route_to_row, sc + p->sl.x_rows, d.t_max, s);
-  });
-  if (e != hipSuccess) return MOE_ERR_HIP;
   BwdArgs bw13{hdr, offsets, mtoff, nullptr, nullptr, dh1, sc + p->sl.x_rows, g->dw13, nullptr,
                0, 0, d.f, d.d, d.e, 0, d.d, 2 * d.f};
   bw13.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
-  hot_wgrad(p, ws, bw13);
-  e = timed(p, "w13_wgrad", s, [&] { return launch_wgrad(dw_f32, 13, bw13, cus, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  // dW13's A rows: a packed copy of the x rows (its loads then stream)
+  auto gather = [&] {
+    return timed(p, "gather", s, [&] {
+      return launch_gather(x, d.d, p->es, d.k, hdr, route_to_row, sc + p->sl.x_rows, d.t_max,
+                           s);
+    });
+  };
+  if (mega) {
+    // msync: [W2 tickets | one counter per expert and 256-column block of F | W13 tickets]
+    uint32_t* ready = msync + kXcds;
+    uint32_t* t13 = ready + int64_t(d.e) * msync_blocks(d.f);
+    e = timed(p, "w2_bwd_mega", s, [&] {
+      return launch_bwd_mega(0, dw_f32, b, bw2, msync, ready, cus, s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = gather();
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = timed(p, "w13_bwd_mega", s, [&] {
+      return launch_bwd_mega(1, dw_f32, b13, bw13, t13, nullptr, cus, s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  } else {
+    e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_dgrad(0, b, p->mt_max, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    hot_wgrad(p, ws, bw2);
+    e = timed(p, "w2_wgrad", s, [&] { return launch_wgrad(dw_f32, 2, bw2, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = timed(p, "w13_dgrad", s, [&] { return launch_dgrad(1, b13, p->mt_max, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = gather();
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    hot_wgrad(p, ws, bw13);
+    e = timed(p, "w13_wgrad", s, [&] { return launch_wgrad(dw_f32, 13, bw13, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   e = timed(p, "dx_reduce", s, [&] {
     return launch_dx_reduce(d.prec, hdr, route_to_row, dxr, g->dx, d.k, d.d, d.t_max,
                             (flags & MOE_BWD_ACCUMULATE_DX) ? 1 : 0, s);

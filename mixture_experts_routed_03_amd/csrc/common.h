@@ -87,8 +87,10 @@ constexpr int64_t kArenaHdrBytes = 4096;  // data region starts here
 struct RouteLayout {
   int64_t hdr, counts, offsets, poffsets, mtoff, gtoff, chunk_hist, chunk_flags,
       sorted_route, route_to_row, total;
-  // Fused (Mega) forward: kXcds work-queue tickets, then one W13-tile
-  // completion counter per expert (uint32, zeroed before each fused call)
+  // Fused (Mega) launches: kXcds work-queue tickets, completion counters
+  // (forward: W13 tiles per expert; backward: W2 DGRAD tiles per expert and
+  // 256-column block of F, E * ceil(F / 256) words), then kXcds tickets of the
+  // fused W13 backward (uint32, zeroed before each fused call)
   int64_t msync;
   // BF16 forward split: the cold experts' 64-row stage and m-tile prefixes
   // (hot experts count 0) and the hot experts' 256-row m-tile prefix; BF16

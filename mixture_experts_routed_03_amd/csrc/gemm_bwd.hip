@@ -114,13 +114,17 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 // Eight waves: 256 output columns (32 per wave) x up to 128 token rows.  A
 // 256-column tile reads 512-byte weight row segments, which HBM serves
 // faster than 256-byte ones, and shares each token stage among eight waves.
-template <int KIND>
-__global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
-  constexpr int kW = 64 * 512;       // weight stage: 64 contraction rows x 256 columns
-  constexpr int kT = kBMX * 128;     // token stage: up to 128 rows x 64 values
-  constexpr int kStage = kW + kT;
-  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
-  const int tid = threadIdx.x;
+constexpr int kDgW = 64 * 512;       // weight stage: 64 contraction rows x 256 columns
+constexpr int kDgT = kBMX * 128;     // token stage: up to 128 rows x 64 values
+constexpr int kDgStage = kDgW + kDgT;
+constexpr int kDgLds = 2 * kDgStage;
+
+// One DGRAD work item: output columns nt * 256 .. + 255 of m-tile mt of
+// expert e (mt_e m-tiles).  `between` runs when the contraction is done,
+// before the epilogue (a launch takes its next item there).
+template <int KIND, typename Between>
+__device__ __forceinline__ void dgrad_item(const BwdArgs& a, char* lds, int tid, int e, int nt,
+                                           int mt, int mt_e, Between&& between) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 31;
@@ -136,6 +140,179 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
   const int tr_chunk = 4 * wave + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_byte = 8 * (lane & 1);
 
+  const int S = a.Kd / 64;
+  const int64_t N = a.N;
+  const uint16_t* h1 = global_ptr<const uint16_t>(a.hdr->rec.h1);
+  const int bm = gemm_tile_rows(a.offsets[e + 1] - a.offsets[e]);
+  const int row0 = a.offsets[e] + mt * bm;
+  const int rows = min(bm, a.offsets[e + 1] - row0);
+  // The last tile of an N that is an odd multiple of 128 has 128 columns:
+  // the loads of its upper half re-read the lower half, and waves 4..7
+  // multiply them but store nothing.  Every load stays unconditional, so
+  // the stage loop has no branches.
+  const int ncols = min(256, int(N) - nt * 256);
+  const int wcol = c32 * 8 < ncols ? c32 * 8 : c32 * 8 - 128;
+  const uint16_t* wsrc = reinterpret_cast<const uint16_t*>(a.W) +
+                         (int64_t(e) * a.Kd + kp) * N + nt * 256 + wcol;
+  // Tile rows past the expert's last row re-read that row (outputs not stored).
+  const char* tsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    tsrc[j] = reinterpret_cast<const char*>(a.tok) +
+              int64_t(row0 + min(lrow + 64 * j, rows - 1)) * a.Kd * 2 + lc * 16;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
+  u32x4 R0[6], R1[6];
+  // NB: 32-token blocks multiplied (1, 2 or 4; one loop copy each, so no
+  // accumulator depends on a branch inside the stage loop); the token stage
+  // holds 64 rows per pass of the 512 threads (rows past the tile repeat its
+  // last row).
+  // W2 rows (the contraction of the W2 DGRAD) are F values apart, a
+  // power-of-two byte pitch at the usual widths, and the n-tiles of one
+  // expert run side by side: each starts its contraction at its own
+  // offset, nt * S / NT stages, so at any moment they read different row
+  // bands instead of the same one (the sum's order is fixed per item).
+  const int rot = KIND == 0 ? int(int64_t(nt) * S / a.NT) : 0;
+  auto load = [&](u32x4* R, int s, auto nb_c, auto tm_c) {
+    constexpr int NB = decltype(nb_c)::value;
+    constexpr bool TM = decltype(tm_c)::value;
+    s += rot;
+    if (s >= S) s -= S;
+    const uint16_t* p = wsrc + int64_t(s) * 64 * N;
+    // weights stream through once: non-temporal loads keep them from
+    // evicting the token tiles the other n-tiles of this expert re-read
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(p + 16 * i * N);
+      if constexpr (TM)
+        R[i] = *src;
+      else
+        R[i] = __builtin_nontemporal_load(src);
+    }
+#pragma unroll
+    for (int j = 0; j < (NB + 3) / 4 + (NB == 4); ++j)
+      R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
+  };
+  auto store = [&](const u32x4* R, int buf, auto nb_c) {
+    constexpr int NB = decltype(nb_c)::value;
+    char* la = lds + buf * kDgStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(la + wsw(kp + 16 * i, c32)) = R[i];
+    char* lt = la + kDgW;
+#pragma unroll
+    for (int j = 0; j < (NB + 3) / 4 + (NB == 4); ++j)
+      *reinterpret_cast<u32x4*>(lt + swz(lrow + 64 * j, lc)) = R[4 + j];
+  };
+  auto compute = [&](int buf, auto nb_c) {
+    constexpr int NB = decltype(nb_c)::value;
+    const char* la = lds + buf * kDgStage;
+    const char* lt = la + kDgW;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int g = 2 * q + lh;
+      const u32x2 lo = lds_read_tr16(la + wsw(16 * q + tr_row, tr_chunk) + tr_byte);
+      const u32x2 hi = lds_read_tr16(la + wsw(16 * q + tr_row + 4, tr_chunk) + tr_byte);
+      const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+      u32x4 bv[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) bv[b] = *reinterpret_cast<const u32x4*>(lt + swz(32 * b + lr, g));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) mfma_bf16(acc[b], av, bv[b]);
+    }
+  };
+  // Pipeline as in the forward kernels: LDS buffer 0 holds stage s, R1
+  // stage s + 1 and R0 stage s + 2 (indices past the end repeat the last).
+  auto run = [&](auto nb_c, auto tm_c) {
+    load(R0, 0, nb_c, tm_c);
+    load(R1, min(1, S - 1), nb_c, tm_c);
+    store(R0, 0, nb_c);
+    load(R0, min(2, S - 1), nb_c, tm_c);
+    lds_barrier();
+    for (int s = 0; s + 1 < S; s += 2) {
+      compute(0, nb_c);
+      store(R1, 1, nb_c);
+      load(R1, min(s + 3, S - 1), nb_c, tm_c);
+      lds_barrier();
+      compute(1, nb_c);
+      store(R0, 0, nb_c);
+      load(R0, min(s + 4, S - 1), nb_c, tm_c);
+      lds_barrier();
+    }
+    if (S & 1) {
+      compute(0, nb_c);
+      lds_barrier();
+    }
+  };
+  // An expert cut into several m-tiles re-reads its weight tiles once per
+  // m-tile; those items run side by side on one XCD, so its weights are
+  // loaded with the default (L2-allocating) policy to serve the sibling
+  // tiles from L2.  A single-tile expert streams its weights non-temporally.
+  auto go = [&](auto tm_c) {
+    if (rows > 64)
+      run(std::integral_constant<int, 4>{}, tm_c);
+    else if (rows > 32)
+      run(std::integral_constant<int, 2>{}, tm_c);
+    else
+      run(std::integral_constant<int, 1>{}, tm_c);
+  };
+  if (mt_e > 1)
+    go(std::true_type{});
+  else
+    go(std::false_type{});
+  between();
+
+  // acc[b][v]: output column 32*wave + 8*(v/4) + 4*lh + v%4, token 32*b + lr
+  const int col = nt * 256 + 32 * wave + 4 * lh;
+#pragma unroll
+  for (int b = 0; b < 4 && 32 * wave < ncols; ++b) {
+    const int m = 32 * b + lr;
+    if (m >= rows) continue;
+    const int64_t row = row0 + m;
+    if (KIND == 0) {
+      const int F = a.F;
+      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + row * (2 * F);
+      uint16_t* h2o = reinterpret_cast<uint16_t*>(a.out2);
+      const uint16_t* hr = h1 + row * (2 * F);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int j = col + 8 * g4;
+        float gv[4], uv[4], dg[4], du[4], hv[4];
+        load4_bf16(hr + j, gv);
+        load4_bf16(hr + F + j, uv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float dh2 = acc[b][4 * g4 + i];
+          // clamped SwiGLU backward: no gradient through a clamped value
+          const float L = a.limit;
+          const float gc = clamp_gate(gv[i], L), uc = clamp_up(uv[i], L);
+          const float sg = sigmoid_f(gc);
+          const float sl = silu_f(gc);
+          dg[i] = gv[i] > L ? 0.0f : dh2 * uc * (sg * (1.0f + gc * (1.0f - sg)));
+          du[i] = (uv[i] > L || uv[i] < -L) ? 0.0f : dh2 * sl;
+          hv[i] = sl * uc;
+        }
+        store4<uint16_t>(o + j, dg[0], dg[1], dg[2], dg[3]);
+        store4<uint16_t>(o + F + j, du[0], du[1], du[2], du[3]);
+        if (h2o) store4<uint16_t>(h2o + row * F + j, hv[0], hv[1], hv[2], hv[3]);
+      }
+    } else {
+      // dXr rows go to their route slots, so the input-gradient sum reads
+      // each token's K rows as one contiguous run
+      float* o = reinterpret_cast<float*>(a.out) + int64_t(a.row_slot[row]) * N;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        store4<float>(o + col + 8 * g4, acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2],
+                      acc[b][4 * g4 + 3]);
+    }
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kDgLds];
+  const int tid = threadIdx.x;
   const RouteHdr* hdr = a.hdr;
   const int xcd = blockIdx.x % kXcds;
   const int per = gridDim.x / kXcds;
@@ -143,9 +320,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
   // 64 rows); the XCDs split the items by token rows
   const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
   const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
-  const int S = a.Kd / 64;
-  const int64_t N = a.N;
-  const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
   // items [first, last) of this XCD come from its work queue, in order
   // (with skewed routing: when some expert spans several m-tiles; otherwise
@@ -162,173 +336,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;
-    const int mt = u - nt * mt_e;
-    const int bm = gemm_tile_rows(a.offsets[e + 1] - a.offsets[e]);
-    const int row0 = a.offsets[e] + mt * bm;
-    const int rows = min(bm, a.offsets[e + 1] - row0);
-    // The last tile of an N that is an odd multiple of 128 has 128 columns:
-    // the loads of its upper half re-read the lower half, and waves 4..7
-    // multiply them but store nothing.  Every load stays unconditional, so
-    // the stage loop has no branches.
-    const int ncols = min(256, int(N) - nt * 256);
-    const int wcol = c32 * 8 < ncols ? c32 * 8 : c32 * 8 - 128;
-    const uint16_t* wsrc = reinterpret_cast<const uint16_t*>(a.W) +
-                           (int64_t(e) * a.Kd + kp) * N + nt * 256 + wcol;
-    // Tile rows past the expert's last row re-read that row (outputs not stored).
-    const char* tsrc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      tsrc[j] = reinterpret_cast<const char*>(a.tok) +
-                int64_t(row0 + min(lrow + 64 * j, rows - 1)) * a.Kd * 2 + lc * 16;
-
-    f32x16 acc[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
-    u32x4 R0[6], R1[6];
-    // NB: 32-token blocks multiplied (1, 2 or 4; one loop copy each, so no
-    // accumulator depends on a branch inside the stage loop); the token stage
-    // holds 64 rows per pass of the 512 threads (rows past the tile repeat its
-    // last row).
-    // W2 rows (the contraction of the W2 DGRAD) are F values apart, a
-    // power-of-two byte pitch at the usual widths, and the n-tiles of one
-    // expert run side by side: each starts its contraction at its own
-    // offset, nt * S / NT stages, so at any moment they read different row
-    // bands instead of the same one (the sum's order is fixed per item).
-    const int rot = KIND == 0 ? int(int64_t(nt) * S / a.NT) : 0;
-    auto load = [&](u32x4* R, int s, auto nb_c, auto tm_c) {
-      constexpr int NB = decltype(nb_c)::value;
-      constexpr bool TM = decltype(tm_c)::value;
-      s += rot;
-      if (s >= S) s -= S;
-      const uint16_t* p = wsrc + int64_t(s) * 64 * N;
-      // weights stream through once: non-temporal loads keep them from
-      // evicting the token tiles the other n-tiles of this expert re-read
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(p + 16 * i * N);
-        if constexpr (TM)
-          R[i] = *src;
-        else
-          R[i] = __builtin_nontemporal_load(src);
-      }
-#pragma unroll
-      for (int j = 0; j < (NB + 3) / 4 + (NB == 4); ++j)
-        R[4 + j] = *reinterpret_cast<const u32x4*>(tsrc[j] + int64_t(s) * 128);
-    };
-    auto store = [&](const u32x4* R, int buf, auto nb_c) {
-      constexpr int NB = decltype(nb_c)::value;
-      char* la = lds + buf * kStage;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(la + wsw(kp + 16 * i, c32)) = R[i];
-      char* lt = la + kW;
-#pragma unroll
-      for (int j = 0; j < (NB + 3) / 4 + (NB == 4); ++j)
-        *reinterpret_cast<u32x4*>(lt + swz(lrow + 64 * j, lc)) = R[4 + j];
-    };
-    auto compute = [&](int buf, auto nb_c) {
-      constexpr int NB = decltype(nb_c)::value;
-      const char* la = lds + buf * kStage;
-      const char* lt = la + kW;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int g = 2 * q + lh;
-        const u32x2 lo = lds_read_tr16(la + wsw(16 * q + tr_row, tr_chunk) + tr_byte);
-        const u32x2 hi = lds_read_tr16(la + wsw(16 * q + tr_row + 4, tr_chunk) + tr_byte);
-        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-        u32x4 bv[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) bv[b] = *reinterpret_cast<const u32x4*>(lt + swz(32 * b + lr, g));
-#pragma unroll
-        for (int b = 0; b < NB; ++b) mfma_bf16(acc[b], av, bv[b]);
-      }
-    };
-    // Pipeline as in the forward kernels: LDS buffer 0 holds stage s, R1
-    // stage s + 1 and R0 stage s + 2 (indices past the end repeat the last).
-    auto run = [&](auto nb_c, auto tm_c) {
-      load(R0, 0, nb_c, tm_c);
-      load(R1, min(1, S - 1), nb_c, tm_c);
-      store(R0, 0, nb_c);
-      load(R0, min(2, S - 1), nb_c, tm_c);
-      lds_barrier();
-      for (int s = 0; s + 1 < S; s += 2) {
-        compute(0, nb_c);
-        store(R1, 1, nb_c);
-        load(R1, min(s + 3, S - 1), nb_c, tm_c);
-        lds_barrier();
-        compute(1, nb_c);
-        store(R0, 0, nb_c);
-        load(R0, min(s + 4, S - 1), nb_c, tm_c);
-        lds_barrier();
-      }
-      if (S & 1) {
-        compute(0, nb_c);
-        lds_barrier();
-      }
-    };
-    // An expert cut into several m-tiles re-reads its weight tiles once per
-    // m-tile; those items run side by side on one XCD, so its weights are
-    // loaded with the default (L2-allocating) policy to serve the sibling
-    // tiles from L2.  A single-tile expert streams its weights non-temporally.
-    auto go = [&](auto tm_c) {
-      if (rows > 64)
-        run(std::integral_constant<int, 4>{}, tm_c);
-      else if (rows > 32)
-        run(std::integral_constant<int, 2>{}, tm_c);
-      else
-        run(std::integral_constant<int, 1>{}, tm_c);
-    };
-    if (mt_e > 1)
-      go(std::true_type{});
-    else
-      go(std::false_type{});
-    // the next item, taken while this one's epilogue runs
     int taken = 0;
-    if (dyn && tid == 0) taken = wq_take(hdr, xcd);
-
-    // acc[b][v]: output column 32*wave + 8*(v/4) + 4*lh + v%4, token 32*b + lr
-    const int col = nt * 256 + 32 * wave + 4 * lh;
-#pragma unroll
-    for (int b = 0; b < 4 && 32 * wave < ncols; ++b) {
-      const int m = 32 * b + lr;
-      if (m >= rows) continue;
-      const int64_t row = row0 + m;
-      if (KIND == 0) {
-        const int F = a.F;
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + row * (2 * F);
-        uint16_t* h2o = reinterpret_cast<uint16_t*>(a.out2);
-        const uint16_t* hr = h1 + row * (2 * F);
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int j = col + 8 * g4;
-          float gv[4], uv[4], dg[4], du[4], hv[4];
-          load4_bf16(hr + j, gv);
-          load4_bf16(hr + F + j, uv);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float dh2 = acc[b][4 * g4 + i];
-            // clamped SwiGLU backward: no gradient through a clamped value
-            const float L = a.limit;
-            const float gc = clamp_gate(gv[i], L), uc = clamp_up(uv[i], L);
-            const float sg = sigmoid_f(gc);
-            const float sl = silu_f(gc);
-            dg[i] = gv[i] > L ? 0.0f : dh2 * uc * (sg * (1.0f + gc * (1.0f - sg)));
-            du[i] = (uv[i] > L || uv[i] < -L) ? 0.0f : dh2 * sl;
-            hv[i] = sl * uc;
-          }
-          store4<uint16_t>(o + j, dg[0], dg[1], dg[2], dg[3]);
-          store4<uint16_t>(o + F + j, du[0], du[1], du[2], du[3]);
-          if (h2o) store4<uint16_t>(h2o + row * F + j, hv[0], hv[1], hv[2], hv[3]);
-        }
-      } else {
-        // dXr rows go to their route slots, so the input-gradient sum reads
-        // each token's K rows as one contiguous run
-        float* o = reinterpret_cast<float*>(a.out) + int64_t(a.row_slot[row]) * N;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          store4<float>(o + col + 8 * g4, acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2],
-                        acc[b][4 * g4 + 3]);
-      }
-    }
+    dgrad_item<KIND>(a, lds, tid, e, nt, u - nt * mt_e, mt_e, [&] {
+      // the next item, taken while this one's epilogue runs
+      if (dyn && tid == 0) taken = wq_take(hdr, xcd);
+    });
     if (dyn) {
       if (tid == 0) s_next = taken;
       lds_barrier();
@@ -352,10 +364,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
 // rows; chunks XOR-swizzled by 4 (m & 3)) and are read with transpose reads.
 __device__ __forceinline__ int bsw(int m, int c) { return m * 256 + ((c ^ ((m & 3) << 2)) << 4); }
 
+constexpr int kWgLds = 64 * 512 + 64 * 256;   // A and B operand stages
+
+// The WGRAD items w0, w0 + step, ... below w1 (expert-major, NA x NB tiles
+// per expert), each tile's first stage loaded while the previous tile is
+// stored.  With a.hot_wg the experts of kHotWgRows rows or more are skipped
+// (k_wgrad_hot's).  lds: kWgLds bytes.
 // ACC: in-place accumulation (dW += result): the tile is staged in fp32 and
 // each copied-out value is added to the dW value it replaces, rounded once.
 template <typename TW, int TAG, int ACC>
-__global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
+__device__ __forceinline__ void wgrad_run(const BwdArgs& a, char* lds, int tid, int w0, int w1,
+                                          int step) {
   typedef typename std::conditional<ACC != 0, float, TW>::type TS;   // staging type
   constexpr int kA = 64 * 512;                         // A stage: 64 token rows x 256 columns
   constexpr int kB = 64 * 256;                         // B stage: 64 token rows x 128 columns
@@ -363,8 +382,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
   constexpr int kRowsPerPass = sizeof(TS) == 4 ? 32 : 64;
   constexpr int kPasses = 128 / kRowsPerPass;
   static_assert(kRowsPerPass * kRowB <= kA + kB, "output staging reuses the operand stages");
-  __shared__ __attribute__((aligned(16))) char lds[kA + kB];
-  const int tid = threadIdx.x;
+  static_assert(kA + kB == kWgLds, "operand stages");
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wa = wave & 3;    // 64-column block of the tile
@@ -384,22 +402,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
   const int a_ld = a.a_ld, b_ld = a.b_ld;
   const int NA = (a_ld + 255) / 256, NB = b_ld / 128;
   const int per_e = NA * NB;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int per = gridDim.x / kXcds;
-  // with hot_wg the experts of kHotWgRows rows or more are k_wgrad_hot's:
-  // split by the cold experts' stages (theirs count 0, plus 1 per item)
-  const int32_t* cost = a.hot_wg ? a.cst : a.mtoff;
-  const int first = xcd_first_item(cost, a.E, per_e, xcd);
-  const int last = xcd_first_item(cost, a.E, per_e, xcd + 1);
+  const int last = w1, per = step;
   const uint16_t* asrc = reinterpret_cast<const uint16_t*>(a.arows);
   const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(a.grad);
 
   struct Item {
     int e, ta, tb, r0, Me, S, ncols;
   };
-  // Work items of this workgroup: w = first + slot + i * per below last.
-  int wcur = first + slot;
+  // Work items of this workgroup: w = w0 + i * per below last.
+  int wcur = w0;
   auto fill = [&](Item& t) {
     int e = 0;
     for (;;) {   // with hot_wg, step over the hot experts' items
@@ -543,6 +554,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
   }
 }
 
+template <typename TW, int TAG, int ACC>
+__global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kWgLds];
+  const int per_e = ((a.a_ld + 255) / 256) * (a.b_ld / 128);
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per = gridDim.x / kXcds;
+  // with hot_wg the experts of kHotWgRows rows or more are k_wgrad_hot's:
+  // split by the other experts' stages (theirs count 0, plus 1 per item)
+  const int32_t* cost = a.hot_wg ? a.cst : a.mtoff;
+  const int first = xcd_first_item(cost, a.E, per_e, xcd);
+  const int last = xcd_first_item(cost, a.E, per_e, xcd + 1);
+  wgrad_run<TW, TAG, ACC>(a, lds, threadIdx.x, first + slot, last, per);
+}
 
 // ------------------------------------------------------------------ WGRAD, hot experts
 // An expert with at least kHotWgRows rows contracts its weight gradient over
@@ -787,6 +812,186 @@ __global__ __launch_bounds__(512, 1) void k_wgrad_hot(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ fused (Mega) backward
+// One persistent grid runs a projection's DGRAD and WGRAD work records,
+// each expert's DGRAD tile range placed next to its WGRAD range (Dist-MoE
+// explainer, section 05, Mega backward).  Two launches, after the combine
+// backward: W2 (dH1 with the SwiGLU backward, and dW2) and W13 (dX rows and
+// dW13).
+//
+// Unit of work: 1 / NT of an expert, NT = its DGRAD n-tiles: the DGRAD
+// records of n-tile nt (one per m-tile) and dW items nt * NB .. + NB - 1 of
+// the streaming WGRAD launch's order (NB = 128-row bands of dW, NT x NB
+// items per expert).  For dW2 (band fastest) those are the tiles of dW
+// columns nt * 256 .. + 255, which read h2 columns nt * 256 .. + 255, which
+// the W2 DGRAD records of n-tile nt rebuild from h1: the unit is the unit of
+// the data dependency.  W13's records read dH1 and the x rows, complete
+// before the launch, and never wait; its units take the dW13 items in the
+// streaming order (column tile fastest, 4 x 8 blocks for hot experts), so
+// concurrent records share operand rows in L2 as there.
+//
+// MI355X design, as in the fused forward: an agent-scope release/acquire
+// pair (an L2 write-back and invalidate) costs more than the hand-off it
+// would order, so producer and consumer of every row share one L2:
+//  * each XCD owns a contiguous run of units, split by the experts' 64-row
+//    stages plus kMegaBwdCw per unit for its weight reads and dW writes (a
+//    hot expert's blocks spread over the XCDs), and runs their records from
+//    its own ticket queue (on the XCD the workgroup runs on: hw_xcd);
+//  * queue block j holds the DGRAD records of unit j, then the WGRAD
+//    records of unit j - look (look = the XCD's workgroup count, so a
+//    unit's DGRAD records are running or done when its WGRAD records come
+//    up).  A WGRAD record is about kMegaWgStages stages of work: up to
+//    kMegaWgStages dW tiles of an expert with one 64-row stage, a single
+//    tile of one with kMegaWgStages or more (every tile's first stage is
+//    loaded while the previous one is stored).  Each workgroup first sums
+//    the records per expert into LDS;
+//  * W2: a DGRAD record stores, waits until its stores are in L2 (vmcnt 0)
+//    and counts itself in ready[unit]; a WGRAD record first waits (one
+//    thread, atomic reads, bounded) until ready[unit] equals the unit's
+//    DGRAD record count.  No workgroup on that CU read those h2 lines
+//    earlier in the launch;
+//  * a workgroup takes its next ticket as it starts a record, so the
+//    ticket's latency hides behind the record, and starts that record after
+//    finishing the current one.
+// Every wait ends: the smallest unfinished ticket is either running, and
+// then waits only for smaller tickets (a unit's DGRAD records come before
+// its WGRAD records), all finished, or it is the next ticket of a workgroup
+// whose current, smaller ticket is finished.  Tickets and counters are
+// zeroed by the backward's planner launch.
+constexpr int kMegaWgStages = 16;    // 64-row stages per WGRAD record (at least one tile)
+constexpr int kMegaBwdCw = 3;        // XCD split: a unit's fixed cost, in 64-row stages
+constexpr int kMegaBwdSpin = 1 << 22;   // polls (each followed by a short sleep)
+
+template <int KIND, typename TW, int ACC>
+__global__ __launch_bounds__(512, 1) void k_bwd_mega(BwdArgs dg, BwdArgs wg, uint32_t* tickets,
+                                                     uint32_t* ready, int look) {
+  constexpr int TAG = KIND == 0 ? 2 : 13;
+  __shared__ __attribute__((aligned(16))) char lds[kDgLds > kWgLds ? kDgLds : kWgLds];
+  __shared__ int s_t;
+  __shared__ int s_wp[kMaxE + 1];   // WGRAD records per unit of the experts before e (E <= kMaxE)
+  __shared__ int s_part[512];
+  const int tid = threadIdx.x;
+  const RouteHdr* hdr = dg.hdr;
+  const int E = dg.E;
+  const int32_t* gt = dg.mtoff;   // DGRAD m-tile prefix
+  const int NU = dg.NT;           // units per expert: 256-column weight blocks
+  const int NAw = (wg.a_ld + 255) / 256, NBw = wg.b_ld / 128;
+  const int per_e = NAw * NBw;    // dW tiles per expert; NBw per unit
+  // dW tiles per WGRAD record of expert e, and records per unit
+  auto group = [&](int e) {
+    const int S = (wg.offsets[e + 1] - wg.offsets[e] + 63) / 64;
+    return S <= 1 ? kMegaWgStages : max(1, kMegaWgStages / S);
+  };
+  auto nrec = [&](int e) {
+    const int G = group(e);
+    return (NBw + G - 1) / G;
+  };
+  {   // s_wp: exclusive prefix of nrec over the experts (each thread a run of experts)
+    const int c = (E + 511) / 512;
+    const int e0 = min(E, tid * c), e1 = min(E, e0 + c);
+    int sum = 0;
+    for (int e = e0; e < e1; ++e) sum += nrec(e);
+    s_part[tid] = sum;
+    lds_barrier();
+    for (int off = 1; off < 512; off <<= 1) {   // inclusive scan of the run sums
+      const int v = tid >= off ? s_part[tid - off] : 0;
+      lds_barrier();
+      s_part[tid] += v;
+      lds_barrier();
+    }
+    int run = s_part[tid] - sum;
+    for (int e = e0; e < e1; ++e) {
+      s_wp[e] = run;
+      run += nrec(e);
+    }
+    if (tid == 511) s_wp[E] = s_part[511];
+    lds_barrier();
+  }
+
+  const int xcd = hw_xcd();
+  uint32_t* ticket = tickets + xcd;
+  const int u_lo = xcd_first_unit(wg.mtoff, kMegaBwdCw, E, NU, xcd);
+  const int u_hi = xcd_first_unit(wg.mtoff, kMegaBwdCw, E, NU, xcd + 1);
+  const int nu = u_hi - u_lo;
+  // DGRAD records before unit u (all m-tiles of the earlier units)
+  auto dpre = [&](int u) {
+    const int e = u / NU, nt = u - e * NU;
+    return gt[e] * NU + (e < E ? nt * (gt[e + 1] - gt[e]) : 0);
+  };
+  // WGRAD records before unit u
+  auto wpre = [&](int u) {
+    const int e = u / NU, nt = u - e * NU;
+    return s_wp[e] * NU + (e < E ? nt * (s_wp[e + 1] - s_wp[e]) : 0);
+  };
+  const int d0 = dpre(u_lo), w0 = wpre(u_lo);
+  // records before queue block j
+  auto start = [&](int j) {
+    return dpre(u_lo + min(j, nu)) - d0 + wpre(u_lo + max(0, min(j - look, nu))) - w0;
+  };
+  const int total = dpre(u_hi) - d0 + wpre(u_hi) - w0;
+
+  if (tid == 0) s_t = int(atomicAdd(ticket, 1u));
+  lds_barrier();
+  // one ticket per workgroup: uniform, so everything derived from it is
+  // scalar (the record's unit, tile and addresses)
+  int t = __builtin_amdgcn_readfirstlane(s_t);
+  int j_lo = 0;   // tickets only grow, so blocks only move forward
+  while (t < total) {
+    int hi = nu + look;   // start(j_lo) <= t < start(hi) = total
+    while (hi - j_lo > 1) {
+      const int mid = (j_lo + hi) >> 1;
+      if (start(mid) <= t)
+        j_lo = mid;
+      else
+        hi = mid;
+    }
+    const int j = j_lo;
+    int r = t - start(j);
+    const int cd = j < nu ? dpre(u_lo + j + 1) - dpre(u_lo + j) : 0;
+    const bool dgr = r < cd;
+    const int unit = dgr ? u_lo + j : u_lo + j - look;
+    if (!dgr) r -= cd;
+    const int e = unit / NU, nt = unit - e * NU;
+    int nxt_t = 0;
+    if (tid == 0) nxt_t = int(atomicAdd(ticket, 1u));
+    // The record's lane constants (loader slots, LDS offsets) are derived
+    // from this copy of the thread index, which the compiler cannot move out
+    // of the loop: hoisted, the two record kinds' constants would be live at
+    // once and spill.
+    int rtid = tid;
+    asm volatile("" : "+v"(rtid));
+    if (dgr) {
+      dgrad_item<KIND>(dg, lds, rtid, e, nt, r, gt[e + 1] - gt[e], [] {});
+      if (KIND == 0) {   // this record's dH1/h2 stores complete in L2, then counted
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (tid == 0) atomicAdd(&ready[unit], 1u);
+      }
+    } else {
+      if (KIND == 0) {
+        if (tid == 0) {
+          const uint32_t need = uint32_t(gt[e + 1] - gt[e]);
+          int n = 0;
+          while (atomicAdd(&ready[unit], 0u) < need && ++n < kMegaBwdSpin)
+            __builtin_amdgcn_s_sleep(4);
+          if (n >= kMegaBwdSpin)
+            atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_SYNC_TIMEOUT);
+        }
+        __syncthreads();
+      }
+      // items b0 .. b1 - 1 of the unit's NBw
+      const int G = group(e);
+      const int b0 = r * G, b1 = min(NBw, b0 + G);
+      const int w = e * per_e + nt * NBw;
+      wgrad_run<TW, TAG, ACC>(wg, lds, rtid, w + b0, w + b1, 1);
+    }
+    if (tid == 0) s_t = nxt_t;
+    lds_barrier();
+    t = __builtin_amdgcn_readfirstlane(s_t);
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 // Resident workgroups per CU of one kernel (queried once per kernel).
 template <int ID, typename K>
@@ -858,6 +1063,39 @@ hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& args, int cus, hipSt
     else
       hipLaunchKernelGGL(k_wgrad_hot<13>, dim3(g), dim3(512), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+// Fused backward of one projection: kind 0 = W2 (DGRAD + SwiGLU backward
+// records with dg, dW2 records with wg; ready: one counter per expert and
+// 256-column block of F), 1 = W13 (dX rows, dW13).  tickets: kXcds
+// counters.  The hot experts' dW tiles stay on the streaming tiles here.
+hipError_t launch_bwd_mega(int kind, int dw_f32, const BwdArgs& dg, const BwdArgs& wg,
+                           uint32_t* tickets, uint32_t* ready, int cus, hipStream_t s) {
+  // units: the DGRAD n-tiles are the dW column tiles (NT x NB dW items per expert)
+  if (dg.NT != (wg.a_ld + 255) / 256) return hipErrorInvalidValue;
+  BwdArgs w = wg;
+  w.hot_wg = 0;
+  const unsigned g = persistent_grid(1, int64_t(cus), cus);
+  const int look = int(g / kXcds);   // the XCD's workgroups
+  const int acc = w.acc_dw ? 1 : 0;
+#define MOE_MB(K, TW, ACC) \
+  hipLaunchKernelGGL((k_bwd_mega<K, TW, ACC>), dim3(g), dim3(512), 0, s, dg, w, tickets, ready, \
+                     look)
+  if (kind == 0) {
+    if (dw_f32) {
+      if (acc) MOE_MB(0, float, 1); else MOE_MB(0, float, 0);
+    } else {
+      if (acc) MOE_MB(0, uint16_t, 1); else MOE_MB(0, uint16_t, 0);
+    }
+  } else {
+    if (dw_f32) {
+      if (acc) MOE_MB(1, float, 1); else MOE_MB(1, float, 0);
+    } else {
+      if (acc) MOE_MB(1, uint16_t, 1); else MOE_MB(1, uint16_t, 0);
+    }
+  }
+#undef MOE_MB
   return hipGetLastError();
 }
 

@@ -593,6 +593,10 @@ __global__ void k_plan_decide(RouteHdr* __restrict__ hdr, PlanArgs a) {
 // backward rebuilds its forward state from x in scratch, as for a layer the
 // planner chose to replay, instead of reading through stale pointers.
 __global__ void k_plan_enter_bwd(RouteHdr* __restrict__ hdr, PlanArgs a) {
+  if (a.zero) {   // the fused backward's tickets and counters
+    uint32_t* z = reinterpret_cast<uint32_t*>(a.zero);
+    for (int i = threadIdx.x; i < a.zero_n; i += blockDim.x) z[i] = 0u;
+  }
   if (threadIdx.x != 0) return;
   LayerRec& rec = hdr->rec;
   if (rec.done) return;

@@ -95,5 +95,6 @@ def test_unknown_backward_flag_rejected(B):
     T, D, F, E, K = 16, 128, 128, 2, 1
     lay = make_inputs(T, D, F, E, K, "bf16", seed=2, training=True)
     layer = B.MoeLayer(T, D, F, E, K, "bf16", training=True)
-    with pytest.raises(B.MoeError):
-        run_train(layer, lay, flags=0x4)
+    for flag in (0x8, 0x80000000):   # bits no MOE_BWD_* flag uses
+        with pytest.raises(B.MoeError):
+            run_train(layer, lay, flags=flag)
