@@ -68,3 +68,59 @@ def test_forward_graph_replays_match_eager(B, pipeline, prec):
         run_forward(layer, lay)
         torch.cuda.synchronize()
     assert layer.status()[0] == 0
+
+
+@pytest.mark.parametrize("mega", [False, True])
+def test_training_step_graph_replays_match_eager(B, mega):
+    """Forward and backward captured in one graph (BF16; with mega, the fused
+    backward, whose tickets and per-block counters the backward's planner
+    launch clears on every call): every replay, with eager steps between,
+    gives the eager step's gradients bit for bit."""
+    banner(f"graph replay training step, fused backward={mega}")
+    T, D, F, E, K = 300, 512, 256, 12, 3
+    lay = make_inputs(T, D, F, E, K, "bf16", zipf=1.1, seed=91, training=True)
+    layer = B.MoeLayer(T, D, F, E, K, "bf16", training=True)
+    flags = B.BWD_MEGA if mega else 0
+    dev = "cuda"
+    y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    grads = [torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((E, 2 * F, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((E, D, F), dtype=torch.bfloat16, device=dev),
+             torch.empty((T, K), dtype=torch.float32, device=dev)]
+
+    def step(out):
+        layer.route(lay["ids"])
+        layer.forward(lay["x"], lay["w13"], lay["w2"])
+        layer.combine(lay["scores"], y)
+        layer.backward(lay["x"], lay["scores"], lay["dy"], lay["w13"], lay["w2"], out[0], out[1],
+                       out[2], out[3], flags=flags)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up off the capture
+        step(grads)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(grads)
+    torch.cuda.synchronize()
+
+    def eager():
+        out = [torch.empty_like(t) for t in grads]
+        step(out)
+        torch.cuda.synchronize()
+        return out
+
+    ref = eager()
+    for i in range(3):
+        for t in grads:
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for name, u, v in zip(("dx", "dw13", "dw2", "ds"), grads, ref):
+            assert torch.equal(u, v), (i, name)
+        got = eager()
+        for u, v in zip(got, ref):
+            assert torch.equal(u, v)
+    assert layer.status()[0] == 0
