@@ -99,6 +99,8 @@ SYMBOLS = {
     "mxfp8": {
         "w13_swiglu": ("moe::k_mx_fwd<0, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
         "mega_fwd": ("moe::k_mx_fwd<2, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
+        "w2_bwd_mega": ("moe::k_mx_bwd_mega<0, unsigned short, 0>", ["gemm_mx.hip", "mxq.h"]),
+        "w13_bwd_mega": ("moe::k_mx_bwd_mega<1, unsigned short, 0>", ["gemm_mx.hip", "mxq.h"]),
         "w2_scatter": ("moe::k_mx_fwd<1, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
         "w2_dgrad_swiglu": ("moe::k_mx_dgrad<0>", ["gemm_mx.hip", "mxq.h"]),
         "w13_dgrad": ("moe::k_mx_dgrad<1>", ["gemm_mx.hip", "mxq.h"]),
@@ -217,6 +219,9 @@ def alg_bytes(name, m):
         "bundle_dh1": R * 2 * F * 2 + q(Rp * 2 * F),
         "w13_dgrad": w13 + q(R * 2 * F) + R * D * 4,
         "w13_wgrad": ne * 2 * F * D * dwb + q(Rp * 2 * F) + q(Rp * D),
+        "w2_bwd_mega": w2 + q(R * D) + 2 * R * 2 * F * 2 + ne * D * F * dwb + q(Rp * D) + q(Rp * F),
+        "w13_bwd_mega": w13 + q(R * 2 * F) + R * D * 4 + ne * 2 * F * D * dwb + q(Rp * 2 * F)
+                        + q(Rp * D),
     }.get(name)
 
 
@@ -320,6 +325,7 @@ def setup(args, dev):
         L = cfg.layers
         budget = wl.ten_layer_budget(cfg)
         st = B.MoeStack(L, T, D, F, E, K, "mxfp8", arena_budget=budget, device=dev)
+        mega = args.pipeline == "mega"
         lays, preps = [], []
         for l in range(L):
             lay = wl.make_layer(cfg, l, device=dev)
@@ -341,10 +347,10 @@ def setup(args, dev):
             for l in range(L):
                 st.route(l, lays[l]["ids"])
                 st.forward(l, lays[l]["x"], None, None, lays[l]["scores"], ys[l],
-                           prepared=preps[l])
+                           prepared=preps[l], mega=mega)
             for l in reversed(range(L)):
                 st.backward(l, lays[l]["x"], lays[l]["scores"], lays[l]["dy"], None, None, dx,
-                            dw13, dw2, ds, prepared=preps[l])
+                            dw13, dw2, ds, prepared=preps[l], flags=B.BWD_MEGA if mega else 0)
 
         def meta():
             out = []
@@ -385,8 +391,8 @@ def setup(args, dev):
 
     fused = args.workload == "bf16_fwd_fused"
     y32 = torch.empty((T, D), dtype=torch.float32, device=dev) if fused else None
-    # the fused backward exists for BF16 plans
-    bwd_flags = B.BWD_MEGA if args.pipeline == "mega" and cfg.prec == "bf16" else 0
+    # the fused backward (BF16 and MXFP8 plans)
+    bwd_flags = B.BWD_MEGA if args.pipeline == "mega" else 0
 
     def step():
         if fused:
@@ -620,7 +626,7 @@ def main():
                                + (f", SwiGLU clamped at {cfg.swiglu_limit:g}"
                                   if cfg.swiglu_limit else "")
                                + ((", fused (Mega) forward and backward"
-                                   if training and prec == "bf16" else ", fused (Mega) forward")
+                                   if training else ", fused (Mega) forward")
                                   if args.pipeline == "mega" else ""),
                    "routes_per_layer": [m["R"] for lab, m in metas if lab == ""],
                    "nonempty_experts": [m["ne"] for lab, m in metas if lab == ""],

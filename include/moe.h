@@ -94,13 +94,16 @@ typedef enum moe_dtype {
  * and rounded once to the dW type; experts with no rows keep their values.
  * dW is then read as well as written. */
 #define MOE_BWD_ACCUMULATE_DW 0x2u
-/* The fused (Mega) backward of the Dist-MoE explainer, section 05: each
- * projection's DGRAD and WGRAD work records run in one persistent grid, each
- * expert's DGRAD tile range next to its WGRAD range (two launches: W2, then
- * W13).  Results are bit-identical to the staged backward (the same tiles,
- * summed in the same order).  BF16 plans only (MXFP8: MOE_ERR_UNSUPPORTED).
- * The W2 launch's dW2 records wait, bounded, for the h2 rows its DGRAD
- * records rebuild; a wait that runs out sets MOE_STATUS_SYNC_TIMEOUT. */
+/* The fused (Mega) backward of the Dist-MoE explainer, section 05 (and
+ * section 0: the MXFP8 path's backward as two fused expert operations, W2
+ * then W13, followed by the input-gradient reduction): each projection's
+ * DGRAD and WGRAD work records run in one persistent grid, each expert's
+ * DGRAD tile range next to its WGRAD range.  Results are bit-identical to
+ * the staged backward (the same tiles, summed in the same order).  BF16 and
+ * MXFP8 plans.  BF16: the W2 launch's dW2 records wait, bounded, for the h2
+ * rows its DGRAD records rebuild; a wait that runs out sets
+ * MOE_STATUS_SYNC_TIMEOUT.  MXFP8 records never wait (both records of a
+ * projection read operands quantized before the launch). */
 #define MOE_BWD_MEGA 0x4u
 
 /* Layer description.  Supported: D % 128 == 0, F % 128 == 0, D and F at

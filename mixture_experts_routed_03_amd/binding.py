@@ -374,10 +374,10 @@ class MoeLayer:
                        self._w(w13, w2, prepared), self.h3 if h3 is None else h3, self.arena,
                        self.scratch)
 
-    def forward_mega(self, x, w13, w2, layer=0, route_ws=None, h3=None):
+    def forward_mega(self, x, w13, w2, layer=0, route_ws=None, h3=None, prepared=None):
         """The expert forward as one fused (Mega) launch; same outputs as forward."""
         moe_expert_fwd_mega(self.plan, layer, self.route_ws if route_ws is None else route_ws, x,
-                            self._w(w13, w2, None), self.h3 if h3 is None else h3, self.arena,
+                            self._w(w13, w2, prepared), self.h3 if h3 is None else h3, self.arena,
                             self.scratch)
 
     def combine(self, scores, y, y_addend=None, route_ws=None, h3=None):
@@ -467,9 +467,10 @@ class MoeStack:
     def route(self, l, ids):
         self.layer.route(ids, route_ws=self.bufs[l][0])
 
-    def forward(self, l, x, w13, w2, scores, y, prepared=None, y_addend=None):
+    def forward(self, l, x, w13, w2, scores, y, prepared=None, y_addend=None, mega=False):
         rw, h3 = self.bufs[l]
-        self.layer.forward(x, w13, w2, layer=l, route_ws=rw, h3=h3, prepared=prepared)
+        fwd = self.layer.forward_mega if mega else self.layer.forward
+        fwd(x, w13, w2, layer=l, route_ws=rw, h3=h3, prepared=prepared)
         self.layer.combine(scores, y, y_addend=y_addend, route_ws=rw, h3=h3)
 
     def backward(self, l, x, scores, dy, w13, w2, dx, dw13, dw2, dscores=None, prepared=None,

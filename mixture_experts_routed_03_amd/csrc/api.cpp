@@ -56,6 +56,8 @@ hipError_t launch_mx_mega(const MxArgs& a13, const MxArgs& a2, uint32_t* msync, 
                           int64_t mt_max, int cus, hipStream_t s);
 hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s);
 hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStream_t s);
+hipError_t launch_mx_bwd_mega(int kind, int dw_f32, const MxArgs& dg, const MxArgs& wg,
+                              uint32_t* tickets, int cus, hipStream_t s);
 hipError_t launch_wgrad(int dw_f32, int tag, const BwdArgs& a, int cus, hipStream_t s);
 hipError_t launch_bwd_mega(int kind, int dw_f32, const BwdArgs& dg, const BwdArgs& wg,
                            uint32_t* tickets, uint32_t* ready, int cus, hipStream_t s);
@@ -310,6 +312,10 @@ hipError_t mx_forward_w13(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, cons
 moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const void* x,
                        const moe_weights* w, const float* scores, const void* dy, const void* h3,
                        void* arena, const moe_grads* g, uint32_t flags, int cus, hipStream_t s) {
+  const bool mega = (flags & MOE_BWD_MEGA) != 0;
+  // msync: [W2 tickets | counters | W13 tickets] (the fused launches')
+  uint32_t* msync = at<uint32_t>(ws, p->rl.msync);
+  uint32_t* t13 = msync + kXcds + int64_t(p->d.e) * msync_blocks(p->d.f);
   const moe_desc& d = p->d;
   const ScratchLayout& L = p->sl;
   const int32_t* offsets = at<int32_t>(ws, p->rl.offsets);
@@ -338,13 +344,20 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
              -1, 0, int(p->R_max)};
   dg2.limit = swiglu_limit(p);
   dg2.stoff = mtoff;
-  e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_mx_dgrad(0, dg2, p->mt_max, cus, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs wg2{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
              u8(L.dh3cq), u8(L.dh3cs), g->dw2, nullptr, 0, 0, d.f, 0, d.e, d.f, d.d, 2, 0};
   wg2.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
-  e = timed(p, "w2_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 2, wg2, cus, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (mega) {
+    e = timed(p, "w2_bwd_mega", s, [&] {
+      return launch_mx_bwd_mega(0, dw_f32, dg2, wg2, msync, cus, s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  } else {
+    e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_mx_dgrad(0, dg2, p->mt_max, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = timed(p, "w2_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 2, wg2, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   RowqArgs r1{hdr, sc + L.dh1, u8(L.qdh1), u8(L.sdh1), 2 * d.f, -1, -1, -1, 0, int(p->R_max)};
   e = timed(p, "quant_dh1", s, [&] { return launch_rowq(r1, p->R_max, s); });
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -357,13 +370,20 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
               nullptr, nullptr, sc + L.dxr, nullptr, 2 * d.f, d.d, d.f, (d.d + 255) / 256, d.e, 0, 0,
               -1, 0, int(p->R_max)};
   dg13.stoff = mtoff;
-  e = timed(p, "w13_dgrad", s, [&] { return launch_mx_dgrad(1, dg13, p->mt_max, cus, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
   MxArgs wg13{hdr, offsets, poffsets, mtoff, sorted_route, nullptr, nullptr, nullptr, nullptr,
               u8(L.dh1cq), u8(L.dh1cs), g->dw13, nullptr, 0, 0, d.f, 0, d.e, d.d, 2 * d.f, 0, 0};
   wg13.acc_dw = (flags & MOE_BWD_ACCUMULATE_DW) ? 1 : 0;
-  e = timed(p, "w13_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 13, wg13, cus, s); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (mega) {
+    e = timed(p, "w13_bwd_mega", s, [&] {
+      return launch_mx_bwd_mega(1, dw_f32, dg13, wg13, t13, cus, s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  } else {
+    e = timed(p, "w13_dgrad", s, [&] { return launch_mx_dgrad(1, dg13, p->mt_max, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = timed(p, "w13_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 13, wg13, cus, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   e = timed(p, "dx_reduce", s, [&] {
     return launch_dx_reduce(d.prec, hdr, route_to_row, reinterpret_cast<float*>(sc + L.dxr), g->dx,
                             d.k, d.d, d.t_max, (flags & MOE_BWD_ACCUMULATE_DX) ? 1 : 0, s);
@@ -912,7 +932,6 @@ moe_status moe_expert_bwd(moe_plan_t p, int32_t layer, void* ws, const void* x,
   const moe_desc& d = p->d;
   if (!d.training || d.prec == MOE_PREC_F32) return MOE_ERR_UNSUPPORTED;
   const bool mega = (flags & MOE_BWD_MEGA) != 0;
-  if (mega && d.prec != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
   if (layer < 0 || layer >= d.max_layers) return MOE_ERR_ARG;
   const bool mx = d.prec == MOE_PREC_MXFP8;
   if (mx ? (!w->q13 || !w->s13 || !w->q2 || !w->s2) : (!w->w13 || !w->w2)) return MOE_ERR_ARG;

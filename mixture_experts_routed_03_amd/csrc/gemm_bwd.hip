@@ -336,13 +336,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dgrad(BwdArgs a) {
     const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
     const int u = w - a.mtoff[e] * a.NT;
     const int nt = u / mt_e;
-    int taken = 0;
     dgrad_item<KIND>(a, lds, tid, e, nt, u - nt * mt_e, mt_e, [&] {
-      // the next item, taken while this one's epilogue runs
-      if (dyn && tid == 0) taken = wq_take(hdr, xcd);
+      // the next item, taken while this one's epilogue runs (every thread
+      // read s_next before this item's stage barriers)
+      if (dyn && tid == 0) s_next = wq_take(hdr, xcd);
     });
     if (dyn) {
-      if (tid == 0) s_next = taken;
       lds_barrier();
       w = first + s_next;
     } else {

@@ -579,14 +579,22 @@ __device__ __forceinline__ int wsw8(int r, int c) { return r * 256 + ((c ^ ((r &
 // 256-byte weight row segments stream faster from HBM than 128-byte ones.
 // (A 128-row variant, four accumulators per wave, does not fit the 256
 // registers of two waves per SIMD without spilling.)
-template <int KIND>
-__global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
-  constexpr int kW = 128 * 256;      // weight stage: 128 contraction rows x 256 columns
-  constexpr int kT = kBM * 128;      // token stage: up to 64 rows x 128 values
-  constexpr int kSc = kBM * 4;       // token exponents of the stage
-  constexpr int kStage = kW + kT + kSc + 32;   // + weight exponents: 8 column blocks x 4 k blocks
-  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
-  const int tid = threadIdx.x;
+constexpr int kMxDgW = 128 * 256;      // weight stage: 128 contraction rows x 256 columns
+constexpr int kMxDgT = kBM * 128;      // token stage: up to 64 rows x 128 values
+constexpr int kMxDgSc = kBM * 4;       // token exponents of the stage
+constexpr int kMxDgStage = kMxDgW + kMxDgT + kMxDgSc + 32;   // + weight exponents: 8 x 4 blocks
+constexpr int kMxDgLds = 2 * kMxDgStage;
+
+// One DGRAD work item: output columns nt * 256 .. + 255 of m-tile mt of
+// expert e (mt_e m-tiles).  `between` runs when the contraction is done,
+// before the epilogue (a launch takes its next item there).
+template <int KIND, typename Between>
+__device__ __forceinline__ void mx_dgrad_item(const MxArgs& a, char* lds, int tid, int e, int nt,
+                                              int mt, int mt_e, Between&& between) {
+  constexpr int kW = kMxDgW;
+  constexpr int kT = kMxDgT;
+  constexpr int kSc = kMxDgSc;
+  constexpr int kStage = kMxDgStage;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 31;
@@ -602,11 +610,6 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
   const int lrow = tid >> 3;  // token loader: tile row
 
   const RouteHdr* hdr = a.hdr;
-  const int xcd = blockIdx.x % kXcds;
-  const int per = gridDim.x / kXcds;
-  // 64-row m-tiles (a.mtoff = a.stoff); the XCDs split the items by token rows
-  const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
-  const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
   const int Kd = a.Kd;
   const int KB = Kd / 32;
   const int S = Kd / 128;
@@ -614,22 +617,7 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
   const int NB32 = int(N / 32);
   const uint16_t* h1 = global_ptr<const uint16_t>(hdr->rec.h1);
 
-  // items [first, last) of this XCD come from its work queue, in order
-  // (with skewed routing: when some expert spans several m-tiles; otherwise
-  // dealt statically, slot, slot + per, ..., which costs no atomics)
-  const bool dyn = hdr->max_count > kBM;
-  const int slot = blockIdx.x / kXcds;
-  __shared__ int s_next;
-  if (dyn && tid == 0) s_next = wq_take(hdr, xcd);
-  lds_barrier();
-  int e_prev = -1;  // expert of this workgroup's previous item
-  for (int w = dyn ? first + s_next : first + slot; w < last;) {
-    const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
-    e_prev = e;
-    const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
-    const int u = w - a.mtoff[e] * a.NT;
-    const int nt = u / mt_e;
-    const int mt = u - nt * mt_e;
+  {
     const int row0 = a.offsets[e] + mt * kBM;
     const int rows = min(kBM, a.offsets[e + 1] - row0);
     // The last tile of an N that is an odd multiple of 128 has 128 columns:
@@ -743,9 +731,7 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
       run(std::integral_constant<int, 2>{});
     else
       run(std::integral_constant<int, 1>{});
-    // the next item, taken while this one's epilogue runs
-    int taken = 0;
-    if (dyn && tid == 0) taken = wq_take(hdr, xcd);
+    between();
 
     const int col = nt * 256 + 32 * wave + 4 * lh;
 #pragma unroll
@@ -785,8 +771,40 @@ __global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
                         acc[b][4 * g4 + 3]);
       }
     }
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void k_mx_dgrad(MxArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMxDgLds];
+  const int tid = threadIdx.x;
+  const RouteHdr* hdr = a.hdr;
+  const int xcd = blockIdx.x % kXcds;
+  const int per = gridDim.x / kXcds;
+  // 64-row m-tiles (a.mtoff = a.stoff); the XCDs split the items by token rows
+  const int first = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd);
+  const int last = xcd_first_tile(a.mtoff, a.stoff, a.E, a.NT, xcd + 1);
+  // items [first, last) of this XCD come from its work queue, in order
+  // (with skewed routing: when some expert spans several m-tiles; otherwise
+  // dealt statically, slot, slot + per, ..., which costs no atomics)
+  const bool dyn = hdr->max_count > kBM;
+  const int slot = blockIdx.x / kXcds;
+  __shared__ int s_next;
+  if (dyn && tid == 0) s_next = wq_take(hdr, xcd);
+  lds_barrier();
+  int e_prev = -1;  // expert of this workgroup's previous item
+  for (int w = dyn ? first + s_next : first + slot; w < last;) {
+    const int e = item_expert(a.mtoff, a.E, a.NT, w, e_prev);
+    e_prev = e;
+    const int mt_e = a.mtoff[e + 1] - a.mtoff[e];
+    const int u = w - a.mtoff[e] * a.NT;
+    const int nt = u / mt_e;
+    mx_dgrad_item<KIND>(a, lds, tid, e, nt, u - nt * mt_e, mt_e, [&] {
+      // the next item, taken while this one's epilogue runs (every thread
+      // read s_next before this item's stage barriers)
+      if (dyn && tid == 0) s_next = wq_take(hdr, xcd);
+    });
     if (dyn) {
-      if (tid == 0) s_next = taken;
       lds_barrier();
       w = first + s_next;
     } else {
@@ -812,8 +830,15 @@ __device__ __forceinline__ uint64_t rec_ptr_m(const RouteHdr* h, int slot) {
 // columns 64 (w & 3) .. + 63: 2 x 2 accumulators of 32 x 32.
 // ACC: in-place accumulation (dW += result): the tile is staged in fp32 and
 // each copied-out value is added to the dW value it replaces, rounded once.
+// operand stages + output staging (64 bf16 rows or 32 fp32 rows of 256 values, padded)
+constexpr int kMxWgLds = 256 * 64 + 128 * 64 + 64 * (256 * 2 + 16);
+
+// The WGRAD items w0, w0 + step, ... below w1 (expert-major, NA x NB tiles
+// per expert), each tile's first stage loaded while the previous tile is
+// stored.  lds: kMxWgLds bytes.
 template <typename TW, int TAG, int ACC>
-__global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
+__device__ __forceinline__ void mx_wgrad_run(const MxArgs& a, char* lds, int tid, int w0, int w1,
+                                             int step) {
   typedef typename std::conditional<ACC != 0, float, TW>::type TS;   // staging type
   constexpr int kOpA = 256 * 64;                       // A stage: 256 columns x 64 rows
   constexpr int kOpB = 128 * 64;                       // B stage: 128 columns x 64 rows
@@ -821,8 +846,7 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
   constexpr int kRowsPerPass = sizeof(TS) == 4 ? 32 : 64;
   constexpr int kPasses = 128 / kRowsPerPass;
   constexpr int kOut = kRowsPerPass * kRowB;
-  __shared__ __attribute__((aligned(16))) char lds[kOpA + kOpB + kOut];
-  const int tid = threadIdx.x;
+  static_assert(kOpA + kOpB + kOut <= kMxWgLds, "operand stages and output staging");
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wa = wave & 3;     // 64-column block of the tile
@@ -836,11 +860,7 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
   const int a_ld = a.a_ld, b_ld = a.b_ld;
   const int NA = (a_ld + 255) / 256, NB = b_ld / 128;
   const int per_e = NA * NB;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int per = gridDim.x / kXcds;
-  const int first = xcd_first_item(a.mtoff, a.E, per_e, xcd);
-  const int last = xcd_first_item(a.mtoff, a.E, per_e, xcd + 1);
+  const int last = w1, per = step;
   const uint8_t* qa = a.a_slot >= 0 ? global_ptr<const uint8_t>(rec_ptr_m(hdr, a.a_slot)) : a.qa;
   const uint8_t* sa = a.a_slot >= 0 ? global_ptr<const uint8_t>(rec_ptr_m(hdr, a.a_slot + 1)) : a.sa;
   const uint8_t* qb = a.qb;
@@ -849,8 +869,8 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
   struct Item {
     int e, ta, tb, pb, mp, S, ncols;
   };
-  // Work items of this workgroup: w = first + slot + i * per below last.
-  int wcur = first + slot;
+  // Work items of this workgroup: w = w0 + i * per below last.
+  int wcur = w0;
   auto fill = [&](Item& t) {
     if (wcur >= last) {
       t.e = -1;
@@ -992,6 +1012,145 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
   }
 }
 
+template <typename TW, int TAG, int ACC>
+__global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kMxWgLds];
+  const int per_e = ((a.a_ld + 255) / 256) * (a.b_ld / 128);
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per = gridDim.x / kXcds;
+  const int first = xcd_first_item(a.mtoff, a.E, per_e, xcd);
+  const int last = xcd_first_item(a.mtoff, a.E, per_e, xcd + 1);
+  mx_wgrad_run<TW, TAG, ACC>(a, lds, threadIdx.x, first + slot, last, per);
+}
+
+// ------------------------------------------------------------------ fused (Mega) backward
+// One persistent grid runs a projection's DGRAD and WGRAD work records,
+// each expert's DGRAD tile range placed next to its WGRAD range (Dist-MoE
+// explainer, section 05, Mega backward; section 0: the MXFP8 backward as
+// two fused expert operations, W2 then W13, then the input-gradient
+// reduction).  Both records of a projection read operands that exist before
+// the launch (W2: the dH3 row blocks and column bundle and the saved or
+// rebuilt h2 column bundle; W13: the dH1 row blocks and column bundle and
+// the x column bundle), so no record waits for another.  Scheduling as in
+// the BF16 fused backward: units of one 256-column weight block of an
+// expert (the DGRAD records of that n-tile, one per 64-row m-tile, and
+// NB dW items of the streaming WGRAD order), split over the XCDs by their
+// 64-row stages + kMxMegaBwdCw, each XCD's queue holding the DGRAD records
+// of unit j and the WGRAD records of unit j - look (look = the XCD's
+// workgroups), a WGRAD record being about kMxWgRecordStages stages of work.
+// A workgroup takes its next ticket as it starts a record.  Tickets are
+// zeroed by the backward's planner launch.
+constexpr int kMxWgRecordStages = 16;   // 64-row stages of work per WGRAD record (>= 1 tile)
+constexpr int kMxMegaBwdCw = 3;         // XCD split: a unit's fixed cost, in 64-row stages
+
+template <int KIND, typename TW, int ACC>
+__global__ __launch_bounds__(512, 1) void k_mx_bwd_mega(MxArgs dg, MxArgs wg, uint32_t* tickets,
+                                                        int look) {
+  constexpr int TAG = KIND == 0 ? 2 : 13;
+  __shared__ __attribute__((aligned(16))) char lds[kMxDgLds > kMxWgLds ? kMxDgLds : kMxWgLds];
+  __shared__ int s_t;
+  __shared__ int s_wp[kMaxE + 1];   // WGRAD records per unit of the experts before e (E <= kMaxE)
+  __shared__ int s_part[512];
+  const int tid = threadIdx.x;
+  const int E = dg.E;
+  const int32_t* gt = dg.mtoff;   // DGRAD m-tile prefix (64-row m-tiles)
+  const int NU = dg.NT;           // units per expert: 256-column weight blocks
+  const int NBw = wg.b_ld / 128;  // dW items per unit
+  const int per_e = ((wg.a_ld + 255) / 256) * NBw;
+  // dW tiles per WGRAD record of expert e, and records per unit
+  auto group = [&](int e) {
+    const int S = (wg.poffsets[e + 1] - wg.poffsets[e] + 63) / 64;
+    return S <= 1 ? kMxWgRecordStages : max(1, kMxWgRecordStages / S);
+  };
+  auto nrec = [&](int e) {
+    const int G = group(e);
+    return (NBw + G - 1) / G;
+  };
+  {   // s_wp: exclusive prefix of nrec over the experts (each thread a run of experts)
+    const int c = (E + 511) / 512;
+    const int e0 = min(E, tid * c), e1 = min(E, e0 + c);
+    int sum = 0;
+    for (int e = e0; e < e1; ++e) sum += nrec(e);
+    s_part[tid] = sum;
+    lds_barrier();
+    for (int off = 1; off < 512; off <<= 1) {   // inclusive scan of the run sums
+      const int v = tid >= off ? s_part[tid - off] : 0;
+      lds_barrier();
+      s_part[tid] += v;
+      lds_barrier();
+    }
+    int run = s_part[tid] - sum;
+    for (int e = e0; e < e1; ++e) {
+      s_wp[e] = run;
+      run += nrec(e);
+    }
+    if (tid == 511) s_wp[E] = s_part[511];
+    lds_barrier();
+  }
+
+  const int xcd = hw_xcd();
+  uint32_t* ticket = tickets + xcd;
+  const int u_lo = xcd_first_unit(wg.mtoff, kMxMegaBwdCw, E, NU, xcd);
+  const int u_hi = xcd_first_unit(wg.mtoff, kMxMegaBwdCw, E, NU, xcd + 1);
+  const int nu = u_hi - u_lo;
+  // DGRAD and WGRAD records before unit u
+  auto dpre = [&](int u) {
+    const int e = u / NU, nt = u - e * NU;
+    return gt[e] * NU + (e < E ? nt * (gt[e + 1] - gt[e]) : 0);
+  };
+  auto wpre = [&](int u) {
+    const int e = u / NU, nt = u - e * NU;
+    return s_wp[e] * NU + (e < E ? nt * (s_wp[e + 1] - s_wp[e]) : 0);
+  };
+  const int d0 = dpre(u_lo), w0 = wpre(u_lo);
+  // records before queue block j
+  auto start = [&](int j) {
+    return dpre(u_lo + min(j, nu)) - d0 + wpre(u_lo + max(0, min(j - look, nu))) - w0;
+  };
+  const int total = dpre(u_hi) - d0 + wpre(u_hi) - w0;
+
+  if (tid == 0) s_t = int(atomicAdd(ticket, 1u));
+  lds_barrier();
+  // one ticket per workgroup: uniform, so everything derived from it is scalar
+  int t = __builtin_amdgcn_readfirstlane(s_t);
+  int j_lo = 0;   // tickets only grow, so blocks only move forward
+  while (t < total) {
+    int hi = nu + look;   // start(j_lo) <= t < start(hi) = total
+    while (hi - j_lo > 1) {
+      const int mid = (j_lo + hi) >> 1;
+      if (start(mid) <= t)
+        j_lo = mid;
+      else
+        hi = mid;
+    }
+    const int j = j_lo;
+    int r = t - start(j);
+    const int cd = j < nu ? dpre(u_lo + j + 1) - dpre(u_lo + j) : 0;
+    const bool dgr = r < cd;
+    const int unit = dgr ? u_lo + j : u_lo + j - look;
+    if (!dgr) r -= cd;
+    const int e = unit / NU, nt = unit - e * NU;
+    int nxt_t = 0;
+    if (tid == 0) nxt_t = int(atomicAdd(ticket, 1u));
+    // lane constants from an opaque copy of the thread index: hoisted out of
+    // the record loop, the two record kinds' constants would be live at once
+    int rtid = tid;
+    asm volatile("" : "+v"(rtid));
+    if (dgr) {
+      mx_dgrad_item<KIND>(dg, lds, rtid, e, nt, r, gt[e + 1] - gt[e], [] {});
+    } else {
+      const int G = group(e);
+      const int b0 = r * G;
+      const int w = e * per_e + nt * NBw;
+      mx_wgrad_run<TW, TAG, ACC>(wg, lds, rtid, w + b0, w + min(NBw, b0 + G), 1);
+    }
+    if (tid == 0) s_t = nxt_t;
+    lds_barrier();
+    t = __builtin_amdgcn_readfirstlane(s_t);
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 template <int ID, typename K>
 static int occupancy_m(K kernel, int threads = 256) {
@@ -1081,6 +1240,35 @@ hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStr
     }
   }
 #undef MOE_MXWG
+  return hipGetLastError();
+}
+
+// Fused backward of one projection (block-scaled): kind 0 = W2 (DGRAD +
+// SwiGLU backward records with dg, dW2 records with wg), 1 = W13 (dX rows,
+// dW13).  tickets: kXcds counters.
+hipError_t launch_mx_bwd_mega(int kind, int dw_f32, const MxArgs& dg, const MxArgs& wg,
+                              uint32_t* tickets, int cus, hipStream_t s) {
+  // units: the DGRAD n-tiles are the dW column tiles (NT x NB dW items per expert)
+  if (dg.NT != (wg.a_ld + 255) / 256) return hipErrorInvalidValue;
+  const unsigned g = grid_m(1, int64_t(cus), cus);
+  const int look = int(g / kXcds);   // the XCD's workgroups
+  const int acc = wg.acc_dw ? 1 : 0;
+#define MOE_MXB(K, TW, ACC) \
+  hipLaunchKernelGGL((k_mx_bwd_mega<K, TW, ACC>), dim3(g), dim3(512), 0, s, dg, wg, tickets, look)
+  if (kind == 0) {
+    if (dw_f32) {
+      if (acc) MOE_MXB(0, float, 1); else MOE_MXB(0, float, 0);
+    } else {
+      if (acc) MOE_MXB(0, uint16_t, 1); else MOE_MXB(0, uint16_t, 0);
+    }
+  } else {
+    if (dw_f32) {
+      if (acc) MOE_MXB(1, float, 1); else MOE_MXB(1, float, 0);
+    } else {
+      if (acc) MOE_MXB(1, uint16_t, 1); else MOE_MXB(1, uint16_t, 0);
+    }
+  }
+#undef MOE_MXB
   return hipGetLastError();
 }
 

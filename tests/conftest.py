@@ -48,12 +48,12 @@ def _poison_workspaces():
             _fill(self.arena[4096:], byte)
         return orig["forward"](self, x, w13, w2, layer, route_ws, h3, prepared)
 
-    def forward_mega(self, x, w13, w2, layer=0, route_ws=None, h3=None):
+    def forward_mega(self, x, w13, w2, layer=0, route_ws=None, h3=None, prepared=None):
         _fill(self.scratch, byte)
         _fill(self.h3 if h3 is None else h3, byte)
         if self.arena is not None and layer == 0:
             _fill(self.arena[4096:], byte)
-        return orig["forward_mega"](self, x, w13, w2, layer, route_ws, h3)
+        return orig["forward_mega"](self, x, w13, w2, layer, route_ws, h3, prepared)
 
     def combine(self, scores, y, y_addend=None, route_ws=None, h3=None):
         if y_addend is None or y_addend.data_ptr() != y.data_ptr():

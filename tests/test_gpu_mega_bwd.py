@@ -1,12 +1,14 @@
 """GPU parity of the fused (Mega) backward (Dist-MoE explainer, section 05,
-Mega backward): for each projection one persistent grid runs the DGRAD and
-WGRAD work records, each expert's DGRAD range next to its WGRAD range; the
-W2 launch's dW2 records wait on per-expert counters for the h2 rows that its
-DGRAD records rebuild from h1.  Every record is one of the staged kernels'
-tiles with the same contraction order, so each gradient must equal the
-staged backward's bit for bit (the staged backward's 256 x 256 dW tiles of
-large experts agree bit for bit with the streaming tiles too); the fused
-gradients are also checked against the fp64 oracle."""
+Mega backward; section 0, the MXFP8 Mega path's two fused backward
+operations): for each projection one persistent grid runs the DGRAD and
+WGRAD work records, each expert's DGRAD range next to its WGRAD range.  In
+BF16 the W2 launch's dW2 records wait on per-block counters for the h2
+columns that its DGRAD records rebuild from h1; in MXFP8 no record waits.
+Every record is one of the staged kernels' tiles with the same contraction
+order, so each gradient must equal the staged backward's bit for bit (the
+staged backward's 256 x 256 dW tiles of large experts agree bit for bit
+with the streaming tiles too); the fused gradients are also checked against
+the fp64 oracle (MXFP8: the quantization-faithful one)."""
 import numpy as np
 import pytest
 import torch
@@ -126,12 +128,76 @@ def test_mega_backward_repeated_calls(B):
             assert torch.equal(u, v), (n, name)
 
 
-def test_mega_backward_rejects_block_scaled(B):
-    T, D, F, E, K = 64, 256, 256, 4, 2
-    layer = B.MoeLayer(T, D, F, E, K, "mxfp8", training=True)
-    lay = make_inputs(T, D, F, E, K, "mxfp8", seed=3, training=True)
-    with pytest.raises(RuntimeError, match="MOE_ERR_UNSUPPORTED"):
-        run_train(layer, lay, flags=B.BWD_MEGA)
+@pytest.mark.parametrize("T,D,F,E,K,zipf,n_pad,dw", [
+    (300, 256, 256, 8, 2, None, 7, "bf16"),     # one expert per XCD, padded routes
+    (1500, 256, 384, 6, 3, 1.2, 0, "bf16"),     # skew: many 64-row m-tiles; F = 3 x 128: half tiles
+    (33, 512, 384, 40, 3, 0.5, 5, "f32"),       # more experts than rows; fp32 dW
+    (700, 128, 128, 2048, 4, None, 0, "bf16"),  # E > 1024
+])
+def test_mega_backward_mxfp8_equals_staged(B, T, D, F, E, K, zipf, n_pad, dw):
+    """MXFP8: the fused backward's records are the staged block-scaled
+    kernels' tiles (no record waits: both of a projection's records read
+    operands quantized before the launch), so every gradient equals the
+    staged backward's bit for bit; against the quantization-faithful oracle
+    as well (small E)."""
+    banner(f"mega backward mxfp8 T={T} D={D} F={F} E={E} K={K} zipf={zipf} dW={dw}")
+    lay = make_inputs(T, D, F, E, K, "mxfp8", zipf=zipf, n_pad=n_pad, seed=T + E + 7,
+                      training=True)
+    outs = {}
+    for mode in ("staged", "mega"):
+        layer = B.MoeLayer(T, D, F, E, K, "mxfp8", dw_dtype=dw, training=True)
+        f = B.BWD_MEGA if mode == "mega" else 0
+        outs[mode] = [t.clone() for t in run_train(layer, lay, flags=f)]
+        torch.cuda.synchronize()
+        assert layer.status()[0] == 0, mode
+    _equal(outs)
+    if E <= 64:
+        ids = lay["ids"].cpu().numpy()
+        _, cache = omx.forward(lay["x"], ids, lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                               keep=True)
+        rdx, rdw13, rdw2, rds = omx.backward(lay["dy"], lay["x"], ids, lay["scores"],
+                                             lay["w13"].cpu(), lay["w2"].cpu(), cache)
+        _, dx, dw13, dw2, ds = outs["mega"]
+        errs = dict(dx=om.max_abs_rel(dx, rdx), ds=om.max_abs_rel(ds, rds),
+                    dw13=om.max_abs_rel(dw13, rdw13), dw2=om.max_abs_rel(dw2, rdw2))
+        report(f"mega backward mxfp8 (bound {TOL['mxfp8']:g})", **errs)
+        for k, v in errs.items():
+            assert v < TOL["mxfp8"], k
+
+
+def test_full_size_mega_backward_mxfp8_equals_staged(B):
+    """T=2048, D=7168, F=2048, E=384, K=6, MXFP8 with Zipf(1.4) routing (the
+    most skewed layer of the ten-layer stack): the fused backward equals the
+    staged backward bit for bit; 32 sampled tokens' dX and dS and the
+    hottest expert's dW match the quantization-faithful oracle."""
+    cfg = wl.CONFIGS["mxfp8_ten_layer"]
+    banner("full-size mega backward mxfp8 zipf 1.4")
+    lay = wl.make_layer(cfg, 3, device="cuda")   # layer 3: Zipf(1.4)
+    T, D, F, E, K = cfg.T, cfg.D, cfg.F, cfg.E, cfg.K
+    outs = {}
+    for mode in ("staged", "mega"):
+        layer = B.MoeLayer(T, D, F, E, K, "mxfp8", training=True)
+        f = B.BWD_MEGA if mode == "mega" else 0
+        outs[mode] = [t.clone() for t in run_train(layer, lay, flags=f)]
+        torch.cuda.synchronize()
+        assert layer.status()[0] == 0, mode
+        del layer
+    _equal(outs)
+    del outs["staged"]
+    _, dx, dw13, dw2, ds = outs["mega"]
+    tokens = full_size_tokens(T, seed=12)
+    ids = lay["ids"].cpu().numpy()
+    counts = torch.bincount(torch.from_numpy(ids[ids >= 0]).long(), minlength=E)
+    experts = [int(torch.argmax(counts))]
+    lay["_wcache"] = {}
+    rdx, rds, rdw13, rdw2 = sampled_backward_ref(lay, tokens, experts, mx=True)
+    errs = dict(dx=om.max_abs_rel(dx[tokens], rdx), ds=om.max_abs_rel(ds[tokens], rds),
+                dw13=om.max_abs_rel(dw13[experts[0]], rdw13[0]),
+                dw2=om.max_abs_rel(dw2[experts[0]], rdw2[0]))
+    report(f"full-size mega backward mxfp8, hottest expert {experts[0]} ({int(counts[experts[0]])} "
+           f"rows) (bound {TOL['mxfp8']:g})", **errs)
+    for k, v in errs.items():
+        assert v < TOL["mxfp8"], k
 
 
 @pytest.mark.parametrize("cfg_name", ["bf16_train_zipf", "bf16_fwd_balanced"])
