@@ -577,25 +577,59 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
 // tile: eight waves, wave (wa, wb) owning dW rows 128 wb .. + 127 and
 // columns 64 wa .. + 63 as 4 x 2 fp32 accumulators of
 // v_mfma_f32_32x32x16_bf16 (8 MFMAs per wave per 16-row step).  A stage is
-// 64 token rows of both operands (256 columns each, 512-byte rows: 64 KiB),
+// 32 token rows of both operands (256 columns each, 512-byte rows: 32 KiB),
 // moved by the gfx950 direct global-to-LDS load (global_load_lds_dwordx4: a
 // wave instruction fills two 512-byte LDS rows, each lane fetching the
-// global chunk that the row's XOR swizzle puts at its slot), into one of two
-// LDS buffers while the other multiplies; the operands are read in MFMA
-// layout with ds_read_b64_tr_b16 as in k_gemm_wgrad.  Token rows past the
-// expert's end are loaded clamped and their B rows zeroed in LDS before the
-// last stage multiplies, so they add nothing.  The tile is staged through
-// LDS in four passes of 64 rows and written as whole 512-byte row segments,
+// global chunk that the row's XOR swizzle puts at its slot).  Four stage
+// buffers keep three stages (96 KiB) in flight while the fourth multiplies
+// (one 64 KiB stage in flight took 1.2 times as long on 2,048-row experts;
+// a fifth buffer measured no faster).  The operands are read
+// in MFMA layout with ds_read_b64_tr_b16 as in k_gemm_wgrad.  Token rows past
+// the expert's end are loaded clamped and their B rows zeroed in LDS before
+// the last stage multiplies, so they add nothing.  The tile is staged
+// through LDS in eight passes of 32 rows while the next item's first two
+// stages stream in, and written as whole 512-byte row segments,
 // non-temporally.  Items: the hot experts' tiles, split over the XCDs by
 // their 64-row stage counts, 4 x 8 blocks of tiles where the grid allows
 // (wgrad_tile); k_gemm_wgrad skips these experts (BwdArgs::hot_wg).
+
+// Barrier of the direct-load pipeline of k_wgrad_hot: this wave's LDS
+// reads and writes have completed (lgkmcnt 0) and every wave has arrived.
+// A workgroup-scope LDS fence would also wait for all of the wave's direct
+// global-to-LDS loads (they count in vmcnt), draining the stages in flight;
+// the wavefront-scope fences only keep the compiler from moving memory
+// accesses across the barrier.  The loads' completion is waited for with
+// explicit vmcnt counts before it.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One direct global-to-LDS load (global_load_lds_dwordx4): lane l's 16
+// bytes at g land at LDS byte address lds + 16 l (lds wave-uniform, in M0).
+// Issued from inline assembly with no output registers: the compiler, which
+// does not follow across a loop which stage buffer such a load writes, then
+// adds no waits of its own before the LDS reads of other stages (it drained
+// every load in flight at one step in four).  Every wait for these loads is
+// explicit: a vmcnt count, then a barrier.  The s_nop is the wait state
+// that an M0 write needs before an LDS DMA.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+
 template <int TAG>
 __global__ __launch_bounds__(512, 1) void k_wgrad_hot(BwdArgs a) {
-  constexpr int kOp = 64 * 512;   // one operand's stage: 64 token rows x 256 columns
+  constexpr int kRows = 32;          // token rows per stage
+  constexpr int kOp = kRows * 512;   // one operand's stage: 32 token rows x 256 columns
+  constexpr int kBuf = 2 * kOp;      // a stage buffer: A then B
   constexpr int kPitch = 512 + 16;   // output-staging row (bf16), padded
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * kOp];
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * kOp];
-  static_assert(64 * kPitch <= 2 * kOp, "a 64-row output pass fits one buffer");
+  constexpr int kNb = 4;             // stage buffers: kNb - 1 stages in flight
+  static_assert((kNb & (kNb - 1)) == 0, "buffer index by mask");
+  __shared__ __attribute__((aligned(1024))) char lds[kNb * kBuf];   // stage s in buffer s mod kNb
+  static_assert(32 * kPitch <= kBuf, "a 32-row output pass fits one buffer");
+  auto buf = [&](int s) { return lds + (s & (kNb - 1)) * kBuf; };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -638,11 +672,11 @@ __global__ __launch_bounds__(512, 1) void k_wgrad_hot(BwdArgs a) {
   const char* asrc = reinterpret_cast<const char*>(a.arows);
   const char* bsrc = reinterpret_cast<const char*>(a.grad);
   // loader roles: waves 0-3 fill the A stage, 4-7 the B stage; wave v & 3
-  // covers stage rows 16 (v & 3) .. + 15, instruction i rows 2 i, 2 i + 1 of
+  // covers stage rows 8 (v & 3) .. + 7, instruction i rows 2 i, 2 i + 1 of
   // those (lanes 0-31 / 32-63), lane slot chunk lane & 31
   const bool aload = wave < 4;
   const int vq = wave & 3;
-  const int ldr = 16 * vq + lh;        // stage row of instruction 0 (+ 2 i)
+  const int ldr = 8 * vq + lh;         // stage row of instruction 0 (+ 2 i)
   const int lchunk = lane & 31;
 
   // this workgroup's units are w0, w0 + per, ...: the first of them, from
@@ -676,35 +710,36 @@ __global__ __launch_bounds__(512, 1) void k_wgrad_hot(BwdArgs a) {
     const int r0 = a.offsets[e];
     t.e = e;
     t.Me = a.offsets[e + 1] - r0;
-    t.S = (t.Me + 63) / 64;
+    t.S = (t.Me + kRows - 1) / kRows;
     wgrad_tile(w - e * per_e, NA, NB, true, false, t.ta, t.tb);
     t.gbase = aload ? asrc + (int64_t(r0) * a_ld + t.ta * 256) * 2
                     : bsrc + (int64_t(r0) * b_ld + t.tb * 256) * 2;
     t.ld2 = int64_t(aload ? a_ld : b_ld) * 2;
   };
-  auto issue = [&](const Item& t, char* buf, int s) {
-    char* dst = buf + (aload ? 0 : kOp) + 16 * vq * 512;
+  // stage s of item t into its buffer: four 1 KiB direct loads per wave
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lds));   // LDS byte address
+  auto issue = [&](const Item& t, int s) {
+    const uint32_t dst = lds0 + (s & (kNb - 1)) * kBuf + (aload ? 0 : kOp) + 8 * vq * 512;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int k = ldr + 2 * i;                      // stage row
-      const int m = min(64 * s + k, t.Me - 1);         // token row, clamped
+      const int m = min(kRows * s + k, t.Me - 1);     // token row, clamped
       const int gc = lchunk ^ ((k & 3) << 2);          // global chunk at this slot
-      __builtin_amdgcn_global_load_lds((gbl_void*)(t.gbase + int64_t(m) * t.ld2 + gc * 16),
-                                       (lds_void*)(dst + i * 1024), 16, 0, 0);
+      dma16(t.gbase + int64_t(m) * t.ld2 + gc * 16, __builtin_amdgcn_readfirstlane(dst + i * 1024));
     }
   };
 
   Item cur, nxt;
   int w = next_hot(first + slot);
-  bool pre = false;   // stage 0 of cur already issued into lds1
+  int pre = 0;   // stages of cur that the previous item issued (into buffers 0, 1)
   while (w < last) {
     decode(w, cur);
     const int S = cur.S;
-    const int tail = cur.Me - 64 * (S - 1);   // live rows of the last stage
+    const int tail = cur.Me - kRows * (S - 1);   // live rows of the last stage
     // zero the B rows of the last stage past the expert's end (after its loads landed)
-    auto zero_tail = [&](char* buf) {
-      char* bb = buf + kOp;
-      for (int i = tid; i < (64 - tail) * 32; i += 512)
+    auto zero_tail = [&](char* b) {
+      char* bb = b + kOp;
+      for (int i = tid; i < (kRows - tail) * 32; i += 512)
         *reinterpret_cast<u32x4*>(bb + (tail + i / 32) * 512 + (i % 32) * 16) = u32x4{0u, 0u, 0u, 0u};
     };
 
@@ -714,11 +749,11 @@ __global__ __launch_bounds__(512, 1) void k_wgrad_hot(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    auto compute = [&](const char* buf) {
-      const char* la = buf;
-      const char* lb = buf + kOp;
+    auto compute = [&](const char* b) {
+      const char* la = b;
+      const char* lb = b + kOp;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kRows / 16; ++q) {
         u32x4 av[2], bv[4];
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
@@ -741,71 +776,73 @@ __global__ __launch_bounds__(512, 1) void k_wgrad_hot(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // stage s multiplies from one buffer while stage s + 1 streams into the
-    // other; each step ends when this wave's loads have landed and every
-    // wave is past its MFMAs (the last stage's tail rows are zeroed between).
-    // Stage 0 sits in lds1 when the previous item prefetched it.
-    char* b0 = pre ? lds1 : lds0;
-    char* b1 = pre ? lds0 : lds1;
-    if (!pre) issue(cur, b0, 0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (S == 1 && tail < 64) {
-      zero_tail(b0);
-      __syncthreads();
-    }
+    // Three stages in flight.  Step s waits until this wave's loads of
+    // stage s have landed (vector memory loads complete in issue order, so
+    // the loads of the stages behind it may stay outstanding), then for every
+    // wave (which also ends every wave's reads of stage s - 1), issues stage
+    // s + 3 into the buffer that stage s - 1 used, and multiplies.  Stores
+    // may complete out of order with loads, so an item that follows a tile's
+    // output stores first waits for everything.
+    if (pre) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    for (int st = pre; st < min(kNb - 1, S); ++st) issue(cur, st);
     for (int s = 0; s < S; ++s) {
-      char* cb = (s & 1) ? b1 : b0;
-      char* nb = (s & 1) ? b0 : b1;
-      if (s + 1 < S) issue(cur, nb, s + 1);
-      compute(cb);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      if (s + 2 == S && tail < 64) {
-        zero_tail(nb);
-        __syncthreads();
+      const int after = min(S - 1 - s, kNb - 2);   // stages in flight behind stage s
+      if (after >= 3)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 12);
+      else if (after == 2)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 8);
+      else if (after == 1)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 4);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      stage_barrier();
+      if (s + 1 == S && tail < kRows) {
+        zero_tail(buf(s));
+        stage_barrier();
       }
+      if (s + kNb - 1 < S) issue(cur, s + kNb - 1);
+      compute(buf(s));
     }
-    // the next item's first stage streams into lds1 while this tile is
-    // staged out through lds0 (both free after the last barrier)
+    stage_barrier();   // every wave past its last MFMAs: all four buffers free
+    // the next item's first two stages stream into buffers 0 and 1 while
+    // this tile is staged out through buffers 2 and 3
     const int wn = next_hot(w + per);
-    pre = wn < last;
-    if (pre) {
+    pre = 0;
+    if (wn < last) {
       decode(wn, nxt);
-      issue(nxt, lds1, 0);
+      pre = min(kNb - 2, nxt.S);
+      for (int st = 0; st < pre; ++st) issue(nxt, st);
     }
 
     // acc[bb][aa][v] = dW[b = tb*256 + 128 wb + 32 bb + lr]
     //                    [a = ta*256 + 64 wa + 32 aa + 8 (v/4) + 4 lh + v%4],
-    // staged in four passes of 64 rows through lds0
+    // staged in eight passes of 32 rows (pass h = 4 wb + bb) through buffers
+    // 2 and 3 in turn; a pass's writes only start after the pass two before
+    // it was read out (every wave has passed the barrier between)
     uint16_t* o = reinterpret_cast<uint16_t*>(a.out) +
                   (int64_t(cur.e) * b_ld + int64_t(cur.tb) * 256) * a_ld + cur.ta * 256;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int r = 128 * wb + 32 * bb;   // first tile row of this accumulator row block
-        if (r / 64 != h) continue;
-        const int rl = r + lr - 64 * h;
+    for (int h = 0; h < 8; ++h) {
+      char* sb = buf(kNb - 2 + (h & 1));
+      if (wb == h / 4) {
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
-          uint16_t* rowp = reinterpret_cast<uint16_t*>(lds0 + rl * kPitch) + 64 * wa + 32 * aa + 4 * lh;
+          uint16_t* rowp = reinterpret_cast<uint16_t*>(sb + lr * kPitch) + 64 * wa + 32 * aa + 4 * lh;
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4)
-            store4<uint16_t>(rowp + 8 * g4, acc[bb][aa][4 * g4], acc[bb][aa][4 * g4 + 1],
-                             acc[bb][aa][4 * g4 + 2], acc[bb][aa][4 * g4 + 3]);
+            store4<uint16_t>(rowp + 8 * g4, acc[h % 4][aa][4 * g4], acc[h % 4][aa][4 * g4 + 1],
+                             acc[h % 4][aa][4 * g4 + 2], acc[h % 4][aa][4 * g4 + 3]);
         }
       }
-      lds_barrier();
+      stage_barrier();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {   // 64 rows x 32 chunks of 16 bytes
-        const int i = tid + 512 * j;
+      for (int jj = 0; jj < 2; ++jj) {   // 32 rows x 32 chunks of 16 bytes
+        const int i = tid + 512 * jj;
         const int rl = i / 32, cc = i % 32;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lds0 + rl * kPitch + cc * 16);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + rl * kPitch + cc * 16);
         __builtin_nontemporal_store(
-            v, reinterpret_cast<u32x4*>(o + int64_t(rl + 64 * h) * a_ld + cc * 8));
+            v, reinterpret_cast<u32x4*>(o + int64_t(rl + 32 * h) * a_ld + cc * 8));
       }
-      lds_barrier();
     }
     w = wn;
   }
