@@ -152,7 +152,7 @@ typedef struct moe_desc {
                                weight-streaming tiles).  Results agree within
                                rounding either way.  In training, 0 and 1
                                also put the bf16 weight gradients of experts
-                               with 512 or more rows on 256 x 256 tiles
+                               with 256 or more rows on 256 x 256 tiles
                                (bit-identical to the streaming tiles; not
                                with MOE_BWD_ACCUMULATE_DW, fp32 dW or
                                widths that are not multiples of 256).

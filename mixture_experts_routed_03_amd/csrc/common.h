@@ -36,11 +36,11 @@ constexpr int kBMH = 256;         // token rows of a hot-expert m-tile
 __host__ __device__ inline bool hot_expert(int c) { return c >= kHotRows; }
 // BF16 weight gradients: an expert with at least kHotWgRows rows runs on
 // k_wgrad_hot's 256 x 256 tiles, the others on k_gemm_wgrad's streaming
-// tiles.  Measured on MI355X: with 32 stages of 64 rows per tile (2,048-row
-// experts) the large tiles took the W13 weight gradient from 0.90 to 0.81 ms;
-// with 4-5 stages (256-row experts) they made the W2 one slower (0.65 to
-// 0.72 ms), the tile's output stores weighing as much as its multiplies.
-constexpr int kHotWgRows = 512;
+// tiles.  Measured on MI355X with three stages in flight in the large tiles:
+// on ~256-row experts (8 or 9 stages of 32 rows) they took the W13 weight
+// gradient from 1.40 to 1.31-1.34 ms and the W2 one from 0.70 to 0.66 ms;
+// cutoffs of 384 and 512 rows measured no better on skewed routing.
+constexpr int kHotWgRows = 256;
 __host__ __device__ inline bool hot_wgrad_expert(int c) { return c >= kHotWgRows; }
 
 // ------------------------------------------------- per-layer planner record

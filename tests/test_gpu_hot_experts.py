@@ -15,7 +15,7 @@ from tests._harness import (TOL, banner, check_route, make_inputs, oracle_forwar
 pytestmark = pytest.mark.gpu
 
 HOT = 256   # rows from which an expert takes the large tiles
-HOT_WG = 512   # rows from which its BF16 weight gradients take them
+HOT_WG = 256   # rows from which its BF16 weight gradients take them
 
 
 @pytest.fixture(scope="module")
@@ -193,12 +193,12 @@ def test_tile_modes_agree(B):
 
 
 @pytest.mark.parametrize("T,D,F,E,K,zipf", [
-    (1200, 512, 256, 5, 2, 1.0),    # 865 and 574 rows on the 256 x 256 tiles; 413, 301, 247 streaming
-    (1500, 256, 384, 6, 3, 1.2),    # dW13 of four experts on them; dW2 (rows of F = 384 values) streaming
+    (1200, 512, 256, 5, 2, 1.0),    # 865, 574, 413, 301 rows on the 256 x 256 tiles; 247 streaming
+    (1500, 256, 384, 6, 3, 1.2),    # dW13 of the experts of 256+ rows on them; dW2 (rows of F = 384 values) streaming
     (2000, 512, 256, 3, 1, None),   # every expert on them, ~670 rows (last stage partly past the end)
 ])
 def test_hot_weight_gradient_tiles_equal_streaming(B, T, D, F, E, K, zipf):
-    """BF16 weight gradients of experts with 512+ rows run on 256 x 256
+    """BF16 weight gradients of experts with 256+ rows run on 256 x 256
     tiles (k_wgrad_hot) in automatic mode, those of smaller experts and the
     forward of these small calls on the streaming tiles; "never" keeps every
     weight gradient on the streaming tiles.  Both contract the same token
