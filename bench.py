@@ -104,8 +104,10 @@ SYMBOLS = {
         "w2_scatter": ("moe::k_mx_fwd<1, 0, 0>", ["gemm_mx.hip", "mxq.h"]),
         "w2_dgrad_swiglu": ("moe::k_mx_dgrad<0>", ["gemm_mx.hip", "mxq.h"]),
         "w13_dgrad": ("moe::k_mx_dgrad<1>", ["gemm_mx.hip", "mxq.h"]),
-        "w2_wgrad": ("moe::k_mx_wgrad<unsigned short, 2, 0>", ["gemm_mx.hip", "mxq.h"]),
-        "w13_wgrad": ("moe::k_mx_wgrad<unsigned short, 13, 0>", ["gemm_mx.hip", "mxq.h"]),
+        "w2_wgrad": (["moe::k_mx_wgrad<unsigned short, 2, 0>", "moe::k_mx_wgrad_hot<2>"],
+                     ["gemm_mx.hip", "mxq.h"]),
+        "w13_wgrad": (["moe::k_mx_wgrad<unsigned short, 13, 0>", "moe::k_mx_wgrad_hot<13>"],
+                      ["gemm_mx.hip", "mxq.h"]),
     },
     "mxfp8_1x32": {
         "w13_swiglu": ("moe::k_mx_fwd<0, 1, 0>", ["gemm_mx.hip", "mxq.h"]),

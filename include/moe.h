@@ -150,14 +150,15 @@ typedef struct moe_desc {
                                per four compute units), 1 = always those
                                tiles, 2 = never (every expert on the
                                weight-streaming tiles).  Results agree within
-                               rounding either way.  In training, 0 and 1
-                               also put the bf16 weight gradients of experts
-                               with 256 or more rows on 256 x 256 tiles
-                               (bit-identical to the streaming tiles; not
-                               with MOE_BWD_ACCUMULATE_DW, fp32 dW or
-                               widths that are not multiples of 256).
-                               Ignored by other
-                               precisions; other values -> MOE_ERR_ARG. */
+                               rounding either way.  In BF16 and MXFP8
+                               training, 0 and 1 also put the bf16 weight
+                               gradients of experts with 256 or more rows on
+                               256 x 256 tiles (bit-identical to the
+                               streaming tiles; not with MOE_BWD_MEGA,
+                               MOE_BWD_ACCUMULATE_DW, fp32 dW or widths that
+                               are not multiples of 256).  The forward
+                               tiling is BF16 only; other values ->
+                               MOE_ERR_ARG. */
 } moe_desc;
 
 /* Byte sizes of the caller-owned buffers (all 256-byte aligned). */

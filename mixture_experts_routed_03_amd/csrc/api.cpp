@@ -187,6 +187,19 @@ static void hot_wgrad(const moe_plan_s* p, void* ws, BwdArgs& a) {
   a.hot_wg = 1;
 }
 
+// MXFP8 weight gradients: the same for k_mx_wgrad_hot (launch_mx_wgrad
+// also requires bf16 dW, no accumulation and widths that are multiples of
+// 256), where the column bundles' exponent offsets and a tile's code offsets
+// fit in 32 bits.
+static void hot_wgrad_mx(const moe_plan_s* p, void* ws, MxArgs& a) {
+  if (p->d.prec != MOE_PREC_MXFP8 || p->d.hot_tiles == 2 || p->R_max < kHotWgRows) return;
+  const int64_t width = std::max<int64_t>(p->d.d, 2 * int64_t(p->d.f));
+  if (width * (p->Rp_max / 32 + 1) >= (int64_t(1) << 31) || 256 * p->Rp_max >= (int64_t(1) << 31))
+    return;
+  a.cst = at<int32_t>(ws, p->rl.cwoff);
+  a.hot_wg = 1;
+}
+
 // Split-K arguments of a BF16/FP32 forward GEMM launch (mode 0: W13, 1: W2).
 static void set_split(const moe_plan_s* p, FwdArgs& a, int mode, char* sc) {
   a.ksplit = mode == 0 ? p->ks13 : p->ks2;
@@ -353,6 +366,7 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
     });
     if (e != hipSuccess) return MOE_ERR_HIP;
   } else {
+    hot_wgrad_mx(p, ws, wg2);
     e = timed(p, "w2_dgrad_swiglu", s, [&] { return launch_mx_dgrad(0, dg2, p->mt_max, cus, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = timed(p, "w2_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 2, wg2, cus, s); });
@@ -379,6 +393,7 @@ moe_status mx_backward(moe_plan_s* p, RouteHdr* hdr, void* ws, char* sc, const v
     });
     if (e != hipSuccess) return MOE_ERR_HIP;
   } else {
+    hot_wgrad_mx(p, ws, wg13);
     e = timed(p, "w13_dgrad", s, [&] { return launch_mx_dgrad(1, dg13, p->mt_max, cus, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = timed(p, "w13_wgrad", s, [&] { return launch_mx_wgrad(dw_f32, 13, wg13, cus, s); });
@@ -608,13 +623,14 @@ moe_status moe_plan_explain(moe_plan_t p, char* buf, size_t cap) {
                   "  experts with >= %d rows: 256 x 256 MFMA forward tiles %s%s\n", kHotRows,
                   kHot[d.hot_tiles], p->hot ? "" : " (not with this shape)");
     s += line;
-    if (d.training && d.hot_tiles != 2 && p->R_max >= kHotWgRows) {
-      std::snprintf(line, sizeof line,
-                    "  experts with >= %d rows: 256 x 256 MFMA weight-gradient tiles "
-                    "(bf16 dW, widths multiples of 256)\n",
-                    kHotWgRows);
-      s += line;
-    }
+  }
+  if ((d.prec == MOE_PREC_BF16 || d.prec == MOE_PREC_MXFP8) && d.training && d.hot_tiles != 2 &&
+      p->R_max >= kHotWgRows) {
+    std::snprintf(line, sizeof line,
+                  "  experts with >= %d rows: 256 x 256 MFMA weight-gradient tiles "
+                  "(bf16 dW, widths multiples of 256)\n",
+                  kHotWgRows);
+    s += line;
   }
   std::snprintf(line, sizeof line, "  route_ws   %10.2f MiB per layer (metadata + planner record)\n",
                 mib(p->rl.total));

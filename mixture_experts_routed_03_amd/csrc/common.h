@@ -214,6 +214,12 @@ struct MxArgs {
   uint8_t* q_out;
   uint8_t* s_out;
   int q_rows;
+  // WGRAD with hot_wg = 1 (bf16 dW, no accumulation, a_ld and b_ld
+  // multiples of 256): the experts of kHotWgRows rows or more run on
+  // k_mx_wgrad_hot's 256 x 256 tiles; cst = routing's 64-row stage prefix of
+  // the other experts (the streaming launch's XCD split)
+  const int32_t* cst;
+  int hot_wg;
 };
 
 // Arguments of the MXFP8 quantizer launches (pointers or layer-record slots:
@@ -319,10 +325,45 @@ __device__ __forceinline__ T* global_ptr(uint64_t addr) {
 // operation of the wave (vmcnt 0; expcnt and lgkmcnt left at their maxima).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// A 32-bit value in the constant address space: read-only for the whole
+// kernel, so a wave-uniform load from it is a scalar (s_load) load, counted
+// in lgkmcnt rather than vmcnt.
+typedef const __attribute__((address_space(4))) int kconst_i32;
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Barrier of the direct-load pipelines (k_wgrad_hot, k_mx_wgrad_hot): this
+// wave's LDS reads and writes have completed (lgkmcnt 0) and every wave
+// has arrived.  A workgroup-scope LDS fence would also wait for all of the
+// wave's direct global-to-LDS loads (they count in vmcnt), draining the
+// stages in flight; the wavefront-scope fences only keep the compiler from
+// moving memory accesses across the barrier.  The loads' completion is
+// waited for with explicit vmcnt counts before it.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Direct global-to-LDS loads (global_load_lds_dwordx4 / _dword): lane l's
+// 16 (4) bytes at g land at LDS byte address lds + 16 l (4 l), lds
+// wave-uniform, in M0.  Issued from inline assembly with no output
+// registers: the compiler, which does not follow across a loop which stage
+// buffer such a load writes, then adds no waits of its own before the LDS
+// reads of other stages (it drained every load in flight at one step in
+// four).  Every wait for these loads is explicit: a vmcnt count, then a
+// barrier.  The s_nop is the wait state that an M0 write needs before an
+// LDS DMA.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds) : "memory");
 }
 
 // Storage element traits: float (F32 plans) or bf16 bits (BF16 / MXFP8 plans).

@@ -593,32 +593,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_wgrad(BwdArgs a) {
 // their 64-row stage counts, 4 x 8 blocks of tiles where the grid allows
 // (wgrad_tile); k_gemm_wgrad skips these experts (BwdArgs::hot_wg).
 
-// Barrier of the direct-load pipeline of k_wgrad_hot: this wave's LDS
-// reads and writes have completed (lgkmcnt 0) and every wave has arrived.
-// A workgroup-scope LDS fence would also wait for all of the wave's direct
-// global-to-LDS loads (they count in vmcnt), draining the stages in flight;
-// the wavefront-scope fences only keep the compiler from moving memory
-// accesses across the barrier.  The loads' completion is waited for with
-// explicit vmcnt counts before it.
-__device__ __forceinline__ void stage_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt at their maxima
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// One direct global-to-LDS load (global_load_lds_dwordx4): lane l's 16
-// bytes at g land at LDS byte address lds + 16 l (lds wave-uniform, in M0).
-// Issued from inline assembly with no output registers: the compiler, which
-// does not follow across a loop which stage buffer such a load writes, then
-// adds no waits of its own before the LDS reads of other stages (it drained
-// every load in flight at one step in four).  Every wait for these loads is
-// explicit: a vmcnt count, then a barrier.  The s_nop is the wait state
-// that an M0 write needs before an LDS DMA.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
-}
-
 template <int TAG>
 __global__ __launch_bounds__(512, 1) void k_wgrad_hot(BwdArgs a) {
   constexpr int kRows = 32;          // token rows per stage

@@ -872,16 +872,26 @@ __device__ __forceinline__ void mx_wgrad_run(const MxArgs& a, char* lds, int tid
   // Work items of this workgroup: w = w0 + i * per below last.
   int wcur = w0;
   auto fill = [&](Item& t) {
-    if (wcur >= last) {
-      t.e = -1;
-      return;
+    int e = 0, p0 = 0, p1 = 0;
+    for (;;) {   // with hot_wg, step over the hot experts' items
+      if (wcur >= last) {
+        t.e = -1;
+        return;
+      }
+      e = wcur / per_e;
+      // scalar loads (constant address space): no wait behind the previous
+      // tile's dW stores, and one round trip per item
+      const int o0 = ((kconst_i32*)a.offsets)[e], o1 = ((kconst_i32*)a.offsets)[e + 1];
+      p0 = ((kconst_i32*)a.poffsets)[e];
+      p1 = ((kconst_i32*)a.poffsets)[e + 1];
+      if (!a.hot_wg || !hot_wgrad_expert(o1 - o0)) break;
+      wcur += ((e + 1) * per_e - wcur + per - 1) / per * per;
     }
     const int w = wcur;
     wcur += per;
-    const int e = w / per_e;
     t.e = e;
-    t.pb = a.poffsets[e];
-    t.mp = a.poffsets[e + 1] - t.pb;
+    t.pb = p0;
+    t.mp = p1 - p0;
     t.S = (t.mp + 63) / 64;
     int ta, tb;
     wgrad_tile(w - e * per_e, NA, NB, TAG == 13 && hot_expert(t.mp), TAG == 2, ta, tb);
@@ -1019,9 +1029,294 @@ __global__ __launch_bounds__(512, 1) void k_mx_wgrad(MxArgs a) {
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int per = gridDim.x / kXcds;
-  const int first = xcd_first_item(a.mtoff, a.E, per_e, xcd);
-  const int last = xcd_first_item(a.mtoff, a.E, per_e, xcd + 1);
+  // with hot_wg the experts of kHotWgRows rows or more are k_mx_wgrad_hot's:
+  // split by the other experts' stages (theirs count 0, plus 1 per item)
+  const int32_t* cost = a.hot_wg ? a.cst : a.mtoff;
+  const int first = xcd_first_item(cost, a.E, per_e, xcd);
+  const int last = xcd_first_item(cost, a.E, per_e, xcd + 1);
   mx_wgrad_run<TW, TAG, ACC>(a, lds, threadIdx.x, first + slot, last, per);
+}
+
+// ------------------------------------------------------------------ WGRAD, hot experts
+// An expert with at least kHotWgRows rows contracts its weight gradient over
+// hundreds to thousands of token rows: MFMA-bound work ("Mixture of Experts:
+// How Routing Becomes GPU Computation", section 1 arithmetic intensity),
+// for which the streaming 128 x 256 tile with one register-staged stage in
+// flight waits on every stage's loads.  As k_wgrad_hot does for BF16, a work
+// item here is a 256 x 256 dW tile: eight waves, wave (wa, wb) owning dW
+// rows 128 wb .. + 127 and columns 64 wa .. + 63 as 4 x 2 accumulators of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (one MFMA step per 64-token stage).  A
+// stage holds 64 tokens of the 256 A and 256 B columns of the tile (E4M3
+// codes, one 64-byte LDS row per column, chunks XOR-swizzled by
+// (column >> 1) & 3) and, per column, the aligned 8-byte window of its
+// exponent bytes that holds the stage's two MX blocks; both are moved by
+// direct global-to-LDS loads (dma16 / dma4), three stages in flight in four
+// LDS buffers.  The last stage of an expert whose padded rows end half-way
+// through it loads in-range chunks in place of the missing ones and zeroes
+// both operands' codes there, and blocks past the expert's end take scale
+// 2^0, as the streaming tiles do: both contract the same tokens in the same
+// MFMA steps, so their gradients are bit-identical.  The tile is staged
+// through LDS in eight passes of 32 rows and written as whole 512-byte row
+// segments, non-temporally.  Items: the hot experts' tiles, split over the
+// XCDs by their 64-row stage counts, 4 x 8 blocks of tiles where the grid
+// allows (wgrad_tile); k_mx_wgrad skips these experts (MxArgs::hot_wg).
+template <int TAG>
+__global__ __launch_bounds__(512, 1) void k_mx_wgrad_hot(MxArgs a) {
+  constexpr int kSeg = 64;                   // codes per column and stage (bytes)
+  constexpr int kOp = 256 * kSeg;            // one operand's codes: 256 columns x 64 bytes
+  constexpr int kExp = 256 * 8;              // one operand's exponent windows
+  constexpr int kBuf = 2 * kOp + 2 * kExp;   // a stage buffer: A, B codes, A, B windows
+  constexpr int kNb = 4;                     // stage buffers: three stages in flight
+  constexpr int kPitch = 512 + 16;           // output-staging row (bf16), padded
+  static_assert((kNb & (kNb - 1)) == 0, "buffer index by mask");
+  __shared__ __attribute__((aligned(1024))) char lds[kNb * kBuf];   // stage s in buffer s mod 4
+  static_assert(32 * kPitch <= kBuf, "a 32-row output pass fits one buffer");
+  auto buf = [&](int s) { return lds + (s & (kNb - 1)) * kBuf; };
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wa = wave & 3;    // 64-column block of the tile
+  const int wb = wave >> 2;   // 128-row block of the tile
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+
+  const RouteHdr* hdr = a.hdr;
+  const int a_ld = a.a_ld, b_ld = a.b_ld;
+  const int NA = a_ld / 256, NB = b_ld / 256;
+  const int per_e = NA * NB;
+  // hot experts' 64-row stages before expert e (routing's cold prefix counts them 0)
+  auto hs = [&](int e) { return a.mtoff[e] - a.cst[e]; };
+  const int E = a.E;
+  if (hs(E) == 0) return;
+  // XCD split: units (expert-major, per_e per expert) of equal total stage cost
+  auto first_unit = [&](int x) {
+    const int64_t W = int64_t(per_e) * hs(E);
+    const int64_t T = W * x / kXcds;
+    int lo = 0, hi = E;   // the largest e with per_e * hs(e) <= T
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (int64_t(per_e) * hs(mid) <= T)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    if (lo >= E) return E * per_e;
+    const int64_t c = hs(lo + 1) - hs(lo);   // >= 1: lo is the largest such e
+    const int64_t i = (T - int64_t(per_e) * hs(lo) + c - 1) / c;
+    return int(min(int64_t(lo) * per_e + i, int64_t(E) * per_e));
+  };
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int per = gridDim.x / kXcds;
+  const int first = first_unit(xcd), last = first_unit(xcd + 1);
+  const uint8_t* qa = a.a_slot >= 0 ? global_ptr<const uint8_t>(rec_ptr_m(hdr, a.a_slot)) : a.qa;
+  const uint8_t* sa = a.a_slot >= 0 ? global_ptr<const uint8_t>(rec_ptr_m(hdr, a.a_slot + 1)) : a.sa;
+  // exponent bytes of each bundle: one per column and 32 padded rows, all
+  // experts (the launcher keeps these offsets, and a tile's code offsets,
+  // below 2^31)
+  const uint32_t nblk = uint32_t(a.poffsets[E]) / 32;
+  const uint32_t sa_end = uint32_t(a_ld) * nblk, sb_end = uint32_t(b_ld) * nblk;
+
+  // loader roles: waves 0-3 fill the A codes and windows, 4-7 the B ones.
+  // Codes: instruction i (< 4) fills columns 64 (v & 3) + 16 i + (lane >> 2),
+  // LDS slot lane & 3, which holds global chunk (lane & 3) ^ ((lane >> 3) & 3)
+  // (the column's swizzle).  Windows: instruction k (< 2) fills dword lane & 1
+  // of column 64 (v & 3) + 32 k + (lane >> 1).
+  const bool aload = wave < 4;
+  const int vq = wave & 3;
+  const int lcol = 64 * vq + (lane >> 2);   // + 16 i
+  const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
+  const int ecol = 64 * vq + (lane >> 1);   // + 32 k
+  const int edw = lane & 1;
+  const uint8_t* qsrc = aload ? qa : a.qb;
+  const uint8_t* ssrc = aload ? sa : a.sb;
+  const uint32_t s_end = aload ? sa_end : sb_end;
+  const int ld = aload ? a_ld : b_ld;
+
+  // this workgroup's units are w0, w0 + per, ...: the first of them, from
+  // w on, that belongs to a hot expert (last: none)
+  auto next_hot = [&](int w) {
+    while (w < last) {
+      const int e = w / per_e;
+      if (hot_wgrad_expert(a.offsets[e + 1] - a.offsets[e])) return w;
+      const int h1 = hs(e + 1);
+      int lo = e + 1, hi = E;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (hs(mid + 1) > h1)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      if (lo >= E) return last;
+      w += (lo * per_e - w + per - 1) / per * per;
+    }
+    return last;
+  };
+  struct Item {
+    int e, ta, tb, mp, nmb, S;
+    const uint8_t* qbase;   // this wave's operand codes: the tile's first column, first token
+    uint32_t sbase;         // this wave's operand exponents: offset of the tile's first column
+    uint32_t a_ex, b_ex;    // the same for the A and B columns the MFMAs read
+  };
+  auto decode = [&](int w, Item& t) {
+    const int e = w / per_e;
+    const int pb = a.poffsets[e];
+    t.e = e;
+    t.mp = a.poffsets[e + 1] - pb;
+    t.nmb = t.mp / 32;
+    t.S = (t.mp + 63) / 64;
+    wgrad_tile(w - e * per_e, NA, NB, true, false, t.ta, t.tb);
+    const int col0 = (aload ? t.ta : t.tb) * 256;
+    t.qbase = qsrc + int64_t(ld) * pb + int64_t(col0) * t.mp;
+    t.sbase = uint32_t(ld) * uint32_t(pb / 32) + uint32_t(col0) * uint32_t(t.nmb);
+    t.a_ex = uint32_t(a_ld) * uint32_t(pb / 32) + uint32_t(t.ta * 256) * uint32_t(t.nmb);
+    t.b_ex = uint32_t(b_ld) * uint32_t(pb / 32) + uint32_t(t.tb * 256) * uint32_t(t.nmb);
+  };
+  // exponent window of a column for stage s: the aligned 8 bytes that hold
+  // its blocks 2 s and 2 s + 1, moved back to lie inside the array
+  auto window = [&](uint32_t off, uint32_t end) { return min(off & ~3u, end - 8u); };
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lds));   // LDS byte address
+  // stage s of item t into its buffer: four 1 KiB code loads and two
+  // 256-byte window loads per wave
+  auto issue = [&](const Item& t, int s) {
+    const uint32_t b0 = lds0 + (s & (kNb - 1)) * kBuf;
+    const uint32_t dq = b0 + (aload ? 0 : kOp) + vq * 64 * kSeg;
+    const int g = 16 * lchunk < t.mp - 64 * s ? lchunk : lchunk - 2;   // in-range chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma16(t.qbase + (uint32_t(lcol + 16 * i) * uint32_t(t.mp) + uint32_t(64 * s + 16 * g)),
+            __builtin_amdgcn_readfirstlane(dq + i * 1024));
+    const uint32_t de = b0 + 2 * kOp + (aload ? 0 : kExp) + vq * 64 * 8;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t off = t.sbase + uint32_t(ecol + 32 * k) * uint32_t(t.nmb) + uint32_t(2 * s);
+      dma4(ssrc + (window(off, s_end) + 4u * edw), __builtin_amdgcn_readfirstlane(de + k * 256));
+    }
+  };
+
+  Item cur, nxt;
+  int w = next_hot(first + slot);
+  int pre = 0;   // stages of cur that the previous item issued (into buffers 0, 1)
+  while (w < last) {
+    decode(w, cur);
+    const int S = cur.S;
+    const bool half = cur.mp - 64 * (S - 1) == 32;   // the last stage holds 32 tokens
+    // zero the codes of tokens 32..63 of both operands in the last stage
+    auto zero_half = [&](char* b) {
+      for (int i = tid; i < 2 * 256 * 2; i += 512) {
+        const int r = i >> 1, c = 2 + (i & 1);   // code row (A then B), chunk
+        *reinterpret_cast<u32x4*>(b + r * kSeg + ((c ^ ((r >> 1) & 3)) << 4)) =
+            u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    auto compute = [&](const char* b, int s) {
+      const char* la = b;
+      const char* lb = b + kOp;
+      const char* ea = b + 2 * kOp;
+      const char* eb = ea + kExp;
+      const int sw = (lr >> 1) & 3;   // the swizzle of every row this lane reads
+      const bool live = 2 * s + lh < cur.nmb;   // this lane's block inside the expert
+      u32x4 a0[2], a1[2];
+      int xa[2];
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) {
+        const int c = 64 * wa + 32 * aa + lr;
+        a0[aa] = *reinterpret_cast<const u32x4*>(la + c * kSeg + ((lh ^ sw) << 4));
+        a1[aa] = *reinterpret_cast<const u32x4*>(la + c * kSeg + (((2 + lh) ^ sw) << 4));
+        const uint32_t off = cur.a_ex + uint32_t(c) * uint32_t(cur.nmb) + uint32_t(2 * s);
+        const int pos = int(off - window(off, sa_end)) + lh;
+        xa[aa] = live ? int(*reinterpret_cast<const uint8_t*>(ea + c * 8 + pos)) : 127;
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int c = 128 * wb + 32 * bb + lr;
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lb + c * kSeg + ((lh ^ sw) << 4));
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(lb + c * kSeg + (((2 + lh) ^ sw) << 4));
+        const uint32_t off = cur.b_ex + uint32_t(c) * uint32_t(cur.nmb) + uint32_t(2 * s);
+        const int pos = int(off - window(off, sb_end)) + lh;
+        const int xb = live ? int(*reinterpret_cast<const uint8_t*>(eb + c * 8 + pos)) : 127;
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) mfma_mx(acc[bb][aa], a0[aa], a1[aa], b0, b1, xa[aa], xb);
+        // at most two B blocks' operands live at once (register pressure)
+        if (bb == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Three stages in flight, as in k_wgrad_hot: step s waits until this
+    // wave's loads of stage s have landed (six per wave per stage; loads
+    // complete in issue order), then for every wave (which also ends every
+    // wave's reads of stage s - 1), issues stage s + 3 into the buffer stage
+    // s - 1 used, and multiplies.  Stores may complete out of order with
+    // loads, so an item that follows a tile's stores first waits for
+    // everything.
+    if (pre) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    for (int st = pre; st < min(kNb - 1, S); ++st) issue(cur, st);
+    for (int s = 0; s < S; ++s) {
+      const int after = min(S - 1 - s, kNb - 2);   // stages in flight behind stage s
+      if (after >= 2)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 12);
+      else if (after == 1)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 6);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      stage_barrier();
+      if (s + 1 == S && half) {
+        zero_half(buf(s));
+        stage_barrier();
+      }
+      if (s + kNb - 1 < S) issue(cur, s + kNb - 1);
+      compute(buf(s), s);
+    }
+    stage_barrier();   // every wave past its last MFMAs: all four buffers free
+    // the next item's first two stages stream into buffers 0 and 1 while
+    // this tile is staged out through buffers 2 and 3
+    const int wn = next_hot(w + per);
+    pre = 0;
+    if (wn < last) {
+      decode(wn, nxt);
+      pre = min(kNb - 2, nxt.S);
+      for (int st = 0; st < pre; ++st) issue(nxt, st);
+    }
+
+    // acc[bb][aa][v] = dW[b = tb*256 + 128 wb + 32 bb + lr]
+    //                    [a = ta*256 + 64 wa + 32 aa + 8 (v/4) + 4 lh + v%4],
+    // staged in eight passes of 32 rows (pass h = 4 wb + bb) through buffers
+    // 2 and 3 in turn; a pass's writes only start after the pass two before
+    // it was read out (every wave has passed the barrier between)
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out0) +
+                  (int64_t(cur.e) * b_ld + int64_t(cur.tb) * 256) * a_ld + cur.ta * 256;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      char* sbp = buf(kNb - 2 + (h & 1));
+      if (wb == h / 4) {
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          uint16_t* rowp = reinterpret_cast<uint16_t*>(sbp + lr * kPitch) + 64 * wa + 32 * aa + 4 * lh;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            store4<uint16_t>(rowp + 8 * g4, acc[h % 4][aa][4 * g4], acc[h % 4][aa][4 * g4 + 1],
+                             acc[h % 4][aa][4 * g4 + 2], acc[h % 4][aa][4 * g4 + 3]);
+        }
+      }
+      stage_barrier();
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {   // 32 rows x 32 chunks of 16 bytes
+        const int i = tid + 512 * jj;
+        const int rl = i / 32, cc = i % 32;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sbp + rl * kPitch + cc * 16);
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4*>(o + int64_t(rl + 32 * h) * a_ld + cc * 8));
+      }
+    }
+    w = wn;
+  }
 }
 
 // ------------------------------------------------------------------ fused (Mega) backward
@@ -1217,9 +1512,14 @@ hipError_t launch_mx_dgrad(int kind, const MxArgs& a, int64_t mt_max, int cus, h
 }
 
 // tag 2: dW2, 13: dW13
-hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStream_t s) {
-  const int64_t items = int64_t(a.E) * ((a.a_ld + 255) / 256) * (a.b_ld / 128);
+hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& args, int cus, hipStream_t s) {
+  const int64_t items = int64_t(args.E) * ((args.a_ld + 255) / 256) * (args.b_ld / 128);
   if (items == 0) return hipSuccess;
+  // the hot experts go to k_mx_wgrad_hot only where it applies; otherwise
+  // every expert stays on k_mx_wgrad
+  MxArgs a = args;
+  a.hot_wg = (args.hot_wg && args.cst && !dw_f32 && !args.acc_dw && args.a_ld % 256 == 0 &&
+              args.b_ld % 256 == 0) ? 1 : 0;
 #define MOE_MXWG(TW, TAG, ACC, ID)                                                            \
   do {                                                                                      \
     const unsigned g = grid_m(occupancy_m<ID>(k_mx_wgrad<TW, TAG, ACC>, 512), items, cus);  \
@@ -1240,6 +1540,13 @@ hipError_t launch_mx_wgrad(int dw_f32, int tag, const MxArgs& a, int cus, hipStr
     }
   }
 #undef MOE_MXWG
+  if (a.hot_wg) {   // the hot experts' 256 x 256 tiles
+    const unsigned g = grid_m(1, int64_t(cus), cus);
+    if (tag == 2)
+      hipLaunchKernelGGL(k_mx_wgrad_hot<2>, dim3(g), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_mx_wgrad_hot<13>, dim3(g), dim3(512), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -224,3 +224,40 @@ def test_hot_weight_gradient_tiles_equal_streaming(B, T, D, F, E, K, zipf):
     for e in range(E):
         assert om.max_abs_rel(dw13[e], rdw13[e]) < TOL["bf16"], e
         assert om.max_abs_rel(dw2[e], rdw2[e]) < TOL["bf16"], e
+
+
+@pytest.mark.parametrize("T,D,F,E,K,zipf", [
+    (1200, 512, 256, 5, 2, 1.0),    # mixed: dW13 and dW2 of the 256+ row experts on the large tiles
+    (1500, 256, 384, 6, 3, 1.2),    # dW13 on them; dW2 (rows of F = 384 values) streaming
+    (2000, 512, 256, 3, 1, None),   # every expert on them; padded rows end half-way through a
+                                    # 64-row stage; the last expert's exponent windows reach the
+                                    # end of the bundles' exponent arrays
+])
+def test_mx_hot_weight_gradient_tiles_equal_streaming(B, T, D, F, E, K, zipf):
+    """MXFP8 weight gradients of experts with 256+ rows run on 256 x 256
+    tiles (k_mx_wgrad_hot) in automatic mode; "never" keeps them on the
+    streaming tiles.  Both contract the same 64-token MFMA steps of the same
+    column bundles with the same block scales (scale 2^0 and zero codes past
+    an expert's padded rows), so every gradient is bit-identical; against
+    the quantization-faithful oracle within the MXFP8 bound."""
+    banner(f"mx hot weight-gradient tiles T={T} D={D} F={F} E={E} K={K} zipf={zipf}")
+    lay = make_inputs(T, D, F, E, K, "mxfp8", zipf=zipf, seed=T + 37, training=True)
+    counts = _counts(lay, E)
+    assert counts.max() >= HOT_WG
+    outs = {}
+    for mode in ("auto", "never"):
+        layer = B.MoeLayer(T, D, F, E, K, "mxfp8", training=True, hot_tiles=mode)
+        outs[mode] = [t.clone() for t in run_train(layer, lay)]
+        torch.cuda.synchronize()
+        assert layer.status() == (0, 0)
+    for name, u, v in zip(("y", "dx", "dw13", "dw2", "ds"), outs["auto"], outs["never"]):
+        assert torch.equal(u, v), name
+    ids = lay["ids"].cpu().numpy()
+    _, cache = omx.forward(lay["x"], ids, lay["scores"], lay["w13"].cpu(), lay["w2"].cpu(),
+                           keep=True)
+    _, rdw13, rdw2, _ = omx.backward(lay["dy"], lay["x"], ids, lay["scores"],
+                                     lay["w13"].cpu(), lay["w2"].cpu(), cache)
+    dw13, dw2 = outs["auto"][2], outs["auto"][3]
+    for e in range(E):
+        assert om.max_abs_rel(dw13[e], rdw13[e]) < TOL["mxfp8"], e
+        assert om.max_abs_rel(dw2[e], rdw2[e]) < TOL["mxfp8"], e
