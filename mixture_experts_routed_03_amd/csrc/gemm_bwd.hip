@@ -411,21 +411,25 @@ __device__ __forceinline__ void wgrad_run(const BwdArgs& a, char* lds, int tid, 
   // Work items of this workgroup: w = w0 + i * per below last.
   int wcur = w0;
   auto fill = [&](Item& t) {
-    int e = 0;
+    int e = 0, o0 = 0, o1 = 0;
     for (;;) {   // with hot_wg, step over the hot experts' items
       if (wcur >= last) {
         t.e = -1;
         return;
       }
       e = wcur / per_e;
-      if (!a.hot_wg || !hot_wgrad_expert(a.offsets[e + 1] - a.offsets[e])) break;
+      // scalar loads (constant address space): no wait behind the previous
+      // tile's dW stores
+      o0 = ((kconst_i32*)a.offsets)[e];
+      o1 = ((kconst_i32*)a.offsets)[e + 1];
+      if (!a.hot_wg || !hot_wgrad_expert(o1 - o0)) break;
       wcur += ((e + 1) * per_e - wcur + per - 1) / per * per;
     }
     const int w = wcur;
     wcur += per;
     t.e = e;
-    t.r0 = a.offsets[e];
-    t.Me = a.offsets[e + 1] - t.r0;
+    t.r0 = o0;
+    t.Me = o1 - o0;
     t.S = (t.Me + 63) / 64;
     int ta, tb;
     wgrad_tile(w - e * per_e, NA, NB, TAG == 13 && hot_expert(t.Me), TAG == 2, ta, tb);
