@@ -202,27 +202,53 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   if (tid < 2 * kXcds) hdr->wq[tid] = 0u;
 }
 
+// Lanes of this wave below the calling lane whose key equals its key: one
+// ballot per key bit keeps, in each lane's mask, the lanes that agree with
+// it on that bit.  Every lane of the wave must call it (no lane masked off);
+// keys are below 2^nbits.
+__device__ __forceinline__ int lanes_below_equal(uint32_t key, int nbits) {
+  uint64_t same = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  return __popcll(same & ((1ull << (threadIdx.x & 63)) - 1ull));
+}
+
+// Routes of earlier waves in sid (16-byte aligned, -1 = no route) whose
+// expert is id: every lane of the wave reads the same four words per step.
+__device__ __forceinline__ int earlier_waves_equal(const int32_t* sid, int id) {
+  const int4* s4 = reinterpret_cast<const int4*>(sid);
+  int rank = 0;
+  for (int q = 0; q < (int(threadIdx.x) >> 6) * 16; ++q) {
+    const int4 v = s4[q];
+    rank += (v.x == id) + (v.y == id) + (v.z == id) + (v.w == id);
+  }
+  return rank;
+}
+
 __global__ __launch_bounds__(256) void k_route_rank(const int32_t* __restrict__ ids, int64_t n,
                                                     int E, const int32_t* __restrict__ chunk_base,
                                                     int32_t* __restrict__ sorted_route,
                                                     int32_t* __restrict__ route_to_row) {
-  __shared__ int32_t sid[kRankChunk];
+  __shared__ __align__(16) int32_t sid[kRankChunk];
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t r = int64_t(c) * kRankChunk + tid;
   int id = r < n ? ids[r] : -1;
   const bool valid = id >= 0 && id < E;
   sid[tid] = valid ? id : -1;
+  // earlier routes of the same expert inside this chunk: in this wave, then
+  // in the earlier waves
+  int rank = lanes_below_equal(valid ? uint32_t(id + 1) : 0u, 32 - __clz(E));
   __syncthreads();
   if (r >= n) return;
   if (!valid) {
     route_to_row[r] = -1;
     return;
   }
-  // Earlier routes of the same expert inside this chunk.  Every lane reads
-  // the same LDS word per step (broadcast), so the loop is conflict-free.
-  int rank = 0;
-  for (int q = 0; q < tid; ++q) rank += (sid[q] == id);
+  rank += earlier_waves_equal(sid, id);
   const int row = chunk_base[int64_t(c) * E + id] + rank;
   sorted_route[row] = int32_t(r);
   route_to_row[r] = row;
@@ -247,7 +273,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
                                                       int32_t* __restrict__ sorted_route,
                                                       int32_t* __restrict__ route_to_row,
                                                       RouteHdr* __restrict__ hdr) {
-  __shared__ int32_t sid[kSmallRoutes];
+  __shared__ __align__(16) int32_t sid[kSmallRoutes];
   __shared__ int32_t cnt[kMaxE];   // counts, then each expert's first row
   __shared__ int sh[16 * kScans];
   __shared__ int carry[kScans];
@@ -266,6 +292,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
     }
   }
   sid[tid] = id;
+  const int below = lanes_below_equal(uint32_t(id + 1), 32 - __clz(E));   // id -1: key 0
   __syncthreads();
   if (id >= 0) atomicAdd(&cnt[id], 1);
   bad = __syncthreads_or(bad);
@@ -306,10 +333,8 @@ __global__ __launch_bounds__(1024) void k_route_small(const int32_t* __restrict_
     if (id < 0) {
       route_to_row[tid] = -1;
     } else {
-      // earlier routes of the same expert (every lane reads the same word per step)
-      int rank = 0;
-      for (int q = 0; q < tid; ++q) rank += (sid[q] == id);
-      const int row = cnt[id] + rank;
+      // earlier routes of the same expert: in this wave, then in earlier waves
+      const int row = cnt[id] + below + earlier_waves_equal(sid, id);
       sorted_route[row] = tid;
       route_to_row[tid] = row;
     }
@@ -397,7 +422,6 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
   int32_t* tot = cnt;
   int32_t* pre = cnt + E;
   int32_t* wcnt = cnt + 2 * E;
-  __shared__ __align__(16) int32_t sid[kRankChunk];
   __shared__ int sh[4 * kScans];
   __shared__ int s_mx;
   const int c = blockIdx.x;
@@ -474,24 +498,18 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
     }
   }
   atomicMax(&s_mx, mx);
-  sid[tid] = mine < n ? my_id : -1;
+  // earlier lanes of this wave with the same expert (key 0: no valid route)
+  const int below = lanes_below_equal(mine < n ? uint32_t(my_id + 1) : 0u, 32 - __clz(E));
   __syncthreads();
   if (mine < n) {
     if (my_id < 0) {
       route_to_row[mine] = -1;
     } else {
       // earlier routes of the same expert in this chunk: those of the earlier
-      // waves (counted), then the earlier lanes of this wave (every lane reads
-      // the same four LDS words per step)
+      // waves (counted), then the earlier lanes of this wave
       const int w = tid >> 6;
-      int rank = 0;
+      int rank = below;
       for (int u = 0; u < w; ++u) rank += wcnt[u * E + my_id];
-      const int4* s4 = reinterpret_cast<const int4*>(sid);
-      for (int q = w * 16; q < (tid >> 2); ++q) {
-        const int4 v = s4[q];
-        rank += (v.x == my_id) + (v.y == my_id) + (v.z == my_id) + (v.w == my_id);
-      }
-      for (int q = tid & ~3; q < tid; ++q) rank += (sid[q] == my_id);
       const int row = pre[my_id] + rank;
       sorted_route[row] = mine;
       route_to_row[mine] = row;
