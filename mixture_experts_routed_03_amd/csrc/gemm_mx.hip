@@ -107,17 +107,21 @@ __device__ __forceinline__ void load4_bf16(const uint16_t* p, float* f) {
 // otherwise the record waits for them before its first loads.
 constexpr int kMxMegaSpin = 1 << 22;   // polls (each followed by a short sleep)
 
-template <int MODE, int W1, int FP4>
+template <int MODE, int W1, int FP4, int RING = 0>
 __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a, MxArgs a2, uint32_t* msync, int look) {
   static_assert(!FP4 || W1, "4-bit weights come in 1x32 blocks");
+  static_assert(RING == 0 || (MODE != 2 && !W1 && RING >= 3 && RING <= 5),
+                "the ring of direct loads serves the MXFP8 32x32 staged passes");
   constexpr int kW = 128 * 128;      // weight stage: 128 rows x 128 bytes
   constexpr int kA = kBM * 128;      // token stage: 64 rows x 128 bytes
   constexpr int kXb = FP4 ? 8 : 4;   // exponent bytes per row and stage
   constexpr int kSc = kBM * kXb;     // token scales of the stage
   // + the weight exponents: one dword per wave (32x32) or per weight row (1x32)
-  constexpr int kStage = kW + kA + kSc + (W1 ? 128 * kXb : 16);
+  // (the ring's weight exponents: 64 dwords, lane l's of wave l mod 4)
+  constexpr int kStage = kW + kA + kSc + (RING ? 256 : W1 ? 128 * kXb : 16);
+  constexpr int kNbuf = RING ? RING : 2;      // LDS stage buffers
   constexpr int kXch = 2 * 2 * 16 * 64 * 4;   // SwiGLU epilogue: up halves of two waves
-  __shared__ __attribute__((aligned(16))) char lds[2 * kStage + (MODE != 1 ? kXch : 0)];
+  __shared__ __attribute__((aligned(16))) char lds[kNbuf * kStage + (MODE != 1 ? kXch : 0)];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -227,6 +231,29 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a, MxArgs a2, uint32_t* m
     // token exponents are grouped by stage: the kXb bytes of (s, row) at
     // (s * sa_rows + row) * kXb
     I.ts = reinterpret_cast<const uint32_t*>(A.sa) + int64_t(row0 + min(tid & 63, rows - 1)) * (kXb / 4);
+    if constexpr (RING > 0) {
+      // Direct loads: load j of this wave fills the eight tile rows from
+      // r0 = 32 wave + 8 j (weights) or 16 wave + 8 j (tokens); lane l
+      // fetches the chunk of row r0 + l / 8 that the swizzle puts at slot
+      // l % 8 of that row.
+      const int lq = lane >> 3, ls = lane & 7;
+      auto chunk = [&](int r) { return (ls ^ ((r ^ (r >> 3)) & 7)) << 4; };
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rho = 32 * wave + 8 * j + lq;
+        const int wr = md == 0 ? (rho < 64 ? nt * 64 + rho : A.F + nt * 64 + rho - 64)
+                               : nt * 128 + rho;
+        I.w[j] = A.qw + (int64_t(e) * A.N + wr) * Kbi + chunk(rho);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 16 * wave + 8 * j + lq;
+        I.t[j] = A.qa + int64_t(row0 + min(r, rows - 1)) * Kbi + chunk(r);
+      }
+      const int q = lane & 3;   // the wave whose block exponents this lane fetches
+      const int q0 = md == 0 ? ((q < 2 ? 0 : A.F) + nt * 64 + (q & 1) * 32) : nt * 128 + q * 32;
+      I.ws = reinterpret_cast<const uint32_t*>(A.sw + (int64_t(e) * (A.N / 32) + q0 / 32) * KBi);
+    }
   };
   // MODE 2 (W1 weights): the exponent rows of the W13 and W2 weights differ
   auto sw_rows = [&](const Item& I) { return MODE == 2 && I.md == 1 ? b2.sw_rows : a.sw_rows; };
@@ -351,84 +378,9 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a, MxArgs a2, uint32_t* m
   auto take = [&]() { return MODE == 2 ? int(atomicAdd(ticket, 1u)) : wq_take(hdr, xcd); };
   // MODE 2: W13 records of expert e, which its W2 records wait for
   auto need = [&](int e) { return uint32_t((gt[e + 1] - gt[e]) * a.NT); };
-  const bool dyn = MODE == 2 || hdr->max_count > kBM;
-  const int slot = blockIdx.x / kXcds;
-  __shared__ int s_q[2];
-  __shared__ int s_ok;
-  if (dyn && tid == 0) {
-    s_q[0] = take();
-    s_q[1] = take();
-  }
-  lds_barrier();
-  int it = dyn ? s_q[0] : slot, itn = dyn ? s_q[1] : slot + per;
-  if (valid(it)) setup(index(it), cur);
-  bool primed = false;  // buffer 0 / R1 / R0 already hold stages 0 / 1 / 2 of cur
-  for (; valid(it);) {
-    const int S = cur.S;
-    // Prefetch across items needs three stages per item (the three stages in
-    // flight at an item's end must all belong to the next item).
-    cross = valid(itn) && S >= 3;
-    if (cross) {
-      setup(index(itn), nxt);
-      if (MODE == 2) {
-        cross = nxt.S >= 3;
-        if (nxt.md == 1) {   // a W2 record: only with its h2 rows complete
-          if (tid == 0) s_ok = atomicAdd(&ready[nxt.e], 0u) >= need(nxt.e);
-          lds_barrier();
-          cross = cross && s_ok;
-        }
-      }
-    }
-    acc0 = f32x16{};
-    acc1 = f32x16{};
-
-    // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
-    // s + 1 and R0 stage s + 2.
-    if (!primed) {
-      if (MODE == 2 && cur.md == 1) {   // wait (bounded) for the h2 rows
-        if (tid == 0) {
-          int n = 0;
-          while (atomicAdd(&ready[cur.e], 0u) < need(cur.e) && ++n < kMxMegaSpin)
-            __builtin_amdgcn_s_sleep(4);
-          if (n >= kMxMegaSpin)
-            atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_SYNC_TIMEOUT);
-        }
-        lds_barrier();
-      }
-      load(R0, S0, 0);
-      load(R1, S1, 1);
-      store(R0, S0, 0);
-      load(R0, S0, 2);
-      lds_barrier();
-    }
-    for (int s = 0; s + 1 < S; s += 2) {
-      compute(0);
-      store(R1, S1, 1);
-      load(R1, S1, s + 3);
-      lds_barrier();
-      compute(1);
-      store(R0, S0, 0);
-      load(R0, S0, s + 4);
-      lds_barrier();
-    }
-    if (S & 1) {
-      compute(0);
-      lds_barrier();
-      if (cross) {   // R1, R0 hold stages 0, 1 of the next item
-        store(R1, S1, 0);
-#pragma unroll
-        for (int j = 0; j < 6; ++j) R1[j] = R0[j];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S1[j] = S0[j];
-        load(R0, S0, S + 2);
-        lds_barrier();
-      }
-    }
+  // The item's epilogue (as the BF16 kernels): acc[b][v] = C[row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
+  auto epilogue = [&]() {
     const int nt = cur.nt, row0 = cur.row0, rows = cur.rows;
-    int taken = 0;
-    if (dyn && tid == 0) taken = take();
-
-    // Epilogue (as the BF16 kernels): acc[b][v] = C[row 8*(v/4) + 4*lh + v%4][token 32*b + lr].
     const int md = MODE == 2 ? cur.md : MODE;
     if (md == 0) {
       const int F = a.F;
@@ -444,7 +396,7 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a, MxArgs a2, uint32_t* m
             store4<uint16_t>(o + 8 * g, acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
         }
       }
-      float* xch = reinterpret_cast<float*>(lds + 2 * kStage);  // not the stage buffers
+      float* xch = reinterpret_cast<float*>(lds + kNbuf * kStage);  // not the stage buffers
       if (wave >= 2) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -543,6 +495,158 @@ __global__ __launch_bounds__(256) void k_mx_fwd(MxArgs a, MxArgs a2, uint32_t* m
         }
       }
     }
+  };
+
+  const bool dyn = MODE == 2 || hdr->max_count > kBM;
+  const int slot = blockIdx.x / kXcds;
+  __shared__ int s_q[2];
+  __shared__ int s_ok;
+  if (dyn && tid == 0) {
+    s_q[0] = take();
+    s_q[1] = take();
+  }
+  lds_barrier();
+  int it = dyn ? s_q[0] : slot, itn = dyn ? s_q[1] : slot + per;
+  if (valid(it)) setup(index(it), cur);
+  if constexpr (RING > 0) {
+    // RING stage buffers in LDS filled by direct global-to-LDS loads, RING - 1
+    // stages in flight, continuing into the next item's first stages while
+    // an item ends (its epilogue uses no stage buffer).  Per wave and stage:
+    // four weight and two token loads of 1 KiB, then one 256-byte exponent
+    // load (waves 0, 2: the token exponents; waves 1, 3: the four waves'
+    // block exponents; both pairs write identical bytes).
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lds));   // LDS byte address
+    auto issue = [&](const Item& I, int st, int b) {
+      const uint32_t base = lds0 + uint32_t(b) * kStage;
+      const int64_t off = int64_t(st) * 128;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma16(I.w[j] + off, __builtin_amdgcn_readfirstlane(base + (32 * wv + 8 * j) * 128));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        dma16(I.t[j] + off, __builtin_amdgcn_readfirstlane(base + kW + (16 * wv + 8 * j) * 128));
+      if (wv & 1)
+        dma4(I.ws + st, __builtin_amdgcn_readfirstlane(base + kW + kA + kSc));
+      else
+        dma4(I.ts + int64_t(st) * a.sa_rows, __builtin_amdgcn_readfirstlane(base + kW + kA));
+    };
+    // until this wave's loads of the stage `after` stages before the newest
+    // have landed (7 per stage; loads complete in issue order)
+    auto wait_behind = [&](int after) {
+      if (after >= 3)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (21 & 15) | ((21 >> 4) << 14));
+      else if (after == 2)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 14);
+      else if (after == 1)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 7);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    };
+    int bq = 0;    // buffer of cur's stage 0
+    int pre = 0;   // stages of cur that the previous item issued
+    for (; valid(it);) {
+      const int S = cur.S;
+      const bool ahead = valid(itn) && S >= RING - 1;   // prefetch into the next item
+      if (ahead) setup(index(itn), nxt);
+      acc0 = f32x16{};
+      acc1 = f32x16{};
+      for (int st = pre; st < min(RING - 1, S); ++st) issue(cur, st, (bq + st) % RING);
+      int b = bq;   // buffer of stage s
+      for (int s = 0; s < S; ++s) {
+        wait_behind(ahead ? RING - 2 : min(S - 1 - s, RING - 2));
+        stage_barrier();   // stage s is in; every wave is done with stage s - 1
+        const int t = s + RING - 1;
+        const int bt = b == 0 ? RING - 1 : b - 1;   // the buffer of stage s - 1
+        if (t < S)
+          issue(cur, t, bt);
+        else if (ahead)
+          issue(nxt, t - S, bt);
+        compute(b);
+        b = b + 1 == RING ? 0 : b + 1;
+      }
+      int taken = 0;
+      if (dyn && tid == 0) taken = take();
+      epilogue();
+      if (dyn && tid == 0) s_q[0] = taken;
+      lds_barrier();
+      pre = ahead ? RING - 1 : 0;
+      if (ahead)
+        cur = nxt;
+      else if (valid(itn))
+        setup(index(itn), cur);
+      bq = b;
+      it = itn;
+      itn = dyn ? s_q[0] : itn + per;
+    }
+    if (dyn && tid == 0) wq_finish(hdr, xcd, per);
+    return;
+  }
+  bool primed = false;  // buffer 0 / R1 / R0 already hold stages 0 / 1 / 2 of cur
+  for (; valid(it);) {
+    const int S = cur.S;
+    // Prefetch across items needs three stages per item (the three stages in
+    // flight at an item's end must all belong to the next item).
+    cross = valid(itn) && S >= 3;
+    if (cross) {
+      setup(index(itn), nxt);
+      if (MODE == 2) {
+        cross = nxt.S >= 3;
+        if (nxt.md == 1) {   // a W2 record: only with its h2 rows complete
+          if (tid == 0) s_ok = atomicAdd(&ready[nxt.e], 0u) >= need(nxt.e);
+          lds_barrier();
+          cross = cross && s_ok;
+        }
+      }
+    }
+    acc0 = f32x16{};
+    acc1 = f32x16{};
+
+    // Pipeline: at the top of each pass LDS buffer 0 holds stage s, R1 stage
+    // s + 1 and R0 stage s + 2.
+    if (!primed) {
+      if (MODE == 2 && cur.md == 1) {   // wait (bounded) for the h2 rows
+        if (tid == 0) {
+          int n = 0;
+          while (atomicAdd(&ready[cur.e], 0u) < need(cur.e) && ++n < kMxMegaSpin)
+            __builtin_amdgcn_s_sleep(4);
+          if (n >= kMxMegaSpin)
+            atomicOr(const_cast<uint32_t*>(&hdr->status), MOE_STATUS_SYNC_TIMEOUT);
+        }
+        lds_barrier();
+      }
+      load(R0, S0, 0);
+      load(R1, S1, 1);
+      store(R0, S0, 0);
+      load(R0, S0, 2);
+      lds_barrier();
+    }
+    for (int s = 0; s + 1 < S; s += 2) {
+      compute(0);
+      store(R1, S1, 1);
+      load(R1, S1, s + 3);
+      lds_barrier();
+      compute(1);
+      store(R0, S0, 0);
+      load(R0, S0, s + 4);
+      lds_barrier();
+    }
+    if (S & 1) {
+      compute(0);
+      lds_barrier();
+      if (cross) {   // R1, R0 hold stages 0, 1 of the next item
+        store(R1, S1, 0);
+#pragma unroll
+        for (int j = 0; j < 6; ++j) R1[j] = R0[j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S1[j] = S0[j];
+        load(R0, S0, S + 2);
+        lds_barrier();
+      }
+    }
+    int taken = 0;
+    if (dyn && tid == 0) taken = take();
+    epilogue();
     if (dyn && tid == 0) s_q[0] = taken;
     lds_barrier();
     if (!cross) {
@@ -1465,17 +1569,20 @@ static unsigned grid_m(int per_cu, int64_t items, int cus) {
   return unsigned(std::max<int64_t>(g, kXcds));
 }
 
+// Stage buffers of the MXFP8 (32x32) forward passes' direct-load ring.
+constexpr int kMxRing = 4;
+
 // mode 0: W13 (+ SwiGLU), 1: W2 -> slots
 hipError_t launch_mx_fwd(int mode, const MxArgs& a, int64_t mt_max, int cus, hipStream_t s) {
   if (mt_max == 0) return hipSuccess;
-#define MOE_MXF(M, W, P, ID)                                                                   \
-  hipLaunchKernelGGL((k_mx_fwd<M, W, P>),                                                     \
-                     dim3(grid_m(occupancy_m<ID>(k_mx_fwd<M, W, P>), mt_max * a.NT, cus)), \
+#define MOE_MXF(M, W, P, R, ID)                                                                   \
+  hipLaunchKernelGGL((k_mx_fwd<M, W, P, R>),                                                     \
+                     dim3(grid_m(occupancy_m<ID>(k_mx_fwd<M, W, P, R>), mt_max * a.NT, cus)), \
                      dim3(256), 0, s, a, a, nullptr, 0)
   if (mode == 0) {
-    if (a.fp4) MOE_MXF(0, 1, 1, 14); else if (a.w1x32) MOE_MXF(0, 1, 0, 12); else MOE_MXF(0, 0, 0, 0);
+    if (a.fp4) MOE_MXF(0, 1, 1, 0, 14); else if (a.w1x32) MOE_MXF(0, 1, 0, 0, 12); else MOE_MXF(0, 0, 0, kMxRing, 0);
   } else {
-    if (a.fp4) MOE_MXF(1, 1, 1, 15); else if (a.w1x32) MOE_MXF(1, 1, 0, 13); else MOE_MXF(1, 0, 0, 1);
+    if (a.fp4) MOE_MXF(1, 1, 1, 0, 15); else if (a.w1x32) MOE_MXF(1, 1, 0, 0, 13); else MOE_MXF(1, 0, 0, kMxRing, 1);
   }
 #undef MOE_MXF
   return hipGetLastError();
