@@ -447,7 +447,8 @@ moe_status moe_plan_create(const moe_desc* desc, moe_plan_t* out) {
     // with 32-bit byte offsets and stores 256-column W2 tiles
     const int64_t lim = int64_t(1) << 32;
     p->hot = d.prec == MOE_PREC_BF16 && d.hot_tiles != 2 && d.d % 256 == 0 &&
-             int64_t(4) * d.f * d.d < lim && d.t_max * d.d * 2 < lim && p->R_max * d.f * 2 < lim;
+             int64_t(4) * d.f * d.d < lim && int64_t(2) * d.t_max * d.d < lim &&
+             p->R_max * d.f * 2 < lim;
   }
   const int64_t E = d.e, D = d.d, F = d.f, R = p->R_max, es = p->es, Rp = p->Rp_max;
   const bool mx = d.prec == MOE_PREC_MXFP8;

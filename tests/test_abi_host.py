@@ -187,6 +187,18 @@ def test_plan_hot_tiles_need_32bit_offsets(b):
             b.moe_plan_destroy(p)
 
 
+def test_plan_hot_tiles_token_rows_need_32bit_offsets(b):
+    """The token rows are addressed with 32-bit byte offsets too: t_max x D
+    bf16 values must span less than 4 GiB (computed in 64 bits; in 32 bits
+    2 * 2^17 * 16,384 wraps to 0)."""
+    for t, on in ((1 << 16, True), (1 << 17, False)):
+        p = b.moe_plan_create(t, 16384, 256, 8, 2, "bf16", hot_tiles="always")
+        try:
+            assert ("not with this shape" in b.moe_plan_explain(p)) != on, t
+        finally:
+            b.moe_plan_destroy(p)
+
+
 @pytest.mark.parametrize("t_max,D,F,E,K,prec,expect", [
     (1, 7168, 2048, 384, 6, "bf16", (8, 3)),     # decode, one token: 192 x 8 and 336 x 3 items
     (8, 7168, 2048, 384, 6, "bf16", None),       # 1,536 W13 items: no split
