@@ -52,6 +52,20 @@ def test_route_maximum_route_count(B):
     assert layer.status()[0] == 0
 
 
+def test_route_unaligned_ids(B):
+    """ids at an address that is 4-byte but not 16-byte aligned (a slice of a
+    larger buffer): the same permutation as the oracle's."""
+    T, E, K = 2048, 384, 6
+    banner("route unaligned ids")
+    layer = B.MoeLayer(T, 128, 128, E, K, "bf16")
+    ids, _ = wl.make_routing(T, E, K, zipf_s=1.2, seed=5)
+    buf = torch.full((T * K + 4,), -1, dtype=torch.int32, device="cuda")
+    buf[1:1 + T * K] = torch.from_numpy(ids.ravel()).cuda()
+    layer.route(buf[1:1 + T * K].view(T, K))
+    check_route(layer.readback(T), ids, E)
+    assert layer.status()[0] == 0
+
+
 def test_route_bad_ids_flagged(B):
     banner("route bad ids")
     layer = B.MoeLayer(4, 128, 128, 4, 2, "bf16")
