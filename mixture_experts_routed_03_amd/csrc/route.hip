@@ -403,7 +403,7 @@ __device__ void block_scan256(int* v /* [N] */, int* sh /* [N][4] */) {
 // read of every id would grow with the square of the call) and for more
 // experts than its LDS counters fit.
 constexpr int kChunkedRoutes = 32768;
-constexpr int kChunkedMaxE = 2560;   // 6 E counters in LDS, within 64 KiB
+constexpr int kChunkedMaxE = 2560;   // 6 E + 2 counters in LDS, within 64 KiB
 
 __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict__ ids, int n,
                                                        int E, int T,
@@ -416,22 +416,24 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
                                                        int32_t* __restrict__ sorted_route,
                                                        int32_t* __restrict__ route_to_row,
                                                        RouteHdr* __restrict__ hdr) {
-  // [E] routes per expert, [E] routes before this chunk, then [4][E] the
-  // chunk's routes per expert in each of its four waves
+  // [E + 1] routes per expert, [E + 1] routes before this chunk (word E of
+  // each counts the invalid ids, so that every route takes an unconditional
+  // atomic), then [4][E] the chunk's routes per expert in each of its four
+  // waves
   extern __shared__ int32_t cnt[];
   int32_t* tot = cnt;
-  int32_t* pre = cnt + E;
-  int32_t* wcnt = cnt + 2 * E;
+  int32_t* pre = cnt + E + 1;
+  int32_t* wcnt = cnt + 2 * E + 2;
   __shared__ int sh[4 * kScans];
   __shared__ int s_mx;
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
-  for (int e = tid; e < 6 * E; e += kRankChunk) cnt[e] = 0;
+  for (int e = tid; e < 6 * E + 2; e += kRankChunk) cnt[e] = 0;
   if (tid == 0) s_mx = 0;
   __syncthreads();
   const int mine = c * kRankChunk + tid;   // this thread's route of the chunk
   const int before = c * kRankChunk;       // routes of the earlier chunks
-  int my_id = -1, bad = 0;
+  int bad = 0;
   constexpr int kBatch = 48;   // independent loads in flight per thread (12,288 routes: one batch)
   for (int r0 = 0; r0 < n; r0 += kRankChunk * kBatch) {
     int v[kBatch];
@@ -442,16 +444,17 @@ __global__ __launch_bounds__(256) void k_route_chunked(const int32_t* __restrict
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int r = r0 + kRankChunk * k + tid;
       const int id = v[k];
-      const bool valid = id >= 0 && id < E;
-      if (id < -1 || id >= E) bad = 1;
-      // one LDS atomic per route: earlier chunks count into pre, the rest
-      // into tot, and tot becomes the total below
-      if (valid) atomicAdd(r < before ? &pre[id] : &tot[id], 1);
-      if (r == mine) my_id = valid ? id : -1;
+      bad |= id < -1 || id >= E;
+      // one LDS atomic per route: earlier chunks (a wave-uniform choice, as
+      // chunks are kRankChunk-aligned) count into pre, the rest into tot,
+      // and tot becomes the total below
+      int32_t* const into = r0 + kRankChunk * k < before ? pre : tot;
+      atomicAdd(into + (id >= 0 && id < E ? id : E), 1);
     }
   }
+  int my_id = mine < n ? ids[mine] : -1;   // this thread's route of the chunk
+  if (my_id < 0 || my_id >= E) my_id = -1;
   if (my_id >= 0) atomicAdd(&wcnt[(tid >> 6) * E + my_id], 1);
   bad = __syncthreads_or(bad);   // also: every count is in
   for (int e = tid; e < E; e += kRankChunk) tot[e] += pre[e];
@@ -659,7 +662,7 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int K, int E, char* ws,
   }
   const int nchunks = int((n + kRankChunk - 1) / kRankChunk);
   if (n <= kChunkedRoutes && E <= kChunkedMaxE) {
-    hipLaunchKernelGGL(k_route_chunked, dim3(nchunks), dim3(kRankChunk), 6 * E * sizeof(int32_t),
+    hipLaunchKernelGGL(k_route_chunked, dim3(nchunks), dim3(kRankChunk), (6 * E + 2) * sizeof(int32_t),
                        s, ids, int(n), E, int(T),
                        reinterpret_cast<int32_t*>(ws + L.counts),
                        reinterpret_cast<int32_t*>(ws + L.offsets),
